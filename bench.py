@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Benchmark of the fp32 matrix multiply C = A x B on one MI355X.
+
+A step is one call of the production kernel on the square 4096^3 workload
+(A, B ~ U[-1, 1], seed 2; inputs resident in HBM before timing starts).
+Prints ONE JSON line with TFLOP/s, the roofline of the dominant kernel, the
+skinny K = 64 workload's HBM rate against the bandwidth measured in the same
+run, and the CPU oracle timed on a bounded sample as a reported baseline.
+
+  python bench.py [--gpus 1] [--steps 50] [--warmup 5]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fp32 GEMM TFLOPS @N=4096 (% of fp32 peak); HBM GB/s on K=64 skinny shape"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+PROD_SOURCE = os.path.join(ROOT, "tiled_fp32_gemm_03_amd", "csrc", "prod.hip")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def prod_source_digest() -> str:
+    with open(PROD_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def time_launches(fn, steps: int, warmup: int, stream) -> tuple[float, float]:
+    """(average ms per launch from HIP events on `stream`, wall seconds)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / steps, wall
+
+
+def measure_hbm(g, stream, reps: int = 8) -> dict:
+    """Streaming probes over 1 GiB arrays (far above the 256 MB Infinity Cache)."""
+    import torch
+    n = 1 << 28  # floats per array
+    dev = torch.device("cuda:0")
+    x = torch.ones(n, device=dev)
+    y = torch.ones(n, device=dev)
+    z = torch.empty(n, device=dev)
+    s = stream.cuda_stream
+    out = {}
+    for kind, name, bytes_per in ((g.PROBE_COPY, "copy", 8), (g.PROBE_FILL, "fill", 4),
+                                  (g.PROBE_VADD, "vector_add", 12)):
+        ms, _ = time_launches(lambda: g.gemm_f32_probe_stream(kind, n, x.data_ptr(), y.data_ptr(),
+                                                               z.data_ptr(), s), reps, 2, stream)
+        out[name] = round(n * bytes_per / (ms * 1e-3) / 1e9, 1)
+    del x, y, z
+    torch.cuda.empty_cache()
+    out["best"] = max(out.values())
+    return out
+
+
+def measure_mfma(g, stream) -> float:
+    import torch
+    wgs, iters = 256 * 4, 2000
+    buf = torch.zeros(wgs * 4, device="cuda:0")
+    ms, _ = time_launches(lambda: g.gemm_f32_probe_mfma(wgs, iters, buf.data_ptr(), stream.cuda_stream),
+                          5, 2, stream)
+    return g.gemm_f32_probe_mfma_flops(wgs, iters) / (ms * 1e-3) / 1e12
+
+
+def load_traffic(workload: str, config_label: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None when
+    absent or taken on a different version of the production kernel."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = data.get(workload)
+    if not rec or rec.get("prod_source_sha256_16") != prod_source_digest():
+        return None
+    if rec.get("config") != config_label:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(a, b, target_s: float) -> dict:
+    """The CPU oracle (test infrastructure) on a bounded row band of the same
+    workload: reported baseline only."""
+    import oracle
+    import numpy as np
+    K = a.shape[1]
+    N = b.shape[1]
+    probe_rows = 8
+    t0 = time.perf_counter()
+    oracle.gemm(np.ascontiguousarray(a[:probe_rows]), b)
+    t_probe = time.perf_counter() - t0
+    rows = int(min(a.shape[0], max(probe_rows, round(target_s / max(t_probe, 1e-6) * probe_rows))))
+    band = np.ascontiguousarray(a[:rows])
+    t0 = time.perf_counter()
+    oracle.gemm(band, b)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * N * K
+    cpu_model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of the {a.shape[0]}x{N}x{K} product "
+                      f"({rows}x{N} outputs, full K), {dt:.1f} s",
+            "seconds": round(dt, 2), "cpu_model": cpu_model}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="square_4096")
+    ap.add_argument("--variant", default="prod")
+    ap.add_argument("--config", type=int, default=-1, help="launch-table entry (-1 = automatic)")
+    ap.add_argument("--skinny-steps", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probes", action="store_true")
+    ap.add_argument("--no-skinny", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported; this library measures one GPU "
+              "(the product is a single-GPU kernel; see the sharding notes in the design doc)",
+              file=sys.stderr, flush=True)
+        return 2
+
+    import torch
+
+    import tiled_fp32_gemm_03_amd as g
+    from gemm_inputs import WORKLOADS, make_workload
+    from tiled_fp32_gemm_03_amd import roofline as rf
+
+    if not torch.cuda.is_available():
+        print("bench.py: no visible GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    w, a, b = make_workload(args.workload)
+    log(f"workload {w.name}: {w.description}; device {props.name}, {props.multi_processor_count} CUs")
+    ta = torch.from_numpy(a).to(dev)
+    tb = torch.from_numpy(b).to(dev)
+    tc = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    tile = g.gemm_f32_tile(args.variant, args.config, w.M, w.N, w.K)
+    label = g.config_name(args.variant, args.config, w.M, w.N, w.K)
+    s = stream.cuda_stream
+
+    def step():
+        g.gemm_f32_ex(w.M, w.N, w.K, ta.data_ptr(), w.K, tb.data_ptr(), w.N, tc.data_ptr(), w.N,
+                      args.variant, args.config, s)
+
+    log(f"timing {label}: {args.warmup} warmup + {args.steps} steps")
+    ms, wall = time_launches(step, args.steps, args.warmup, stream)
+    flops = rf.flops(w.M, w.N, w.K)
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"{label}: {ms:.4f} ms/launch, {tflops:.2f} TFLOP/s (wall {wall:.3f} s for {args.steps})")
+
+    traffic = load_traffic(w.name, label)
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "dist": w.dist,
+                   "seed": w.seed, "variant": args.variant, "tile": label},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 3),
+            "peak": rf.PEAK_FP32_MFMA_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / rf.PEAK_FP32_MFMA_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": label,
+            "algorithmic_flops_per_launch": flops,
+            "compulsory_bytes_per_launch": rf.compulsory_bytes(w.M, w.N, w.K),
+            "model_issued_load_bytes_per_launch": 4 * rf.issued_load_elements(
+                args.variant, w.M, w.N, w.K, tile),
+        },
+        "wall_s_timed_region": round(wall, 4),
+        "device": {"name": props.name, "cus": props.multi_processor_count},
+    }
+    del tc
+    torch.cuda.empty_cache()
+
+    measured = {}
+    if not args.no_probes:
+        log("HBM streaming probes (1 GiB arrays)")
+        hbm = measure_hbm(g, stream)
+        log(f"HBM GB/s: {hbm}")
+        pm = measure_mfma(g, stream)
+        log(f"fp32 MFMA probe: {pm:.1f} TFLOP/s")
+        measured = {"hbm_gbps": hbm, "mfma_fp32_tflops": round(pm, 2)}
+        result["measured_peaks"] = measured
+        result["roofline"]["frac_of_measured_mfma"] = round(tflops / pm, 4)
+
+    if not args.no_skinny:
+        sw, sa, sb = make_workload("skinny_k64")
+        sta, stb = torch.from_numpy(sa).to(dev), torch.from_numpy(sb).to(dev)
+        stc = torch.empty((sw.M, sw.N), dtype=torch.float32, device=dev)
+        slabel = g.config_name("prod", -1, sw.M, sw.N, sw.K)
+
+        def sstep():
+            g.gemm_f32_ex(sw.M, sw.N, sw.K, sta.data_ptr(), sw.K, stb.data_ptr(), sw.N,
+                          stc.data_ptr(), sw.N, "prod", -1, s)
+
+        sms, _ = time_launches(sstep, args.skinny_steps, 3, stream)
+        sbytes = rf.compulsory_bytes(sw.M, sw.N, sw.K)
+        gbps = sbytes / (sms * 1e-3) / 1e9
+        stf = rf.flops(sw.M, sw.N, sw.K) / (sms * 1e-3) / 1e12
+        log(f"skinny {slabel}: {sms:.4f} ms, {gbps:.0f} GB/s, {stf:.1f} TFLOP/s")
+        sk = {"workload": sw.name, "M": sw.M, "N": sw.N, "K": sw.K, "kernel": slabel,
+              "ms_per_launch": round(sms, 5), "gbps": round(gbps, 1),
+              "frac_of_peak_hbm": round(gbps / rf.PEAK_HBM_GBPS, 4),
+              "tflops": round(stf, 3), "frac_of_peak_fp32": round(stf / rf.PEAK_FP32_MFMA_TFLOPS, 4),
+              "intensity_flop_per_byte": round(rf.intensity(sw.M, sw.N, sw.K), 2)}
+        if measured:
+            bmeas = measured["hbm_gbps"]["best"]
+            pmeas = measured["mfma_fp32_tflops"]
+            roof = rf.binding_roof_tflops(sw.M, sw.N, sw.K, pmeas, bmeas)
+            sk["frac_of_measured_hbm"] = round(gbps / bmeas, 4)
+            sk["binding_roof_tflops"] = round(roof, 2)
+            sk["binding_roof"] = "mfma" if pmeas <= rf.intensity(sw.M, sw.N, sw.K) * bmeas / 1000 else "hbm"
+            sk["frac_of_binding_roof"] = round(stf / roof, 4)
+        result["skinny_k64"] = sk
+        del sta, stb, stc
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        log(f"CPU oracle baseline (~{args.cpu_seconds:.0f} s sample)")
+        result["cpu_baseline"] = cpu_baseline(a, b, args.cpu_seconds)
+        log(f"cpu baseline: {result['cpu_baseline']}")
+    else:
+        result["cpu_baseline"] = None
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,136 @@
+/*
+ * gemm_f32.h -- C ABI of the MI355X (gfx950) fp32 matrix-multiply library.
+ *
+ * The operation is the dense product C = A x B in fp32 that the pages build
+ * their kernels for: each output element is the dot product of a row of A
+ * with a column of B along the shared K dimension (ijyty.com tiled-matmul
+ * article, naive-review paragraph; mayulu.co "CUDA 编程系列之三", section 6).
+ * The pages show only kernels over square N x N row-major matrices with
+ * leading dimension N (geek-doc.cn "矩阵乘法 tiling", sections 一 and 四); this
+ * interface generalises that to M x K times K x N with explicit leading
+ * dimensions and keeps the pages' "C is assigned, never accumulated into".
+ *
+ * Layout (all matrices row-major, element type float, 4-byte aligned):
+ *   A[i][k] = A[i*lda + k]  for 0 <= i < M, 0 <= k < K
+ *   B[k][j] = B[k*ldb + j]  for 0 <= k < K, 0 <= j < N
+ *   C[i][j] = C[i*ldc + j]  for 0 <= i < M, 0 <= j < N
+ * Result: C[i][j] = sum_{k<K} A[i][k] * B[k][j], accumulated in fp32 in an
+ * order that depends on the variant (several fp32 results are correct for
+ * non-integer inputs; integer-valued inputs whose partial sums stay below
+ * 2^24 give the exact result on every variant).  Elements of C outside the
+ * M x N window (the ldc padding) are never written.
+ *
+ * Memory and ownership: A, B and C are device pointers owned by the caller
+ * (for example the storage of torch tensors).  The library allocates no
+ * device memory, keeps no per-call state, and is re-entrant.  C must not
+ * overlap A or B.
+ *
+ * Streams: `stream` is a hipStream_t passed as void*; NULL means the null
+ * stream.  Calls are asynchronous: they return once the kernel is enqueued.
+ * Argument errors are returned synchronously before anything is enqueued;
+ * launch errors are the launch call's own status (see gemm_f32_last_error); faults
+ * during execution surface at the caller's next synchronisation.
+ */
+#ifndef GEMM_F32_H
+#define GEMM_F32_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes --------------------------------------------------- */
+#define GEMM_F32_OK 0
+#define GEMM_F32_INVALID_DIM 1   /* M, N or K negative                      */
+#define GEMM_F32_INVALID_LD 2    /* lda < max(1,K), ldb or ldc < max(1,N)   */
+#define GEMM_F32_NULL_PTR 3      /* a needed matrix pointer is NULL         */
+#define GEMM_F32_BAD_VARIANT 4   /* unknown variant                         */
+#define GEMM_F32_LAUNCH_FAILED 5 /* the HIP runtime rejected the launch     */
+#define GEMM_F32_MISALIGNED 6    /* a pointer is not 4-byte aligned         */
+#define GEMM_F32_BAD_CONFIG 7    /* config index outside the launch table   */
+#define GEMM_F32_BAD_ARG 8       /* other invalid argument (query helpers)  */
+
+/* ---- variants: the kernel ladder ------------------------------------ */
+/* One thread per output element, operands read straight from global
+ * memory, fp32 register accumulator (geek-doc.cn section 一; csh0101.cc
+ * section "naive kernel 怎么读数据").  Workgroup 64 x 4 threads: one wave
+ * covers 64 consecutive columns of one row. */
+#define GEMM_F32_NAIVE 0
+/* Textbook T x T tiled kernel with T = 16: per k step every thread loads one
+ * A and one B element into LDS, barrier, T multiply-adds from LDS, barrier
+ * (geek-doc.cn section 四; csh0101.cc section "代码里的样子"; ijyty.com steps
+ * ①-⑧; mayulu.co section 6).  Elements outside the matrices are loaded as 0
+ * (geek-doc.cn section 六; mayulu.co section 7). */
+#define GEMM_F32_TILED 1
+/* Production kernel: BM x BN workgroup tiles, 128-bit global loads into a
+ * register stage, double-buffered padded LDS with one barrier per k step,
+ * per-wave register-blocked 32x32 output blocks computed by fp32 MFMA
+ * (v_mfma_f32_32x32x2_f32).  The "one thread, several outputs" and
+ * "register / wave / instruction block" pyramid the pages point to
+ * (geek-doc.cn sections 三 and 五) on CDNA4 matrix cores. */
+#define GEMM_F32_PROD 2
+/* The textbook kernel with T = 32 (1024 threads per workgroup). */
+#define GEMM_F32_TILED32 3
+/* The textbook kernel with T = 4, the pages' worked tile size (csh0101.cc
+ * T = 4 example; ijyty.com 8x8 / TILE_SIZE = 4 example).  For tests and
+ * teaching; slow. */
+#define GEMM_F32_TILED4 4
+#define GEMM_F32_NUM_VARIANTS 5
+
+/*
+ * gemm_f32 -- C = A x B (overwrite), see the layout above.
+ *   M, N, K        problem size, each >= 0.  M == 0 or N == 0: no-op.
+ *                  K == 0: C is set to 0 (the empty sum).
+ *   A, lda         M x K operand, lda >= max(1, K).  May be NULL if M*K == 0.
+ *   B, ldb         K x N operand, ldb >= max(1, N).  May be NULL if K*N == 0.
+ *   C, ldc         M x N result, ldc >= max(1, N).  May be NULL if M*N == 0.
+ *   variant        one of GEMM_F32_* variants above.
+ *   stream         hipStream_t (NULL = null stream).
+ * Returns GEMM_F32_OK or an error code; on error nothing is launched.
+ */
+int gemm_f32(int M, int N, int K, const float *A, int lda, const float *B,
+             int ldb, float *C, int ldc, int variant, void *stream);
+
+/*
+ * gemm_f32_ex -- gemm_f32 with an explicit launch-table entry.
+ *   config  -1 picks the entry gemm_f32 would use for this shape; otherwise
+ *           an index below gemm_f32_num_configs(variant).
+ * Same semantics and errors as gemm_f32, plus GEMM_F32_BAD_CONFIG.
+ */
+int gemm_f32_ex(int M, int N, int K, const float *A, int lda, const float *B,
+                int ldb, float *C, int ldc, int variant, int config,
+                void *stream);
+
+/* Number of launch-table entries of a variant (0 for an unknown variant). */
+int gemm_f32_num_configs(int variant);
+
+/*
+ * gemm_f32_tile -- the launch-table entry a call would use (host only, no GPU
+ * access).  For config == -1 the shape-based choice is reported.  Writes the
+ * workgroup tile BM x BN, its k step BK, threads per workgroup and the entry
+ * index actually chosen.  Any output pointer may be NULL.  For the naive
+ * variant BM x BN is the 4 x 64 block of outputs a workgroup covers and BK
+ * is 1.  Returns GEMM_F32_OK, GEMM_F32_BAD_VARIANT, GEMM_F32_BAD_CONFIG or
+ * GEMM_F32_INVALID_DIM.
+ */
+int gemm_f32_tile(int variant, int config, int M, int N, int K, int *BM,
+                  int *BN, int *BK, int *threads, int *chosen_config);
+
+/*
+ * gemm_f32_last_error -- detail of the last GEMM_F32_LAUNCH_FAILED returned
+ * on the calling thread: the HIP runtime's error name and message, or "" if
+ * no launch has failed on this thread.  The string is thread-local and stays
+ * valid until the next failing call on the same thread.
+ */
+const char *gemm_f32_last_error(void);
+
+/* Static message for a status code (never NULL). */
+const char *gemm_f32_status_string(int status);
+
+/* Library version string, e.g. "gemm_f32 0.1.0 gfx950". */
+const char *gemm_f32_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_F32_H */

@@ -1,0 +1,53 @@
+/*
+ * gemm_f32_probes.h -- measurement probes shipped with the gemm_f32 library.
+ *
+ * They supply the denominators of the roofline report (page 4, mayulu.co
+ * "CUDA 编程系列之三", sections 1-3: a kernel is bounded by the lower of the
+ * compute roof and intensity x bandwidth) and a copy kernel of known size to
+ * calibrate memory counters.  They are not part of the product C = A x B.
+ *
+ * All pointers are device pointers owned by the caller; nothing is allocated.
+ * Calls are asynchronous on `stream` (hipStream_t as void*, NULL = null
+ * stream).  Status codes are those of gemm_f32.h.
+ */
+#ifndef GEMM_F32_PROBES_H
+#define GEMM_F32_PROBES_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Streaming kinds.  Bytes moved per element: copy 8, fill 4, vector add 12.
+ * Vector add C[i] = A[i] + B[i] is the pages' memory yardstick: one FLOP per
+ * twelve bytes (mayulu.co section 4). */
+#define GEMM_F32_PROBE_COPY 0 /* z[i] = x[i]          */
+#define GEMM_F32_PROBE_FILL 1 /* z[i] = 1.0f          */
+#define GEMM_F32_PROBE_VADD 2 /* z[i] = x[i] + y[i]   */
+
+/*
+ * gemm_f32_probe_stream -- one streaming pass over n floats with 128-bit
+ * accesses.  x (and y for VADD) are read, z is written; for FILL, x and y
+ * may be NULL; for COPY, y may be NULL.  n >= 0.  All pointers must be
+ * 16-byte aligned.  Returns GEMM_F32_BAD_ARG for an unknown kind or a
+ * negative n, GEMM_F32_NULL_PTR / GEMM_F32_MISALIGNED for bad pointers.
+ */
+int gemm_f32_probe_stream(int kind, long long n, const float *x,
+                          const float *y, float *z, void *stream);
+
+/*
+ * gemm_f32_probe_mfma -- fp32 matrix-core throughput probe with no memory
+ * traffic in its loop: `workgroups` workgroups of 256 threads, each wave
+ * running `iters` rounds of 8 independent v_mfma_f32_32x32x2_f32 chains.
+ * One float per wave is written to out (out must hold workgroups * 4
+ * floats) so the work stays live.  workgroups >= 1, iters >= 1.
+ * gemm_f32_probe_mfma_flops returns the FLOPs such a call performs
+ * (-1 for invalid arguments).
+ */
+int gemm_f32_probe_mfma(int workgroups, int iters, float *out, void *stream);
+long long gemm_f32_probe_mfma_flops(int workgroups, int iters);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_F32_PROBES_H */

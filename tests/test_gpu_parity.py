@@ -1,0 +1,314 @@
+"""GPU parity: every rung of the kernel ladder against the CPU oracle, element
+by element on the same seeded inputs, through the C ABI.
+
+Bars (from the arithmetic):
+  * integer-valued inputs whose partial sums stay below 2^24: bit-exact;
+  * other inputs: max |C - C_ref| <= 1e-4 * sqrt(K) and
+    ||C - C_ref||_F / ||C_ref||_F <= 1e-5 (fp64 on the host).
+Full-size workloads are checked on sampled elements (the oracle computes them
+one by one) plus properties that hold at any size.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from gemm_inputs import WORKLOADS, make, make_workload  # noqa: E402
+
+LADDER = ("naive", "tiled", "tiled32", "prod")
+
+
+@pytest.fixture(scope="module")
+def g():
+    import tiled_fp32_gemm_03_amd as lib
+    return lib
+
+
+def _dev():
+    return torch.device("cuda:0")
+
+
+def _tol_check(got: np.ndarray, ref: np.ndarray, K: int, what: str):
+    got64 = got.astype(np.float64)
+    ref64 = ref.astype(np.float64)
+    assert np.all(np.isfinite(got64)), f"{what}: non-finite output"
+    err = np.abs(got64 - ref64)
+    max_err = float(err.max()) if err.size else 0.0
+    denom = float(np.sqrt((ref64 ** 2).sum()))
+    fro = float(np.sqrt((err ** 2).sum())) / denom if denom > 0 else float(np.sqrt((err ** 2).sum()))
+    assert max_err <= 1e-4 * np.sqrt(max(K, 1)), f"{what}: max err {max_err:.3g} (K={K})"
+    assert fro <= 1e-5, f"{what}: relative Frobenius error {fro:.3g}"
+
+
+def _run(g, a, b, variant, config=-1):
+    ta = torch.from_numpy(a).to(_dev())
+    tb = torch.from_numpy(b).to(_dev())
+    c = g.matmul(ta, tb, variant=variant, config=config)
+    torch.cuda.synchronize()
+    return c.cpu().numpy()
+
+
+def _prod_configs(g):
+    return list(range(g.gemm_f32_num_configs("prod")))
+
+
+# ---- small and ragged shapes, every rung ---------------------------------
+
+SMALL_SHAPES = [(1, 1, 1), (3, 5, 7), (33, 65, 17), (64, 64, 64), (127, 129, 131),
+                (257, 383, 129), (300, 200, 700), (130, 520, 33)]
+
+
+@pytest.mark.parametrize("variant", LADDER)
+@pytest.mark.parametrize("shape", SMALL_SHAPES)
+def test_small_integer_bit_exact(g, variant, shape):
+    M, N, K = shape
+    print(f"case: int {variant} {shape}", flush=True)
+    a, b = make(M, N, K, "small_int", seed=M * 7 + N * 3 + K)
+    assert np.array_equal(_run(g, a, b, variant), oracle.gemm(a, b))
+
+
+@pytest.mark.parametrize("variant", LADDER)
+@pytest.mark.parametrize("shape", SMALL_SHAPES)
+def test_small_uniform_tolerance(g, variant, shape):
+    M, N, K = shape
+    print(f"case: uniform {variant} {shape}", flush=True)
+    a, b = make(M, N, K, "uniform", seed=M + N + K)
+    _tol_check(_run(g, a, b, variant), oracle.gemm(a, b), K, f"{variant} {shape}")
+
+
+def test_every_prod_config(g):
+    for cfg in _prod_configs(g):
+        for (M, N, K) in [(257, 383, 129), (512, 256, 64), (1, 300, 40), (200, 1, 33)]:
+            print(f"case: prod config {cfg} {M}x{N}x{K}", flush=True)
+            a, b = make(M, N, K, "small_int", seed=cfg + M)
+            assert np.array_equal(_run(g, a, b, "prod", cfg), oracle.gemm(a, b)), (cfg, M, N, K)
+            a, b = make(M, N, K, "normal", seed=cfg + N)
+            _tol_check(_run(g, a, b, "prod", cfg), oracle.gemm(a, b), K, f"prod cfg {cfg}")
+
+
+def test_edge_sweep(g):
+    """Every remainder against every tile size: sampled combinations of
+    M, N, K around multiples of 16, 32, 64 and 128."""
+    sizes = [1, 2, 3, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257]
+    rng = np.random.default_rng(2024)
+    combos = {(s, s, s) for s in sizes}
+    while len(combos) < 60:
+        combos.add(tuple(int(x) for x in rng.choice(sizes, 3)))
+    for (M, N, K) in sorted(combos):
+        a, b = make(M, N, K, "small_int", seed=M * 1000003 + N * 1009 + K)
+        ref = oracle.gemm(a, b)
+        for variant in LADDER:
+            print(f"case: edge {variant} {M}x{N}x{K}", flush=True)
+            assert np.array_equal(_run(g, a, b, variant), ref), (variant, M, N, K)
+
+
+# ---- the pages' worked example ------------------------------------------
+
+def test_block_decomposition_T4_8x8(g):
+    """8x8 integer matrices with T = 4 tiles (two k phases): the T = 4 rung
+    reproduces C00 = A00 B00 + A01 B10 and the other blocks bit for bit."""
+    rng = np.random.default_rng(42)
+    a = rng.integers(-7, 8, (8, 8)).astype(np.float32)
+    b = rng.integers(-7, 8, (8, 8)).astype(np.float32)
+    c = _run(g, a, b, "tiled4")
+    assert np.array_equal(c, oracle.gemm(a, b))
+    blk = lambda x, r, s: np.ascontiguousarray(x[4 * r:4 * r + 4, 4 * s:4 * s + 4])  # noqa: E731
+    for r in range(2):
+        for s in range(2):
+            want = oracle.gemm(blk(a, r, 0), blk(b, 0, s)) + oracle.gemm(blk(a, r, 1), blk(b, 1, s))
+            assert np.array_equal(blk(c, r, s), want)
+
+
+def test_tiled4_small_shapes(g):
+    for (M, N, K) in [(8, 8, 8), (9, 7, 13), (33, 17, 65)]:
+        a, b = make(M, N, K, "small_int", seed=M)
+        assert np.array_equal(_run(g, a, b, "tiled4"), oracle.gemm(a, b))
+
+
+# ---- leading dimensions, empty cases ------------------------------------
+
+@pytest.mark.parametrize("variant", LADDER)
+def test_leading_dimensions_and_padding_untouched(g, variant):
+    M, N, K = 67, 45, 39
+    lda, ldb, ldc = 41, 53, 47  # odd, larger than the row lengths
+    a, b = make(M, N, K, "small_int", seed=5)
+    dev = _dev()
+    abuf = torch.full((M * lda,), float("nan"), dtype=torch.float32, device=dev)
+    bbuf = torch.full((K * ldb,), float("nan"), dtype=torch.float32, device=dev)
+    cbuf = torch.full((M * ldc,), -7.0, dtype=torch.float32, device=dev)
+    abuf.view(M, lda)[:, :K] = torch.from_numpy(a).to(dev)
+    bbuf.view(K, ldb)[:, :N] = torch.from_numpy(b).to(dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    g.gemm_f32(M, N, K, abuf.data_ptr(), lda, bbuf.data_ptr(), ldb, cbuf.data_ptr(), ldc,
+               variant, stream)
+    torch.cuda.synchronize()
+    c = cbuf.view(M, ldc).cpu().numpy()
+    assert np.array_equal(c[:, :N], oracle.gemm(a, b))
+    assert np.all(c[:, N:] == -7.0)
+
+
+@pytest.mark.parametrize("variant", LADDER)
+def test_aligned_padded_leading_dimensions(g, variant):
+    """ld a multiple of 4 but larger than the row: the 128-bit path with padding."""
+    M, N, K = 130, 132, 72
+    lda, ldb, ldc = 80, 136, 140
+    a, b = make(M, N, K, "uniform", seed=9)
+    dev = _dev()
+    abuf = torch.zeros((M, lda), dtype=torch.float32, device=dev)
+    bbuf = torch.zeros((K, ldb), dtype=torch.float32, device=dev)
+    cbuf = torch.full((M, ldc), 3.0, dtype=torch.float32, device=dev)
+    abuf[:, :K] = torch.from_numpy(a).to(dev)
+    bbuf[:, :N] = torch.from_numpy(b).to(dev)
+    g.matmul(abuf[:, :K], bbuf[:, :N], out=cbuf[:, :N], variant=variant)
+    torch.cuda.synchronize()
+    c = cbuf.cpu().numpy()
+    _tol_check(c[:, :N], oracle.gemm(a, b), K, variant)
+    assert np.all(c[:, N:] == 3.0)
+
+
+@pytest.mark.parametrize("variant", LADDER)
+def test_k_zero_gives_zero_and_empty_is_noop(g, variant):
+    dev = _dev()
+    c = torch.full((5, 7), 9.0, device=dev)
+    g.matmul(torch.empty((5, 0), device=dev), torch.empty((0, 7), device=dev), out=c,
+             variant=variant)
+    torch.cuda.synchronize()
+    assert torch.all(c == 0).item()
+    e = torch.full((0, 7), 1.0, device=dev)
+    g.matmul(torch.empty((0, 3), device=dev), torch.ones((3, 7), device=dev), out=e,
+             variant=variant)
+    torch.cuda.synchronize()
+
+
+# ---- named workloads ------------------------------------------------------
+
+@pytest.mark.parametrize("variant", LADDER + ("tiled4",))
+def test_workload_square_256(g, variant):
+    w, a, b = make_workload("square_256")
+    _tol_check(_run(g, a, b, variant), oracle.gemm(a, b), w.K, f"square_256 {variant}")
+
+
+@pytest.mark.parametrize("variant", LADDER)
+def test_workload_square_1024_int_bit_exact(g, variant):
+    w, a, b = make_workload("square_1024_int")
+    got = _run(g, a, b, variant)
+    ref = oracle.gemm(a, b)
+    assert np.array_equal(got, ref)
+
+
+def _sample_indices(M, N, n, seed):
+    rng = np.random.default_rng(seed)
+    ii = [rng.integers(0, M, n)]
+    jj = [rng.integers(0, N, n)]
+    # whole first/last row and column (every edge tile), and the corners
+    for r in (0, M - 1):
+        cols = np.arange(N)
+        ii.append(np.full(N, r))
+        jj.append(cols)
+    for c in (0, N - 1):
+        rows = np.arange(M)
+        ii.append(rows)
+        jj.append(np.full(M, c))
+    return np.concatenate(ii).astype(np.int64), np.concatenate(jj).astype(np.int64)
+
+
+@pytest.mark.parametrize("name", ["square_4096", "ragged", "skinny_k64"])
+def test_full_size_workload_sampled(g, name):
+    """The launch configuration the benchmark times, at full size, checked on
+    sampled outputs (plus whole edge rows and columns)."""
+    w, a, b = make_workload(name)
+    print(f"case: full-size {name} prod auto", flush=True)
+    dev = _dev()
+    ta, tb = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+    c = g.matmul(ta, tb, variant="prod")
+    torch.cuda.synchronize()
+    assert torch.isfinite(c).all().item()
+    ii, jj = _sample_indices(w.M, w.N, 20000, seed=w.seed)
+    got = c[torch.from_numpy(ii).to(dev), torch.from_numpy(jj).to(dev)].cpu().numpy()
+    ref = oracle.gemm_elems(a, b, ii, jj)
+    _tol_check(got, ref, w.K, f"{name} sampled")
+    del c, ta, tb
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["square_4096", "ragged"])
+def test_full_size_tiled_sampled(g, name):
+    w, a, b = make_workload(name)
+    dev = _dev()
+    ta, tb = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+    for variant in ("tiled", "tiled32"):
+        print(f"case: full-size {name} {variant}", flush=True)
+        c = g.matmul(ta, tb, variant=variant)
+        torch.cuda.synchronize()
+        ii, jj = _sample_indices(w.M, w.N, 4000, seed=w.seed + 1)
+        got = c[torch.from_numpy(ii).to(dev), torch.from_numpy(jj).to(dev)].cpu().numpy()
+        _tol_check(got, oracle.gemm_elems(a, b, ii, jj), w.K, f"{name} {variant}")
+
+
+@pytest.mark.parametrize("variant", LADDER)
+def test_all_ones_full_ragged_shape(g, variant):
+    """C = K everywhere for all-ones inputs at the ragged workload's full shape
+    (a property that holds at any size; every edge tile is exercised)."""
+    w = WORKLOADS["ragged"]
+    dev = _dev()
+    if variant == "naive":
+        M, N, K = 1025, 1023, 2049  # the naive rung is slow; same remainders
+    else:
+        M, N, K = w.M, w.N, w.K
+    c = g.matmul(torch.ones((M, K), device=dev), torch.ones((K, N), device=dev), variant=variant)
+    torch.cuda.synchronize()
+    assert torch.all(c == float(K)).item()
+
+
+@pytest.mark.parametrize("variant", LADDER)
+def test_identity_exact(g, variant):
+    w, a, _ = make_workload("ragged")
+    a = np.ascontiguousarray(a[:513])
+    dev = _dev()
+    eye = torch.eye(a.shape[1], device=dev)
+    c = g.matmul(torch.from_numpy(a).to(dev), eye, variant=variant)
+    torch.cuda.synchronize()
+    assert np.array_equal(c.cpu().numpy(), a)
+
+
+def test_streams_are_respected(g):
+    """A call on a side stream is ordered after work queued before it there."""
+    dev = _dev()
+    a, b = make(300, 260, 100, "small_int", seed=77)
+    ta, tb = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        c = g.matmul(ta, tb, variant="prod")
+    s.synchronize()
+    assert np.array_equal(c.cpu().numpy(), oracle.gemm(a, b))
+
+
+# ---- probes -----------------------------------------------------------
+
+def test_stream_probes(g):
+    dev = _dev()
+    n = (1 << 20) + 3
+    x = torch.randn(n, device=dev)
+    y = torch.randn(n, device=dev)
+    z = torch.empty(n, device=dev)
+    s = torch.cuda.current_stream().cuda_stream
+    g.gemm_f32_probe_stream(g.PROBE_COPY, n, x.data_ptr(), 0, z.data_ptr(), s)
+    torch.cuda.synchronize()
+    assert torch.equal(z, x)
+    g.gemm_f32_probe_stream(g.PROBE_VADD, n, x.data_ptr(), y.data_ptr(), z.data_ptr(), s)
+    torch.cuda.synchronize()
+    assert torch.equal(z, x + y)
+    g.gemm_f32_probe_stream(g.PROBE_FILL, n, 0, 0, z.data_ptr(), s)
+    torch.cuda.synchronize()
+    assert torch.all(z == 1.0).item()
+
+
+def test_mfma_probe_runs(g):
+    dev = _dev()
+    out = torch.zeros(8 * 4, device=dev)
+    g.gemm_f32_probe_mfma(8, 10, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item() and torch.all(out != 0).item()

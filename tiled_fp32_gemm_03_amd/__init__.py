@@ -1,0 +1,197 @@
+"""Python binding of the gfx950 fp32 matrix-multiply library ``libgemm_f32.so``.
+
+Argument marshalling only: every step of C = A x B runs in the library's HIP
+kernels.  If the library is missing the import fails loudly; there is no
+CPU or PyTorch fallback.
+
+Raw C-ABI mirrors (same names and argument order as ``include/gemm_f32.h``):
+  gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, variant, stream)
+  gemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, variant, config, stream)
+  gemm_f32_tile(variant, config, M, N, K) -> dict
+  gemm_f32_num_configs(variant), gemm_f32_status_string(rc), gemm_f32_version()
+  gemm_f32_probe_stream(kind, n, x, y, z, stream)      (include/gemm_f32_probes.h)
+  gemm_f32_probe_mfma(workgroups, iters, out, stream), gemm_f32_probe_mfma_flops(...)
+Pointers are device addresses (ints); ``stream`` is a hipStream_t as int
+(0 = null stream).  A non-zero status raises ``GemmError``.
+
+Tensor convenience: ``matmul(A, B, out=None, variant="prod", config=-1)``
+takes float32 CUDA tensors whose last stride is 1 and passes ``stride(0)`` as
+the leading dimension, on torch's current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "GemmError", "VARIANTS", "config_name", "PROBE_COPY", "PROBE_FILL", "PROBE_VADD",
+    "gemm_f32", "gemm_f32_ex", "gemm_f32_tile", "gemm_f32_num_configs",
+    "gemm_f32_status_string", "gemm_f32_version", "gemm_f32_last_error", "gemm_f32_probe_stream",
+    "gemm_f32_probe_mfma", "gemm_f32_probe_mfma_flops", "matmul", "library_path",
+    "exported_symbols",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libgemm_f32.so")
+
+# One HIP runtime per process: PyTorch ships its own libamdhip64 (same
+# soname).  Loading torch first makes this library bind to that copy instead
+# of pulling in a second runtime from /opt/rocm, which could not launch on
+# memory that torch's runtime allocated.
+import torch  # noqa: E402,F401
+
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(
+        f"{_LIB_PATH} is not built; run __graft_entry__.build() or "
+        "python tiled_fp32_gemm_03_amd/build_lib.py (needs ROCm hipcc)")
+
+_lib = ctypes.CDLL(_LIB_PATH)
+
+_i = ctypes.c_int
+_ll = ctypes.c_longlong
+_p = ctypes.c_void_p
+_ip = ctypes.POINTER(ctypes.c_int)
+
+_SIGS = {
+    "gemm_f32": ([_i, _i, _i, _p, _i, _p, _i, _p, _i, _i, _p], _i),
+    "gemm_f32_ex": ([_i, _i, _i, _p, _i, _p, _i, _p, _i, _i, _i, _p], _i),
+    "gemm_f32_num_configs": ([_i], _i),
+    "gemm_f32_tile": ([_i, _i, _i, _i, _i, _ip, _ip, _ip, _ip, _ip], _i),
+    "gemm_f32_status_string": ([_i], ctypes.c_char_p),
+    "gemm_f32_version": ([], ctypes.c_char_p),
+    "gemm_f32_last_error": ([], ctypes.c_char_p),
+    "gemm_f32_probe_stream": ([_i, _ll, _p, _p, _p, _p], _i),
+    "gemm_f32_probe_mfma": ([_i, _i, _p, _p], _i),
+    "gemm_f32_probe_mfma_flops": ([_i, _i], _ll),
+}
+for _name, (_args, _ret) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _ret
+
+# Variant ids of include/gemm_f32.h.
+VARIANTS = {"naive": 0, "tiled": 1, "prod": 2, "tiled32": 3, "tiled4": 4}
+PROBE_COPY, PROBE_FILL, PROBE_VADD = 0, 1, 2
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        detail = gemm_f32_last_error() if status == 5 else ""
+        super().__init__(f"{where}: status {status} ({gemm_f32_status_string(status)})"
+                         + (f": {detail}" if detail else ""))
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def exported_symbols() -> tuple[str, ...]:
+    return tuple(_SIGS)
+
+
+def _variant(v) -> int:
+    if isinstance(v, str):
+        try:
+            return VARIANTS[v]
+        except KeyError:
+            raise ValueError(f"unknown variant {v!r}; one of {sorted(VARIANTS)}") from None
+    return int(v)
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != 0:
+        raise GemmError(rc, where)
+
+
+def gemm_f32_status_string(status: int) -> str:
+    return _lib.gemm_f32_status_string(int(status)).decode()
+
+
+def gemm_f32_last_error() -> str:
+    return _lib.gemm_f32_last_error().decode()
+
+
+def gemm_f32_version() -> str:
+    return _lib.gemm_f32_version().decode()
+
+
+def gemm_f32_num_configs(variant) -> int:
+    return int(_lib.gemm_f32_num_configs(_variant(variant)))
+
+
+def gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, variant, stream=0) -> None:
+    rc = _lib.gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, _variant(variant), stream or None)
+    _check(rc, "gemm_f32")
+
+
+def gemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, variant, config, stream=0) -> None:
+    rc = _lib.gemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, _variant(variant), int(config),
+                          stream or None)
+    _check(rc, "gemm_f32_ex")
+
+
+def gemm_f32_tile(variant, config, M, N, K) -> dict:
+    vals = [ctypes.c_int(0) for _ in range(5)]
+    rc = _lib.gemm_f32_tile(_variant(variant), int(config), M, N, K,
+                            *[ctypes.byref(v) for v in vals])
+    _check(rc, "gemm_f32_tile")
+    bm, bn, bk, nt, chosen = (v.value for v in vals)
+    return {"BM": bm, "BN": bn, "BK": bk, "threads": nt, "config": chosen}
+
+
+def gemm_f32_probe_stream(kind, n, x, y, z, stream=0) -> None:
+    _check(_lib.gemm_f32_probe_stream(int(kind), int(n), x or None, y or None, z or None,
+                                      stream or None), "gemm_f32_probe_stream")
+
+
+def gemm_f32_probe_mfma(workgroups, iters, out, stream=0) -> None:
+    _check(_lib.gemm_f32_probe_mfma(int(workgroups), int(iters), out or None, stream or None),
+           "gemm_f32_probe_mfma")
+
+
+def gemm_f32_probe_mfma_flops(workgroups, iters) -> int:
+    return int(_lib.gemm_f32_probe_mfma_flops(int(workgroups), int(iters)))
+
+
+def config_name(variant, config: int = -1, M: int = 1, N: int = 1, K: int = 1) -> str:
+    """Readable name of a launch-table entry, e.g. "prod#0:128x128x32/256t"."""
+    t = gemm_f32_tile(variant, config, M, N, K)
+    v = _variant(variant)
+    vname = next(k for k, val in VARIANTS.items() if val == v)
+    return f"{vname}#{t['config']}:{t['BM']}x{t['BN']}x{t['BK']}/{t['threads']}t"
+
+
+def _ld(t) -> int:
+    if t.dim() != 2:
+        raise ValueError("expected a 2-D tensor")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("the last dimension must be contiguous (stride 1)")
+    if t.shape[0] > 1 and t.stride(0) < t.shape[1]:
+        raise ValueError("rows overlap (row stride smaller than the row length)")
+    return max(1, t.stride(0) if t.shape[0] > 1 else t.shape[1])
+
+
+def matmul(A, B, out=None, variant="prod", config: int = -1, stream=None):
+    """C = A x B on the GPU for float32 tensors (row-major views with unit last stride)."""
+    import torch
+
+    for name, t in (("A", A), ("B", B)):
+        if t.dtype != torch.float32 or not t.is_cuda:
+            raise TypeError(f"{name} must be a float32 CUDA tensor")
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {tuple(A.shape)} x {tuple(B.shape)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (M, N) or not out.is_cuda:
+        raise TypeError("out must be a float32 CUDA tensor of shape (M, N)")
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device).cuda_stream
+    lda = max(_ld(A), max(1, K))
+    ldb = max(_ld(B), max(1, N))
+    ldc = max(_ld(out), max(1, N))
+    gemm_f32_ex(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, out.data_ptr(), ldc,
+                variant, config, stream)
+    return out

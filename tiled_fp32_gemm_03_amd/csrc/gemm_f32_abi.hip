@@ -1,0 +1,139 @@
+// C-ABI front end of the gemm_f32 library: argument validation, the variant
+// ladder and the launch tables.  Validation touches no GPU state, so every
+// error is returned before anything is enqueued.
+#include "gemm_f32.h"
+#include "gemm_internal.hpp"
+
+#include <cstdint>
+#include <cstdio>
+
+using namespace gemm_f32_impl;
+
+namespace {
+
+constexpr int kTiledT[GEMM_F32_NUM_VARIANTS] = {0, 16, 0, 32, 4};
+
+thread_local char t_last_error[256] = "";
+
+int launch_status(hipError_t err, const char *what) {
+  if (err == hipSuccess) return GEMM_F32_OK;
+  std::snprintf(t_last_error, sizeof(t_last_error), "%s: %s (%s)", what,
+                hipGetErrorName(err), hipGetErrorString(err));
+  return GEMM_F32_LAUNCH_FAILED;
+}
+
+bool misaligned(const void *p) {
+  return (reinterpret_cast<std::uintptr_t>(p) & 3u) != 0;
+}
+
+int max1(int v) { return v > 1 ? v : 1; }
+
+int num_configs(int variant) {
+  if (variant < 0 || variant >= GEMM_F32_NUM_VARIANTS) return 0;
+  return variant == GEMM_F32_PROD ? prod_num_configs() : 1;
+}
+
+// Shape checks shared by the product and the tile query.
+int check_shape(int M, int N, int K) {
+  if (M < 0 || N < 0 || K < 0) return GEMM_F32_INVALID_DIM;
+  return GEMM_F32_OK;
+}
+
+int resolve_config(int variant, int config, int M, int N, int K, int *out) {
+  if (variant < 0 || variant >= GEMM_F32_NUM_VARIANTS)
+    return GEMM_F32_BAD_VARIANT;
+  if (config < -1 || config >= num_configs(variant)) return GEMM_F32_BAD_CONFIG;
+  if (config == -1)
+    config = variant == GEMM_F32_PROD ? prod_choose(M, N, K) : 0;
+  *out = config;
+  return GEMM_F32_OK;
+}
+
+int validate(int M, int N, int K, const float *A, int lda, const float *B,
+             int ldb, float *C, int ldc, int variant, int config,
+             int *chosen) {
+  int rc = check_shape(M, N, K);
+  if (rc != GEMM_F32_OK) return rc;
+  if (lda < max1(K) || ldb < max1(N) || ldc < max1(N))
+    return GEMM_F32_INVALID_LD;
+  rc = resolve_config(variant, config, M, N, K, chosen);
+  if (rc != GEMM_F32_OK) return rc;
+  if (M == 0 || N == 0) return GEMM_F32_OK;
+  if (C == nullptr) return GEMM_F32_NULL_PTR;
+  if (K > 0 && (A == nullptr || B == nullptr)) return GEMM_F32_NULL_PTR;
+  if (misaligned(C) || (K > 0 && (misaligned(A) || misaligned(B))))
+    return GEMM_F32_MISALIGNED;
+  return GEMM_F32_OK;
+}
+
+}  // namespace
+
+extern "C" int gemm_f32_ex(int M, int N, int K, const float *A, int lda,
+                           const float *B, int ldb, float *C, int ldc,
+                           int variant, int config, void *stream) {
+  int chosen = 0;
+  int rc = validate(M, N, K, A, lda, B, ldb, C, ldc, variant, config, &chosen);
+  if (rc != GEMM_F32_OK) return rc;
+  if (M == 0 || N == 0) return GEMM_F32_OK;
+
+  const Problem p{M, N, K, A, lda, B, ldb, C, ldc};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (K == 0) return launch_status(launch_zero(p, s), "zero fill");  // the empty sum
+  if (variant == GEMM_F32_NAIVE) return launch_status(launch_naive(p, s), "naive");
+  if (variant == GEMM_F32_PROD) return launch_status(launch_prod(chosen, p, s), "prod");
+  return launch_status(launch_tiled(kTiledT[variant], p, s), "tiled");
+}
+
+extern "C" int gemm_f32(int M, int N, int K, const float *A, int lda,
+                        const float *B, int ldb, float *C, int ldc,
+                        int variant, void *stream) {
+  return gemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, variant, -1, stream);
+}
+
+extern "C" int gemm_f32_num_configs(int variant) { return num_configs(variant); }
+
+extern "C" int gemm_f32_tile(int variant, int config, int M, int N, int K,
+                             int *BM, int *BN, int *BK, int *threads,
+                             int *chosen_config) {
+  int rc = check_shape(M, N, K);
+  if (rc != GEMM_F32_OK) return rc;
+  int chosen = 0;
+  rc = resolve_config(variant, config, M, N, K, &chosen);
+  if (rc != GEMM_F32_OK) return rc;
+  int bm, bn, bk, nt;
+  if (variant == GEMM_F32_NAIVE) {
+    bm = 4, bn = 64, bk = 1, nt = 256;
+  } else if (variant == GEMM_F32_PROD) {
+    const ProdConfig &c = prod_config(chosen);
+    bm = c.BM, bn = c.BN, bk = c.BK, nt = 64 * c.WGM * c.WGN;
+  } else {
+    const int t = kTiledT[variant];
+    bm = bn = bk = t, nt = t * t;
+  }
+  if (BM) *BM = bm;
+  if (BN) *BN = bn;
+  if (BK) *BK = bk;
+  if (threads) *threads = nt;
+  if (chosen_config) *chosen_config = chosen;
+  return GEMM_F32_OK;
+}
+
+extern "C" const char *gemm_f32_last_error(void) { return t_last_error; }
+
+extern "C" const char *gemm_f32_status_string(int status) {
+  switch (status) {
+    case GEMM_F32_OK: return "ok";
+    case GEMM_F32_INVALID_DIM: return "invalid dimension: M, N and K must be >= 0";
+    case GEMM_F32_INVALID_LD:
+      return "invalid leading dimension: need lda >= max(1,K), ldb >= max(1,N), ldc >= max(1,N)";
+    case GEMM_F32_NULL_PTR: return "null pointer for a non-empty matrix";
+    case GEMM_F32_BAD_VARIANT: return "unknown variant";
+    case GEMM_F32_LAUNCH_FAILED: return "kernel launch failed";
+    case GEMM_F32_MISALIGNED: return "pointer not aligned to its element size";
+    case GEMM_F32_BAD_CONFIG: return "launch-table index out of range";
+    case GEMM_F32_BAD_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+extern "C" const char *gemm_f32_version(void) { return "gemm_f32 0.1.0 gfx950"; }

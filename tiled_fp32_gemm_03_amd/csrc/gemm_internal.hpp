@@ -1,0 +1,42 @@
+// Internal declarations shared by the kernel translation units and the C-ABI
+// front end of the gemm_f32 library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace gemm_f32_impl {
+
+// One product C = A x B, row-major with leading dimensions (elements).
+struct Problem {
+  int M, N, K;
+  const float *A;
+  long long lda;
+  const float *B;
+  long long ldb;
+  float *C;
+  long long ldc;
+};
+
+// Launch-table entry of the production kernel.
+struct ProdConfig {
+  int BM, BN, BK;  // workgroup tile and k step
+  int WGM, WGN;    // waves along M and N (threads = 64 * WGM * WGN)
+  int occupancy;   // intended workgroups per CU (documentation, grid sizing)
+  const char *name;
+};
+
+// Largest grid.y the runtime accepts; kernels loop when a dimension exceeds it.
+constexpr int kMaxGridY = 65535;
+
+hipError_t launch_zero(const Problem &p, hipStream_t s);
+hipError_t launch_naive(const Problem &p, hipStream_t s);
+hipError_t launch_tiled(int T, const Problem &p, hipStream_t s);
+
+int prod_num_configs();
+const ProdConfig &prod_config(int index);
+int prod_choose(int M, int N, int K);
+hipError_t launch_prod(int index, const Problem &p, hipStream_t s);
+
+}  // namespace gemm_f32_impl

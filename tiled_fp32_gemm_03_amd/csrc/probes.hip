@@ -1,0 +1,141 @@
+// Measurement probes: HBM streaming passes (copy, fill and the pages' vector
+// add, mayulu.co "CUDA 编程系列之三", section 4) and an fp32 MFMA throughput
+// loop.  They give the roofline's measured denominators and a copy kernel of
+// known traffic for counter calibration; they are not part of C = A x B.
+#include "gemm_f32.h"
+#include "gemm_f32_probes.h"
+#include "launch_util.hpp"
+
+#include <cstdint>
+
+using namespace gemm_f32_impl;
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kStreamThreads = 256;
+
+template <int KIND>
+__global__ void __launch_bounds__(kStreamThreads)
+    stream_kernel(long long n4, const f32x4 *__restrict__ x,
+                  const f32x4 *__restrict__ y, f32x4 *__restrict__ z) {
+  const long long stride = (long long)gridDim.x * kStreamThreads;
+  for (long long i = (long long)blockIdx.x * kStreamThreads + threadIdx.x;
+       i < n4; i += stride) {
+    if constexpr (KIND == GEMM_F32_PROBE_COPY) {
+      z[i] = x[i];
+    } else if constexpr (KIND == GEMM_F32_PROBE_FILL) {
+      z[i] = f32x4{1.f, 1.f, 1.f, 1.f};
+    } else {
+      z[i] = x[i] + y[i];
+    }
+  }
+}
+
+// Tail (n % 4 elements) handled by one small scalar launch.
+template <int KIND>
+__global__ void stream_tail(long long start, long long n, const float *x,
+                            const float *y, float *z) {
+  const long long i = start + threadIdx.x;
+  if (i >= n) return;
+  if constexpr (KIND == GEMM_F32_PROBE_COPY) {
+    z[i] = x[i];
+  } else if constexpr (KIND == GEMM_F32_PROBE_FILL) {
+    z[i] = 1.f;
+  } else {
+    z[i] = x[i] + y[i];
+  }
+}
+
+constexpr int kMfmaChains = 8;
+constexpr int kMfmaThreads = 256;
+
+__global__ void __launch_bounds__(kMfmaThreads)
+    mfma_probe_kernel(int iters, float *out) {
+  const int lane = threadIdx.x & 63;
+  float a = 1.0f + lane * 1e-3f;
+  float b = 1.0f - lane * 1e-3f;
+  f32x16 acc[kMfmaChains];
+#pragma unroll
+  for (int c = 0; c < kMfmaChains; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[c][r] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < kMfmaChains; ++c)
+      acc[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc[c], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kMfmaChains; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[c][r];
+  if (lane == 0) out[blockIdx.x * (kMfmaThreads / 64) + (threadIdx.x >> 6)] = s;
+}
+
+bool misaligned16(const void *p) {
+  return (reinterpret_cast<std::uintptr_t>(p) & 15u) != 0;
+}
+
+template <int KIND>
+hipError_t launch_stream(long long n, const float *x, const float *y, float *z,
+                         hipStream_t s) {
+  const long long n4 = n / 4;
+  if (n4 > 0) {
+    long long blocks = ceil_div(n4, kStreamThreads);
+    const long long cap = 256LL * 64;  // 64 workgroups per CU, grid-stride beyond
+    if (blocks > cap) blocks = cap;
+    hipError_t e = launch_kernel(
+        stream_kernel<KIND>, dim3((unsigned)blocks), dim3(kStreamThreads), s, n4,
+        reinterpret_cast<const f32x4 *>(x), reinterpret_cast<const f32x4 *>(y),
+        reinterpret_cast<f32x4 *>(z));
+    if (e != hipSuccess) return e;
+  }
+  if (n % 4) {
+    return launch_kernel(stream_tail<KIND>, dim3(1), dim3(4), s, n4 * 4, n, x,
+                         y, z);
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" int gemm_f32_probe_stream(int kind, long long n, const float *x,
+                                     const float *y, float *z, void *stream) {
+  if (n < 0 || kind < GEMM_F32_PROBE_COPY || kind > GEMM_F32_PROBE_VADD)
+    return GEMM_F32_BAD_ARG;
+  if (n == 0) return GEMM_F32_OK;
+  if (z == nullptr) return GEMM_F32_NULL_PTR;
+  if (kind != GEMM_F32_PROBE_FILL && x == nullptr) return GEMM_F32_NULL_PTR;
+  if (kind == GEMM_F32_PROBE_VADD && y == nullptr) return GEMM_F32_NULL_PTR;
+  if (misaligned16(z) || (x && misaligned16(x)) || (y && misaligned16(y)))
+    return GEMM_F32_MISALIGNED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (kind) {
+    case GEMM_F32_PROBE_COPY: e = launch_stream<GEMM_F32_PROBE_COPY>(n, x, y, z, s); break;
+    case GEMM_F32_PROBE_FILL: e = launch_stream<GEMM_F32_PROBE_FILL>(n, x, y, z, s); break;
+    default: e = launch_stream<GEMM_F32_PROBE_VADD>(n, x, y, z, s); break;
+  }
+  return e == hipSuccess ? GEMM_F32_OK : GEMM_F32_LAUNCH_FAILED;
+}
+
+extern "C" long long gemm_f32_probe_mfma_flops(int workgroups, int iters) {
+  if (workgroups < 1 || iters < 1) return -1;
+  const long long per_mfma = 2LL * 32 * 32 * 2;
+  return (long long)workgroups * (kMfmaThreads / 64) * (long long)iters *
+         kMfmaChains * per_mfma;
+}
+
+extern "C" int gemm_f32_probe_mfma(int workgroups, int iters, float *out,
+                                   void *stream) {
+  if (workgroups < 1 || iters < 1) return GEMM_F32_BAD_ARG;
+  if (out == nullptr) return GEMM_F32_NULL_PTR;
+  if (reinterpret_cast<std::uintptr_t>(out) & 3u) return GEMM_F32_MISALIGNED;
+  hipError_t e = launch_kernel(mfma_probe_kernel, dim3(workgroups),
+                               dim3(kMfmaThreads), static_cast<hipStream_t>(stream),
+                               iters, out);
+  return e == hipSuccess ? GEMM_F32_OK : GEMM_F32_LAUNCH_FAILED;
+}

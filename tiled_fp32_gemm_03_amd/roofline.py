@@ -1,0 +1,52 @@
+"""Roofline bookkeeping for the benchmark: algorithmic work, the tiled load
+model per launch-table entry, and MI355X peak figures.
+
+Algorithmic work of C = A x B (beta = 0): 2*M*N*K FLOP; compulsory bytes
+4*(M*K + K*N + M*N) -- A and B read once, C written once and never read.
+Intensity is their ratio and the binding roof is the lower of the compute
+peak and intensity x bandwidth (mayulu.co "CUDA 编程系列之三", sections 2-3).
+
+Issued global loads of a workgroup-tiled kernel: every tile of C walks all
+k steps and loads a BM x BK block of A plus a BK x BN block of B per step;
+with ceilings for ragged edges that is (BM*BK + BK*BN) * ceil(K/BK) *
+ceil(M/BM) * ceil(N/BN) elements (the T x T case is geek-doc.cn "矩阵乘法
+tiling", section 三: 2N^3/T).  The naive kernel issues 2*M*N*K loads
+(csh0101.cc "CUDA 深入浅出（二）", naive section).
+"""
+from __future__ import annotations
+
+# MI355X published peaks (dense, no sparsity).
+PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_FP32_VALU_TFLOPS = 157.3
+PEAK_HBM_GBPS = 8000.0
+CUS = 256
+CLOCK_GHZ = 2.4
+
+
+def flops(M: int, N: int, K: int) -> int:
+    return 2 * M * N * K
+
+
+def compulsory_bytes(M: int, N: int, K: int) -> int:
+    return 4 * (M * K + K * N + M * N)
+
+
+def intensity(M: int, N: int, K: int) -> float:
+    b = compulsory_bytes(M, N, K)
+    return flops(M, N, K) / b if b else 0.0
+
+
+def _cdiv(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def issued_load_elements(variant: str, M: int, N: int, K: int, tile: dict) -> int:
+    """Model element loads for the launch-table entry ``tile`` (from gemm_f32_tile)."""
+    if variant == "naive":
+        return 2 * M * N * K
+    bm, bn, bk = tile["BM"], tile["BN"], tile["BK"]
+    return (bm * bk + bk * bn) * _cdiv(K, bk) * _cdiv(M, bm) * _cdiv(N, bn)
+
+
+def binding_roof_tflops(M: int, N: int, K: int, peak_tflops: float, bw_gbps: float) -> float:
+    return min(peak_tflops, intensity(M, N, K) * bw_gbps / 1000.0)
