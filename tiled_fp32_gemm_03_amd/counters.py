@@ -1,0 +1,200 @@
+"""Summaries of rocprofv3 output for the roofline report (measurement harness).
+
+Two subcommands, both reading CSV files that rocprofv3 wrote
+(``--output-format csv``); neither touches the GPU.
+
+  trace  --csv <..._kernel_trace.csv> --command "<profiled command>"
+         Per (kernel, grid, workgroup) launch counts and durations.  The
+         trace is used instead of rocprofv3's own stats file because one
+         template instance can serve several workloads with different grids.
+
+  pmc    --run <ladder.jsonl>:<..._counter_collection.csv> [--run ...]
+         --command "<command of run 1>" [--command ...]
+         [--traffic-out profiles/traffic.json]
+         Joins each counter run's dispatches of this library's kernels, in
+         order, with the ladder tool's records (one launch per record, no
+         warm-up), and reports the counters per kernel.  The streaming copy
+         probe that the ladder runs first (``--copy-mib``) moves a known
+         number of bytes each way; FETCH_SIZE and WRITE_SIZE are scaled by
+         known / counted on that probe to give HBM bytes per launch.  With
+         ``--traffic-out`` the production kernels' calibrated bytes are
+         written for the benchmark, stamped with a digest of the kernel
+         source so that a changed kernel reports no stale traffic.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+from collections import OrderedDict, defaultdict
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+PROD_SOURCE = os.path.join(HERE, "csrc", "prod.hip")
+OUR_KERNELS = re.compile(r"(gemm_f32_impl|prod_kernel|naive_kernel|tiled_kernel|stream_kernel|stream_tail|mfma_probe_kernel|zero_kernel)")
+
+
+def prod_source_digest() -> str:
+    with open(PROD_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def short_name(name: str) -> str:
+    s = name.replace("gemm_f32_impl::", "").replace("(anonymous namespace)::", "")
+    s = re.sub(r"\(.*\)$", "", s).replace("void ", "")
+    return s.strip()
+
+
+def cmd_trace(args) -> int:
+    groups: dict = OrderedDict()
+    for path in args.csv:
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                key = (short_name(row["Kernel_Name"]), int(row["Grid_Size_X"]),
+                       int(row["Workgroup_Size_X"]) * int(row["Workgroup_Size_Y"]) * int(row["Workgroup_Size_Z"]))
+                dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1000.0
+                groups.setdefault(key, []).append(dur)
+    lines = [f"# {args.title}", "", "Command:", "", "```", *args.command, "```", "",
+             "| kernel | workgroups | threads/WG | calls | avg us | min us | max us |",
+             "|---|---|---|---|---|---|---|"]
+    for (name, grid, wg), durs in groups.items():
+        if args.only_ours and not OUR_KERNELS.search(name):
+            continue
+        lines.append(f"| `{name}` | {grid // wg} | {wg} | {len(durs)} | {statistics.mean(durs):.1f} "
+                     f"| {min(durs):.1f} | {max(durs):.1f} |")
+    text = "\n".join(lines) + "\n"
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    print(text)
+    return 0
+
+
+def _read_counter_csv(path: str):
+    """Dispatches of this library's kernels, in dispatch order: list of
+    (kernel short name, grid threads, {counter: value})."""
+    by_dispatch: dict = OrderedDict()
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            name = row["Kernel_Name"]
+            if not OUR_KERNELS.search(name):
+                continue
+            did = int(row["Dispatch_Id"])
+            ent = by_dispatch.setdefault(did, {"name": short_name(name), "grid": int(row["Grid_Size"]),
+                                               "counters": defaultdict(float)})
+            ent["counters"][row["Counter_Name"]] += float(row["Counter_Value"])
+    return [by_dispatch[k] for k in sorted(by_dispatch)]
+
+
+def _read_ladder(path: str):
+    recs = []
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("{"):
+                recs.append(json.loads(line))
+    return recs
+
+
+def cmd_pmc(args) -> int:
+    joined = []  # per record: merged counters over runs
+    for run in args.run:
+        jl, cs = run.split(":", 1)
+        recs = _read_ladder(jl)
+        disp = _read_counter_csv(cs)
+        if len(recs) != len(disp):
+            raise SystemExit(f"{run}: {len(recs)} ladder records but {len(disp)} dispatches")
+        for i, (r, d) in enumerate(zip(recs, disp)):
+            if i >= len(joined):
+                joined.append({"rec": r, "name": d["name"], "grid": d["grid"], "counters": {}})
+            elif joined[i]["rec"].get("kernel") != r.get("kernel"):
+                raise SystemExit(f"{run}: record {i} is {r.get('kernel')} in one run and "
+                                 f"{joined[i]['rec'].get('kernel')} in another")
+            joined[i]["counters"].update(d["counters"])
+
+    cal = {}
+    for j in joined:
+        if j["rec"].get("kernel") == "probe_copy":
+            kib = j["rec"]["bytes_read"] / 1024.0
+            for cname in ("FETCH_SIZE", "WRITE_SIZE"):
+                if cname in j["counters"] and j["counters"][cname] > 0:
+                    cal[cname] = kib / j["counters"][cname]
+
+    counters = sorted({c for j in joined for c in j["counters"]})
+    lines = [f"# {args.title}", "", "Commands:", "", "```", *args.command, "```", ""]
+    if cal:
+        lines += ["Calibration on the streaming copy probe (known bytes / counted bytes): " +
+                  ", ".join(f"{k} x{v:.4f}" for k, v in cal.items()), ""]
+    hdr = ["workload", "kernel", *counters]
+    if "FETCH_SIZE" in counters:
+        hdr.append("HBM read MB (cal.)")
+    if "WRITE_SIZE" in counters:
+        hdr.append("HBM write MB (cal.)")
+    hdr.append("model issued-load MB")
+    lines += ["| " + " | ".join(hdr) + " |", "|" + "---|" * len(hdr)]
+    traffic = {}
+    for j in joined:
+        r, c = j["rec"], j["counters"]
+        row = [r.get("workload", "-"), r.get("kernel", j["name"])]
+        row += [f"{c[k]:.6g}" if k in c else "-" for k in counters]
+        rd = c.get("FETCH_SIZE", 0.0) * 1024 * cal.get("FETCH_SIZE", 1.0)
+        wr = c.get("WRITE_SIZE", 0.0) * 1024 * cal.get("WRITE_SIZE", 1.0)
+        if "FETCH_SIZE" in counters:
+            row.append(f"{rd / 1e6:.1f}")
+        if "WRITE_SIZE" in counters:
+            row.append(f"{wr / 1e6:.1f}")
+        row.append(f"{r['model_issued_load_bytes'] / 1e6:.1f}" if "model_issued_load_bytes" in r else "-")
+        lines.append("| " + " | ".join(row) + " |")
+        if (r.get("variant") == "prod" and "FETCH_SIZE" in c and "WRITE_SIZE" in c
+                and "FETCH_SIZE" in cal and "WRITE_SIZE" in cal):
+            traffic[r["workload"]] = {
+                "config": r["kernel"], "prod_source_sha256_16": prod_source_digest(),
+                "fetch_kib_counted": c["FETCH_SIZE"], "write_kib_counted": c["WRITE_SIZE"],
+                "fetch_scale": cal["FETCH_SIZE"], "write_scale": cal["WRITE_SIZE"],
+                "hbm_read_bytes": round(rd), "hbm_write_bytes": round(wr),
+                "hbm_bytes_per_launch": round(rd + wr)}
+    text = "\n".join(lines) + "\n"
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    print(text)
+    if args.traffic_out and traffic:
+        old = {}
+        if os.path.exists(args.traffic_out):
+            with open(args.traffic_out) as f:
+                old = json.load(f)
+        old.update(traffic)
+        old["_about"] = ("HBM bytes per launch of the production kernel: rocprofv3 FETCH_SIZE and "
+                         "WRITE_SIZE (KiB per dispatch) scaled by the streaming copy probe's "
+                         "known/counted ratio; commands in the matching profiles/*.md summary.")
+        with open(args.traffic_out, "w") as f:
+            json.dump(old, f, indent=1, sort_keys=True)
+            f.write("\n")
+    return 0
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("--csv", action="append", required=True)
+    t.add_argument("--command", action="append", default=[])
+    t.add_argument("--title", default="rocprofv3 kernel trace")
+    t.add_argument("--out")
+    t.add_argument("--only-ours", action="store_true")
+    p = sub.add_parser("pmc")
+    p.add_argument("--run", action="append", required=True, help="LADDER_JSONL:COUNTER_CSV")
+    p.add_argument("--command", action="append", default=[])
+    p.add_argument("--title", default="rocprofv3 counters")
+    p.add_argument("--out")
+    p.add_argument("--traffic-out")
+    args = ap.parse_args(argv)
+    return cmd_trace(args) if args.cmd == "trace" else cmd_pmc(args)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -9,14 +9,15 @@
 // and 五).  On CDNA4 the instruction block is the fp32 matrix-core op
 // v_mfma_f32_32x32x2_f32.
 //
-// Per workgroup: a BM x BN tile of C, WGM x WGN waves, each wave a
+// Per workgroup: BM x BN tiles of C, WGM x WGN waves, each wave a
 // (BM/WGM) x (BN/WGN) sub-tile made of 32 x 32 MFMA blocks whose
-// accumulators stay in registers for the whole k loop.
+// accumulators stay in registers for the whole k loop of a tile.
 //
 // Data path per k step (depth BK):
-//   global -> registers: the next step's A and B tiles, 128-bit loads where
-//     rows are 16-byte aligned (scalar loads otherwise), consecutive lanes on
-//     consecutive addresses;
+//   global -> registers: the next step's A and B tiles as 128-bit loads,
+//     consecutive lanes on consecutive addresses.  Rows only need 4-byte
+//     alignment (CDNA accepts dword-aligned multi-dword accesses), so odd
+//     leading dimensions take the same path;
 //   registers -> LDS: into the stage not being read (two stages), rows padded
 //     so that the fragment reads below do not collide in LDS banks;
 //   LDS -> MFMA: per 8-deep k group a lane reads one 128-bit A fragment per
@@ -25,6 +26,11 @@
 //   only after the barrier that follows its last read.  (The pages' single
 //   buffer needs its two barriers per step; the two-stage form here is a
 //   departure from them.)
+//
+// Persistent schedule.  The grid holds at most as many workgroups as fit on
+// the chip at once; each walks its tiles' k steps as one flat sequence, so
+// the loads of the next tile's first step are in flight while the current
+// tile finishes, and its C stores drain while the next tile computes.
 //
 // Operand roles.  An MFMA lane supplies one element of each operand: lane l
 // gives row l%32 of the first operand and column l%32 of the second at k
@@ -39,8 +45,9 @@
 //
 // Edges.  Steps and tiles that overhang K, M or N use guarded loads that
 // write 0 for elements outside the matrices (geek-doc.cn section 六; mayulu.co
-// section 7), and guarded stores that leave C outside M x N untouched.
-// Interior steps take unguarded loads.
+// section 7), per element where a 4-wide chunk straddles an edge, and
+// guarded stores that leave C outside M x N untouched.  Interior steps take
+// unguarded loads.
 //
 // Workgroup order.  Workgroups are dealt to the 8 XCDs round robin by
 // launch index; the index is remapped so that each XCD receives a contiguous
@@ -49,12 +56,14 @@
 #include "gemm_internal.hpp"
 #include "launch_util.hpp"
 
+#include <atomic>
 #include <cstdint>
 
 namespace gemm_f32_impl {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kPadA = 4;  // floats after each LDS row of A (k-contiguous rows)
@@ -62,9 +71,10 @@ constexpr int kPadB = 8;  // floats after each LDS row of B (n-contiguous rows)
 constexpr int kXcds = 8;
 constexpr int kGroupRows = 8;
 
-template <int BM_, int BN_, int BK_, int WGM_, int WGN_>
+template <int BM_, int BN_, int BK_, int WGM_, int WGN_, bool NT_STORE_>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_;
+  static constexpr bool NT_STORE = NT_STORE_;
   static constexpr int NT = 64 * WGM * WGN;
   static constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave sub-tile
   static constexpr int TM = WTM / 32, TN = WTN / 32;    // MFMA blocks per wave
@@ -73,32 +83,29 @@ struct Tile {
   static constexpr int A_STAGE = BM * SA;
   static constexpr int B_STAGE = BK * SB;
   static constexpr int LDS_FLOATS = 2 * (A_STAGE + B_STAGE);
-  // vector (128-bit) staging: chunks of 4 floats
-  static constexpr int A_CHUNKS = BM * BK / 4 / NT;  // per thread
+  static constexpr int A_CHUNKS = BM * BK / 4 / NT;  // 4-float chunks per thread
   static constexpr int B_CHUNKS = BK * BN / 4 / NT;
   static constexpr int A_ROWS_PER_PASS = NT / (BK / 4);
   static constexpr int B_ROWS_PER_PASS = NT / (BN / 4);
-  // scalar staging
-  static constexpr int A_ELEMS = BM * BK / NT;
-  static constexpr int B_ELEMS = BK * BN / NT;
-  static constexpr int A_ROWS_PER_PASS_S = NT / BK;
-  static constexpr int B_ROWS_PER_PASS_S = NT / BN;
 
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be 32-aligned");
   static_assert(BK % 8 == 0, "BK must be a multiple of 8");
-  static_assert(NT % (BK / 4) == 0 && NT % (BN / 4) == 0, "vector staging map");
-  static_assert(NT % BK == 0 && NT % BN == 0, "scalar staging map");
+  static_assert(NT % (BK / 4) == 0 && NT % (BN / 4) == 0, "staging map");
   static_assert((BM * BK) % (4 * NT) == 0 && (BK * BN) % (4 * NT) == 0,
                 "tile must split evenly over threads");
   static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS budget of a gfx950 CU");
 };
 
-// Remap the launch index so each XCD gets a contiguous run of tile ids,
-// then walk tiles in groups of kGroupRows tile rows, column by column.
-__device__ inline void tile_of(int b, int G, int tiles_m, int tiles_n, int &tm,
-                               int &tn) {
+// Launch index -> logical id: each XCD gets a contiguous run of ids.
+__device__ inline int xcd_remap(int b, int G) {
   const int per = G / kXcds, rem = G % kXcds, x = b % kXcds;
-  const int lid = x * per + (x < rem ? x : rem) + b / kXcds;
+  return x * per + (x < rem ? x : rem) + b / kXcds;
+}
+
+// Tile id -> (tile row, tile column), in groups of kGroupRows tile rows
+// walked column by column.
+__device__ inline void tile_coords(int lid, int tiles_m, int tiles_n, int &tm,
+                                   int &tn) {
   const int per_group = kGroupRows * tiles_n;
   const int g = lid / per_group;
   const int first = g * kGroupRows;
@@ -108,83 +115,64 @@ __device__ inline void tile_of(int b, int G, int tiles_m, int tiles_n, int &tm,
   tn = r / rows;
 }
 
-template <class S, bool VEC>
+template <class S>
 struct Stage {
   // registers holding one k step of A and B on their way to LDS
-  f32x4 a[VEC ? S::A_CHUNKS : S::A_ELEMS / 4];
-  f32x4 b[VEC ? S::B_CHUNKS : S::B_ELEMS / 4];
+  f32x4 a[S::A_CHUNKS];
+  f32x4 b[S::B_CHUNKS];
 };
 
-template <class S, bool VEC, bool GUARD>
-__device__ inline void load_global(Stage<S, VEC> &st, const Problem &p, int m0,
+__device__ inline f32x4 load4(const float *src) {
+  return *reinterpret_cast<const f32x4u *>(src);
+}
+
+// Four elements src[0..3] with those at index >= valid read as 0.
+__device__ inline f32x4 load_partial(const float *src, int valid) {
+  f32x4 v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (e < valid) v[e] = src[e];
+  return v;
+}
+
+template <class S, bool GUARD>
+__device__ inline void load_global(Stage<S> &st, const Problem &p, int m0,
                                    int n0, int k0, int tid) {
-  if constexpr (VEC) {
-    const int arow = tid / (S::BK / 4), akq = (tid % (S::BK / 4)) * 4;
+  const int arow = tid / (S::BK / 4), akq = (tid % (S::BK / 4)) * 4;
 #pragma unroll
-    for (int i = 0; i < S::A_CHUNKS; ++i) {
-      const int gm = m0 + arow + i * S::A_ROWS_PER_PASS;
-      const int gk = k0 + akq;
-      const float *src = p.A + (long long)gm * p.lda + gk;
-      if (!GUARD || (gm < p.M && gk < p.K))
-        st.a[i] = *reinterpret_cast<const f32x4 *>(src);
-      else
-        st.a[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    const int bkr = tid / (S::BN / 4), bnq = (tid % (S::BN / 4)) * 4;
+  for (int i = 0; i < S::A_CHUNKS; ++i) {
+    const int gm = m0 + arow + i * S::A_ROWS_PER_PASS;
+    const int gk = k0 + akq;
+    const float *src = p.A + (long long)gm * p.lda + gk;
+    if (!GUARD || (gm < p.M && gk + 4 <= p.K))
+      st.a[i] = load4(src);
+    else
+      st.a[i] = load_partial(src, gm < p.M ? p.K - gk : 0);
+  }
+  const int bkr = tid / (S::BN / 4), bnq = (tid % (S::BN / 4)) * 4;
 #pragma unroll
-    for (int i = 0; i < S::B_CHUNKS; ++i) {
-      const int gk = k0 + bkr + i * S::B_ROWS_PER_PASS;
-      const int gn = n0 + bnq;
-      const float *src = p.B + (long long)gk * p.ldb + gn;
-      if (!GUARD || (gk < p.K && gn < p.N))
-        st.b[i] = *reinterpret_cast<const f32x4 *>(src);
-      else
-        st.b[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  } else {
-    const int arow = tid / S::BK, ak = tid % S::BK;
-#pragma unroll
-    for (int i = 0; i < S::A_ELEMS; ++i) {
-      const int gm = m0 + arow + i * S::A_ROWS_PER_PASS_S;
-      const int gk = k0 + ak;
-      float v = 0.f;
-      if (!GUARD || (gm < p.M && gk < p.K)) v = p.A[(long long)gm * p.lda + gk];
-      st.a[i / 4][i % 4] = v;
-    }
-    const int bkr = tid / S::BN, bn = tid % S::BN;
-#pragma unroll
-    for (int i = 0; i < S::B_ELEMS; ++i) {
-      const int gk = k0 + bkr + i * S::B_ROWS_PER_PASS_S;
-      const int gn = n0 + bn;
-      float v = 0.f;
-      if (!GUARD || (gk < p.K && gn < p.N)) v = p.B[(long long)gk * p.ldb + gn];
-      st.b[i / 4][i % 4] = v;
-    }
+  for (int i = 0; i < S::B_CHUNKS; ++i) {
+    const int gk = k0 + bkr + i * S::B_ROWS_PER_PASS;
+    const int gn = n0 + bnq;
+    const float *src = p.B + (long long)gk * p.ldb + gn;
+    if (!GUARD || (gk < p.K && gn + 4 <= p.N))
+      st.b[i] = load4(src);
+    else
+      st.b[i] = load_partial(src, gk < p.K ? p.N - gn : 0);
   }
 }
 
-template <class S, bool VEC>
-__device__ inline void store_lds(const Stage<S, VEC> &st, float *as, float *bs,
+template <class S>
+__device__ inline void store_lds(const Stage<S> &st, float *as, float *bs,
                                  int tid) {
-  if constexpr (VEC) {
-    const int arow = tid / (S::BK / 4), akq = (tid % (S::BK / 4)) * 4;
+  const int arow = tid / (S::BK / 4), akq = (tid % (S::BK / 4)) * 4;
 #pragma unroll
-    for (int i = 0; i < S::A_CHUNKS; ++i)
-      *reinterpret_cast<f32x4 *>(as + (arow + i * S::A_ROWS_PER_PASS) * S::SA + akq) = st.a[i];
-    const int bkr = tid / (S::BN / 4), bnq = (tid % (S::BN / 4)) * 4;
+  for (int i = 0; i < S::A_CHUNKS; ++i)
+    *reinterpret_cast<f32x4 *>(as + (arow + i * S::A_ROWS_PER_PASS) * S::SA + akq) = st.a[i];
+  const int bkr = tid / (S::BN / 4), bnq = (tid % (S::BN / 4)) * 4;
 #pragma unroll
-    for (int i = 0; i < S::B_CHUNKS; ++i)
-      *reinterpret_cast<f32x4 *>(bs + (bkr + i * S::B_ROWS_PER_PASS) * S::SB + bnq) = st.b[i];
-  } else {
-    const int arow = tid / S::BK, ak = tid % S::BK;
-#pragma unroll
-    for (int i = 0; i < S::A_ELEMS; ++i)
-      as[(arow + i * S::A_ROWS_PER_PASS_S) * S::SA + ak] = st.a[i / 4][i % 4];
-    const int bkr = tid / S::BN, bn = tid % S::BN;
-#pragma unroll
-    for (int i = 0; i < S::B_ELEMS; ++i)
-      bs[(bkr + i * S::B_ROWS_PER_PASS_S) * S::SB + bn] = st.b[i / 4][i % 4];
-  }
+  for (int i = 0; i < S::B_CHUNKS; ++i)
+    *reinterpret_cast<f32x4 *>(bs + (bkr + i * S::B_ROWS_PER_PASS) * S::SB + bnq) = st.b[i];
 }
 
 // All MFMAs of one k step out of one LDS stage.
@@ -218,10 +206,18 @@ __device__ inline void compute_stage(f32x16 (&acc)[S::TM][S::TN],
   }
 }
 
-template <class S, bool VEC_C>
+template <bool NT>
+__device__ inline void store4(float *dst, const f32x4 &v) {
+  if constexpr (NT)
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4u *>(dst));
+  else
+    *reinterpret_cast<f32x4u *>(dst) = v;
+}
+
+template <class S>
 __device__ inline void store_c(const f32x16 (&acc)[S::TM][S::TN],
                                const Problem &p, int m0, int n0, int wm,
-                               int wn, int lane) {
+                               int wn, int lane, bool guard) {
   const int l32 = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int tm = 0; tm < S::TM; ++tm) {
@@ -234,22 +230,38 @@ __device__ inline void store_c(const f32x16 (&acc)[S::TM][S::TN],
         const int col = n0 + wn * S::WTN + tn * 32 + 8 * q + 4 * h;
         const f32x4 v{acc[tm][tn][4 * q + 0], acc[tm][tn][4 * q + 1],
                       acc[tm][tn][4 * q + 2], acc[tm][tn][4 * q + 3]};
-        if constexpr (VEC_C) {
-          // N % 4 == 0: a 4-column run is wholly inside or outside C.
-          if (row < p.M && col < p.N) *reinterpret_cast<f32x4 *>(crow + col) = v;
-        } else {
-          if (row < p.M) {
+        if (!guard || (row < p.M && col + 4 <= p.N)) {
+          store4<S::NT_STORE>(crow + col, v);
+        } else if (row < p.M) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (col + r < p.N) crow[col + r] = v[r];
-          }
+          for (int r = 0; r < 4; ++r)
+            if (col + r < p.N) crow[col + r] = v[r];
         }
       }
     }
   }
 }
 
-template <class S, bool VEC_AB, bool VEC_C>
+template <class S>
+__device__ inline void tile_origin(int t, int tiles_m, int tiles_n, int &m0,
+                                   int &n0, bool &interior, const Problem &p) {
+  int tm, tn;
+  tile_coords(t, tiles_m, tiles_n, tm, tn);
+  m0 = tm * S::BM;
+  n0 = tn * S::BN;
+  interior = (m0 + S::BM <= p.M) && (n0 + S::BN <= p.N);
+}
+
+template <class S>
+__device__ inline void load_step(Stage<S> &st, const Problem &p, int m0,
+                                 int n0, int k0, bool interior, int tid) {
+  if (interior && k0 + S::BK <= p.K)
+    load_global<S, false>(st, p, m0, n0, k0, tid);
+  else
+    load_global<S, true>(st, p, m0, n0, k0, tid);
+}
+
+template <class S>
 __global__ void __launch_bounds__(S::NT)
     prod_kernel(Problem p, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(16))) float lds[S::LDS_FLOATS];
@@ -261,69 +273,117 @@ __global__ void __launch_bounds__(S::NT)
   const int wm = wave / S::WGN, wn = wave % S::WGN;
   const int ntiles = tiles_m * tiles_n;
   const int nk = (p.K + S::BK - 1) / S::BK;
+  const int G = gridDim.x;
+  const int lid = xcd_remap(blockIdx.x, G);
+  if (lid >= ntiles) return;  // uniform per workgroup
+  // This workgroup's tiles are lid, lid + G, lid + 2G, ...
+  const int my_tiles = (ntiles - lid + G - 1) / G;
+  const long long steps = (long long)my_tiles * nk;
 
-  for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    int tm, tn;
-    tile_of(t, ntiles, tiles_m, tiles_n, tm, tn);
-    const int m0 = tm * S::BM, n0 = tn * S::BN;
-    const bool interior = (m0 + S::BM <= p.M) && (n0 + S::BN <= p.N);
+  int t = lid, kt = 0;
+  int m0, n0;
+  bool interior;
+  tile_origin<S>(t, tiles_m, tiles_n, m0, n0, interior, p);
 
-    f32x16 acc[S::TM][S::TN];
+  f32x16 acc[S::TM][S::TN];
 #pragma unroll
-    for (int i = 0; i < S::TM; ++i)
+  for (int i = 0; i < S::TM; ++i)
 #pragma unroll
-      for (int j = 0; j < S::TN; ++j)
+    for (int j = 0; j < S::TN; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    Stage<S, VEC_AB> st;
-    if (interior && S::BK <= p.K)
-      load_global<S, VEC_AB, false>(st, p, m0, n0, 0, tid);
-    else
-      load_global<S, VEC_AB, true>(st, p, m0, n0, 0, tid);
-    store_lds<S, VEC_AB>(st, as0, bs0, tid);
-    __syncthreads();
+  Stage<S> st;
+  load_step<S>(st, p, m0, n0, 0, interior, tid);
+  store_lds<S>(st, as0, bs0, tid);
+  __syncthreads();
 
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      const bool more = kt + 1 < nk;
-      if (more) {
-        const int k1 = (kt + 1) * S::BK;
-        if (interior && k1 + S::BK <= p.K)
-          load_global<S, VEC_AB, false>(st, p, m0, n0, k1, tid);
-        else
-          load_global<S, VEC_AB, true>(st, p, m0, n0, k1, tid);
-      }
-      compute_stage<S>(acc, as0 + cur * S::A_STAGE, bs0 + cur * S::B_STAGE, wm,
-                       wn, lane);
-      if (more)
-        store_lds<S, VEC_AB>(st, as0 + (cur ^ 1) * S::A_STAGE,
-                             bs0 + (cur ^ 1) * S::B_STAGE, tid);
-      __syncthreads();
+  for (long long it = 0; it < steps; ++it) {
+    const int cur = (int)(it & 1);
+    const bool more = it + 1 < steps;
+    // Coordinates of the next step in this workgroup's flat sequence.
+    int nt = t, nkt = kt + 1;
+    int nm0 = m0, nn0 = n0;
+    bool ninterior = interior;
+    if (nkt == nk) {
+      nkt = 0;
+      nt = t + G;
+      if (more) tile_origin<S>(nt, tiles_m, tiles_n, nm0, nn0, ninterior, p);
     }
-    store_c<S, VEC_C>(acc, p, m0, n0, wm, wn, lane);
+    if (more) load_step<S>(st, p, nm0, nn0, nkt * S::BK, ninterior, tid);
+
+    compute_stage<S>(acc, as0 + cur * S::A_STAGE, bs0 + cur * S::B_STAGE, wm,
+                     wn, lane);
+
+    if (kt == nk - 1) {
+      // Tile done: stores drain while the next tile computes.
+      store_c<S>(acc, p, m0, n0, wm, wn, lane, !interior);
+#pragma unroll
+      for (int i = 0; i < S::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < S::TN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    }
+    if (more)
+      store_lds<S>(st, as0 + (cur ^ 1) * S::A_STAGE,
+                   bs0 + (cur ^ 1) * S::B_STAGE, tid);
+    __syncthreads();
+    t = nt;
+    kt = nkt;
+    m0 = nm0;
+    n0 = nn0;
+    interior = ninterior;
   }
 }
 
 // ---- launch table ----------------------------------------------------
 
-using T128x128x32 = Tile<128, 128, 32, 2, 2>;
-using T128x128x16 = Tile<128, 128, 16, 2, 2>;
-using T256x128x16 = Tile<256, 128, 16, 4, 2>;
-using T64x64x32 = Tile<64, 64, 32, 2, 2>;
-using T128x64x32 = Tile<128, 64, 32, 2, 2>;
+using C0 = Tile<128, 128, 32, 2, 2, false>;
+using C1 = Tile<128, 128, 16, 2, 2, false>;
+using C2 = Tile<256, 128, 16, 4, 2, false>;
+using C3 = Tile<64, 64, 32, 2, 2, false>;
+using C4 = Tile<128, 64, 32, 2, 2, false>;
+using C5 = Tile<128, 128, 32, 2, 2, true>;
+using C6 = Tile<128, 128, 16, 2, 2, true>;
+using C7 = Tile<256, 128, 32, 4, 2, false>;
 
 const ProdConfig kConfigs[] = {
     {128, 128, 32, 2, 2, 2, "128x128x32_w2x2"},
-    {128, 128, 16, 2, 2, 4, "128x128x16_w2x2"},
+    {128, 128, 16, 2, 2, 3, "128x128x16_w2x2"},
     {256, 128, 16, 4, 2, 2, "256x128x16_w4x2"},
     {64, 64, 32, 2, 2, 4, "64x64x32_w2x2"},
-    {128, 64, 32, 2, 2, 4, "128x64x32_w2x2"},
+    {128, 64, 32, 2, 2, 2, "128x64x32_w2x2"},
+    {128, 128, 32, 2, 2, 2, "128x128x32_w2x2_nt"},
+    {128, 128, 16, 2, 2, 3, "128x128x16_w2x2_nt"},
+    {256, 128, 32, 4, 2, 1, "256x128x32_w4x2"},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
-bool aligned16(const void *q) {
-  return (reinterpret_cast<std::uintptr_t>(q) & 15u) == 0;
+// Workgroups of kernel `k` resident on the whole device at once (cached per
+// kernel and device; computed on first use).
+constexpr int kMaxDevices = 64;
+
+template <class S>
+int resident_workgroups() {
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
+  if (dev >= 0) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prod_kernel<S>, S::NT, 0) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) !=
+          hipSuccess ||
+      cus < 1)
+    cus = 1;
+  const int total = per_cu * cus;
+  if (dev >= 0) cache[dev].store(total, std::memory_order_relaxed);
+  return total;
 }
 
 template <class S>
@@ -331,18 +391,10 @@ hipError_t launch_shape(const Problem &p, hipStream_t s) {
   const long long tiles_m = ceil_div(p.M, S::BM), tiles_n = ceil_div(p.N, S::BN);
   const long long ntiles = tiles_m * tiles_n;
   if (ntiles > 0x7fffffffLL) return hipErrorInvalidValue;
-  const bool vec_ab = p.K % 4 == 0 && p.N % 4 == 0 && p.lda % 4 == 0 &&
-                      p.ldb % 4 == 0 && aligned16(p.A) && aligned16(p.B);
-  const bool vec_c = p.N % 4 == 0 && p.ldc % 4 == 0 && aligned16(p.C);
-  const dim3 grid((unsigned)ntiles), block(S::NT);
-  const int tm = (int)tiles_m, tn = (int)tiles_n;
-  if (vec_ab && vec_c)
-    return launch_kernel(prod_kernel<S, true, true>, grid, block, s, p, tm, tn);
-  if (vec_ab)
-    return launch_kernel(prod_kernel<S, true, false>, grid, block, s, p, tm, tn);
-  if (vec_c)
-    return launch_kernel(prod_kernel<S, false, true>, grid, block, s, p, tm, tn);
-  return launch_kernel(prod_kernel<S, false, false>, grid, block, s, p, tm, tn);
+  long long grid = resident_workgroups<S>();
+  if (grid > ntiles) grid = ntiles;
+  return launch_kernel(prod_kernel<S>, dim3((unsigned)grid), dim3(S::NT), s, p,
+                       (int)tiles_m, (int)tiles_n);
 }
 
 }  // namespace
@@ -351,23 +403,27 @@ int prod_num_configs() { return kNumConfigs; }
 
 const ProdConfig &prod_config(int index) { return kConfigs[index]; }
 
-// Shape-based choice: the largest tile that still gives every CU work.
+// Shape-based choice from measurements on MI355X (square 4096: 256x128x16;
+// smaller squares: 64x64 tiles to give every CU work; skinny K: 128x128x16).
 int prod_choose(int M, int N, int K) {
-  (void)K;
-  const long long t128 = ceil_div(M, 128) * ceil_div(N, 128);
-  if (t128 >= 512) return 0;
-  const long long t64 = ceil_div(M, 128) * ceil_div(N, 64);
-  if (t64 >= 256) return 4;
+  const long long t256x128 = ceil_div(M, 256) * ceil_div(N, 128);
+  const long long t64 = ceil_div(M, 64) * ceil_div(N, 64);
+  if (K <= 128 && t256x128 >= 1024) return 1;
+  if (t256x128 >= 512) return 2;
+  if (t64 >= 2048) return 4;
   return 3;
 }
 
 hipError_t launch_prod(int index, const Problem &p, hipStream_t s) {
   switch (index) {
-    case 0: return launch_shape<T128x128x32>(p, s);
-    case 1: return launch_shape<T128x128x16>(p, s);
-    case 2: return launch_shape<T256x128x16>(p, s);
-    case 3: return launch_shape<T64x64x32>(p, s);
-    case 4: return launch_shape<T128x64x32>(p, s);
+    case 0: return launch_shape<C0>(p, s);
+    case 1: return launch_shape<C1>(p, s);
+    case 2: return launch_shape<C2>(p, s);
+    case 3: return launch_shape<C3>(p, s);
+    case 4: return launch_shape<C4>(p, s);
+    case 5: return launch_shape<C5>(p, s);
+    case 6: return launch_shape<C6>(p, s);
+    case 7: return launch_shape<C7>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

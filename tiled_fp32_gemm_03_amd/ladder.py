@@ -1,0 +1,134 @@
+"""Time the kernel ladder on the named workloads (measurement harness).
+
+    python -m tiled_fp32_gemm_03_amd.ladder --workloads square_4096 \
+        --variants naive,tiled,tiled32,prod --reps 10
+
+``--variants`` takes rung names (naive, tiled, tiled32, tiled4, prod) and,
+for the production rung, ``prod:<i>`` for launch-table entry i or
+``prod:all`` for every entry.  ``--copy-mib N`` first runs the streaming copy
+probe once over N MiB (a kernel of known traffic: N MiB read, N MiB written)
+so that memory counters collected over the same run can be calibrated.
+
+Each measurement prints one JSON line (kernel, ms per launch from HIP events
+on the launch stream, TFLOP/s, compulsory-byte GB/s, the tiled load model);
+a markdown table goes to stderr at the end.  Inputs come from the seeded
+generator and are resident on the GPU before timing.  This tool does not
+check results; the test suite does.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def _expand_variants(spec: str, g) -> list[tuple[str, int]]:
+    out = []
+    for item in spec.split(","):
+        item = item.strip()
+        if not item:
+            continue
+        if ":" in item:
+            name, cfg = item.split(":", 1)
+            if cfg == "all":
+                out += [(name, i) for i in range(g.gemm_f32_num_configs(name))]
+            else:
+                out.append((name, int(cfg)))
+        else:
+            out.append((item, -1))
+    return out
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--workloads", default="square_256,square_1024_int,square_4096,ragged,skinny_k64")
+    ap.add_argument("--variants", default="naive,tiled,tiled32,prod")
+    ap.add_argument("--reps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--copy-mib", type=int, default=0)
+    ap.add_argument("--max-naive-gflop", type=float, default=200.0,
+                    help="skip the naive rung on workloads above this many GFLOP")
+    args = ap.parse_args(argv)
+
+    import torch
+
+    import tiled_fp32_gemm_03_amd as g
+    from gemm_inputs import make_workload
+    from tiled_fp32_gemm_03_amd import roofline as rf
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    s = stream.cuda_stream
+
+    def timed(fn, reps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(reps):
+            fn()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / max(reps, 1)
+
+    if args.copy_mib > 0:
+        n = args.copy_mib * (1 << 20) // 4
+        x = torch.ones(n, device=dev)
+        z = torch.empty(n, device=dev)
+        torch.cuda.synchronize()
+        print(f"[ladder] copy probe over {args.copy_mib} MiB", file=sys.stderr, flush=True)
+        ms = timed(lambda: g.gemm_f32_probe_stream(g.PROBE_COPY, n, x.data_ptr(), 0, z.data_ptr(), s), 1, 0)
+        print(json.dumps({"kernel": "probe_copy", "bytes_read": n * 4, "bytes_written": n * 4,
+                          "ms": round(ms, 5)}), flush=True)
+        del x, z
+        torch.cuda.empty_cache()
+
+    rows = []
+    for wname in [w for w in args.workloads.split(",") if w]:
+        w, a, b = make_workload(wname)
+        ta, tb = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+        tc = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        for vname, cfg in _expand_variants(args.variants, g):
+            gflop = rf.flops(w.M, w.N, w.K) / 1e9
+            if vname == "naive" and gflop > args.max_naive_gflop:
+                continue
+            label = g.config_name(vname, cfg, w.M, w.N, w.K)
+            tile = g.gemm_f32_tile(vname, cfg, w.M, w.N, w.K)
+            reps = args.reps if vname != "naive" else max(1, min(args.reps, 3))
+            print(f"[ladder] {wname} {label} reps={reps}", file=sys.stderr, flush=True)
+
+            def call():
+                g.gemm_f32_ex(w.M, w.N, w.K, ta.data_ptr(), w.K, tb.data_ptr(), w.N,
+                              tc.data_ptr(), w.N, vname, cfg, s)
+
+            ms = timed(call, reps, args.warmup if vname != "naive" else min(args.warmup, 1))
+            tflops = rf.flops(w.M, w.N, w.K) / (ms * 1e-3) / 1e12
+            rec = {"workload": wname, "kernel": label, "variant": vname, "config": tile["config"],
+                   "ms": round(ms, 5), "tflops": round(tflops, 3),
+                   "frac_peak_fp32": round(tflops / rf.PEAK_FP32_MFMA_TFLOPS, 4),
+                   "gbps_compulsory": round(rf.compulsory_bytes(w.M, w.N, w.K) / (ms * 1e-3) / 1e9, 1),
+                   "model_issued_load_bytes": 4 * rf.issued_load_elements(vname, w.M, w.N, w.K, tile),
+                   "flops": rf.flops(w.M, w.N, w.K)}
+            rows.append(rec)
+            print(json.dumps(rec), flush=True)
+        del ta, tb, tc
+        torch.cuda.empty_cache()
+
+    print("\n| workload | kernel | ms | TFLOP/s | % fp32 peak | GB/s (compulsory) |", file=sys.stderr)
+    print("|---|---|---|---|---|---|", file=sys.stderr)
+    for r in rows:
+        print(f"| {r['workload']} | {r['kernel']} | {r['ms']:.4f} | {r['tflops']:.2f} | "
+              f"{100 * r['frac_peak_fp32']:.1f} | {r['gbps_compulsory']:.0f} |", file=sys.stderr)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
