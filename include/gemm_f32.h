@@ -46,7 +46,9 @@ extern "C" {
 #define GEMM_F32_BAD_VARIANT 4   /* unknown variant                         */
 #define GEMM_F32_LAUNCH_FAILED 5 /* the HIP runtime rejected the launch     */
 #define GEMM_F32_MISALIGNED 6    /* a pointer is not 4-byte aligned         */
-#define GEMM_F32_BAD_CONFIG 7    /* config index outside the launch table   */
+#define GEMM_F32_BAD_CONFIG 7    /* config outside the launch table, or not
+                                    valid for this shape (small-K entries
+                                    need K <= their BK)                      */
 #define GEMM_F32_BAD_ARG 8       /* other invalid argument (query helpers)  */
 
 /* ---- variants: the kernel ladder ------------------------------------ */
@@ -93,7 +95,12 @@ int gemm_f32(int M, int N, int K, const float *A, int lda, const float *B,
 /*
  * gemm_f32_ex -- gemm_f32 with an explicit launch-table entry.
  *   config  -1 picks the entry gemm_f32 would use for this shape; otherwise
- *           an index below gemm_f32_num_configs(variant).
+ *           an index below gemm_f32_num_configs(variant).  Production
+ *           entries whose kernel holds all of K in one LDS stage ("panel"
+ *           entries, reported with BK = their K limit) accept K <= BK only.
+ *           Whatever the entry, a thin remainder strip of rows or columns
+ *           (an overhanging tile at most 1/8 full) is computed by a second
+ *           launch with small tiles on the same stream.
  * Same semantics and errors as gemm_f32, plus GEMM_F32_BAD_CONFIG.
  */
 int gemm_f32_ex(int M, int N, int K, const float *A, int lda, const float *B,

@@ -114,6 +114,14 @@ def test_tile_queries():
         assert q["BM"] % 32 == 0 and q["BN"] % 32 == 0 and q["BK"] % 8 == 0
     with pytest.raises(g.GemmError):
         g.gemm_f32_tile("prod", n, 64, 64, 64)
+    # automatic choice for the skinny K = 64 shape is a small-K entry; such
+    # entries refuse K above their BK with BAD_CONFIG, before any launch
+    q = g.gemm_f32_tile("prod", -1, 16384, 16384, 64)
+    assert q["BK"] == 64
+    with pytest.raises(g.GemmError) as e:
+        g.gemm_f32_tile("prod", q["config"], 16384, 16384, 65)
+    assert e.value.status == 7
+    assert _call(256, 256, 65, A=256, B=512, C=1024, variant=2, config=q["config"]) == 7
     with pytest.raises(g.GemmError):
         g.gemm_f32_tile("prod", -1, -1, 64, 64)
     assert g.gemm_f32_num_configs(17) == 0
@@ -129,7 +137,11 @@ def test_package_load_model_matches_oracle_model():
             t = g.gemm_f32_tile(v, -1, M, N, K)
             assert roofline.issued_load_elements(v, M, N, K, t) == model.tiled_loads(M, N, K, t["BM"])
         for i in range(g.gemm_f32_num_configs("prod")):
-            t = g.gemm_f32_tile("prod", i, M, N, K)
+            try:
+                t = g.gemm_f32_tile("prod", i, M, N, K)
+            except g.GemmError as e:  # small-K entries reject K above their BK
+                assert e.status == 7 and K > g.gemm_f32_tile("prod", i, 1, 1, 1)["BK"]
+                continue
             assert roofline.issued_load_elements("prod", M, N, K, t) == model.blocked_loads(
                 M, N, K, t["BM"], t["BN"], t["BK"])
         assert roofline.flops(M, N, K) == model.flops(M, N, K)

@@ -79,14 +79,66 @@ def test_small_uniform_tolerance(g, variant, shape):
     _tol_check(_run(g, a, b, variant), oracle.gemm(a, b), K, f"{variant} {shape}")
 
 
+def _supported(g, cfg, M, N, K):
+    try:
+        g.gemm_f32_tile("prod", cfg, M, N, K)
+        return True
+    except g.GemmError:
+        return False
+
+
 def test_every_prod_config(g):
     for cfg in _prod_configs(g):
-        for (M, N, K) in [(257, 383, 129), (512, 256, 64), (1, 300, 40), (200, 1, 33)]:
+        for (M, N, K) in [(257, 383, 129), (512, 256, 64), (1, 300, 40), (200, 1, 33),
+                          (300, 260, 17)]:
+            if not _supported(g, cfg, M, N, K):
+                continue
             print(f"case: prod config {cfg} {M}x{N}x{K}", flush=True)
             a, b = make(M, N, K, "small_int", seed=cfg + M)
             assert np.array_equal(_run(g, a, b, "prod", cfg), oracle.gemm(a, b)), (cfg, M, N, K)
             a, b = make(M, N, K, "normal", seed=cfg + N)
             _tol_check(_run(g, a, b, "prod", cfg), oracle.gemm(a, b), K, f"prod cfg {cfg}")
+
+
+def _small_k_configs(g):
+    return [c for c in _prod_configs(g) if g.gemm_f32_tile("prod", c, 1, 1, 1)["BK"] == 64
+            and not _supported(g, c, 1, 1, 65)]
+
+
+def test_small_k_panel_configs(g):
+    """The small-K entries: whole-tile shapes (several tiles per workgroup on
+    the persistent grid), K below and at the limit, and ragged shapes whose
+    remainders go to the strip launches."""
+    cfgs = _small_k_configs(g)
+    assert cfgs, "expected small-K launch-table entries"
+    shapes = [(2048, 2048, 64), (1024, 4096, 64), (512, 512, 63), (1024, 1024, 17),
+              (768, 640, 3), (256, 256, 1), (300, 520, 64), (129, 4100, 40), (5000, 129, 64),
+              (100, 100, 64)]
+    for cfg in cfgs:
+        for (M, N, K) in shapes:
+            print(f"case: small-K config {cfg} {M}x{N}x{K}", flush=True)
+            a, b = make(M, N, K, "small_int", seed=cfg * 31 + M + K)
+            assert np.array_equal(_run(g, a, b, "prod", cfg), oracle.gemm(a, b)), (cfg, M, N, K)
+            a, b = make(M, N, K, "uniform", seed=cfg * 17 + N + K)
+            _tol_check(_run(g, a, b, "prod", cfg), oracle.gemm(a, b), K, f"small-K cfg {cfg}")
+
+
+def test_small_k_padded_leading_dimensions(g):
+    dev = _dev()
+    M, N, K = 1024, 768, 64
+    lda, ldb, ldc = 68, 772, 777  # ldc odd: dword-aligned rows of C
+    a, b = make(M, N, K, "small_int", seed=3)
+    for cfg in _small_k_configs(g):
+        abuf = torch.zeros((M, lda), device=dev)
+        bbuf = torch.zeros((K, ldb), device=dev)
+        cbuf = torch.full((M, ldc), -1.0, device=dev)
+        abuf[:, :K] = torch.from_numpy(a).to(dev)
+        bbuf[:, :N] = torch.from_numpy(b).to(dev)
+        g.matmul(abuf[:, :K], bbuf[:, :N], out=cbuf[:, :N], variant="prod", config=cfg)
+        torch.cuda.synchronize()
+        c = cbuf.cpu().numpy()
+        assert np.array_equal(c[:, :N], oracle.gemm(a, b))
+        assert np.all(c[:, N:] == -1.0)
 
 
 def test_edge_sweep(g):

@@ -45,6 +45,8 @@ int resolve_config(int variant, int config, int M, int N, int K, int *out) {
   if (config < -1 || config >= num_configs(variant)) return GEMM_F32_BAD_CONFIG;
   if (config == -1)
     config = variant == GEMM_F32_PROD ? prod_choose(M, N, K) : 0;
+  if (variant == GEMM_F32_PROD && !prod_supports(config, M, N, K))
+    return GEMM_F32_BAD_CONFIG;
   *out = config;
   return GEMM_F32_OK;
 }
@@ -130,7 +132,8 @@ extern "C" const char *gemm_f32_status_string(int status) {
     case GEMM_F32_BAD_VARIANT: return "unknown variant";
     case GEMM_F32_LAUNCH_FAILED: return "kernel launch failed";
     case GEMM_F32_MISALIGNED: return "pointer not aligned to its element size";
-    case GEMM_F32_BAD_CONFIG: return "launch-table index out of range";
+    case GEMM_F32_BAD_CONFIG:
+      return "launch-table index out of range or not valid for this shape";
     case GEMM_F32_BAD_ARG: return "invalid argument";
     default: return "unknown status";
   }

@@ -37,6 +37,7 @@ hipError_t launch_tiled(int T, const Problem &p, hipStream_t s);
 int prod_num_configs();
 const ProdConfig &prod_config(int index);
 int prod_choose(int M, int N, int K);
+bool prod_supports(int index, int M, int N, int K);
 hipError_t launch_prod(int index, const Problem &p, hipStream_t s);
 
 }  // namespace gemm_f32_impl

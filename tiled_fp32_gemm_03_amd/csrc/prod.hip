@@ -93,8 +93,9 @@ struct Tile {
   static_assert(NT % (BK / 4) == 0 && NT % (BN / 4) == 0, "staging map");
   static_assert((BM * BK) % (4 * NT) == 0 && (BK * BN) % (4 * NT) == 0,
                 "tile must split evenly over threads");
-  static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS budget of a gfx950 CU");
 };
+
+constexpr int kLdsBytes = 160 * 1024;  // LDS of one gfx950 CU
 
 // Launch index -> logical id: each XCD gets a contiguous run of ids.
 __device__ inline int xcd_remap(int b, int G) {
@@ -264,6 +265,7 @@ __device__ inline void load_step(Stage<S> &st, const Problem &p, int m0,
 template <class S>
 __global__ void __launch_bounds__(S::NT)
     prod_kernel(Problem p, int tiles_m, int tiles_n) {
+  static_assert(S::LDS_FLOATS * 4 <= kLdsBytes, "two stages must fit in LDS");
   __shared__ __attribute__((aligned(16))) float lds[S::LDS_FLOATS];
   float *const as0 = lds;
   float *const bs0 = lds + 2 * S::A_STAGE;
@@ -337,6 +339,76 @@ __global__ void __launch_bounds__(S::NT)
   }
 }
 
+// s_waitcnt immediate that waits until at most `n` vector-memory operations
+// of this wave are outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt and lgkmcnt left at their "no wait" maxima).
+constexpr int vmcnt_wait_imm(int n) {
+  return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+}
+
+// Small-K kernel: the whole K (<= BK) of a tile fits one LDS stage, so each
+// iteration of the persistent loop is one complete tile.  It covers only
+// whole tiles (the launcher sends edge strips to the k-loop kernel), which
+// keeps the loop straight-line.  Order per tile: issue the next tile's loads
+// into registers, run all MFMAs, issue this tile's TM*TN*4 C stores per
+// lane, barrier (every wave done reading LDS), wait until at most those
+// stores are outstanding -- the vector-memory counter retires in issue
+// order, so this waits for the loads but leaves the stores draining while
+// the next tile computes -- write the stage, barrier.  The last iteration
+// reloads its own tile so every iteration has the same shape.
+template <class S, bool KFULL>
+__global__ void __launch_bounds__(S::NT)
+    panel_kernel(Problem p, int tiles_m, int tiles_n) {
+  static_assert((S::A_STAGE + S::B_STAGE) * 4 <= kLdsBytes, "stage must fit in LDS");
+  __shared__ __attribute__((aligned(16))) float lds[S::A_STAGE + S::B_STAGE];
+  float *const as = lds;
+  float *const bs = lds + S::A_STAGE;
+  constexpr int kStoresPerTile = S::TM * S::TN * 4;
+  static_assert(kStoresPerTile < 64, "vmcnt holds at most 63");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / S::WGN, wn = wave % S::WGN;
+  const int ntiles = tiles_m * tiles_n;
+  const int G = gridDim.x;
+  const int lid = xcd_remap(blockIdx.x, G);
+  if (lid >= ntiles) return;  // uniform per workgroup
+  const int my_tiles = (ntiles - lid + G - 1) / G;
+
+  int t = lid, m0, n0;
+  bool interior;  // always true: the launcher passes whole tiles only
+  tile_origin<S>(t, tiles_m, tiles_n, m0, n0, interior, p);
+  Stage<S> st;
+  load_global<S, !KFULL>(st, p, m0, n0, 0, tid);
+  store_lds<S>(st, as, bs, tid);
+  __syncthreads();
+
+  for (int i = 0; i < my_tiles; ++i) {
+    const int tnext = i + 1 < my_tiles ? t + G : t;
+    int nm0, nn0;
+    tile_origin<S>(tnext, tiles_m, tiles_n, nm0, nn0, interior, p);
+    load_global<S, !KFULL>(st, p, nm0, nn0, 0, tid);
+    // Keep the loads ahead of the MFMAs so their latency hides under them.
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 acc[S::TM][S::TN];
+#pragma unroll
+    for (int a = 0; a < S::TM; ++a)
+#pragma unroll
+      for (int b = 0; b < S::TN; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+    compute_stage<S>(acc, as, bs, wm, wn, lane);
+    store_c<S>(acc, p, m0, n0, wm, wn, lane, false);
+    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(kStoresPerTile));
+    store_lds<S>(st, as, bs, tid);
+    __syncthreads();
+    t = tnext;
+    m0 = nm0;
+    n0 = nn0;
+  }
+}
+
 // ---- launch table ----------------------------------------------------
 
 using C0 = Tile<128, 128, 32, 2, 2, false>;
@@ -347,24 +419,36 @@ using C4 = Tile<128, 64, 32, 2, 2, false>;
 using C5 = Tile<128, 128, 32, 2, 2, true>;
 using C6 = Tile<128, 128, 16, 2, 2, true>;
 using C7 = Tile<256, 128, 32, 4, 2, false>;
+using P8 = Tile<128, 128, 64, 2, 2, false>;  // small-K panel kernel, K <= 64
+using P9 = Tile<256, 128, 64, 4, 2, false>;  // small-K panel kernel, K <= 64
 
-const ProdConfig kConfigs[] = {
-    {128, 128, 32, 2, 2, 2, "128x128x32_w2x2"},
-    {128, 128, 16, 2, 2, 3, "128x128x16_w2x2"},
-    {256, 128, 16, 4, 2, 2, "256x128x16_w4x2"},
-    {64, 64, 32, 2, 2, 4, "64x64x32_w2x2"},
-    {128, 64, 32, 2, 2, 2, "128x64x32_w2x2"},
-    {128, 128, 32, 2, 2, 2, "128x128x32_w2x2_nt"},
-    {128, 128, 16, 2, 2, 3, "128x128x16_w2x2_nt"},
-    {256, 128, 32, 4, 2, 1, "256x128x32_w4x2"},
+enum Kind { kKloop, kPanel };
+
+struct Entry {
+  ProdConfig cfg;
+  Kind kind;
 };
-constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
-// Workgroups of kernel `k` resident on the whole device at once (cached per
+const Entry kEntries[] = {
+    {{128, 128, 32, 2, 2, 2, "128x128x32_w2x2"}, kKloop},
+    {{128, 128, 16, 2, 2, 3, "128x128x16_w2x2"}, kKloop},
+    {{256, 128, 16, 4, 2, 2, "256x128x16_w4x2"}, kKloop},
+    {{64, 64, 32, 2, 2, 4, "64x64x32_w2x2"}, kKloop},
+    {{128, 64, 32, 2, 2, 2, "128x64x32_w2x2"}, kKloop},
+    {{128, 128, 32, 2, 2, 2, "128x128x32_w2x2_nt"}, kKloop},
+    {{128, 128, 16, 2, 2, 3, "128x128x16_w2x2_nt"}, kKloop},
+    {{256, 128, 32, 4, 2, 1, "256x128x32_w4x2"}, kKloop},
+    {{128, 128, 64, 2, 2, 2, "panel128x128_k64"}, kPanel},
+    {{256, 128, 64, 4, 2, 1, "panel256x128_k64"}, kPanel},
+};
+constexpr int kNumConfigs = sizeof(kEntries) / sizeof(kEntries[0]);
+constexpr int kRemainderConfig = 3;  // thin edge strips
+
+// Workgroups of a kernel resident on the whole device at once (cached per
 // kernel and device; computed on first use).
 constexpr int kMaxDevices = 64;
 
-template <class S>
+template <void (*KERNEL)(Problem, int, int), int NT>
 int resident_workgroups() {
   static std::atomic<int> cache[kMaxDevices];
   int dev = 0;
@@ -374,7 +458,7 @@ int resident_workgroups() {
     if (c > 0) return c;
   }
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prod_kernel<S>, S::NT, 0) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, KERNEL, NT, 0) != hipSuccess ||
       per_cu < 1)
     per_cu = 1;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) !=
@@ -386,46 +470,114 @@ int resident_workgroups() {
   return total;
 }
 
-template <class S>
-hipError_t launch_shape(const Problem &p, hipStream_t s) {
+template <class S, void (*KERNEL)(Problem, int, int)>
+hipError_t launch_grid(const Problem &p, hipStream_t s) {
   const long long tiles_m = ceil_div(p.M, S::BM), tiles_n = ceil_div(p.N, S::BN);
   const long long ntiles = tiles_m * tiles_n;
   if (ntiles > 0x7fffffffLL) return hipErrorInvalidValue;
-  long long grid = resident_workgroups<S>();
+  long long grid = resident_workgroups<KERNEL, S::NT>();
   if (grid > ntiles) grid = ntiles;
-  return launch_kernel(prod_kernel<S>, dim3((unsigned)grid), dim3(S::NT), s, p,
+  return launch_kernel(KERNEL, dim3((unsigned)grid), dim3(S::NT), s, p,
                        (int)tiles_m, (int)tiles_n);
+}
+
+template <class S>
+hipError_t launch_kloop(const Problem &p, hipStream_t s) {
+  return launch_grid<S, prod_kernel<S>>(p, s);
+}
+
+// Whole tiles only: the caller (launch_prod) splits edge strips off first.
+template <class S>
+hipError_t launch_panel(const Problem &p, hipStream_t s) {
+  if (p.K > S::BK || p.M % S::BM != 0 || p.N % S::BN != 0) return hipErrorInvalidValue;
+  if (p.K == S::BK) return launch_grid<S, panel_kernel<S, true>>(p, s);
+  return launch_grid<S, panel_kernel<S, false>>(p, s);
+}
+
+hipError_t launch_one(int index, const Problem &p, hipStream_t s) {
+  switch (index) {
+    case 0: return launch_kloop<C0>(p, s);
+    case 1: return launch_kloop<C1>(p, s);
+    case 2: return launch_kloop<C2>(p, s);
+    case 3: return launch_kloop<C3>(p, s);
+    case 4: return launch_kloop<C4>(p, s);
+    case 5: return launch_kloop<C5>(p, s);
+    case 6: return launch_kloop<C6>(p, s);
+    case 7: return launch_kloop<C7>(p, s);
+    case 8: return launch_panel<P8>(p, s);
+    case 9: return launch_panel<P9>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Rows (or columns) of a thin remainder strip worth a separate launch: an
+// overhanging tile row that is at most 1/8 full would cost a whole extra
+// round of tiles for almost no work.
+int thin_remainder(int extent, int tile) {
+  const int rem = extent % tile;
+  return (extent > tile && rem > 0 && rem * 8 <= tile) ? rem : 0;
 }
 
 }  // namespace
 
 int prod_num_configs() { return kNumConfigs; }
 
-const ProdConfig &prod_config(int index) { return kConfigs[index]; }
+const ProdConfig &prod_config(int index) { return kEntries[index].cfg; }
 
-// Shape-based choice from measurements on MI355X (square 4096: 256x128x16;
-// smaller squares: 64x64 tiles to give every CU work; skinny K: 128x128x16).
+bool prod_supports(int index, int M, int N, int K) {
+  (void)M;
+  (void)N;
+  return kEntries[index].kind != kPanel || K <= kEntries[index].cfg.BK;
+}
+
+// Shape-based choice from measurements on MI355X: the small-K panel kernel
+// for K <= 64 with many tiles; 256x128x16 for large squares; 64x64 tiles for
+// smaller problems so that every CU has work.
 int prod_choose(int M, int N, int K) {
   const long long t256x128 = ceil_div(M, 256) * ceil_div(N, 128);
   const long long t64 = ceil_div(M, 64) * ceil_div(N, 64);
-  if (K <= 128 && t256x128 >= 1024) return 1;
+  if (K <= 64 && ceil_div(M, 128) * ceil_div(N, 128) >= 2048) return 8;
   if (t256x128 >= 512) return 2;
   if (t64 >= 2048) return 4;
   return 3;
 }
 
+// One product with launch-table entry `index`.  Thin remainder strips along
+// M or N (and, for the small-K panel entries, any remainder) go to separate
+// launches with small tiles; all launches share the stream, so they run in
+// order.
 hipError_t launch_prod(int index, const Problem &p, hipStream_t s) {
-  switch (index) {
-    case 0: return launch_shape<C0>(p, s);
-    case 1: return launch_shape<C1>(p, s);
-    case 2: return launch_shape<C2>(p, s);
-    case 3: return launch_shape<C3>(p, s);
-    case 4: return launch_shape<C4>(p, s);
-    case 5: return launch_shape<C5>(p, s);
-    case 6: return launch_shape<C6>(p, s);
-    case 7: return launch_shape<C7>(p, s);
-    default: return hipErrorInvalidValue;
+  if (!prod_supports(index, p.M, p.N, p.K)) return hipErrorInvalidValue;
+  const ProdConfig &c = kEntries[index].cfg;
+  int rm = index == kRemainderConfig ? 0 : thin_remainder(p.M, c.BM);
+  int rn = index == kRemainderConfig ? 0 : thin_remainder(p.N, c.BN);
+  if (kEntries[index].kind == kPanel) {  // whole tiles only; every remainder is a strip
+    rm = p.M % c.BM;
+    rn = p.N % c.BN;
+    if (p.M < c.BM || p.N < c.BN) return launch_one(kRemainderConfig, p, s);
   }
+  Problem main_part = p;
+  main_part.M = p.M - rm;
+  main_part.N = p.N - rn;
+  hipError_t e = launch_one(index, main_part, s);
+  if (e != hipSuccess) return e;
+  if (rn > 0) {  // right strip beside the main block
+    Problem strip = p;
+    strip.M = main_part.M;
+    strip.N = rn;
+    strip.B = p.B + main_part.N;
+    strip.C = p.C + main_part.N;
+    e = launch_one(kRemainderConfig, strip, s);
+    if (e != hipSuccess) return e;
+  }
+  if (rm > 0) {  // bottom strip, full width
+    Problem strip = p;
+    strip.M = rm;
+    strip.A = p.A + (long long)main_part.M * p.lda;
+    strip.C = p.C + (long long)main_part.M * p.ldc;
+    e = launch_one(kRemainderConfig, strip, s);
+  }
+  return e;
 }
 
 }  // namespace gemm_f32_impl

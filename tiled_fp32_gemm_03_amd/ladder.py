@@ -100,8 +100,11 @@ def main(argv=None) -> int:
             gflop = rf.flops(w.M, w.N, w.K) / 1e9
             if vname == "naive" and gflop > args.max_naive_gflop:
                 continue
+            try:
+                tile = g.gemm_f32_tile(vname, cfg, w.M, w.N, w.K)
+            except g.GemmError:  # entry does not accept this shape (small-K entries)
+                continue
             label = g.config_name(vname, cfg, w.M, w.N, w.K)
-            tile = g.gemm_f32_tile(vname, cfg, w.M, w.N, w.K)
             reps = args.reps if vname != "naive" else max(1, min(args.reps, 3))
             print(f"[ladder] {wname} {label} reps={reps}", file=sys.stderr, flush=True)
 
