@@ -141,6 +141,34 @@ def test_small_k_padded_leading_dimensions(g):
         assert np.all(c[:, N:] == -1.0)
 
 
+def test_thin_remainder_strips(g):
+    """Main block plus thin remainder strips: a bottom strip of 1-8 rows goes
+    to the thin-M strip kernel, 9 up to BM/8 rows to small tiles; a right
+    strip of up to BN/8 columns to small tiles."""
+    for cfg in (0, 2, 7):
+        t = g.gemm_f32_tile("prod", cfg, 1, 1, 1)
+        bm, bn = t["BM"], t["BN"]
+        for r in sorted({1, 2, 5, 8, 9, bm // 8}):
+            for (N, K) in [(200, 130), (2 * bn + max(1, bn // 8), 33)]:
+                M = 2 * bm + r
+                print(f"case: strips cfg {cfg} {M}x{N}x{K}", flush=True)
+                a, b = make(M, N, K, "small_int", seed=cfg * 101 + r + N)
+                assert np.array_equal(_run(g, a, b, "prod", cfg), oracle.gemm(a, b)), (cfg, M, N, K)
+                a, b = make(M, N, K, "normal", seed=cfg * 103 + r + K)
+                _tol_check(_run(g, a, b, "prod", cfg), oracle.gemm(a, b), K, f"strips cfg {cfg}")
+
+
+def test_guarded_windows_short_rows(g):
+    """Rows of exactly 4 and of 1-3 elements (the per-element fallback), and
+    K tails of 1-3 past a multiple of 4 (the shifted-window loads)."""
+    for (M, N, K) in [(300, 4, 4), (300, 3, 5), (257, 260, 3), (129, 130, 1), (300, 261, 66),
+                      (515, 133, 2049), (260, 4095, 7)]:
+        for cfg in (0, 2, 3):
+            print(f"case: windows cfg {cfg} {M}x{N}x{K}", flush=True)
+            a, b = make(M, N, K, "small_int", seed=M + N + K + cfg)
+            assert np.array_equal(_run(g, a, b, "prod", cfg), oracle.gemm(a, b)), (cfg, M, N, K)
+
+
 def test_edge_sweep(g):
     """Every remainder against every tile size: sampled combinations of
     M, N, K around multiples of 16, 32, 64 and 128."""

@@ -118,16 +118,50 @@ __device__ inline void tile_coords(int lid, int tiles_m, int tiles_n, int &tm,
 
 template <class S>
 struct Stage {
-  // registers holding one k step of A and B on their way to LDS
+  // registers holding one k step of A and B on their way to LDS, and per
+  // chunk how to place the loaded 4-float window: (valid << 2) | shift --
+  // element e of the chunk is window[e + shift] if e < valid, else 0.
   f32x4 a[S::A_CHUNKS];
   f32x4 b[S::B_CHUNKS];
+  int ameta[S::A_CHUNKS];
+  int bmeta[S::B_CHUNKS];
 };
+
+constexpr int kMetaFull = 4 << 2;  // four valid elements, no shift
 
 __device__ inline f32x4 load4(const float *src) {
   return *reinterpret_cast<const f32x4u *>(src);
 }
 
-// Four elements src[0..3] with those at index >= valid read as 0.
+// Branch-free guarded chunk load.  Every lane issues one 128-bit load at an
+// address that is always inside the matrix: a chunk wholly inside its row is
+// loaded in place; one that straddles the row end loads the 4-float window
+// ending at the row end (so no byte past the row is touched) and records the
+// shift; a chunk outside the matrix loads from the matrix origin and is
+// marked empty.  The zeroing happens when the stage is written to LDS, after
+// the data has arrived, so no lane's path waits on another's load.
+// Needs row length >= 4 (the caller takes the per-element path otherwise).
+__device__ inline f32x4 load_chunk_guarded(const float *base, long long ld,
+                                           int row, int rows, int col,
+                                           int cols, int &meta) {
+  int valid = 0, shift = 0;
+  long long off = 0;
+  if (row < rows && col < cols) {
+    if (col + 4 <= cols) {
+      valid = 4;
+      off = (long long)row * ld + col;
+    } else {
+      valid = cols - col;
+      shift = col - (cols - 4);
+      off = (long long)row * ld + (cols - 4);
+    }
+  }
+  meta = (valid << 2) | shift;
+  return load4(base + off);
+}
+
+// Four elements src[0..3] with those at index >= valid read as 0 (per
+// element; used only for rows shorter than 4 elements).
 __device__ inline f32x4 load_partial(const float *src, int valid) {
   f32x4 v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -136,44 +170,89 @@ __device__ inline f32x4 load_partial(const float *src, int valid) {
   return v;
 }
 
+__device__ inline float pick(const f32x4 &w, int j) {
+  return j == 0 ? w[0] : j == 1 ? w[1] : j == 2 ? w[2] : w[3];
+}
+
+// Place a loaded window according to its meta code (see Stage).
+__device__ inline f32x4 place(const f32x4 &w, int meta) {
+  const int valid = meta >> 2, shift = meta & 3;
+  f32x4 v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = e < valid ? pick(w, e + shift) : 0.f;
+  return v;
+}
+
 template <class S, bool GUARD>
 __device__ inline void load_global(Stage<S> &st, const Problem &p, int m0,
                                    int n0, int k0, int tid) {
   const int arow = tid / (S::BK / 4), akq = (tid % (S::BK / 4)) * 4;
+  const int bkr = tid / (S::BN / 4), bnq = (tid % (S::BN / 4)) * 4;
+  if (!GUARD) {
 #pragma unroll
-  for (int i = 0; i < S::A_CHUNKS; ++i) {
-    const int gm = m0 + arow + i * S::A_ROWS_PER_PASS;
-    const int gk = k0 + akq;
-    const float *src = p.A + (long long)gm * p.lda + gk;
-    if (!GUARD || (gm < p.M && gk + 4 <= p.K))
-      st.a[i] = load4(src);
-    else
-      st.a[i] = load_partial(src, gm < p.M ? p.K - gk : 0);
+    for (int i = 0; i < S::A_CHUNKS; ++i) {
+      const int gm = m0 + arow + i * S::A_ROWS_PER_PASS;
+      st.a[i] = load4(p.A + (long long)gm * p.lda + k0 + akq);
+      st.ameta[i] = kMetaFull;
+    }
+#pragma unroll
+    for (int i = 0; i < S::B_CHUNKS; ++i) {
+      const int gk = k0 + bkr + i * S::B_ROWS_PER_PASS;
+      st.b[i] = load4(p.B + (long long)gk * p.ldb + n0 + bnq);
+      st.bmeta[i] = kMetaFull;
+    }
+  } else if (p.K >= 4 && p.N >= 4) {
+#pragma unroll
+    for (int i = 0; i < S::A_CHUNKS; ++i)
+      st.a[i] = load_chunk_guarded(p.A, p.lda, m0 + arow + i * S::A_ROWS_PER_PASS, p.M,
+                                   k0 + akq, p.K, st.ameta[i]);
+#pragma unroll
+    for (int i = 0; i < S::B_CHUNKS; ++i)
+      st.b[i] = load_chunk_guarded(p.B, p.ldb, k0 + bkr + i * S::B_ROWS_PER_PASS, p.K,
+                                   n0 + bnq, p.N, st.bmeta[i]);
+  } else {
+    // rows shorter than one chunk: per-element loads (tiny problems only)
+#pragma unroll
+    for (int i = 0; i < S::A_CHUNKS; ++i) {
+      const int gm = m0 + arow + i * S::A_ROWS_PER_PASS;
+      const int gk = k0 + akq;
+      st.a[i] = load_partial(p.A + (long long)gm * p.lda + gk, gm < p.M ? p.K - gk : 0);
+      st.ameta[i] = kMetaFull;
+    }
+#pragma unroll
+    for (int i = 0; i < S::B_CHUNKS; ++i) {
+      const int gk = k0 + bkr + i * S::B_ROWS_PER_PASS;
+      const int gn = n0 + bnq;
+      st.b[i] = load_partial(p.B + (long long)gk * p.ldb + gn, gk < p.K ? p.N - gn : 0);
+      st.bmeta[i] = kMetaFull;
+    }
   }
+}
+
+// Write one staged k step to LDS.  PLACED: the stage came from guarded loads
+// and each chunk is placed by its meta code; otherwise it is stored as is.
+template <class S, bool PLACED>
+__device__ inline void store_lds_as(const Stage<S> &st, float *as, float *bs,
+                                    int tid) {
+  const int arow = tid / (S::BK / 4), akq = (tid % (S::BK / 4)) * 4;
+#pragma unroll
+  for (int i = 0; i < S::A_CHUNKS; ++i)
+    *reinterpret_cast<f32x4 *>(as + (arow + i * S::A_ROWS_PER_PASS) * S::SA + akq) =
+        PLACED ? place(st.a[i], st.ameta[i]) : st.a[i];
   const int bkr = tid / (S::BN / 4), bnq = (tid % (S::BN / 4)) * 4;
 #pragma unroll
-  for (int i = 0; i < S::B_CHUNKS; ++i) {
-    const int gk = k0 + bkr + i * S::B_ROWS_PER_PASS;
-    const int gn = n0 + bnq;
-    const float *src = p.B + (long long)gk * p.ldb + gn;
-    if (!GUARD || (gk < p.K && gn + 4 <= p.N))
-      st.b[i] = load4(src);
-    else
-      st.b[i] = load_partial(src, gk < p.K ? p.N - gn : 0);
-  }
+  for (int i = 0; i < S::B_CHUNKS; ++i)
+    *reinterpret_cast<f32x4 *>(bs + (bkr + i * S::B_ROWS_PER_PASS) * S::SB + bnq) =
+        PLACED ? place(st.b[i], st.bmeta[i]) : st.b[i];
 }
 
 template <class S>
 __device__ inline void store_lds(const Stage<S> &st, float *as, float *bs,
-                                 int tid) {
-  const int arow = tid / (S::BK / 4), akq = (tid % (S::BK / 4)) * 4;
-#pragma unroll
-  for (int i = 0; i < S::A_CHUNKS; ++i)
-    *reinterpret_cast<f32x4 *>(as + (arow + i * S::A_ROWS_PER_PASS) * S::SA + akq) = st.a[i];
-  const int bkr = tid / (S::BN / 4), bnq = (tid % (S::BN / 4)) * 4;
-#pragma unroll
-  for (int i = 0; i < S::B_CHUNKS; ++i)
-    *reinterpret_cast<f32x4 *>(bs + (bkr + i * S::B_ROWS_PER_PASS) * S::SB + bnq) = st.b[i];
+                                 int tid, bool guarded) {
+  if (guarded)
+    store_lds_as<S, true>(st, as, bs, tid);
+  else
+    store_lds_as<S, false>(st, as, bs, tid);
 }
 
 // All MFMAs of one k step out of one LDS stage.
@@ -253,13 +332,16 @@ __device__ inline void tile_origin(int t, int tiles_m, int tiles_n, int &m0,
   interior = (m0 + S::BM <= p.M) && (n0 + S::BN <= p.N);
 }
 
+// Load one k step; returns whether the guarded path was taken (uniform).
 template <class S>
-__device__ inline void load_step(Stage<S> &st, const Problem &p, int m0,
+__device__ inline bool load_step(Stage<S> &st, const Problem &p, int m0,
                                  int n0, int k0, bool interior, int tid) {
-  if (interior && k0 + S::BK <= p.K)
+  if (interior && k0 + S::BK <= p.K) {
     load_global<S, false>(st, p, m0, n0, k0, tid);
-  else
-    load_global<S, true>(st, p, m0, n0, k0, tid);
+    return false;
+  }
+  load_global<S, true>(st, p, m0, n0, k0, tid);
+  return true;
 }
 
 template <class S>
@@ -296,8 +378,8 @@ __global__ void __launch_bounds__(S::NT)
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   Stage<S> st;
-  load_step<S>(st, p, m0, n0, 0, interior, tid);
-  store_lds<S>(st, as0, bs0, tid);
+  bool guarded = load_step<S>(st, p, m0, n0, 0, interior, tid);
+  store_lds<S>(st, as0, bs0, tid, guarded);
   __syncthreads();
 
   for (long long it = 0; it < steps; ++it) {
@@ -312,7 +394,7 @@ __global__ void __launch_bounds__(S::NT)
       nt = t + G;
       if (more) tile_origin<S>(nt, tiles_m, tiles_n, nm0, nn0, ninterior, p);
     }
-    if (more) load_step<S>(st, p, nm0, nn0, nkt * S::BK, ninterior, tid);
+    if (more) guarded = load_step<S>(st, p, nm0, nn0, nkt * S::BK, ninterior, tid);
 
     compute_stage<S>(acc, as0 + cur * S::A_STAGE, bs0 + cur * S::B_STAGE, wm,
                      wn, lane);
@@ -329,7 +411,7 @@ __global__ void __launch_bounds__(S::NT)
     }
     if (more)
       store_lds<S>(st, as0 + (cur ^ 1) * S::A_STAGE,
-                   bs0 + (cur ^ 1) * S::B_STAGE, tid);
+                   bs0 + (cur ^ 1) * S::B_STAGE, tid, guarded);
     __syncthreads();
     t = nt;
     kt = nkt;
@@ -380,7 +462,7 @@ __global__ void __launch_bounds__(S::NT)
   tile_origin<S>(t, tiles_m, tiles_n, m0, n0, interior, p);
   Stage<S> st;
   load_global<S, !KFULL>(st, p, m0, n0, 0, tid);
-  store_lds<S>(st, as, bs, tid);
+  store_lds_as<S, !KFULL>(st, as, bs, tid);
   __syncthreads();
 
   for (int i = 0; i < my_tiles; ++i) {
@@ -401,13 +483,65 @@ __global__ void __launch_bounds__(S::NT)
     store_c<S>(acc, p, m0, n0, wm, wn, lane, false);
     __syncthreads();
     __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(kStoresPerTile));
-    store_lds<S>(st, as, bs, tid);
+    store_lds_as<S, !KFULL>(st, as, bs, tid);
     __syncthreads();
     t = tnext;
     m0 = nm0;
     n0 = nn0;
   }
 }
+
+// Thin-M kernel for a bottom remainder strip of at most R rows (a strip too
+// thin for MFMA tiles: a 256-row tile holding one valid row would cost a
+// whole round of tiles).  Each workgroup owns 16 columns; its 256 threads are
+// 16 columns x 16 k-slices (slice q takes k = q, q + 16, ...).  Each thread
+// accumulates R outputs in fp32 over its slice in ascending k; the 16 slice
+// sums are added in slice order through LDS, so the result is deterministic.
+template <int R>
+__global__ void __launch_bounds__(256) strip_kernel(Problem p) {
+  constexpr int KS = 16;
+  __shared__ float red[KS][R][16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15;
+  const int ks = (lane >> 4) + 4 * wave;
+  const long long n = (long long)blockIdx.x * 16 + col;
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+  if (n < p.N) {
+    const float *bcol = p.B + n;
+#pragma unroll 8
+    for (int k = ks; k < p.K; k += KS) {
+      const float b = bcol[(long long)k * p.ldb];
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (r < p.M) acc[r] += p.A[(long long)r * p.lda + k] * b;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) red[ks][r][col] = acc[r];
+  __syncthreads();
+  if (tid < 16 * R) {
+    const int r = tid / 16, c = tid % 16;
+    const long long n2 = (long long)blockIdx.x * 16 + c;
+    if (r < p.M && n2 < p.N) {
+      float sum = 0.f;
+#pragma unroll
+      for (int q = 0; q < KS; ++q) sum += red[q][r][c];
+      p.C[(long long)r * p.ldc + n2] = sum;
+    }
+  }
+}
+
+hipError_t launch_strip(const Problem &p, hipStream_t s) {
+  const dim3 grid((unsigned)ceil_div(p.N, 16)), block(256);
+  if (p.M <= 1) return launch_kernel(strip_kernel<1>, grid, block, s, p);
+  if (p.M <= 2) return launch_kernel(strip_kernel<2>, grid, block, s, p);
+  if (p.M <= 4) return launch_kernel(strip_kernel<4>, grid, block, s, p);
+  if (p.M <= 8) return launch_kernel(strip_kernel<8>, grid, block, s, p);
+  return hipErrorInvalidValue;
+}
+constexpr int kStripMaxRows = 8;
 
 // ---- launch table ----------------------------------------------------
 
@@ -575,7 +709,7 @@ hipError_t launch_prod(int index, const Problem &p, hipStream_t s) {
     strip.M = rm;
     strip.A = p.A + (long long)main_part.M * p.lda;
     strip.C = p.C + (long long)main_part.M * p.ldc;
-    e = launch_one(kRemainderConfig, strip, s);
+    e = rm <= kStripMaxRows ? launch_strip(strip, s) : launch_one(kRemainderConfig, strip, s);
   }
   return e;
 }
