@@ -11,9 +11,12 @@ Two subcommands, both reading CSV files that rocprofv3 wrote
   pmc    --run <ladder.jsonl>:<..._counter_collection.csv> [--run ...]
          --command "<command of run 1>" [--command ...]
          [--traffic-out profiles/traffic.json]
-         Joins each counter run's dispatches of this library's kernels, in
-         order, with the ladder tool's records (one launch per record, no
-         warm-up), and reports the counters per kernel.  The streaming copy
+         Joins each counter run's dispatches of this library's kernels with
+         the ladder tool's records: the ladder launches a marker (a 3-float
+         fill, kernel stream_tail<1>) before each record, and every dispatch
+         up to the next marker belongs to that record (one rep, no warm-up;
+         a product may take several launches).  Counters are summed per
+         record.  The streaming copy
          probe that the ladder runs first (``--copy-mib``) moves a known
          number of bytes each way; FETCH_SIZE and WRITE_SIZE are scaled by
          known / counted on that probe to give HBM bytes per launch.  With
@@ -74,6 +77,27 @@ def cmd_trace(args) -> int:
     return 0
 
 
+MARKER = "stream_tail<1>"
+
+
+def _segments(dispatches):
+    """Split dispatches at marker launches; each segment sums its counters."""
+    segs = []
+    for d in dispatches:
+        if d["name"] == MARKER:
+            segs.append({"name": None, "grid": 0, "counters": defaultdict(float), "kernels": []})
+            continue
+        if not segs:
+            raise SystemExit("counter run starts without a marker dispatch")
+        seg = segs[-1]
+        seg["kernels"].append(d["name"])
+        seg["name"] = seg["name"] or d["name"]
+        seg["grid"] += d["grid"]
+        for k, v in d["counters"].items():
+            seg["counters"][k] += v
+    return segs
+
+
 def _read_counter_csv(path: str):
     """Dispatches of this library's kernels, in dispatch order: list of
     (kernel short name, grid threads, {counter: value})."""
@@ -105,12 +129,13 @@ def cmd_pmc(args) -> int:
     for run in args.run:
         jl, cs = run.split(":", 1)
         recs = _read_ladder(jl)
-        disp = _read_counter_csv(cs)
+        disp = _segments(_read_counter_csv(cs))
         if len(recs) != len(disp):
-            raise SystemExit(f"{run}: {len(recs)} ladder records but {len(disp)} dispatches")
+            raise SystemExit(f"{run}: {len(recs)} ladder records but {len(disp)} marked segments")
         for i, (r, d) in enumerate(zip(recs, disp)):
             if i >= len(joined):
-                joined.append({"rec": r, "name": d["name"], "grid": d["grid"], "counters": {}})
+                joined.append({"rec": r, "name": d["name"], "grid": d["grid"], "counters": {},
+                               "kernels": d["kernels"]})
             elif joined[i]["rec"].get("kernel") != r.get("kernel"):
                 raise SystemExit(f"{run}: record {i} is {r.get('kernel')} in one run and "
                                  f"{joined[i]['rec'].get('kernel')} in another")
@@ -129,7 +154,7 @@ def cmd_pmc(args) -> int:
     if cal:
         lines += ["Calibration on the streaming copy probe (known bytes / counted bytes): " +
                   ", ".join(f"{k} x{v:.4f}" for k, v in cal.items()), ""]
-    hdr = ["workload", "kernel", *counters]
+    hdr = ["workload", "kernel", "launches", *counters]
     if "FETCH_SIZE" in counters:
         hdr.append("HBM read MB (cal.)")
     if "WRITE_SIZE" in counters:
@@ -139,7 +164,7 @@ def cmd_pmc(args) -> int:
     traffic = {}
     for j in joined:
         r, c = j["rec"], j["counters"]
-        row = [r.get("workload", "-"), r.get("kernel", j["name"])]
+        row = [r.get("workload", "-"), r.get("kernel", j["name"]), str(len(j["kernels"]))]
         row += [f"{c[k]:.6g}" if k in c else "-" for k in counters]
         rd = c.get("FETCH_SIZE", 0.0) * 1024 * cal.get("FETCH_SIZE", 1.0)
         wr = c.get("WRITE_SIZE", 0.0) * 1024 * cal.get("WRITE_SIZE", 1.0)

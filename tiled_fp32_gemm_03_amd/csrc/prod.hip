@@ -670,7 +670,7 @@ bool prod_supports(int index, int M, int N, int K) {
 int prod_choose(int M, int N, int K) {
   const long long t256x128 = ceil_div(M, 256) * ceil_div(N, 128);
   const long long t64 = ceil_div(M, 64) * ceil_div(N, 64);
-  if (K <= 64 && ceil_div(M, 128) * ceil_div(N, 128) >= 2048) return 8;
+  if (K <= 64 && t256x128 >= 1024) return 9;
   if (t256x128 >= 512) return 2;
   if (t64 >= 2048) return 4;
   return 3;

@@ -8,6 +8,10 @@ for the production rung, ``prod:<i>`` for launch-table entry i or
 ``prod:all`` for every entry.  ``--copy-mib N`` first runs the streaming copy
 probe once over N MiB (a kernel of known traffic: N MiB read, N MiB written)
 so that memory counters collected over the same run can be calibrated.
+Before each record the tool launches a marker (a 3-float fill, which runs
+only the scalar tail kernel), so that a
+counter run can attribute every dispatch between two markers -- a product
+may take more than one launch -- to the record that follows the marker.
 
 Each measurement prints one JSON line (kernel, ms per launch from HIP events
 on the launch stream, TFLOP/s, compulsory-byte GB/s, the tiled load model);
@@ -78,12 +82,18 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / max(reps, 1)
 
+    marker = torch.empty(4, device=dev)
+
+    def mark():
+        g.gemm_f32_probe_stream(g.PROBE_FILL, 3, 0, 0, marker.data_ptr(), s)
+
     if args.copy_mib > 0:
         n = args.copy_mib * (1 << 20) // 4
         x = torch.ones(n, device=dev)
         z = torch.empty(n, device=dev)
         torch.cuda.synchronize()
         print(f"[ladder] copy probe over {args.copy_mib} MiB", file=sys.stderr, flush=True)
+        mark()
         ms = timed(lambda: g.gemm_f32_probe_stream(g.PROBE_COPY, n, x.data_ptr(), 0, z.data_ptr(), s), 1, 0)
         print(json.dumps({"kernel": "probe_copy", "bytes_read": n * 4, "bytes_written": n * 4,
                           "ms": round(ms, 5)}), flush=True)
@@ -111,6 +121,8 @@ def main(argv=None) -> int:
             def call():
                 g.gemm_f32_ex(w.M, w.N, w.K, ta.data_ptr(), w.K, tb.data_ptr(), w.N,
                               tc.data_ptr(), w.N, vname, cfg, s)
+
+            mark()
 
             ms = timed(call, reps, args.warmup if vname != "naive" else min(args.warmup, 1))
             tflops = rf.flops(w.M, w.N, w.K) / (ms * 1e-3) / 1e12
