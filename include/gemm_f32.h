@@ -76,7 +76,11 @@ extern "C" {
  * T = 4 example; ijyty.com 8x8 / TILE_SIZE = 4 example).  For tests and
  * teaching; slow. */
 #define GEMM_F32_TILED4 4
-#define GEMM_F32_NUM_VARIANTS 5
+/* The T = 32 textbook kernel with each LDS row padded by one float, the
+ * shared-memory bank-conflict remedy the pages point to (geek-doc.cn
+ * section 五).  Same results as GEMM_F32_TILED32; a measurement rung. */
+#define GEMM_F32_TILED32_PAD 5
+#define GEMM_F32_NUM_VARIANTS 6
 
 /*
  * gemm_f32 -- C = A x B (overwrite), see the layout above.

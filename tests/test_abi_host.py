@@ -62,7 +62,7 @@ def test_validation_codes():
     assert _call(4, 4, 4, ldb=3) == bad_ld
     assert _call(4, 4, 4, ldc=3) == bad_ld
     assert _call(4, 4, 0, lda=0) == bad_ld          # lda >= max(1, K)
-    assert _call(4, 4, 4, variant=5) == bad_var
+    assert _call(4, 4, 4, variant=6) == bad_var
     assert _call(4, 4, 4, variant=-1) == bad_var
     assert _call(4, 4, 4, variant=2, config=99) == bad_cfg
     assert _call(4, 4, 4, variant=0, config=1) == bad_cfg
@@ -103,7 +103,7 @@ def test_probe_validation():
 
 def test_tile_queries():
     assert g.gemm_f32_tile("naive", -1, 8, 8, 8) == {"BM": 4, "BN": 64, "BK": 1, "threads": 256, "config": 0}
-    for name, t in (("tiled", 16), ("tiled32", 32), ("tiled4", 4)):
+    for name, t in (("tiled", 16), ("tiled32", 32), ("tiled4", 4), ("tiled32_pad", 32)):
         q = g.gemm_f32_tile(name, -1, 100, 100, 100)
         assert (q["BM"], q["BN"], q["BK"], q["threads"]) == (t, t, t, t * t)
     n = g.gemm_f32_num_configs("prod")
@@ -133,7 +133,7 @@ def test_package_load_model_matches_oracle_model():
     shapes = [(4096, 4096, 4096), (4097, 4095, 2049), (16384, 16384, 64), (5, 7, 3), (256, 256, 256)]
     for M, N, K in shapes:
         assert roofline.issued_load_elements("naive", M, N, K, {}) == model.naive_loads(M, N, K)
-        for v in ("tiled", "tiled32", "tiled4"):
+        for v in ("tiled", "tiled32", "tiled4", "tiled32_pad"):
             t = g.gemm_f32_tile(v, -1, M, N, K)
             assert roofline.issued_load_elements(v, M, N, K, t) == model.tiled_loads(M, N, K, t["BM"])
         for i in range(g.gemm_f32_num_configs("prod")):

@@ -18,7 +18,7 @@ torch = pytest.importorskip("torch")
 import oracle  # noqa: E402
 from gemm_inputs import WORKLOADS, make, make_workload  # noqa: E402
 
-LADDER = ("naive", "tiled", "tiled32", "prod")
+LADDER = ("naive", "tiled", "tiled32", "tiled32_pad", "prod")
 
 
 @pytest.fixture(scope="module")

@@ -70,7 +70,7 @@ for _name, (_args, _ret) in _SIGS.items():
     _fn.restype = _ret
 
 # Variant ids of include/gemm_f32.h.
-VARIANTS = {"naive": 0, "tiled": 1, "prod": 2, "tiled32": 3, "tiled4": 4}
+VARIANTS = {"naive": 0, "tiled": 1, "prod": 2, "tiled32": 3, "tiled4": 4, "tiled32_pad": 5}
 PROBE_COPY, PROBE_FILL, PROBE_VADD = 0, 1, 2
 
 

@@ -11,7 +11,7 @@ using namespace gemm_f32_impl;
 
 namespace {
 
-constexpr int kTiledT[GEMM_F32_NUM_VARIANTS] = {0, 16, 0, 32, 4};
+constexpr int kTiledT[GEMM_F32_NUM_VARIANTS] = {0, 16, 0, 32, 4, 32};
 
 thread_local char t_last_error[256] = "";
 
@@ -83,7 +83,8 @@ extern "C" int gemm_f32_ex(int M, int N, int K, const float *A, int lda,
   if (K == 0) return launch_status(launch_zero(p, s), "zero fill");  // the empty sum
   if (variant == GEMM_F32_NAIVE) return launch_status(launch_naive(p, s), "naive");
   if (variant == GEMM_F32_PROD) return launch_status(launch_prod(chosen, p, s), "prod");
-  return launch_status(launch_tiled(kTiledT[variant], p, s), "tiled");
+  return launch_status(
+      launch_tiled(kTiledT[variant], variant == GEMM_F32_TILED32_PAD, p, s), "tiled");
 }
 
 extern "C" int gemm_f32(int M, int N, int K, const float *A, int lda,

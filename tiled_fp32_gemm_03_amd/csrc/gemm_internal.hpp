@@ -32,7 +32,7 @@ constexpr int kMaxGridY = 65535;
 
 hipError_t launch_zero(const Problem &p, hipStream_t s);
 hipError_t launch_naive(const Problem &p, hipStream_t s);
-hipError_t launch_tiled(int T, const Problem &p, hipStream_t s);
+hipError_t launch_tiled(int T, bool padded, const Problem &p, hipStream_t s);
 
 int prod_num_configs();
 const ProdConfig &prod_config(int index);

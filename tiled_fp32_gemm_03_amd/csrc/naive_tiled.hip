@@ -49,10 +49,15 @@ __global__ void __launch_bounds__(kNaiveX *kNaiveY)
   }
 }
 
-template <int T>
+// PAD floats after each LDS row: the padded form the pages point to for
+// shared-memory bank conflicts (geek-doc.cn section 五).  With this access
+// pattern (As[ty][k] is one address per row of threads, Bs[k][tx] walks
+// consecutive words) the unpadded tiles are already conflict-free on CDNA4's
+// LDS; the padded rung exists to measure that claim.
+template <int T, int PAD = 0>
 __global__ void __launch_bounds__(T *T) tiled_kernel(Problem p, int tiles_m) {
-  __shared__ float As[T][T];
-  __shared__ float Bs[T][T];
+  __shared__ float As[T][T + PAD];
+  __shared__ float Bs[T][T + PAD];
   const int tx = threadIdx.x, ty = threadIdx.y;
   const long long col = (long long)blockIdx.x * T + tx;
   const int phases = (p.K + T - 1) / T;
@@ -93,10 +98,14 @@ hipError_t launch_naive(const Problem &p, hipStream_t s) {
                        dim3(kNaiveX, kNaiveY), s, p, (int)rows);
 }
 
-hipError_t launch_tiled(int T, const Problem &p, hipStream_t s) {
+hipError_t launch_tiled(int T, bool padded, const Problem &p, hipStream_t s) {
   const long long gx = ceil_div(p.N, T);
   const long long tiles_m = ceil_div(p.M, T);
   const dim3 grid((unsigned)gx, clamp_grid_y(tiles_m));
+  if (padded) {
+    if (T != 32) return hipErrorInvalidValue;
+    return launch_kernel(tiled_kernel<32, 1>, grid, dim3(32, 32), s, p, (int)tiles_m);
+  }
   switch (T) {
     case 4: return launch_kernel(tiled_kernel<4>, grid, dim3(4, 4), s, p, (int)tiles_m);
     case 16: return launch_kernel(tiled_kernel<16>, grid, dim3(16, 16), s, p, (int)tiles_m);

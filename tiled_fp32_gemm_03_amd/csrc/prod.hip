@@ -555,6 +555,10 @@ using C6 = Tile<128, 128, 16, 2, 2, true>;
 using C7 = Tile<256, 128, 32, 4, 2, false>;
 using P8 = Tile<128, 128, 64, 2, 2, false>;  // small-K panel kernel, K <= 64
 using P9 = Tile<256, 128, 64, 4, 2, false>;  // small-K panel kernel, K <= 64
+using C10 = Tile<256, 256, 16, 4, 4, false>;
+using C11 = Tile<256, 256, 16, 4, 2, false>;
+using C12 = Tile<256, 256, 32, 4, 4, false>;
+
 
 enum Kind { kKloop, kPanel };
 
@@ -574,6 +578,9 @@ const Entry kEntries[] = {
     {{256, 128, 32, 4, 2, 1, "256x128x32_w4x2"}, kKloop},
     {{128, 128, 64, 2, 2, 2, "panel128x128_k64"}, kPanel},
     {{256, 128, 64, 4, 2, 1, "panel256x128_k64"}, kPanel},
+    {{256, 256, 16, 4, 4, 1, "256x256x16_w4x4"}, kKloop},
+    {{256, 256, 16, 4, 2, 1, "256x256x16_w4x2"}, kKloop},
+    {{256, 256, 32, 4, 4, 1, "256x256x32_w4x4"}, kKloop},
 };
 constexpr int kNumConfigs = sizeof(kEntries) / sizeof(kEntries[0]);
 constexpr int kRemainderConfig = 3;  // thin edge strips
@@ -640,6 +647,10 @@ hipError_t launch_one(int index, const Problem &p, hipStream_t s) {
     case 7: return launch_kloop<C7>(p, s);
     case 8: return launch_panel<P8>(p, s);
     case 9: return launch_panel<P9>(p, s);
+    case 10: return launch_kloop<C10>(p, s);
+    case 11: return launch_kloop<C11>(p, s);
+    case 12: return launch_kloop<C12>(p, s);
+
     default: return hipErrorInvalidValue;
   }
 }
@@ -665,12 +676,15 @@ bool prod_supports(int index, int M, int N, int K) {
 }
 
 // Shape-based choice from measurements on MI355X: the small-K panel kernel
-// for K <= 64 with many tiles; 256x128x16 for large squares; 64x64 tiles for
-// smaller problems so that every CU has work.
+// for K <= 64 with many tiles; 256x256x32 tiles (16 waves, one workgroup per
+// CU) once there is a tile for every CU; 256x128x16 below that; 64x64 tiles
+// for smaller problems so that every CU has work.
 int prod_choose(int M, int N, int K) {
+  const long long t256x256 = ceil_div(M, 256) * ceil_div(N, 256);
   const long long t256x128 = ceil_div(M, 256) * ceil_div(N, 128);
   const long long t64 = ceil_div(M, 64) * ceil_div(N, 64);
   if (K <= 64 && t256x128 >= 1024) return 9;
+  if (t256x256 >= 256) return 12;
   if (t256x128 >= 512) return 2;
   if (t64 >= 2048) return 4;
   return 3;
