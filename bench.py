@@ -85,6 +85,15 @@ def measure_mfma(g, stream) -> float:
     return g.gemm_f32_probe_mfma_flops(wgs, iters) / (ms * 1e-3) / 1e12
 
 
+def measure_valu(g, stream) -> float:
+    import torch
+    wgs, iters = 256 * 8, 500
+    buf = torch.zeros(wgs * 4, device="cuda:0")
+    ms, _ = time_launches(lambda: g.gemm_f32_probe_valu(wgs, iters, buf.data_ptr(), stream.cuda_stream),
+                          5, 2, stream)
+    return g.gemm_f32_probe_valu_flops(wgs, iters) / (ms * 1e-3) / 1e12
+
+
 def load_traffic(workload: str, config_label: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, or None when
     absent or taken on a different version of the production kernel."""
@@ -230,7 +239,10 @@ def main() -> int:
         log(f"HBM GB/s: {hbm}")
         pm = measure_mfma(g, stream)
         log(f"fp32 MFMA probe: {pm:.1f} TFLOP/s")
-        measured = {"hbm_gbps": hbm, "mfma_fp32_tflops": round(pm, 2)}
+        pv = measure_valu(g, stream)
+        log(f"fp32 vector FMA probe: {pv:.1f} TFLOP/s")
+        measured = {"hbm_gbps": hbm, "mfma_fp32_tflops": round(pm, 2),
+                    "valu_fp32_tflops": round(pv, 2)}
         result["measured_peaks"] = measured
         result["roofline"]["frac_of_measured_mfma"] = round(tflops / pm, 4)
 

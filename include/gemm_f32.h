@@ -80,7 +80,14 @@ extern "C" {
  * shared-memory bank-conflict remedy the pages point to (geek-doc.cn
  * section 五).  Same results as GEMM_F32_TILED32; a measurement rung. */
 #define GEMM_F32_TILED32_PAD 5
-#define GEMM_F32_NUM_VARIANTS 6
+/* Register-blocked kernel on the vector ALU (no matrix cores): 128 x 128
+ * workgroup tiles, 256 threads, each thread owns 8 x 8 outputs (four 4 x 4
+ * blocks) in registers and does 64 fp32 FMAs per k from 16 LDS values; A is
+ * stored k-major in LDS, two LDS stages, one barrier per 8-deep k step,
+ * out-of-range elements loaded as 0.  The "one thread, several outputs"
+ * step the pages point to (geek-doc.cn sections 三 and 五) without MFMA. */
+#define GEMM_F32_VALU 6
+#define GEMM_F32_NUM_VARIANTS 7
 
 /*
  * gemm_f32 -- C = A x B (overwrite), see the layout above.

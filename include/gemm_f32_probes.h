@@ -46,6 +46,19 @@ int gemm_f32_probe_stream(int kind, long long n, const float *x,
 int gemm_f32_probe_mfma(int workgroups, int iters, float *out, void *stream);
 long long gemm_f32_probe_mfma_flops(int workgroups, int iters);
 
+/*
+ * gemm_f32_probe_valu -- fp32 vector-ALU throughput probe, the compute roof
+ * of kernels that multiply-add on the vector ALU rather than on matrix cores:
+ * `workgroups` workgroups of 256 threads, each lane running `iters` loop
+ * trips of 8 rounds over 16 independent scalar fused multiply-add chains
+ * (v_fmac_f32, 128 per trip).  One float
+ * per wave is written to out (out must hold workgroups * 4 floats).
+ * workgroups >= 1, iters >= 1.  gemm_f32_probe_valu_flops returns the FLOPs
+ * such a call performs (2 per FMA per lane; -1 for invalid arguments).
+ */
+int gemm_f32_probe_valu(int workgroups, int iters, float *out, void *stream);
+long long gemm_f32_probe_valu_flops(int workgroups, int iters);
+
 #ifdef __cplusplus
 }
 #endif

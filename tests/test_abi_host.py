@@ -31,7 +31,8 @@ def test_headers_declare_expected_entry_points():
     names = set(_declared_functions())
     assert {"gemm_f32", "gemm_f32_ex", "gemm_f32_tile", "gemm_f32_num_configs",
             "gemm_f32_status_string", "gemm_f32_version", "gemm_f32_probe_stream",
-            "gemm_f32_probe_mfma", "gemm_f32_probe_mfma_flops"} <= names
+            "gemm_f32_probe_mfma", "gemm_f32_probe_mfma_flops", "gemm_f32_probe_valu",
+            "gemm_f32_probe_valu_flops"} <= names
 
 
 def test_every_declared_symbol_is_exported():
@@ -62,7 +63,7 @@ def test_validation_codes():
     assert _call(4, 4, 4, ldb=3) == bad_ld
     assert _call(4, 4, 4, ldc=3) == bad_ld
     assert _call(4, 4, 0, lda=0) == bad_ld          # lda >= max(1, K)
-    assert _call(4, 4, 4, variant=6) == bad_var
+    assert _call(4, 4, 4, variant=7) == bad_var
     assert _call(4, 4, 4, variant=-1) == bad_var
     assert _call(4, 4, 4, variant=2, config=99) == bad_cfg
     assert _call(4, 4, 4, variant=0, config=1) == bad_cfg
@@ -99,6 +100,12 @@ def test_probe_validation():
     assert lib.gemm_f32_probe_mfma(1, 1, None, None) == 3
     assert g.gemm_f32_probe_mfma_flops(2, 3) == 2 * 4 * 3 * 8 * (2 * 32 * 32 * 2)
     assert g.gemm_f32_probe_mfma_flops(0, 3) == -1
+    assert lib.gemm_f32_probe_valu(0, 1, 256, None) == 8
+    assert lib.gemm_f32_probe_valu(1, 0, 256, None) == 8
+    assert lib.gemm_f32_probe_valu(1, 1, None, None) == 3
+    assert lib.gemm_f32_probe_valu(1, 1, 258, None) == 6
+    assert g.gemm_f32_probe_valu_flops(2, 3) == 2 * 256 * 3 * 8 * 16 * 2
+    assert g.gemm_f32_probe_valu_flops(2, 0) == -1
 
 
 def test_tile_queries():
@@ -106,6 +113,11 @@ def test_tile_queries():
     for name, t in (("tiled", 16), ("tiled32", 32), ("tiled4", 4), ("tiled32_pad", 32)):
         q = g.gemm_f32_tile(name, -1, 100, 100, 100)
         assert (q["BM"], q["BN"], q["BK"], q["threads"]) == (t, t, t, t * t)
+    q = g.gemm_f32_tile("valu", -1, 100, 100, 100)
+    assert (q["BM"], q["BN"], q["BK"], q["threads"]) == (128, 128, 8, 256)
+    assert g.gemm_f32_num_configs("valu") >= 2
+    for i in range(g.gemm_f32_num_configs("valu")):
+        assert g.gemm_f32_tile("valu", i, 9, 9, 9)["config"] == i
     n = g.gemm_f32_num_configs("prod")
     assert n >= 3
     for i in range(n):
@@ -136,6 +148,8 @@ def test_package_load_model_matches_oracle_model():
         for v in ("tiled", "tiled32", "tiled4", "tiled32_pad"):
             t = g.gemm_f32_tile(v, -1, M, N, K)
             assert roofline.issued_load_elements(v, M, N, K, t) == model.tiled_loads(M, N, K, t["BM"])
+        t = g.gemm_f32_tile("valu", -1, M, N, K)
+        assert roofline.issued_load_elements("valu", M, N, K, t) == model.blocked_loads(M, N, K, 128, 128, 8)
         for i in range(g.gemm_f32_num_configs("prod")):
             try:
                 t = g.gemm_f32_tile("prod", i, M, N, K)

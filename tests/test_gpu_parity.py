@@ -18,7 +18,7 @@ torch = pytest.importorskip("torch")
 import oracle  # noqa: E402
 from gemm_inputs import WORKLOADS, make, make_workload  # noqa: E402
 
-LADDER = ("naive", "tiled", "tiled32", "tiled32_pad", "prod")
+LADDER = ("naive", "tiled", "tiled32", "tiled32_pad", "valu", "prod")
 
 
 @pytest.fixture(scope="module")
@@ -85,6 +85,19 @@ def _supported(g, cfg, M, N, K):
         return True
     except g.GemmError:
         return False
+
+
+def test_every_valu_config(g):
+    """Every register-budget entry of the VALU rung: the k loop rolled and
+    unrolled, K below, at and past one 8-deep step, ragged tiles."""
+    for cfg in range(g.gemm_f32_num_configs("valu")):
+        for (M, N, K) in [(257, 383, 129), (128, 128, 8), (1, 300, 7), (200, 1, 33),
+                          (300, 260, 17), (129, 131, 1)]:
+            print(f"case: valu config {cfg} {M}x{N}x{K}", flush=True)
+            a, b = make(M, N, K, "small_int", seed=cfg + M + K)
+            assert np.array_equal(_run(g, a, b, "valu", cfg), oracle.gemm(a, b)), (cfg, M, N, K)
+            a, b = make(M, N, K, "normal", seed=cfg + N + K)
+            _tol_check(_run(g, a, b, "valu", cfg), oracle.gemm(a, b), K, f"valu cfg {cfg}")
 
 
 def test_every_prod_config(g):
@@ -319,7 +332,7 @@ def test_full_size_tiled_sampled(g, name):
     w, a, b = make_workload(name)
     dev = _dev()
     ta, tb = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
-    for variant in ("tiled", "tiled32"):
+    for variant in ("tiled", "tiled32", "valu"):
         print(f"case: full-size {name} {variant}", flush=True)
         c = g.matmul(ta, tb, variant=variant)
         torch.cuda.synchronize()
@@ -390,5 +403,13 @@ def test_mfma_probe_runs(g):
     dev = _dev()
     out = torch.zeros(8 * 4, device=dev)
     g.gemm_f32_probe_mfma(8, 10, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item() and torch.all(out != 0).item()
+
+
+def test_valu_probe_runs(g):
+    dev = _dev()
+    out = torch.zeros(8 * 4, device=dev)
+    g.gemm_f32_probe_valu(8, 10, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert torch.isfinite(out).all().item() and torch.all(out != 0).item()

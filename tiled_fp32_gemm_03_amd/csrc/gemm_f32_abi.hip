@@ -11,7 +11,7 @@ using namespace gemm_f32_impl;
 
 namespace {
 
-constexpr int kTiledT[GEMM_F32_NUM_VARIANTS] = {0, 16, 0, 32, 4, 32};
+constexpr int kTiledT[GEMM_F32_NUM_VARIANTS] = {0, 16, 0, 32, 4, 32, 0};
 
 thread_local char t_last_error[256] = "";
 
@@ -30,7 +30,9 @@ int max1(int v) { return v > 1 ? v : 1; }
 
 int num_configs(int variant) {
   if (variant < 0 || variant >= GEMM_F32_NUM_VARIANTS) return 0;
-  return variant == GEMM_F32_PROD ? prod_num_configs() : 1;
+  if (variant == GEMM_F32_PROD) return prod_num_configs();
+  if (variant == GEMM_F32_VALU) return valu_num_configs();
+  return 1;
 }
 
 // Shape checks shared by the product and the tile query.
@@ -43,8 +45,11 @@ int resolve_config(int variant, int config, int M, int N, int K, int *out) {
   if (variant < 0 || variant >= GEMM_F32_NUM_VARIANTS)
     return GEMM_F32_BAD_VARIANT;
   if (config < -1 || config >= num_configs(variant)) return GEMM_F32_BAD_CONFIG;
-  if (config == -1)
-    config = variant == GEMM_F32_PROD ? prod_choose(M, N, K) : 0;
+  if (config == -1) {
+    if (variant == GEMM_F32_PROD) config = prod_choose(M, N, K);
+    else if (variant == GEMM_F32_VALU) config = valu_choose(M, N, K);
+    else config = 0;
+  }
   if (variant == GEMM_F32_PROD && !prod_supports(config, M, N, K))
     return GEMM_F32_BAD_CONFIG;
   *out = config;
@@ -83,6 +88,7 @@ extern "C" int gemm_f32_ex(int M, int N, int K, const float *A, int lda,
   if (K == 0) return launch_status(launch_zero(p, s), "zero fill");  // the empty sum
   if (variant == GEMM_F32_NAIVE) return launch_status(launch_naive(p, s), "naive");
   if (variant == GEMM_F32_PROD) return launch_status(launch_prod(chosen, p, s), "prod");
+  if (variant == GEMM_F32_VALU) return launch_status(launch_valu(chosen, p, s), "valu");
   return launch_status(
       launch_tiled(kTiledT[variant], variant == GEMM_F32_TILED32_PAD, p, s), "tiled");
 }
@@ -109,6 +115,8 @@ extern "C" int gemm_f32_tile(int variant, int config, int M, int N, int K,
   } else if (variant == GEMM_F32_PROD) {
     const ProdConfig &c = prod_config(chosen);
     bm = c.BM, bn = c.BN, bk = c.BK, nt = 64 * c.WGM * c.WGN;
+  } else if (variant == GEMM_F32_VALU) {
+    bm = bn = kValuTile, bk = kValuBK, nt = kValuThreads;
   } else {
     const int t = kTiledT[variant];
     bm = bn = bk = t, nt = t * t;

@@ -34,6 +34,13 @@ hipError_t launch_zero(const Problem &p, hipStream_t s);
 hipError_t launch_naive(const Problem &p, hipStream_t s);
 hipError_t launch_tiled(int T, bool padded, const Problem &p, hipStream_t s);
 
+// Register-blocked VALU kernel: 128 x 128 tiles, 256 threads, k step 8; its
+// launch-table entries differ only in register budget.
+constexpr int kValuTile = 128, kValuBK = 8, kValuThreads = 256;
+int valu_num_configs();
+int valu_choose(int M, int N, int K);
+hipError_t launch_valu(int index, const Problem &p, hipStream_t s);
+
 int prod_num_configs();
 const ProdConfig &prod_config(int index);
 int prod_choose(int M, int N, int K);

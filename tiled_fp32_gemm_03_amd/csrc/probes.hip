@@ -1,6 +1,6 @@
 // Measurement probes: HBM streaming passes (copy, fill and the pages' vector
-// add, mayulu.co "CUDA 编程系列之三", section 4) and an fp32 MFMA throughput
-// loop.  They give the roofline's measured denominators and a copy kernel of
+// add, mayulu.co "CUDA 编程系列之三", section 4) and fp32 MFMA and vector-ALU
+// FMA throughput loops.  They give the roofline's measured denominators and a copy kernel of
 // known traffic for counter calibration; they are not part of C = A x B.
 #include "gemm_f32.h"
 #include "gemm_f32_probes.h"
@@ -75,6 +75,34 @@ __global__ void __launch_bounds__(kMfmaThreads)
   if (lane == 0) out[blockIdx.x * (kMfmaThreads / 64) + (threadIdx.x >> 6)] = s;
 }
 
+constexpr int kValuChains = 16;
+constexpr int kValuRounds = 8;  // rounds per loop trip, so the branch is rare
+constexpr int kValuThreads = 256;
+
+// Independent scalar FMA chains per lane, acc = x * y + acc with x and y in
+// registers: the v_fmac_f32 form a register-blocked GEMM issues (never the
+// packed form: the library is built with packed fp32 disabled).  The chains
+// grow by about 1e-6 per round, so values stay finite for any iteration count.
+__global__ void __launch_bounds__(kValuThreads)
+    valu_probe_kernel(int iters, float *out) {
+  const int lane = threadIdx.x & 63;
+  const float x = 1e-3f + lane * 1e-7f;
+  const float y = 1e-3f - lane * 1e-7f;
+  float acc[kValuChains];
+#pragma unroll
+  for (int c = 0; c < kValuChains; ++c) acc[c] = (float)c;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int r = 0; r < kValuRounds; ++r)
+#pragma unroll
+      for (int c = 0; c < kValuChains; ++c) acc[c] = __builtin_fmaf(x, y, acc[c]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kValuChains; ++c) s += acc[c];
+  if (lane == 0) out[blockIdx.x * (kValuThreads / 64) + (threadIdx.x >> 6)] = s;
+}
+
 bool misaligned16(const void *p) {
   return (reinterpret_cast<std::uintptr_t>(p) & 15u) != 0;
 }
@@ -136,6 +164,23 @@ extern "C" int gemm_f32_probe_mfma(int workgroups, int iters, float *out,
   if (reinterpret_cast<std::uintptr_t>(out) & 3u) return GEMM_F32_MISALIGNED;
   hipError_t e = launch_kernel(mfma_probe_kernel, dim3(workgroups),
                                dim3(kMfmaThreads), static_cast<hipStream_t>(stream),
+                               iters, out);
+  return e == hipSuccess ? GEMM_F32_OK : GEMM_F32_LAUNCH_FAILED;
+}
+
+extern "C" long long gemm_f32_probe_valu_flops(int workgroups, int iters) {
+  if (workgroups < 1 || iters < 1) return -1;
+  return (long long)workgroups * kValuThreads * (long long)iters * kValuRounds *
+         kValuChains * 2;
+}
+
+extern "C" int gemm_f32_probe_valu(int workgroups, int iters, float *out,
+                                   void *stream) {
+  if (workgroups < 1 || iters < 1) return GEMM_F32_BAD_ARG;
+  if (out == nullptr) return GEMM_F32_NULL_PTR;
+  if (reinterpret_cast<std::uintptr_t>(out) & 3u) return GEMM_F32_MISALIGNED;
+  hipError_t e = launch_kernel(valu_probe_kernel, dim3(workgroups),
+                               dim3(kValuThreads), static_cast<hipStream_t>(stream),
                                iters, out);
   return e == hipSuccess ? GEMM_F32_OK : GEMM_F32_LAUNCH_FAILED;
 }

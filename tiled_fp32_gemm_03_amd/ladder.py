@@ -3,9 +3,11 @@
     python -m tiled_fp32_gemm_03_amd.ladder --workloads square_4096 \
         --variants naive,tiled,tiled32,prod --reps 10
 
-``--variants`` takes rung names (naive, tiled, tiled32, tiled4, prod) and,
-for the production rung, ``prod:<i>`` for launch-table entry i or
-``prod:all`` for every entry.  ``--copy-mib N`` first runs the streaming copy
+``--variants`` takes rung names (naive, tiled, tiled32, tiled32_pad, tiled4,
+valu, prod) and, for rungs with a launch table, ``<rung>:<i>`` for entry i or
+``<rung>:all`` for every entry.  ``--alu-probes`` first measures the fp32
+vector-FMA probe at 1, 2, 4, 8 and 16 waves per SIMD and the fp32 MFMA probe
+(the compute roofs of the VALU and MFMA rungs).  ``--copy-mib N`` first runs the streaming copy
 probe once over N MiB (a kernel of known traffic: N MiB read, N MiB written)
 so that memory counters collected over the same run can be calibrated.
 Before each record the tool launches a marker (a 3-float fill, which runs
@@ -55,6 +57,7 @@ def main(argv=None) -> int:
     ap.add_argument("--reps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--copy-mib", type=int, default=0)
+    ap.add_argument("--alu-probes", action="store_true")
     ap.add_argument("--max-naive-gflop", type=float, default=200.0,
                     help="skip the naive rung on workloads above this many GFLOP")
     args = ap.parse_args(argv)
@@ -99,6 +102,24 @@ def main(argv=None) -> int:
                           "ms": round(ms, 5)}), flush=True)
         del x, z
         torch.cuda.empty_cache()
+
+    if args.alu_probes:
+        simds = 4 * torch.cuda.get_device_properties(dev).multi_processor_count
+        for waves in (1, 2, 4, 8, 16):
+            wgs = waves * simds // 4  # 4 waves per 256-thread workgroup
+            iters = 1000
+            buf = torch.zeros(wgs * 4, device=dev)
+            ms = timed(lambda: g.gemm_f32_probe_valu(wgs, iters, buf.data_ptr(), s), 5, 2)
+            tf = g.gemm_f32_probe_valu_flops(wgs, iters) / (ms * 1e-3) / 1e12
+            print(json.dumps({"kernel": "probe_valu", "waves_per_simd": waves, "workgroups": wgs,
+                              "ms": round(ms, 5), "tflops": round(tf, 2)}), flush=True)
+        wgs, iters = simds, 2000
+        buf = torch.zeros(wgs * 4, device=dev)
+        ms = timed(lambda: g.gemm_f32_probe_mfma(wgs, iters, buf.data_ptr(), s), 5, 2)
+        tf = g.gemm_f32_probe_mfma_flops(wgs, iters) / (ms * 1e-3) / 1e12
+        print(json.dumps({"kernel": "probe_mfma", "workgroups": wgs, "ms": round(ms, 5),
+                          "tflops": round(tf, 2)}), flush=True)
+        del buf
 
     rows = []
     for wname in [w for w in args.workloads.split(",") if w]:
