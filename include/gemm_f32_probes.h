@@ -59,6 +59,18 @@ long long gemm_f32_probe_mfma_flops(int workgroups, int iters);
 int gemm_f32_probe_valu(int workgroups, int iters, float *out, void *stream);
 long long gemm_f32_probe_valu_flops(int workgroups, int iters);
 
+/*
+ * gemm_f32_probe_lds -- LDS read-bandwidth probe, the on-chip roof of the
+ * tiled kernels (their inner products read operands from LDS):
+ * `workgroups` workgroups of 256 threads, each holding 64 KiB of LDS and
+ * running `iters` trips of 8 conflict-free 128-bit reads per lane.  One
+ * float per wave is written to out (out must hold workgroups * 4 floats).
+ * workgroups >= 1, iters >= 1.  gemm_f32_probe_lds_bytes returns the bytes
+ * such a call reads from LDS (-1 for invalid arguments).
+ */
+int gemm_f32_probe_lds(int workgroups, int iters, float *out, void *stream);
+long long gemm_f32_probe_lds_bytes(int workgroups, int iters);
+
 #ifdef __cplusplus
 }
 #endif

@@ -32,7 +32,7 @@ def test_headers_declare_expected_entry_points():
     assert {"gemm_f32", "gemm_f32_ex", "gemm_f32_tile", "gemm_f32_num_configs",
             "gemm_f32_status_string", "gemm_f32_version", "gemm_f32_probe_stream",
             "gemm_f32_probe_mfma", "gemm_f32_probe_mfma_flops", "gemm_f32_probe_valu",
-            "gemm_f32_probe_valu_flops"} <= names
+            "gemm_f32_probe_valu_flops", "gemm_f32_probe_lds", "gemm_f32_probe_lds_bytes"} <= names
 
 
 def test_every_declared_symbol_is_exported():
@@ -106,6 +106,9 @@ def test_probe_validation():
     assert lib.gemm_f32_probe_valu(1, 1, 258, None) == 6
     assert g.gemm_f32_probe_valu_flops(2, 3) == 2 * 256 * 3 * 8 * 16 * 2
     assert g.gemm_f32_probe_valu_flops(2, 0) == -1
+    assert lib.gemm_f32_probe_lds(0, 1, 256, None) == 8
+    assert lib.gemm_f32_probe_lds(1, 1, None, None) == 3
+    assert g.gemm_f32_probe_lds_bytes(2, 3) == 2 * 256 * 3 * 8 * 16
 
 
 def test_tile_queries():

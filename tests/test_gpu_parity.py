@@ -413,3 +413,11 @@ def test_valu_probe_runs(g):
     g.gemm_f32_probe_valu(8, 10, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert torch.isfinite(out).all().item() and torch.all(out != 0).item()
+
+
+def test_lds_probe_runs(g):
+    dev = _dev()
+    out = torch.full((8 * 4,), -1.0, device=dev)
+    g.gemm_f32_probe_lds(8, 10, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item() and torch.all(out >= 0).item()

@@ -12,6 +12,7 @@ Raw C-ABI mirrors (same names and argument order as ``include/gemm_f32.h``):
   gemm_f32_probe_stream(kind, n, x, y, z, stream)      (include/gemm_f32_probes.h)
   gemm_f32_probe_mfma(workgroups, iters, out, stream), gemm_f32_probe_mfma_flops(...)
   gemm_f32_probe_valu(workgroups, iters, out, stream), gemm_f32_probe_valu_flops(...)
+  gemm_f32_probe_lds(workgroups, iters, out, stream), gemm_f32_probe_lds_bytes(...)
 Pointers are device addresses (ints); ``stream`` is a hipStream_t as int
 (0 = null stream).  A non-zero status raises ``GemmError``.
 
@@ -29,7 +30,7 @@ __all__ = [
     "gemm_f32", "gemm_f32_ex", "gemm_f32_tile", "gemm_f32_num_configs",
     "gemm_f32_status_string", "gemm_f32_version", "gemm_f32_last_error", "gemm_f32_probe_stream",
     "gemm_f32_probe_mfma", "gemm_f32_probe_mfma_flops", "gemm_f32_probe_valu",
-    "gemm_f32_probe_valu_flops", "matmul", "library_path",
+    "gemm_f32_probe_valu_flops", "gemm_f32_probe_lds", "gemm_f32_probe_lds_bytes", "matmul", "library_path",
     "exported_symbols",
 ]
 
@@ -67,6 +68,8 @@ _SIGS = {
     "gemm_f32_probe_mfma_flops": ([_i, _i], _ll),
     "gemm_f32_probe_valu": ([_i, _i, _p, _p], _i),
     "gemm_f32_probe_valu_flops": ([_i, _i], _ll),
+    "gemm_f32_probe_lds": ([_i, _i, _p, _p], _i),
+    "gemm_f32_probe_lds_bytes": ([_i, _i], _ll),
 }
 for _name, (_args, _ret) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -166,6 +169,15 @@ def gemm_f32_probe_valu(workgroups, iters, out, stream=0) -> None:
 
 def gemm_f32_probe_valu_flops(workgroups, iters) -> int:
     return int(_lib.gemm_f32_probe_valu_flops(int(workgroups), int(iters)))
+
+
+def gemm_f32_probe_lds(workgroups, iters, out, stream=0) -> None:
+    _check(_lib.gemm_f32_probe_lds(int(workgroups), int(iters), out or None, stream or None),
+           "gemm_f32_probe_lds")
+
+
+def gemm_f32_probe_lds_bytes(workgroups, iters) -> int:
+    return int(_lib.gemm_f32_probe_lds_bytes(int(workgroups), int(iters)))
 
 
 def config_name(variant, config: int = -1, M: int = 1, N: int = 1, K: int = 1) -> str:

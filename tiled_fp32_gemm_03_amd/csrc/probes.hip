@@ -103,6 +103,31 @@ __global__ void __launch_bounds__(kValuThreads)
   if (lane == 0) out[blockIdx.x * (kValuThreads / 64) + (threadIdx.x >> 6)] = s;
 }
 
+constexpr int kLdsThreads = 256;
+constexpr int kLdsVecs = 4096;  // 64 KiB of float4 per workgroup
+constexpr int kLdsReadsPerTrip = 8;
+
+// 128-bit LDS reads, conflict-free (consecutive lanes read consecutive
+// 16-byte words).  Each trip issues 8 independent reads 4 KiB apart and
+// folds them into a running sum; the window slides by one word per trip so
+// no read repeats an address of the trip before.
+__global__ void __launch_bounds__(kLdsThreads) lds_probe_kernel(int iters, float *out) {
+  __shared__ f32x4 buf[kLdsVecs];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kLdsVecs; i += kLdsThreads) buf[i] = f32x4{1.f, 0.f, 0.f, 0.f} * (float)(i & 7);
+  __syncthreads();
+  f32x4 acc{0.f, 0.f, 0.f, 0.f};
+  int base = 0;
+  for (int it = 0; it < iters; ++it) {
+    const f32x4 *p = buf + tid + base;  // highest index 255 + 255 + 7 * 256 < kLdsVecs
+#pragma unroll
+    for (int r = 0; r < kLdsReadsPerTrip; ++r) acc += p[r * kLdsThreads];
+    base = (base + 1) & (kLdsThreads - 1);
+  }
+  const float s = acc[0] + acc[1] + acc[2] + acc[3];
+  if ((tid & 63) == 0) out[blockIdx.x * (kLdsThreads / 64) + (tid >> 6)] = s;
+}
+
 bool misaligned16(const void *p) {
   return (reinterpret_cast<std::uintptr_t>(p) & 15u) != 0;
 }
@@ -182,5 +207,19 @@ extern "C" int gemm_f32_probe_valu(int workgroups, int iters, float *out,
   hipError_t e = launch_kernel(valu_probe_kernel, dim3(workgroups),
                                dim3(kValuThreads), static_cast<hipStream_t>(stream),
                                iters, out);
+  return e == hipSuccess ? GEMM_F32_OK : GEMM_F32_LAUNCH_FAILED;
+}
+
+extern "C" long long gemm_f32_probe_lds_bytes(int workgroups, int iters) {
+  if (workgroups < 1 || iters < 1) return -1;
+  return (long long)workgroups * kLdsThreads * (long long)iters * kLdsReadsPerTrip * 16;
+}
+
+extern "C" int gemm_f32_probe_lds(int workgroups, int iters, float *out, void *stream) {
+  if (workgroups < 1 || iters < 1) return GEMM_F32_BAD_ARG;
+  if (out == nullptr) return GEMM_F32_NULL_PTR;
+  if (reinterpret_cast<std::uintptr_t>(out) & 3u) return GEMM_F32_MISALIGNED;
+  hipError_t e = launch_kernel(lds_probe_kernel, dim3(workgroups), dim3(kLdsThreads),
+                               static_cast<hipStream_t>(stream), iters, out);
   return e == hipSuccess ? GEMM_F32_OK : GEMM_F32_LAUNCH_FAILED;
 }

@@ -6,8 +6,8 @@
 ``--variants`` takes rung names (naive, tiled, tiled32, tiled32_pad, tiled4,
 valu, prod) and, for rungs with a launch table, ``<rung>:<i>`` for entry i or
 ``<rung>:all`` for every entry.  ``--alu-probes`` first measures the fp32
-vector-FMA probe at 1, 2, 4, 8 and 16 waves per SIMD and the fp32 MFMA probe
-(the compute roofs of the VALU and MFMA rungs).  ``--copy-mib N`` first runs the streaming copy
+vector-FMA probe at 1, 2, 4, 8 and 16 waves per SIMD, the LDS read-bandwidth
+probe and the fp32 MFMA probe (the compute and on-chip roofs of the rungs).  ``--copy-mib N`` first runs the streaming copy
 probe once over N MiB (a kernel of known traffic: N MiB read, N MiB written)
 so that memory counters collected over the same run can be calibrated.
 Before each record the tool launches a marker (a 3-float fill, which runs
@@ -113,6 +113,15 @@ def main(argv=None) -> int:
             tf = g.gemm_f32_probe_valu_flops(wgs, iters) / (ms * 1e-3) / 1e12
             print(json.dumps({"kernel": "probe_valu", "waves_per_simd": waves, "workgroups": wgs,
                               "ms": round(ms, 5), "tflops": round(tf, 2)}), flush=True)
+        for wg_per_cu in (1, 2, 8):
+            wgs, iters = wg_per_cu * simds // 4, 2000
+            buf = torch.zeros(wgs * 4, device=dev)
+            ms = timed(lambda: g.gemm_f32_probe_lds(wgs, iters, buf.data_ptr(), s), 5, 2)
+            nbytes = g.gemm_f32_probe_lds_bytes(wgs, iters)
+            print(json.dumps({"kernel": "probe_lds", "workgroups": wgs, "ms": round(ms, 5),
+                              "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                              "bytes_per_cu_clock_at_2p4ghz": round(
+                                  nbytes / (ms * 1e-3) / (simds // 4) / 2.4e9, 1)}), flush=True)
         wgs, iters = simds, 2000
         buf = torch.zeros(wgs * 4, device=dev)
         ms = timed(lambda: g.gemm_f32_probe_mfma(wgs, iters, buf.data_ptr(), s), 5, 2)
