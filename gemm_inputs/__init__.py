@@ -28,7 +28,8 @@ from dataclasses import dataclass
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "draw", "make", "make_workload", "sha256"]
+__all__ = ["Workload", "WORKLOADS", "draw", "make", "make_workload", "sha256",
+           "to_code16", "make_mixed", "make_mixed_workload"]
 
 
 @dataclass(frozen=True)
@@ -99,6 +100,37 @@ def make(M: int, N: int, K: int, dist: str, seed: int) -> tuple[np.ndarray, np.n
 def make_workload(name: str) -> tuple[Workload, np.ndarray, np.ndarray]:
     w = WORKLOADS[name]
     a, b = make(w.M, w.N, w.K, w.dist, w.seed)
+    return w, a, b
+
+
+def to_code16(x: np.ndarray, fmt: str) -> np.ndarray:
+    """Round float32 values to 16-bit codes (uint16), nearest-even.
+
+    Input preparation for the 16-bit-input product, the step a caller takes
+    before handing matrices over; the product itself only reads the codes.
+    "f16": numpy's float32 -> float16 conversion.  "bf16": the upper half of
+    the binary32 word after adding half an ulp of the 16-bit result (ties to
+    even); inputs here are finite.
+    """
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    if fmt == "f16":
+        return x.astype(np.float16).view(np.uint16)
+    if fmt == "bf16":
+        u = x.view(np.uint32).astype(np.uint64)
+        return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    raise ValueError(f"unknown 16-bit format {fmt!r}")
+
+
+def make_mixed(M: int, N: int, K: int, dist: str, seed: int,
+               fmt: str) -> tuple[np.ndarray, np.ndarray]:
+    """The float32 pair of ``make`` rounded to 16-bit codes of ``fmt``."""
+    a, b = make(M, N, K, dist, seed)
+    return to_code16(a, fmt), to_code16(b, fmt)
+
+
+def make_mixed_workload(name: str, fmt: str) -> tuple[Workload, np.ndarray, np.ndarray]:
+    w = WORKLOADS[name]
+    a, b = make_mixed(w.M, w.N, w.K, w.dist, w.seed, fmt)
     return w, a, b
 
 

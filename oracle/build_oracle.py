@@ -26,7 +26,7 @@ def build(verbose: bool = False) -> str:
     if cc is None:
         raise RuntimeError("no C compiler (gcc) found to build the oracle")
     tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [cc, *CFLAGS, SRC, "-o", tmp]
+    cmd = [cc, *CFLAGS, SRC, "-o", tmp, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
