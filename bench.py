@@ -12,7 +12,6 @@ run, and the CPU oracle timed on a bounded sample as a reported baseline.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import platform
@@ -25,16 +24,10 @@ if ROOT not in sys.path:
 
 METRIC = "fp32 GEMM TFLOPS @N=4096 (% of fp32 peak); HBM GB/s on K=64 skinny shape"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-PROD_SOURCE = os.path.join(ROOT, "tiled_fp32_gemm_03_amd", "csrc", "prod.hip")
 
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
-
-
-def prod_source_digest() -> str:
-    with open(PROD_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
 def time_launches(fn, steps: int, warmup: int, stream) -> tuple[float, float]:
@@ -102,6 +95,8 @@ def load_traffic(workload: str, config_label: str):
             data = json.load(f)
     except (OSError, ValueError):
         return None
+    from tiled_fp32_gemm_03_amd.counters import prod_source_digest
+
     rec = data.get(workload)
     if not rec or rec.get("prod_source_sha256_16") != prod_source_digest():
         return None

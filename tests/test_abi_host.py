@@ -22,7 +22,7 @@ def _declared_functions():
             continue
         text = open(os.path.join(INCLUDE, fname)).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(gemm_f32\w*)\s*\(", text, re.M):
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(gemm_\w*)\s*\(", text, re.M):
             names.append(m.group(1))
     return names
 
@@ -32,7 +32,8 @@ def test_headers_declare_expected_entry_points():
     assert {"gemm_f32", "gemm_f32_ex", "gemm_f32_tile", "gemm_f32_num_configs",
             "gemm_f32_status_string", "gemm_f32_version", "gemm_f32_probe_stream",
             "gemm_f32_probe_mfma", "gemm_f32_probe_mfma_flops", "gemm_f32_probe_valu",
-            "gemm_f32_probe_valu_flops", "gemm_f32_probe_lds", "gemm_f32_probe_lds_bytes"} <= names
+            "gemm_f32_probe_valu_flops", "gemm_f32_probe_lds", "gemm_f32_probe_lds_bytes",
+            "gemm_mixed", "gemm_mixed_num_configs", "gemm_mixed_tile"} <= names
 
 
 def test_every_declared_symbol_is_exported():
@@ -78,6 +79,49 @@ def test_validation_codes():
     for code in range(0, 9):
         assert g.gemm_f32_status_string(code) != "unknown status"
     assert g.gemm_f32_status_string(1234) == "unknown status"
+
+
+def _mixed(M, N, K, A=0, lda=None, B=0, ldb=None, C=0, ldc=None, fmt=0, config=-1):
+    lda = max(1, K) if lda is None else lda
+    ldb = max(1, N) if ldb is None else ldb
+    ldc = max(1, N) if ldc is None else ldc
+    return g._lib.gemm_mixed(M, N, K, A or None, lda, B or None, ldb, C or None, ldc, fmt,
+                             config, None)
+
+
+def test_mixed_validation_codes():
+    ok, bad_dim, bad_ld, null, misal, bad_cfg, bad_arg = 0, 1, 2, 3, 6, 7, 8
+    assert _mixed(-1, 4, 4) == bad_dim
+    assert _mixed(4, 4, 4, lda=3) == bad_ld
+    assert _mixed(4, 4, 4, ldb=3) == bad_ld
+    assert _mixed(4, 4, 4, ldc=3) == bad_ld
+    assert _mixed(4, 4, 4, fmt=2) == bad_arg
+    assert _mixed(4, 4, 4, fmt=-1) == bad_arg
+    assert _mixed(4, 4, 4, config=g.gemm_mixed_num_configs()) == bad_cfg
+    assert _mixed(4, 4, 4, config=-2) == bad_cfg
+    assert _mixed(4, 4, 4) == null
+    assert _mixed(4, 4, 4, C=256) == null
+    assert _mixed(4, 4, 4, A=257, B=512, C=1024) == misal   # codes need 2-byte alignment
+    assert _mixed(4, 4, 4, A=256, B=513, C=1024) == misal
+    assert _mixed(4, 4, 4, A=256, B=512, C=1026) == misal   # C needs 4-byte alignment
+    assert _mixed(0, 4, 4) == ok
+    assert _mixed(4, 0, 4) == ok
+    with pytest.raises(ValueError):
+        g.gemm_mixed(4, 4, 4, 0, 4, 0, 4, 0, 4, "fp8")
+
+
+def test_mixed_tile_queries():
+    n = g.gemm_mixed_num_configs()
+    assert n >= 2
+    for i in range(n):
+        q = g.gemm_mixed_tile(i, 64, 64, 64)
+        assert q["config"] == i and q["BK"] == 64 and q["threads"] % 64 == 0
+        assert q["BM"] % 32 == 0 and q["BN"] % 32 == 0
+    assert g.gemm_mixed_tile(-1, 4096, 4096, 4096)["config"] in range(n)
+    with pytest.raises(g.GemmError):
+        g.gemm_mixed_tile(n, 64, 64, 64)
+    with pytest.raises(g.GemmError):
+        g.gemm_mixed_tile(-1, 64, -1, 64)
 
 
 def test_python_raw_wrapper_raises():

@@ -17,6 +17,8 @@ torch = pytest.importorskip("torch")
 
 import oracle  # noqa: E402
 from gemm_inputs import WORKLOADS, make, make_workload  # noqa: E402
+from parity_util import sample_indices as _sample_indices  # noqa: E402
+from parity_util import tol_check as _tol_check  # noqa: E402
 
 LADDER = ("naive", "tiled", "tiled32", "tiled32_pad", "valu", "prod")
 
@@ -29,18 +31,6 @@ def g():
 
 def _dev():
     return torch.device("cuda:0")
-
-
-def _tol_check(got: np.ndarray, ref: np.ndarray, K: int, what: str):
-    got64 = got.astype(np.float64)
-    ref64 = ref.astype(np.float64)
-    assert np.all(np.isfinite(got64)), f"{what}: non-finite output"
-    err = np.abs(got64 - ref64)
-    max_err = float(err.max()) if err.size else 0.0
-    denom = float(np.sqrt((ref64 ** 2).sum()))
-    fro = float(np.sqrt((err ** 2).sum())) / denom if denom > 0 else float(np.sqrt((err ** 2).sum()))
-    assert max_err <= 1e-4 * np.sqrt(max(K, 1)), f"{what}: max err {max_err:.3g} (K={K})"
-    assert fro <= 1e-5, f"{what}: relative Frobenius error {fro:.3g}"
 
 
 def _run(g, a, b, variant, config=-1):
@@ -290,22 +280,6 @@ def test_workload_square_1024_int_bit_exact(g, variant):
     got = _run(g, a, b, variant)
     ref = oracle.gemm(a, b)
     assert np.array_equal(got, ref)
-
-
-def _sample_indices(M, N, n, seed):
-    rng = np.random.default_rng(seed)
-    ii = [rng.integers(0, M, n)]
-    jj = [rng.integers(0, N, n)]
-    # whole first/last row and column (every edge tile), and the corners
-    for r in (0, M - 1):
-        cols = np.arange(N)
-        ii.append(np.full(N, r))
-        jj.append(cols)
-    for c in (0, N - 1):
-        rows = np.arange(M)
-        ii.append(rows)
-        jj.append(np.full(M, c))
-    return np.concatenate(ii).astype(np.int64), np.concatenate(jj).astype(np.int64)
 
 
 @pytest.mark.parametrize("name", ["square_4096", "ragged", "skinny_k64"])

@@ -13,12 +13,18 @@ Raw C-ABI mirrors (same names and argument order as ``include/gemm_f32.h``):
   gemm_f32_probe_mfma(workgroups, iters, out, stream), gemm_f32_probe_mfma_flops(...)
   gemm_f32_probe_valu(workgroups, iters, out, stream), gemm_f32_probe_valu_flops(...)
   gemm_f32_probe_lds(workgroups, iters, out, stream), gemm_f32_probe_lds_bytes(...)
+  gemm_mixed(M, N, K, A, lda, B, ldb, C, ldc, format, config, stream)
+  gemm_mixed_tile(config, M, N, K) -> dict, gemm_mixed_num_configs()
+                                                        (include/gemm_mixed.h)
 Pointers are device addresses (ints); ``stream`` is a hipStream_t as int
 (0 = null stream).  A non-zero status raises ``GemmError``.
 
-Tensor convenience: ``matmul(A, B, out=None, variant="prod", config=-1)``
+Tensor conveniences: ``matmul(A, B, out=None, variant="prod", config=-1)``
 takes float32 CUDA tensors whose last stride is 1 and passes ``stride(0)`` as
-the leading dimension, on torch's current stream.
+the leading dimension, on torch's current stream.  ``matmul_mixed(A, B,
+out=None, config=-1)`` does the same for bfloat16 or float16 tensors (fp32
+result); ``format`` names the 16-bit format when A and B hold raw codes
+(int16 / uint16).
 """
 from __future__ import annotations
 
@@ -30,7 +36,10 @@ __all__ = [
     "gemm_f32", "gemm_f32_ex", "gemm_f32_tile", "gemm_f32_num_configs",
     "gemm_f32_status_string", "gemm_f32_version", "gemm_f32_last_error", "gemm_f32_probe_stream",
     "gemm_f32_probe_mfma", "gemm_f32_probe_mfma_flops", "gemm_f32_probe_valu",
-    "gemm_f32_probe_valu_flops", "gemm_f32_probe_lds", "gemm_f32_probe_lds_bytes", "matmul", "library_path",
+    "gemm_f32_probe_valu_flops", "gemm_f32_probe_lds", "gemm_f32_probe_lds_bytes", "matmul",
+    "gemm_mixed", "gemm_mixed_tile", "gemm_mixed_num_configs", "matmul_mixed", "MIXED_FORMATS",
+    "mixed_config_name",
+    "library_path",
     "exported_symbols",
 ]
 
@@ -69,6 +78,9 @@ _SIGS = {
     "gemm_f32_probe_valu": ([_i, _i, _p, _p], _i),
     "gemm_f32_probe_valu_flops": ([_i, _i], _ll),
     "gemm_f32_probe_lds": ([_i, _i, _p, _p], _i),
+    "gemm_mixed": ([_i, _i, _i, _p, _i, _p, _i, _p, _i, _i, _i, _p], _i),
+    "gemm_mixed_num_configs": ([], _i),
+    "gemm_mixed_tile": ([_i, _i, _i, _i, _ip, _ip, _ip, _ip, _ip], _i),
     "gemm_f32_probe_lds_bytes": ([_i, _i], _ll),
 }
 for _name, (_args, _ret) in _SIGS.items():
@@ -80,6 +92,8 @@ for _name, (_args, _ret) in _SIGS.items():
 VARIANTS = {"naive": 0, "tiled": 1, "prod": 2, "tiled32": 3, "tiled4": 4, "tiled32_pad": 5,
             "valu": 6}
 PROBE_COPY, PROBE_FILL, PROBE_VADD = 0, 1, 2
+# Input formats of include/gemm_mixed.h.
+MIXED_FORMATS = {"bf16": 0, "f16": 1}
 
 
 class GemmError(RuntimeError):
@@ -180,12 +194,46 @@ def gemm_f32_probe_lds_bytes(workgroups, iters) -> int:
     return int(_lib.gemm_f32_probe_lds_bytes(int(workgroups), int(iters)))
 
 
+def _format(fmt) -> int:
+    if isinstance(fmt, str):
+        try:
+            return MIXED_FORMATS[fmt]
+        except KeyError:
+            raise ValueError(f"unknown 16-bit format {fmt!r}; one of {sorted(MIXED_FORMATS)}") from None
+    return int(fmt)
+
+
+def gemm_mixed(M, N, K, A, lda, B, ldb, C, ldc, format, config=-1, stream=0) -> None:
+    rc = _lib.gemm_mixed(M, N, K, A or None, lda, B or None, ldb, C or None, ldc,
+                         _format(format), int(config), stream or None)
+    _check(rc, "gemm_mixed")
+
+
+def gemm_mixed_num_configs() -> int:
+    return int(_lib.gemm_mixed_num_configs())
+
+
+def gemm_mixed_tile(config, M, N, K) -> dict:
+    vals = [ctypes.c_int(0) for _ in range(5)]
+    rc = _lib.gemm_mixed_tile(int(config), M, N, K, *[ctypes.byref(v) for v in vals])
+    _check(rc, "gemm_mixed_tile")
+    bm, bn, bk, nt, chosen = (v.value for v in vals)
+    return {"BM": bm, "BN": bn, "BK": bk, "threads": nt, "config": chosen}
+
+
 def config_name(variant, config: int = -1, M: int = 1, N: int = 1, K: int = 1) -> str:
     """Readable name of a launch-table entry, e.g. "prod#0:128x128x32/256t"."""
     t = gemm_f32_tile(variant, config, M, N, K)
     v = _variant(variant)
     vname = next(k for k, val in VARIANTS.items() if val == v)
     return f"{vname}#{t['config']}:{t['BM']}x{t['BN']}x{t['BK']}/{t['threads']}t"
+
+
+def mixed_config_name(fmt, config: int = -1, M: int = 1, N: int = 1, K: int = 1) -> str:
+    """Readable name of a gemm_mixed entry, e.g. "bf16#0:256x256x64/512t"."""
+    t = gemm_mixed_tile(config, M, N, K)
+    f = next(k for k, val in MIXED_FORMATS.items() if val == _format(fmt))
+    return f"{f}#{t['config']}:{t['BM']}x{t['BN']}x{t['BK']}/{t['threads']}t"
 
 
 def _ld(t) -> int:
@@ -220,4 +268,43 @@ def matmul(A, B, out=None, variant="prod", config: int = -1, stream=None):
     ldc = max(_ld(out), max(1, N))
     gemm_f32_ex(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, out.data_ptr(), ldc,
                 variant, config, stream)
+    return out
+
+
+def matmul_mixed(A, B, out=None, config: int = -1, stream=None, format=None):
+    """C = A x B on the GPU for bfloat16 or float16 tensors, fp32 result.
+
+    A and B must share one 16-bit dtype (or be int16 / uint16 codes with
+    ``format`` given) and have unit last stride.
+    """
+    import torch
+
+    kinds = {torch.bfloat16: "bf16", torch.float16: "f16"}
+    if A.dtype != B.dtype:
+        raise TypeError("A and B must have the same dtype")
+    if A.dtype in kinds:
+        fmt = kinds[A.dtype] if format is None else format
+        if format is not None and _format(format) != MIXED_FORMATS[kinds[A.dtype]]:
+            raise TypeError(f"format {format!r} does not match dtype {A.dtype}")
+    elif A.dtype in (torch.int16, torch.uint16) and format is not None:
+        fmt = format
+    else:
+        raise TypeError("A and B must be bfloat16 / float16 tensors (or 16-bit codes with format=)")
+    if not (A.is_cuda and B.is_cuda):
+        raise TypeError("A and B must be CUDA tensors")
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {tuple(A.shape)} x {tuple(B.shape)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (M, N) or not out.is_cuda:
+        raise TypeError("out must be a float32 CUDA tensor of shape (M, N)")
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device).cuda_stream
+    lda = max(_ld(A), max(1, K))
+    ldb = max(_ld(B), max(1, N))
+    ldc = max(_ld(out), max(1, N))
+    gemm_mixed(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, out.data_ptr(), ldc, fmt,
+               config, stream)
     return out

@@ -20,7 +20,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgemm_f32.so")
 ARCH = "gfx950"
 
-SOURCES = ["gemm_f32_abi.hip", "naive_tiled.hip", "prod.hip", "valu.hip", "probes.hip"]
+SOURCES = ["gemm_f32_abi.hip", "naive_tiled.hip", "prod.hip", "valu.hip", "mixed.hip", "probes.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

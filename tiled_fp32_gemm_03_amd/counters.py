@@ -37,13 +37,20 @@ import sys
 from collections import OrderedDict, defaultdict
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-PROD_SOURCE = os.path.join(HERE, "csrc", "prod.hip")
-OUR_KERNELS = re.compile(r"(gemm_f32_impl|prod_kernel|naive_kernel|tiled_kernel|stream_kernel|stream_tail|mfma_probe_kernel|zero_kernel)")
+# Sources that define the production kernel's code.
+PROD_SOURCES = [os.path.join(HERE, "csrc", n) for n in ("prod.hip", "tile_order.hpp")]
+OUR_KERNELS = re.compile(r"(gemm_f32_impl|prod_kernel|panel_kernel|strip_kernel|naive_kernel|tiled_kernel|"
+                         r"valu_kernel|mixed_kernel|stream_kernel|stream_tail|mfma_probe_kernel|"
+                         r"valu_probe_kernel|lds_probe_kernel|zero_kernel)")
 
 
 def prod_source_digest() -> str:
-    with open(PROD_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Digest of the production kernel's sources, stamped on measured traffic."""
+    h = hashlib.sha256()
+    for path in PROD_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def short_name(name: str) -> str:

@@ -3,6 +3,7 @@
 // error is returned before anything is enqueued.
 #include "gemm_f32.h"
 #include "gemm_internal.hpp"
+#include "gemm_mixed.h"
 
 #include <cstdint>
 #include <cstdio>
@@ -125,6 +126,64 @@ extern "C" int gemm_f32_tile(int variant, int config, int M, int N, int K,
   if (BN) *BN = bn;
   if (BK) *BK = bk;
   if (threads) *threads = nt;
+  if (chosen_config) *chosen_config = chosen;
+  return GEMM_F32_OK;
+}
+
+// ---- 16-bit inputs ---------------------------------------------------------
+
+namespace {
+
+int mixed_resolve(int config, int M, int N, int K, int *out) {
+  if (config < -1 || config >= mixed_num_configs()) return GEMM_F32_BAD_CONFIG;
+  *out = config == -1 ? mixed_choose(M, N, K) : config;
+  return GEMM_F32_OK;
+}
+
+bool misaligned2(const void *p) {
+  return (reinterpret_cast<std::uintptr_t>(p) & 1u) != 0;
+}
+
+}  // namespace
+
+extern "C" int gemm_mixed(int M, int N, int K, const void *A, int lda, const void *B,
+                          int ldb, float *C, int ldc, int format, int config,
+                          void *stream) {
+  int rc = check_shape(M, N, K);
+  if (rc != GEMM_F32_OK) return rc;
+  if (lda < max1(K) || ldb < max1(N) || ldc < max1(N)) return GEMM_F32_INVALID_LD;
+  if (format != GEMM_MIXED_BF16 && format != GEMM_MIXED_F16) return GEMM_F32_BAD_ARG;
+  int chosen = 0;
+  rc = mixed_resolve(config, M, N, K, &chosen);
+  if (rc != GEMM_F32_OK) return rc;
+  if (M == 0 || N == 0) return GEMM_F32_OK;
+  if (C == nullptr) return GEMM_F32_NULL_PTR;
+  if (K > 0 && (A == nullptr || B == nullptr)) return GEMM_F32_NULL_PTR;
+  if (misaligned(C) || (K > 0 && (misaligned2(A) || misaligned2(B))))
+    return GEMM_F32_MISALIGNED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (K == 0) return launch_status(launch_zero_f32(C, M, N, ldc, s), "zero fill");
+  const MixedProblem p{M, N, K, static_cast<const uint16_t *>(A), lda,
+                       static_cast<const uint16_t *>(B), ldb, C, ldc};
+  return launch_status(
+      launch_mixed(format == GEMM_MIXED_BF16 ? kMixedBf16 : kMixedF16, chosen, p, s),
+      "mixed");
+}
+
+extern "C" int gemm_mixed_num_configs(void) { return mixed_num_configs(); }
+
+extern "C" int gemm_mixed_tile(int config, int M, int N, int K, int *BM, int *BN, int *BK,
+                               int *threads, int *chosen_config) {
+  int rc = check_shape(M, N, K);
+  if (rc != GEMM_F32_OK) return rc;
+  int chosen = 0;
+  rc = mixed_resolve(config, M, N, K, &chosen);
+  if (rc != GEMM_F32_OK) return rc;
+  const MixedConfig &c = mixed_config(chosen);
+  if (BM) *BM = c.BM;
+  if (BN) *BN = c.BN;
+  if (BK) *BK = c.BK;
+  if (threads) *threads = 64 * c.WGM * c.WGN;
   if (chosen_config) *chosen_config = chosen;
   return GEMM_F32_OK;
 }

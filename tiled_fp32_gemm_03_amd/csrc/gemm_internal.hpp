@@ -41,6 +41,33 @@ int valu_num_configs();
 int valu_choose(int M, int N, int K);
 hipError_t launch_valu(int index, const Problem &p, hipStream_t s);
 
+// One product with 16-bit inputs (codes of kMixedBf16 or kMixedF16) and an
+// fp32 result, row-major with leading dimensions (elements).
+struct MixedProblem {
+  int M, N, K;
+  const uint16_t *A;
+  long long lda;
+  const uint16_t *B;
+  long long ldb;
+  float *C;
+  long long ldc;
+};
+
+constexpr int kMixedBf16 = 0, kMixedF16 = 1;
+
+struct MixedConfig {
+  int BM, BN, BK;
+  int WGM, WGN;   // waves along M and N (threads = 64 * WGM * WGN)
+  int occupancy;  // workgroups per CU that fit in LDS
+  const char *name;
+};
+
+int mixed_num_configs();
+const MixedConfig &mixed_config(int index);
+int mixed_choose(int M, int N, int K);
+hipError_t launch_mixed(int format, int index, const MixedProblem &p, hipStream_t s);
+hipError_t launch_zero_f32(float *C, int M, int N, long long ldc, hipStream_t s);
+
 int prod_num_configs();
 const ProdConfig &prod_config(int index);
 int prod_choose(int M, int N, int K);

@@ -91,6 +91,11 @@ hipError_t launch_zero(const Problem &p, hipStream_t s) {
   return launch_kernel(zero_kernel, dim3((unsigned)blocks), dim3(256), s, p);
 }
 
+hipError_t launch_zero_f32(float *C, int M, int N, long long ldc, hipStream_t s) {
+  const Problem p{M, N, 0, nullptr, 1, nullptr, 1, C, ldc};
+  return launch_zero(p, s);
+}
+
 hipError_t launch_naive(const Problem &p, hipStream_t s) {
   const long long gx = ceil_div(p.N, kNaiveX);
   const long long rows = ceil_div(p.M, kNaiveY);

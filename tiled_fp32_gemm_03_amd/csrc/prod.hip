@@ -55,6 +55,7 @@
 // tiles sharing an XCD's L2 also share A rows and B columns.
 #include "gemm_internal.hpp"
 #include "launch_util.hpp"
+#include "tile_order.hpp"
 
 #include <atomic>
 #include <cstdint>
@@ -68,8 +69,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kPadA = 4;  // floats after each LDS row of A (k-contiguous rows)
 constexpr int kPadB = 8;  // floats after each LDS row of B (n-contiguous rows)
-constexpr int kXcds = 8;
-constexpr int kGroupRows = 8;
 
 template <int BM_, int BN_, int BK_, int WGM_, int WGN_, bool NT_STORE_>
 struct Tile {
@@ -96,25 +95,6 @@ struct Tile {
 };
 
 constexpr int kLdsBytes = 160 * 1024;  // LDS of one gfx950 CU
-
-// Launch index -> logical id: each XCD gets a contiguous run of ids.
-__device__ inline int xcd_remap(int b, int G) {
-  const int per = G / kXcds, rem = G % kXcds, x = b % kXcds;
-  return x * per + (x < rem ? x : rem) + b / kXcds;
-}
-
-// Tile id -> (tile row, tile column), in groups of kGroupRows tile rows
-// walked column by column.
-__device__ inline void tile_coords(int lid, int tiles_m, int tiles_n, int &tm,
-                                   int &tn) {
-  const int per_group = kGroupRows * tiles_n;
-  const int g = lid / per_group;
-  const int first = g * kGroupRows;
-  const int rows = tiles_m - first < kGroupRows ? tiles_m - first : kGroupRows;
-  const int r = lid - g * per_group;
-  tm = first + r % rows;
-  tn = r / rows;
-}
 
 template <class S>
 struct Stage {

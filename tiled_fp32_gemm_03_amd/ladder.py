@@ -4,8 +4,10 @@
         --variants naive,tiled,tiled32,prod --reps 10
 
 ``--variants`` takes rung names (naive, tiled, tiled32, tiled32_pad, tiled4,
-valu, prod) and, for rungs with a launch table, ``<rung>:<i>`` for entry i or
-``<rung>:all`` for every entry.  ``--alu-probes`` first measures the fp32
+valu, prod, and the 16-bit-input rungs bf16 and f16) and, for rungs with a
+launch table, ``<rung>:<i>`` for entry i or ``<rung>:all`` for every entry.
+The 16-bit rungs take each workload rounded to their format (the seeded
+generator's rounding) and report against the dense bf16/fp16 matrix peak.  ``--alu-probes`` first measures the fp32
 vector-FMA probe at 1, 2, 4, 8 and 16 waves per SIMD, the LDS read-bandwidth
 probe and the fp32 MFMA probe (the compute and on-chip roofs of the rungs).  ``--copy-mib N`` first runs the streaming copy
 probe once over N MiB (a kernel of known traffic: N MiB read, N MiB written)
@@ -33,6 +35,13 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 
+MIXED = ("bf16", "f16")
+
+
+def _num_configs(g, name: str) -> int:
+    return g.gemm_mixed_num_configs() if name in MIXED else g.gemm_f32_num_configs(name)
+
+
 def _expand_variants(spec: str, g) -> list[tuple[str, int]]:
     out = []
     for item in spec.split(","):
@@ -42,7 +51,7 @@ def _expand_variants(spec: str, g) -> list[tuple[str, int]]:
         if ":" in item:
             name, cfg = item.split(":", 1)
             if cfg == "all":
-                out += [(name, i) for i in range(g.gemm_f32_num_configs(name))]
+                out += [(name, i) for i in range(_num_configs(g, name))]
             else:
                 out.append((name, int(cfg)))
         else:
@@ -62,10 +71,11 @@ def main(argv=None) -> int:
                     help="skip the naive rung on workloads above this many GFLOP")
     args = ap.parse_args(argv)
 
+    import numpy as np
     import torch
 
     import tiled_fp32_gemm_03_amd as g
-    from gemm_inputs import make_workload
+    from gemm_inputs import make_mixed_workload, make_workload
     from tiled_fp32_gemm_03_amd import roofline as rf
 
     dev = torch.device("cuda:0")
@@ -131,47 +141,66 @@ def main(argv=None) -> int:
         del buf
 
     rows = []
+    specs = _expand_variants(args.variants, g)
     for wname in [w for w in args.workloads.split(",") if w]:
+        fmts = sorted({v for v, _ in specs if v in MIXED})
         w, a, b = make_workload(wname)
-        ta, tb = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+        ops = {"f32": (torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev))}
+        for fmt in fmts:
+            _, a16, b16 = make_mixed_workload(wname, fmt)
+            ops[fmt] = (torch.from_numpy(a16.view(np.int16)).to(dev),
+                        torch.from_numpy(b16.view(np.int16)).to(dev))
+        del a, b
         tc = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
-        for vname, cfg in _expand_variants(args.variants, g):
+        for vname, cfg in specs:
             gflop = rf.flops(w.M, w.N, w.K) / 1e9
             if vname == "naive" and gflop > args.max_naive_gflop:
                 continue
+            mixed = vname in MIXED
             try:
-                tile = g.gemm_f32_tile(vname, cfg, w.M, w.N, w.K)
+                tile = (g.gemm_mixed_tile(cfg, w.M, w.N, w.K) if mixed
+                        else g.gemm_f32_tile(vname, cfg, w.M, w.N, w.K))
             except g.GemmError:  # entry does not accept this shape (small-K entries)
                 continue
-            label = g.config_name(vname, cfg, w.M, w.N, w.K)
+            label = (g.mixed_config_name(vname, cfg, w.M, w.N, w.K) if mixed
+                     else g.config_name(vname, cfg, w.M, w.N, w.K))
             reps = args.reps if vname != "naive" else max(1, min(args.reps, 3))
             print(f"[ladder] {wname} {label} reps={reps}", file=sys.stderr, flush=True)
+            ta, tb = ops[vname if mixed else "f32"]
 
-            def call():
-                g.gemm_f32_ex(w.M, w.N, w.K, ta.data_ptr(), w.K, tb.data_ptr(), w.N,
-                              tc.data_ptr(), w.N, vname, cfg, s)
+            if mixed:
+                def call():
+                    g.gemm_mixed(w.M, w.N, w.K, ta.data_ptr(), w.K, tb.data_ptr(), w.N,
+                                 tc.data_ptr(), w.N, vname, cfg, s)
+            else:
+                def call():
+                    g.gemm_f32_ex(w.M, w.N, w.K, ta.data_ptr(), w.K, tb.data_ptr(), w.N,
+                                  tc.data_ptr(), w.N, vname, cfg, s)
 
             mark()
 
             ms = timed(call, reps, args.warmup if vname != "naive" else min(args.warmup, 1))
             tflops = rf.flops(w.M, w.N, w.K) / (ms * 1e-3) / 1e12
+            peak = rf.PEAK_BF16_MFMA_TFLOPS if mixed else rf.PEAK_FP32_MFMA_TFLOPS
+            elem = 2 if mixed else 4
             rec = {"workload": wname, "kernel": label, "variant": vname, "config": tile["config"],
                    "ms": round(ms, 5), "tflops": round(tflops, 3),
-                   "frac_peak_fp32": round(tflops / rf.PEAK_FP32_MFMA_TFLOPS, 4),
-                   "gbps_compulsory": round(rf.compulsory_bytes(w.M, w.N, w.K) / (ms * 1e-3) / 1e9, 1),
-                   "model_issued_load_bytes": 4 * rf.issued_load_elements(vname, w.M, w.N, w.K, tile),
+                   "frac_peak": round(tflops / peak, 4), "peak_tflops": peak,
+                   "gbps_compulsory": round(rf.compulsory_bytes(w.M, w.N, w.K, elem) / (ms * 1e-3) / 1e9, 1),
+                   "model_issued_load_bytes": elem * rf.issued_load_elements(
+                       "prod" if mixed else vname, w.M, w.N, w.K, tile),
                    "flops": rf.flops(w.M, w.N, w.K)}
             rows.append(rec)
             print(json.dumps(rec), flush=True)
-        del ta, tb, tc
+        del ops, tc
         torch.cuda.empty_cache()
 
-    print("\n| workload | kernel | ms | TFLOP/s | % fp32 peak | GB/s (compulsory) |", file=sys.stderr)
+    print("\n| workload | kernel | ms | TFLOP/s | % of dtype peak | GB/s (compulsory) |", file=sys.stderr)
     print("|---|---|---|---|---|---|", file=sys.stderr)
     for r in rows:
         print(f"| {r['workload']} | {r['kernel']} | {r['ms']:.4f} | {r['tflops']:.2f} | "
-              f"{100 * r['frac_peak_fp32']:.1f} | {r['gbps_compulsory']:.0f} |", file=sys.stderr)
+              f"{100 * r['frac_peak']:.1f} | {r['gbps_compulsory']:.0f} |", file=sys.stderr)
     return 0
 
 

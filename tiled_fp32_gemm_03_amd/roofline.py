@@ -18,6 +18,7 @@ from __future__ import annotations
 # MI355X published peaks (dense, no sparsity).
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_FP32_VALU_TFLOPS = 157.3
+PEAK_BF16_MFMA_TFLOPS = 2500.0  # also fp16
 PEAK_HBM_GBPS = 8000.0
 CUS = 256
 CLOCK_GHZ = 2.4
@@ -27,8 +28,9 @@ def flops(M: int, N: int, K: int) -> int:
     return 2 * M * N * K
 
 
-def compulsory_bytes(M: int, N: int, K: int) -> int:
-    return 4 * (M * K + K * N + M * N)
+def compulsory_bytes(M: int, N: int, K: int, in_bytes: int = 4) -> int:
+    """A and B read once (``in_bytes`` per element), fp32 C written once."""
+    return in_bytes * (M * K + K * N) + 4 * M * N
 
 
 def intensity(M: int, N: int, K: int) -> float:
