@@ -16,6 +16,9 @@ seeds fixed for this project:
   square_4096     4096^3, uniform[-1, 1], seed 2 (the pages' worked size)
   ragged          M=4097, N=4095, K=2049, standard normal, seed 3
   skinny_k64      M=N=16384, K=64, uniform[-1, 1], seed 4
+  deep_k          M=N=256, K=16384, uniform[-1, 1], seed 5 -- not one of the
+                  benchmark's configurations: a deep-K product with fewer
+                  output tiles than compute units, the case K-splitting is for
 
 Generator.  numpy's PCG64 via ``numpy.random.default_rng(seed)``; A is drawn
 first and B second from the same generator.  Matrices are returned as
@@ -62,6 +65,8 @@ WORKLOADS: dict[str, Workload] = {
                  "ragged M=4097 N=4095 K=2049, A,B ~ N(0,1), seed 3"),
         Workload("skinny_k64", 16384, 16384, 64, "uniform", 4,
                  "skinny M=N=16384 K=64, A,B ~ U[-1,1], seed 4"),
+        Workload("deep_k", 256, 256, 16384, "uniform", 5,
+                 "deep-K M=N=256 K=16384, A,B ~ U[-1,1], seed 5"),
     )
 }
 

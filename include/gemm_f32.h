@@ -50,6 +50,8 @@ extern "C" {
                                     valid for this shape (small-K entries
                                     need K <= their BK)                      */
 #define GEMM_F32_BAD_ARG 8       /* other invalid argument (query helpers)  */
+#define GEMM_F32_BAD_WORKSPACE 9 /* split-K workspace NULL, too small or not
+                                    4-byte aligned                          */
 
 /* ---- variants: the kernel ladder ------------------------------------ */
 /* One thread per output element, operands read straight from global
@@ -117,6 +119,46 @@ int gemm_f32(int M, int N, int K, const float *A, int lda, const float *B,
 int gemm_f32_ex(int M, int N, int K, const float *A, int lda, const float *B,
                 int ldb, float *C, int ldc, int variant, int config,
                 void *stream);
+
+/*
+ * ---- split-K ---------------------------------------------------------------
+ * The pages tie the choice of tile size to occupancy (geek-doc.cn "矩阵乘法
+ * tiling", section 六: block size interacts with occupancy, bank conflicts
+ * and register pressure; mayulu.co "CUDA 编程系列之三", section 7: on-chip
+ * memory per block is taken from occupancy).  This entry extends that
+ * trade-off to products with fewer output tiles than the GPU has compute
+ * units: instead of shrinking the tile, K is cut into chunks of kc values.  Workgroup (tile, chunk) computes the production kernel's tile
+ * over its chunk into slab `chunk` of a workspace; a second kernel on the
+ * same stream sums the slabs in chunk order into C.  The result is
+ * deterministic for a given plan; it re-associates the k sum differently
+ * from gemm_f32, so on non-integer inputs the two differ by rounding.
+ *
+ * gemm_f32_splitk_plan -- the plan gemm_f32_splitk would use (host only).
+ *   config  -1 = automatic (128x128x32 tiles, 64x64 for outputs below
+ *           128x128), or a production k-loop entry (small-K panel and
+ *           non-temporal-store entries are refused with GEMM_F32_BAD_CONFIG).
+ *   splits  0 = automatic (one workgroup per CU where K allows at least four
+ *           k steps per chunk; products with a tile per CU, or with fewer
+ *           than 32 k steps, are not split),
+ *           else the requested count, capped at one k step per chunk.
+ *   Writes the entry, the chunks actually used (1 means a plain product;
+ *   with config -1 it then runs the entry gemm_f32 would choose),
+ *   kc, and the workspace bytes needed (splits * M * N * 4, or 0 for one
+ *   chunk).  Any output pointer may be NULL.
+ *
+ * gemm_f32_splitk -- C = A x B through that plan.  Arguments as gemm_f32_ex,
+ * plus a device workspace of workspace_bytes (4-byte aligned, not
+ * overlapping A, B or C; may be NULL when the plan needs none).  The
+ * workspace's contents are overwritten and need no initialisation.
+ * Returns GEMM_F32_BAD_WORKSPACE when it is missing or too small.
+ */
+int gemm_f32_splitk_plan(int M, int N, int K, int config, int splits,
+                         int *config_out, int *splits_out, int *kc_out,
+                         long long *workspace_bytes);
+int gemm_f32_splitk(int M, int N, int K, const float *A, int lda,
+                    const float *B, int ldb, float *C, int ldc, int config,
+                    int splits, void *workspace, long long workspace_bytes,
+                    void *stream);
 
 /* Number of launch-table entries of a variant (0 for an unknown variant). */
 int gemm_f32_num_configs(int variant);

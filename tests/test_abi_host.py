@@ -33,7 +33,8 @@ def test_headers_declare_expected_entry_points():
             "gemm_f32_status_string", "gemm_f32_version", "gemm_f32_probe_stream",
             "gemm_f32_probe_mfma", "gemm_f32_probe_mfma_flops", "gemm_f32_probe_valu",
             "gemm_f32_probe_valu_flops", "gemm_f32_probe_lds", "gemm_f32_probe_lds_bytes",
-            "gemm_mixed", "gemm_mixed_num_configs", "gemm_mixed_tile"} <= names
+            "gemm_mixed", "gemm_mixed_num_configs", "gemm_mixed_tile", "gemm_f32_splitk",
+            "gemm_f32_splitk_plan"} <= names
 
 
 def test_every_declared_symbol_is_exported():
@@ -76,7 +77,7 @@ def test_validation_codes():
     # empty output: nothing to do, no pointers needed, nothing launched
     assert _call(0, 4, 4) == ok
     assert _call(4, 0, 4) == ok
-    for code in range(0, 9):
+    for code in range(0, 10):
         assert g.gemm_f32_status_string(code) != "unknown status"
     assert g.gemm_f32_status_string(1234) == "unknown status"
 
@@ -122,6 +123,60 @@ def test_mixed_tile_queries():
         g.gemm_mixed_tile(n, 64, 64, 64)
     with pytest.raises(g.GemmError):
         g.gemm_mixed_tile(-1, 64, -1, 64)
+
+
+def test_splitk_plans():
+    # an under-filled product is split, one workgroup per CU, four k steps deep at least
+    p = g.gemm_f32_splitk_plan(1024, 1024, 1024)
+    t = g.gemm_f32_tile("prod", p["config"], 1024, 1024, 1024)
+    tiles = -(-1024 // t["BM"]) * -(-1024 // t["BN"])
+    assert p["splits"] > 1 and p["kc"] % t["BK"] == 0 and p["kc"] >= 4 * t["BK"]
+    assert tiles * p["splits"] <= 2 * 256
+    assert (p["splits"] - 1) * p["kc"] < 1024 <= p["splits"] * p["kc"]
+    assert p["workspace_bytes"] == p["splits"] * 1024 * 1024 * 4
+    # a product with a tile for every CU is not split and needs no workspace
+    p = g.gemm_f32_splitk_plan(4096, 4096, 4096)
+    assert p["splits"] == 1 and p["workspace_bytes"] == 0
+    # explicit counts are honoured up to one k step per split
+    t0 = g.gemm_f32_tile("prod", 0, 1, 1, 1)
+    p = g.gemm_f32_splitk_plan(300, 300, 100, 0, 64)
+    assert p["splits"] == -(-100 // t0["BK"]) and p["kc"] == t0["BK"]
+    p = g.gemm_f32_splitk_plan(300, 300, 1000, 0, 3)
+    assert p["splits"] == 3 and p["kc"] % t0["BK"] == 0 and 2 * p["kc"] < 1000 <= 3 * p["kc"]
+    p = g.gemm_f32_splitk_plan(8, 8, 0)
+    assert p["splits"] == 1 and p["workspace_bytes"] == 0
+    # a short k loop is left alone by the automatic plan, which then runs the
+    # plain product's own entry
+    p = g.gemm_f32_splitk_plan(256, 256, 256)
+    assert p["splits"] == 1 and p["config"] == g.gemm_f32_tile("prod", -1, 256, 256, 256)["config"]
+    p = g.gemm_f32_splitk_plan(4096, 4096, 4096)
+    assert p["config"] == g.gemm_f32_tile("prod", -1, 4096, 4096, 4096)["config"]
+    # small-K panel entries cannot split
+    panel = g.gemm_f32_tile("prod", -1, 16384, 16384, 64)["config"]
+    with pytest.raises(g.GemmError) as e:
+        g.gemm_f32_splitk_plan(512, 512, 64, panel, 2)
+    assert e.value.status == 7
+    with pytest.raises(g.GemmError) as e:
+        g.gemm_f32_splitk_plan(512, 512, 64, -1, -1)
+    assert e.value.status == 8
+
+
+def test_splitk_validation_codes():
+    lib = g._lib
+    need = g.gemm_f32_splitk_plan(1024, 1024, 1024)["workspace_bytes"]
+
+    def call(ws, ws_bytes, A=256, B=512, C=1024, lda=1024):
+        return lib.gemm_f32_splitk(1024, 1024, 1024, A, lda, B, 1024, C, 1024, -1, 0, ws,
+                                   ws_bytes, None)
+    assert call(None, 0) == 9
+    assert call(4096, need - 4) == 9
+    assert call(4098, need) == 9                    # workspace must be 4-byte aligned
+    assert call(4096, need, lda=1000) == 2
+    assert call(4096, need, A=None) == 3
+    assert call(4096, need, C=1026) == 6
+    assert lib.gemm_f32_splitk(0, 8, 8, None, 8, None, 8, None, 8, -1, 0, None, 0, None) == 0
+    assert lib.gemm_f32_splitk(8, 8, 8, None, 8, None, 8, None, 8, 8, 0, None, 0, None) == 7
+    assert lib.gemm_f32_splitk(8, 8, 8, None, 8, None, 8, None, 8, -1, -3, None, 0, None) == 8
 
 
 def test_python_raw_wrapper_raises():

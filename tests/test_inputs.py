@@ -12,11 +12,11 @@ HASHES = os.path.join(os.path.dirname(__file__), "golden", "input_hashes.json")
 
 def test_workload_table():
     assert [w.name for w in WORKLOADS.values()] == [
-        "square_256", "square_1024_int", "square_4096", "ragged", "skinny_k64"]
+        "square_256", "square_1024_int", "square_4096", "ragged", "skinny_k64", "deep_k"]
     r = WORKLOADS["ragged"]
     for d in (r.M, r.N, r.K):
         assert all(d % t for t in (4, 16, 32, 64, 128, 256))
-    assert [w.seed for w in WORKLOADS.values()] == [0, 1, 2, 3, 4]
+    assert [w.seed for w in WORKLOADS.values()] == [0, 1, 2, 3, 4, 5]
 
 
 def test_deterministic():

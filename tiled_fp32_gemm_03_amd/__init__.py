@@ -13,6 +13,8 @@ Raw C-ABI mirrors (same names and argument order as ``include/gemm_f32.h``):
   gemm_f32_probe_mfma(workgroups, iters, out, stream), gemm_f32_probe_mfma_flops(...)
   gemm_f32_probe_valu(workgroups, iters, out, stream), gemm_f32_probe_valu_flops(...)
   gemm_f32_probe_lds(workgroups, iters, out, stream), gemm_f32_probe_lds_bytes(...)
+  gemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, config, splits, workspace,
+                  workspace_bytes, stream), gemm_f32_splitk_plan(M, N, K, config, splits)
   gemm_mixed(M, N, K, A, lda, B, ldb, C, ldc, format, config, stream)
   gemm_mixed_tile(config, M, N, K) -> dict, gemm_mixed_num_configs()
                                                         (include/gemm_mixed.h)
@@ -24,7 +26,9 @@ takes float32 CUDA tensors whose last stride is 1 and passes ``stride(0)`` as
 the leading dimension, on torch's current stream.  ``matmul_mixed(A, B,
 out=None, config=-1)`` does the same for bfloat16 or float16 tensors (fp32
 result); ``format`` names the 16-bit format when A and B hold raw codes
-(int16 / uint16).
+(int16 / uint16).  ``matmul_splitk(A, B, out=None, config=-1, splits=0,
+workspace=None)`` runs the split-K form; it allocates the workspace as a torch
+tensor when none is given.
 """
 from __future__ import annotations
 
@@ -37,6 +41,7 @@ __all__ = [
     "gemm_f32_status_string", "gemm_f32_version", "gemm_f32_last_error", "gemm_f32_probe_stream",
     "gemm_f32_probe_mfma", "gemm_f32_probe_mfma_flops", "gemm_f32_probe_valu",
     "gemm_f32_probe_valu_flops", "gemm_f32_probe_lds", "gemm_f32_probe_lds_bytes", "matmul",
+    "gemm_f32_splitk", "gemm_f32_splitk_plan", "matmul_splitk",
     "gemm_mixed", "gemm_mixed_tile", "gemm_mixed_num_configs", "matmul_mixed", "MIXED_FORMATS",
     "mixed_config_name",
     "library_path",
@@ -78,6 +83,8 @@ _SIGS = {
     "gemm_f32_probe_valu": ([_i, _i, _p, _p], _i),
     "gemm_f32_probe_valu_flops": ([_i, _i], _ll),
     "gemm_f32_probe_lds": ([_i, _i, _p, _p], _i),
+    "gemm_f32_splitk": ([_i, _i, _i, _p, _i, _p, _i, _p, _i, _i, _i, _p, _ll, _p], _i),
+    "gemm_f32_splitk_plan": ([_i, _i, _i, _i, _i, _ip, _ip, _ip, ctypes.POINTER(_ll)], _i),
     "gemm_mixed": ([_i, _i, _i, _p, _i, _p, _i, _p, _i, _i, _i, _p], _i),
     "gemm_mixed_num_configs": ([], _i),
     "gemm_mixed_tile": ([_i, _i, _i, _i, _ip, _ip, _ip, _ip, _ip], _i),
@@ -194,6 +201,24 @@ def gemm_f32_probe_lds_bytes(workgroups, iters) -> int:
     return int(_lib.gemm_f32_probe_lds_bytes(int(workgroups), int(iters)))
 
 
+def gemm_f32_splitk_plan(M, N, K, config=-1, splits=0) -> dict:
+    ints = [ctypes.c_int(0) for _ in range(3)]
+    ws = ctypes.c_longlong(0)
+    rc = _lib.gemm_f32_splitk_plan(M, N, K, int(config), int(splits),
+                                   *[ctypes.byref(v) for v in ints], ctypes.byref(ws))
+    _check(rc, "gemm_f32_splitk_plan")
+    cfg, used, kc = (v.value for v in ints)
+    return {"config": cfg, "splits": used, "kc": kc, "workspace_bytes": ws.value}
+
+
+def gemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, config, splits, workspace,
+                    workspace_bytes, stream=0) -> None:
+    rc = _lib.gemm_f32_splitk(M, N, K, A or None, lda, B or None, ldb, C or None, ldc,
+                              int(config), int(splits), workspace or None, int(workspace_bytes),
+                              stream or None)
+    _check(rc, "gemm_f32_splitk")
+
+
 def _format(fmt) -> int:
     if isinstance(fmt, str):
         try:
@@ -307,4 +332,38 @@ def matmul_mixed(A, B, out=None, config: int = -1, stream=None, format=None):
     ldc = max(_ld(out), max(1, N))
     gemm_mixed(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, out.data_ptr(), ldc, fmt,
                config, stream)
+    return out
+
+
+def matmul_splitk(A, B, out=None, config: int = -1, splits: int = 0, workspace=None, stream=None):
+    """C = A x B through the split-K plan, for float32 CUDA tensors.
+
+    ``workspace`` is a CUDA tensor of at least the plan's workspace bytes; when
+    None, one is allocated with torch for this call.
+    """
+    import torch
+
+    for name, t in (("A", A), ("B", B)):
+        if t.dtype != torch.float32 or not t.is_cuda:
+            raise TypeError(f"{name} must be a float32 CUDA tensor")
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {tuple(A.shape)} x {tuple(B.shape)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (M, N) or not out.is_cuda:
+        raise TypeError("out must be a float32 CUDA tensor of shape (M, N)")
+    plan = gemm_f32_splitk_plan(M, N, K, config, splits)
+    if workspace is None and plan["workspace_bytes"] > 0:
+        workspace = torch.empty(plan["workspace_bytes"] // 4, dtype=torch.float32, device=A.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device).cuda_stream
+    lda = max(_ld(A), max(1, K))
+    ldb = max(_ld(B), max(1, N))
+    ldc = max(_ld(out), max(1, N))
+    gemm_f32_splitk(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, out.data_ptr(), ldc, config,
+                    splits, ws_ptr, ws_bytes, stream)
     return out

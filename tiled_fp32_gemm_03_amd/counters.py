@@ -4,7 +4,10 @@ Two subcommands, both reading CSV files that rocprofv3 wrote
 (``--output-format csv``); neither touches the GPU.
 
   trace  --csv <..._kernel_trace.csv> --command "<profiled command>"
-         Per (kernel, grid, workgroup) launch counts and durations.  The
+         [--ladder <ladder.jsonl>]
+         Per (kernel, grid, workgroup) launch counts and durations; with
+         --ladder, per ladder record (dispatches between its marker and the
+         next), so that workloads sharing a grid stay apart.  The
          trace is used instead of rocprofv3's own stats file because one
          template instance can serve several workloads with different grids.
 
@@ -41,7 +44,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 PROD_SOURCES = [os.path.join(HERE, "csrc", n) for n in ("prod.hip", "tile_order.hpp")]
 OUR_KERNELS = re.compile(r"(gemm_f32_impl|prod_kernel|panel_kernel|strip_kernel|naive_kernel|tiled_kernel|"
                          r"valu_kernel|mixed_kernel|stream_kernel|stream_tail|mfma_probe_kernel|"
-                         r"valu_probe_kernel|lds_probe_kernel|zero_kernel)")
+                         r"valu_probe_kernel|lds_probe_kernel|zero_kernel|prod_split_kernel|"
+                         r"splitk_reduce_kernel)")
 
 
 def prod_source_digest() -> str:
@@ -59,23 +63,67 @@ def short_name(name: str) -> str:
     return s.strip()
 
 
-def cmd_trace(args) -> int:
-    groups: dict = OrderedDict()
-    for path in args.csv:
+def _workgroups(row) -> int:
+    n = 1
+    for d in ("X", "Y", "Z"):
+        n *= max(1, int(row[f"Grid_Size_{d}"]) // max(1, int(row[f"Workgroup_Size_{d}"])))
+    return n
+
+
+def _threads(row) -> int:
+    return int(row["Workgroup_Size_X"]) * int(row["Workgroup_Size_Y"]) * int(row["Workgroup_Size_Z"])
+
+
+def _trace_rows(paths):
+    rows = []
+    for path in paths:
         with open(path, newline="") as f:
-            for row in csv.DictReader(f):
-                key = (short_name(row["Kernel_Name"]), int(row["Grid_Size_X"]),
-                       int(row["Workgroup_Size_X"]) * int(row["Workgroup_Size_Y"]) * int(row["Workgroup_Size_Z"]))
-                dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1000.0
-                groups.setdefault(key, []).append(dur)
-    lines = [f"# {args.title}", "", "Command:", "", "```", *args.command, "```", "",
-             "| kernel | workgroups | threads/WG | calls | avg us | min us | max us |",
-             "|---|---|---|---|---|---|---|"]
-    for (name, grid, wg), durs in groups.items():
-        if args.only_ours and not OUR_KERNELS.search(name):
-            continue
-        lines.append(f"| `{name}` | {grid // wg} | {wg} | {len(durs)} | {statistics.mean(durs):.1f} "
-                     f"| {min(durs):.1f} | {max(durs):.1f} |")
+            rows += list(csv.DictReader(f))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    return rows
+
+
+def cmd_trace(args) -> int:
+    rows = _trace_rows(args.csv)
+    lines = [f"# {args.title}", "", "Command:", "", "```", *args.command, "```", ""]
+    if args.ladder:
+        # One block per ladder record: the dispatches between its marker and
+        # the next (warm-up and timed calls), per kernel and grid.
+        recs = _read_ladder(args.ladder)
+        segs, cur = [], None
+        for r in rows:
+            name = short_name(r["Kernel_Name"])
+            if name == MARKER:
+                cur = OrderedDict()
+                segs.append(cur)
+                continue
+            if cur is None or (args.only_ours and not OUR_KERNELS.search(name)):
+                continue
+            key = (name, _workgroups(r), _threads(r))
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+            cur.setdefault(key, []).append(dur)
+        if len(segs) != len(recs):
+            raise SystemExit(f"{len(recs)} ladder records but {len(segs)} marked segments")
+        lines += ["| workload | record | kernel | workgroups | threads/WG | calls | avg us | min us | max us |",
+                  "|---|---|---|---|---|---|---|---|---|"]
+        for rec, seg in zip(recs, segs):
+            for (name, wgs, wg), durs in seg.items():
+                lines.append(f"| {rec.get('workload', '-')} | {rec.get('kernel', '-')} | `{name}` | {wgs} "
+                             f"| {wg} | {len(durs)} | {statistics.mean(durs):.1f} | {min(durs):.1f} "
+                             f"| {max(durs):.1f} |")
+    else:
+        groups: dict = OrderedDict()
+        for r in rows:
+            key = (short_name(r["Kernel_Name"]), _workgroups(r), _threads(r))
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+            groups.setdefault(key, []).append(dur)
+        lines += ["| kernel | workgroups | threads/WG | calls | avg us | min us | max us |",
+                  "|---|---|---|---|---|---|---|"]
+        for (name, wgs, wg), durs in groups.items():
+            if args.only_ours and not OUR_KERNELS.search(name):
+                continue
+            lines.append(f"| `{name}` | {wgs} | {wg} | {len(durs)} | {statistics.mean(durs):.1f} "
+                         f"| {min(durs):.1f} | {max(durs):.1f} |")
     text = "\n".join(lines) + "\n"
     if args.out:
         with open(args.out, "w") as f:
@@ -218,6 +266,7 @@ def main(argv=None) -> int:
     t.add_argument("--title", default="rocprofv3 kernel trace")
     t.add_argument("--out")
     t.add_argument("--only-ours", action="store_true")
+    t.add_argument("--ladder", help="ladder JSONL of the traced run: group dispatches per record")
     p = sub.add_parser("pmc")
     p.add_argument("--run", action="append", required=True, help="LADDER_JSONL:COUNTER_CSV")
     p.add_argument("--command", action="append", default=[])

@@ -130,6 +130,46 @@ extern "C" int gemm_f32_tile(int variant, int config, int M, int N, int K,
   return GEMM_F32_OK;
 }
 
+// ---- split-K ---------------------------------------------------------------
+
+extern "C" int gemm_f32_splitk_plan(int M, int N, int K, int config, int splits,
+                                    int *config_out, int *splits_out, int *kc_out,
+                                    long long *workspace_bytes) {
+  int rc = check_shape(M, N, K);
+  if (rc != GEMM_F32_OK) return rc;
+  if (splits < 0) return GEMM_F32_BAD_ARG;
+  SplitPlan plan;
+  if (!splitk_plan(M, N, K, config, splits, &plan)) return GEMM_F32_BAD_CONFIG;
+  if (config_out) *config_out = plan.config;
+  if (splits_out) *splits_out = plan.splits;
+  if (kc_out) *kc_out = plan.kc;
+  if (workspace_bytes) *workspace_bytes = plan.workspace_bytes;
+  return GEMM_F32_OK;
+}
+
+extern "C" int gemm_f32_splitk(int M, int N, int K, const float *A, int lda, const float *B,
+                               int ldb, float *C, int ldc, int config, int splits,
+                               void *workspace, long long workspace_bytes, void *stream) {
+  int rc = check_shape(M, N, K);
+  if (rc != GEMM_F32_OK) return rc;
+  if (lda < max1(K) || ldb < max1(N) || ldc < max1(N)) return GEMM_F32_INVALID_LD;
+  if (splits < 0) return GEMM_F32_BAD_ARG;
+  SplitPlan plan;
+  if (!splitk_plan(M, N, K, config, splits, &plan)) return GEMM_F32_BAD_CONFIG;
+  if (M == 0 || N == 0) return GEMM_F32_OK;
+  if (C == nullptr) return GEMM_F32_NULL_PTR;
+  if (K > 0 && (A == nullptr || B == nullptr)) return GEMM_F32_NULL_PTR;
+  if (misaligned(C) || (K > 0 && (misaligned(A) || misaligned(B))))
+    return GEMM_F32_MISALIGNED;
+  if (plan.workspace_bytes > 0 &&
+      (workspace == nullptr || workspace_bytes < plan.workspace_bytes || misaligned(workspace)))
+    return GEMM_F32_BAD_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Problem p{M, N, K, A, lda, B, ldb, C, ldc};
+  if (K == 0) return launch_status(launch_zero(p, s), "zero fill");
+  return launch_status(launch_prod_split(plan, p, static_cast<float *>(workspace), s), "splitk");
+}
+
 // ---- 16-bit inputs ---------------------------------------------------------
 
 namespace {
@@ -203,6 +243,8 @@ extern "C" const char *gemm_f32_status_string(int status) {
     case GEMM_F32_BAD_CONFIG:
       return "launch-table index out of range or not valid for this shape";
     case GEMM_F32_BAD_ARG: return "invalid argument";
+    case GEMM_F32_BAD_WORKSPACE:
+      return "split-K workspace missing, smaller than the plan needs, or not 4-byte aligned";
     default: return "unknown status";
   }
 }

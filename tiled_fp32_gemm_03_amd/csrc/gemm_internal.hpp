@@ -74,4 +74,17 @@ int prod_choose(int M, int N, int K);
 bool prod_supports(int index, int M, int N, int K);
 hipError_t launch_prod(int index, const Problem &p, hipStream_t s);
 
+// Split-K form of the production kernel: K is cut into `splits` chunks of
+// kc (a multiple of the entry's BK); each chunk's partial product goes to its
+// own M x N slab of a caller-provided workspace, and a second kernel sums the
+// slabs in chunk order into C.
+struct SplitPlan {
+  int config;                 // launch-table entry
+  int splits;                 // chunks actually used (1 = plain product)
+  int kc;                     // k values per chunk
+  long long workspace_bytes;  // splits * M * N * 4, or 0 when splits == 1
+};
+bool splitk_plan(int M, int N, int K, int config, int splits, SplitPlan *out);
+hipError_t launch_prod_split(const SplitPlan &plan, const Problem &p, float *ws, hipStream_t s);
+
 }  // namespace gemm_f32_impl

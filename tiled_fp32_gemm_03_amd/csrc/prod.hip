@@ -324,9 +324,10 @@ __device__ inline bool load_step(Stage<S> &st, const Problem &p, int m0,
   return true;
 }
 
+// The persistent tile loop of one product: workgroup `bid` of `G` walks
+// tiles bid, bid + G, ... (after the XCD renumbering), each over all of p.K.
 template <class S>
-__global__ void __launch_bounds__(S::NT)
-    prod_kernel(Problem p, int tiles_m, int tiles_n) {
+__device__ __forceinline__ void prod_body(Problem p, int tiles_m, int tiles_n, int bid, int G) {
   static_assert(S::LDS_FLOATS * 4 <= kLdsBytes, "two stages must fit in LDS");
   __shared__ __attribute__((aligned(16))) float lds[S::LDS_FLOATS];
   float *const as0 = lds;
@@ -337,8 +338,7 @@ __global__ void __launch_bounds__(S::NT)
   const int wm = wave / S::WGN, wn = wave % S::WGN;
   const int ntiles = tiles_m * tiles_n;
   const int nk = (p.K + S::BK - 1) / S::BK;
-  const int G = gridDim.x;
-  const int lid = xcd_remap(blockIdx.x, G);
+  const int lid = xcd_remap(bid, G);
   if (lid >= ntiles) return;  // uniform per workgroup
   // This workgroup's tiles are lid, lid + G, lid + 2G, ...
   const int my_tiles = (ntiles - lid + G - 1) / G;
@@ -398,6 +398,69 @@ __global__ void __launch_bounds__(S::NT)
     m0 = nm0;
     n0 = nn0;
     interior = ninterior;
+  }
+}
+
+template <class S>
+__global__ void __launch_bounds__(S::NT)
+    prod_kernel(Problem p, int tiles_m, int tiles_n) {
+  prod_body<S>(p, tiles_m, tiles_n, blockIdx.x, gridDim.x);
+}
+
+// Split-K: grid row y computes the partial product over k in
+// [y * kc, min(K, (y + 1) * kc)) into its own M x N slab of `ws` (row pitch
+// N), by the same tile loop on the sub-problem.  The slabs are summed by
+// splitk_reduce_kernel.
+template <class S>
+__global__ void __launch_bounds__(S::NT)
+    prod_split_kernel(Problem p, int tiles_m, int tiles_n, int kc, float *ws) {
+  const int y = blockIdx.y;
+  const int k0 = y * kc;
+  Problem ps = p;
+  ps.A = p.A + k0;
+  ps.B = p.B + (long long)k0 * p.ldb;
+  ps.K = p.K - k0 < kc ? p.K - k0 : kc;
+  ps.C = ws + (long long)y * p.M * p.N;
+  ps.ldc = p.N;
+  prod_body<S>(ps, tiles_m, tiles_n, blockIdx.x, gridDim.x);
+}
+
+constexpr int kReduceThreads = 256;
+
+// C[i][j] = sum over y = 0 .. splits-1, in that order, of ws[y][i][j]: one
+// thread per 4 consecutive columns of a row, grid-stride.
+__global__ void __launch_bounds__(kReduceThreads)
+    splitk_reduce_kernel(const float *ws, int splits, int M, int N, float *C, long long ldc) {
+  const long long slab = (long long)M * N;
+  const int nq = (N + 3) / 4;
+  const long long total = (long long)M * nq;
+  const long long stride = (long long)gridDim.x * kReduceThreads;
+  for (long long e = (long long)blockIdx.x * kReduceThreads + threadIdx.x; e < total;
+       e += stride) {
+    const long long i = e / nq;
+    const int j = (int)(e - i * nq) * 4;
+    const float *w = ws + i * N + j;
+    float *c = C + i * ldc + j;
+    if (j + 4 <= N) {
+      // Loads of 8 slabs are issued together; the additions keep slab order.
+      f32x4 acc = *reinterpret_cast<const f32x4u *>(w);
+      int y = 1;
+      for (; y + 8 <= splits; y += 8) {
+        f32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x4u *>(w + (y + u) * slab);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += v[u];
+      }
+      for (; y < splits; ++y) acc += *reinterpret_cast<const f32x4u *>(w + y * slab);
+      *reinterpret_cast<f32x4u *>(c) = acc;
+    } else {
+      for (int e2 = 0; j + e2 < N; ++e2) {
+        float acc = w[e2];
+        for (int y = 1; y < splits; ++y) acc += w[e2 + y * slab];
+        c[e2] = acc;
+      }
+    }
   }
 }
 
@@ -607,6 +670,23 @@ hipError_t launch_kloop(const Problem &p, hipStream_t s) {
   return launch_grid<S, prod_kernel<S>>(p, s);
 }
 
+// Split-K launch: every (tile, split) pair is one workgroup (grid y = the
+// split), then the reduction over the slabs into C.
+template <class S>
+hipError_t launch_split(const Problem &p, int splits, int kc, float *ws, hipStream_t s) {
+  const long long tiles_m = ceil_div(p.M, S::BM), tiles_n = ceil_div(p.N, S::BN);
+  const long long ntiles = tiles_m * tiles_n;
+  if (ntiles > 0x7fffffffLL || splits < 1 || splits > kMaxGridY) return hipErrorInvalidValue;
+  hipError_t e = launch_kernel(prod_split_kernel<S>, dim3((unsigned)ntiles, (unsigned)splits),
+                               dim3(S::NT), s, p, (int)tiles_m, (int)tiles_n, kc, ws);
+  if (e != hipSuccess) return e;
+  const long long quads = (long long)p.M * ((p.N + 3) / 4);
+  long long blocks = ceil_div(quads, kReduceThreads);
+  if (blocks > 4096) blocks = 4096;
+  return launch_kernel(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(kReduceThreads), s,
+                       static_cast<const float *>(ws), splits, p.M, p.N, p.C, p.ldc);
+}
+
 // Whole tiles only: the caller (launch_prod) splits edge strips off first.
 template <class S>
 hipError_t launch_panel(const Problem &p, hipStream_t s) {
@@ -631,6 +711,20 @@ hipError_t launch_one(int index, const Problem &p, hipStream_t s) {
     case 11: return launch_kloop<C11>(p, s);
     case 12: return launch_kloop<C12>(p, s);
 
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_split_one(int index, const Problem &p, int splits, int kc, float *ws,
+                            hipStream_t s) {
+  switch (index) {
+    case 0: return launch_split<C0>(p, splits, kc, ws, s);
+    case 1: return launch_split<C1>(p, splits, kc, ws, s);
+    case 2: return launch_split<C2>(p, splits, kc, ws, s);
+    case 3: return launch_split<C3>(p, splits, kc, ws, s);
+    case 4: return launch_split<C4>(p, splits, kc, ws, s);
+    case 7: return launch_split<C7>(p, splits, kc, ws, s);
+    case 12: return launch_split<C12>(p, splits, kc, ws, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -668,6 +762,55 @@ int prod_choose(int M, int N, int K) {
   if (t256x128 >= 512) return 2;
   if (t64 >= 2048) return 4;
   return 3;
+}
+
+// Entries the split-K path can run: the k-loop kernels without
+// non-temporal stores (the slabs are read back at once).
+static bool split_supports(int index) {
+  switch (index) {
+    case 0: case 1: case 2: case 3: case 4: case 7: case 12: return true;
+    default: return false;
+  }
+}
+
+// Split-K plan.  Automatic entry: 128 x 128 x 32 tiles (64 x 64 below a
+// 128 x 128 output), two workgroups per CU.  Automatic split count: enough
+// (tile, split) pairs to give every CU a workgroup, each split at least four
+// k steps deep; products that already have a tile for every CU, or fewer
+// than 32 k steps, are not split.  An explicit count is honoured up to one k step per split.  The
+// chunk kc is a multiple of BK, and splits = ceil(K / kc).
+bool splitk_plan(int M, int N, int K, int config, int splits, SplitPlan *out) {
+  if (M < 0 || N < 0 || K < 0 || splits < 0) return false;
+  const bool auto_config = config == -1;
+  if (auto_config) config = (M < 128 && N < 128) ? 3 : 0;
+  if (config < 0 || config >= kNumConfigs || !split_supports(config)) return false;
+  const ProdConfig &c = kEntries[config].cfg;
+  const long long tiles = ceil_div(M, c.BM) * ceil_div(N, c.BN);
+  const long long ksteps = ceil_div(K, c.BK);
+  long long want = splits;
+  if (want == 0) {
+    const long long cus = 256;
+    want = tiles >= cus ? 1 : ceil_div(cus, tiles > 0 ? tiles : 1);
+    const long long deep = ksteps / 4;
+    if (want > deep) want = deep;
+    if (ksteps < 32) want = 1;  // a short k loop: the extra launch costs more than it saves
+  }
+  if (want > ksteps) want = ksteps;
+  if (want > kMaxGridY) want = kMaxGridY;
+  if (want < 1) want = 1;
+  const long long kc = ceil_div(ksteps, want) * c.BK;
+  const long long used = K > 0 ? ceil_div(K, kc) : 1;
+  // Unsplit with an automatic entry: the plain product's own choice.
+  out->config = used == 1 && auto_config ? prod_choose(M, N, K) : config;
+  out->splits = (int)used;
+  out->kc = (int)kc;
+  out->workspace_bytes = used > 1 ? used * (long long)M * N * 4 : 0;
+  return true;
+}
+
+hipError_t launch_prod_split(const SplitPlan &plan, const Problem &p, float *ws, hipStream_t s) {
+  if (plan.splits <= 1) return launch_prod(plan.config, p, s);
+  return launch_split_one(plan.config, p, plan.splits, plan.kc, ws, s);
 }
 
 // One product with launch-table entry `index`.  Thin remainder strips along

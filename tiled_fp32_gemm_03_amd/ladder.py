@@ -7,7 +7,10 @@
 valu, prod, and the 16-bit-input rungs bf16 and f16) and, for rungs with a
 launch table, ``<rung>:<i>`` for entry i or ``<rung>:all`` for every entry.
 The 16-bit rungs take each workload rounded to their format (the seeded
-generator's rounding) and report against the dense bf16/fp16 matrix peak.  ``--alu-probes`` first measures the fp32
+generator's rounding) and report against the dense bf16/fp16 matrix peak.
+``splitk`` runs the split-K form of the production kernel with its automatic
+plan; ``splitk:<s>`` asks for s chunks (workspace allocated once per record,
+outside the timed region).  ``--alu-probes`` first measures the fp32
 vector-FMA probe at 1, 2, 4, 8 and 16 waves per SIMD, the LDS read-bandwidth
 probe and the fp32 MFMA probe (the compute and on-chip roofs of the rungs).  ``--copy-mib N`` first runs the streaming copy
 probe once over N MiB (a kernel of known traffic: N MiB read, N MiB written)
@@ -39,6 +42,8 @@ MIXED = ("bf16", "f16")
 
 
 def _num_configs(g, name: str) -> int:
+    if name == "splitk":
+        raise ValueError("splitk takes a chunk count (splitk:<s>), not 'all'")
     return g.gemm_mixed_num_configs() if name in MIXED else g.gemm_f32_num_configs(name)
 
 
@@ -158,13 +163,25 @@ def main(argv=None) -> int:
             if vname == "naive" and gflop > args.max_naive_gflop:
                 continue
             mixed = vname in MIXED
+            split = vname == "splitk"
             try:
-                tile = (g.gemm_mixed_tile(cfg, w.M, w.N, w.K) if mixed
-                        else g.gemm_f32_tile(vname, cfg, w.M, w.N, w.K))
+                if mixed:
+                    tile = g.gemm_mixed_tile(cfg, w.M, w.N, w.K)
+                elif split:
+                    plan = g.gemm_f32_splitk_plan(w.M, w.N, w.K, -1, max(cfg, 0))
+                    tile = g.gemm_f32_tile("prod", plan["config"], w.M, w.N, w.K)
+                else:
+                    tile = g.gemm_f32_tile(vname, cfg, w.M, w.N, w.K)
             except g.GemmError:  # entry does not accept this shape (small-K entries)
                 continue
-            label = (g.mixed_config_name(vname, cfg, w.M, w.N, w.K) if mixed
-                     else g.config_name(vname, cfg, w.M, w.N, w.K))
+            if mixed:
+                label = g.mixed_config_name(vname, cfg, w.M, w.N, w.K)
+            elif split:
+                label = (g.config_name("prod", plan["config"], w.M, w.N, w.K).replace("prod", "splitk")
+                         + f"/{plan['splits']}x{plan['kc']}")
+                ws = torch.empty(max(plan["workspace_bytes"] // 4, 1), dtype=torch.float32, device=dev)
+            else:
+                label = g.config_name(vname, cfg, w.M, w.N, w.K)
             reps = args.reps if vname != "naive" else max(1, min(args.reps, 3))
             print(f"[ladder] {wname} {label} reps={reps}", file=sys.stderr, flush=True)
             ta, tb = ops[vname if mixed else "f32"]
@@ -173,6 +190,11 @@ def main(argv=None) -> int:
                 def call():
                     g.gemm_mixed(w.M, w.N, w.K, ta.data_ptr(), w.K, tb.data_ptr(), w.N,
                                  tc.data_ptr(), w.N, vname, cfg, s)
+            elif split:
+                def call():
+                    g.gemm_f32_splitk(w.M, w.N, w.K, ta.data_ptr(), w.K, tb.data_ptr(), w.N,
+                                      tc.data_ptr(), w.N, -1, plan["splits"], ws.data_ptr(),
+                                      ws.numel() * 4, s)
             else:
                 def call():
                     g.gemm_f32_ex(w.M, w.N, w.K, ta.data_ptr(), w.K, tb.data_ptr(), w.N,
@@ -189,7 +211,7 @@ def main(argv=None) -> int:
                    "frac_peak": round(tflops / peak, 4), "peak_tflops": peak,
                    "gbps_compulsory": round(rf.compulsory_bytes(w.M, w.N, w.K, elem) / (ms * 1e-3) / 1e9, 1),
                    "model_issued_load_bytes": elem * rf.issued_load_elements(
-                       "prod" if mixed else vname, w.M, w.N, w.K, tile),
+                       "prod" if (mixed or split) else vname, w.M, w.N, w.K, tile),
                    "flops": rf.flops(w.M, w.N, w.K)}
             rows.append(rec)
             print(json.dumps(rec), flush=True)
