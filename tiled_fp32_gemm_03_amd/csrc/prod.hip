@@ -236,7 +236,8 @@ __device__ inline void store_lds(const Stage<S> &st, float *as, float *bs,
 }
 
 // All MFMAs of one k step out of one LDS stage.
-template <class S>
+// k groups [KG0, KG1) of one stage (8 k values per group).
+template <class S, int KG0 = 0, int KG1 = S::BK / 8>
 __device__ inline void compute_stage(f32x16 (&acc)[S::TM][S::TN],
                                      const float *as, const float *bs,
                                      int wm, int wn, int lane) {
@@ -244,7 +245,7 @@ __device__ inline void compute_stage(f32x16 (&acc)[S::TM][S::TN],
   const float *a_base = as + (wm * S::WTM + l32) * S::SA + 4 * h;
   const float *b_base = bs + (4 * h) * S::SB + wn * S::WTN + l32;
 #pragma unroll
-  for (int kg = 0; kg < S::BK / 8; ++kg) {
+  for (int kg = KG0; kg < KG1; ++kg) {
     f32x4 af[S::TM];
     float bf[S::TN][4];
 #pragma unroll
@@ -376,8 +377,16 @@ __device__ __forceinline__ void prod_body(Problem p, int tiles_m, int tiles_n, i
     }
     if (more) guarded = load_step<S>(st, p, nm0, nn0, nkt * S::BK, ninterior, tid);
 
-    compute_stage<S>(acc, as0 + cur * S::A_STAGE, bs0 + cur * S::B_STAGE, wm,
-                     wn, lane);
+    // First half of this step's matrix work, then the next stage's LDS
+    // write (that buffer was last read before the previous barrier), then
+    // the second half: the write leaves the barrier's critical path.
+    compute_stage<S, 0, S::BK / 16>(acc, as0 + cur * S::A_STAGE, bs0 + cur * S::B_STAGE, wm,
+                                    wn, lane);
+    if (more)
+      store_lds<S>(st, as0 + (cur ^ 1) * S::A_STAGE,
+                   bs0 + (cur ^ 1) * S::B_STAGE, tid, guarded);
+    compute_stage<S, S::BK / 16, S::BK / 8>(acc, as0 + cur * S::A_STAGE,
+                                            bs0 + cur * S::B_STAGE, wm, wn, lane);
 
     if (kt == nk - 1) {
       // Tile done: stores drain while the next tile computes.
@@ -389,9 +398,6 @@ __device__ __forceinline__ void prod_body(Problem p, int tiles_m, int tiles_n, i
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     }
-    if (more)
-      store_lds<S>(st, as0 + (cur ^ 1) * S::A_STAGE,
-                   bs0 + (cur ^ 1) * S::B_STAGE, tid, guarded);
     __syncthreads();
     t = nt;
     kt = nkt;
