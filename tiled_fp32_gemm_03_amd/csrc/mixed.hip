@@ -28,6 +28,7 @@
 #include "tile_order.hpp"
 
 #include <cstdint>
+#include <type_traits>
 
 namespace gemm_f32_impl {
 namespace {
@@ -46,18 +47,23 @@ constexpr int kMixedBK = 64;
 constexpr int kUnits = kMixedBK / 8;  // 16-byte units per LDS row
 constexpr int kPitch = kUnits + 1;    // units per LDS row, with one pad unit
 
-template <int BM_, int BN_, int WGM_, int WGN_>
+// BKB: k depth of the B block one thread transposes (8, or 4 when there
+// are twice as many threads as 8 x 8 blocks).
+template <int BM_, int BN_, int WGM_, int WGN_, int BKB_ = 8>
 struct MTile {
-  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, BKB = BKB_;
   static constexpr int NT = 64 * WGM * WGN;
   static constexpr int WTM = BM / WGM, WTN = BN / WGN;
   static constexpr int TM = WTM / 32, TN = WTN / 32;
-  static constexpr int HALF = NT / 2;      // threads staging A (and B)
-  static constexpr int A_ROWS = HALF / 8;  // A rows covered by one load pass
-  static constexpr int B_NB = BN / 8;      // 8-column blocks of B
+  static constexpr int HALF = NT / 2;          // threads staging A (and B)
+  static constexpr int A_ROWS = HALF / 8;      // A rows covered by one load pass
+  static constexpr int A_PER = BM / A_ROWS;    // A pieces per staging thread
+  static constexpr int B_NB = BN / 8;          // 8-column blocks of B
   static constexpr int A_UNITS = BM * kPitch;
   static constexpr int STAGE_UNITS = (BM + BN) * kPitch;
-  static_assert(BM == HALF && BN == HALF, "each staging thread moves 8 units of A or B");
+  static_assert(BKB == 8 || BKB == 4, "B blocks are 8 or 4 k deep");
+  static_assert((kMixedBK / BKB) * B_NB == HALF, "one B block per staging thread");
+  static_assert(A_PER * A_ROWS == BM && A_PER <= 8, "A rows split evenly over staging threads");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be 32-aligned");
   static_assert(2 * STAGE_UNITS * 16 <= 160 * 1024, "two stages must fit in LDS");
 };
@@ -74,7 +80,8 @@ __device__ inline f32x16 mfma16(u32x4 x, u32x4 y, f32x16 acc) {
 
 __device__ inline int b_swizzle(int n) { return (n >> 4) & 7; }
 
-// One k step of this thread's share: 8 sixteen-byte pieces of A or of B.
+// One k step of this thread's share: up to 8 sixteen-byte pieces of A or
+// of B (S::A_PER or S::BKB of them are used).
 struct MStage {
   u32x4 v[8];
 };
@@ -91,29 +98,37 @@ __device__ inline u32x4 load8_guarded(const uint16_t *p, int valid) {
   return u32x4{pack2(c[0], c[1]), pack2(c[2], c[3]), pack2(c[4], c[5]), pack2(c[6], c[7])};
 }
 
-template <class S, bool GUARD>
+// Element offset of a lane's piece from the tile's origin.  OFF32: the
+// launcher has checked that the tile's span fits in 32 bits, so the origin
+// stays a uniform (scalar) pointer and each lane keeps only a 32-bit offset
+// -- fewer registers than one 64-bit pointer per piece.
+template <bool OFF32>
+using MOffset = typename std::conditional<OFF32, unsigned int, long long>::type;
+
+template <class S, bool GUARD, bool OFF32>
 __device__ inline void mixed_load(MStage &st, const MixedProblem &p, int m0, int n0,
                                   int k0, int tid) {
+  using Off = MOffset<OFF32>;
   if (tid < S::HALF) {
     const int u = tid & 7, r0 = tid >> 3;
-    const int k = k0 + 8 * u;
+    const uint16_t *origin = p.A + (long long)m0 * p.lda + k0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int m = m0 + r0 + j * S::A_ROWS;
-      const uint16_t *src = p.A + (long long)m * p.lda + k;
+    for (int j = 0; j < S::A_PER; ++j) {
+      const int r = r0 + j * S::A_ROWS;
+      const uint16_t *src = origin + ((Off)r * (Off)p.lda + (Off)(8 * u));
       if (!GUARD) st.v[j] = *reinterpret_cast<const u32x4u *>(src);
-      else st.v[j] = load8_guarded(src, m < p.M ? p.K - k : 0);
+      else st.v[j] = load8_guarded(src, m0 + r < p.M ? p.K - (k0 + 8 * u) : 0);
     }
   } else {
     const int t = tid - S::HALF;
     const int nb = t % S::B_NB, kb = t / S::B_NB;
-    const int n = n0 + 8 * nb;
+    const uint16_t *origin = p.B + (long long)k0 * p.ldb + n0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int k = k0 + 8 * kb + j;
-      const uint16_t *src = p.B + (long long)k * p.ldb + n;
+    for (int j = 0; j < S::BKB; ++j) {
+      const int r = S::BKB * kb + j;
+      const uint16_t *src = origin + ((Off)r * (Off)p.ldb + (Off)(8 * nb));
       if (!GUARD) st.v[j] = *reinterpret_cast<const u32x4u *>(src);
-      else st.v[j] = load8_guarded(src, k < p.K ? p.N - n : 0);
+      else st.v[j] = load8_guarded(src, k0 + r < p.K ? p.N - (n0 + 8 * nb) : 0);
     }
   }
 }
@@ -123,36 +138,44 @@ __device__ inline void mixed_store_lds(const MStage &st, u32x4 *stage, int tid) 
   if (tid < S::HALF) {
     const int u = tid & 7, r0 = tid >> 3;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) stage[(r0 + j * S::A_ROWS) * kPitch + u] = st.v[j];
+    for (int j = 0; j < S::A_PER; ++j) stage[(r0 + j * S::A_ROWS) * kPitch + u] = st.v[j];
   } else {
     const int t = tid - S::HALF;
     const int nb = t % S::B_NB, kb = t / S::B_NB;
     u32x4 *bs = stage + S::A_UNITS;
-    // st.v[j] holds B[k0 + 8kb + j][n .. n+7]; column piece i gathers
-    // element i of each of the 8 rows, two codes per dword.
+    // st.v[j] holds B[k0 + BKB kb + j][n .. n+7]; column piece i gathers
+    // element i of each of the BKB rows, two codes per dword.
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int w = i >> 1;
-      u32x4 col;
+      unsigned int col[S::BKB / 2];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
+      for (int d = 0; d < S::BKB / 2; ++d) {
         const unsigned int lo = st.v[2 * d][w], hi = st.v[2 * d + 1][w];
         col[d] = (i & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
       }
       const int n = 8 * nb + i;
-      bs[n * kPitch + (kb ^ b_swizzle(n))] = col;
+      if constexpr (S::BKB == 8) {
+        bs[n * kPitch + (kb ^ b_swizzle(n))] = u32x4{col[0], col[1], col[2], col[3]};
+      } else {
+        // 4 k values: one half of unit kb / 2.
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        u32x2 *half = reinterpret_cast<u32x2 *>(bs + n * kPitch + ((kb >> 1) ^ b_swizzle(n)));
+        half[kb & 1] = u32x2{col[0], col[1]};
+      }
     }
   }
 }
 
-template <class S, int FMT>
+// k slices [KK0, KK1) of one stage (16 k values per slice).
+template <class S, int FMT, int KK0 = 0, int KK1 = kUnits / 2>
 __device__ inline void mixed_compute(const u32x4 *stage, f32x16 (&acc)[S::TM][S::TN], int wm,
                                      int wn, int lane) {
   const u32x4 *as = stage;
   const u32x4 *bs = stage + S::A_UNITS;
   const int r = lane & 31, h = lane >> 5;
 #pragma unroll
-  for (int kk = 0; kk < kUnits / 2; ++kk) {
+  for (int kk = KK0; kk < KK1; ++kk) {
     const int u = 2 * kk + h;
     u32x4 af[S::TM], bf[S::TN];
 #pragma unroll
@@ -170,7 +193,7 @@ __device__ inline void mixed_compute(const u32x4 *stage, f32x16 (&acc)[S::TM][S:
   }
 }
 
-template <class S, int FMT>
+template <class S, int FMT, bool OFF32>
 __global__ void __launch_bounds__(S::NT)
     mixed_kernel(MixedProblem p, int tiles_m, int tiles_n) {
   __shared__ u32x4 lds[2 * S::STAGE_UNITS];
@@ -191,8 +214,8 @@ __global__ void __launch_bounds__(S::NT)
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   MStage st;
-  if (fast && kMixedBK <= p.K) mixed_load<S, false>(st, p, m0, n0, 0, tid);
-  else mixed_load<S, true>(st, p, m0, n0, 0, tid);
+  if (fast && kMixedBK <= p.K) mixed_load<S, false, OFF32>(st, p, m0, n0, 0, tid);
+  else mixed_load<S, true, OFF32>(st, p, m0, n0, 0, tid);
   mixed_store_lds<S>(st, lds, tid);
   __syncthreads();
 
@@ -201,11 +224,14 @@ __global__ void __launch_bounds__(S::NT)
     const bool more = kt + 1 < nk;
     if (more) {
       const int k1 = (kt + 1) * kMixedBK;
-      if (fast && k1 + kMixedBK <= p.K) mixed_load<S, false>(st, p, m0, n0, k1, tid);
-      else mixed_load<S, true>(st, p, m0, n0, k1, tid);
+      if (fast && k1 + kMixedBK <= p.K) mixed_load<S, false, OFF32>(st, p, m0, n0, k1, tid);
+      else mixed_load<S, true, OFF32>(st, p, m0, n0, k1, tid);
     }
-    mixed_compute<S, FMT>(lds + cur * S::STAGE_UNITS, acc, wm, wn, lane);
+    // The next stage's buffer was last read before the previous barrier, so
+    // its write goes between the two halves of this step's matrix work.
+    mixed_compute<S, FMT, 0, kUnits / 4>(lds + cur * S::STAGE_UNITS, acc, wm, wn, lane);
     if (more) mixed_store_lds<S>(st, lds + (cur ^ 1) * S::STAGE_UNITS, tid);
+    mixed_compute<S, FMT, kUnits / 4, kUnits / 2>(lds + cur * S::STAGE_UNITS, acc, wm, wn, lane);
     __syncthreads();
   }
 
@@ -236,12 +262,15 @@ __global__ void __launch_bounds__(S::NT)
   }
 }
 
-using Mixed256 = MTile<256, 256, 2, 4>;  // 8 waves, 128 x 64 per wave
-using Mixed128 = MTile<128, 128, 2, 2>;  // 4 waves, 64 x 64 per wave
+using Mixed256 = MTile<256, 256, 2, 4>;     // 8 waves, 128 x 64 per wave
+using Mixed128 = MTile<128, 128, 2, 2>;     // 4 waves, 64 x 64 per wave
+using Mixed256w16 = MTile<256, 256, 4, 4, 4>;  // 16 waves, 64 x 64 per wave
 
 const MixedConfig kMixedConfigs[] = {
     {Mixed256::BM, Mixed256::BN, kMixedBK, Mixed256::WGM, Mixed256::WGN, 1, "256x256x64 w2x4"},
     {Mixed128::BM, Mixed128::BN, kMixedBK, Mixed128::WGM, Mixed128::WGN, 2, "128x128x64 w2x2"},
+    {Mixed256w16::BM, Mixed256w16::BN, kMixedBK, Mixed256w16::WGM, Mixed256w16::WGN, 1,
+     "256x256x64 w4x4"},
 };
 constexpr int kMixedNumConfigs = sizeof(kMixedConfigs) / sizeof(kMixedConfigs[0]);
 
@@ -250,7 +279,13 @@ hipError_t launch_one(const MixedProblem &p, hipStream_t s) {
   const long long tiles_m = ceil_div(p.M, S::BM), tiles_n = ceil_div(p.N, S::BN);
   const long long tiles = tiles_m * tiles_n;
   if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
-  return launch_kernel(mixed_kernel<S, FMT>, dim3((unsigned)tiles), dim3(S::NT), s, p,
+  // Largest element offset from a tile origin: BM rows of A, kMixedBK rows of B.
+  const bool off32 = (long long)S::BM * p.lda < (1LL << 31) &&
+                     (long long)kMixedBK * p.ldb < (1LL << 31);
+  if (off32)
+    return launch_kernel(mixed_kernel<S, FMT, true>, dim3((unsigned)tiles), dim3(S::NT), s, p,
+                         (int)tiles_m, (int)tiles_n);
+  return launch_kernel(mixed_kernel<S, FMT, false>, dim3((unsigned)tiles), dim3(S::NT), s, p,
                        (int)tiles_m, (int)tiles_n);
 }
 
@@ -285,6 +320,8 @@ hipError_t launch_mixed(int format, int index, const MixedProblem &p, hipStream_
   switch (index) {
     case 0: return bf ? launch_one<Mixed256, kMixedBf16>(p, s) : launch_one<Mixed256, kMixedF16>(p, s);
     case 1: return bf ? launch_one<Mixed128, kMixedBf16>(p, s) : launch_one<Mixed128, kMixedF16>(p, s);
+    case 2:
+      return bf ? launch_one<Mixed256w16, kMixedBf16>(p, s) : launch_one<Mixed256w16, kMixedF16>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
