@@ -7,7 +7,7 @@ Prints ONE JSON line with TFLOP/s, the roofline of the dominant kernel, the
 skinny K = 64 workload's HBM rate against the bandwidth measured in the same
 run, and the CPU oracle timed on a bounded sample as a reported baseline.
 
-  python bench.py [--gpus 1] [--steps 50] [--warmup 5]
+  python bench.py [--gpus 1] [--steps 100] [--warmup 20]
 """
 from __future__ import annotations
 
@@ -141,12 +141,15 @@ def cpu_baseline(a, b, target_s: float) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # Defaults long enough to reach steady clocks: a few milliseconds of work
+    # measure the clock ramp rather than the kernel.
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="square_4096")
     ap.add_argument("--variant", default="prod")
     ap.add_argument("--config", type=int, default=-1, help="launch-table entry (-1 = automatic)")
-    ap.add_argument("--skinny-steps", type=int, default=20)
+    ap.add_argument("--skinny-steps", type=int, default=100)
+    ap.add_argument("--skinny-warmup", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probes", action="store_true")
@@ -251,7 +254,7 @@ def main() -> int:
             g.gemm_f32_ex(sw.M, sw.N, sw.K, sta.data_ptr(), sw.K, stb.data_ptr(), sw.N,
                           stc.data_ptr(), sw.N, "prod", -1, s)
 
-        sms, _ = time_launches(sstep, args.skinny_steps, 3, stream)
+        sms, _ = time_launches(sstep, args.skinny_steps, args.skinny_warmup, stream)
         sbytes = rf.compulsory_bytes(sw.M, sw.N, sw.K)
         gbps = sbytes / (sms * 1e-3) / 1e9
         stf = rf.flops(sw.M, sw.N, sw.K) / (sms * 1e-3) / 1e12

@@ -42,10 +42,15 @@ from collections import OrderedDict, defaultdict
 HERE = os.path.dirname(os.path.abspath(__file__))
 # Sources that define the production kernel's code.
 PROD_SOURCES = [os.path.join(HERE, "csrc", n) for n in ("prod.hip", "tile_order.hpp")]
-OUR_KERNELS = re.compile(r"(gemm_f32_impl|prod_kernel|panel_kernel|strip_kernel|naive_kernel|tiled_kernel|"
-                         r"valu_kernel|mixed_kernel|stream_kernel|stream_tail|mfma_probe_kernel|"
-                         r"valu_probe_kernel|lds_probe_kernel|zero_kernel|prod_split_kernel|"
-                         r"splitk_reduce_kernel)")
+# Kernels of this library: everything in its namespace, plus the probes
+# (file-local kernels of probes.hip), matched on the raw kernel name.
+OUR_NAMESPACE = "gemm_f32_impl"
+OUR_PROBES = re.compile(r"\b(stream_kernel|stream_tail|mfma_probe_kernel|valu_probe_kernel|"
+                        r"lds_probe_kernel)\b")
+
+
+def is_ours(raw_name: str) -> bool:
+    return OUR_NAMESPACE in raw_name or OUR_PROBES.search(raw_name) is not None
 
 
 def prod_source_digest() -> str:
@@ -97,7 +102,7 @@ def cmd_trace(args) -> int:
                 cur = OrderedDict()
                 segs.append(cur)
                 continue
-            if cur is None or (args.only_ours and not OUR_KERNELS.search(name)):
+            if cur is None or (args.only_ours and not is_ours(r["Kernel_Name"])):
                 continue
             key = (name, _workgroups(r), _threads(r))
             dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
@@ -114,14 +119,14 @@ def cmd_trace(args) -> int:
     else:
         groups: dict = OrderedDict()
         for r in rows:
+            if args.only_ours and not is_ours(r["Kernel_Name"]):
+                continue
             key = (short_name(r["Kernel_Name"]), _workgroups(r), _threads(r))
             dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
             groups.setdefault(key, []).append(dur)
         lines += ["| kernel | workgroups | threads/WG | calls | avg us | min us | max us |",
                   "|---|---|---|---|---|---|---|"]
         for (name, wgs, wg), durs in groups.items():
-            if args.only_ours and not OUR_KERNELS.search(name):
-                continue
             lines.append(f"| `{name}` | {wgs} | {wg} | {len(durs)} | {statistics.mean(durs):.1f} "
                          f"| {min(durs):.1f} | {max(durs):.1f} |")
     text = "\n".join(lines) + "\n"
@@ -160,7 +165,7 @@ def _read_counter_csv(path: str):
     with open(path, newline="") as f:
         for row in csv.DictReader(f):
             name = row["Kernel_Name"]
-            if not OUR_KERNELS.search(name):
+            if not is_ours(name):
                 continue
             did = int(row["Dispatch_Id"])
             ent = by_dispatch.setdefault(did, {"name": short_name(name), "grid": int(row["Grid_Size"]),

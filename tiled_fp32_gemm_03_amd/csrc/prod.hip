@@ -540,6 +540,102 @@ __global__ void __launch_bounds__(S::NT)
   }
 }
 
+// One tile of the pipelined small-K kernel: issue the next tile's loads,
+// run this tile's MFMAs into `acc` while the previous tile's results in
+// `prev` go out as C stores, one store after every 8 MFMAs (the ratio of a
+// 64 x 64 wave tile at K = 64), then refill the stage.  Stores that drain
+// beside matrix work instead of in a burst after it keep the store path
+// busy through the whole tile.
+template <class S, bool KFULL, bool STORE>
+__device__ __forceinline__ void panel_pipe_step(f32x16 (&acc)[S::TM][S::TN],
+                                                const f32x16 (&prev)[S::TM][S::TN],
+                                                const Problem &p, int pm0, int pn0, int nm0,
+                                                int nn0, Stage<S> &st, float *as, float *bs,
+                                                int wm, int wn, int lane, int tid) {
+  constexpr int kStores = S::TM * S::TN * 4;
+  constexpr int kMfmas = S::TM * S::TN * (S::BK / 2);
+  static_assert(kMfmas % kStores == 0, "MFMAs must split evenly between stores");
+  load_global<S, !KFULL>(st, p, nm0, nn0, 0, tid);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int a = 0; a < S::TM; ++a)
+#pragma unroll
+    for (int b = 0; b < S::TN; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+  compute_stage<S>(acc, as, bs, wm, wn, lane);
+  if constexpr (STORE) {
+    store_c<S>(prev, p, pm0, pn0, wm, wn, lane, false);
+#pragma unroll
+    for (int g = 0; g < kStores; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, kMfmas / kStores, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x040, 1, 0);                 // VMEM write
+    }
+  }
+  __syncthreads();
+  // Loads done; this tile's stores (issued after them) may still drain.
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(STORE ? kStores : 0));
+  store_lds_as<S, !KFULL>(st, as, bs, tid);
+  __syncthreads();
+}
+
+// Small-K kernel with the C stores of tile i interleaved into the MFMAs of
+// tile i + 1 (two accumulator sets, alternating; the loop is unrolled by two
+// so each set has fixed registers).  Otherwise as panel_kernel: whole tiles
+// only, persistent, the last tile reloads itself.
+template <class S, bool KFULL>
+__global__ void __launch_bounds__(S::NT)
+    panel_pipe_kernel(Problem p, int tiles_m, int tiles_n) {
+  static_assert((S::A_STAGE + S::B_STAGE) * 4 <= kLdsBytes, "stage must fit in LDS");
+  __shared__ __attribute__((aligned(16))) float lds[S::A_STAGE + S::B_STAGE];
+  float *const as = lds;
+  float *const bs = lds + S::A_STAGE;
+  static_assert(S::TM * S::TN * 4 < 64, "vmcnt holds at most 63");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / S::WGN, wn = wave % S::WGN;
+  const int ntiles = tiles_m * tiles_n;
+  const int G = gridDim.x;
+  const int lid = xcd_remap(blockIdx.x, G);
+  if (lid >= ntiles) return;  // uniform per workgroup
+  const int n = (ntiles - lid + G - 1) / G;  // this workgroup's tiles: lid, lid + G, ...
+
+  bool interior;  // always true: the launcher passes whole tiles only
+  int m0, n0;
+  tile_origin<S>(lid, tiles_m, tiles_n, m0, n0, interior, p);
+  Stage<S> st;
+  load_global<S, !KFULL>(st, p, m0, n0, 0, tid);
+  store_lds_as<S, !KFULL>(st, as, bs, tid);
+  __syncthreads();
+
+  f32x16 acc0[S::TM][S::TN], acc1[S::TM][S::TN];
+  // Tile i sits in LDS; (m0, n0) is its origin, (pm0, pn0) the previous one.
+  int pm0 = m0, pn0 = n0, nm0, nn0;
+  tile_origin<S>(n > 1 ? lid + G : lid, tiles_m, tiles_n, nm0, nn0, interior, p);
+  panel_pipe_step<S, KFULL, false>(acc0, acc0, p, 0, 0, nm0, nn0, st, as, bs, wm, wn, lane, tid);
+  int i = 1;
+  for (; i + 1 < n; i += 2) {
+    pm0 = m0, pn0 = n0, m0 = nm0, n0 = nn0;
+    tile_origin<S>(lid + (i + 1) * G, tiles_m, tiles_n, nm0, nn0, interior, p);
+    panel_pipe_step<S, KFULL, true>(acc1, acc0, p, pm0, pn0, nm0, nn0, st, as, bs, wm, wn, lane,
+                                    tid);
+    pm0 = m0, pn0 = n0, m0 = nm0, n0 = nn0;
+    tile_origin<S>(i + 2 < n ? lid + (i + 2) * G : lid + (i + 1) * G, tiles_m, tiles_n, nm0,
+                   nn0, interior, p);
+    panel_pipe_step<S, KFULL, true>(acc0, acc1, p, pm0, pn0, nm0, nn0, st, as, bs, wm, wn, lane,
+                                    tid);
+  }
+  if (i < n) {  // one tile left: compute it while the previous one drains
+    pm0 = m0, pn0 = n0, m0 = nm0, n0 = nn0;
+    panel_pipe_step<S, KFULL, true>(acc1, acc0, p, pm0, pn0, m0, n0, st, as, bs, wm, wn, lane,
+                                    tid);
+    store_c<S>(acc1, p, m0, n0, wm, wn, lane, false);
+  } else {
+    store_c<S>(acc0, p, m0, n0, wm, wn, lane, false);
+  }
+}
+
 // Thin-M kernel for a bottom remainder strip of at most R rows (a strip too
 // thin for MFMA tiles: a 256-row tile holding one valid row would cost a
 // whole round of tiles).  Each workgroup owns 16 columns; its 256 threads are
@@ -630,6 +726,7 @@ const Entry kEntries[] = {
     {{256, 256, 16, 4, 4, 1, "256x256x16_w4x4"}, kKloop},
     {{256, 256, 16, 4, 2, 1, "256x256x16_w4x2"}, kKloop},
     {{256, 256, 32, 4, 4, 1, "256x256x32_w4x4"}, kKloop},
+    {{256, 128, 64, 4, 2, 1, "panel256x128_k64_pipe"}, kPanel},
 };
 constexpr int kNumConfigs = sizeof(kEntries) / sizeof(kEntries[0]);
 constexpr int kRemainderConfig = 3;  // thin edge strips
@@ -694,9 +791,13 @@ hipError_t launch_split(const Problem &p, int splits, int kc, float *ws, hipStre
 }
 
 // Whole tiles only: the caller (launch_prod) splits edge strips off first.
-template <class S>
+template <class S, bool PIPE = false>
 hipError_t launch_panel(const Problem &p, hipStream_t s) {
   if (p.K > S::BK || p.M % S::BM != 0 || p.N % S::BN != 0) return hipErrorInvalidValue;
+  if constexpr (PIPE) {
+    if (p.K == S::BK) return launch_grid<S, panel_pipe_kernel<S, true>>(p, s);
+    return launch_grid<S, panel_pipe_kernel<S, false>>(p, s);
+  }
   if (p.K == S::BK) return launch_grid<S, panel_kernel<S, true>>(p, s);
   return launch_grid<S, panel_kernel<S, false>>(p, s);
 }
@@ -716,6 +817,7 @@ hipError_t launch_one(int index, const Problem &p, hipStream_t s) {
     case 10: return launch_kloop<C10>(p, s);
     case 11: return launch_kloop<C11>(p, s);
     case 12: return launch_kloop<C12>(p, s);
+    case 13: return launch_panel<P9, true>(p, s);
 
     default: return hipErrorInvalidValue;
   }
@@ -755,15 +857,16 @@ bool prod_supports(int index, int M, int N, int K) {
   return kEntries[index].kind != kPanel || K <= kEntries[index].cfg.BK;
 }
 
-// Shape-based choice from measurements on MI355X: the small-K panel kernel
-// for K <= 64 with many tiles; 256x256x32 tiles (16 waves, one workgroup per
+// Shape-based choice from measurements on MI355X: the pipelined small-K
+// panel kernel (C stores interleaved with the next tile's MFMAs) for K <= 64
+// with many tiles; 256x256x32 tiles (16 waves, one workgroup per
 // CU) once there is a tile for every CU; 256x128x16 below that; 64x64 tiles
 // for smaller problems so that every CU has work.
 int prod_choose(int M, int N, int K) {
   const long long t256x256 = ceil_div(M, 256) * ceil_div(N, 256);
   const long long t256x128 = ceil_div(M, 256) * ceil_div(N, 128);
   const long long t64 = ceil_div(M, 64) * ceil_div(N, 64);
-  if (K <= 64 && t256x128 >= 1024) return 9;
+  if (K <= 64 && t256x128 >= 1024) return 13;
   if (t256x256 >= 256) return 12;
   if (t256x128 >= 512) return 2;
   if (t64 >= 2048) return 4;
