@@ -126,6 +126,23 @@ def test_small_k_panel_configs(g):
             _tol_check(_run(g, a, b, "prod", cfg), oracle.gemm(a, b), K, f"small-K cfg {cfg}")
 
 
+def test_small_k_many_tiles_per_workgroup(g):
+    """Tall products where every small-K workgroup walks several output tiles
+    (both parities of the tile count, K at and below the limit), checked on
+    sampled elements plus whole edge rows and columns."""
+    for cfg in _small_k_configs(g):
+        for (M, N, K) in [(16384, 2560, 64), (16384, 1536, 40), (8192, 3968, 64)]:
+            print(f"case: small-K many tiles config {cfg} {M}x{N}x{K}", flush=True)
+            a, b = make(M, N, K, "small_int", seed=cfg + M + N + K)
+            dev = _dev()
+            c = g.matmul(torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev), variant="prod",
+                         config=cfg)
+            torch.cuda.synchronize()
+            ii, jj = _sample_indices(M, N, 20000, seed=cfg + K)
+            got = c[torch.from_numpy(ii).to(dev), torch.from_numpy(jj).to(dev)].cpu().numpy()
+            assert np.array_equal(got, oracle.gemm_elems(a, b, ii, jj)), (cfg, M, N, K)
+
+
 def test_small_k_padded_leading_dimensions(g):
     dev = _dev()
     M, N, K = 1024, 768, 64

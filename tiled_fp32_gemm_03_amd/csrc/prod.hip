@@ -163,44 +163,44 @@ __device__ inline f32x4 place(const f32x4 &w, int meta) {
   return v;
 }
 
-template <class S, bool GUARD>
+template <class S, bool GUARD, bool DO_A = true, bool DO_B = true>
 __device__ inline void load_global(Stage<S> &st, const Problem &p, int m0,
                                    int n0, int k0, int tid) {
   const int arow = tid / (S::BK / 4), akq = (tid % (S::BK / 4)) * 4;
   const int bkr = tid / (S::BN / 4), bnq = (tid % (S::BN / 4)) * 4;
   if (!GUARD) {
 #pragma unroll
-    for (int i = 0; i < S::A_CHUNKS; ++i) {
+    for (int i = 0; i < (DO_A ? S::A_CHUNKS : 0); ++i) {
       const int gm = m0 + arow + i * S::A_ROWS_PER_PASS;
       st.a[i] = load4(p.A + (long long)gm * p.lda + k0 + akq);
       st.ameta[i] = kMetaFull;
     }
 #pragma unroll
-    for (int i = 0; i < S::B_CHUNKS; ++i) {
+    for (int i = 0; i < (DO_B ? S::B_CHUNKS : 0); ++i) {
       const int gk = k0 + bkr + i * S::B_ROWS_PER_PASS;
       st.b[i] = load4(p.B + (long long)gk * p.ldb + n0 + bnq);
       st.bmeta[i] = kMetaFull;
     }
   } else if (p.K >= 4 && p.N >= 4) {
 #pragma unroll
-    for (int i = 0; i < S::A_CHUNKS; ++i)
+    for (int i = 0; i < (DO_A ? S::A_CHUNKS : 0); ++i)
       st.a[i] = load_chunk_guarded(p.A, p.lda, m0 + arow + i * S::A_ROWS_PER_PASS, p.M,
                                    k0 + akq, p.K, st.ameta[i]);
 #pragma unroll
-    for (int i = 0; i < S::B_CHUNKS; ++i)
+    for (int i = 0; i < (DO_B ? S::B_CHUNKS : 0); ++i)
       st.b[i] = load_chunk_guarded(p.B, p.ldb, k0 + bkr + i * S::B_ROWS_PER_PASS, p.K,
                                    n0 + bnq, p.N, st.bmeta[i]);
   } else {
     // rows shorter than one chunk: per-element loads (tiny problems only)
 #pragma unroll
-    for (int i = 0; i < S::A_CHUNKS; ++i) {
+    for (int i = 0; i < (DO_A ? S::A_CHUNKS : 0); ++i) {
       const int gm = m0 + arow + i * S::A_ROWS_PER_PASS;
       const int gk = k0 + akq;
       st.a[i] = load_partial(p.A + (long long)gm * p.lda + gk, gm < p.M ? p.K - gk : 0);
       st.ameta[i] = kMetaFull;
     }
 #pragma unroll
-    for (int i = 0; i < S::B_CHUNKS; ++i) {
+    for (int i = 0; i < (DO_B ? S::B_CHUNKS : 0); ++i) {
       const int gk = k0 + bkr + i * S::B_ROWS_PER_PASS;
       const int gn = n0 + bnq;
       st.b[i] = load_partial(p.B + (long long)gk * p.ldb + gn, gk < p.K ? p.N - gn : 0);
@@ -211,17 +211,17 @@ __device__ inline void load_global(Stage<S> &st, const Problem &p, int m0,
 
 // Write one staged k step to LDS.  PLACED: the stage came from guarded loads
 // and each chunk is placed by its meta code; otherwise it is stored as is.
-template <class S, bool PLACED>
+template <class S, bool PLACED, bool DO_A = true, bool DO_B = true>
 __device__ inline void store_lds_as(const Stage<S> &st, float *as, float *bs,
                                     int tid) {
   const int arow = tid / (S::BK / 4), akq = (tid % (S::BK / 4)) * 4;
 #pragma unroll
-  for (int i = 0; i < S::A_CHUNKS; ++i)
+  for (int i = 0; i < (DO_A ? S::A_CHUNKS : 0); ++i)
     *reinterpret_cast<f32x4 *>(as + (arow + i * S::A_ROWS_PER_PASS) * S::SA + akq) =
         PLACED ? place(st.a[i], st.ameta[i]) : st.a[i];
   const int bkr = tid / (S::BN / 4), bnq = (tid % (S::BN / 4)) * 4;
 #pragma unroll
-  for (int i = 0; i < S::B_CHUNKS; ++i)
+  for (int i = 0; i < (DO_B ? S::B_CHUNKS : 0); ++i)
     *reinterpret_cast<f32x4 *>(bs + (bkr + i * S::B_ROWS_PER_PASS) * S::SB + bnq) =
         PLACED ? place(st.b[i], st.bmeta[i]) : st.b[i];
 }
@@ -636,6 +636,108 @@ __global__ void __launch_bounds__(S::NT)
   }
 }
 
+// One column tile of the A-resident small-K kernel: load the next tile's B
+// (the last tile reloads its own, so every step has the same shape), run
+// the first half of this tile's MFMAs from the resident A and B buffer `cur`
+// into `acc` while `prev` goes out as C stores (one per 4 MFMAs), write the
+// next B into the other buffer -- last read before the previous barrier --
+// run the second half, and synchronise.
+template <class S, bool KFULL, bool STORE>
+__device__ __forceinline__ void panel_arow_step(f32x16 (&acc)[S::TM][S::TN],
+                                                const f32x16 (&prev)[S::TM][S::TN],
+                                                const Problem &p, int m0, int pn0, int nn0,
+                                                Stage<S> &st, const float *as, const float *bcur,
+                                                float *bnext, int wm, int wn, int lane,
+                                                int tid) {
+  constexpr int kStores = S::TM * S::TN * 4;
+  constexpr int kMfmas = S::TM * S::TN * (S::BK / 2);
+  static_assert(kMfmas % kStores == 0, "MFMAs must split evenly between stores");
+  load_global<S, !KFULL, false, true>(st, p, m0, nn0, 0, tid);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int a = 0; a < S::TM; ++a)
+#pragma unroll
+    for (int b = 0; b < S::TN; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+  compute_stage<S, 0, S::BK / 16>(acc, as, bcur, wm, wn, lane);
+  if constexpr (STORE) {
+    store_c<S>(prev, p, m0, pn0, wm, wn, lane, false);
+#pragma unroll
+    for (int g = 0; g < kStores; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, kMfmas / kStores / 2, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x040, 1, 0);                     // VMEM write
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // The B loads are done; the stores issued after them may still drain.
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(STORE ? kStores : 0));
+  store_lds_as<S, !KFULL, false, true>(st, nullptr, bnext, tid);
+  compute_stage<S, S::BK / 16, S::BK / 8>(acc, as, bcur, wm, wn, lane);
+  __syncthreads();
+}
+
+// Small-K kernel with A resident in LDS.  Workgroup (panel, chunk) owns the
+// BM rows of panel `panel` -- all of K (<= BK), loaded once -- and the chunk
+// of BN-column tiles [t0, t1) of that panel.  Per tile only B moves (one of
+// two LDS buffers, written while the other is read), so a tile costs one
+// barrier and a third of the staging traffic of panel_pipe_kernel; C stores
+// drain during the next tile's MFMAs as there.  Whole tiles only.
+template <class S, bool KFULL>
+__global__ void __launch_bounds__(S::NT)
+    panel_arow_kernel(Problem p, int panels, int chunks, int tiles_n) {
+  static_assert((S::A_STAGE + 2 * S::B_STAGE) * 4 <= kLdsBytes, "A and two B buffers must fit");
+  __shared__ __attribute__((aligned(16))) float lds[S::A_STAGE + 2 * S::B_STAGE];
+  float *const as = lds;
+  float *const bs0 = lds + S::A_STAGE;
+  float *const bs1 = bs0 + S::B_STAGE;
+  static_assert(S::TM * S::TN * 4 < 64, "vmcnt holds at most 63");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / S::WGN, wn = wave % S::WGN;
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int panel = lid / chunks, chunk = lid % chunks;
+  if (panel >= panels) return;  // uniform per workgroup
+  const int t0 = (int)((long long)chunk * tiles_n / chunks);
+  const int t1 = (int)((long long)(chunk + 1) * tiles_n / chunks);
+  const int n = t1 - t0;  // >= 1: the launcher keeps chunks <= tiles_n
+  const int m0 = panel * S::BM;
+
+  Stage<S> st;
+  load_global<S, !KFULL>(st, p, m0, (t0 + panel % n) * S::BN, 0, tid);
+  store_lds_as<S, !KFULL>(st, as, bs0, tid);
+  __syncthreads();
+
+  f32x16 acc0[S::TM][S::TN], acc1[S::TM][S::TN];
+  // The i-th tile of this workgroup (in buffer i % 2) is column tile
+  // t0 + (i + rot) % n: workgroups start their runs at different columns so
+  // that the C rows written at any one time spread over all of C's columns
+  // (in lockstep every workgroup would write the same few columns, whose
+  // rows lie 4N bytes apart on a few memory channels).
+  const int rot = panel % n;
+  auto col = [&](int i) {
+    const int k = i < n ? i : n - 1;
+    return (t0 + (k + rot) % n) * S::BN;
+  };
+  panel_arow_step<S, KFULL, false>(acc0, acc0, p, m0, 0, col(1), st, as, bs0, bs1, wm, wn,
+                                   lane, tid);
+  int i = 1;
+  for (; i + 1 < n; i += 2) {
+    panel_arow_step<S, KFULL, true>(acc1, acc0, p, m0, col(i - 1), col(i + 1), st, as, bs1,
+                                    bs0, wm, wn, lane, tid);
+    panel_arow_step<S, KFULL, true>(acc0, acc1, p, m0, col(i), col(i + 2), st, as, bs0, bs1, wm,
+                                    wn, lane, tid);
+  }
+  if (i < n) {  // one tile left, in buffer 1: compute it while the previous one drains
+    panel_arow_step<S, KFULL, true>(acc1, acc0, p, m0, col(i - 1), col(i), st, as, bs1, bs0, wm,
+                                    wn, lane, tid);
+    store_c<S>(acc1, p, m0, col(i), wm, wn, lane, false);
+  } else {
+    store_c<S>(acc0, p, m0, col(i - 1), wm, wn, lane, false);
+  }
+}
+
 // Thin-M kernel for a bottom remainder strip of at most R rows (a strip too
 // thin for MFMA tiles: a 256-row tile holding one valid row would cost a
 // whole round of tiles).  Each workgroup owns 16 columns; its 256 threads are
@@ -727,6 +829,7 @@ const Entry kEntries[] = {
     {{256, 256, 16, 4, 2, 1, "256x256x16_w4x2"}, kKloop},
     {{256, 256, 32, 4, 4, 1, "256x256x32_w4x4"}, kKloop},
     {{256, 128, 64, 4, 2, 1, "panel256x128_k64_pipe"}, kPanel},
+    {{256, 128, 64, 4, 2, 1, "panel256x128_k64_arow"}, kPanel},
 };
 constexpr int kNumConfigs = sizeof(kEntries) / sizeof(kEntries[0]);
 constexpr int kRemainderConfig = 3;  // thin edge strips
@@ -735,7 +838,7 @@ constexpr int kRemainderConfig = 3;  // thin edge strips
 // kernel and device; computed on first use).
 constexpr int kMaxDevices = 64;
 
-template <void (*KERNEL)(Problem, int, int), int NT>
+template <auto KERNEL, int NT>
 int resident_workgroups() {
   static std::atomic<int> cache[kMaxDevices];
   int dev = 0;
@@ -802,6 +905,27 @@ hipError_t launch_panel(const Problem &p, hipStream_t s) {
   return launch_grid<S, panel_kernel<S, false>>(p, s);
 }
 
+// A-resident small-K launch: one workgroup per (row panel, chunk of column
+// tiles), enough chunks per panel to give every resident slot a workgroup.
+template <class S>
+hipError_t launch_arow(const Problem &p, hipStream_t s) {
+  if (p.K > S::BK || p.M % S::BM != 0 || p.N % S::BN != 0) return hipErrorInvalidValue;
+  const long long panels = p.M / S::BM, tiles_n = p.N / S::BN;
+  if (panels * tiles_n > 0x7fffffffLL) return hipErrorInvalidValue;
+  const bool full = p.K == S::BK;
+  const long long slots = full ? resident_workgroups<panel_arow_kernel<S, true>, S::NT>()
+                               : resident_workgroups<panel_arow_kernel<S, false>, S::NT>();
+  long long chunks = ceil_div(slots, panels);
+  if (chunks > tiles_n) chunks = tiles_n;
+  if (chunks < 1) chunks = 1;
+  const dim3 grid((unsigned)(panels * chunks));
+  if (full)
+    return launch_kernel(panel_arow_kernel<S, true>, grid, dim3(S::NT), s, p, (int)panels,
+                         (int)chunks, (int)tiles_n);
+  return launch_kernel(panel_arow_kernel<S, false>, grid, dim3(S::NT), s, p, (int)panels,
+                       (int)chunks, (int)tiles_n);
+}
+
 hipError_t launch_one(int index, const Problem &p, hipStream_t s) {
   switch (index) {
     case 0: return launch_kloop<C0>(p, s);
@@ -818,6 +942,7 @@ hipError_t launch_one(int index, const Problem &p, hipStream_t s) {
     case 11: return launch_kloop<C11>(p, s);
     case 12: return launch_kloop<C12>(p, s);
     case 13: return launch_panel<P9, true>(p, s);
+    case 14: return launch_arow<P9>(p, s);
 
     default: return hipErrorInvalidValue;
   }
@@ -857,16 +982,16 @@ bool prod_supports(int index, int M, int N, int K) {
   return kEntries[index].kind != kPanel || K <= kEntries[index].cfg.BK;
 }
 
-// Shape-based choice from measurements on MI355X: the pipelined small-K
-// panel kernel (C stores interleaved with the next tile's MFMAs) for K <= 64
-// with many tiles; 256x256x32 tiles (16 waves, one workgroup per
+// Shape-based choice from measurements on MI355X: the A-resident small-K
+// panel kernel (only B moves per tile; C stores interleaved with the next
+// tile's MFMAs) for K <= 64 with many tiles; 256x256x32 tiles (16 waves, one workgroup per
 // CU) once there is a tile for every CU; 256x128x16 below that; 64x64 tiles
 // for smaller problems so that every CU has work.
 int prod_choose(int M, int N, int K) {
   const long long t256x256 = ceil_div(M, 256) * ceil_div(N, 256);
   const long long t256x128 = ceil_div(M, 256) * ceil_div(N, 128);
   const long long t64 = ceil_div(M, 64) * ceil_div(N, 64);
-  if (K <= 64 && t256x128 >= 1024) return 13;
+  if (K <= 64 && t256x128 >= 1024) return 14;
   if (t256x256 >= 256) return 12;
   if (t256x128 >= 512) return 2;
   if (t64 >= 2048) return 4;
