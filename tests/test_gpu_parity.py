@@ -126,6 +126,24 @@ def test_small_k_panel_configs(g):
             _tol_check(_run(g, a, b, "prod", cfg), oracle.gemm(a, b), K, f"small-K cfg {cfg}")
 
 
+def test_kloop_entries_agree_bitwise_on_ragged_floats(g):
+    """Every k-loop entry sums each element in the same k order, whatever
+    the tile size, the tile's position or whether its edge tile was moved
+    back inside C (overlapping a neighbour) -- so on float inputs they must
+    agree bit for bit.  The shapes leave no thin remainder for any tile size
+    (a thin strip goes to the strip kernel, which sums K in another order)."""
+    kloop = [c for c in _prod_configs(g) if _supported(g, c, 1, 1, 65)]
+    for (M, N, K) in [(1000, 1003, 515), (3000, 300, 129), (700, 4000, 64)]:
+        for cfg in kloop:
+            t = g.gemm_f32_tile("prod", cfg, M, N, K)
+            assert M % t["BM"] * 8 > t["BM"] and N % t["BN"] * 8 > t["BN"], (cfg, M, N)
+        a, b = make(M, N, K, "normal", seed=M + N)
+        ref = _run(g, a, b, "prod", kloop[0])
+        for cfg in kloop[1:]:
+            print(f"case: bitwise agreement config {cfg} {M}x{N}x{K}", flush=True)
+            assert np.array_equal(_run(g, a, b, "prod", cfg), ref), (cfg, M, N, K)
+
+
 def test_small_k_many_tiles_per_workgroup(g):
     """Tall products where every small-K workgroup walks several output tiles
     (both parities of the tile count, K at and below the limit), checked on

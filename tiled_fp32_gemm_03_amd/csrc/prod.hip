@@ -303,6 +303,11 @@ __device__ inline void store_c(const f32x16 (&acc)[S::TM][S::TN],
   }
 }
 
+// Tile t's origin.  A last tile row or column that would overhang C is
+// moved back to end at C's edge (when C is at least one tile wide): it then
+// overlaps its neighbour, and both compute the shared elements with the same
+// k order, so they store identical values -- while the tile needs no guarded
+// loads.  Only a product narrower than one tile keeps guarded edges.
 template <class S>
 __device__ inline void tile_origin(int t, int tiles_m, int tiles_n, int &m0,
                                    int &n0, bool &interior, const Problem &p) {
@@ -310,6 +315,8 @@ __device__ inline void tile_origin(int t, int tiles_m, int tiles_n, int &m0,
   tile_coords(t, tiles_m, tiles_n, tm, tn);
   m0 = tm * S::BM;
   n0 = tn * S::BN;
+  if (m0 + S::BM > p.M && p.M >= S::BM) m0 = p.M - S::BM;
+  if (n0 + S::BN > p.N && p.N >= S::BN) n0 = p.N - S::BN;
   interior = (m0 + S::BM <= p.M) && (n0 + S::BN <= p.N);
 }
 
