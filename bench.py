@@ -225,7 +225,8 @@ def main() -> int:
                 args.variant, w.M, w.N, w.K, tile),
         },
         "wall_s_timed_region": round(wall, 4),
-        "device": {"name": props.name, "cus": props.multi_processor_count},
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                   **g.gemm_f32_device_props(0)},
     }
     del tc
     torch.cuda.empty_cache()

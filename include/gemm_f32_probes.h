@@ -71,6 +71,15 @@ long long gemm_f32_probe_valu_flops(int workgroups, int iters);
 int gemm_f32_probe_lds(int workgroups, int iters, float *out, void *stream);
 long long gemm_f32_probe_lds_bytes(int workgroups, int iters);
 
+/*
+ * gemm_f32_device_props -- properties of HIP device `device` that the
+ * roofline report quotes: compute units, peak engine clock (kHz), LDS bytes
+ * per compute unit, wave size and L2 bytes.  Any output pointer may be NULL.
+ * Returns GEMM_F32_BAD_ARG if the runtime cannot answer (no such device).
+ */
+int gemm_f32_device_props(int device, int *cus, int *clock_khz, int *lds_per_cu,
+                          int *wave_size, int *l2_bytes);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,7 +33,7 @@ def test_headers_declare_expected_entry_points():
             "gemm_f32_status_string", "gemm_f32_version", "gemm_f32_probe_stream",
             "gemm_f32_probe_mfma", "gemm_f32_probe_mfma_flops", "gemm_f32_probe_valu",
             "gemm_f32_probe_valu_flops", "gemm_f32_probe_lds", "gemm_f32_probe_lds_bytes",
-            "gemm_mixed", "gemm_mixed_num_configs", "gemm_mixed_tile", "gemm_f32_splitk",
+            "gemm_f32_device_props", "gemm_mixed", "gemm_mixed_num_configs", "gemm_mixed_tile", "gemm_f32_splitk",
             "gemm_f32_splitk_plan"} <= names
 
 

@@ -430,3 +430,9 @@ def test_lds_probe_runs(g):
     g.gemm_f32_probe_lds(8, 10, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert torch.isfinite(out).all().item() and torch.all(out >= 0).item()
+
+
+def test_device_props(g):
+    d = g.gemm_f32_device_props(0)
+    assert d["cus"] == torch.cuda.get_device_properties(0).multi_processor_count
+    assert d["wave_size"] == 64 and d["clock_mhz"] > 500 and d["lds_bytes_per_cu"] >= 65536

@@ -13,6 +13,7 @@ Raw C-ABI mirrors (same names and argument order as ``include/gemm_f32.h``):
   gemm_f32_probe_mfma(workgroups, iters, out, stream), gemm_f32_probe_mfma_flops(...)
   gemm_f32_probe_valu(workgroups, iters, out, stream), gemm_f32_probe_valu_flops(...)
   gemm_f32_probe_lds(workgroups, iters, out, stream), gemm_f32_probe_lds_bytes(...)
+  gemm_f32_device_props(device) -> dict
   gemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, config, splits, workspace,
                   workspace_bytes, stream), gemm_f32_splitk_plan(M, N, K, config, splits)
   gemm_mixed(M, N, K, A, lda, B, ldb, C, ldc, format, config, stream)
@@ -40,7 +41,8 @@ __all__ = [
     "gemm_f32", "gemm_f32_ex", "gemm_f32_tile", "gemm_f32_num_configs",
     "gemm_f32_status_string", "gemm_f32_version", "gemm_f32_last_error", "gemm_f32_probe_stream",
     "gemm_f32_probe_mfma", "gemm_f32_probe_mfma_flops", "gemm_f32_probe_valu",
-    "gemm_f32_probe_valu_flops", "gemm_f32_probe_lds", "gemm_f32_probe_lds_bytes", "matmul",
+    "gemm_f32_probe_valu_flops", "gemm_f32_probe_lds", "gemm_f32_probe_lds_bytes",
+    "gemm_f32_device_props", "matmul",
     "gemm_f32_splitk", "gemm_f32_splitk_plan", "matmul_splitk",
     "gemm_mixed", "gemm_mixed_tile", "gemm_mixed_num_configs", "matmul_mixed", "MIXED_FORMATS",
     "mixed_config_name",
@@ -89,6 +91,7 @@ _SIGS = {
     "gemm_mixed_num_configs": ([], _i),
     "gemm_mixed_tile": ([_i, _i, _i, _i, _ip, _ip, _ip, _ip, _ip], _i),
     "gemm_f32_probe_lds_bytes": ([_i, _i], _ll),
+    "gemm_f32_device_props": ([_i, _ip, _ip, _ip, _ip, _ip], _i),
 }
 for _name, (_args, _ret) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -199,6 +202,15 @@ def gemm_f32_probe_lds(workgroups, iters, out, stream=0) -> None:
 
 def gemm_f32_probe_lds_bytes(workgroups, iters) -> int:
     return int(_lib.gemm_f32_probe_lds_bytes(int(workgroups), int(iters)))
+
+
+def gemm_f32_device_props(device: int = 0) -> dict:
+    vals = [ctypes.c_int(0) for _ in range(5)]
+    _check(_lib.gemm_f32_device_props(int(device), *[ctypes.byref(v) for v in vals]),
+           "gemm_f32_device_props")
+    cus, clk, lds, wave, l2 = (v.value for v in vals)
+    return {"cus": cus, "clock_mhz": clk / 1000.0, "lds_bytes_per_cu": lds, "wave_size": wave,
+            "l2_bytes": l2}
 
 
 def gemm_f32_splitk_plan(M, N, K, config=-1, splits=0) -> dict:

@@ -223,3 +223,21 @@ extern "C" int gemm_f32_probe_lds(int workgroups, int iters, float *out, void *s
                                static_cast<hipStream_t>(stream), iters, out);
   return e == hipSuccess ? GEMM_F32_OK : GEMM_F32_LAUNCH_FAILED;
 }
+
+extern "C" int gemm_f32_device_props(int device, int *cus, int *clock_khz, int *lds_per_cu,
+                                     int *wave_size, int *l2_bytes) {
+  struct Q {
+    int *out;
+    hipDeviceAttribute_t attr;
+  };
+  const Q qs[] = {{cus, hipDeviceAttributeMultiprocessorCount},
+                  {clock_khz, hipDeviceAttributeClockRate},
+                  {lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor},
+                  {wave_size, hipDeviceAttributeWarpSize},
+                  {l2_bytes, hipDeviceAttributeL2CacheSize}};
+  for (const Q &q : qs) {
+    if (q.out == nullptr) continue;
+    if (hipDeviceGetAttribute(q.out, q.attr, device) != hipSuccess) return GEMM_F32_BAD_ARG;
+  }
+  return GEMM_F32_OK;
+}

@@ -20,8 +20,11 @@ only the scalar tail kernel), so that a
 counter run can attribute every dispatch between two markers -- a product
 may take more than one launch -- to the record that follows the marker.
 
-Each measurement prints one JSON line (kernel, ms per launch from HIP events
-on the launch stream, TFLOP/s, compulsory-byte GB/s, the tiled load model);
+Each measurement prints one JSON line (kernel; ms per launch from HIP events
+on the launch stream -- the mean over back-to-back calls, plus the median and
+minimum of the per-call times read from events between the calls; TFLOP/s,
+compulsory-byte GB/s, the tiled load model; with ``--cold`` the same timings
+for calls that each follow a 1 GiB fill, i.e. inputs out of the caches);
 a markdown table goes to stderr at the end.  Inputs come from the seeded
 generator and are resident on the GPU before timing.  This tool does not
 check results; the test suite does.
@@ -31,6 +34,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -72,6 +76,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--copy-mib", type=int, default=0)
     ap.add_argument("--alu-probes", action="store_true")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time each call after a 1 GiB fill (inputs out of the caches)")
     ap.add_argument("--max-naive-gflop", type=float, default=200.0,
                     help="skip the naive rung on workloads above this many GFLOP")
     args = ap.parse_args(argv)
@@ -87,18 +93,45 @@ def main(argv=None) -> int:
     stream = torch.cuda.current_stream(dev)
     s = stream.cuda_stream
 
-    def timed(fn, reps, warmup):
+    flush = None
+    if args.cold:
+        flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+
+        def flush():
+            g.gemm_f32_probe_stream(g.PROBE_FILL, flush_buf.numel(), 0, 0, flush_buf.data_ptr(), s)
+
+    def timed_stats(fn, reps, warmup, cold=False):
+        """(mean, median, min) ms per call.  Warm: the calls run back to back
+        with an event between consecutive calls (no extra work on the
+        stream); mean = whole span / reps.  Cold: a 1 GiB fill runs before
+        each call, outside its events."""
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record(stream)
-        for _ in range(reps):
+        if cold:
+            spans = []
+            for _ in range(reps):
+                flush()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                spans.append((e0, e1))
+            torch.cuda.synchronize()
+            per = [a.elapsed_time(b) for a, b in spans]
+            return sum(per) / len(per), statistics.median(per), min(per)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for i in range(reps):
             fn()
-        t1.record(stream)
+            ev[i + 1].record(stream)
         torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / max(reps, 1)
+        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+        return ev[0].elapsed_time(ev[reps]) / max(reps, 1), statistics.median(per), min(per)
+
+    def timed(fn, reps, warmup):
+        return timed_stats(fn, reps, warmup)[0]
 
     marker = torch.empty(4, device=dev)
 
@@ -202,27 +235,36 @@ def main(argv=None) -> int:
 
             mark()
 
-            ms = timed(call, reps, args.warmup if vname != "naive" else min(args.warmup, 1))
+            ms, ms_med, ms_min = timed_stats(call, reps,
+                                             args.warmup if vname != "naive" else min(args.warmup, 1))
             tflops = rf.flops(w.M, w.N, w.K) / (ms * 1e-3) / 1e12
             peak = rf.PEAK_BF16_MFMA_TFLOPS if mixed else rf.PEAK_FP32_MFMA_TFLOPS
             elem = 2 if mixed else 4
             rec = {"workload": wname, "kernel": label, "variant": vname, "config": tile["config"],
-                   "ms": round(ms, 5), "tflops": round(tflops, 3),
+                   "ms": round(ms, 5), "ms_median": round(ms_med, 5), "ms_min": round(ms_min, 5),
+                   "tflops": round(tflops, 3),
                    "frac_peak": round(tflops / peak, 4), "peak_tflops": peak,
                    "gbps_compulsory": round(rf.compulsory_bytes(w.M, w.N, w.K, elem) / (ms * 1e-3) / 1e9, 1),
                    "model_issued_load_bytes": elem * rf.issued_load_elements(
                        "prod" if (mixed or split) else vname, w.M, w.N, w.K, tile),
                    "flops": rf.flops(w.M, w.N, w.K)}
+            if args.cold:
+                cms, cmed, cmin = timed_stats(call, reps, 0, cold=True)
+                rec.update({"cold_ms": round(cms, 5), "cold_ms_median": round(cmed, 5),
+                            "cold_ms_min": round(cmin, 5)})
             rows.append(rec)
             print(json.dumps(rec), flush=True)
         del ops, tc
         torch.cuda.empty_cache()
 
-    print("\n| workload | kernel | ms | TFLOP/s | % of dtype peak | GB/s (compulsory) |", file=sys.stderr)
-    print("|---|---|---|---|---|---|", file=sys.stderr)
+    print("\n| workload | kernel | ms | TFLOP/s | % of dtype peak | GB/s (compulsory) | median ms | min ms |"
+          + (" cold median ms |" if args.cold else ""), file=sys.stderr)
+    print("|---|---|---|---|---|---|---|---|" + ("---|" if args.cold else ""), file=sys.stderr)
     for r in rows:
         print(f"| {r['workload']} | {r['kernel']} | {r['ms']:.4f} | {r['tflops']:.2f} | "
-              f"{100 * r['frac_peak']:.1f} | {r['gbps_compulsory']:.0f} |", file=sys.stderr)
+              f"{100 * r['frac_peak']:.1f} | {r['gbps_compulsory']:.0f} | {r['ms_median']:.4f} | "
+              f"{r['ms_min']:.4f} |" + (f" {r['cold_ms_median']:.4f} |" if args.cold else ""),
+              file=sys.stderr)
     return 0
 
 
