@@ -170,6 +170,19 @@ def test_all_ones_full_ragged_shape(g, fmt):
         assert torch.all(c == float(w.K)).item()
 
 
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_entries_agree_bitwise_on_ragged_floats(g, fmt):
+    """Every entry sums each element in the same k order, whatever the tile
+    size or whether its edge tiles were moved back inside C (overlapping a
+    neighbour), so they agree bit for bit on float inputs."""
+    for (M, N, K) in [(1000, 1003, 515), (700, 300, 129)]:
+        a, b = make_mixed(M, N, K, "normal", seed=M + N, fmt=fmt)
+        ref = _run(g, a, b, fmt, 0)
+        for cfg in range(1, g.gemm_mixed_num_configs()):
+            print(f"case: mixed {fmt} bitwise agreement config {cfg} {M}x{N}x{K}", flush=True)
+            assert np.array_equal(_run(g, a, b, fmt, cfg), ref), (fmt, cfg, M, N, K)
+
+
 def test_runs_on_the_given_stream(g):
     a, b = make_mixed(384, 384, 256, "small_int", seed=3, fmt="bf16")
     ta, tb = _to_dev(a, "bf16"), _to_dev(b, "bf16")

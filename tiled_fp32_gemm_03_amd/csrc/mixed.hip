@@ -201,7 +201,13 @@ __global__ void __launch_bounds__(S::NT)
   const int wm = wave % S::WGM, wn = wave / S::WGM;
   int tm, tn;
   tile_coords(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * S::BM, n0 = tn * S::BN;
+  // A last tile row or column that would overhang C is moved back to end at
+  // C's edge (when C is at least one tile wide): it overlaps its neighbour,
+  // both compute the shared elements in the same k order and store the same
+  // values, and the tile avoids element-wise edge loads.
+  int m0 = tm * S::BM, n0 = tn * S::BN;
+  if (m0 + S::BM > p.M && p.M >= S::BM) m0 = p.M - S::BM;
+  if (n0 + S::BN > p.N && p.N >= S::BN) n0 = p.N - S::BN;
   const bool fast = m0 + S::BM <= p.M && n0 + S::BN <= p.N;
   const int nk = (p.K + kMixedBK - 1) / kMixedBK;
 
