@@ -77,6 +77,17 @@ def _supported(g, cfg, M, N, K):
         return False
 
 
+def test_valu_entries_agree_bitwise_on_ragged_floats(g):
+    """Each element is one FMA chain in ascending k in every entry and tile
+    position, edge tiles moved inside C included: identical bits."""
+    for (M, N, K) in [(1000, 1003, 515), (700, 300, 129)]:
+        a, b = make(M, N, K, "normal", seed=M * N)
+        ref = _run(g, a, b, "valu", 0)
+        for cfg in range(1, g.gemm_f32_num_configs("valu")):
+            print(f"case: valu bitwise agreement config {cfg} {M}x{N}x{K}", flush=True)
+            assert np.array_equal(_run(g, a, b, "valu", cfg), ref), (cfg, M, N, K)
+
+
 def test_every_valu_config(g):
     """Every register-budget entry of the VALU rung: the k loop rolled and
     unrolled, K below, at and past one 8-deep step, ragged tiles."""

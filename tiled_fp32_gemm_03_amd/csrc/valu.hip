@@ -87,7 +87,13 @@ __global__ void __launch_bounds__(kVThreads) __attribute__((amdgpu_waves_per_eu(
   const int nk = (p.K + kVBK - 1) / kVBK;
 
   for (long long t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const int m0 = (int)(t / tiles_n) * kVT, n0 = (int)(t % tiles_n) * kVT;
+    // An overhanging last tile row or column is moved back to end at C's
+    // edge (when C is at least one tile wide); the overlap with its
+    // neighbour is stored twice with identical values (every element is one
+    // FMA chain in ascending k), and the tile needs no guarded loads.
+    int m0 = (int)(t / tiles_n) * kVT, n0 = (int)(t % tiles_n) * kVT;
+    if (m0 + kVT > p.M && p.M >= kVT) m0 = p.M - kVT;
+    if (n0 + kVT > p.N && p.N >= kVT) n0 = p.N - kVT;
     const bool interior = m0 + kVT <= p.M && n0 + kVT <= p.N;
     float acc[8][8];
 #pragma unroll
