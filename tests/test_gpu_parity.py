@@ -207,6 +207,22 @@ def test_thin_remainder_strips(g):
                 _tol_check(_run(g, a, b, "prod", cfg), oracle.gemm(a, b), K, f"strips cfg {cfg}")
 
 
+def test_strip_kernel_long_k(g):
+    """The thin-M strip kernel with K spanning many of its 128 k-slices,
+    column counts that leave a partial last group of 16, odd ldb (rows of B
+    only 4-byte aligned) and a single column."""
+    for cfg in (0, 12):
+        bm = g.gemm_f32_tile("prod", cfg, 1, 1, 1)["BM"]
+        for (r, N, K) in [(1, 1001, 2049), (8, 4095, 1500), (3, 16, 5000), (5, 17, 300),
+                          (2, 1, 700), (7, 33, 129)]:
+            M = bm + r
+            print(f"case: strip long-k cfg {cfg} {M}x{N}x{K}", flush=True)
+            a, b = make(M, N, K, "small_int", seed=cfg + r * N + K)
+            assert np.array_equal(_run(g, a, b, "prod", cfg), oracle.gemm(a, b)), (cfg, M, N, K)
+            a, b = make(M, N, K, "normal", seed=cfg + r + N * K)
+            _tol_check(_run(g, a, b, "prod", cfg), oracle.gemm(a, b), K, f"strip long-k cfg {cfg}")
+
+
 def test_guarded_windows_short_rows(g):
     """Rows of exactly 4 and of 1-3 elements (the per-element fallback), and
     K tails of 1-3 past a multiple of 4 (the shifted-window loads)."""

@@ -747,48 +747,76 @@ __global__ void __launch_bounds__(S::NT)
 
 // Thin-M kernel for a bottom remainder strip of at most R rows (a strip too
 // thin for MFMA tiles: a 256-row tile holding one valid row would cost a
-// whole round of tiles).  Each workgroup owns 16 columns; its 256 threads are
-// 16 columns x 16 k-slices (slice q takes k = q, q + 16, ...).  Each thread
-// accumulates R outputs in fp32 over its slice in ascending k; the 16 slice
-// sums are added in slice order through LDS, so the result is deterministic.
+// whole round of tiles).  The strip's time is the stream of B, so the kernel
+// is built to keep many 128-bit loads in flight: each workgroup owns 16
+// columns, and its 512 threads are 4 column quads x 128 k-slices (slice q
+// takes k = q, q + 128, ...), each lane loading 4 columns of a B row at once.
+// Each thread accumulates its R x 4 outputs in fp32 over its slice in
+// ascending k; the 128 slice sums are added in slice order through LDS, so the
+// result is deterministic.  Rows of B need only 4-byte alignment.
+constexpr int kStripThreads = 512;
+constexpr int kStripCols = 16;
+constexpr int kStripSlices = kStripThreads / (kStripCols / 4);
+
 template <int R>
-__global__ void __launch_bounds__(256) strip_kernel(Problem p) {
-  constexpr int KS = 16;
-  __shared__ float red[KS][R][16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 15;
-  const int ks = (lane >> 4) + 4 * wave;
-  const long long n = (long long)blockIdx.x * 16 + col;
-  float acc[R];
+__global__ void __launch_bounds__(kStripThreads) strip_kernel(Problem p) {
+  constexpr int KS = kStripSlices;
+  __shared__ float red[KS][R][kStripCols];
+  const int tid = threadIdx.x;
+  const int c4 = (tid & 3) * 4;  // first of this lane's 4 columns
+  const int ks = tid >> 2;       // k slice
+  const long long n0 = (long long)blockIdx.x * kStripCols;
+  float acc[R][4];
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = 0.f;
-  if (n < p.N) {
-    const float *bcol = p.B + n;
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[r][j] = 0.f;
+  const float *bp = p.B + n0 + c4;
+  if (n0 + kStripCols <= p.N) {  // whole workgroup inside: 128-bit loads
 #pragma unroll 8
     for (int k = ks; k < p.K; k += KS) {
-      const float b = bcol[(long long)k * p.ldb];
+      const f32x4 b = *reinterpret_cast<const f32x4u *>(bp + (long long)k * p.ldb);
 #pragma unroll
       for (int r = 0; r < R; ++r)
-        if (r < p.M) acc[r] += p.A[(long long)r * p.lda + k] * b;
+        if (r < p.M) {
+          const float a = p.A[(long long)r * p.lda + k];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[r][j] += a * b[j];
+        }
+    }
+  } else {  // last workgroup of a ragged strip: per-element guards
+    const int valid = (int)(p.N - n0) - c4;  // columns of this lane inside C
+    for (int k = ks; k < p.K; k += KS) {
+      float b[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = j < valid ? bp[(long long)k * p.ldb + j] : 0.f;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (r < p.M) {
+          const float a = p.A[(long long)r * p.lda + k];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[r][j] += a * b[j];
+        }
     }
   }
 #pragma unroll
-  for (int r = 0; r < R; ++r) red[ks][r][col] = acc[r];
-  __syncthreads();
-  if (tid < 16 * R) {
-    const int r = tid / 16, c = tid % 16;
-    const long long n2 = (long long)blockIdx.x * 16 + c;
-    if (r < p.M && n2 < p.N) {
-      float sum = 0.f;
+  for (int r = 0; r < R; ++r)
 #pragma unroll
+    for (int j = 0; j < 4; ++j) red[ks][r][c4 + j] = acc[r][j];
+  __syncthreads();
+  if (tid < kStripCols * R) {
+    const int r = tid / kStripCols, c = tid % kStripCols;
+    if (r < p.M && n0 + c < p.N) {
+      float sum = 0.f;
+#pragma unroll 16
       for (int q = 0; q < KS; ++q) sum += red[q][r][c];
-      p.C[(long long)r * p.ldc + n2] = sum;
+      p.C[(long long)r * p.ldc + n0 + c] = sum;
     }
   }
 }
 
 hipError_t launch_strip(const Problem &p, hipStream_t s) {
-  const dim3 grid((unsigned)ceil_div(p.N, 16)), block(256);
+  const dim3 grid((unsigned)ceil_div(p.N, kStripCols)), block(kStripThreads);
   if (p.M <= 1) return launch_kernel(strip_kernel<1>, grid, block, s, p);
   if (p.M <= 2) return launch_kernel(strip_kernel<2>, grid, block, s, p);
   if (p.M <= 4) return launch_kernel(strip_kernel<4>, grid, block, s, p);
