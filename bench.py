@@ -70,11 +70,14 @@ def measure_hbm(g, stream, reps: int = 8) -> dict:
 
 
 def measure_mfma(g, stream) -> float:
+    """fp32 MFMA probe: 8 independent accumulator chains per wave, two waves
+    per SIMD, about 1.7 ms per launch; 20 timed launches after 5 warm-up ones
+    so that the clock has settled (short runs read the clock ramp)."""
     import torch
-    wgs, iters = 256 * 4, 2000
+    wgs, iters = 256 * 2, 4000
     buf = torch.zeros(wgs * 4, device="cuda:0")
     ms, _ = time_launches(lambda: g.gemm_f32_probe_mfma(wgs, iters, buf.data_ptr(), stream.cuda_stream),
-                          5, 2, stream)
+                          20, 5, stream)
     return g.gemm_f32_probe_mfma_flops(wgs, iters) / (ms * 1e-3) / 1e12
 
 

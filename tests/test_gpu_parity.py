@@ -155,6 +155,51 @@ def test_kloop_entries_agree_bitwise_on_ragged_floats(g):
             assert np.array_equal(_run(g, a, b, "prod", cfg), ref), (cfg, M, N, K)
 
 
+LDS_DMA_ENTRY = 15  # 256x256x32 with direct-to-LDS loads
+REG_STAGED_ENTRY = 12  # the same tiles through registers
+
+
+def test_lds_dma_entry_matches_register_staged(g):
+    """The direct-to-LDS entry takes its direct path only when A and B rows
+    are 16-byte aligned and N % 4 == 0, and the register path for the K tail
+    and for tiles of products narrower than one tile.  It sums every element
+    in the same k order as the register-staged kernel with the same tiles,
+    so on float inputs the two agree bit for bit: K tails, tiles moved
+    inside C, products narrower than a tile, K below one step, workgroups
+    that walk two tiles, padded leading dimensions, and unaligned rows (the
+    fallback)."""
+    assert g.gemm_f32_tile("prod", LDS_DMA_ENTRY, 1, 1, 1) == {
+        **g.gemm_f32_tile("prod", REG_STAGED_ENTRY, 1, 1, 1), "config": LDS_DMA_ENTRY}
+    dev = _dev()
+    cases = [  # (M, N, K, pad_a, pad_b)
+        (1024, 1024, 1000, 0, 0), (1300, 1028, 512, 0, 0), (200, 512, 300, 0, 0),
+        (512, 200, 96, 0, 0), (4352, 4352, 256, 0, 0), (1024, 1024, 4, 0, 0),
+        (600, 1024, 2048, 0, 0), (777, 1028, 515, 4, 8), (1024, 1024, 1024, 1, 0),
+        (1024, 1020, 640, 0, 3)]
+    for (M, N, K, pa, pb) in cases:
+        print(f"case: lds-dma vs register-staged {M}x{N}x{K} pad {pa},{pb}", flush=True)
+        a, b = make(M, N, K, "normal", seed=M + 3 * N + 7 * K)
+        abuf = torch.zeros((M, K + pa), device=dev)
+        bbuf = torch.zeros((K, N + pb), device=dev)
+        abuf[:, :K] = torch.from_numpy(a).to(dev)
+        bbuf[:, :N] = torch.from_numpy(b).to(dev)
+        outs = []
+        for cfg in (REG_STAGED_ENTRY, LDS_DMA_ENTRY):
+            c = g.matmul(abuf[:, :K], bbuf[:, :N], variant="prod", config=cfg)
+            torch.cuda.synchronize()
+            outs.append(c.cpu().numpy())
+        assert np.array_equal(outs[0], outs[1]), (M, N, K, pa, pb)
+        ii, jj = _sample_indices(M, N, 4000, seed=M + K)
+        _tol_check(outs[1][ii, jj], oracle.gemm_elems(a, b, ii, jj), K, f"lds-dma {M}x{N}x{K}")
+
+
+def test_lds_dma_entry_integer_exact(g):
+    for (M, N, K) in [(1024, 1024, 1000), (520, 516, 260), (256, 256, 32)]:
+        print(f"case: lds-dma integer {M}x{N}x{K}", flush=True)
+        a, b = make(M, N, K, "small_int", seed=M * 5 + K)
+        assert np.array_equal(_run(g, a, b, "prod", LDS_DMA_ENTRY), oracle.gemm(a, b)), (M, N, K)
+
+
 def test_small_k_many_tiles_per_workgroup(g):
     """Tall products where every small-K workgroup walks several output tiles
     (both parities of the tile count, K at and below the limit), checked on

@@ -484,6 +484,206 @@ constexpr int vmcnt_wait_imm(int n) {
   return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
 }
 
+// ---- k-loop kernel with direct-to-LDS operand loads ---------------------
+// global_load_lds_dwordx4 writes each lane's 16 bytes straight into LDS at
+// the wave's base address + 16 * lane.  An interior k step then needs no
+// staging registers, no LDS write instructions and no wait in the middle of
+// the step: the next stage's loads are issued at the top of the step and
+// waited for just before the step's barrier.  One instruction fills 1 KB of
+// LDS, so A (rows of BK = 32 k-contiguous floats) is stored without padding,
+// with the 16-byte chunks of each row permuted (chunk c of row r sits at
+// position c ^ ((r >> 1) & 7)) so that the fragment reads of 16 consecutive
+// rows fall on distinct banks; a B row of BN = 256 floats is exactly one
+// instruction and keeps the padded pitch of the register-staged kernel.
+// Steps that cannot use it (the K tail, and every step of a tile that
+// overhangs a product narrower than one tile) go through registers and write
+// the same layout before the step's MFMAs.  Each element is summed in the
+// same k order as in prod_kernel, so the two give identical bits.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void global_void_t;
+
+__device__ inline void load_to_lds16(const float *src, float *lds_dst) {
+  __builtin_amdgcn_global_load_lds((global_void_t *)src, (lds_void_t *)lds_dst, 16, 0, 0);
+}
+
+template <class S>
+struct LdsDma {
+  static constexpr int CPR = S::BK / 4;           // 16-byte chunks per A row
+  static constexpr int RPB = 64 / CPR;            // A rows per 1 KB instruction
+  static constexpr int NW = S::NT / 64;
+  static constexpr int A_BLK = S::BM / RPB / NW;  // A instructions per wave
+  static constexpr int B_ROWS = S::BK / NW;       // B instructions (rows) per wave
+  static constexpr int A_STAGE = S::BM * S::BK;   // unpadded
+  static constexpr int B_STAGE = S::B_STAGE;
+  static_assert(S::BN == 256, "one B row per instruction");
+  static_assert(CPR == 8, "the row permutation is written for 8 chunks per A row");
+  static_assert(S::BM % (RPB * NW) == 0 && S::BK % NW == 0, "instructions split evenly");
+  static_assert(S::WTM % 16 == 0, "the permutation is the same for every 32-row block");
+};
+
+__device__ inline int a_chunk_perm(int r) { return (r >> 1) & 7; }
+
+template <class S>
+__device__ inline void lds_dma_issue(const Problem &p, int m0, int n0, int k0, float *as,
+                                     float *bs, int lane, int wave) {
+  using D = LdsDma<S>;
+  const int pos = lane % D::CPR;
+#pragma unroll
+  for (int j = 0; j < D::A_BLK; ++j) {
+    const int blk = wave * D::A_BLK + j;
+    const int r = blk * D::RPB + lane / D::CPR;
+    const int c = pos ^ a_chunk_perm(r);
+    load_to_lds16(p.A + (long long)(m0 + r) * p.lda + k0 + 4 * c, as + blk * 256);
+  }
+#pragma unroll
+  for (int j = 0; j < D::B_ROWS; ++j) {
+    const int k = wave * D::B_ROWS + j;
+    load_to_lds16(p.B + (long long)(k0 + k) * p.ldb + n0 + 4 * lane, bs + k * S::SB);
+  }
+}
+
+// Register-path write of one staged k step into the direct-load layout.
+template <class S, bool PLACED>
+__device__ inline void store_lds_perm_as(const Stage<S> &st, float *as, float *bs, int tid) {
+  const int arow = tid / (S::BK / 4), c = tid % (S::BK / 4);
+#pragma unroll
+  for (int i = 0; i < S::A_CHUNKS; ++i) {
+    const int r = arow + i * S::A_ROWS_PER_PASS;
+    *reinterpret_cast<f32x4 *>(as + r * S::BK + 4 * (c ^ a_chunk_perm(r))) =
+        PLACED ? place(st.a[i], st.ameta[i]) : st.a[i];
+  }
+  const int bkr = tid / (S::BN / 4), bnq = (tid % (S::BN / 4)) * 4;
+#pragma unroll
+  for (int i = 0; i < S::B_CHUNKS; ++i)
+    *reinterpret_cast<f32x4 *>(bs + (bkr + i * S::B_ROWS_PER_PASS) * S::SB + bnq) =
+        PLACED ? place(st.b[i], st.bmeta[i]) : st.b[i];
+}
+
+// All MFMAs of one k step from the direct-load layout (A chunks permuted).
+template <class S>
+__device__ inline void compute_stage_perm(f32x16 (&acc)[S::TM][S::TN], const float *as,
+                                          const float *bs, int wm, int wn, int lane) {
+  const int l32 = lane & 31, h = lane >> 5;
+  const int perm = a_chunk_perm(l32);
+  const float *a_row = as + (wm * S::WTM + l32) * S::BK;
+  const float *b_base = bs + (4 * h) * S::SB + wn * S::WTN + l32;
+#pragma unroll
+  for (int kg = 0; kg < S::BK / 8; ++kg) {
+    f32x4 af[S::TM];
+    float bf[S::TN][4];
+    const int pos = (2 * kg + h) ^ perm;
+#pragma unroll
+    for (int tm = 0; tm < S::TM; ++tm)
+      af[tm] = *reinterpret_cast<const f32x4 *>(a_row + tm * 32 * S::BK + 4 * pos);
+#pragma unroll
+    for (int tn = 0; tn < S::TN; ++tn)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) bf[tn][s] = b_base[(kg * 8 + s) * S::SB + tn * 32];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int tm = 0; tm < S::TM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < S::TN; ++tn)
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x2f32(bf[tn][s], af[tm][s], acc[tm][tn],
+                                                             0, 0, 0);
+  }
+}
+
+// The persistent tile loop of prod_kernel with direct-to-LDS loads.  The
+// launcher guarantees 16-byte aligned rows of A and B (pointers and leading
+// dimensions) and N % 4 == 0, so every tile origin is 16-byte aligned.
+template <class S>
+__global__ void __launch_bounds__(S::NT) lds_dma_kernel(Problem p, int tiles_m, int tiles_n) {
+  using D = LdsDma<S>;
+  static_assert(2 * (D::A_STAGE + D::B_STAGE) * 4 <= kLdsBytes, "two stages must fit in LDS");
+  __shared__ __attribute__((aligned(16))) float lds[2 * (D::A_STAGE + D::B_STAGE)];
+  float *const as0 = lds;
+  float *const bs0 = lds + 2 * D::A_STAGE;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / S::WGN, wn = wave % S::WGN;
+  const int ntiles = tiles_m * tiles_n;
+  const int nk = (p.K + S::BK - 1) / S::BK;
+  const int G = gridDim.x;
+  const int lid = xcd_remap(blockIdx.x, G);
+  if (lid >= ntiles) return;  // uniform per workgroup
+  const int my_tiles = (ntiles - lid + G - 1) / G;
+  const long long steps = (long long)my_tiles * nk;
+
+  int t = lid, kt = 0;
+  int m0, n0;
+  bool interior;
+  tile_origin<S>(t, tiles_m, tiles_n, m0, n0, interior, p);
+
+  f32x16 acc[S::TM][S::TN];
+#pragma unroll
+  for (int i = 0; i < S::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < S::TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  Stage<S> st;
+  if (interior && S::BK <= p.K) {
+    lds_dma_issue<S>(p, m0, n0, 0, as0, bs0, lane, wave);
+  } else {
+    const bool g = load_step<S>(st, p, m0, n0, 0, interior, tid);
+    if (g)
+      store_lds_perm_as<S, true>(st, as0, bs0, tid);
+    else
+      store_lds_perm_as<S, false>(st, as0, bs0, tid);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(0));
+  __syncthreads();
+
+  for (long long it = 0; it < steps; ++it) {
+    const int cur = (int)(it & 1);
+    const bool more = it + 1 < steps;
+    int nt = t, nkt = kt + 1;
+    int nm0 = m0, nn0 = n0;
+    bool ninterior = interior;
+    if (nkt == nk) {
+      nkt = 0;
+      nt = t + G;
+      if (more) tile_origin<S>(nt, tiles_m, tiles_n, nm0, nn0, ninterior, p);
+    }
+    if (more) {
+      // The other stage was last read before the previous barrier.
+      float *const an = as0 + (cur ^ 1) * D::A_STAGE;
+      float *const bn = bs0 + (cur ^ 1) * D::B_STAGE;
+      const int nk0 = nkt * S::BK;
+      if (ninterior && nk0 + S::BK <= p.K) {
+        lds_dma_issue<S>(p, nm0, nn0, nk0, an, bn, lane, wave);
+      } else {  // rare: written before this step's MFMAs, so no stage stays live
+        const bool g = load_step<S>(st, p, nm0, nn0, nk0, ninterior, tid);
+        if (g)
+          store_lds_perm_as<S, true>(st, an, bn, tid);
+        else
+          store_lds_perm_as<S, false>(st, an, bn, tid);
+      }
+    }
+    compute_stage_perm<S>(acc, as0 + cur * D::A_STAGE, bs0 + cur * D::B_STAGE, wm, wn, lane);
+    if (kt == nk - 1) {
+      store_c<S>(acc, p, m0, n0, wm, wn, lane, !interior);
+#pragma unroll
+      for (int i = 0; i < S::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < S::TN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(0));  // this wave's direct loads landed
+    __syncthreads();
+    t = nt;
+    kt = nkt;
+    m0 = nm0;
+    n0 = nn0;
+    interior = ninterior;
+  }
+}
+
 // Small-K kernel: the whole K (<= BK) of a tile fits one LDS stage, so each
 // iteration of the persistent loop is one complete tile.  It covers only
 // whole tiles (the launcher sends edge strips to the k-loop kernel), which
@@ -865,6 +1065,7 @@ const Entry kEntries[] = {
     {{256, 256, 32, 4, 4, 1, "256x256x32_w4x4"}, kKloop},
     {{256, 128, 64, 4, 2, 1, "panel256x128_k64_pipe"}, kPanel},
     {{256, 128, 64, 4, 2, 1, "panel256x128_k64_arow"}, kPanel},
+    {{256, 256, 32, 4, 4, 1, "256x256x32_w4x4_ldsdma"}, kKloop},
 };
 constexpr int kNumConfigs = sizeof(kEntries) / sizeof(kEntries[0]);
 constexpr int kRemainderConfig = 3;  // thin edge strips
@@ -909,6 +1110,17 @@ hipError_t launch_grid(const Problem &p, hipStream_t s) {
 template <class S>
 hipError_t launch_kloop(const Problem &p, hipStream_t s) {
   return launch_grid<S, prod_kernel<S>>(p, s);
+}
+
+// The direct-to-LDS kernel when A and B rows are 16-byte aligned and
+// N % 4 == 0; otherwise the register-staged kernel with the same tiles.
+template <class S>
+hipError_t launch_lds_dma(const Problem &p, hipStream_t s) {
+  const bool aligned = (reinterpret_cast<uintptr_t>(p.A) & 15) == 0 &&
+                       (reinterpret_cast<uintptr_t>(p.B) & 15) == 0 && (p.lda & 3) == 0 &&
+                       (p.ldb & 3) == 0 && (p.N & 3) == 0;
+  if (!aligned) return launch_kloop<S>(p, s);
+  return launch_grid<S, lds_dma_kernel<S>>(p, s);
 }
 
 // Split-K launch: every (tile, split) pair is one workgroup (grid y = the
@@ -978,6 +1190,7 @@ hipError_t launch_one(int index, const Problem &p, hipStream_t s) {
     case 12: return launch_kloop<C12>(p, s);
     case 13: return launch_panel<P9, true>(p, s);
     case 14: return launch_arow<P9>(p, s);
+    case 15: return launch_lds_dma<C12>(p, s);
 
     default: return hipErrorInvalidValue;
   }
@@ -1020,14 +1233,15 @@ bool prod_supports(int index, int M, int N, int K) {
 // Shape-based choice from measurements on MI355X: the A-resident small-K
 // panel kernel (only B moves per tile; C stores interleaved with the next
 // tile's MFMAs) for K <= 64 with many tiles; 256x256x32 tiles (16 waves, one workgroup per
-// CU) once there is a tile for every CU; 256x128x16 below that; 64x64 tiles
+// CU, direct-to-LDS loads when the rows allow them) once there is a tile for every CU;
+// 256x128x16 below that; 64x64 tiles
 // for smaller problems so that every CU has work.
 int prod_choose(int M, int N, int K) {
   const long long t256x256 = ceil_div(M, 256) * ceil_div(N, 256);
   const long long t256x128 = ceil_div(M, 256) * ceil_div(N, 128);
   const long long t64 = ceil_div(M, 64) * ceil_div(N, 64);
   if (K <= 64 && t256x128 >= 1024) return 14;
-  if (t256x256 >= 256) return 12;
+  if (t256x256 >= 256) return 15;
   if (t256x128 >= 512) return 2;
   if (t64 >= 2048) return 4;
   return 3;
