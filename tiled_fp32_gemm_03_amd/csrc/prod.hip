@@ -684,6 +684,313 @@ __global__ void __launch_bounds__(S::NT) lds_dma_kernel(Problem p, int tiles_m, 
   }
 }
 
+// ---- 64x64 tiles with K split over the waves, 3-stage direct-load pipe --
+// For products with about one 64x64 tile per CU (1024^3 has 256), where a
+// k step of a 64x64 tile is too short to hide the latency of its loads.
+// Each of the 4 waves computes the whole 64x64 tile over its own quarter of
+// every 64-deep k step (k in [16w, 16w + 16) of the step) with
+// v_mfma_f32_16x16x4_f32: 16 independent 16x16 accumulator blocks per wave,
+// so one wave per SIMD keeps the matrix pipe busy.  The four partial tiles
+// are added in wave order through LDS at the end of the tile, so the result
+// is deterministic (but summed in a different order from the other entries).
+// Operands arrive by global_load_lds_dwordx4 into three LDS stages: the
+// loads for step i + 3 are issued during step i, into the stage whose
+// fragments every wave already holds in registers (fragments are read one
+// step ahead), so each load has two steps to land.
+//
+// MFMA operand roles: B is the first operand, A the second, so lane l of
+// block (bm, bn) holds C[m = 16 bm + l % 16][n = 16 bn + 4 (l / 16) + r],
+// r = 0..3.  Within a wave's 16 k of a step, MFMA t takes k = 4 g + t for
+// lane group g = l / 16, so a lane's A operand for t = 0..3 is one 128-bit
+// LDS read.  LDS layouts (16-byte chunks, rows of 64 floats):
+//   A: chunk c of row r at position c ^ (r & 15);
+//   B: chunk c of k row k at position c ^ (4 ((k >> 2) & 3)).
+// Both make the fragment reads of a wave conflict-free.
+using KsTile = Tile<64, 64, 64, 2, 2, false>;  // staging map for the register path
+constexpr int kKsStages = 3;
+constexpr int kKsStageFloats = 64 * 64 * 2;   // A and B, unpadded
+constexpr int kKsRedFloats = 4 * 64 * 64;     // the four partial tiles
+constexpr int kKsDmaPerWave = 8;              // 4 A + 4 B instructions of 1 KB
+
+// The direct loads of this kernel are issued from inline assembly, with an
+// SGPR base address, a per-lane 32-bit byte offset and the wave's LDS
+// destination in M0, so that the compiler does not see them as LDS writes:
+// it would otherwise wait for every outstanding one (vmcnt(0)) before each
+// later LDS read, which would serialise the pipeline.  The kernel orders
+// them itself: explicit vmcnt waits before each barrier, and every LDS read
+// of a stage happens after the barrier that follows its loads.
+__device__ inline void ks_load_to_lds16(unsigned voff, const float *sbase, unsigned lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+__device__ inline int ks_a_pos(int r, int c) { return r * 16 + (c ^ (r & 15)); }
+__device__ inline int ks_b_pos(int k, int c) { return k * 16 + (c ^ (4 * ((k >> 2) & 3))); }
+
+template <bool PLACED>
+__device__ inline void ks_store_stage(const Stage<KsTile> &sg, float *st, int tid) {
+  const int arow = tid / 16, c = tid % 16;
+#pragma unroll
+  for (int i = 0; i < KsTile::A_CHUNKS; ++i) {
+    const int r = arow + i * KsTile::A_ROWS_PER_PASS;
+    *reinterpret_cast<f32x4 *>(st + 4 * ks_a_pos(r, c)) =
+        PLACED ? place(sg.a[i], sg.ameta[i]) : sg.a[i];
+  }
+#pragma unroll
+  for (int i = 0; i < KsTile::B_CHUNKS; ++i) {
+    const int k = arow + i * KsTile::B_ROWS_PER_PASS;
+    *reinterpret_cast<f32x4 *>(st + 64 * 64 + 4 * ks_b_pos(k, c)) =
+        PLACED ? place(sg.b[i], sg.bmeta[i]) : sg.b[i];
+  }
+}
+
+struct KsFrag {
+  f32x4 a[4];     // per row block bm: A[16 bm + l%16][16 w + 4 g + t], t = 0..3
+  float b[4][4];  // per column block bn and t: B[16 w + 4 g + t][16 bn + l%16]
+};
+
+__device__ inline void ks_read_frag(KsFrag &f, const float *st, int lane, int wave) {
+  const int l16 = lane & 15, g = lane >> 4;
+  const int ca = 4 * wave + g;  // A chunk holding k = 16 w + 4 g .. + 3
+#pragma unroll
+  for (int bm = 0; bm < 4; ++bm)
+    f.a[bm] = *reinterpret_cast<const f32x4 *>(st + 4 * ks_a_pos(16 * bm + l16, ca));
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int k = 16 * wave + 4 * g + t;
+#pragma unroll
+    for (int bn = 0; bn < 4; ++bn) {
+      const int n = 16 * bn + l16;
+      f.b[bn][t] = st[64 * 64 + 4 * ks_b_pos(k, n >> 2) + (n & 3)];
+    }
+  }
+}
+
+// The step's 64 MFMAs in 8 groups of 8; with DMA, direct load q of the next
+// stage is issued after group q, so its issue overlaps the matrix work of a
+// lone wave.
+template <bool DMA>
+__device__ inline void ks_mfma(f32x4 (&acc)[4][4], const KsFrag &f, const unsigned (&voff)[8],
+                               const float *abase, const float *bbase, unsigned lds_a,
+                               unsigned lds_b) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int bm = 2 * half; bm < 2 * half + 2; ++bm)
+#pragma unroll
+        for (int bn = 0; bn < 4; ++bn)
+          acc[bm][bn] = __builtin_amdgcn_mfma_f32_16x16x4f32(f.b[bn][t], f.a[bm][t],
+                                                             acc[bm][bn], 0, 0, 0);
+      if constexpr (DMA) {
+        __builtin_amdgcn_sched_barrier(0);  // keep each load after its group
+        const int q = 2 * t + half;
+        if (q < 4)
+          ks_load_to_lds16(voff[q], abase, lds_a + q * 4 * 64 * 4);
+        else
+          ks_load_to_lds16(voff[q], bbase, lds_b + (q - 4) * 4 * 64 * 4);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+}
+
+// Waits until this wave's LDS operations have completed (as a builtin, so
+// the compiler knows the fragment registers are ready), then the workgroup
+// barrier.  Unlike __syncthreads() it does not wait for outstanding
+// vector-memory loads, so direct loads of later steps stay in flight; the
+// memory clobber keeps the compiler from moving memory accesses across it.
+constexpr int kLgkmWait0 = 0xF | (0x3 << 14) | (0x7 << 4);  // lgkmcnt(0) only
+
+__device__ inline void ks_lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(kLgkmWait0);
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// The launcher guarantees M, N >= 64 (every tile lies inside C after the
+// edge shift), N % 4 == 0, 16-byte aligned rows of A and B, and leading
+// dimensions below 2^24 (the per-lane byte offsets fit in 32 bits).
+__global__ void __launch_bounds__(256) ksplit_kernel(Problem p, int tiles_m, int tiles_n) {
+  static_assert((kKsStages * kKsStageFloats + kKsRedFloats) * 4 <= kLdsBytes, "LDS budget");
+  __shared__ __attribute__((aligned(16))) float lds[kKsStages * kKsStageFloats + kKsRedFloats];
+  float *const red = lds + kKsStages * kKsStageFloats;
+  const unsigned lds_u = (unsigned)(uintptr_t)(lds_void_t *)lds;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ntiles = tiles_m * tiles_n;
+  const int nk = (p.K + 63) / 64;
+  const int G = gridDim.x;
+  const int lid = xcd_remap(blockIdx.x, G);
+  if (lid >= ntiles) return;  // uniform per workgroup
+  const int my_tiles = (ntiles - lid + G - 1) / G;
+  const int steps = my_tiles * nk;
+  const bool k_tail = (p.K & 63) != 0;  // the last step of every tile is partial
+
+  // Per-lane byte offsets of this wave's direct loads from the step's base
+  // addresses: q < 4 are A rows 16 w + 4 q + l / 16, the others B k rows
+  // 16 w + 4 (q - 4) + l / 16; the chunk is permuted as in the LDS layout.
+  unsigned voff[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = 16 * wave + 4 * q + (lane >> 4);
+    const int c = (lane & 15) ^ (r & 15);
+    voff[q] = (unsigned)(((long long)r * p.lda + 4 * c) * 4);
+    const int k = 16 * wave + 4 * q + (lane >> 4);
+    const int cb = (lane & 15) ^ (4 * ((k >> 2) & 3));
+    voff[4 + q] = (unsigned)(((long long)k * p.ldb + 4 * cb) * 4);
+  }
+  const unsigned wave_a = (unsigned)(16 * wave * 64 * 4);            // LDS bytes
+  const unsigned wave_b = (unsigned)((64 * 64 + 16 * wave * 64) * 4);
+
+  // The issue side walks steps it + 3 ahead of the consumer: its tile, k
+  // step and tile origin are kept incrementally.
+  int is_t = 0, is_k = 0, is_m0 = 0, is_n0 = 0;
+  auto issue_origin = [&]() __attribute__((always_inline)) {
+    bool interior;
+    tile_origin<KsTile>(lid + is_t * G, tiles_m, tiles_n, is_m0, is_n0, interior, p);
+  };
+  auto issue_advance = [&]() __attribute__((always_inline)) {
+    if (++is_k == nk) {
+      is_k = 0;
+      ++is_t;
+      if (is_t < my_tiles) issue_origin();
+    }
+  };
+  auto issue_direct = [&]() __attribute__((always_inline)) {
+    return !k_tail || is_k != nk - 1;
+  };
+  // Register path for one step (the K tail): loads, placement, LDS writes.
+  auto issue_regs = [&](float *st) __attribute__((always_inline)) {
+    Stage<KsTile> sg;
+    const bool g = load_step<KsTile>(sg, p, is_m0, is_n0, is_k * 64, true, tid);
+    if (g)
+      ks_store_stage<true>(sg, st, tid);
+    else
+      ks_store_stage<false>(sg, st, tid);
+    // Nothing of this path stays outstanding: without this wait the
+    // compiler, merging paths, would wait on all vector memory before later
+    // LDS reads, which includes the direct loads in flight.
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(0));
+  };
+  auto abase_of = [&]() __attribute__((always_inline)) {
+    return p.A + (long long)is_m0 * p.lda + is_k * 64;
+  };
+  auto bbase_of = [&]() __attribute__((always_inline)) {
+    return p.B + (long long)(is_k * 64) * p.ldb + is_n0;
+  };
+
+  f32x4 acc[4][4];
+  issue_origin();
+  // Prologue: steps 0..2 in flight, step 0 visible, its fragments read.
+  for (int s = 0; s < kKsStages && s < steps; ++s) {
+    const unsigned st = lds_u + s * kKsStageFloats * 4;
+    if (issue_direct()) {
+      const float *ab = abase_of(), *bb = bbase_of();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        ks_load_to_lds16(voff[q], ab, st + wave_a + q * 4 * 64 * 4);
+        ks_load_to_lds16(voff[4 + q], bb, st + wave_b + q * 4 * 64 * 4);
+      }
+    } else {
+      issue_regs(lds + s * kKsStageFloats);
+    }
+    issue_advance();
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(0));
+  ks_lds_barrier();
+  KsFrag f0, f1;
+  ks_read_frag(f0, lds, lane, wave);
+
+  // One step: `fc` holds this step's fragments, `fn` receives the next's.
+  auto step = [&](int it, KsFrag &fc, KsFrag &fn) __attribute__((always_inline)) {
+    const int cur = it % kKsStages;
+    // Stage of step it + 1 has landed (own loads), and every wave holds the
+    // fragments of step it (own reads), so after the barrier stage `cur`
+    // may be refilled and stage it + 1 may be read.  Step it + 2 is the
+    // issue side's previous step.
+    if (it + 1 < steps) {
+      const bool next2_direct =
+          it + 2 < steps && (!k_tail || (is_k + nk - 1) % nk != nk - 1);
+      if (next2_direct)
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(kKsDmaPerWave));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(0));
+    }
+    ks_lds_barrier();
+    if (it + 1 < steps)
+      ks_read_frag(fn, lds + ((it + 1) % kKsStages) * kKsStageFloats, lane, wave);
+    // Step it + 3 goes into stage `cur`: direct loads spread over this
+    // step's MFMAs, or (for a K tail) the register path before them.
+    if (it + kKsStages < steps) {
+      const unsigned st = lds_u + cur * kKsStageFloats * 4;
+      if (issue_direct()) {
+        ks_mfma<true>(acc, fc, voff, abase_of(), bbase_of(), st + wave_a, st + wave_b);
+      } else {
+        issue_regs(lds + cur * kKsStageFloats);
+        ks_mfma<false>(acc, fc, voff, nullptr, nullptr, 0, 0);
+      }
+      issue_advance();
+    } else {
+      ks_mfma<false>(acc, fc, voff, nullptr, nullptr, 0, 0);
+    }
+  };
+  // Tile done: add the four partial tiles in wave order and store.
+  auto finish_tile = [&](int t) __attribute__((always_inline)) {
+    int m0, n0;
+    bool interior;
+    tile_origin<KsTile>(lid + t * G, tiles_m, tiles_n, m0, n0, interior, p);
+    const int l16 = lane & 15, g = lane >> 4;
+    float *mine = red + wave * 64 * 64;
+#pragma unroll
+    for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+      for (int bn = 0; bn < 4; ++bn)
+        *reinterpret_cast<f32x4 *>(mine + 4 * ks_a_pos(16 * bm + l16, 4 * bn + g)) =
+            acc[bm][bn];
+    ks_lds_barrier();
+    // Wave w finishes rows 16 w .. 16 w + 15: lane (row, q) holds chunks
+    // 4 j + q, j = 0..3, of its row.
+    const int row = 16 * wave + (lane >> 2), q = lane & 3;
+    const int gm = m0 + row;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = 4 * j + q;
+      f32x4 v = *reinterpret_cast<const f32x4 *>(red + 4 * ks_a_pos(row, c));
+#pragma unroll
+      for (int w = 1; w < 4; ++w)
+        v += *reinterpret_cast<const f32x4 *>(red + w * 64 * 64 + 4 * ks_a_pos(row, c));
+      const int gn = n0 + 4 * c;
+      *reinterpret_cast<f32x4u *>(p.C + (long long)gm * p.ldc + gn) = v;
+    }
+    // The partial-tile buffer is rewritten only at the next tile's end,
+    // after the barriers of that tile's steps.
+  };
+
+  // Tile loop outside, k steps inside (unrolled by two so that the fragment
+  // sets keep fixed registers); the accumulators stay in one register class.
+  int it = 0;
+  for (int t = 0; t < my_tiles; ++t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kk = 0; kk + 1 < nk; kk += 2, it += 2) {
+      step(it, f0, f1);
+      step(it + 1, f1, f0);
+    }
+    if (nk & 1) {
+      step(it, f0, f1);
+      ++it;
+      f0 = f1;  // the next step's fragments are read into f1
+    }
+    finish_tile(t);
+  }
+}
+
 // Small-K kernel: the whole K (<= BK) of a tile fits one LDS stage, so each
 // iteration of the persistent loop is one complete tile.  It covers only
 // whole tiles (the launcher sends edge strips to the k-loop kernel), which
@@ -1042,7 +1349,7 @@ using C11 = Tile<256, 256, 16, 4, 2, false>;
 using C12 = Tile<256, 256, 32, 4, 4, false>;
 
 
-enum Kind { kKloop, kPanel };
+enum Kind { kKloop, kPanel, kKsplit };
 
 struct Entry {
   ProdConfig cfg;
@@ -1066,6 +1373,7 @@ const Entry kEntries[] = {
     {{256, 128, 64, 4, 2, 1, "panel256x128_k64_pipe"}, kPanel},
     {{256, 128, 64, 4, 2, 1, "panel256x128_k64_arow"}, kPanel},
     {{256, 256, 32, 4, 4, 1, "256x256x32_w4x4_ldsdma"}, kKloop},
+    {{64, 64, 64, 2, 2, 1, "64x64x64_ksplit4_ldsdma"}, kKsplit},
 };
 constexpr int kNumConfigs = sizeof(kEntries) / sizeof(kEntries[0]);
 constexpr int kRemainderConfig = 3;  // thin edge strips
@@ -1110,6 +1418,25 @@ hipError_t launch_grid(const Problem &p, hipStream_t s) {
 template <class S>
 hipError_t launch_kloop(const Problem &p, hipStream_t s) {
   return launch_grid<S, prod_kernel<S>>(p, s);
+}
+
+// K split over the waves of a 64x64 tile (ksplit_kernel) when A and B rows
+// are 16-byte aligned, N % 4 == 0, C is at least one tile each way and the
+// leading dimensions are below 2^24; otherwise the register-staged 64x64x32
+// kernel.
+hipError_t launch_ksplit(const Problem &p, hipStream_t s) {
+  const bool ok = (reinterpret_cast<uintptr_t>(p.A) & 15) == 0 &&
+                  (reinterpret_cast<uintptr_t>(p.B) & 15) == 0 && (p.lda & 3) == 0 &&
+                  (p.ldb & 3) == 0 && (p.N & 3) == 0 && p.M >= 64 && p.N >= 64 &&
+                  p.lda < (1 << 24) && p.ldb < (1 << 24);
+  if (!ok) return launch_kloop<C3>(p, s);
+  const long long tiles_m = ceil_div(p.M, 64), tiles_n = ceil_div(p.N, 64);
+  const long long ntiles = tiles_m * tiles_n;
+  if (ntiles > 0x7fffffffLL) return hipErrorInvalidValue;
+  long long grid = resident_workgroups<ksplit_kernel, 256>();
+  if (grid > ntiles) grid = ntiles;
+  return launch_kernel(ksplit_kernel, dim3((unsigned)grid), dim3(256), s, p, (int)tiles_m,
+                       (int)tiles_n);
 }
 
 // The direct-to-LDS kernel when A and B rows are 16-byte aligned and
@@ -1191,6 +1518,7 @@ hipError_t launch_one(int index, const Problem &p, hipStream_t s) {
     case 13: return launch_panel<P9, true>(p, s);
     case 14: return launch_arow<P9>(p, s);
     case 15: return launch_lds_dma<C12>(p, s);
+    case 16: return launch_ksplit(p, s);
 
     default: return hipErrorInvalidValue;
   }
@@ -1234,8 +1562,9 @@ bool prod_supports(int index, int M, int N, int K) {
 // panel kernel (only B moves per tile; C stores interleaved with the next
 // tile's MFMAs) for K <= 64 with many tiles; 256x256x32 tiles (16 waves, one workgroup per
 // CU, direct-to-LDS loads when the rows allow them) once there is a tile for every CU;
-// 256x128x16 below that; 64x64 tiles
-// for smaller problems so that every CU has work.
+// 256x128x16 below that; 128x64 tiles from 2048 64x64 tiles up; below that
+// 64x64 tiles with K split over the waves and a 3-stage direct-load pipeline
+// (the register-staged 64x64x32 kernel when rows are not 16-byte aligned).
 int prod_choose(int M, int N, int K) {
   const long long t256x256 = ceil_div(M, 256) * ceil_div(N, 256);
   const long long t256x128 = ceil_div(M, 256) * ceil_div(N, 128);
@@ -1244,7 +1573,7 @@ int prod_choose(int M, int N, int K) {
   if (t256x256 >= 256) return 15;
   if (t256x128 >= 512) return 2;
   if (t64 >= 2048) return 4;
-  return 3;
+  return 16;
 }
 
 // Entries the split-K path can run: the k-loop kernels without
