@@ -143,7 +143,7 @@ def test_kloop_entries_agree_bitwise_on_ragged_floats(g):
     back inside C (overlapping a neighbour) -- so on float inputs they must
     agree bit for bit.  The shapes leave no thin remainder for any tile size
     (a thin strip goes to the strip kernel, which sums K in another order)."""
-    kloop = [c for c in _prod_configs(g) if _supported(g, c, 1, 1, 65) and c != KSPLIT_ENTRY]
+    kloop = [c for c in _prod_configs(g) if _supported(g, c, 1, 1, 65) and c not in OWN_ORDER_ENTRIES]
     for (M, N, K) in [(1000, 1003, 515), (3000, 300, 129), (700, 4000, 64)]:
         for cfg in kloop:
             t = g.gemm_f32_tile("prod", cfg, M, N, K)
@@ -156,6 +156,8 @@ def test_kloop_entries_agree_bitwise_on_ragged_floats(g):
 
 
 KSPLIT_ENTRY = 16  # 64x64x64, K split over the waves (its own summation order)
+W16_ENTRIES = (17,)  # one wave per SIMD, 16x16 MFMAs (their own k order inside a step)
+OWN_ORDER_ENTRIES = (KSPLIT_ENTRY,) + W16_ENTRIES
 LDS_DMA_ENTRY = 15  # 256x256x32 with direct-to-LDS loads
 REG_STAGED_ENTRY = 12  # the same tiles through registers
 
@@ -194,30 +196,32 @@ def test_lds_dma_entry_matches_register_staged(g):
         _tol_check(outs[1][ii, jj], oracle.gemm_elems(a, b, ii, jj), K, f"lds-dma {M}x{N}x{K}")
 
 
-def test_ksplit_entry(g):
-    """The 64x64 K-split entry: each wave sums its quarter of every 64-deep
-    k step and the four partial tiles are added in wave order, so it is held
-    to the fp32 bar (and is exact on integers), not to bit agreement with the
-    other entries.  Shapes: one tile per CU, K tails (register path), K below
-    one step, tiles moved inside C, several tiles per workgroup, a single
-    tile, padded leading dimensions, and unaligned rows (the 64x64x32
-    fallback)."""
+@pytest.mark.parametrize("entry", OWN_ORDER_ENTRIES)
+def test_own_order_entries(g, entry):
+    """Entries that sum each element in their own order: the 64x64 K-split
+    entry (each wave sums its quarter of every 64-deep k step; the four
+    partial tiles are added in wave order) and the one-wave-per-SIMD 16x16
+    MFMA entries.  They are held to the fp32 bar (exact on integers), not to
+    bit agreement with the other entries.  Shapes: one tile per CU, K tails
+    (register path), K below one step, tiles moved inside C, several tiles
+    per workgroup, a single tile, padded leading dimensions, unaligned rows
+    and products narrower than a tile (the register-staged fallbacks)."""
     dev = _dev()
     cases = [  # (M, N, K, pad_a, pad_b, pad_c)
         (1024, 1024, 1024, 0, 0, 0), (1000, 1028, 1000, 0, 0, 0), (100, 68, 4, 0, 0, 0),
         (130, 1000, 2048, 0, 0, 0), (2048, 2048, 512, 0, 0, 0), (64, 64, 64, 0, 0, 0),
-        (777, 516, 700, 4, 8, 5), (300, 300, 257, 1, 0, 0), (512, 260, 96, 0, 3, 0)]
+        (777, 516, 700, 4, 8, 5), (300, 300, 257, 1, 0, 0), (512, 260, 96, 0, 3, 0),
+        (2304, 1280, 320, 0, 0, 0), (260, 132, 100, 0, 0, 0)]
     for (M, N, K, pa, pb, pc) in cases:
         for dist in ("small_int", "normal"):
-            print(f"case: ksplit {M}x{N}x{K} pad {pa},{pb},{pc} {dist}", flush=True)
+            print(f"case: entry {entry} {M}x{N}x{K} pad {pa},{pb},{pc} {dist}", flush=True)
             a, b = make(M, N, K, dist, seed=M + 5 * N + 11 * K)
             abuf = torch.zeros((M, K + pa), device=dev)
             bbuf = torch.zeros((K, N + pb), device=dev)
             cbuf = torch.full((M, N + pc), -3.0, device=dev)
             abuf[:, :K] = torch.from_numpy(a).to(dev)
             bbuf[:, :N] = torch.from_numpy(b).to(dev)
-            g.matmul(abuf[:, :K], bbuf[:, :N], out=cbuf[:, :N], variant="prod",
-                     config=KSPLIT_ENTRY)
+            g.matmul(abuf[:, :K], bbuf[:, :N], out=cbuf[:, :N], variant="prod", config=entry)
             torch.cuda.synchronize()
             c = cbuf.cpu().numpy()
             assert np.all(c[:, N:] == -3.0)
@@ -225,8 +229,8 @@ def test_ksplit_entry(g):
             if dist == "small_int":
                 assert np.array_equal(got, ref), (M, N, K, pa, pb, pc)
             else:
-                _tol_check(got, ref, K, f"ksplit {M}x{N}x{K}")
-                again = g.matmul(abuf[:, :K], bbuf[:, :N], variant="prod", config=KSPLIT_ENTRY)
+                _tol_check(got, ref, K, f"entry {entry} {M}x{N}x{K}")
+                again = g.matmul(abuf[:, :K], bbuf[:, :N], variant="prod", config=entry)
                 torch.cuda.synchronize()
                 assert np.array_equal(again.cpu().numpy(), got), "not deterministic"
 

@@ -991,6 +991,271 @@ __global__ void __launch_bounds__(256) ksplit_kernel(Problem p, int tiles_m, int
   }
 }
 
+// ---- one wave per SIMD, 16x16x4 MFMAs, direct-load pipeline -----------
+// The large-product form of the K-split kernel's recipe: a BM x BN tile
+// (BM = 2 WTM, BN = 2 WTN) over 4 waves, each computing a WTM x WTN sub-tile
+// as 16x16 blocks with v_mfma_f32_16x16x4_f32 -- (WTM/16)(WTN/16)
+// independent accumulator chains, so a lone wave keeps the matrix pipe busy.
+// Operands arrive by direct loads (inline assembly, as in ksplit_kernel)
+// into STAGES LDS stages of BK-deep k steps: the loads of step
+// i + STAGES - 1 are issued during step i, into the stage that step i - 1
+// used.  Inside a step the fragments are read 16 k at a time, one chunk
+// ahead of the MFMAs.  Within a 16-deep chunk h, MFMA t takes
+// k = 16 h + 4 g + t for lane group g = l / 16.  LDS layouts (16-byte
+// chunks): A rows of BK floats, chunk c of row r at c ^ ((r >> 1) & 7) for
+// BK = 32 and at c ^ (r & 15) for BK = 64; B rows of BN floats,
+// chunk c of k row k at c ^ (4 ((k >> 2) & 3)).  Each element is summed in
+// one fp32 accumulator in ascending k steps, but the k order inside a step
+// differs from prod_kernel, so the bits may differ.
+template <int WTM_, int WTN_, int BK_, int STAGES_>
+struct W16 {
+  static constexpr int WTM = WTM_, WTN = WTN_, BK = BK_, STAGES = STAGES_;
+  static constexpr int BM = 2 * WTM, BN = 2 * WTN;
+  static constexpr int TBM = WTM / 16, TBN = WTN / 16;
+  static constexpr int NQ = BK / 16;      // 16-deep chunks per step
+  static constexpr int ACH = BK / 4;      // 16-byte chunks per A row
+  static constexpr int ARPI = 64 / ACH;   // A rows per 1 KB instruction
+  static constexpr int BCH = BN / 4;      // 16-byte chunks per B row
+  static constexpr int BRPI = 64 / BCH;   // B rows per instruction
+  static constexpr int A_FLOATS = BM * BK, B_FLOATS = BK * BN, STAGE = A_FLOATS + B_FLOATS;
+  static constexpr int A_DMA = A_FLOATS / 256 / 4;  // instructions per wave and step
+  static constexpr int B_DMA = B_FLOATS / 256 / 4;
+  static constexpr int DMA = A_DMA + B_DMA;
+  using Staging = Tile<BM, BN, BK, 2, 2, false>;  // map for the register path
+  static_assert(BK == 32 || BK == 64, "A rows of 32 or 64 floats");
+  static_assert(BCH >= 16 && 64 % BCH == 0, "B rows of 64..256 floats");
+  static_assert(A_FLOATS % 1024 == 0 && B_FLOATS % 1024 == 0, "whole instructions per wave");
+  static_assert(STAGES >= 2 && STAGES * STAGE * 4 <= kLdsBytes, "LDS budget");
+};
+
+// Row permutation of A chunks: 16 consecutive rows land on distinct banks
+// (rows of 128 B pair up in a 256-byte bank window; rows of 256 B fill it).
+template <int ACH>
+__device__ inline int w16_a_perm(int r) {
+  return ACH == 16 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int ACH>
+__device__ inline int w16_a_pos(int r, int c) {
+  return r * ACH + (c ^ w16_a_perm<ACH>(r));
+}
+template <int BCH>
+__device__ inline int w16_b_pos(int k, int c) {
+  return k * BCH + (c ^ (4 * ((k >> 2) & 3)));
+}
+
+template <class W, bool PLACED>
+__device__ inline void w16_store_stage(const Stage<typename W::Staging> &sg, float *st, int tid) {
+  using T = typename W::Staging;
+  const int arow = tid / (T::BK / 4), ac = tid % (T::BK / 4);
+#pragma unroll
+  for (int i = 0; i < T::A_CHUNKS; ++i) {
+    const int r = arow + i * T::A_ROWS_PER_PASS;
+    *reinterpret_cast<f32x4 *>(st + 4 * w16_a_pos<W::ACH>(r, ac)) =
+        PLACED ? place(sg.a[i], sg.ameta[i]) : sg.a[i];
+  }
+  const int bkr = tid / (T::BN / 4), bc = tid % (T::BN / 4);
+#pragma unroll
+  for (int i = 0; i < T::B_CHUNKS; ++i) {
+    const int k = bkr + i * T::B_ROWS_PER_PASS;
+    *reinterpret_cast<f32x4 *>(st + W::A_FLOATS + 4 * w16_b_pos<W::BCH>(k, bc)) =
+        PLACED ? place(sg.b[i], sg.bmeta[i]) : sg.b[i];
+  }
+}
+
+template <class W>
+struct W16Frag {
+  f32x4 a[W::TBM];     // A[row][16 h + 4 g .. + 3]
+  float b[W::TBN][4];  // B[16 h + 4 g + t][col]
+};
+
+template <class W>
+__device__ inline void w16_read_frag(W16Frag<W> &f, const float *st, int h, int lane, int wm,
+                                     int wn) {
+  const int l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int bm = 0; bm < W::TBM; ++bm)
+    f.a[bm] = *reinterpret_cast<const f32x4 *>(
+        st + 4 * w16_a_pos<W::ACH>(wm * W::WTM + 16 * bm + l16, 4 * h + g));
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int k = 16 * h + 4 * g + t;
+#pragma unroll
+    for (int bn = 0; bn < W::TBN; ++bn) {
+      const int n = wn * W::WTN + 16 * bn + l16;
+      f.b[bn][t] = st[W::A_FLOATS + 4 * w16_b_pos<W::BCH>(k, n >> 2) + (n & 3)];
+    }
+  }
+}
+
+template <class W>
+__device__ inline void w16_mfma(f32x4 (&acc)[W::TBM][W::TBN], const W16Frag<W> &f, int t) {
+#pragma unroll
+  for (int bm = 0; bm < W::TBM; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < W::TBN; ++bn)
+      acc[bm][bn] =
+          __builtin_amdgcn_mfma_f32_16x16x4f32(f.b[bn][t], f.a[bm][t], acc[bm][bn], 0, 0, 0);
+}
+
+// The launcher guarantees M >= BM, N >= BN (every tile lies inside C after
+// the edge shift), N % 4 == 0, 16-byte aligned rows of A and B, and leading
+// dimensions below 2^24.
+template <class W>
+__global__ void __launch_bounds__(256) w16_kernel(Problem p, int tiles_m, int tiles_n) {
+  using T = typename W::Staging;
+  __shared__ __attribute__((aligned(16))) float lds[W::STAGES * W::STAGE];
+  const unsigned lds_u = (unsigned)(uintptr_t)(lds_void_t *)lds;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int ntiles = tiles_m * tiles_n;
+  const int nk = (p.K + W::BK - 1) / W::BK;
+  const int G = gridDim.x;
+  const int lid = xcd_remap(blockIdx.x, G);
+  if (lid >= ntiles) return;  // uniform per workgroup
+  const int my_tiles = (ntiles - lid + G - 1) / G;
+  const int steps = my_tiles * nk;
+  const bool k_tail = (p.K % W::BK) != 0;  // the last step of every tile is partial
+
+  // Per-lane byte offsets of this wave's direct loads from the step's base
+  // addresses (chunks permuted as in the LDS layouts).
+  unsigned voff[W::DMA];
+#pragma unroll
+  for (int q = 0; q < W::A_DMA; ++q) {
+    const int blk = wave * W::A_DMA + q;
+    const int r = W::ARPI * blk + lane / W::ACH;
+    const int c = (lane % W::ACH) ^ w16_a_perm<W::ACH>(r);
+    voff[q] = (unsigned)(((long long)r * p.lda + 4 * c) * 4);
+  }
+#pragma unroll
+  for (int q = 0; q < W::B_DMA; ++q) {
+    const int blk = wave * W::B_DMA + q;
+    const int k = W::BRPI * blk + lane / W::BCH;
+    const int c = (lane % W::BCH) ^ (4 * ((k >> 2) & 3));
+    voff[W::A_DMA + q] = (unsigned)(((long long)k * p.ldb + 4 * c) * 4);
+  }
+  const unsigned wave_a = (unsigned)(wave * W::A_DMA * 1024);
+  const unsigned wave_b = (unsigned)(W::A_FLOATS * 4 + wave * W::B_DMA * 1024);
+
+  // The issue side runs STAGES - 1 steps ahead of the consumer.
+  int is_t = 0, is_k = 0, is_m0 = 0, is_n0 = 0;
+  auto issue_origin = [&]() __attribute__((always_inline)) {
+    bool interior;
+    tile_origin<T>(lid + is_t * G, tiles_m, tiles_n, is_m0, is_n0, interior, p);
+  };
+  auto issue_advance = [&]() __attribute__((always_inline)) {
+    if (++is_k == nk) {
+      is_k = 0;
+      ++is_t;
+      if (is_t < my_tiles) issue_origin();
+    }
+  };
+  auto k_direct = [&](int k) __attribute__((always_inline)) { return !k_tail || k != nk - 1; };
+  auto issue_regs = [&](float *st) __attribute__((always_inline)) {
+    Stage<T> sg;
+    const bool g = load_step<T>(sg, p, is_m0, is_n0, is_k * W::BK, true, tid);
+    if (g)
+      w16_store_stage<W, true>(sg, st, tid);
+    else
+      w16_store_stage<W, false>(sg, st, tid);
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(0));  // nothing of this path outstanding
+  };
+  auto issue_dma = [&](unsigned st, int q0, int q1) __attribute__((always_inline)) {
+    const float *ab = p.A + (long long)is_m0 * p.lda + is_k * W::BK;
+    const float *bb = p.B + (long long)(is_k * W::BK) * p.ldb + is_n0;
+#pragma unroll
+    for (int q = 0; q < W::DMA; ++q) {
+      if (q < q0 || q >= q1) continue;
+      if (q < W::A_DMA)
+        ks_load_to_lds16(voff[q], ab, st + wave_a + q * 1024);
+      else
+        ks_load_to_lds16(voff[q], bb, st + wave_b + (q - W::A_DMA) * 1024);
+    }
+  };
+
+  f32x4 acc[W::TBM][W::TBN];
+  issue_origin();
+  for (int s = 0; s < W::STAGES - 1 && s < steps; ++s) {
+    if (k_direct(is_k))
+      issue_dma(lds_u + s * W::STAGE * 4, 0, W::DMA);
+    else
+      issue_regs(lds + s * W::STAGE);
+    issue_advance();
+  }
+
+  // One step: wait for its stage (own loads; loads of later steps may stay
+  // in flight), barrier, then the MFMAs chunk by chunk with the next chunk's
+  // fragments read ahead and the direct loads of step it + STAGES - 1
+  // spread over the first half of the step.
+  auto step = [&](int it) __attribute__((always_inline)) {
+    const int cur = it % W::STAGES;
+    {
+      // Outstanding younger steps: it + 1 .. it + STAGES - 2.
+      int younger = 0;
+      for (int d = 1; d <= W::STAGES - 2; ++d)
+        if (it + d < steps && k_direct((it + d) % nk)) ++younger;
+      if (younger == W::STAGES - 2 && W::STAGES > 2)
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm((W::STAGES - 2) * W::DMA));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(0));
+    }
+    ks_lds_barrier();
+    const float *st = lds + cur * W::STAGE;
+    const int ns = it + W::STAGES - 1;
+    const bool issue = ns < steps;
+    const bool direct = issue && k_direct(is_k);
+    const unsigned nst = lds_u + (ns % W::STAGES) * W::STAGE * 4;
+    if (issue && !direct) issue_regs(lds + (ns % W::STAGES) * W::STAGE);
+    W16Frag<W> fa, fb;
+    w16_read_frag<W>(fa, st, 0, lane, wm, wn);
+#pragma unroll
+    for (int h = 0; h < W::NQ; ++h) {
+      W16Frag<W> &fc = (h & 1) ? fb : fa;
+      W16Frag<W> &fn = (h & 1) ? fa : fb;
+      if (h + 1 < W::NQ) w16_read_frag<W>(fn, st, h + 1, lane, wm, wn);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        w16_mfma<W>(acc, fc, t);
+        // direct loads over the first half of the step's MFMA groups
+        constexpr int GROUPS = 4 * W::NQ, SPREAD = GROUPS / 2 > 0 ? GROUPS / 2 : 1;
+        const int grp = 4 * h + t;
+        if (direct && grp < SPREAD) {
+          __builtin_amdgcn_sched_barrier(0);
+          issue_dma(nst, grp * W::DMA / SPREAD, (grp + 1) * W::DMA / SPREAD);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    if (issue) issue_advance();
+  };
+  auto store_tile = [&](int t) __attribute__((always_inline)) {
+    int m0, n0;
+    bool interior;
+    tile_origin<T>(lid + t * G, tiles_m, tiles_n, m0, n0, interior, p);
+    const int l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int bm = 0; bm < W::TBM; ++bm) {
+      float *crow = p.C + (long long)(m0 + wm * W::WTM + 16 * bm + l16) * p.ldc + n0 +
+                    wn * W::WTN + 4 * g;
+#pragma unroll
+      for (int bn = 0; bn < W::TBN; ++bn)
+        *reinterpret_cast<f32x4u *>(crow + 16 * bn) = acc[bm][bn];
+    }
+  };
+
+  int it = 0;
+  for (int t = 0; t < my_tiles; ++t) {
+#pragma unroll
+    for (int i = 0; i < W::TBM; ++i)
+#pragma unroll
+      for (int j = 0; j < W::TBN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kk = 0; kk < nk; ++kk, ++it) step(it);
+    store_tile(t);
+  }
+}
+
 // Small-K kernel: the whole K (<= BK) of a tile fits one LDS stage, so each
 // iteration of the persistent loop is one complete tile.  It covers only
 // whole tiles (the launcher sends edge strips to the k-loop kernel), which
@@ -1374,6 +1639,7 @@ const Entry kEntries[] = {
     {{256, 128, 64, 4, 2, 1, "panel256x128_k64_arow"}, kPanel},
     {{256, 256, 32, 4, 4, 1, "256x256x32_w4x4_ldsdma"}, kKloop},
     {{64, 64, 64, 2, 2, 1, "64x64x64_ksplit4_ldsdma"}, kKsplit},
+    {{128, 128, 64, 2, 2, 1, "128x128x64_w16_ldsdma"}, kKsplit},
 };
 constexpr int kNumConfigs = sizeof(kEntries) / sizeof(kEntries[0]);
 constexpr int kRemainderConfig = 3;  // thin edge strips
@@ -1436,6 +1702,26 @@ hipError_t launch_ksplit(const Problem &p, hipStream_t s) {
   long long grid = resident_workgroups<ksplit_kernel, 256>();
   if (grid > ntiles) grid = ntiles;
   return launch_kernel(ksplit_kernel, dim3((unsigned)grid), dim3(256), s, p, (int)tiles_m,
+                       (int)tiles_n);
+}
+
+// One wave per SIMD with 16x16 MFMAs (w16_kernel) when A and B rows are
+// 16-byte aligned, N % 4 == 0, C is at least one tile each way and the
+// leading dimensions are below 2^24; otherwise the register-staged kernel
+// FALLBACK.
+template <class W, class FALLBACK>
+hipError_t launch_w16(const Problem &p, hipStream_t s) {
+  const bool ok = (reinterpret_cast<uintptr_t>(p.A) & 15) == 0 &&
+                  (reinterpret_cast<uintptr_t>(p.B) & 15) == 0 && (p.lda & 3) == 0 &&
+                  (p.ldb & 3) == 0 && (p.N & 3) == 0 && p.M >= W::BM && p.N >= W::BN &&
+                  p.lda < (1 << 24) && p.ldb < (1 << 24);
+  if (!ok) return launch_kloop<FALLBACK>(p, s);
+  const long long tiles_m = ceil_div(p.M, W::BM), tiles_n = ceil_div(p.N, W::BN);
+  const long long ntiles = tiles_m * tiles_n;
+  if (ntiles > 0x7fffffffLL) return hipErrorInvalidValue;
+  long long grid = resident_workgroups<w16_kernel<W>, 256>();
+  if (grid > ntiles) grid = ntiles;
+  return launch_kernel(w16_kernel<W>, dim3((unsigned)grid), dim3(256), s, p, (int)tiles_m,
                        (int)tiles_n);
 }
 
@@ -1519,6 +1805,7 @@ hipError_t launch_one(int index, const Problem &p, hipStream_t s) {
     case 14: return launch_arow<P9>(p, s);
     case 15: return launch_lds_dma<C12>(p, s);
     case 16: return launch_ksplit(p, s);
+    case 17: return launch_w16<W16<64, 64, 64, 2>, C0>(p, s);
 
     default: return hipErrorInvalidValue;
   }
@@ -1558,22 +1845,38 @@ bool prod_supports(int index, int M, int N, int K) {
   return kEntries[index].kind != kPanel || K <= kEntries[index].cfg.BK;
 }
 
-// Shape-based choice from measurements on MI355X: the A-resident small-K
-// panel kernel (only B moves per tile; C stores interleaved with the next
-// tile's MFMAs) for K <= 64 with many tiles; 256x256x32 tiles (16 waves, one workgroup per
-// CU, direct-to-LDS loads when the rows allow them) once there is a tile for every CU;
-// 256x128x16 below that; 128x64 tiles from 2048 64x64 tiles up; below that
-// 64x64 tiles with K split over the waves and a 3-stage direct-load pipeline
-// (the register-staged 64x64x32 kernel when rows are not 16-byte aligned).
+// Shape-based choice from measurements on MI355X.  K <= 64 with many tiles:
+// the A-resident small-K panel kernel (only B moves per tile; C stores
+// interleaved with the next tile's MFMAs).  Otherwise the k-loop entry with
+// the best modelled rate: its measured full-occupancy rate times the
+// fraction of workgroup slots its tiles fill over whole rounds (one
+// workgroup per CU, 256 CUs), counting tiles after the thin remainder
+// strips are split off.  Candidates: 256x256x32 with direct-to-LDS loads
+// (136 TFLOP/s), 128x128x64 with one wave per SIMD and 16x16 MFMAs (124),
+// and 64x64x64 with K split over the waves (95).
 int prod_choose(int M, int N, int K) {
-  const long long t256x256 = ceil_div(M, 256) * ceil_div(N, 256);
   const long long t256x128 = ceil_div(M, 256) * ceil_div(N, 128);
-  const long long t64 = ceil_div(M, 64) * ceil_div(N, 64);
   if (K <= 64 && t256x128 >= 1024) return 14;
-  if (t256x256 >= 256) return 15;
-  if (t256x128 >= 512) return 2;
-  if (t64 >= 2048) return 4;
-  return 16;
+  struct Cand {
+    int entry, tile;
+    double rate;
+  };
+  constexpr Cand cands[] = {{15, 256, 136.0}, {17, 128, 124.0}, {16, 64, 95.0}};
+  constexpr long long kSlots = 256;  // CUs of an MI355X, one workgroup each
+  int best = 16;
+  double best_score = -1.0;
+  for (const Cand &c : cands) {
+    const long long tm = ceil_div(M - thin_remainder(M, c.tile), c.tile);
+    const long long tn = ceil_div(N - thin_remainder(N, c.tile), c.tile);
+    const long long tiles = tm * tn;
+    const long long rounds = ceil_div(tiles, kSlots);
+    const double score = rounds > 0 ? c.rate * (double)tiles / (double)(rounds * kSlots) : 0.0;
+    if (score > best_score) {
+      best_score = score;
+      best = c.entry;
+    }
+  }
+  return best;
 }
 
 // Entries the split-K path can run: the k-loop kernels without
