@@ -156,7 +156,7 @@ def test_kloop_entries_agree_bitwise_on_ragged_floats(g):
 
 
 KSPLIT_ENTRY = 16  # 64x64x64, K split over the waves (its own summation order)
-W16_ENTRIES = (17,)  # one wave per SIMD, 16x16 MFMAs (their own k order inside a step)
+W16_ENTRIES = (17, 18)  # 16x16 MFMAs: one wave per SIMD (17); 256x256 direct-to-LDS (18)
 OWN_ORDER_ENTRIES = (KSPLIT_ENTRY,) + W16_ENTRIES
 LDS_DMA_ENTRY = 15  # 256x256x32 with direct-to-LDS loads
 REG_STAGED_ENTRY = 12  # the same tiles through registers

@@ -684,6 +684,203 @@ __global__ void __launch_bounds__(S::NT) lds_dma_kernel(Problem p, int tiles_m, 
   }
 }
 
+// ---- the direct-to-LDS k loop on 16x16x4 MFMAs -------------------------
+// lds_dma_kernel with each wave's WTM x WTN sub-tile computed as 16x16
+// blocks on v_mfma_f32_16x16x4_f32 instead of 32x32 blocks on 32x32x2: the
+// same matrix-pipe time and the same LDS traffic, but (WTM/16)(WTN/16)
+// independent accumulator chains per wave instead of (WTM/32)(WTN/32).
+// Within a 16-deep chunk h of a step, MFMA t takes k = 16 h + 4 g + t for
+// lane group g = l / 16; the A layout is lds_dma_kernel's, B rows use a
+// pitch of BN + 4 floats so that the four lane groups, reading k rows 4
+// apart, fall on distinct banks.  The k order inside a step differs from
+// prod_kernel, so the bits may differ.
+template <class S>
+struct LdsDma16 {
+  static constexpr int SB = S::BN + 4;
+  static constexpr int A_STAGE = S::BM * S::BK;
+  static constexpr int B_STAGE = S::BK * SB;
+  static constexpr int TBM = S::WTM / 16, TBN = S::WTN / 16;
+};
+
+template <class S>
+__device__ inline void lds_dma16_issue(const Problem &p, int m0, int n0, int k0, float *as,
+                                       float *bs, int lane, int wave) {
+  using D = LdsDma<S>;
+  const int pos = lane % D::CPR;
+#pragma unroll
+  for (int j = 0; j < D::A_BLK; ++j) {
+    const int blk = wave * D::A_BLK + j;
+    const int r = blk * D::RPB + lane / D::CPR;
+    const int c = pos ^ a_chunk_perm(r);
+    load_to_lds16(p.A + (long long)(m0 + r) * p.lda + k0 + 4 * c, as + blk * 256);
+  }
+#pragma unroll
+  for (int j = 0; j < D::B_ROWS; ++j) {
+    const int k = wave * D::B_ROWS + j;
+    load_to_lds16(p.B + (long long)(k0 + k) * p.ldb + n0 + 4 * lane,
+                  bs + k * LdsDma16<S>::SB);
+  }
+}
+
+template <class S, bool PLACED>
+__device__ inline void store_lds_perm16_as(const Stage<S> &st, float *as, float *bs, int tid) {
+  const int arow = tid / (S::BK / 4), c = tid % (S::BK / 4);
+#pragma unroll
+  for (int i = 0; i < S::A_CHUNKS; ++i) {
+    const int r = arow + i * S::A_ROWS_PER_PASS;
+    *reinterpret_cast<f32x4 *>(as + r * S::BK + 4 * (c ^ a_chunk_perm(r))) =
+        PLACED ? place(st.a[i], st.ameta[i]) : st.a[i];
+  }
+  const int bkr = tid / (S::BN / 4), bnq = (tid % (S::BN / 4)) * 4;
+#pragma unroll
+  for (int i = 0; i < S::B_CHUNKS; ++i)
+    *reinterpret_cast<f32x4 *>(bs + (bkr + i * S::B_ROWS_PER_PASS) * LdsDma16<S>::SB + bnq) =
+        PLACED ? place(st.b[i], st.bmeta[i]) : st.b[i];
+}
+
+template <class S>
+__device__ inline void compute_stage16(f32x4 (&acc)[LdsDma16<S>::TBM][LdsDma16<S>::TBN],
+                                       const float *as, const float *bs, int wm, int wn,
+                                       int lane) {
+  using D = LdsDma16<S>;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int perm = a_chunk_perm(l16);  // rows of a wave differ by multiples of 16
+  const float *a_row = as + (wm * S::WTM + l16) * S::BK;
+  const float *b_base = bs + (4 * g) * D::SB + wn * S::WTN + l16;
+#pragma unroll
+  for (int h = 0; h < S::BK / 16; ++h) {
+    f32x4 af[D::TBM];
+    float bf[D::TBN][4];
+    const int pos = (4 * h + g) ^ perm;
+#pragma unroll
+    for (int bm = 0; bm < D::TBM; ++bm)
+      af[bm] = *reinterpret_cast<const f32x4 *>(a_row + bm * 16 * S::BK + 4 * pos);
+#pragma unroll
+    for (int bn = 0; bn < D::TBN; ++bn)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) bf[bn][t] = b_base[(16 * h + t) * D::SB + bn * 16];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int bm = 0; bm < D::TBM; ++bm)
+#pragma unroll
+        for (int bn = 0; bn < D::TBN; ++bn)
+          acc[bm][bn] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf[bn][t], af[bm][t], acc[bm][bn],
+                                                             0, 0, 0);
+  }
+}
+
+template <class S>
+__device__ inline void store_c16(const f32x4 (&acc)[LdsDma16<S>::TBM][LdsDma16<S>::TBN],
+                                 const Problem &p, int m0, int n0, int wm, int wn, int lane,
+                                 bool guard) {
+  using D = LdsDma16<S>;
+  const int l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int bm = 0; bm < D::TBM; ++bm) {
+    const int row = m0 + wm * S::WTM + 16 * bm + l16;
+    float *crow = p.C + (long long)row * p.ldc;
+#pragma unroll
+    for (int bn = 0; bn < D::TBN; ++bn) {
+      const int col = n0 + wn * S::WTN + 16 * bn + 4 * g;
+      const f32x4 v = acc[bm][bn];
+      if (!guard || (row < p.M && col + 4 <= p.N)) {
+        *reinterpret_cast<f32x4u *>(crow + col) = v;
+      } else if (row < p.M) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (col + r < p.N) crow[col + r] = v[r];
+      }
+    }
+  }
+}
+
+template <class S>
+__global__ void __launch_bounds__(S::NT) lds_dma16_kernel(Problem p, int tiles_m, int tiles_n) {
+  using D = LdsDma16<S>;
+  static_assert(2 * (D::A_STAGE + D::B_STAGE) * 4 <= kLdsBytes, "two stages must fit in LDS");
+  __shared__ __attribute__((aligned(16))) float lds[2 * (D::A_STAGE + D::B_STAGE)];
+  float *const as0 = lds;
+  float *const bs0 = lds + 2 * D::A_STAGE;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / S::WGN, wn = wave % S::WGN;
+  const int ntiles = tiles_m * tiles_n;
+  const int nk = (p.K + S::BK - 1) / S::BK;
+  const int G = gridDim.x;
+  const int lid = xcd_remap(blockIdx.x, G);
+  if (lid >= ntiles) return;  // uniform per workgroup
+  const int my_tiles = (ntiles - lid + G - 1) / G;
+  const long long steps = (long long)my_tiles * nk;
+
+  int t = lid, kt = 0;
+  int m0, n0;
+  bool interior;
+  tile_origin<S>(t, tiles_m, tiles_n, m0, n0, interior, p);
+
+  f32x4 acc[D::TBM][D::TBN];
+#pragma unroll
+  for (int i = 0; i < D::TBM; ++i)
+#pragma unroll
+    for (int j = 0; j < D::TBN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  Stage<S> st;
+  if (interior && S::BK <= p.K) {
+    lds_dma16_issue<S>(p, m0, n0, 0, as0, bs0, lane, wave);
+  } else {
+    const bool g = load_step<S>(st, p, m0, n0, 0, interior, tid);
+    if (g)
+      store_lds_perm16_as<S, true>(st, as0, bs0, tid);
+    else
+      store_lds_perm16_as<S, false>(st, as0, bs0, tid);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(0));
+  __syncthreads();
+
+  for (long long it = 0; it < steps; ++it) {
+    const int cur = (int)(it & 1);
+    const bool more = it + 1 < steps;
+    int nt = t, nkt = kt + 1;
+    int nm0 = m0, nn0 = n0;
+    bool ninterior = interior;
+    if (nkt == nk) {
+      nkt = 0;
+      nt = t + G;
+      if (more) tile_origin<S>(nt, tiles_m, tiles_n, nm0, nn0, ninterior, p);
+    }
+    if (more) {
+      float *const an = as0 + (cur ^ 1) * D::A_STAGE;
+      float *const bn = bs0 + (cur ^ 1) * D::B_STAGE;
+      const int nk0 = nkt * S::BK;
+      if (ninterior && nk0 + S::BK <= p.K) {
+        lds_dma16_issue<S>(p, nm0, nn0, nk0, an, bn, lane, wave);
+      } else {
+        const bool g = load_step<S>(st, p, nm0, nn0, nk0, ninterior, tid);
+        if (g)
+          store_lds_perm16_as<S, true>(st, an, bn, tid);
+        else
+          store_lds_perm16_as<S, false>(st, an, bn, tid);
+      }
+    }
+    compute_stage16<S>(acc, as0 + cur * D::A_STAGE, bs0 + cur * D::B_STAGE, wm, wn, lane);
+    if (kt == nk - 1) {
+      store_c16<S>(acc, p, m0, n0, wm, wn, lane, !interior);
+#pragma unroll
+      for (int i = 0; i < D::TBM; ++i)
+#pragma unroll
+        for (int j = 0; j < D::TBN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(0));
+    __syncthreads();
+    t = nt;
+    kt = nkt;
+    m0 = nm0;
+    n0 = nn0;
+    interior = ninterior;
+  }
+}
+
 // ---- 64x64 tiles with K split over the waves, 3-stage direct-load pipe --
 // For products with about one 64x64 tile per CU (1024^3 has 256), where a
 // k step of a 64x64 tile is too short to hide the latency of its loads.
@@ -1640,6 +1837,7 @@ const Entry kEntries[] = {
     {{256, 256, 32, 4, 4, 1, "256x256x32_w4x4_ldsdma"}, kKloop},
     {{64, 64, 64, 2, 2, 1, "64x64x64_ksplit4_ldsdma"}, kKsplit},
     {{128, 128, 64, 2, 2, 1, "128x128x64_w16_ldsdma"}, kKsplit},
+    {{256, 256, 32, 4, 4, 1, "256x256x32_w4x4_ldsdma_mfma16"}, kKsplit},
 };
 constexpr int kNumConfigs = sizeof(kEntries) / sizeof(kEntries[0]);
 constexpr int kRemainderConfig = 3;  // thin edge strips
@@ -1728,6 +1926,15 @@ hipError_t launch_w16(const Problem &p, hipStream_t s) {
 // The direct-to-LDS kernel when A and B rows are 16-byte aligned and
 // N % 4 == 0; otherwise the register-staged kernel with the same tiles.
 template <class S>
+hipError_t launch_lds_dma16(const Problem &p, hipStream_t s) {
+  const bool aligned = (reinterpret_cast<uintptr_t>(p.A) & 15) == 0 &&
+                       (reinterpret_cast<uintptr_t>(p.B) & 15) == 0 && (p.lda & 3) == 0 &&
+                       (p.ldb & 3) == 0 && (p.N & 3) == 0;
+  if (!aligned) return launch_kloop<S>(p, s);
+  return launch_grid<S, lds_dma16_kernel<S>>(p, s);
+}
+
+template <class S>
 hipError_t launch_lds_dma(const Problem &p, hipStream_t s) {
   const bool aligned = (reinterpret_cast<uintptr_t>(p.A) & 15) == 0 &&
                        (reinterpret_cast<uintptr_t>(p.B) & 15) == 0 && (p.lda & 3) == 0 &&
@@ -1806,6 +2013,7 @@ hipError_t launch_one(int index, const Problem &p, hipStream_t s) {
     case 15: return launch_lds_dma<C12>(p, s);
     case 16: return launch_ksplit(p, s);
     case 17: return launch_w16<W16<64, 64, 64, 2>, C0>(p, s);
+    case 18: return launch_lds_dma16<C12>(p, s);
 
     default: return hipErrorInvalidValue;
   }
@@ -1851,9 +2059,9 @@ bool prod_supports(int index, int M, int N, int K) {
 // the best modelled rate: its measured full-occupancy rate times the
 // fraction of workgroup slots its tiles fill over whole rounds (one
 // workgroup per CU, 256 CUs), counting tiles after the thin remainder
-// strips are split off.  Candidates: 256x256x32 with direct-to-LDS loads
-// (136 TFLOP/s), 128x128x64 with one wave per SIMD and 16x16 MFMAs (124),
-// and 64x64x64 with K split over the waves (95).
+// strips are split off.  Candidates: 256x256x32 with direct-to-LDS loads on
+// 16x16 MFMAs (138 TFLOP/s), 128x128x64 with one wave per SIMD and 16x16
+// MFMAs (124), and 64x64x64 with K split over the waves (95).
 int prod_choose(int M, int N, int K) {
   const long long t256x128 = ceil_div(M, 256) * ceil_div(N, 128);
   if (K <= 64 && t256x128 >= 1024) return 14;
@@ -1861,7 +2069,7 @@ int prod_choose(int M, int N, int K) {
     int entry, tile;
     double rate;
   };
-  constexpr Cand cands[] = {{15, 256, 136.0}, {17, 128, 124.0}, {16, 64, 95.0}};
+  constexpr Cand cands[] = {{18, 256, 138.0}, {17, 128, 124.0}, {16, 64, 95.0}};
   constexpr long long kSlots = 256;  // CUs of an MI355X, one workgroup each
   int best = 16;
   double best_score = -1.0;
