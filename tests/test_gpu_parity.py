@@ -156,7 +156,9 @@ def test_kloop_entries_agree_bitwise_on_ragged_floats(g):
 
 
 KSPLIT_ENTRY = 16  # 64x64x64, K split over the waves (its own summation order)
-W16_ENTRIES = (17, 18)  # 16x16 MFMAs: one wave per SIMD (17); 256x256 direct-to-LDS (18)
+# 16x16 MFMAs: one wave per SIMD on 64x64 (17) and 128x128 (19) wave tiles;
+# 256x256 direct-to-LDS on 16 waves (18)
+W16_ENTRIES = (17, 18, 19)
 OWN_ORDER_ENTRIES = (KSPLIT_ENTRY,) + W16_ENTRIES
 LDS_DMA_ENTRY = 15  # 256x256x32 with direct-to-LDS loads
 REG_STAGED_ENTRY = 12  # the same tiles through registers
@@ -211,7 +213,8 @@ def test_own_order_entries(g, entry):
         (1024, 1024, 1024, 0, 0, 0), (1000, 1028, 1000, 0, 0, 0), (100, 68, 4, 0, 0, 0),
         (130, 1000, 2048, 0, 0, 0), (2048, 2048, 512, 0, 0, 0), (64, 64, 64, 0, 0, 0),
         (777, 516, 700, 4, 8, 5), (300, 300, 257, 1, 0, 0), (512, 260, 96, 0, 3, 0),
-        (2304, 1280, 320, 0, 0, 0), (260, 132, 100, 0, 0, 0)]
+        (2304, 1280, 320, 0, 0, 0), (260, 132, 100, 0, 0, 0), (4352, 4100, 32, 0, 0, 0),
+        (600, 520, 96, 4, 8, 5)]
     for (M, N, K, pa, pb, pc) in cases:
         for dist in ("small_int", "normal"):
             print(f"case: entry {entry} {M}x{N}x{K} pad {pa},{pb},{pc} {dist}", flush=True)

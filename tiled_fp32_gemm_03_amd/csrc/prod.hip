@@ -1259,6 +1259,44 @@ __device__ inline void w16_store_stage(const Stage<typename W::Staging> &sg, flo
   }
 }
 
+// Fragments, per lane (l16 = lane % 16, g = lane / 16): for 16-deep chunk
+// h, A[row l16 of block bm][k = 16 h + 4 g .. + 3] as one 16-byte read,
+// and for MFMA t of the chunk B[k = 16 h + 4 g + t][column l16 of block bn].
+template <class W>
+__device__ inline void w16_read_a(f32x4 (&a)[W::TBM], const float *st, int h, int lane, int wm) {
+  const int l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int bm = 0; bm < W::TBM; ++bm)
+    a[bm] = *reinterpret_cast<const f32x4 *>(
+        st + 4 * w16_a_pos<W::ACH>(wm * W::WTM + 16 * bm + l16, 4 * h + g));
+}
+
+template <class W>
+__device__ inline void w16_read_b(float (&b)[W::TBN], const float *st, int h, int t, int lane,
+                                  int wn) {
+  const int l16 = lane & 15, g = lane >> 4;
+  const int k = 16 * h + 4 * g + t;
+#pragma unroll
+  for (int bn = 0; bn < W::TBN; ++bn) {
+    const int n = wn * W::WTN + 16 * bn + l16;
+    b[bn] = st[W::A_FLOATS + 4 * w16_b_pos<W::BCH>(k, n >> 2) + (n & 3)];
+  }
+}
+
+// MFMA t of a chunk over all blocks of the wave tile, from separately held
+// A (chunk) and B (MFMA t) fragments.
+template <class W>
+__device__ inline void w16_mfma_t(f32x4 (&acc)[W::TBM][W::TBN], const f32x4 (&a)[W::TBM],
+                                  const float (&b)[W::TBN], int t) {
+#pragma unroll
+  for (int bm = 0; bm < W::TBM; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < W::TBN; ++bn)
+      acc[bm][bn] = __builtin_amdgcn_mfma_f32_16x16x4f32(b[bn], a[bm][t], acc[bm][bn], 0, 0, 0);
+}
+
+// All fragments of one chunk, read together (w16_kernel reads a chunk
+// ahead of its MFMAs).
 template <class W>
 struct W16Frag {
   f32x4 a[W::TBM];     // A[row][16 h + 4 g .. + 3]
@@ -1451,6 +1489,185 @@ __global__ void __launch_bounds__(256) w16_kernel(Problem p, int tiles_m, int ti
     for (int kk = 0; kk < nk; ++kk, ++it) step(it);
     store_tile(t);
   }
+}
+
+// ---- one wave per SIMD, 128x128 wave tiles -----------------------------
+// For large products whose K is a whole number of k steps: a 256x256 tile
+// over 4 waves (2 x 2), each computing a 128x128 sub-tile as 8 x 8 blocks
+// of v_mfma_f32_16x16x4_f32.  The 64 accumulator chains (256 registers per
+// lane) live in the accumulation registers; per 32-deep k step a wave
+// issues 512 MFMAs (16384 matrix-pipe cycles) against 16 direct loads,
+// 16 A and 64 B fragment reads and one barrier, so the non-matrix work of
+// a step is small and one barrier per step is cheap among 4 waves.  Two
+// LDS stages: the loads of step i + 1 are issued during step i, into the
+// stage step i - 1 used.  The k loop has no branch: the stage alternates
+// by parity, the step after a tile's last is the next tile's first, and
+// the workgroup's very last step reloads its own tile's first operands
+// into the idle stage.  LDS layouts and the per-element k order are those
+// of w16_kernel.
+template <class W>
+__global__ void __launch_bounds__(256) big16_kernel(Problem p, int tiles_m, int tiles_n) {
+  using T = typename W::Staging;
+  static_assert(W::STAGES == 2, "two stages");
+  __shared__ __attribute__((aligned(16))) float lds[2 * W::STAGE];
+  const unsigned lds_u = (unsigned)(uintptr_t)(lds_void_t *)lds;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int ntiles = tiles_m * tiles_n;
+  const int nk = p.K / W::BK;
+  const int G = gridDim.x;
+  const int lid = xcd_remap(blockIdx.x, G);
+  if (lid >= ntiles) return;  // uniform per workgroup
+  const int my_tiles = (ntiles - lid + G - 1) / G;
+
+  // Per-lane byte offsets of this wave's direct loads from a step's base
+  // addresses (chunks permuted as in the LDS layouts).
+  unsigned voff[W::DMA];
+#pragma unroll
+  for (int q = 0; q < W::A_DMA; ++q) {
+    const int blk = wave * W::A_DMA + q;
+    const int r = W::ARPI * blk + lane / W::ACH;
+    const int c = (lane % W::ACH) ^ w16_a_perm<W::ACH>(r);
+    voff[q] = (unsigned)(((long long)r * p.lda + 4 * c) * 4);
+  }
+#pragma unroll
+  for (int q = 0; q < W::B_DMA; ++q) {
+    const int blk = wave * W::B_DMA + q;
+    const int k = W::BRPI * blk + lane / W::BCH;
+    const int c = (lane % W::BCH) ^ (4 * ((k >> 2) & 3));
+    voff[W::A_DMA + q] = (unsigned)(((long long)k * p.ldb + 4 * c) * 4);
+  }
+  const unsigned wave_a = (unsigned)(wave * W::A_DMA * 1024);
+  const unsigned wave_b = (unsigned)(W::A_FLOATS * 4 + wave * W::B_DMA * 1024);
+  const long long b_step = (long long)W::BK * p.ldb;
+
+  auto tile_base = [&](int t, const float *&ab, const float *&bb) __attribute__((always_inline)) {
+    int m0, n0;
+    bool interior;
+    tile_origin<T>(lid + t * G, tiles_m, tiles_n, m0, n0, interior, p);
+    ab = p.A + (long long)m0 * p.lda;
+    bb = p.B + n0;
+  };
+  auto issue = [&](unsigned st, const float *ab, const float *bb, int q0, int q1)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < W::DMA; ++q) {
+      if (q < q0 || q >= q1) continue;
+      if (q < W::A_DMA)
+        ks_load_to_lds16(voff[q], ab, st + wave_a + q * 1024);
+      else
+        ks_load_to_lds16(voff[q], bb, st + wave_b + (q - W::A_DMA) * 1024);
+    }
+  };
+
+  const float *is_a, *is_b;  // operands of the step most recently issued
+  tile_base(0, is_a, is_b);
+  issue(lds_u, is_a, is_b, 0, W::DMA);
+  int stage = 0;
+
+  f32x4 acc[W::TBM][W::TBN];
+  for (int t = 0; t < my_tiles; ++t) {
+    const float *nt_a, *nt_b;  // the next tile's first step (this tile's on the last)
+    tile_base(t + 1 < my_tiles ? t + 1 : t, nt_a, nt_b);
+#pragma unroll
+    for (int i = 0; i < W::TBM; ++i)
+#pragma unroll
+      for (int j = 0; j < W::TBN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int kk = 0; kk < nk; ++kk) {
+      const bool last = kk + 1 == nk;
+      const float *ia = last ? nt_a : is_a + W::BK;
+      const float *ib = last ? nt_b : is_b + b_step;
+      __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(0));  // this step's loads (own)
+      ks_lds_barrier();                                // everyone's; stage stage^1 free
+      const float *st = lds + stage * W::STAGE;
+      const unsigned nst = lds_u + (stage ^ 1) * W::STAGE * 4;
+
+      // Fragments: A one chunk ahead, B one MFMA group ahead.  After the
+      // barrier, group 0's operands are read in the order its MFMAs use
+      // them (B, then A row block by row block), so the first MFMAs wait
+      // for two reads rather than for the whole group's.  Inside a group,
+      // the next group's reads are issued after its first half, and the
+      // next step's 16 direct loads one after every other row of 8 MFMAs
+      // over the first two groups.  sched_barrier pins these positions.
+      f32x4 a0[W::TBM], a1[W::TBM];
+      float b0[W::TBN], b1[W::TBN];
+      w16_read_b<W>(b0, st, 0, 0, lane, wn);
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        const int l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+        for (int bm = 0; bm < W::TBM; ++bm) {
+          a0[bm] = *reinterpret_cast<const f32x4 *>(
+              st + 4 * w16_a_pos<W::ACH>(wm * W::WTM + 16 * bm + l16, g));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < W::NQ; ++h) {
+        f32x4(&ac)[W::TBM] = (h & 1) ? a1 : a0;
+        f32x4(&an)[W::TBM] = (h & 1) ? a0 : a1;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int grp = 4 * h + u;
+          float(&bc)[W::TBN] = (grp & 1) ? b1 : b0;
+          float(&bnx)[W::TBN] = (grp & 1) ? b0 : b1;
+#pragma unroll
+          for (int bm = 0; bm < W::TBM; ++bm) {
+#pragma unroll
+            for (int bn = 0; bn < W::TBN; ++bn)
+              acc[bm][bn] =
+                  __builtin_amdgcn_mfma_f32_16x16x4f32(bc[bn], ac[bm][u], acc[bm][bn], 0, 0, 0);
+            constexpr int kRowsPerLoad = 2;
+            const int row = grp * W::TBM + bm;
+            if (row % kRowsPerLoad == 0 && row / kRowsPerLoad < W::DMA) {
+              __builtin_amdgcn_sched_barrier(0);
+              issue(nst, ia, ib, row / kRowsPerLoad, row / kRowsPerLoad + 1);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            if (bm == W::TBM / 2 - 1) {
+              __builtin_amdgcn_sched_barrier(0);
+              if (u < 3)
+                w16_read_b<W>(bnx, st, h, u + 1, lane, wn);
+              else if (h + 1 < W::NQ)
+                w16_read_b<W>(bnx, st, h + 1, 0, lane, wn);
+              if (u == 1 && h + 1 < W::NQ) w16_read_a<W>(an, st, h + 1, lane, wm);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+        }
+      }
+      is_a = ia;
+      is_b = ib;
+      stage ^= 1;
+      // Hand every accumulator to the next step in an accumulation
+      // register (an empty asm with an "a" operand): without it the
+      // register allocator keeps part of the 256 in ordinary VGPRs across
+      // the loop and copies them to and from the accumulation registers
+      // around the MFMAs every step.
+#pragma unroll
+      for (int i = 0; i < W::TBM; ++i)
+#pragma unroll
+        for (int j = 0; j < W::TBN; ++j) asm volatile("" : "+a"(acc[i][j]));
+    }
+
+    int m0, n0;
+    bool interior;
+    tile_origin<T>(lid + t * G, tiles_m, tiles_n, m0, n0, interior, p);
+    const int l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int bm = 0; bm < W::TBM; ++bm) {
+      float *crow = p.C + (long long)(m0 + wm * W::WTM + 16 * bm + l16) * p.ldc + n0 +
+                    wn * W::WTN + 4 * g;
+#pragma unroll
+      for (int bn = 0; bn < W::TBN; ++bn)
+        *reinterpret_cast<f32x4u *>(crow + 16 * bn) = acc[bm][bn];
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(0));  // the redundant last reload
 }
 
 // Small-K kernel: the whole K (<= BK) of a tile fits one LDS stage, so each
@@ -1838,6 +2055,7 @@ const Entry kEntries[] = {
     {{64, 64, 64, 2, 2, 1, "64x64x64_ksplit4_ldsdma"}, kKsplit},
     {{128, 128, 64, 2, 2, 1, "128x128x64_w16_ldsdma"}, kKsplit},
     {{256, 256, 32, 4, 4, 1, "256x256x32_w4x4_ldsdma_mfma16"}, kKsplit},
+    {{256, 256, 32, 2, 2, 1, "256x256x32_w2x2_ldsdma_mfma16"}, kKsplit},
 };
 constexpr int kNumConfigs = sizeof(kEntries) / sizeof(kEntries[0]);
 constexpr int kRemainderConfig = 3;  // thin edge strips
@@ -1923,6 +2141,13 @@ hipError_t launch_w16(const Problem &p, hipStream_t s) {
                        (int)tiles_n);
 }
 
+// The 128x128-wave kernel (big16_kernel) when A and B rows are 16-byte
+// aligned, N % 4 == 0, K is a positive multiple of the k step, C is at
+// least one tile each way and the leading dimensions are below 2^24;
+// otherwise entry 18's launcher (direct loads on 64x64 wave tiles).
+template <class W>
+hipError_t launch_big16(const Problem &p, hipStream_t s);
+
 // The direct-to-LDS kernel when A and B rows are 16-byte aligned and
 // N % 4 == 0; otherwise the register-staged kernel with the same tiles.
 template <class S>
@@ -1993,6 +2218,22 @@ hipError_t launch_arow(const Problem &p, hipStream_t s) {
                        (int)chunks, (int)tiles_n);
 }
 
+template <class W>
+hipError_t launch_big16(const Problem &p, hipStream_t s) {
+  const bool ok = (reinterpret_cast<uintptr_t>(p.A) & 15) == 0 &&
+                  (reinterpret_cast<uintptr_t>(p.B) & 15) == 0 && (p.lda & 3) == 0 &&
+                  (p.ldb & 3) == 0 && (p.N & 3) == 0 && p.M >= W::BM && p.N >= W::BN &&
+                  p.K > 0 && p.K % W::BK == 0 && p.lda < (1 << 24) && p.ldb < (1 << 24);
+  if (!ok) return launch_lds_dma16<C12>(p, s);
+  const long long tiles_m = ceil_div(p.M, W::BM), tiles_n = ceil_div(p.N, W::BN);
+  const long long ntiles = tiles_m * tiles_n;
+  if (ntiles > 0x7fffffffLL) return hipErrorInvalidValue;
+  long long grid = resident_workgroups<big16_kernel<W>, 256>();
+  if (grid > ntiles) grid = ntiles;
+  return launch_kernel(big16_kernel<W>, dim3((unsigned)grid), dim3(256), s, p, (int)tiles_m,
+                       (int)tiles_n);
+}
+
 hipError_t launch_one(int index, const Problem &p, hipStream_t s) {
   switch (index) {
     case 0: return launch_kloop<C0>(p, s);
@@ -2014,6 +2255,7 @@ hipError_t launch_one(int index, const Problem &p, hipStream_t s) {
     case 16: return launch_ksplit(p, s);
     case 17: return launch_w16<W16<64, 64, 64, 2>, C0>(p, s);
     case 18: return launch_lds_dma16<C12>(p, s);
+    case 19: return launch_big16<W16<128, 128, 32, 2>>(p, s);
 
     default: return hipErrorInvalidValue;
   }
@@ -2060,8 +2302,9 @@ bool prod_supports(int index, int M, int N, int K) {
 // fraction of workgroup slots its tiles fill over whole rounds (one
 // workgroup per CU, 256 CUs), counting tiles after the thin remainder
 // strips are split off.  Candidates: 256x256x32 with direct-to-LDS loads on
-// 16x16 MFMAs (138 TFLOP/s), 128x128x64 with one wave per SIMD and 16x16
-// MFMAs (124), and 64x64x64 with K split over the waves (95).
+// 16x16 MFMAs -- 128x128 wave tiles when K is a multiple of 32 (148
+// TFLOP/s), else 64x64 ones (138) --, 128x128x64 with one wave per SIMD and
+// 16x16 MFMAs (124), and 64x64x64 with K split over the waves (95).
 int prod_choose(int M, int N, int K) {
   const long long t256x128 = ceil_div(M, 256) * ceil_div(N, 128);
   if (K <= 64 && t256x128 >= 1024) return 14;
@@ -2069,7 +2312,9 @@ int prod_choose(int M, int N, int K) {
     int entry, tile;
     double rate;
   };
-  constexpr Cand cands[] = {{18, 256, 138.0}, {17, 128, 124.0}, {16, 64, 95.0}};
+  const bool whole_steps = K % 32 == 0;
+  const Cand cands[] = {whole_steps ? Cand{19, 256, 148.0} : Cand{18, 256, 138.0},
+                        {17, 128, 124.0}, {16, 64, 95.0}};
   constexpr long long kSlots = 256;  // CUs of an MI355X, one workgroup each
   int best = 16;
   double best_score = -1.0;
