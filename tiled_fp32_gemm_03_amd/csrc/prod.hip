@@ -1670,6 +1670,214 @@ __global__ void __launch_bounds__(256) big16_kernel(Problem p, int tiles_m, int 
   __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(0));  // the redundant last reload
 }
 
+// ---- the same tiles with operands staged through registers --------------
+// For products whose rows are not 16-byte aligned or whose K is not a whole
+// number of k steps (direct loads need both): big16_kernel's tile, waves,
+// LDS layout and MFMA schedule, with each step's operands loaded into
+// registers by 128-bit loads (4-byte alignment suffices) during the first
+// rows of MFMAs of the previous step and written to the idle stage during
+// its second half.  Rows and columns need no guard: C is at least one tile
+// each way and edge tiles are moved inside it.  The K tail does: the step
+// that loads a tile's partial last step keeps its loads inside the
+// matrices (A columns clamped to the last 4-float window of the row, every
+// B chunk read from row 0) and then, after its MFMAs, rewrites that stage
+// from guarded loads -- an A chunk that straddles K is loaded as the window
+// ending at K and shifted into place, A chunks past K and B rows at or
+// past K are zeroed.  Full steps thus carry no per-element selects, and
+// the one rewrite per tile sits outside the MFMA stream.  Per-element k
+// order as in big16_kernel (the zeroed tail adds exact zeros).
+template <class W>
+__global__ void __launch_bounds__(256) big16r_kernel(Problem p, int tiles_m, int tiles_n) {
+  using T = typename W::Staging;
+  static_assert(W::STAGES == 2, "two stages");
+  __shared__ __attribute__((aligned(16))) float lds[2 * W::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int ntiles = tiles_m * tiles_n;
+  const int nk = (p.K + W::BK - 1) / W::BK;
+  const bool k_tail = p.K % W::BK != 0;  // the last step of every tile is partial
+  const int G = gridDim.x;
+  const int lid = xcd_remap(blockIdx.x, G);
+  if (lid >= ntiles) return;  // uniform per workgroup
+  const int my_tiles = (ntiles - lid + G - 1) / G;
+
+  // Staging map: A chunk i of this thread is row arow + A_ROWS_PER_PASS i,
+  // k chunk ac; B chunk i is k row bkr + B_ROWS_PER_PASS i, column chunk bc.
+  const int arow = tid / W::ACH, ac = tid % W::ACH;
+  const int bkr = tid / W::BCH, bc = tid % W::BCH;
+  constexpr int kChunks = T::A_CHUNKS + T::B_CHUNKS;
+  f32x4 ra[T::A_CHUNKS], rb[T::B_CHUNKS];
+  const long long a_stride = (long long)T::A_ROWS_PER_PASS * p.lda;
+
+  // Unguarded loads of the step at (m0, n0, k0), kept inside the matrices
+  // when the step is the partial one (clamp).
+  const float *a_src = p.A, *b_src = p.B;
+  long long b_stride = 0;
+  auto load_setup = [&](int m0, int n0, int k0) __attribute__((always_inline)) {
+    const bool partial = k0 + W::BK > p.K;  // uniform
+    const int kc = k0 + 4 * ac;
+    a_src = p.A + (long long)(m0 + arow) * p.lda + (partial ? min(kc, p.K - 4) : kc);
+    b_src = p.B + (partial ? 0LL : (long long)(k0 + bkr) * p.ldb) + n0 + 4 * bc;
+    b_stride = partial ? 0LL : (long long)T::B_ROWS_PER_PASS * p.ldb;
+  };
+  auto load_chunk = [&](int q) __attribute__((always_inline)) {
+    if (q < T::A_CHUNKS)
+      ra[q] = load4(a_src + q * a_stride);
+    else
+      rb[q - T::A_CHUNKS] = load4(b_src + (q - T::A_CHUNKS) * b_stride);
+  };
+  auto store_chunk = [&](float *st, int q) __attribute__((always_inline)) {
+    if (q < T::A_CHUNKS)
+      *reinterpret_cast<f32x4 *>(
+          st + 4 * w16_a_pos<W::ACH>(arow + q * T::A_ROWS_PER_PASS, ac)) = ra[q];
+    else
+      *reinterpret_cast<f32x4 *>(
+          st + W::A_FLOATS +
+          4 * w16_b_pos<W::BCH>(bkr + (q - T::A_CHUNKS) * T::B_ROWS_PER_PASS, bc)) =
+          rb[q - T::A_CHUNKS];
+  };
+  // The guarded form of one step, loaded and written in one go.
+  auto write_guarded = [&](float *st, int m0, int n0, int k0) __attribute__((always_inline)) {
+    const int kc = k0 + 4 * ac;
+    const int valid = kc + 4 <= p.K ? 4 : (kc < p.K ? p.K - kc : 0);
+    const int col = valid == 4 ? kc : p.K - 4;
+    const int a_meta = (valid << 2) | (valid > 0 && valid < 4 ? kc - col : 0);
+    const float *as = p.A + (long long)(m0 + arow) * p.lda + col;
+#pragma unroll
+    for (int i = 0; i < T::A_CHUNKS; ++i) ra[i] = load4(as + i * a_stride);
+    int b_ok = 0;
+#pragma unroll
+    for (int i = 0; i < T::B_CHUNKS; ++i) {
+      const int k = k0 + bkr + i * T::B_ROWS_PER_PASS;
+      const bool ok = k < p.K;
+      b_ok |= (int)ok << i;
+      rb[i] = load4(p.B + (long long)(ok ? k : p.K - 1) * p.ldb + n0 + 4 * bc);
+    }
+    const f32x4 z{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < T::A_CHUNKS; ++i) ra[i] = place(ra[i], a_meta);
+#pragma unroll
+    for (int i = 0; i < T::B_CHUNKS; ++i) rb[i] = (b_ok >> i) & 1 ? rb[i] : z;
+#pragma unroll
+    for (int q = 0; q < kChunks; ++q) store_chunk(st, q);
+  };
+
+  int is_m0, is_n0, is_k0 = 0;  // operands of the step most recently loaded
+  {
+    bool interior;
+    tile_origin<T>(lid, tiles_m, tiles_n, is_m0, is_n0, interior, p);
+  }
+  write_guarded(lds, is_m0, is_n0, 0);
+  int stage = 0;
+
+  f32x4 acc[W::TBM][W::TBN];
+  for (int t = 0; t < my_tiles; ++t) {
+    const int cur_m0 = is_m0, cur_n0 = is_n0;
+    int nt_m0, nt_n0;
+    {
+      bool interior;
+      tile_origin<T>(lid + (t + 1 < my_tiles ? t + 1 : t) * G, tiles_m, tiles_n, nt_m0, nt_n0,
+                     interior, p);
+    }
+#pragma unroll
+    for (int i = 0; i < W::TBM; ++i)
+#pragma unroll
+      for (int j = 0; j < W::TBN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int kk = 0; kk < nk; ++kk) {
+      const bool last = kk + 1 == nk;
+      is_m0 = last ? nt_m0 : cur_m0;
+      is_n0 = last ? nt_n0 : cur_n0;
+      is_k0 = last ? 0 : is_k0 + W::BK;
+      ks_lds_barrier();  // this stage written by every wave; the other one free
+      const float *st = lds + stage * W::STAGE;
+      float *nst = lds + (stage ^ 1) * W::STAGE;
+      load_setup(is_m0, is_n0, is_k0);
+
+      // As big16_kernel, with register loads and LDS writes of the next
+      // step in place of its direct loads: one 128-bit load after each of
+      // the step's first rows of 8 MFMAs (from the second on), one LDS
+      // write after every second row of its second half.
+      f32x4 a0[W::TBM], a1[W::TBM];
+      float b0[W::TBN], b1[W::TBN];
+      w16_read_b<W>(b0, st, 0, 0, lane, wn);
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        const int l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+        for (int bm = 0; bm < W::TBM; ++bm) {
+          a0[bm] = *reinterpret_cast<const f32x4 *>(
+              st + 4 * w16_a_pos<W::ACH>(wm * W::WTM + 16 * bm + l16, g));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < W::NQ; ++h) {
+        f32x4(&acur)[W::TBM] = (h & 1) ? a1 : a0;
+        f32x4(&anext)[W::TBM] = (h & 1) ? a0 : a1;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int grp = 4 * h + u;
+          float(&bcur)[W::TBN] = (grp & 1) ? b1 : b0;
+          float(&bnext)[W::TBN] = (grp & 1) ? b0 : b1;
+#pragma unroll
+          for (int bm = 0; bm < W::TBM; ++bm) {
+#pragma unroll
+            for (int bn = 0; bn < W::TBN; ++bn)
+              acc[bm][bn] = __builtin_amdgcn_mfma_f32_16x16x4f32(bcur[bn], acur[bm][u],
+                                                                 acc[bm][bn], 0, 0, 0);
+            const int lrow = grp * W::TBM + bm - 1;
+            if (lrow >= 0 && lrow < kChunks) {
+              __builtin_amdgcn_sched_barrier(0);
+              load_chunk(lrow);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            constexpr int kRowsPerWrite = 2;
+            constexpr int kFirstRow = 2 * W::NQ * W::TBM;  // the step's second half
+            const int row = grp * W::TBM + bm - kFirstRow;
+            if (row >= 0 && row % kRowsPerWrite == 0 && row / kRowsPerWrite < kChunks) {
+              __builtin_amdgcn_sched_barrier(0);
+              store_chunk(nst, row / kRowsPerWrite);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            if (bm == W::TBM / 2 - 1) {
+              __builtin_amdgcn_sched_barrier(0);
+              if (u < 3)
+                w16_read_b<W>(bnext, st, h, u + 1, lane, wn);
+              else if (h + 1 < W::NQ)
+                w16_read_b<W>(bnext, st, h + 1, 0, lane, wn);
+              if (u == 1 && h + 1 < W::NQ) w16_read_a<W>(anext, st, h + 1, lane, wm);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+        }
+      }
+      // The stage just written holds a partial step: rewrite it zero-filled
+      // (same thread, same addresses, so the rewrite lands last).
+      if (k_tail && kk + 2 == nk) write_guarded(nst, is_m0, is_n0, is_k0);
+      stage ^= 1;
+      // accumulators handed on in accumulation registers (see big16_kernel)
+#pragma unroll
+      for (int i = 0; i < W::TBM; ++i)
+#pragma unroll
+        for (int j = 0; j < W::TBN; ++j) asm volatile("" : "+a"(acc[i][j]));
+    }
+
+    const int l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int bm = 0; bm < W::TBM; ++bm) {
+      float *crow = p.C + (long long)(cur_m0 + wm * W::WTM + 16 * bm + l16) * p.ldc + cur_n0 +
+                    wn * W::WTN + 4 * g;
+#pragma unroll
+      for (int bn = 0; bn < W::TBN; ++bn)
+        *reinterpret_cast<f32x4u *>(crow + 16 * bn) = acc[bm][bn];
+    }
+  }
+}
+
 // Small-K kernel: the whole K (<= BK) of a tile fits one LDS stage, so each
 // iteration of the persistent loop is one complete tile.  It covers only
 // whole tiles (the launcher sends edge strips to the k-loop kernel), which
@@ -2056,6 +2264,7 @@ const Entry kEntries[] = {
     {{128, 128, 64, 2, 2, 1, "128x128x64_w16_ldsdma"}, kKsplit},
     {{256, 256, 32, 4, 4, 1, "256x256x32_w4x4_ldsdma_mfma16"}, kKsplit},
     {{256, 256, 32, 2, 2, 1, "256x256x32_w2x2_ldsdma_mfma16"}, kKsplit},
+    {{256, 256, 32, 2, 2, 1, "256x256x32_w2x2_regs_mfma16"}, kKsplit},
 };
 constexpr int kNumConfigs = sizeof(kEntries) / sizeof(kEntries[0]);
 constexpr int kRemainderConfig = 3;  // thin edge strips
@@ -2141,10 +2350,10 @@ hipError_t launch_w16(const Problem &p, hipStream_t s) {
                        (int)tiles_n);
 }
 
-// The 128x128-wave kernel (big16_kernel) when A and B rows are 16-byte
-// aligned, N % 4 == 0, K is a positive multiple of the k step, C is at
-// least one tile each way and the leading dimensions are below 2^24;
-// otherwise entry 18's launcher (direct loads on 64x64 wave tiles).
+// The 128x128-wave kernel with direct loads (big16_kernel) when A and B
+// rows are 16-byte aligned, N % 4 == 0, K is a positive multiple of the k
+// step, C is at least one tile each way and the leading dimensions are below
+// 2^24; otherwise launch_big16r (the same tiles staged through registers).
 template <class W>
 hipError_t launch_big16(const Problem &p, hipStream_t s);
 
@@ -2218,20 +2427,33 @@ hipError_t launch_arow(const Problem &p, hipStream_t s) {
                        (int)chunks, (int)tiles_n);
 }
 
-template <class W>
-hipError_t launch_big16(const Problem &p, hipStream_t s) {
-  const bool ok = (reinterpret_cast<uintptr_t>(p.A) & 15) == 0 &&
-                  (reinterpret_cast<uintptr_t>(p.B) & 15) == 0 && (p.lda & 3) == 0 &&
-                  (p.ldb & 3) == 0 && (p.N & 3) == 0 && p.M >= W::BM && p.N >= W::BN &&
-                  p.K > 0 && p.K % W::BK == 0 && p.lda < (1 << 24) && p.ldb < (1 << 24);
-  if (!ok) return launch_lds_dma16<C12>(p, s);
+template <class W, auto KERNEL>
+hipError_t launch_big16_grid(const Problem &p, hipStream_t s) {
   const long long tiles_m = ceil_div(p.M, W::BM), tiles_n = ceil_div(p.N, W::BN);
   const long long ntiles = tiles_m * tiles_n;
   if (ntiles > 0x7fffffffLL) return hipErrorInvalidValue;
-  long long grid = resident_workgroups<big16_kernel<W>, 256>();
+  long long grid = resident_workgroups<KERNEL, 256>();
   if (grid > ntiles) grid = ntiles;
-  return launch_kernel(big16_kernel<W>, dim3((unsigned)grid), dim3(256), s, p, (int)tiles_m,
-                       (int)tiles_n);
+  return launch_kernel(KERNEL, dim3((unsigned)grid), dim3(256), s, p, (int)tiles_m, (int)tiles_n);
+}
+
+// 128x128-wave tiles with register staging (big16r_kernel) when C is at
+// least one tile each way and K >= 4; otherwise the register-staged 32x32
+// kernel with the same tiles.
+template <class W>
+hipError_t launch_big16r(const Problem &p, hipStream_t s) {
+  if (p.M < W::BM || p.N < W::BN || p.K < 4) return launch_kloop<C12>(p, s);
+  return launch_big16_grid<W, big16r_kernel<W>>(p, s);
+}
+
+template <class W>
+hipError_t launch_big16(const Problem &p, hipStream_t s) {
+  const bool direct = (reinterpret_cast<uintptr_t>(p.A) & 15) == 0 &&
+                      (reinterpret_cast<uintptr_t>(p.B) & 15) == 0 && (p.lda & 3) == 0 &&
+                      (p.ldb & 3) == 0 && (p.N & 3) == 0 && p.M >= W::BM && p.N >= W::BN &&
+                      p.K > 0 && p.K % W::BK == 0 && p.lda < (1 << 24) && p.ldb < (1 << 24);
+  if (!direct) return launch_big16r<W>(p, s);
+  return launch_big16_grid<W, big16_kernel<W>>(p, s);
 }
 
 hipError_t launch_one(int index, const Problem &p, hipStream_t s) {
@@ -2256,6 +2478,7 @@ hipError_t launch_one(int index, const Problem &p, hipStream_t s) {
     case 17: return launch_w16<W16<64, 64, 64, 2>, C0>(p, s);
     case 18: return launch_lds_dma16<C12>(p, s);
     case 19: return launch_big16<W16<128, 128, 32, 2>>(p, s);
+    case 20: return launch_big16r<W16<128, 128, 32, 2>>(p, s);
 
     default: return hipErrorInvalidValue;
   }
@@ -2301,10 +2524,11 @@ bool prod_supports(int index, int M, int N, int K) {
 // the best modelled rate: its measured full-occupancy rate times the
 // fraction of workgroup slots its tiles fill over whole rounds (one
 // workgroup per CU, 256 CUs), counting tiles after the thin remainder
-// strips are split off.  Candidates: 256x256x32 with direct-to-LDS loads on
-// 16x16 MFMAs -- 128x128 wave tiles when K is a multiple of 32 (148
-// TFLOP/s), else 64x64 ones (138) --, 128x128x64 with one wave per SIMD and
-// 16x16 MFMAs (124), and 64x64x64 with K split over the waves (95).
+// strips are split off.  Candidates: 256x256x32 on 16x16 MFMAs with
+// 128x128 wave tiles (148 TFLOP/s with direct loads, which need K a
+// multiple of 32 and aligned rows; about 135 staged through registers),
+// 128x128x64 with one wave per SIMD and 16x16 MFMAs (124), and 64x64x64
+// with K split over the waves (95).
 int prod_choose(int M, int N, int K) {
   const long long t256x128 = ceil_div(M, 256) * ceil_div(N, 128);
   if (K <= 64 && t256x128 >= 1024) return 14;
@@ -2313,8 +2537,7 @@ int prod_choose(int M, int N, int K) {
     double rate;
   };
   const bool whole_steps = K % 32 == 0;
-  const Cand cands[] = {whole_steps ? Cand{19, 256, 148.0} : Cand{18, 256, 138.0},
-                        {17, 128, 124.0}, {16, 64, 95.0}};
+  const Cand cands[] = {{19, 256, whole_steps ? 148.0 : 135.0}, {17, 128, 124.0}, {16, 64, 95.0}};
   constexpr long long kSlots = 256;  // CUs of an MI355X, one workgroup each
   int best = 16;
   double best_score = -1.0;
