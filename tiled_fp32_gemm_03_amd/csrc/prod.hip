@@ -2139,6 +2139,254 @@ __global__ void __launch_bounds__(S::NT)
   }
 }
 
+// ---- A-resident small-K kernel on 16x16 MFMAs, one wave per SIMD ---------
+// The skinny product's recipe (A panel resident, only B moves per column
+// tile, C stores of one tile drained during the next tile's MFMAs) on the
+// 128x128-wave kernel's machinery: a 256x128 tile over 4 waves (2 x 2),
+// each computing 128x64 as 8 x 4 blocks of v_mfma_f32_16x16x4_f32 -- 32
+// chains and 128 accumulators per set, two sets (256 accumulation
+// registers) so that tile i computes into one set while tile i - 1 leaves
+// from the other.  K is exactly 64.  LDS: the 256x64 A panel (64 KB, rows of
+// 16 chunks at c ^ (r & 15)) loaded once, and two 64x128 B buffers (32 KB
+// each, chunks of k row k at c ^ (4 ((k >> 2) & 3))), all by direct loads.
+// Per tile a wave issues 512 MFMAs against 8 direct loads (the next tile's
+// B, in the first rows), 32 C stores (spread over the rest) and one
+// barrier; the wait before it lets the stores drain (the vector-memory
+// counter retires in issue order and the loads went first).
+struct Arow16 {
+  static constexpr int WTM = 128, WTN = 64, BK = 64;
+  static constexpr int BM = 2 * WTM, BN = 2 * WTN;
+  static constexpr int TBM = WTM / 16, TBN = WTN / 16;
+  static constexpr int NQ = BK / 16;
+  static constexpr int ACH = BK / 4, BCH = BN / 4;
+  static constexpr int A_FLOATS = BM * BK, B_FLOATS = BK * BN;
+  static constexpr int A_DMA = A_FLOATS / 1024;  // per wave: (A_FLOATS * 4 / 1024) / 4
+  static constexpr int B_DMA = B_FLOATS / 1024;
+  static constexpr int ARPI = 64 / ACH, BRPI = 64 / BCH;
+  static constexpr int STORES = TBM * TBN;  // 16-byte stores per lane and tile
+  static_assert((A_FLOATS + 2 * B_FLOATS) * 4 <= kLdsBytes, "A and two B buffers fit");
+  static_assert(STORES + B_DMA < 64, "vmcnt holds at most 63");
+};
+
+using Acc16 = f32x4[Arow16::TBM][Arow16::TBN];
+
+__device__ inline void arow16_store(const Acc16 &acc, const Problem &p, int m0, int n0, int wm,
+                                    int wn, int lane, int i) {
+  const int l16 = lane & 15, g = lane >> 4;
+  const int bm = i / Arow16::TBN, bn = i % Arow16::TBN;
+  float *dst = p.C + (long long)(m0 + wm * Arow16::WTM + 16 * bm + l16) * p.ldc + n0 +
+               wn * Arow16::WTN + 16 * bn + 4 * g;
+  *reinterpret_cast<f32x4 *>(dst) = acc[bm][bn];
+}
+
+// One column tile: MFMAs of tile n0 from B buffer `buf` into `acc` (zeroed
+// first), the next tile's B (column nn0) into the other buffer, and, with
+// STORE, the previous tile (column pn0, in `prev`) out to C.
+// Fragment reads from per-lane LDS pointers with the rest of each address
+// a constant: a[h] points at the A chunk h of row block 0 (row block bm is
+// bm * 1024 floats further), b[bn] at B column block bn, k row 4 g, of
+// buffer 0 (k row 16 h + t is (16 h + t) * BN floats further, buffer 1
+// B_FLOATS further).
+struct Arow16Lane {
+  const float *a[Arow16::NQ];
+  const float *b[Arow16::TBN];
+};
+
+__device__ inline Arow16Lane arow16_lane(const float *lds, int lane, int wm, int wn) {
+  using W = Arow16;
+  const int l16 = lane & 15, g = lane >> 4;
+  Arow16Lane o;
+#pragma unroll
+  for (int h = 0; h < W::NQ; ++h)
+    o.a[h] = lds + 4 * w16_a_pos<W::ACH>(wm * W::WTM + l16, 4 * h + g);
+#pragma unroll
+  for (int bn = 0; bn < W::TBN; ++bn) {
+    const int n = wn * W::WTN + 16 * bn + l16;
+    o.b[bn] = lds + W::A_FLOATS + 4 * w16_b_pos<W::BCH>(4 * g, n >> 2) + (n & 3);
+  }
+  return o;
+}
+
+template <int H, int BUF>
+__device__ inline void arow16_read_a(f32x4 (&a)[Arow16::TBM], const Arow16Lane &o) {
+#pragma unroll
+  for (int bm = 0; bm < Arow16::TBM; ++bm)
+    a[bm] = *reinterpret_cast<const f32x4 *>(o.a[H] + bm * 1024);
+}
+template <int KROW, int BUF>
+__device__ inline void arow16_read_b(float (&b)[Arow16::TBN], const Arow16Lane &o) {
+#pragma unroll
+  for (int bn = 0; bn < Arow16::TBN; ++bn)
+    b[bn] = o.b[bn][KROW * Arow16::BN + BUF * Arow16::B_FLOATS];
+}
+
+template <bool STORE, int BUF>
+__device__ __forceinline__ void arow16_tile(Acc16 &acc, Acc16 &prev, const Problem &p,
+                                            int m0, int pn0, int nn0, const float *lds,
+                                            unsigned lds_u, const unsigned (&voff)[Arow16::B_DMA],
+                                            const Arow16Lane &o, int wave, int wm, int wn,
+                                            int lane) {
+  constexpr int buf = BUF;
+  using W = Arow16;
+#pragma unroll
+  for (int i = 0; i < W::TBM; ++i)
+#pragma unroll
+    for (int j = 0; j < W::TBN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float *bsrc = p.B + nn0;
+  const unsigned bdst = lds_u + (W::A_FLOATS + (buf ^ 1) * W::B_FLOATS) * 4 + wave * W::B_DMA * 1024;
+  f32x4 a0[W::TBM], a1[W::TBM];
+  float b0[W::TBN], b1[W::TBN];
+  arow16_read_b<0, BUF>(b0, o);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int bm = 0; bm < W::TBM; ++bm) {
+    a0[bm] = *reinterpret_cast<const f32x4 *>(o.a[0] + bm * 1024);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  auto mfma_rows = [&](auto hc, auto uc, f32x4(&acur)[W::TBM], f32x4(&anext)[W::TBM],
+                       float(&bcur)[W::TBN], float(&bnext)[W::TBN]) __attribute__((always_inline)) {
+    constexpr int h = decltype(hc)::value, u = decltype(uc)::value;
+    constexpr int grp = 4 * h + u;
+#pragma unroll
+    for (int bm = 0; bm < W::TBM; ++bm) {
+#pragma unroll
+      for (int bn = 0; bn < W::TBN; ++bn)
+        acc[bm][bn] =
+            __builtin_amdgcn_mfma_f32_16x16x4f32(bcur[bn], acur[bm][u], acc[bm][bn], 0, 0, 0);
+      // rows of 4 MFMAs: the next B's direct loads after rows 0, 2, ..,
+      // then one C store after every third row
+      const int row = grp * W::TBM + bm;
+      if (row % 2 == 0 && row / 2 < W::B_DMA) {
+        __builtin_amdgcn_sched_barrier(0);
+        ks_load_to_lds16(voff[row / 2], bsrc, bdst + (row / 2) * 1024);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      constexpr int kFirstStoreRow = 2 * W::B_DMA;
+      const int srow = row - kFirstStoreRow;
+      if (STORE && srow >= 0 && srow % 3 == 0 && srow / 3 < W::STORES) {
+        __builtin_amdgcn_sched_barrier(0);
+        arow16_store(prev, p, m0, pn0, wm, wn, lane, srow / 3);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (bm == W::TBM / 2 - 1) {
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (u < 3)
+          arow16_read_b<16 * h + u + 1, BUF>(bnext, o);
+        else if constexpr (h + 1 < W::NQ)
+          arow16_read_b<16 * (h + 1), BUF>(bnext, o);
+        if constexpr (u == 1 && h + 1 < W::NQ)
+          arow16_read_a<(h + 1 < W::NQ ? h + 1 : 0), BUF>(anext, o);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  static_assert(W::NQ == 4, "four 16-deep chunks");
+  mfma_rows(I0{}, I0{}, a0, a1, b0, b1);
+  mfma_rows(I0{}, I1{}, a0, a1, b1, b0);
+  mfma_rows(I0{}, I2{}, a0, a1, b0, b1);
+  mfma_rows(I0{}, I3{}, a0, a1, b1, b0);
+  mfma_rows(I1{}, I0{}, a1, a0, b0, b1);
+  mfma_rows(I1{}, I1{}, a1, a0, b1, b0);
+  mfma_rows(I1{}, I2{}, a1, a0, b0, b1);
+  mfma_rows(I1{}, I3{}, a1, a0, b1, b0);
+  mfma_rows(I2{}, I0{}, a0, a1, b0, b1);
+  mfma_rows(I2{}, I1{}, a0, a1, b1, b0);
+  mfma_rows(I2{}, I2{}, a0, a1, b0, b1);
+  mfma_rows(I2{}, I3{}, a0, a1, b1, b0);
+  mfma_rows(I3{}, I0{}, a1, a0, b0, b1);
+  mfma_rows(I3{}, I1{}, a1, a0, b1, b0);
+  mfma_rows(I3{}, I2{}, a1, a0, b0, b1);
+  mfma_rows(I3{}, I3{}, a1, a0, b1, b0);
+  // The next B is in (own loads; the stores issued after them may drain),
+  // then every wave's, and every wave is done with this buffer.
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(STORE ? W::STORES : 0));
+  ks_lds_barrier();
+#pragma unroll
+  for (int i = 0; i < W::TBM; ++i)
+#pragma unroll
+    for (int j = 0; j < W::TBN; ++j) {
+      asm volatile("" : "+a"(acc[i][j]));
+      asm volatile("" : "+a"(prev[i][j]));
+    }
+}
+
+// Workgroup (panel, chunk) owns rows [256 panel, +256) and the column tiles
+// [t0, t1) of that panel, walked from a rotated start as in
+// panel_arow_kernel.  The launcher guarantees K == 64, M % 256 == 0,
+// N % 128 == 0, 16-byte aligned rows of A and B and leading dimensions
+// below 2^24.
+__global__ void __launch_bounds__(256) arow16_kernel(Problem p, int panels, int chunks,
+                                                     int tiles_n) {
+  using W = Arow16;
+  __shared__ __attribute__((aligned(16))) float lds[W::A_FLOATS + 2 * W::B_FLOATS];
+  const unsigned lds_u = (unsigned)(uintptr_t)(lds_void_t *)lds;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int panel = lid / chunks, chunk = lid % chunks;
+  if (panel >= panels) return;  // uniform per workgroup
+  const int t0 = (int)((long long)chunk * tiles_n / chunks);
+  const int t1 = (int)((long long)(chunk + 1) * tiles_n / chunks);
+  const int n = t1 - t0;  // >= 1: the launcher keeps chunks <= tiles_n
+  const int m0 = panel * W::BM;
+  const int rot = panel % n;
+  auto col = [&](int i) __attribute__((always_inline)) {
+    const int k = i < n ? i : n - 1;
+    return (t0 + (k + rot) % n) * W::BN;
+  };
+
+  // Direct-load offsets: the A panel (once) and a B tile (per tile).
+  unsigned voff[W::B_DMA];
+#pragma unroll
+  for (int q = 0; q < W::B_DMA; ++q) {
+    const int k = W::BRPI * (wave * W::B_DMA + q) + lane / W::BCH;
+    const int c = (lane % W::BCH) ^ (4 * ((k >> 2) & 3));
+    voff[q] = (unsigned)(((long long)k * p.ldb + 4 * c) * 4);
+  }
+  {
+    const float *asrc = p.A + (long long)m0 * p.lda;
+#pragma unroll
+    for (int q = 0; q < W::A_DMA; ++q) {
+      const int blk = wave * W::A_DMA + q;
+      const int r = W::ARPI * blk + lane / W::ACH;
+      const int c = (lane % W::ACH) ^ w16_a_perm<W::ACH>(r);
+      ks_load_to_lds16((unsigned)(((long long)r * p.lda + 4 * c) * 4), asrc, lds_u + blk * 1024);
+    }
+    const float *bsrc = p.B + col(0);
+#pragma unroll
+    for (int q = 0; q < W::B_DMA; ++q)
+      ks_load_to_lds16(voff[q], bsrc, lds_u + W::A_FLOATS * 4 + (wave * W::B_DMA + q) * 1024);
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(0));
+    ks_lds_barrier();
+  }
+
+  const Arow16Lane o = arow16_lane(lds, lane, wm, wn);
+  Acc16 acc0, acc1;
+  arow16_tile<false, 0>(acc0, acc0, p, m0, 0, col(1), lds, lds_u, voff, o, wave, wm, wn, lane);
+  int i = 1;
+  for (; i + 1 < n; i += 2) {
+    arow16_tile<true, 1>(acc1, acc0, p, m0, col(i - 1), col(i + 1), lds, lds_u, voff, o, wave,
+                         wm, wn, lane);
+    arow16_tile<true, 0>(acc0, acc1, p, m0, col(i), col(i + 2), lds, lds_u, voff, o, wave, wm,
+                         wn, lane);
+  }
+  if (i < n) {  // one tile left, in buffer 1: compute it while the previous one drains
+    arow16_tile<true, 1>(acc1, acc0, p, m0, col(i - 1), col(i), lds, lds_u, voff, o, wave, wm,
+                         wn, lane);
+#pragma unroll
+    for (int q = 0; q < W::STORES; ++q) arow16_store(acc1, p, m0, col(i), wm, wn, lane, q);
+  } else {
+#pragma unroll
+    for (int q = 0; q < W::STORES; ++q) arow16_store(acc0, p, m0, col(i - 1), wm, wn, lane, q);
+  }
+}
+
 // Thin-M kernel for a bottom remainder strip of at most R rows (a strip too
 // thin for MFMA tiles: a 256-row tile holding one valid row would cost a
 // whole round of tiles).  The strip's time is the stream of B, so the kernel
@@ -2265,6 +2513,7 @@ const Entry kEntries[] = {
     {{256, 256, 32, 4, 4, 1, "256x256x32_w4x4_ldsdma_mfma16"}, kKsplit},
     {{256, 256, 32, 2, 2, 1, "256x256x32_w2x2_ldsdma_mfma16"}, kKsplit},
     {{256, 256, 32, 2, 2, 1, "256x256x32_w2x2_regs_mfma16"}, kKsplit},
+    {{256, 128, 64, 2, 2, 1, "panel256x128_k64_arow_mfma16"}, kPanel},
 };
 constexpr int kNumConfigs = sizeof(kEntries) / sizeof(kEntries[0]);
 constexpr int kRemainderConfig = 3;  // thin edge strips
@@ -2456,6 +2705,26 @@ hipError_t launch_big16(const Problem &p, hipStream_t s) {
   return launch_big16_grid<W, big16_kernel<W>>(p, s);
 }
 
+// The A-resident kernel on 16x16 MFMAs (arow16_kernel) when K == 64, C is
+// whole 256x128 tiles, A and B rows are 16-byte aligned and the leading
+// dimensions are below 2^24; otherwise the 32x32-MFMA A-resident kernel.
+hipError_t launch_arow16(const Problem &p, hipStream_t s) {
+  using W = Arow16;
+  const bool ok = p.K == W::BK && p.M % W::BM == 0 && p.N % W::BN == 0 && p.M > 0 && p.N > 0 &&
+                  (reinterpret_cast<uintptr_t>(p.A) & 15) == 0 &&
+                  (reinterpret_cast<uintptr_t>(p.B) & 15) == 0 && (p.lda & 3) == 0 &&
+                  (p.ldb & 3) == 0 && p.lda < (1 << 24) && p.ldb < (1 << 24);
+  if (!ok) return launch_arow<P9>(p, s);
+  const long long panels = p.M / W::BM, tiles_n = p.N / W::BN;
+  if (panels * tiles_n > 0x7fffffffLL) return hipErrorInvalidValue;
+  const long long slots = resident_workgroups<arow16_kernel, 256>();
+  long long chunks = ceil_div(slots, panels);
+  if (chunks > tiles_n) chunks = tiles_n;
+  if (chunks < 1) chunks = 1;
+  return launch_kernel(arow16_kernel, dim3((unsigned)(panels * chunks)), dim3(256), s, p,
+                       (int)panels, (int)chunks, (int)tiles_n);
+}
+
 hipError_t launch_one(int index, const Problem &p, hipStream_t s) {
   switch (index) {
     case 0: return launch_kloop<C0>(p, s);
@@ -2479,6 +2748,7 @@ hipError_t launch_one(int index, const Problem &p, hipStream_t s) {
     case 18: return launch_lds_dma16<C12>(p, s);
     case 19: return launch_big16<W16<128, 128, 32, 2>>(p, s);
     case 20: return launch_big16r<W16<128, 128, 32, 2>>(p, s);
+    case 21: return launch_arow16(p, s);
 
     default: return hipErrorInvalidValue;
   }
@@ -2520,7 +2790,9 @@ bool prod_supports(int index, int M, int N, int K) {
 
 // Shape-based choice from measurements on MI355X.  K <= 64 with many tiles:
 // the A-resident small-K panel kernel (only B moves per tile; C stores
-// interleaved with the next tile's MFMAs).  Otherwise the k-loop entry with
+// interleaved with the next tile's MFMAs), on 16x16 MFMAs with one wave per
+// SIMD when K == 64 and the rows are aligned (entry 21's launcher falls
+// back to the 32x32 form otherwise).  Otherwise the k-loop entry with
 // the best modelled rate: its measured full-occupancy rate times the
 // fraction of workgroup slots its tiles fill over whole rounds (one
 // workgroup per CU, 256 CUs), counting tiles after the thin remainder
@@ -2531,7 +2803,7 @@ bool prod_supports(int index, int M, int N, int K) {
 // with K split over the waves (95).
 int prod_choose(int M, int N, int K) {
   const long long t256x128 = ceil_div(M, 256) * ceil_div(N, 128);
-  if (K <= 64 && t256x128 >= 1024) return 14;
+  if (K <= 64 && t256x128 >= 1024) return 21;
   struct Cand {
     int entry, tile;
     double rate;
