@@ -215,7 +215,12 @@ def test_own_order_entries(g, entry):
         (130, 1000, 2048, 0, 0, 0), (2048, 2048, 512, 0, 0, 0), (64, 64, 64, 0, 0, 0),
         (777, 516, 700, 4, 8, 5), (300, 300, 257, 1, 0, 0), (512, 260, 96, 0, 3, 0),
         (2304, 1280, 320, 0, 0, 0), (260, 132, 100, 0, 0, 0), (4352, 4100, 32, 0, 0, 0),
-        (600, 520, 96, 4, 8, 5)]
+        (600, 520, 96, 4, 8, 5),
+        # register-staged 128x128-wave path: K below one step, a tail of 1
+        # after one full step, the 4-element minimum, rows not 16-byte
+        # aligned, and workgroups that walk two tiles with a K tail
+        (256, 256, 31, 0, 0, 0), (512, 300, 33, 1, 0, 0), (300, 260, 4, 0, 1, 0),
+        (4352, 4096, 40, 0, 0, 0)]
     for (M, N, K, pa, pb, pc) in cases:
         for dist in ("small_int", "normal"):
             print(f"case: entry {entry} {M}x{N}x{K} pad {pa},{pb},{pc} {dist}", flush=True)
