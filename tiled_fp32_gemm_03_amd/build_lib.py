@@ -20,7 +20,12 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgemm_f32.so")
 ARCH = "gfx950"
 
-SOURCES = ["gemm_f32_abi.hip", "naive_tiled.hip", "prod.hip", "valu.hip", "mixed.hip", "probes.hip"]
+SOURCES = ["gemm_f32_abi.hip", "naive_tiled.hip", "prod.hip", "big192.hip", "valu.hip", "mixed.hip",
+           "probes.hip"]
+
+# Per-source flags: the 192x192 kernel keeps its accumulators in VGPRs (the
+# MFMAs' VGPR form); see big192.hip.
+SOURCE_FLAGS = {"big192.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
@@ -39,7 +44,8 @@ def hipcc() -> str:
 
 def _compile(src: str, extra: list[str], verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src),
+           "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

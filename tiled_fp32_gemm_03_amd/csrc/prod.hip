@@ -56,6 +56,7 @@
 #include "gemm_internal.hpp"
 #include "launch_util.hpp"
 #include "tile_order.hpp"
+#include "w16_tiles.hpp"
 
 #include <atomic>
 #include <cstdint>
@@ -63,8 +64,6 @@
 namespace gemm_f32_impl {
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kPadA = 4;  // floats after each LDS row of A (k-contiguous rows)
@@ -94,7 +93,11 @@ struct Tile {
                 "tile must split evenly over threads");
 };
 
-constexpr int kLdsBytes = 160 * 1024;  // LDS of one gfx950 CU
+
+// Register staging map of a W16 tile (the K-tail and narrow-product path
+// of the 16x16-MFMA kernels).
+template <class W>
+using W16Staging = Tile<W::BM, W::BN, W::BK, 2, 2, false>;
 
 template <class S>
 struct Stage {
@@ -303,23 +306,6 @@ __device__ inline void store_c(const f32x16 (&acc)[S::TM][S::TN],
   }
 }
 
-// Tile t's origin.  A last tile row or column that would overhang C is
-// moved back to end at C's edge (when C is at least one tile wide): it then
-// overlaps its neighbour, and both compute the shared elements with the same
-// k order, so they store identical values -- while the tile needs no guarded
-// loads.  Only a product narrower than one tile keeps guarded edges.
-template <class S>
-__device__ inline void tile_origin(int t, int tiles_m, int tiles_n, int &m0,
-                                   int &n0, bool &interior, const Problem &p) {
-  int tm, tn;
-  tile_coords(t, tiles_m, tiles_n, tm, tn);
-  m0 = tm * S::BM;
-  n0 = tn * S::BN;
-  if (m0 + S::BM > p.M && p.M >= S::BM) m0 = p.M - S::BM;
-  if (n0 + S::BN > p.N && p.N >= S::BN) n0 = p.N - S::BN;
-  interior = (m0 + S::BM <= p.M) && (n0 + S::BN <= p.N);
-}
-
 // Load one k step; returns whether the guarded path was taken (uniform).
 template <class S>
 __device__ inline bool load_step(Stage<S> &st, const Problem &p, int m0,
@@ -477,13 +463,6 @@ __global__ void __launch_bounds__(kReduceThreads)
   }
 }
 
-// s_waitcnt immediate that waits until at most `n` vector-memory operations
-// of this wave are outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
-// expcnt and lgkmcnt left at their "no wait" maxima).
-constexpr int vmcnt_wait_imm(int n) {
-  return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
-}
-
 // ---- k-loop kernel with direct-to-LDS operand loads ---------------------
 // global_load_lds_dwordx4 writes each lane's 16 bytes straight into LDS at
 // the wave's base address + 16 * lane.  An interior k step then needs no
@@ -499,8 +478,6 @@ constexpr int vmcnt_wait_imm(int n) {
 // overhangs a product narrower than one tile) go through registers and write
 // the same layout before the step's MFMAs.  Each element is summed in the
 // same k order as in prod_kernel, so the two give identical bits.
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void global_void_t;
 
 __device__ inline void load_to_lds16(const float *src, float *lds_dst) {
   __builtin_amdgcn_global_load_lds((global_void_t *)src, (lds_void_t *)lds_dst, 16, 0, 0);
@@ -909,20 +886,6 @@ constexpr int kKsStageFloats = 64 * 64 * 2;   // A and B, unpadded
 constexpr int kKsRedFloats = 4 * 64 * 64;     // the four partial tiles
 constexpr int kKsDmaPerWave = 8;              // 4 A + 4 B instructions of 1 KB
 
-// The direct loads of this kernel are issued from inline assembly, with an
-// SGPR base address, a per-lane 32-bit byte offset and the wave's LDS
-// destination in M0, so that the compiler does not see them as LDS writes:
-// it would otherwise wait for every outstanding one (vmcnt(0)) before each
-// later LDS read, which would serialise the pipeline.  The kernel orders
-// them itself: explicit vmcnt waits before each barrier, and every LDS read
-// of a stage happens after the barrier that follows its loads.
-__device__ inline void ks_load_to_lds16(unsigned voff, const float *sbase, unsigned lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(lds_addr)
-               : "memory", "m0");
-}
-
 __device__ inline int ks_a_pos(int r, int c) { return r * 16 + (c ^ (r & 15)); }
 __device__ inline int ks_b_pos(int k, int c) { return k * 16 + (c ^ (4 * ((k >> 2) & 3))); }
 
@@ -992,18 +955,6 @@ __device__ inline void ks_mfma(f32x4 (&acc)[4][4], const KsFrag &f, const unsign
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-}
-
-// Waits until this wave's LDS operations have completed (as a builtin, so
-// the compiler knows the fragment registers are ready), then the workgroup
-// barrier.  Unlike __syncthreads() it does not wait for outstanding
-// vector-memory loads, so direct loads of later steps stay in flight; the
-// memory clobber keeps the compiler from moving memory accesses across it.
-constexpr int kLgkmWait0 = 0xF | (0x3 << 14) | (0x7 << 4);  // lgkmcnt(0) only
-
-__device__ inline void ks_lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(kLgkmWait0);
-  asm volatile("s_barrier" ::: "memory");
 }
 
 // The launcher guarantees M, N >= 64 (every tile lies inside C after the
@@ -1188,61 +1139,9 @@ __global__ void __launch_bounds__(256) ksplit_kernel(Problem p, int tiles_m, int
   }
 }
 
-// ---- one wave per SIMD, 16x16x4 MFMAs, direct-load pipeline -----------
-// The large-product form of the K-split kernel's recipe: a BM x BN tile
-// (BM = 2 WTM, BN = 2 WTN) over 4 waves, each computing a WTM x WTN sub-tile
-// as 16x16 blocks with v_mfma_f32_16x16x4_f32 -- (WTM/16)(WTN/16)
-// independent accumulator chains, so a lone wave keeps the matrix pipe busy.
-// Operands arrive by direct loads (inline assembly, as in ksplit_kernel)
-// into STAGES LDS stages of BK-deep k steps: the loads of step
-// i + STAGES - 1 are issued during step i, into the stage that step i - 1
-// used.  Inside a step the fragments are read 16 k at a time, one chunk
-// ahead of the MFMAs.  Within a 16-deep chunk h, MFMA t takes
-// k = 16 h + 4 g + t for lane group g = l / 16.  LDS layouts (16-byte
-// chunks): A rows of BK floats, chunk c of row r at c ^ ((r >> 1) & 7) for
-// BK = 32 and at c ^ (r & 15) for BK = 64; B rows of BN floats,
-// chunk c of k row k at c ^ (4 ((k >> 2) & 3)).  Each element is summed in
-// one fp32 accumulator in ascending k steps, but the k order inside a step
-// differs from prod_kernel, so the bits may differ.
-template <int WTM_, int WTN_, int BK_, int STAGES_>
-struct W16 {
-  static constexpr int WTM = WTM_, WTN = WTN_, BK = BK_, STAGES = STAGES_;
-  static constexpr int BM = 2 * WTM, BN = 2 * WTN;
-  static constexpr int TBM = WTM / 16, TBN = WTN / 16;
-  static constexpr int NQ = BK / 16;      // 16-deep chunks per step
-  static constexpr int ACH = BK / 4;      // 16-byte chunks per A row
-  static constexpr int ARPI = 64 / ACH;   // A rows per 1 KB instruction
-  static constexpr int BCH = BN / 4;      // 16-byte chunks per B row
-  static constexpr int BRPI = 64 / BCH;   // B rows per instruction
-  static constexpr int A_FLOATS = BM * BK, B_FLOATS = BK * BN, STAGE = A_FLOATS + B_FLOATS;
-  static constexpr int A_DMA = A_FLOATS / 256 / 4;  // instructions per wave and step
-  static constexpr int B_DMA = B_FLOATS / 256 / 4;
-  static constexpr int DMA = A_DMA + B_DMA;
-  using Staging = Tile<BM, BN, BK, 2, 2, false>;  // map for the register path
-  static_assert(BK == 32 || BK == 64, "A rows of 32 or 64 floats");
-  static_assert(BCH >= 16 && 64 % BCH == 0, "B rows of 64..256 floats");
-  static_assert(A_FLOATS % 1024 == 0 && B_FLOATS % 1024 == 0, "whole instructions per wave");
-  static_assert(STAGES >= 2 && STAGES * STAGE * 4 <= kLdsBytes, "LDS budget");
-};
-
-// Row permutation of A chunks: 16 consecutive rows land on distinct banks
-// (rows of 128 B pair up in a 256-byte bank window; rows of 256 B fill it).
-template <int ACH>
-__device__ inline int w16_a_perm(int r) {
-  return ACH == 16 ? (r & 15) : ((r >> 1) & 7);
-}
-template <int ACH>
-__device__ inline int w16_a_pos(int r, int c) {
-  return r * ACH + (c ^ w16_a_perm<ACH>(r));
-}
-template <int BCH>
-__device__ inline int w16_b_pos(int k, int c) {
-  return k * BCH + (c ^ (4 * ((k >> 2) & 3)));
-}
-
 template <class W, bool PLACED>
-__device__ inline void w16_store_stage(const Stage<typename W::Staging> &sg, float *st, int tid) {
-  using T = typename W::Staging;
+__device__ inline void w16_store_stage(const Stage<W16Staging<W>> &sg, float *st, int tid) {
+  using T = W16Staging<W>;
   const int arow = tid / (T::BK / 4), ac = tid % (T::BK / 4);
 #pragma unroll
   for (int i = 0; i < T::A_CHUNKS; ++i) {
@@ -1257,42 +1156,6 @@ __device__ inline void w16_store_stage(const Stage<typename W::Staging> &sg, flo
     *reinterpret_cast<f32x4 *>(st + W::A_FLOATS + 4 * w16_b_pos<W::BCH>(k, bc)) =
         PLACED ? place(sg.b[i], sg.bmeta[i]) : sg.b[i];
   }
-}
-
-// Fragments, per lane (l16 = lane % 16, g = lane / 16): for 16-deep chunk
-// h, A[row l16 of block bm][k = 16 h + 4 g .. + 3] as one 16-byte read,
-// and for MFMA t of the chunk B[k = 16 h + 4 g + t][column l16 of block bn].
-template <class W>
-__device__ inline void w16_read_a(f32x4 (&a)[W::TBM], const float *st, int h, int lane, int wm) {
-  const int l16 = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int bm = 0; bm < W::TBM; ++bm)
-    a[bm] = *reinterpret_cast<const f32x4 *>(
-        st + 4 * w16_a_pos<W::ACH>(wm * W::WTM + 16 * bm + l16, 4 * h + g));
-}
-
-template <class W>
-__device__ inline void w16_read_b(float (&b)[W::TBN], const float *st, int h, int t, int lane,
-                                  int wn) {
-  const int l16 = lane & 15, g = lane >> 4;
-  const int k = 16 * h + 4 * g + t;
-#pragma unroll
-  for (int bn = 0; bn < W::TBN; ++bn) {
-    const int n = wn * W::WTN + 16 * bn + l16;
-    b[bn] = st[W::A_FLOATS + 4 * w16_b_pos<W::BCH>(k, n >> 2) + (n & 3)];
-  }
-}
-
-// MFMA t of a chunk over all blocks of the wave tile, from separately held
-// A (chunk) and B (MFMA t) fragments.
-template <class W>
-__device__ inline void w16_mfma_t(f32x4 (&acc)[W::TBM][W::TBN], const f32x4 (&a)[W::TBM],
-                                  const float (&b)[W::TBN], int t) {
-#pragma unroll
-  for (int bm = 0; bm < W::TBM; ++bm)
-#pragma unroll
-    for (int bn = 0; bn < W::TBN; ++bn)
-      acc[bm][bn] = __builtin_amdgcn_mfma_f32_16x16x4f32(b[bn], a[bm][t], acc[bm][bn], 0, 0, 0);
 }
 
 // All fragments of one chunk, read together (w16_kernel reads a chunk
@@ -1337,7 +1200,7 @@ __device__ inline void w16_mfma(f32x4 (&acc)[W::TBM][W::TBN], const W16Frag<W> &
 // dimensions below 2^24.
 template <class W>
 __global__ void __launch_bounds__(256) w16_kernel(Problem p, int tiles_m, int tiles_n) {
-  using T = typename W::Staging;
+  using T = W16Staging<W>;
   __shared__ __attribute__((aligned(16))) float lds[W::STAGES * W::STAGE];
   const unsigned lds_u = (unsigned)(uintptr_t)(lds_void_t *)lds;
 
@@ -1366,9 +1229,9 @@ __global__ void __launch_bounds__(256) w16_kernel(Problem p, int tiles_m, int ti
   }
 #pragma unroll
   for (int q = 0; q < W::B_DMA; ++q) {
-    const int blk = wave * W::B_DMA + q;
-    const int k = W::BRPI * blk + lane / W::BCH;
-    const int c = (lane % W::BCH) ^ (4 * ((k >> 2) & 3));
+    const int j = 64 * (wave * W::B_DMA + q) + lane;  // LDS chunk this lane fills
+    const int k = j / W::BCH;
+    const int c = (j % W::BCH) ^ (4 * ((k >> 2) & 3));
     voff[W::A_DMA + q] = (unsigned)(((long long)k * p.ldb + 4 * c) * 4);
   }
   const unsigned wave_a = (unsigned)(wave * W::A_DMA * 1024);
@@ -1491,185 +1354,6 @@ __global__ void __launch_bounds__(256) w16_kernel(Problem p, int tiles_m, int ti
   }
 }
 
-// ---- one wave per SIMD, 128x128 wave tiles -----------------------------
-// For large products whose K is a whole number of k steps: a 256x256 tile
-// over 4 waves (2 x 2), each computing a 128x128 sub-tile as 8 x 8 blocks
-// of v_mfma_f32_16x16x4_f32.  The 64 accumulator chains (256 registers per
-// lane) live in the accumulation registers; per 32-deep k step a wave
-// issues 512 MFMAs (16384 matrix-pipe cycles) against 16 direct loads,
-// 16 A and 64 B fragment reads and one barrier, so the non-matrix work of
-// a step is small and one barrier per step is cheap among 4 waves.  Two
-// LDS stages: the loads of step i + 1 are issued during step i, into the
-// stage step i - 1 used.  The k loop has no branch: the stage alternates
-// by parity, the step after a tile's last is the next tile's first, and
-// the workgroup's very last step reloads its own tile's first operands
-// into the idle stage.  LDS layouts and the per-element k order are those
-// of w16_kernel.
-template <class W>
-__global__ void __launch_bounds__(256) big16_kernel(Problem p, int tiles_m, int tiles_n) {
-  using T = typename W::Staging;
-  static_assert(W::STAGES == 2, "two stages");
-  __shared__ __attribute__((aligned(16))) float lds[2 * W::STAGE];
-  const unsigned lds_u = (unsigned)(uintptr_t)(lds_void_t *)lds;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
-  const int ntiles = tiles_m * tiles_n;
-  const int nk = p.K / W::BK;
-  const int G = gridDim.x;
-  const int lid = xcd_remap(blockIdx.x, G);
-  if (lid >= ntiles) return;  // uniform per workgroup
-  const int my_tiles = (ntiles - lid + G - 1) / G;
-
-  // Per-lane byte offsets of this wave's direct loads from a step's base
-  // addresses (chunks permuted as in the LDS layouts).
-  unsigned voff[W::DMA];
-#pragma unroll
-  for (int q = 0; q < W::A_DMA; ++q) {
-    const int blk = wave * W::A_DMA + q;
-    const int r = W::ARPI * blk + lane / W::ACH;
-    const int c = (lane % W::ACH) ^ w16_a_perm<W::ACH>(r);
-    voff[q] = (unsigned)(((long long)r * p.lda + 4 * c) * 4);
-  }
-#pragma unroll
-  for (int q = 0; q < W::B_DMA; ++q) {
-    const int blk = wave * W::B_DMA + q;
-    const int k = W::BRPI * blk + lane / W::BCH;
-    const int c = (lane % W::BCH) ^ (4 * ((k >> 2) & 3));
-    voff[W::A_DMA + q] = (unsigned)(((long long)k * p.ldb + 4 * c) * 4);
-  }
-  const unsigned wave_a = (unsigned)(wave * W::A_DMA * 1024);
-  const unsigned wave_b = (unsigned)(W::A_FLOATS * 4 + wave * W::B_DMA * 1024);
-  const long long b_step = (long long)W::BK * p.ldb;
-
-  auto tile_base = [&](int t, const float *&ab, const float *&bb) __attribute__((always_inline)) {
-    int m0, n0;
-    bool interior;
-    tile_origin<T>(lid + t * G, tiles_m, tiles_n, m0, n0, interior, p);
-    ab = p.A + (long long)m0 * p.lda;
-    bb = p.B + n0;
-  };
-  auto issue = [&](unsigned st, const float *ab, const float *bb, int q0, int q1)
-      __attribute__((always_inline)) {
-#pragma unroll
-    for (int q = 0; q < W::DMA; ++q) {
-      if (q < q0 || q >= q1) continue;
-      if (q < W::A_DMA)
-        ks_load_to_lds16(voff[q], ab, st + wave_a + q * 1024);
-      else
-        ks_load_to_lds16(voff[q], bb, st + wave_b + (q - W::A_DMA) * 1024);
-    }
-  };
-
-  const float *is_a, *is_b;  // operands of the step most recently issued
-  tile_base(0, is_a, is_b);
-  issue(lds_u, is_a, is_b, 0, W::DMA);
-  int stage = 0;
-
-  f32x4 acc[W::TBM][W::TBN];
-  for (int t = 0; t < my_tiles; ++t) {
-    const float *nt_a, *nt_b;  // the next tile's first step (this tile's on the last)
-    tile_base(t + 1 < my_tiles ? t + 1 : t, nt_a, nt_b);
-#pragma unroll
-    for (int i = 0; i < W::TBM; ++i)
-#pragma unroll
-      for (int j = 0; j < W::TBN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int kk = 0; kk < nk; ++kk) {
-      const bool last = kk + 1 == nk;
-      const float *ia = last ? nt_a : is_a + W::BK;
-      const float *ib = last ? nt_b : is_b + b_step;
-      __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(0));  // this step's loads (own)
-      ks_lds_barrier();                                // everyone's; stage stage^1 free
-      const float *st = lds + stage * W::STAGE;
-      const unsigned nst = lds_u + (stage ^ 1) * W::STAGE * 4;
-
-      // Fragments: A one chunk ahead, B one MFMA group ahead.  After the
-      // barrier, group 0's operands are read in the order its MFMAs use
-      // them (B, then A row block by row block), so the first MFMAs wait
-      // for two reads rather than for the whole group's.  Inside a group,
-      // the next group's reads are issued after its first half, and the
-      // next step's 16 direct loads one after every other row of 8 MFMAs
-      // over the first two groups.  sched_barrier pins these positions.
-      f32x4 a0[W::TBM], a1[W::TBM];
-      float b0[W::TBN], b1[W::TBN];
-      w16_read_b<W>(b0, st, 0, 0, lane, wn);
-      __builtin_amdgcn_sched_barrier(0);
-      {
-        const int l16 = lane & 15, g = lane >> 4;
-#pragma unroll
-        for (int bm = 0; bm < W::TBM; ++bm) {
-          a0[bm] = *reinterpret_cast<const f32x4 *>(
-              st + 4 * w16_a_pos<W::ACH>(wm * W::WTM + 16 * bm + l16, g));
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < W::NQ; ++h) {
-        f32x4(&ac)[W::TBM] = (h & 1) ? a1 : a0;
-        f32x4(&an)[W::TBM] = (h & 1) ? a0 : a1;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int grp = 4 * h + u;
-          float(&bc)[W::TBN] = (grp & 1) ? b1 : b0;
-          float(&bnx)[W::TBN] = (grp & 1) ? b0 : b1;
-#pragma unroll
-          for (int bm = 0; bm < W::TBM; ++bm) {
-#pragma unroll
-            for (int bn = 0; bn < W::TBN; ++bn)
-              acc[bm][bn] =
-                  __builtin_amdgcn_mfma_f32_16x16x4f32(bc[bn], ac[bm][u], acc[bm][bn], 0, 0, 0);
-            constexpr int kRowsPerLoad = 2;
-            const int row = grp * W::TBM + bm;
-            if (row % kRowsPerLoad == 0 && row / kRowsPerLoad < W::DMA) {
-              __builtin_amdgcn_sched_barrier(0);
-              issue(nst, ia, ib, row / kRowsPerLoad, row / kRowsPerLoad + 1);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-            if (bm == W::TBM / 2 - 1) {
-              __builtin_amdgcn_sched_barrier(0);
-              if (u < 3)
-                w16_read_b<W>(bnx, st, h, u + 1, lane, wn);
-              else if (h + 1 < W::NQ)
-                w16_read_b<W>(bnx, st, h + 1, 0, lane, wn);
-              if (u == 1 && h + 1 < W::NQ) w16_read_a<W>(an, st, h + 1, lane, wm);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-          }
-        }
-      }
-      is_a = ia;
-      is_b = ib;
-      stage ^= 1;
-      // Hand every accumulator to the next step in an accumulation
-      // register (an empty asm with an "a" operand): without it the
-      // register allocator keeps part of the 256 in ordinary VGPRs across
-      // the loop and copies them to and from the accumulation registers
-      // around the MFMAs every step.
-#pragma unroll
-      for (int i = 0; i < W::TBM; ++i)
-#pragma unroll
-        for (int j = 0; j < W::TBN; ++j) asm volatile("" : "+a"(acc[i][j]));
-    }
-
-    int m0, n0;
-    bool interior;
-    tile_origin<T>(lid + t * G, tiles_m, tiles_n, m0, n0, interior, p);
-    const int l16 = lane & 15, g = lane >> 4;
-#pragma unroll
-    for (int bm = 0; bm < W::TBM; ++bm) {
-      float *crow = p.C + (long long)(m0 + wm * W::WTM + 16 * bm + l16) * p.ldc + n0 +
-                    wn * W::WTN + 4 * g;
-#pragma unroll
-      for (int bn = 0; bn < W::TBN; ++bn)
-        *reinterpret_cast<f32x4u *>(crow + 16 * bn) = acc[bm][bn];
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(0));  // the redundant last reload
-}
-
 // ---- the same tiles with operands staged through registers --------------
 // For products whose rows are not 16-byte aligned or whose K is not a whole
 // number of k steps (direct loads need both): big16_kernel's tile, waves,
@@ -1688,7 +1372,7 @@ __global__ void __launch_bounds__(256) big16_kernel(Problem p, int tiles_m, int 
 // order as in big16_kernel (the zeroed tail adds exact zeros).
 template <class W>
 __global__ void __launch_bounds__(256) big16r_kernel(Problem p, int tiles_m, int tiles_n) {
-  using T = typename W::Staging;
+  using T = W16Staging<W>;
   static_assert(W::STAGES == 2, "two stages");
   __shared__ __attribute__((aligned(16))) float lds[2 * W::STAGE];
 
@@ -2514,35 +2198,10 @@ const Entry kEntries[] = {
     {{256, 256, 32, 2, 2, 1, "256x256x32_w2x2_ldsdma_mfma16"}, kKsplit},
     {{256, 256, 32, 2, 2, 1, "256x256x32_w2x2_regs_mfma16"}, kKsplit},
     {{256, 128, 64, 2, 2, 1, "panel256x128_k64_arow_mfma16"}, kPanel},
+    {{192, 192, 32, 2, 2, 1, "192x192x32_w2x2_ldsdma_mfma16"}, kKsplit},
 };
 constexpr int kNumConfigs = sizeof(kEntries) / sizeof(kEntries[0]);
 constexpr int kRemainderConfig = 3;  // thin edge strips
-
-// Workgroups of a kernel resident on the whole device at once (cached per
-// kernel and device; computed on first use).
-constexpr int kMaxDevices = 64;
-
-template <auto KERNEL, int NT>
-int resident_workgroups() {
-  static std::atomic<int> cache[kMaxDevices];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
-  if (dev >= 0) {
-    const int c = cache[dev].load(std::memory_order_relaxed);
-    if (c > 0) return c;
-  }
-  int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, KERNEL, NT, 0) != hipSuccess ||
-      per_cu < 1)
-    per_cu = 1;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) !=
-          hipSuccess ||
-      cus < 1)
-    cus = 1;
-  const int total = per_cu * cus;
-  if (dev >= 0) cache[dev].store(total, std::memory_order_relaxed);
-  return total;
-}
 
 template <class S, void (*KERNEL)(Problem, int, int)>
 hipError_t launch_grid(const Problem &p, hipStream_t s) {
@@ -2602,8 +2261,10 @@ hipError_t launch_w16(const Problem &p, hipStream_t s) {
 // The 128x128-wave kernel with direct loads (big16_kernel) when A and B
 // rows are 16-byte aligned, N % 4 == 0, K is a positive multiple of the k
 // step, C is at least one tile each way and the leading dimensions are below
-// 2^24; otherwise launch_big16r (the same tiles staged through registers).
-template <class W>
+// 2^24; otherwise FALLBACK (for the 256x256 tiles, the same tiles staged
+// through registers).
+using Launcher = hipError_t (*)(const Problem &, hipStream_t);
+template <class W, Launcher FALLBACK>
 hipError_t launch_big16(const Problem &p, hipStream_t s);
 
 // The direct-to-LDS kernel when A and B rows are 16-byte aligned and
@@ -2676,16 +2337,6 @@ hipError_t launch_arow(const Problem &p, hipStream_t s) {
                        (int)chunks, (int)tiles_n);
 }
 
-template <class W, auto KERNEL>
-hipError_t launch_big16_grid(const Problem &p, hipStream_t s) {
-  const long long tiles_m = ceil_div(p.M, W::BM), tiles_n = ceil_div(p.N, W::BN);
-  const long long ntiles = tiles_m * tiles_n;
-  if (ntiles > 0x7fffffffLL) return hipErrorInvalidValue;
-  long long grid = resident_workgroups<KERNEL, 256>();
-  if (grid > ntiles) grid = ntiles;
-  return launch_kernel(KERNEL, dim3((unsigned)grid), dim3(256), s, p, (int)tiles_m, (int)tiles_n);
-}
-
 // 128x128-wave tiles with register staging (big16r_kernel) when C is at
 // least one tile each way and K >= 4; otherwise the register-staged 32x32
 // kernel with the same tiles.
@@ -2695,13 +2346,13 @@ hipError_t launch_big16r(const Problem &p, hipStream_t s) {
   return launch_big16_grid<W, big16r_kernel<W>>(p, s);
 }
 
-template <class W>
+template <class W, Launcher FALLBACK>
 hipError_t launch_big16(const Problem &p, hipStream_t s) {
   const bool direct = (reinterpret_cast<uintptr_t>(p.A) & 15) == 0 &&
                       (reinterpret_cast<uintptr_t>(p.B) & 15) == 0 && (p.lda & 3) == 0 &&
                       (p.ldb & 3) == 0 && (p.N & 3) == 0 && p.M >= W::BM && p.N >= W::BN &&
                       p.K > 0 && p.K % W::BK == 0 && p.lda < (1 << 24) && p.ldb < (1 << 24);
-  if (!direct) return launch_big16r<W>(p, s);
+  if (!direct) return FALLBACK(p, s);
   return launch_big16_grid<W, big16_kernel<W>>(p, s);
 }
 
@@ -2746,9 +2397,12 @@ hipError_t launch_one(int index, const Problem &p, hipStream_t s) {
     case 16: return launch_ksplit(p, s);
     case 17: return launch_w16<W16<64, 64, 64, 2>, C0>(p, s);
     case 18: return launch_lds_dma16<C12>(p, s);
-    case 19: return launch_big16<W16<128, 128, 32, 2>>(p, s);
+    case 19: return launch_big16<W16<128, 128, 32, 2>, launch_big16r<W16<128, 128, 32, 2>>>(p, s);
     case 20: return launch_big16r<W16<128, 128, 32, 2>>(p, s);
     case 21: return launch_arow16(p, s);
+    case 22:  // 192x192 direct-load tiles (built apart); else the 256x256 register path
+      return big16_192_fits(p) ? launch_big16_192(p, s)
+                               : launch_big16r<W16<128, 128, 32, 2>>(p, s);
 
     default: return hipErrorInvalidValue;
   }
@@ -2799,8 +2453,9 @@ bool prod_supports(int index, int M, int N, int K) {
 // strips are split off.  Candidates: 256x256x32 on 16x16 MFMAs with
 // 128x128 wave tiles (148 TFLOP/s with direct loads, which need K a
 // multiple of 32 and aligned rows; about 135 staged through registers),
-// 128x128x64 with one wave per SIMD and 16x16 MFMAs (124), and 64x64x64
-// with K split over the waves (95).
+// 192x192x32 on 96x96 wave tiles with direct loads (138, K a multiple of
+// 32), 128x128x64 with one wave per SIMD and 16x16 MFMAs (124), and
+// 64x64x64 with K split over the waves (95).
 int prod_choose(int M, int N, int K) {
   const long long t256x128 = ceil_div(M, 256) * ceil_div(N, 128);
   if (K <= 64 && t256x128 >= 1024) return 21;
@@ -2809,7 +2464,10 @@ int prod_choose(int M, int N, int K) {
     double rate;
   };
   const bool whole_steps = K % 32 == 0;
-  const Cand cands[] = {{19, 256, whole_steps ? 148.0 : 135.0}, {17, 128, 124.0}, {16, 64, 95.0}};
+  const Cand cands[] = {{19, 256, whole_steps ? 148.0 : 135.0},
+                        {22, 192, whole_steps ? 138.0 : 0.0},
+                        {17, 128, 124.0},
+                        {16, 64, 95.0}};
   constexpr long long kSlots = 256;  // CUs of an MI355X, one workgroup each
   int best = 16;
   double best_score = -1.0;

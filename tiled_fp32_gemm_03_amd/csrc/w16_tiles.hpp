@@ -1,0 +1,383 @@
+// Shared pieces of the 16x16-MFMA kernels with direct-to-LDS operand loads
+// (gfx950): the W16 tile family, its LDS layouts and fragment readers, the
+// inline-assembly direct load and the barrier they use, and the 128x128-wave
+// kernel template (big16_kernel), which is instantiated in more than one
+// translation unit because its best register form differs with the wave
+// tile.  Everything here has internal linkage.
+#pragma once
+
+#include "gemm_internal.hpp"
+#include "launch_util.hpp"
+#include "tile_order.hpp"
+
+#include <atomic>
+#include <cstdint>
+
+namespace gemm_f32_impl {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
+
+constexpr int kLdsBytes = 160 * 1024;  // LDS of one gfx950 CU
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void global_void_t;
+
+// Tile t's origin.  A last tile row or column that would overhang C is
+// moved back to end at C's edge (when C is at least one tile wide): it then
+// overlaps its neighbour, and both compute the shared elements with the same
+// k order, so they store identical values -- while the tile needs no guarded
+// loads.  Only a product narrower than one tile keeps guarded edges.
+template <class S>
+__device__ inline void tile_origin(int t, int tiles_m, int tiles_n, int &m0,
+                                   int &n0, bool &interior, const Problem &p) {
+  int tm, tn;
+  tile_coords(t, tiles_m, tiles_n, tm, tn);
+  m0 = tm * S::BM;
+  n0 = tn * S::BN;
+  if (m0 + S::BM > p.M && p.M >= S::BM) m0 = p.M - S::BM;
+  if (n0 + S::BN > p.N && p.N >= S::BN) n0 = p.N - S::BN;
+  interior = (m0 + S::BM <= p.M) && (n0 + S::BN <= p.N);
+}
+
+// s_waitcnt immediate that waits until at most `n` vector-memory operations
+// of this wave are outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt and lgkmcnt left at their "no wait" maxima).
+constexpr int vmcnt_wait_imm(int n) {
+  return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+}
+
+// The direct loads of this kernel are issued from inline assembly, with an
+// SGPR base address, a per-lane 32-bit byte offset and the wave's LDS
+// destination in M0, so that the compiler does not see them as LDS writes:
+// it would otherwise wait for every outstanding one (vmcnt(0)) before each
+// later LDS read, which would serialise the pipeline.  The kernel orders
+// them itself: explicit vmcnt waits before each barrier, and every LDS read
+// of a stage happens after the barrier that follows its loads.
+__device__ inline void ks_load_to_lds16(unsigned voff, const float *sbase, unsigned lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+// Waits until this wave's LDS operations have completed (as a builtin, so
+// the compiler knows the fragment registers are ready), then the workgroup
+// barrier.  Unlike __syncthreads() it does not wait for outstanding
+// vector-memory loads, so direct loads of later steps stay in flight; the
+// memory clobber keeps the compiler from moving memory accesses across it.
+constexpr int kLgkmWait0 = 0xF | (0x3 << 14) | (0x7 << 4);  // lgkmcnt(0) only
+
+__device__ inline void ks_lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(kLgkmWait0);
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// ---- one wave per SIMD, 16x16x4 MFMAs, direct-load pipeline -----------
+// The large-product form of the K-split kernel's recipe: a BM x BN tile
+// (BM = 2 WTM, BN = 2 WTN) over 4 waves, each computing a WTM x WTN sub-tile
+// as 16x16 blocks with v_mfma_f32_16x16x4_f32 -- (WTM/16)(WTN/16)
+// independent accumulator chains, so a lone wave keeps the matrix pipe busy.
+// Operands arrive by direct loads (ks_load_to_lds16)
+// into STAGES LDS stages of BK-deep k steps: the loads of step
+// i + STAGES - 1 are issued during step i, into the stage that step i - 1
+// used.  Inside a step the fragments are read 16 k at a time, one chunk
+// ahead of the MFMAs.  Within a 16-deep chunk h, MFMA t takes
+// k = 16 h + 4 g + t for lane group g = l / 16.  LDS layouts (16-byte
+// chunks): A rows of BK floats, chunk c of row r at c ^ ((r >> 1) & 7) for
+// BK = 32 and at c ^ (r & 15) for BK = 64; B rows of BN floats,
+// chunk c of k row k at c ^ (4 ((k >> 2) & 3)).  Each element is summed in
+// one fp32 accumulator in ascending k steps, but the k order inside a step
+// differs from the 32x32-MFMA kernels, so the bits may differ from theirs.
+template <int WTM_, int WTN_, int BK_, int STAGES_>
+struct W16 {
+  static constexpr int WTM = WTM_, WTN = WTN_, BK = BK_, STAGES = STAGES_;
+  static constexpr int BM = 2 * WTM, BN = 2 * WTN;
+  static constexpr int TBM = WTM / 16, TBN = WTN / 16;
+  static constexpr int NQ = BK / 16;      // 16-deep chunks per step
+  static constexpr int ACH = BK / 4;      // 16-byte chunks per A row
+  static constexpr int ARPI = 64 / ACH;   // A rows per 1 KB instruction
+  static constexpr int BCH = BN / 4;      // 16-byte chunks per B row
+  // B: instruction q of the step fills LDS chunks 64 q .. 64 q + 63 in k-row
+  // order (BCH chunks per row), so it may span parts of several rows.
+  static constexpr int A_FLOATS = BM * BK, B_FLOATS = BK * BN, STAGE = A_FLOATS + B_FLOATS;
+  static constexpr int A_DMA = A_FLOATS / 256 / 4;  // instructions per wave and step
+  static constexpr int B_DMA = B_FLOATS / 256 / 4;
+  static constexpr int DMA = A_DMA + B_DMA;
+  static_assert(BK == 32 || BK == 64, "A rows of 32 or 64 floats");
+  static_assert(BCH % 16 == 0, "B rows of whole 16-chunk groups (the permutation stays in one)");
+  static_assert(A_FLOATS % 1024 == 0 && B_FLOATS % 1024 == 0, "whole instructions per wave");
+  static_assert(STAGES >= 2 && STAGES * STAGE * 4 <= kLdsBytes, "LDS budget");
+};
+
+// Row permutation of A chunks: 16 consecutive rows land on distinct banks
+// (rows of 128 B pair up in a 256-byte bank window; rows of 256 B fill it).
+template <int ACH>
+__device__ inline int w16_a_perm(int r) {
+  return ACH == 16 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int ACH>
+__device__ inline int w16_a_pos(int r, int c) {
+  return r * ACH + (c ^ w16_a_perm<ACH>(r));
+}
+template <int BCH>
+__device__ inline int w16_b_pos(int k, int c) {
+  return k * BCH + (c ^ (4 * ((k >> 2) & 3)));
+}
+
+// Fragments, per lane (l16 = lane % 16, g = lane / 16): for 16-deep chunk
+// h, A[row l16 of block bm][k = 16 h + 4 g .. + 3] as one 16-byte read,
+// and for MFMA t of the chunk B[k = 16 h + 4 g + t][column l16 of block bn].
+template <class W>
+__device__ inline void w16_read_a(f32x4 (&a)[W::TBM], const float *st, int h, int lane, int wm) {
+  const int l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int bm = 0; bm < W::TBM; ++bm)
+    a[bm] = *reinterpret_cast<const f32x4 *>(
+        st + 4 * w16_a_pos<W::ACH>(wm * W::WTM + 16 * bm + l16, 4 * h + g));
+}
+
+template <class W>
+__device__ inline void w16_read_b(float (&b)[W::TBN], const float *st, int h, int t, int lane,
+                                  int wn) {
+  const int l16 = lane & 15, g = lane >> 4;
+  const int k = 16 * h + 4 * g + t;
+#pragma unroll
+  for (int bn = 0; bn < W::TBN; ++bn) {
+    const int n = wn * W::WTN + 16 * bn + l16;
+    b[bn] = st[W::A_FLOATS + 4 * w16_b_pos<W::BCH>(k, n >> 2) + (n & 3)];
+  }
+}
+
+// MFMA t of a chunk over all blocks of the wave tile, from separately held
+// A (chunk) and B (MFMA t) fragments.
+template <class W>
+__device__ inline void w16_mfma_t(f32x4 (&acc)[W::TBM][W::TBN], const f32x4 (&a)[W::TBM],
+                                  const float (&b)[W::TBN], int t) {
+#pragma unroll
+  for (int bm = 0; bm < W::TBM; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < W::TBN; ++bn)
+      acc[bm][bn] = __builtin_amdgcn_mfma_f32_16x16x4f32(b[bn], a[bm][t], acc[bm][bn], 0, 0, 0);
+}
+
+// Workgroups of a kernel resident on the whole device at once (cached per
+// kernel and device; computed on first use).
+constexpr int kMaxDevices = 64;
+
+template <auto KERNEL, int NT>
+int resident_workgroups() {
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
+  if (dev >= 0) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, KERNEL, NT, 0) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) !=
+          hipSuccess ||
+      cus < 1)
+    cus = 1;
+  const int total = per_cu * cus;
+  if (dev >= 0) cache[dev].store(total, std::memory_order_relaxed);
+  return total;
+}
+
+// ---- one wave per SIMD, 128x128 wave tiles -----------------------------
+// For large products whose K is a whole number of k steps: a 256x256 tile
+// over 4 waves (2 x 2), each computing a 128x128 sub-tile as 8 x 8 blocks
+// of v_mfma_f32_16x16x4_f32.  The 64 accumulator chains (256 registers per
+// lane) live in the accumulation registers; per 32-deep k step a wave
+// issues 512 MFMAs (16384 matrix-pipe cycles) against 16 direct loads,
+// 16 A and 64 B fragment reads and one barrier, so the non-matrix work of
+// a step is small and one barrier per step is cheap among 4 waves.  Two
+// LDS stages: the loads of step i + 1 are issued during step i, into the
+// stage step i - 1 used.  The k loop has no branch: the stage alternates
+// by parity, the step after a tile's last is the next tile's first, and
+// the workgroup's very last step reloads its own tile's first operands
+// into the idle stage.  LDS layouts and the per-element k order are those
+// of w16_kernel.
+template <class W>
+__global__ void __launch_bounds__(256) big16_kernel(Problem p, int tiles_m, int tiles_n) {
+  static_assert(W::STAGES == 2, "two stages");
+  __shared__ __attribute__((aligned(16))) float lds[2 * W::STAGE];
+  const unsigned lds_u = (unsigned)(uintptr_t)(lds_void_t *)lds;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int ntiles = tiles_m * tiles_n;
+  const int nk = p.K / W::BK;
+  const int G = gridDim.x;
+  const int lid = xcd_remap(blockIdx.x, G);
+  if (lid >= ntiles) return;  // uniform per workgroup
+  const int my_tiles = (ntiles - lid + G - 1) / G;
+
+  // Per-lane byte offsets of this wave's direct loads from a step's base
+  // addresses (chunks permuted as in the LDS layouts).
+  unsigned voff[W::DMA];
+#pragma unroll
+  for (int q = 0; q < W::A_DMA; ++q) {
+    const int blk = wave * W::A_DMA + q;
+    const int r = W::ARPI * blk + lane / W::ACH;
+    const int c = (lane % W::ACH) ^ w16_a_perm<W::ACH>(r);
+    voff[q] = (unsigned)(((long long)r * p.lda + 4 * c) * 4);
+  }
+#pragma unroll
+  for (int q = 0; q < W::B_DMA; ++q) {
+    const int j = 64 * (wave * W::B_DMA + q) + lane;  // LDS chunk this lane fills
+    const int k = j / W::BCH;
+    const int c = (j % W::BCH) ^ (4 * ((k >> 2) & 3));
+    voff[W::A_DMA + q] = (unsigned)(((long long)k * p.ldb + 4 * c) * 4);
+  }
+  const unsigned wave_a = (unsigned)(wave * W::A_DMA * 1024);
+  const unsigned wave_b = (unsigned)(W::A_FLOATS * 4 + wave * W::B_DMA * 1024);
+  const long long b_step = (long long)W::BK * p.ldb;
+
+  auto tile_base = [&](int t, const float *&ab, const float *&bb) __attribute__((always_inline)) {
+    int m0, n0;
+    bool interior;
+    tile_origin<W>(lid + t * G, tiles_m, tiles_n, m0, n0, interior, p);
+    ab = p.A + (long long)m0 * p.lda;
+    bb = p.B + n0;
+  };
+  auto issue = [&](unsigned st, const float *ab, const float *bb, int q0, int q1)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < W::DMA; ++q) {
+      if (q < q0 || q >= q1) continue;
+      if (q < W::A_DMA)
+        ks_load_to_lds16(voff[q], ab, st + wave_a + q * 1024);
+      else
+        ks_load_to_lds16(voff[q], bb, st + wave_b + (q - W::A_DMA) * 1024);
+    }
+  };
+
+  const float *is_a, *is_b;  // operands of the step most recently issued
+  tile_base(0, is_a, is_b);
+  issue(lds_u, is_a, is_b, 0, W::DMA);
+  int stage = 0;
+
+  f32x4 acc[W::TBM][W::TBN];
+  for (int t = 0; t < my_tiles; ++t) {
+    const float *nt_a, *nt_b;  // the next tile's first step (this tile's on the last)
+    tile_base(t + 1 < my_tiles ? t + 1 : t, nt_a, nt_b);
+#pragma unroll
+    for (int i = 0; i < W::TBM; ++i)
+#pragma unroll
+      for (int j = 0; j < W::TBN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int kk = 0; kk < nk; ++kk) {
+      const bool last = kk + 1 == nk;
+      const float *ia = last ? nt_a : is_a + W::BK;
+      const float *ib = last ? nt_b : is_b + b_step;
+      __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(0));  // this step's loads (own)
+      ks_lds_barrier();                                // everyone's; stage stage^1 free
+      const float *st = lds + stage * W::STAGE;
+      const unsigned nst = lds_u + (stage ^ 1) * W::STAGE * 4;
+
+      // Fragments: A one chunk ahead, B one MFMA group ahead.  After the
+      // barrier, group 0's operands are read in the order its MFMAs use
+      // them (B, then A row block by row block), so the first MFMAs wait
+      // for two reads rather than for the whole group's.  Inside a group,
+      // the next group's reads are issued after its first half, and the
+      // next step's 16 direct loads one after every other row of 8 MFMAs
+      // over the first two groups.  sched_barrier pins these positions.
+      f32x4 a0[W::TBM], a1[W::TBM];
+      float b0[W::TBN], b1[W::TBN];
+      w16_read_b<W>(b0, st, 0, 0, lane, wn);
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        const int l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+        for (int bm = 0; bm < W::TBM; ++bm) {
+          a0[bm] = *reinterpret_cast<const f32x4 *>(
+              st + 4 * w16_a_pos<W::ACH>(wm * W::WTM + 16 * bm + l16, g));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < W::NQ; ++h) {
+        f32x4(&ac)[W::TBM] = (h & 1) ? a1 : a0;
+        f32x4(&an)[W::TBM] = (h & 1) ? a0 : a1;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int grp = 4 * h + u;
+          float(&bc)[W::TBN] = (grp & 1) ? b1 : b0;
+          float(&bnx)[W::TBN] = (grp & 1) ? b0 : b1;
+#pragma unroll
+          for (int bm = 0; bm < W::TBM; ++bm) {
+#pragma unroll
+            for (int bn = 0; bn < W::TBN; ++bn)
+              acc[bm][bn] =
+                  __builtin_amdgcn_mfma_f32_16x16x4f32(bc[bn], ac[bm][u], acc[bm][bn], 0, 0, 0);
+            constexpr int kRowsPerLoad = 2;
+            const int row = grp * W::TBM + bm;
+            if (row % kRowsPerLoad == 0 && row / kRowsPerLoad < W::DMA) {
+              __builtin_amdgcn_sched_barrier(0);
+              issue(nst, ia, ib, row / kRowsPerLoad, row / kRowsPerLoad + 1);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            if (bm == W::TBM / 2 - 1) {
+              __builtin_amdgcn_sched_barrier(0);
+              if (u < 3)
+                w16_read_b<W>(bnx, st, h, u + 1, lane, wn);
+              else if (h + 1 < W::NQ)
+                w16_read_b<W>(bnx, st, h + 1, 0, lane, wn);
+              if (u == 1 && h + 1 < W::NQ) w16_read_a<W>(an, st, h + 1, lane, wm);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+        }
+      }
+      is_a = ia;
+      is_b = ib;
+      stage ^= 1;
+      // With 256 accumulators per lane, hand every one to the next step in
+      // an accumulation register (an empty asm with an "a" operand):
+      // without it the register allocator keeps part of them in ordinary
+      // VGPRs across the loop and copies them to and from the accumulation
+      // registers around the MFMAs every step.  (Smaller wave tiles are
+      // built with the MFMAs' VGPR form, where no such copies arise.)
+      if constexpr (W::TBM * W::TBN * 4 == 256) {
+#pragma unroll
+        for (int i = 0; i < W::TBM; ++i)
+#pragma unroll
+          for (int j = 0; j < W::TBN; ++j) asm volatile("" : "+a"(acc[i][j]));
+      }
+    }
+
+    int m0, n0;
+    bool interior;
+    tile_origin<W>(lid + t * G, tiles_m, tiles_n, m0, n0, interior, p);
+    const int l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int bm = 0; bm < W::TBM; ++bm) {
+      float *crow = p.C + (long long)(m0 + wm * W::WTM + 16 * bm + l16) * p.ldc + n0 +
+                    wn * W::WTN + 4 * g;
+#pragma unroll
+      for (int bn = 0; bn < W::TBN; ++bn)
+        *reinterpret_cast<f32x4u *>(crow + 16 * bn) = acc[bm][bn];
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(0));  // the redundant last reload
+}
+
+template <class W, auto KERNEL>
+hipError_t launch_big16_grid(const Problem &p, hipStream_t s) {
+  const long long tiles_m = ceil_div(p.M, W::BM), tiles_n = ceil_div(p.N, W::BN);
+  const long long ntiles = tiles_m * tiles_n;
+  if (ntiles > 0x7fffffffLL) return hipErrorInvalidValue;
+  long long grid = resident_workgroups<KERNEL, 256>();
+  if (grid > ntiles) grid = ntiles;
+  return launch_kernel(KERNEL, dim3((unsigned)grid), dim3(256), s, p, (int)tiles_m, (int)tiles_n);
+}
+
+}  // namespace
+}  // namespace gemm_f32_impl
