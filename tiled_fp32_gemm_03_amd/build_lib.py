@@ -20,12 +20,12 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgemm_f32.so")
 ARCH = "gfx950"
 
-SOURCES = ["gemm_f32_abi.hip", "naive_tiled.hip", "prod.hip", "big192.hip", "valu.hip", "mixed.hip",
+SOURCES = ["gemm_f32_abi.hip", "naive_tiled.hip", "prod.hip", "w16_vgpr.hip", "valu.hip", "mixed.hip",
            "probes.hip"]
 
-# Per-source flags: the 192x192 kernel keeps its accumulators in VGPRs (the
-# MFMAs' VGPR form); see big192.hip.
-SOURCE_FLAGS = {"big192.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source flags: the kernels of w16_vgpr.hip keep their accumulators in
+# VGPRs (the MFMAs' VGPR form); see that file.
+SOURCE_FLAGS = {"w16_vgpr.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

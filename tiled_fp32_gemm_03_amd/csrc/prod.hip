@@ -2199,6 +2199,7 @@ const Entry kEntries[] = {
     {{256, 256, 32, 2, 2, 1, "256x256x32_w2x2_regs_mfma16"}, kKsplit},
     {{256, 128, 64, 2, 2, 1, "panel256x128_k64_arow_mfma16"}, kPanel},
     {{192, 192, 32, 2, 2, 1, "192x192x32_w2x2_ldsdma_mfma16"}, kKsplit},
+    {{128, 128, 32, 2, 2, 2, "128x128x32_w2x2_ldsdma_mfma16"}, kKsplit},
 };
 constexpr int kNumConfigs = sizeof(kEntries) / sizeof(kEntries[0]);
 constexpr int kRemainderConfig = 3;  // thin edge strips
@@ -2403,6 +2404,8 @@ hipError_t launch_one(int index, const Problem &p, hipStream_t s) {
     case 22:  // 192x192 direct-load tiles (built apart); else the 256x256 register path
       return big16_192_fits(p) ? launch_big16_192(p, s)
                                : launch_big16r<W16<128, 128, 32, 2>>(p, s);
+    case 23:  // 128x128 direct-load tiles (built apart); else entry 17's launcher
+      return big16_128_fits(p) ? launch_big16_128(p, s) : launch_w16<W16<64, 64, 64, 2>, C0>(p, s);
 
     default: return hipErrorInvalidValue;
   }
@@ -2446,37 +2449,43 @@ bool prod_supports(int index, int M, int N, int K) {
 // the A-resident small-K panel kernel (only B moves per tile; C stores
 // interleaved with the next tile's MFMAs), on 16x16 MFMAs with one wave per
 // SIMD when K == 64 and the rows are aligned (entry 21's launcher falls
-// back to the 32x32 form otherwise).  Otherwise the k-loop entry with
-// the best modelled rate: its measured full-occupancy rate times the
-// fraction of workgroup slots its tiles fill over whole rounds (one
-// workgroup per CU, 256 CUs), counting tiles after the thin remainder
-// strips are split off.  Candidates: 256x256x32 on 16x16 MFMAs with
-// 128x128 wave tiles (148 TFLOP/s with direct loads, which need K a
-// multiple of 32 and aligned rows; about 135 staged through registers),
-// 192x192x32 on 96x96 wave tiles with direct loads (138, K a multiple of
-// 32), 128x128x64 with one wave per SIMD and 16x16 MFMAs (124), and
-// 64x64x64 with K split over the waves (95).
+// back to the 32x32 form otherwise).  Otherwise the k-loop entry with the
+// best modelled rate: its measured rate when every CU is busy, times the
+// fraction of the time the CUs are busy on the persistent grid -- G =
+// min(resident workgroups, tiles) workgroups, ceil(G / 256) of them per CU,
+// ceil(tiles / G) tiles each, against tiles / 256 if the work spread
+// evenly -- counting tiles after the thin remainder strips are split off.
+// Candidates (K a multiple of 32 and aligned rows take the direct-load
+// forms): 256x256x32 on 128x128 wave tiles (148 TFLOP/s with direct loads,
+// about 135 staged through registers), 192x192x32 on 96x96 waves (138),
+// 128x128x32 on 64x64 waves, two workgroups per CU (141), 128x128x64 on
+// 64x64 waves with a register path for K tails (124), and 64x64x64 with K
+// split over the waves (95).
 int prod_choose(int M, int N, int K) {
   const long long t256x128 = ceil_div(M, 256) * ceil_div(N, 128);
   if (K <= 64 && t256x128 >= 1024) return 21;
   struct Cand {
     int entry, tile;
     double rate;
+    int slots;  // resident workgroups on 256 CUs
   };
   const bool whole_steps = K % 32 == 0;
-  const Cand cands[] = {{19, 256, whole_steps ? 148.0 : 135.0},
-                        {22, 192, whole_steps ? 138.0 : 0.0},
-                        {17, 128, 124.0},
-                        {16, 64, 95.0}};
-  constexpr long long kSlots = 256;  // CUs of an MI355X, one workgroup each
+  const Cand cands[] = {{19, 256, whole_steps ? 148.0 : 135.0, 256},
+                        {22, 192, whole_steps ? 138.0 : 0.0, 256},
+                        {23, 128, whole_steps ? 141.0 : 0.0, 512},
+                        {17, 128, 124.0, 256},
+                        {16, 64, 95.0, 256}};
+  constexpr long long kCus = 256;  // CUs of an MI355X
   int best = 16;
   double best_score = -1.0;
   for (const Cand &c : cands) {
     const long long tm = ceil_div(M - thin_remainder(M, c.tile), c.tile);
     const long long tn = ceil_div(N - thin_remainder(N, c.tile), c.tile);
     const long long tiles = tm * tn;
-    const long long rounds = ceil_div(tiles, kSlots);
-    const double score = rounds > 0 ? c.rate * (double)tiles / (double)(rounds * kSlots) : 0.0;
+    if (tiles <= 0) continue;
+    const long long grid = tiles < c.slots ? tiles : c.slots;
+    const long long busy = ceil_div(grid, kCus) * ceil_div(tiles, grid);  // tile times per CU
+    const double score = c.rate * (double)tiles / (double)(busy * kCus);
     if (score > best_score) {
       best_score = score;
       best = c.entry;

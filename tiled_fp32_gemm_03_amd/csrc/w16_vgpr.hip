@@ -1,0 +1,50 @@
+// Members of the 16x16-MFMA direct-load kernel family (big16_kernel) whose
+// accumulators fit in VGPRs beside their fragments:
+//   192x192 tiles on 96x96 waves, 32-deep steps (144 accumulators per lane),
+//     for products whose tile count leaves 256x256 tiles a partial last
+//     round (3072^3 is exactly one round of 192x192 tiles, 6144^3 four);
+//   128x128 tiles on 64x64 waves, 32-deep steps (64 accumulators, 64 KB of
+//     LDS, two workgroups per CU), for mid-size products.
+//
+// This translation unit is built with the MFMAs in their VGPR form
+// (-mllvm -amdgpu-mfma-vgpr-form=1, for this file only): with fewer than
+// 256 accumulators per lane the accumulation-register form lets the
+// register allocator move accumulators between the register files every
+// step.  The 256x256 members (256 accumulators) stay in prod.hip in the
+// accumulation-register form.
+#include "w16_tiles.hpp"
+
+namespace gemm_f32_impl {
+namespace {
+
+using W192 = W16<96, 96, 32, 2>;
+using W128 = W16<64, 64, 32, 2>;
+
+// Direct loads need 16-byte aligned rows of A and B and N % 4 == 0; the
+// kernel needs C at least one tile each way, K a positive multiple of the
+// step and leading dimensions below 2^24 (32-bit lane offsets).
+template <class W>
+bool direct_fits(const Problem &p) {
+  return (reinterpret_cast<uintptr_t>(p.A) & 15) == 0 &&
+         (reinterpret_cast<uintptr_t>(p.B) & 15) == 0 && (p.lda & 3) == 0 && (p.ldb & 3) == 0 &&
+         (p.N & 3) == 0 && p.M >= W::BM && p.N >= W::BN && p.K > 0 && p.K % W::BK == 0 &&
+         p.lda < (1 << 24) && p.ldb < (1 << 24);
+}
+
+}  // namespace
+
+bool big16_192_fits(const Problem &p) { return direct_fits<W192>(p); }
+
+hipError_t launch_big16_192(const Problem &p, hipStream_t s) {
+  if (!direct_fits<W192>(p)) return hipErrorInvalidValue;
+  return launch_big16_grid<W192, big16_kernel<W192>>(p, s);
+}
+
+bool big16_128_fits(const Problem &p) { return direct_fits<W128>(p); }
+
+hipError_t launch_big16_128(const Problem &p, hipStream_t s) {
+  if (!direct_fits<W128>(p)) return hipErrorInvalidValue;
+  return launch_big16_grid<W128, big16_kernel<W128>>(p, s);
+}
+
+}  // namespace gemm_f32_impl
