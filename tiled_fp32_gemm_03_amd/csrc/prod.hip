@@ -2460,7 +2460,8 @@ bool prod_supports(int index, int M, int N, int K) {
 // about 135 staged through registers), 192x192x32 on 96x96 waves (138),
 // 128x128x32 on 64x64 waves, two workgroups per CU (141), 128x128x64 on
 // 64x64 waves with a register path for K tails (124), and 64x64x64 with K
-// split over the waves (95).
+// split over the waves (108 at 24 steps per tile; less for shorter K, where
+// it wins anyway by filling the CUs).
 int prod_choose(int M, int N, int K) {
   const long long t256x128 = ceil_div(M, 256) * ceil_div(N, 128);
   if (K <= 64 && t256x128 >= 1024) return 21;
@@ -2474,7 +2475,7 @@ int prod_choose(int M, int N, int K) {
                         {22, 192, whole_steps ? 138.0 : 0.0, 256},
                         {23, 128, whole_steps ? 141.0 : 0.0, 512},
                         {17, 128, 124.0, 256},
-                        {16, 64, 95.0, 256}};
+                        {16, 64, 108.0, 256}};
   constexpr long long kCus = 256;  // CUs of an MI355X
   int best = 16;
   double best_score = -1.0;
