@@ -170,11 +170,43 @@ def test_all_ones_full_ragged_shape(g, fmt):
         assert torch.all(c == float(w.K)).item()
 
 
+DIRECT_ENTRY = 3  # 16x16x32 MFMAs with direct loads: its own summation order
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_direct_entry_many_tiles(g, fmt):
+    """The direct-load entry where workgroups walk two tiles and the last
+    tile row and column are moved back inside C: exact on small integers
+    (sampled elements plus whole edge rows and columns), within the fp32
+    bar on normal inputs (sampled)."""
+    M, N, K = 4400, 4352, 128
+    for dist in ("small_int", "normal"):
+        print(f"case: mixed {fmt} direct entry {M}x{N}x{K} {dist}", flush=True)
+        a, b = make_mixed(M, N, K, dist, seed=M + K, fmt=fmt)
+        c = g.matmul_mixed(_to_dev(a, fmt), _to_dev(b, fmt), config=DIRECT_ENTRY)
+        torch.cuda.synchronize()
+        ii, jj = sample_indices(M, N, 20000, seed=K)
+        got = c[torch.from_numpy(ii).to(_dev()), torch.from_numpy(jj).to(_dev())].cpu().numpy()
+        ref = oracle.gemm_mixed_elems(a, b, fmt, ii, jj)
+        if dist == "small_int":
+            assert np.array_equal(got, ref)
+            rows = np.array([0, 255, 4143, 4144, M - 1])
+            edge_i = np.repeat(rows, N)
+            edge_j = np.tile(np.arange(N), len(rows))
+            got_e = c[torch.from_numpy(edge_i).to(_dev()),
+                      torch.from_numpy(edge_j).to(_dev())].cpu().numpy()
+            assert np.array_equal(got_e, oracle.gemm_mixed_elems(a, b, fmt, edge_i, edge_j))
+        else:
+            tol_check(got, ref, K, f"{fmt} direct entry")
+
+
 @pytest.mark.parametrize("fmt", FORMATS)
 def test_entries_agree_bitwise_on_ragged_floats(g, fmt):
-    """Every entry sums each element in the same k order, whatever the tile
-    size or whether its edge tiles were moved back inside C (overlapping a
-    neighbour), so they agree bit for bit on float inputs."""
+    """Every 32x32x16 entry sums each element in the same k order, whatever
+    the tile size or whether its edge tiles were moved back inside C
+    (overlapping a neighbour), so they agree bit for bit on float inputs.
+    (On these shapes the direct-load entry takes entry 0's kernel: K is not
+    a multiple of its step.)"""
     for (M, N, K) in [(1000, 1003, 515), (700, 300, 129)]:
         a, b = make_mixed(M, N, K, "normal", seed=M + N, fmt=fmt)
         ref = _run(g, a, b, fmt, 0)

@@ -21,7 +21,7 @@ LIB = os.path.join(HERE, "libgemm_f32.so")
 ARCH = "gfx950"
 
 SOURCES = ["gemm_f32_abi.hip", "naive_tiled.hip", "prod.hip", "w16_vgpr.hip", "valu.hip", "mixed.hip",
-           "probes.hip"]
+           "mixed16.hip", "probes.hip"]
 
 # Per-source flags: the kernels of w16_vgpr.hip keep their accumulators in
 # VGPRs (the MFMAs' VGPR form); see that file.

@@ -62,6 +62,13 @@ struct MixedConfig {
   const char *name;
 };
 
+// The 16x16x32-MFMA kernel with direct loads (mixed16.hip): whether it
+// takes the product (16-byte aligned rows of A and B, N % 8 == 0, C at least
+// 256 x 256, K a positive multiple of 64, leading dimensions below 2^24),
+// and its launch.
+bool mixed16_fits(const MixedProblem &p);
+hipError_t launch_mixed16(int format, const MixedProblem &p, hipStream_t s);
+
 int mixed_num_configs();
 const MixedConfig &mixed_config(int index);
 int mixed_choose(int M, int N, int K);

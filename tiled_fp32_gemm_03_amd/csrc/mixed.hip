@@ -277,6 +277,7 @@ const MixedConfig kMixedConfigs[] = {
     {Mixed128::BM, Mixed128::BN, kMixedBK, Mixed128::WGM, Mixed128::WGN, 2, "128x128x64 w2x2"},
     {Mixed256w16::BM, Mixed256w16::BN, kMixedBK, Mixed256w16::WGM, Mixed256w16::WGN, 1,
      "256x256x64 w4x4"},
+    {256, 256, kMixedBK, 2, 2, 1, "256x256x64 w2x2 ldsdma mfma16x16x32"},
 };
 constexpr int kMixedNumConfigs = sizeof(kMixedConfigs) / sizeof(kMixedConfigs[0]);
 
@@ -306,11 +307,15 @@ const MixedConfig &mixed_config(int index) { return kMixedConfigs[index]; }
 // Below four k steps a lone 256 x 256 workgroup per CU cannot hide its
 // loads and stores behind matrix work, so short K takes the 128 x 128 entry
 // (two workgroups per CU overlap each other's epilogues).
+//
+// A 256 x 256 choice becomes entry 3 (direct loads on 16x16x32 MFMAs, one
+// wave per SIMD) when K is a multiple of its 64-deep step; its launcher
+// falls back to entry 0 for rows that are not 16-byte aligned.
 int mixed_choose(int M, int N, int K) {
   if (K < 4 * kMixedBK) return 1;
   int best = 0;
   double best_cost = 0;
-  for (int c = 0; c < kMixedNumConfigs; ++c) {
+  for (int c = 0; c < 3; ++c) {
     const MixedConfig &cfg = kMixedConfigs[c];
     const double tiles = (double)ceil_div(M, cfg.BM) * (double)ceil_div(N, cfg.BN);
     const double slots = 256.0 * cfg.occupancy;
@@ -318,6 +323,7 @@ int mixed_choose(int M, int N, int K) {
     const double cost = rounds * cfg.BM * cfg.BN * cfg.occupancy;
     if (c == 0 || cost < best_cost) best = c, best_cost = cost;
   }
+  if (kMixedConfigs[best].BM == 256 && K % kMixedBK == 0) return 3;
   return best;
 }
 
@@ -328,6 +334,9 @@ hipError_t launch_mixed(int format, int index, const MixedProblem &p, hipStream_
     case 1: return bf ? launch_one<Mixed128, kMixedBf16>(p, s) : launch_one<Mixed128, kMixedF16>(p, s);
     case 2:
       return bf ? launch_one<Mixed256w16, kMixedBf16>(p, s) : launch_one<Mixed256w16, kMixedF16>(p, s);
+    case 3:  // direct loads on 16x16x32 MFMAs where they fit, else entry 0
+      if (mixed16_fits(p)) return launch_mixed16(format, p, s);
+      return bf ? launch_one<Mixed256, kMixedBf16>(p, s) : launch_one<Mixed256, kMixedF16>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
