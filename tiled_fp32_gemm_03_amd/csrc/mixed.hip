@@ -308,10 +308,12 @@ const MixedConfig &mixed_config(int index) { return kMixedConfigs[index]; }
 // loads and stores behind matrix work, so short K takes the 128 x 128 entry
 // (two workgroups per CU overlap each other's epilogues).
 //
-// A 256 x 256 choice becomes entry 3 (direct loads on 16x16x32 MFMAs, one
-// wave per SIMD) when K is a multiple of its 64-deep step; its launcher
-// falls back to entry 0 for rows that are not 16-byte aligned.
+// Entry 3 (direct loads on 16x16x32 MFMAs, one wave per SIMD) takes every
+// product whose K is a multiple of its 64-deep step and whose 256 x 256
+// tiles fill the GPU, and any other 256 x 256 choice with such a K; its
+// launcher falls back to entry 0 for rows that are not 16-byte aligned.
 int mixed_choose(int M, int N, int K) {
+  if (K % kMixedBK == 0 && ceil_div(M, 256) * ceil_div(N, 256) >= 256) return 3;
   if (K < 4 * kMixedBK) return 1;
   int best = 0;
   double best_cost = 0;

@@ -49,6 +49,7 @@ struct M16 {
   static constexpr int BSL = BN / 16;  // 32-byte slots per B row
   static_assert(2 * STAGE <= kLdsBytes, "two stages fit in LDS");
   static_assert(ACH == 8, "the A permutation is written for 8 chunks per row");
+  static_assert(DMA <= 2 * KG * TBM, "two direct loads per row of MFMAs cover a step's");
 };
 
 __device__ inline int m16_a_pos(int r, int c) { return r * M16::ACH + (c ^ ((r >> 1) & 7)); }
@@ -179,7 +180,7 @@ __global__ void __launch_bounds__(256) mixed16_kernel(MixedProblem p, int tiles_
 
       // Group 0's operands in the order its first row of MFMAs uses them,
       // then each group's MFMAs row by row, the next group's fragments read
-      // after the first half, one direct load of the next step per row.
+      // after the first half, two direct loads of the next step per row.
       i16x8 a0[W::TBM], a1[W::TBM], b0[W::TBN], b1[W::TBN];
       b0[0] = m16_read_b(st, wn, 0, 0, lane);
       __builtin_amdgcn_sched_barrier(0);
@@ -204,10 +205,11 @@ __global__ void __launch_bounds__(256) mixed16_kernel(MixedProblem p, int tiles_
 #pragma unroll
           for (int bn = 0; bn < W::TBN; ++bn)
             acc[bm][bn] = mfma32<FMT>(bc[bn], ac[bm], acc[bm][bn]);
+          constexpr int kLoadsPerRow = 2;
           const int row = kg * W::TBM + bm;
-          if (row < W::DMA) {
+          if (row * kLoadsPerRow < W::DMA) {
             __builtin_amdgcn_sched_barrier(0);
-            issue(nst, ia, ib, row, row + 1);
+            issue(nst, ia, ib, row * kLoadsPerRow, (row + 1) * kLoadsPerRow);
             __builtin_amdgcn_sched_barrier(0);
           }
           if (kg + 1 < W::KG && bm == W::TBM / 2 - 1) {
@@ -220,10 +222,6 @@ __global__ void __launch_bounds__(256) mixed16_kernel(MixedProblem p, int tiles_
           }
         }
       }
-      // the remaining direct loads of the next step
-      __builtin_amdgcn_sched_barrier(0);
-      issue(nst, ia, ib, W::KG * W::TBM, W::DMA);
-      __builtin_amdgcn_sched_barrier(0);
       is_a = ia;
       is_b = ib;
       stage ^= 1;
