@@ -50,9 +50,13 @@ extern "C" {
  *   config    -1 picks a launch-table entry for the shape, otherwise an
  *             index below gemm_mixed_num_configs() (else GEMM_F32_BAD_CONFIG).
  * Returns GEMM_F32_OK or an error code of gemm_f32.h; on error nothing is
- * launched.  Kernel: BM x BN workgroup tiles with k step 64, both operands
- * staged in LDS as rows of 64 k values (B transposed on the way in), two LDS
- * stages, v_mfma_f32_32x32x16_bf16 / _f16 on 32 x 32 blocks per wave.
+ * launched.  Kernels: entries 0-2 use BM x BN workgroup tiles with k step
+ * 64, both operands staged in LDS as rows of 64 k values (B transposed on
+ * the way in), two LDS stages, v_mfma_f32_32x32x16_bf16 / _f16 on 32 x 32
+ * blocks per wave; entry 3 loads both operands straight into LDS in their
+ * row-major layouts (16-byte aligned rows of A and B, N % 8 == 0 and K a
+ * multiple of 64; otherwise it runs entry 0), reads B's operands with the
+ * transposing LDS read and computes on v_mfma_f32_16x16x32_bf16 / _f16.
  */
 int gemm_mixed(int M, int N, int K, const void *A, int lda, const void *B,
                int ldb, float *C, int ldc, int format, int config,
