@@ -54,7 +54,11 @@ constexpr int vmcnt_wait_imm(int n) {
 // it would otherwise wait for every outstanding one (vmcnt(0)) before each
 // later LDS read, which would serialise the pipeline.  The kernel orders
 // them itself: explicit vmcnt waits before each barrier, and every LDS read
-// of a stage happens after the barrier that follows its loads.
+// of a stage happens after the barrier that follows its loads.  M0 is named
+// as clobbered; the compiler warns that it reserves M0 for itself, and in
+// the kernels that use this load nothing else sets or reads M0 (the
+// generated code touches M0 only in these sequences), so no value of the
+// compiler's is lost.
 __device__ inline void ks_load_to_lds16(unsigned voff, const float *sbase, unsigned lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
