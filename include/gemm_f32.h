@@ -134,13 +134,14 @@ int gemm_f32_ex(int M, int N, int K, const float *A, int lda, const float *B,
  * from gemm_f32, so on non-integer inputs the two differ by rounding.
  *
  * gemm_f32_splitk_plan -- the plan gemm_f32_splitk would use (host only).
- *   config  -1 = automatic (128x128x32 tiles, 64x64 for outputs below
- *           128x128), or a production k-loop entry (small-K panel and
+ *   config  -1 = automatic (entry 23's 128x128x32 tiles, 64x64 for outputs
+ *           below 128x128), or a production k-loop entry (small-K panel and
  *           non-temporal-store entries are refused with GEMM_F32_BAD_CONFIG).
- *   splits  0 = automatic (one workgroup per CU where K allows at least four
- *           k steps per chunk; products with a tile per CU, or with fewer
- *           than 32 k steps, are not split),
- *           else the requested count, capped at one k step per chunk.
+ *   splits  0 = automatic: the count with the least modelled time, from the
+ *           busiest CU's share of (tile, chunk) pairs and the slab traffic,
+ *           with at least four k steps per chunk; products with more than
+ *           half a tile per CU, or with fewer than 32 k steps, are not split.
+ *           Else the requested count, capped at one k step per chunk.
  *   Writes the entry, the chunks actually used (1 means a plain product;
  *   with config -1 it then runs the entry gemm_f32 would choose),
  *   kc, and the workspace bytes needed (splits * M * N * 4, or 0 for one

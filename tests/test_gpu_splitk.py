@@ -40,6 +40,10 @@ CASES = [  # (M, N, K, config, splits)
     (257, 383, 129, 0, 5), (128, 128, 4096, 0, 16), (65, 70, 1001, 3, 0), (1, 300, 700, -1, 4),
     (200, 1, 333, -1, 3), (512, 512, 40, 0, 2), (777, 555, 2049, 4, 0), (130, 129, 31, 0, 4),
     (512, 384, 2048, 2, 4), (600, 520, 1536, 12, 3), (300, 300, 1000, 7, 2),
+    # entry 23: the direct-load kernel per chunk, ragged tiles and a short last
+    # chunk; K = 1000 is no multiple of its k step and takes entry 0's kernel
+    (512, 512, 8192, 23, 16), (300, 260, 992, 23, 3), (128, 128, 4096, 23, 16),
+    (1024, 640, 4096, 23, 4), (260, 300, 1000, 23, 3),
 ]
 
 

@@ -83,6 +83,13 @@ bool big16_192_fits(const Problem &p);
 hipError_t launch_big16_192(const Problem &p, hipStream_t s);
 bool big16_128_fits(const Problem &p);
 hipError_t launch_big16_128(const Problem &p, hipStream_t s);
+// Split-K form of the 128x128 kernel: grid row y computes k in
+// [y kc, (y + 1) kc) into slab y of ws (M x N, row pitch N); kc must be a
+// multiple of 32 and the product must fit as above.  The slabs are summed
+// by the caller.
+bool big16_128_split_fits(const Problem &p, int kc);
+hipError_t launch_big16_128_split(const Problem &p, int splits, int kc, float *ws,
+                                  hipStream_t s);
 
 int prod_num_configs();
 const ProdConfig &prod_config(int index);

@@ -2290,6 +2290,8 @@ hipError_t launch_lds_dma(const Problem &p, hipStream_t s) {
 
 // Split-K launch: every (tile, split) pair is one workgroup (grid y = the
 // split), then the reduction over the slabs into C.
+hipError_t launch_splitk_reduce(const Problem &p, int splits, const float *ws, hipStream_t s);
+
 template <class S>
 hipError_t launch_split(const Problem &p, int splits, int kc, float *ws, hipStream_t s) {
   const long long tiles_m = ceil_div(p.M, S::BM), tiles_n = ceil_div(p.N, S::BN);
@@ -2298,6 +2300,11 @@ hipError_t launch_split(const Problem &p, int splits, int kc, float *ws, hipStre
   hipError_t e = launch_kernel(prod_split_kernel<S>, dim3((unsigned)ntiles, (unsigned)splits),
                                dim3(S::NT), s, p, (int)tiles_m, (int)tiles_n, kc, ws);
   if (e != hipSuccess) return e;
+  return launch_splitk_reduce(p, splits, ws, s);
+}
+
+// The slab sum into C, after the partial products.
+hipError_t launch_splitk_reduce(const Problem &p, int splits, const float *ws, hipStream_t s) {
   const long long quads = (long long)p.M * ((p.N + 3) / 4);
   long long blocks = ceil_div(quads, kReduceThreads);
   if (blocks > 4096) blocks = 4096;
@@ -2421,6 +2428,11 @@ hipError_t launch_split_one(int index, const Problem &p, int splits, int kc, flo
     case 4: return launch_split<C4>(p, splits, kc, ws, s);
     case 7: return launch_split<C7>(p, splits, kc, ws, s);
     case 12: return launch_split<C12>(p, splits, kc, ws, s);
+    case 23: {  // the VGPR-form 128x128 kernel where it fits, else entry 0's kernel
+      if (!big16_128_split_fits(p, kc)) return launch_split<C0>(p, splits, kc, ws, s);
+      const hipError_t e = launch_big16_128_split(p, splits, kc, ws, s);
+      return e != hipSuccess ? e : launch_splitk_reduce(p, splits, ws, s);
+    }
     default: return hipErrorInvalidValue;
   }
 }
@@ -2499,21 +2511,29 @@ int prod_choose(int M, int N, int K) {
 // non-temporal stores (the slabs are read back at once).
 static bool split_supports(int index) {
   switch (index) {
-    case 0: case 1: case 2: case 3: case 4: case 7: case 12: return true;
+    case 0: case 1: case 2: case 3: case 4: case 7: case 12: case 23: return true;
     default: return false;
   }
 }
 
 // Split-K plan.  Automatic entry: 128 x 128 x 32 tiles (64 x 64 below a
-// 128 x 128 output), two workgroups per CU.  Automatic split count: enough
-// (tile, split) pairs to give every CU a workgroup, each split at least four
-// k steps deep; products that already have a tile for every CU, or fewer
-// than 32 k steps, are not split.  An explicit count is honoured up to one k step per split.  The
-// chunk kc is a multiple of BK, and splits = ceil(K / kc).
+// 128 x 128 output), two workgroups per CU -- entry 23, whose split form
+// runs the direct-load 16x16-MFMA kernel where the product fits it and
+// entry 0's otherwise.  Automatic split count: the one with the least
+// estimated time, counted in k steps of one tile,
+//   rounds(s) * ceil(ksteps / s) + (partial-slab bytes written and read back) / B,
+// where rounds(s) = ceil(tiles * s / 256): a CU given two (tile, chunk) pairs
+// takes about twice as long as one given one, so the launch's time is its
+// busiest CU's; B is the HBM bytes moved in the time of one k step (a
+// 128x128x32 step is 1 MFLOP, about 2 us on one CU; HBM moves about 9 MB in
+// that time).  Each split is at least four k steps deep; products with more
+// than half a tile per CU, or fewer than 32 k steps, are not split.  An
+// explicit count is honoured up to one k step per split.  The chunk kc is a
+// multiple of BK, and splits = ceil(K / kc).
 bool splitk_plan(int M, int N, int K, int config, int splits, SplitPlan *out) {
   if (M < 0 || N < 0 || K < 0 || splits < 0) return false;
   const bool auto_config = config == -1;
-  if (auto_config) config = (M < 128 && N < 128) ? 3 : 0;
+  if (auto_config) config = (M < 128 && N < 128) ? 3 : 23;
   if (config < 0 || config >= kNumConfigs || !split_supports(config)) return false;
   const ProdConfig &c = kEntries[config].cfg;
   const long long tiles = ceil_div(M, c.BM) * ceil_div(N, c.BN);
@@ -2521,10 +2541,20 @@ bool splitk_plan(int M, int N, int K, int config, int splits, SplitPlan *out) {
   long long want = splits;
   if (want == 0) {
     const long long cus = 256;
-    want = tiles >= cus ? 1 : ceil_div(cus, tiles > 0 ? tiles : 1);
-    const long long deep = ksteps / 4;
-    if (want > deep) want = deep;
-    if (ksteps < 32) want = 1;  // a short k loop: the extra launch costs more than it saves
+    want = 1;
+    if (tiles > 0 && 2 * tiles <= cus && ksteps >= 32) {
+      // bytes HBM moves while one CU runs one k step of this entry's tile
+      const double step_bytes = 9.0e6 * ((double)c.BM * c.BN * c.BK / (128.0 * 128.0 * 32.0));
+      const double slab_bytes = 8.0 * M * N;  // one chunk's partial written and read back
+      long long most = ksteps / 4;
+      if (most > 4 * cus) most = 4 * cus;
+      double best = (double)ksteps;           // one split: one round, no slabs
+      for (long long sp = 2; sp <= most; ++sp) {
+        const double est = (double)ceil_div(tiles * sp, cus) * ceil_div(ksteps, sp) +
+                           sp * slab_bytes / step_bytes;
+        if (est < best) { best = est; want = sp; }
+      }
+    }
   }
   if (want > ksteps) want = ksteps;
   if (want > kMaxGridY) want = kMaxGridY;

@@ -206,8 +206,12 @@ int resident_workgroups() {
 // the workgroup's very last step reloads its own tile's first operands
 // into the idle stage.  LDS layouts and the per-element k order are those
 // of w16_kernel.
+//
+// The body is shared by the plain kernel and the split-K kernel (which runs
+// it on one chunk of K per grid row); `bid` of `G` is the workgroup's place
+// in the persistent grid.
 template <class W>
-__global__ void __launch_bounds__(256) big16_kernel(Problem p, int tiles_m, int tiles_n) {
+__device__ __forceinline__ void big16_body(Problem p, int tiles_m, int tiles_n, int bid, int G) {
   static_assert(W::STAGES == 2, "two stages");
   __shared__ __attribute__((aligned(16))) float lds[2 * W::STAGE];
   const unsigned lds_u = (unsigned)(uintptr_t)(lds_void_t *)lds;
@@ -218,8 +222,7 @@ __global__ void __launch_bounds__(256) big16_kernel(Problem p, int tiles_m, int 
   const int wm = wave >> 1, wn = wave & 1;
   const int ntiles = tiles_m * tiles_n;
   const int nk = p.K / W::BK;
-  const int G = gridDim.x;
-  const int lid = xcd_remap(blockIdx.x, G);
+  const int lid = xcd_remap(bid, G);
   if (lid >= ntiles) return;  // uniform per workgroup
   const int my_tiles = (ntiles - lid + G - 1) / G;
 
@@ -371,6 +374,29 @@ __global__ void __launch_bounds__(256) big16_kernel(Problem p, int tiles_m, int 
     }
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(0));  // the redundant last reload
+}
+
+template <class W>
+__global__ void __launch_bounds__(256) big16_kernel(Problem p, int tiles_m, int tiles_n) {
+  big16_body<W>(p, tiles_m, tiles_n, blockIdx.x, gridDim.x);
+}
+
+// Split-K: grid row y computes the partial product over k in
+// [y * kc, min(K, (y + 1) * kc)) into its own M x N slab of `ws` (row pitch
+// N), one tile per workgroup; the caller sums the slabs.  kc and K are
+// multiples of the k step.
+template <class W>
+__global__ void __launch_bounds__(256)
+    big16_split_kernel(Problem p, int tiles_m, int tiles_n, int kc, float *ws) {
+  const int y = blockIdx.y;
+  const int k0 = y * kc;
+  Problem ps = p;
+  ps.A = p.A + k0;
+  ps.B = p.B + (long long)k0 * p.ldb;
+  ps.K = p.K - k0 < kc ? p.K - k0 : kc;
+  ps.C = ws + (long long)y * p.M * p.N;
+  ps.ldc = p.N;
+  big16_body<W>(ps, tiles_m, tiles_n, blockIdx.x, gridDim.x);
 }
 
 template <class W, auto KERNEL>

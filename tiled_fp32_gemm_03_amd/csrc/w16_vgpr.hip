@@ -4,7 +4,8 @@
 //     for products whose tile count leaves 256x256 tiles a partial last
 //     round (3072^3 is exactly one round of 192x192 tiles, 6144^3 four);
 //   128x128 tiles on 64x64 waves, 32-deep steps (64 accumulators, 64 KB of
-//     LDS, two workgroups per CU), for mid-size products.
+//     LDS, two workgroups per CU), for mid-size products, and in split-K
+//     form for products with few output tiles.
 //
 // This translation unit is built with the MFMAs in their VGPR form
 // (-mllvm -amdgpu-mfma-vgpr-form=1, for this file only): with fewer than
@@ -45,6 +46,20 @@ bool big16_128_fits(const Problem &p) { return direct_fits<W128>(p); }
 hipError_t launch_big16_128(const Problem &p, hipStream_t s) {
   if (!direct_fits<W128>(p)) return hipErrorInvalidValue;
   return launch_big16_grid<W128, big16_kernel<W128>>(p, s);
+}
+
+bool big16_128_split_fits(const Problem &p, int kc) {
+  return direct_fits<W128>(p) && kc > 0 && kc % W128::BK == 0;
+}
+
+hipError_t launch_big16_128_split(const Problem &p, int splits, int kc, float *ws,
+                                  hipStream_t s) {
+  if (!big16_128_split_fits(p, kc)) return hipErrorInvalidValue;
+  const long long tiles_m = ceil_div(p.M, W128::BM), tiles_n = ceil_div(p.N, W128::BN);
+  const long long ntiles = tiles_m * tiles_n;
+  if (ntiles > 0x7fffffffLL || splits < 1 || splits > kMaxGridY) return hipErrorInvalidValue;
+  return launch_kernel(big16_split_kernel<W128>, dim3((unsigned)ntiles, (unsigned)splits),
+                       dim3(256), s, p, (int)tiles_m, (int)tiles_n, kc, ws);
 }
 
 }  // namespace gemm_f32_impl
