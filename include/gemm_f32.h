@@ -139,8 +139,9 @@ int gemm_f32_ex(int M, int N, int K, const float *A, int lda, const float *B,
  *           non-temporal-store entries are refused with GEMM_F32_BAD_CONFIG).
  *   splits  0 = automatic: the count with the least modelled time, from the
  *           busiest CU's share of (tile, chunk) pairs and the slab traffic,
- *           with at least four k steps per chunk; products with more than
- *           half a tile per CU, or with fewer than 32 k steps, are not split.
+ *           with at least four k steps per chunk, against the plain
+ *           product's modelled time; products with a tile for every CU, or
+ *           with fewer than 32 k steps, are not split.
  *           Else the requested count, capped at one k step per chunk.
  *   Writes the entry, the chunks actually used (1 means a plain product;
  *   with config -1 it then runs the entry gemm_f32 would choose),

@@ -126,14 +126,21 @@ def test_mixed_tile_queries():
 
 
 def test_splitk_plans():
-    # an under-filled product is split, one workgroup per CU, four k steps deep at least
-    p = g.gemm_f32_splitk_plan(1024, 1024, 1024)
-    t = g.gemm_f32_tile("prod", p["config"], 1024, 1024, 1024)
+    # an under-filled product is split, four k steps deep at least
+    p = g.gemm_f32_splitk_plan(1024, 1024, 4096)
+    t = g.gemm_f32_tile("prod", p["config"], 1024, 1024, 4096)
     tiles = -(-1024 // t["BM"]) * -(-1024 // t["BN"])
     assert p["splits"] > 1 and p["kc"] % t["BK"] == 0 and p["kc"] >= 4 * t["BK"]
     assert tiles * p["splits"] <= 2 * 256
-    assert (p["splits"] - 1) * p["kc"] < 1024 <= p["splits"] * p["kc"]
+    assert (p["splits"] - 1) * p["kc"] < 4096 <= p["splits"] * p["kc"]
     assert p["workspace_bytes"] == p["splits"] * 1024 * 1024 * 4
+    # few tiles and a long K: every CU gets a (tile, chunk) pair
+    p = g.gemm_f32_splitk_plan(256, 256, 16384)
+    assert p["splits"] * 4 == 256 and p["kc"] * p["splits"] == 16384
+    # 1024^3: the plain entry's 64x64 tiles fill every CU, and its modelled
+    # time beats the split's
+    p = g.gemm_f32_splitk_plan(1024, 1024, 1024)
+    assert p["splits"] == 1 and p["config"] == g.gemm_f32_tile("prod", -1, 1024, 1024, 1024)["config"]
     # a product with a tile for every CU is not split and needs no workspace
     p = g.gemm_f32_splitk_plan(4096, 4096, 4096)
     assert p["splits"] == 1 and p["workspace_bytes"] == 0
@@ -163,10 +170,11 @@ def test_splitk_plans():
 
 def test_splitk_validation_codes():
     lib = g._lib
-    need = g.gemm_f32_splitk_plan(1024, 1024, 1024)["workspace_bytes"]
+    need = g.gemm_f32_splitk_plan(1024, 1024, 4096)["workspace_bytes"]
+    assert need > 0
 
-    def call(ws, ws_bytes, A=256, B=512, C=1024, lda=1024):
-        return lib.gemm_f32_splitk(1024, 1024, 1024, A, lda, B, 1024, C, 1024, -1, 0, ws,
+    def call(ws, ws_bytes, A=256, B=512, C=1024, lda=4096):
+        return lib.gemm_f32_splitk(1024, 1024, 4096, A, lda, B, 1024, C, 1024, -1, 0, ws,
                                    ws_bytes, None)
     assert call(None, 0) == 9
     assert call(4096, need - 4) == 9

@@ -43,7 +43,7 @@ CASES = [  # (M, N, K, config, splits)
     # entry 23: the direct-load kernel per chunk, ragged tiles and a short last
     # chunk; K = 1000 is no multiple of its k step and takes entry 0's kernel
     (512, 512, 8192, 23, 16), (300, 260, 992, 23, 3), (128, 128, 4096, 23, 16),
-    (1024, 640, 4096, 23, 4), (260, 300, 1000, 23, 3),
+    (1024, 640, 4096, 23, 4), (260, 300, 1000, 23, 3), (1536, 1280, 2048, -1, 0),
 ]
 
 
@@ -65,7 +65,7 @@ def test_float_tolerance(g, case):
 
 
 def test_plans_really_split(g):
-    assert g.gemm_f32_splitk_plan(1024, 1024, 1024)["splits"] > 1
+    assert g.gemm_f32_splitk_plan(1024, 1024, 4096)["splits"] > 1
     assert g.gemm_f32_splitk_plan(257, 383, 129, 0, 5)["splits"] == 5
     assert g.gemm_f32_splitk_plan(128, 128, 4096, 0, 16)["splits"] == 16
 

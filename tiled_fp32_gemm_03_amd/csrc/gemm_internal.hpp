@@ -93,7 +93,7 @@ hipError_t launch_big16_128_split(const Problem &p, int splits, int kc, float *w
 
 int prod_num_configs();
 const ProdConfig &prod_config(int index);
-int prod_choose(int M, int N, int K);
+int prod_choose(int M, int N, int K, double *full_rate = nullptr);
 bool prod_supports(int index, int M, int N, int K);
 hipError_t launch_prod(int index, const Problem &p, hipStream_t s);
 

@@ -2474,7 +2474,11 @@ bool prod_supports(int index, int M, int N, int K) {
 // 64x64 waves with a register path for K tails (124), and 64x64x64 with K
 // split over the waves (108 at 24 steps per tile; less for shorter K, where
 // it wins anyway by filling the CUs).
-int prod_choose(int M, int N, int K) {
+// The plain product's automatic entry, and through `full_rate` (if given)
+// its modelled TFLOP/s when its tiles fill every workgroup slot (the rates
+// below are full-occupancy rates), else 0.
+int prod_choose(int M, int N, int K, double *full_rate) {
+  if (full_rate) *full_rate = 0.0;
   const long long t256x128 = ceil_div(M, 256) * ceil_div(N, 128);
   if (K <= 64 && t256x128 >= 1024) return 21;
   struct Cand {
@@ -2502,6 +2506,7 @@ int prod_choose(int M, int N, int K) {
     if (score > best_score) {
       best_score = score;
       best = c.entry;
+      if (full_rate) *full_rate = tiles >= c.slots ? score : 0.0;
     }
   }
   return best;
@@ -2526,8 +2531,11 @@ static bool split_supports(int index) {
 // takes about twice as long as one given one, so the launch's time is its
 // busiest CU's; B is the HBM bytes moved in the time of one k step (a
 // 128x128x32 step is 1 MFLOP, about 2 us on one CU; HBM moves about 9 MB in
-// that time).  Each split is at least four k steps deep; products with more
-// than half a tile per CU, or fewer than 32 k steps, are not split.  An
+// that time).  One split is the plain product: ceil(tiles / 256) * ksteps,
+// or, when the plain product's own entry fills every workgroup slot (so its
+// full-occupancy rate applies), that rate's time at 2 us per 1-MFLOP step.
+// Each split is at least four k steps deep; products with a tile for every
+// CU, or fewer than 32 k steps, are not split.  An
 // explicit count is honoured up to one k step per split.  The chunk kc is a
 // multiple of BK, and splits = ceil(K / kc).
 bool splitk_plan(int M, int N, int K, int config, int splits, SplitPlan *out) {
@@ -2542,13 +2550,19 @@ bool splitk_plan(int M, int N, int K, int config, int splits, SplitPlan *out) {
   if (want == 0) {
     const long long cus = 256;
     want = 1;
-    if (tiles > 0 && 2 * tiles <= cus && ksteps >= 32) {
+    if (tiles > 0 && tiles < cus && ksteps >= 32) {
       // bytes HBM moves while one CU runs one k step of this entry's tile
       const double step_bytes = 9.0e6 * ((double)c.BM * c.BN * c.BK / (128.0 * 128.0 * 32.0));
       const double slab_bytes = 8.0 * M * N;  // one chunk's partial written and read back
       long long most = ksteps / 4;
       if (most > 4 * cus) most = 4 * cus;
       double best = (double)ksteps;           // one split: one round, no slabs
+      double plain_rate;
+      prod_choose(M, N, K, &plain_rate);
+      if (plain_rate > 0.0) {                 // TFLOP/s -> k steps of 1 MFLOP at 2 us
+        const double plain_steps = 2.0 * M * N * (double)K / (plain_rate * 1e6) / 2.0;
+        if (plain_steps < best) best = plain_steps;
+      }
       for (long long sp = 2; sp <= most; ++sp) {
         const double est = (double)ceil_div(tiles * sp, cus) * ceil_div(ksteps, sp) +
                            sp * slab_bytes / step_bytes;
