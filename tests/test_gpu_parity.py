@@ -159,7 +159,7 @@ KSPLIT_ENTRY = 16  # 64x64x64, K split over the waves (its own summation order)
 # 16x16 MFMAs: one wave per SIMD on 64x64 (17, 23), 128x128 (19) and 96x96
 # (22) wave tiles; 256x256 direct-to-LDS on 16 waves (18); 128x128 wave
 # tiles staged through registers (20)
-W16_ENTRIES = (17, 18, 19, 20, 22, 23)
+W16_ENTRIES = (17, 18, 19, 20, 22, 23, 24)
 OWN_ORDER_ENTRIES = (KSPLIT_ENTRY,) + W16_ENTRIES
 LDS_DMA_ENTRY = 15  # 256x256x32 with direct-to-LDS loads
 REG_STAGED_ENTRY = 12  # the same tiles through registers

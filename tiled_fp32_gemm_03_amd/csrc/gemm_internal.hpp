@@ -75,12 +75,14 @@ int mixed_choose(int M, int N, int K);
 hipError_t launch_mixed(int format, int index, const MixedProblem &p, hipStream_t s);
 hipError_t launch_zero_f32(float *C, int M, int N, long long ldc, hipStream_t s);
 
-// The 192x192 and 128x128 direct-load kernels (w16_vgpr.hip): whether each
+// The 192x192, 192x256 and 128x128 direct-load kernels (w16_vgpr.hip): whether each
 // takes the product (16-byte aligned rows of A and B, N % 4 == 0, C at
 // least one tile each way, K a positive multiple of 32, leading dimensions
 // below 2^24), and its launch.
 bool big16_192_fits(const Problem &p);
 hipError_t launch_big16_192(const Problem &p, hipStream_t s);
+bool big16_192x256_fits(const Problem &p);
+hipError_t launch_big16_192x256(const Problem &p, hipStream_t s);
 bool big16_128_fits(const Problem &p);
 hipError_t launch_big16_128(const Problem &p, hipStream_t s);
 // Split-K form of the 128x128 kernel: grid row y computes k in

@@ -2200,6 +2200,7 @@ const Entry kEntries[] = {
     {{256, 128, 64, 2, 2, 1, "panel256x128_k64_arow_mfma16"}, kPanel},
     {{192, 192, 32, 2, 2, 1, "192x192x32_w2x2_ldsdma_mfma16"}, kKsplit},
     {{128, 128, 32, 2, 2, 2, "128x128x32_w2x2_ldsdma_mfma16"}, kKsplit},
+    {{192, 256, 32, 2, 2, 1, "192x256x32_w2x2_ldsdma_mfma16"}, kKsplit},
 };
 constexpr int kNumConfigs = sizeof(kEntries) / sizeof(kEntries[0]);
 constexpr int kRemainderConfig = 3;  // thin edge strips
@@ -2406,6 +2407,10 @@ hipError_t launch_one(int index, const Problem &p, hipStream_t s) {
     case 17: return launch_w16<W16<64, 64, 64, 2>, C0>(p, s);
     case 18: return launch_lds_dma16<C12>(p, s);
     case 19: return launch_big16<W16<128, 128, 32, 2>, launch_big16r<W16<128, 128, 32, 2>>>(p, s);
+    case 24:  // 192x256 direct-load tiles (built apart); else entry 19's launcher
+      return big16_192x256_fits(p)
+                 ? launch_big16_192x256(p, s)
+                 : launch_big16<W16<128, 128, 32, 2>, launch_big16r<W16<128, 128, 32, 2>>>(p, s);
     case 20: return launch_big16r<W16<128, 128, 32, 2>>(p, s);
     case 21: return launch_arow16(p, s);
     case 22:  // 192x192 direct-load tiles (built apart); else the 256x256 register path
@@ -2482,22 +2487,23 @@ int prod_choose(int M, int N, int K, double *full_rate) {
   const long long t256x128 = ceil_div(M, 256) * ceil_div(N, 128);
   if (K <= 64 && t256x128 >= 1024) return 21;
   struct Cand {
-    int entry, tile;
+    int entry, bm, bn;
     double rate;
     int slots;  // resident workgroups on 256 CUs
   };
   const bool whole_steps = K % 32 == 0;
-  const Cand cands[] = {{19, 256, whole_steps ? 148.0 : 135.0, 256},
-                        {22, 192, whole_steps ? 138.0 : 0.0, 256},
-                        {23, 128, whole_steps ? 141.0 : 0.0, 512},
-                        {17, 128, 124.0, 256},
-                        {16, 64, 108.0, 256}};
+  const Cand cands[] = {{19, 256, 256, whole_steps ? 148.0 : 135.0, 256},
+                        {24, 192, 256, whole_steps ? 140.0 : 0.0, 256},
+                        {22, 192, 192, whole_steps ? 138.0 : 0.0, 256},
+                        {23, 128, 128, whole_steps ? 141.0 : 0.0, 512},
+                        {17, 128, 128, 124.0, 256},
+                        {16, 64, 64, 108.0, 256}};
   constexpr long long kCus = 256;  // CUs of an MI355X
   int best = 16;
   double best_score = -1.0;
   for (const Cand &c : cands) {
-    const long long tm = ceil_div(M - thin_remainder(M, c.tile), c.tile);
-    const long long tn = ceil_div(N - thin_remainder(N, c.tile), c.tile);
+    const long long tm = ceil_div(M - thin_remainder(M, c.bm), c.bm);
+    const long long tn = ceil_div(N - thin_remainder(N, c.bn), c.bn);
     const long long tiles = tm * tn;
     if (tiles <= 0) continue;
     const long long grid = tiles < c.slots ? tiles : c.slots;

@@ -5,7 +5,10 @@
 //     round (3072^3 is exactly one round of 192x192 tiles, 6144^3 four);
 //   128x128 tiles on 64x64 waves, 32-deep steps (64 accumulators, 64 KB of
 //     LDS, two workgroups per CU), for mid-size products, and in split-K
-//     form for products with few output tiles.
+//     form for products with few output tiles;
+//   192x256 tiles on 96x128 waves, 32-deep steps (192 accumulators, 112 KB
+//     of LDS), for products whose 256x256 tiles leave a partial last round
+//     and whose 192x256 tiles do not (3072x4096 is one round, 6144^2 three).
 //
 // This translation unit is built with the MFMAs in their VGPR form
 // (-mllvm -amdgpu-mfma-vgpr-form=1, for this file only): with fewer than
@@ -20,6 +23,7 @@ namespace {
 
 using W192 = W16<96, 96, 32, 2>;
 using W128 = W16<64, 64, 32, 2>;
+using W192x256 = W16<96, 128, 32, 2>;
 
 // Direct loads need 16-byte aligned rows of A and B and N % 4 == 0; the
 // kernel needs C at least one tile each way, K a positive multiple of the
@@ -39,6 +43,13 @@ bool big16_192_fits(const Problem &p) { return direct_fits<W192>(p); }
 hipError_t launch_big16_192(const Problem &p, hipStream_t s) {
   if (!direct_fits<W192>(p)) return hipErrorInvalidValue;
   return launch_big16_grid<W192, big16_kernel<W192>>(p, s);
+}
+
+bool big16_192x256_fits(const Problem &p) { return direct_fits<W192x256>(p); }
+
+hipError_t launch_big16_192x256(const Problem &p, hipStream_t s) {
+  if (!direct_fits<W192x256>(p)) return hipErrorInvalidValue;
+  return launch_big16_grid<W192x256, big16_kernel<W192x256>>(p, s);
 }
 
 bool big16_128_fits(const Problem &p) { return direct_fits<W128>(p); }
