@@ -160,7 +160,10 @@ KSPLIT_ENTRY = 16  # 64x64x64, K split over the waves (its own summation order)
 # (22) wave tiles; 256x256 direct-to-LDS on 16 waves (18); 128x128 wave
 # tiles staged through registers (20)
 W16_ENTRIES = (17, 18, 19, 20, 22, 23, 24)
-OWN_ORDER_ENTRIES = (KSPLIT_ENTRY,) + W16_ENTRIES
+# rows in whole rounds of entry 19's tiles plus a remainder on its own entry,
+# or the whole product on the model's entry: the order of whichever runs
+ROW_REGION_ENTRY = 25
+OWN_ORDER_ENTRIES = (KSPLIT_ENTRY,) + W16_ENTRIES + (ROW_REGION_ENTRY,)
 LDS_DMA_ENTRY = 15  # 256x256x32 with direct-to-LDS loads
 REG_STAGED_ENTRY = 12  # the same tiles through registers
 
@@ -559,3 +562,31 @@ def test_device_props(g):
     d = g.gemm_f32_device_props(0)
     assert d["cus"] == torch.cuda.get_device_properties(0).multi_processor_count
     assert d["wave_size"] == 64 and d["clock_mhz"] > 500 and d["lds_bytes_per_cu"] >= 65536
+
+
+@pytest.mark.parametrize("case", [(4608, 4096, 256, "small_int"), (4608, 4100, 128, "normal")])
+def test_row_region_entry(g, case):
+    """Entry 25 cuts C by rows: 4096 rows in one round of 256x256 tiles
+    (entry 19), the other 512 in a second launch on their own entry.  Random
+    samples plus every element of the rows on both sides of the cut."""
+    M, N, K, dist = case
+    assert g.gemm_f32_tile("prod", -1, M, N, K)["config"] == ROW_REGION_ENTRY
+    print(f"case: row region {case}", flush=True)
+    a, b = make(M, N, K, dist, seed=M + N + K)
+    c = _run(g, a, b, "prod")
+    ii, jj = _sample_indices(M, N, 20000, seed=K)
+    rows = np.repeat(np.arange(4094, 4098), N)
+    cols = np.tile(np.arange(N), 4)
+    ii, jj = np.concatenate([ii, rows]), np.concatenate([jj, cols])
+    want = oracle.gemm_elems(a, b, ii, jj)
+    if dist == "small_int":
+        assert np.array_equal(c[ii, jj], want)
+    else:
+        _tol_check(c[ii, jj], want, K, f"row region {case}")
+
+
+def test_row_region_entry_without_a_cut(g):
+    """Where no cut pays, entry 25 runs the product on the model's own entry."""
+    a, b = make(600, 520, 96, "small_int", seed=25)
+    print("case: row region, no cut, 600x520x96", flush=True)
+    assert np.array_equal(_run(g, a, b, "prod", ROW_REGION_ENTRY), oracle.gemm(a, b))

@@ -2201,6 +2201,7 @@ const Entry kEntries[] = {
     {{192, 192, 32, 2, 2, 1, "192x192x32_w2x2_ldsdma_mfma16"}, kKsplit},
     {{128, 128, 32, 2, 2, 2, "128x128x32_w2x2_ldsdma_mfma16"}, kKsplit},
     {{192, 256, 32, 2, 2, 1, "192x256x32_w2x2_ldsdma_mfma16"}, kKsplit},
+    {{256, 256, 32, 2, 2, 1, "rows256_rounds+rest"}, kKsplit},
 };
 constexpr int kNumConfigs = sizeof(kEntries) / sizeof(kEntries[0]);
 constexpr int kRemainderConfig = 3;  // thin edge strips
@@ -2385,6 +2386,15 @@ hipError_t launch_arow16(const Problem &p, hipStream_t s) {
                        (int)panels, (int)chunks, (int)tiles_n);
 }
 
+// The best k-loop entry by the automatic choice's model, its modelled
+// TFLOP/s, and that rate again if its tiles fill every workgroup slot (else 0).
+struct KloopModel {
+  int entry;
+  double score, full_rate;
+};
+KloopModel model_kloop(int M, int N, int K);
+int region_rows(int M, int N, int K);
+
 hipError_t launch_one(int index, const Problem &p, hipStream_t s) {
   switch (index) {
     case 0: return launch_kloop<C0>(p, s);
@@ -2407,6 +2417,17 @@ hipError_t launch_one(int index, const Problem &p, hipStream_t s) {
     case 17: return launch_w16<W16<64, 64, 64, 2>, C0>(p, s);
     case 18: return launch_lds_dma16<C12>(p, s);
     case 19: return launch_big16<W16<128, 128, 32, 2>, launch_big16r<W16<128, 128, 32, 2>>>(p, s);
+    case 25: {  // rows in whole rounds of entry 19's tiles, the rest on its own entry
+      const int r = region_rows(p.M, p.N, p.K);
+      if (r == 0) return launch_prod(model_kloop(p.M, p.N, p.K).entry, p, s);
+      Problem top = p, rest = p;
+      top.M = 256 * r;
+      rest.M = p.M - top.M;
+      rest.A = p.A + (long long)top.M * p.lda;
+      rest.C = p.C + (long long)top.M * p.ldc;
+      const hipError_t e = launch_prod(19, top, s);
+      return e != hipSuccess ? e : launch_prod(model_kloop(rest.M, rest.N, rest.K).entry, rest, s);
+    }
     case 24:  // 192x256 direct-load tiles (built apart); else entry 19's launcher
       return big16_192x256_fits(p)
                  ? launch_big16_192x256(p, s)
@@ -2450,6 +2471,66 @@ int thin_remainder(int extent, int tile) {
   return (extent > tile && rem > 0 && rem * 8 <= tile) ? rem : 0;
 }
 
+// The model of the automatic choice (prod_choose, below).
+
+KloopModel model_kloop(int M, int N, int K) {
+  struct Cand {
+    int entry, bm, bn;
+    double rate;
+    int slots;  // resident workgroups on 256 CUs
+  };
+  const bool whole_steps = K % 32 == 0;
+  const Cand cands[] = {{19, 256, 256, whole_steps ? 148.0 : 135.0, 256},
+                        {24, 192, 256, whole_steps ? 140.0 : 0.0, 256},
+                        {22, 192, 192, whole_steps ? 138.0 : 0.0, 256},
+                        {23, 128, 128, whole_steps ? 141.0 : 0.0, 512},
+                        {17, 128, 128, 124.0, 256},
+                        {16, 64, 64, 108.0, 256}};
+  constexpr long long kCus = 256;  // CUs of an MI355X
+  KloopModel best{16, -1.0, 0.0};
+  for (const Cand &c : cands) {
+    const long long tm = ceil_div(M - thin_remainder(M, c.bm), c.bm);
+    const long long tn = ceil_div(N - thin_remainder(N, c.bn), c.bn);
+    const long long tiles = tm * tn;
+    if (tiles <= 0) continue;
+    const long long grid = tiles < c.slots ? tiles : c.slots;
+    const long long busy = ceil_div(grid, kCus) * ceil_div(tiles, grid);  // tile times per CU
+    const double score = c.rate * (double)tiles / (double)(busy * kCus);
+    if (score > best.score) best = {c.entry, score, tiles >= c.slots ? score : 0.0};
+  }
+  return best;
+}
+
+// Entry 25 cuts C by rows: rows [0, 256 r) run entry 19 on whole rounds of
+// 256x256 tiles (r * tiles-per-row <= 256 q for some q), the rest runs its
+// own best k-loop entry in a second launch.  Returns the r whose modelled
+// time beats the best single entry by more than a launch (4 us), else 0.
+int region_rows(int M, int N, int K) {
+  if (K % 32 != 0 || M < 512 || N < 256) return 0;
+  const long long tn = ceil_div(N - thin_remainder(N, 256), 256);
+  const long long tm = M / 256;
+  const double flops_per_row = 2.0 * N * (double)K;
+  const KloopModel whole = model_kloop(M, N, K);
+  double best_us = flops_per_row * M / (whole.score * 1e6);
+  int best_r = 0;
+  for (long long q = 1; q <= 8; ++q) {
+    const long long r = 256 * q / tn;
+    if (r < 1) continue;
+    if (r >= tm) break;
+    const int m1 = (int)(256 * r);
+    if (M - m1 < 128) break;
+    const double top = 148.0 * (double)(r * tn) / (double)(ceil_div(r * tn, 256) * 256);
+    const KloopModel rest = model_kloop(M - m1, N, K);
+    const double us = flops_per_row * m1 / (top * 1e6) +
+                      flops_per_row * (M - m1) / (rest.score * 1e6) + 4.0;
+    if (us < best_us) {
+      best_us = us;
+      best_r = (int)r;
+    }
+  }
+  return best_r;
+}
+
 }  // namespace
 
 int prod_num_configs() { return kNumConfigs; }
@@ -2486,36 +2567,10 @@ int prod_choose(int M, int N, int K, double *full_rate) {
   if (full_rate) *full_rate = 0.0;
   const long long t256x128 = ceil_div(M, 256) * ceil_div(N, 128);
   if (K <= 64 && t256x128 >= 1024) return 21;
-  struct Cand {
-    int entry, bm, bn;
-    double rate;
-    int slots;  // resident workgroups on 256 CUs
-  };
-  const bool whole_steps = K % 32 == 0;
-  const Cand cands[] = {{19, 256, 256, whole_steps ? 148.0 : 135.0, 256},
-                        {24, 192, 256, whole_steps ? 140.0 : 0.0, 256},
-                        {22, 192, 192, whole_steps ? 138.0 : 0.0, 256},
-                        {23, 128, 128, whole_steps ? 141.0 : 0.0, 512},
-                        {17, 128, 128, 124.0, 256},
-                        {16, 64, 64, 108.0, 256}};
-  constexpr long long kCus = 256;  // CUs of an MI355X
-  int best = 16;
-  double best_score = -1.0;
-  for (const Cand &c : cands) {
-    const long long tm = ceil_div(M - thin_remainder(M, c.bm), c.bm);
-    const long long tn = ceil_div(N - thin_remainder(N, c.bn), c.bn);
-    const long long tiles = tm * tn;
-    if (tiles <= 0) continue;
-    const long long grid = tiles < c.slots ? tiles : c.slots;
-    const long long busy = ceil_div(grid, kCus) * ceil_div(tiles, grid);  // tile times per CU
-    const double score = c.rate * (double)tiles / (double)(busy * kCus);
-    if (score > best_score) {
-      best_score = score;
-      best = c.entry;
-      if (full_rate) *full_rate = tiles >= c.slots ? score : 0.0;
-    }
-  }
-  return best;
+  if (region_rows(M, N, K) > 0) return 25;
+  const KloopModel m = model_kloop(M, N, K);
+  if (full_rate) *full_rate = m.full_rate;
+  return m.entry;
 }
 
 // Entries the split-K path can run: the k-loop kernels without
