@@ -2495,7 +2495,11 @@ KloopModel model_kloop(int M, int N, int K) {
     if (tiles <= 0) continue;
     const long long grid = tiles < c.slots ? tiles : c.slots;
     const long long busy = ceil_div(grid, kCus) * ceil_div(tiles, grid);  // tile times per CU
-    const double score = c.rate * (double)tiles / (double)(busy * kCus);
+    // the last tile row and column are moved back inside C, so part of
+    // their work overlaps a neighbour's and is done twice
+    const double useful = (double)(M - thin_remainder(M, c.bm)) * (N - thin_remainder(N, c.bn)) /
+                          ((double)tm * c.bm * (double)tn * c.bn);
+    const double score = c.rate * useful * (double)tiles / (double)(busy * kCus);
     if (score > best.score) best = {c.entry, score, tiles >= c.slots ? score : 0.0};
   }
   return best;
