@@ -2556,17 +2556,21 @@ bool prod_supports(int index, int M, int N, int K) {
 // fraction of the time the CUs are busy on the persistent grid -- G =
 // min(resident workgroups, tiles) workgroups, ceil(G / 256) of them per CU,
 // ceil(tiles / G) tiles each, against tiles / 256 if the work spread
-// evenly -- counting tiles after the thin remainder strips are split off.
-// Candidates (K a multiple of 32 and aligned rows take the direct-load
-// forms): 256x256x32 on 128x128 wave tiles (148 TFLOP/s with direct loads,
-// about 135 staged through registers), 192x192x32 on 96x96 waves (138),
-// 128x128x32 on 64x64 waves, two workgroups per CU (141), 128x128x64 on
-// 64x64 waves with a register path for K tails (124), and 64x64x64 with K
-// split over the waves (108 at 24 steps per tile; less for shorter K, where
-// it wins anyway by filling the CUs).
-// The plain product's automatic entry, and through `full_rate` (if given)
-// its modelled TFLOP/s when its tiles fill every workgroup slot (the rates
-// below are full-occupancy rates), else 0.
+// evenly -- and times the useful fraction of the tiles' work (edge tiles
+// moved back inside C repeat part of a neighbour's), counting tiles after
+// the thin remainder strips are split off.  Candidates (K a multiple of 32
+// and aligned rows take the direct-load forms): 256x256x32 on 128x128 wave
+// tiles (148 TFLOP/s with direct loads, about 135 staged through
+// registers), 192x256x32 on 96x128 waves (140), 192x192x32 on 96x96 waves
+// (138), 128x128x32 on 64x64 waves, two workgroups per CU (141), 128x128x64
+// on 64x64 waves with a register path for K tails (124), and 64x64x64 with
+// K split over the waves (108 at 24 steps per tile; less for shorter K,
+// where it wins anyway by filling the CUs).  Entry 25 (region_rows) when
+// cutting C by rows into whole rounds of 256x256 tiles plus a remainder
+// models faster still.
+// Returns the plain product's automatic entry, and through `full_rate` (if
+// given) its modelled TFLOP/s when its tiles fill every workgroup slot (the
+// rates are full-occupancy rates), else 0.
 int prod_choose(int M, int N, int K, double *full_rate) {
   if (full_rate) *full_rate = 0.0;
   const long long t256x128 = ceil_div(M, 256) * ceil_div(N, 128);
