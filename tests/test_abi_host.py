@@ -278,3 +278,24 @@ def test_single_hip_runtime_in_process():
     with open("/proc/self/maps") as f:
         libs = {ln.split()[-1] for ln in f if "libamdhip64" in ln}
     assert len(libs) == 1, libs
+
+
+def test_automatic_choice_on_measured_shapes():
+    """The plain product's automatic entry on shapes where every large entry
+    was timed: the choice that measured fastest (or within 0.5% of it).  A
+    change to the model that moves one of these needs new measurements."""
+    expected = {
+        (4096, 4096, 4096): 19,    # one whole round of 256x256 tiles
+        (4097, 4095, 2049): 19,    # K tail: register-staged 256x256, strips
+        (16384, 16384, 64): 21,    # small-K A-resident panel
+        (1024, 1024, 1024): 16,    # 64x64 tiles, K split over the waves
+        (2048, 2048, 2048): 23,    # 128x128, two workgroups per CU
+        (3072, 3072, 3072): 22,    # one whole round of 192x192 tiles
+        (6144, 6144, 6144): 24,    # three whole rounds of 192x256 tiles
+        (3072, 4096, 4096): 24,    # one whole round of 192x256 tiles
+        (4608, 4608, 4608): 25,    # row cut: whole round of 256x256 + rest
+        (7168, 7168, 7168): 25,
+        (5632, 5632, 5632): 19,
+    }
+    got = {s: g.gemm_f32_tile("prod", -1, *s)["config"] for s in expected}
+    assert got == expected
