@@ -3,9 +3,22 @@
 
 A step is one call of the production kernel on the square 4096^3 workload
 (A, B ~ U[-1, 1], seed 2; inputs resident in HBM before timing starts).
-Prints ONE JSON line with TFLOP/s, the roofline of the dominant kernel, the
-skinny K = 64 workload's HBM rate against the bandwidth measured in the same
-run, and the CPU oracle timed on a bounded sample as a reported baseline.
+Before the timed steps the same call runs for a fixed settle period, so the
+timed region sees the engine clock the kernel sustains rather than its ramp.
+
+Prints ONE JSON line with TFLOP/s, the roofline of the dominant kernel, and,
+as extra keys:
+  * measured denominators (HBM streaming probes, fp32 MFMA probe, the fused
+    MFMA + store probe at the skinny product's intensity, with the engine
+    clock it ran at);
+  * one record per workload (square_256, square_1024_int, square_4096,
+    ragged, skinny_k64): the automatic entry, its time, TFLOP/s, GB/s and the
+    fraction of its binding roof, the CPU oracle's time for the same full
+    product on this host, and the verdict of comparing every element of the
+    GPU result with the oracle's (bit-exact on integer inputs, the fp32
+    tolerance otherwise), taken outside the timed regions;
+  * the skinny K = 64 block against the bandwidth measured in the same run;
+  * the CPU oracle on the benchmark workload as the reported baseline.
 
   python bench.py [--gpus 1] [--steps 100] [--warmup 20]
 """
@@ -15,6 +28,7 @@ import argparse
 import json
 import os
 import platform
+import statistics
 import sys
 import time
 
@@ -24,10 +38,26 @@ if ROOT not in sys.path:
 
 METRIC = "fp32 GEMM TFLOPS @N=4096 (% of fp32 peak); HBM GB/s on K=64 skinny shape"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+WORKLOADS = ("square_256", "square_1024_int", "square_4096", "ragged", "skinny_k64")
+# Timed calls per workload record: more for the few-microsecond products.
+RECORD_REPS = {"square_256": 50, "square_1024_int": 50}
 
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def settle(fn, settle_ms: float) -> tuple[int, float]:
+    """Run fn back to back for at least settle_ms of wall time (synchronising
+    every few launches), so the engine clock reaches what this load sustains."""
+    import torch
+    n, t0 = 0, time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < settle_ms:
+        for _ in range(8):
+            fn()
+        n += 8
+        torch.cuda.synchronize()
+    return n, time.perf_counter() - t0
 
 
 def time_launches(fn, steps: int, warmup: int, stream) -> tuple[float, float]:
@@ -46,6 +76,24 @@ def time_launches(fn, steps: int, warmup: int, stream) -> tuple[float, float]:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return start.elapsed_time(end) / steps, wall
+
+
+def time_each(fn, reps: int, warmup: int, stream) -> dict:
+    """Per-call times from events recorded between back-to-back calls on
+    `stream` (no work added to the stream): mean, median and min in ms."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for i in range(reps):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+    return {"mean_ms": ev[0].elapsed_time(ev[-1]) / reps, "median_ms": statistics.median(per),
+            "min_ms": min(per), "reps": reps}
 
 
 def measure_hbm(g, stream, reps: int = 8) -> dict:
@@ -71,8 +119,7 @@ def measure_hbm(g, stream, reps: int = 8) -> dict:
 
 def measure_mfma(g, stream) -> float:
     """fp32 MFMA probe: 8 independent accumulator chains per wave, two waves
-    per SIMD, about 1.7 ms per launch; 20 timed launches after 5 warm-up ones
-    so that the clock has settled (short runs read the clock ramp)."""
+    per SIMD, about 1.7 ms per launch; 20 timed launches after 5 warm-up ones."""
     import torch
     wgs, iters = 256 * 2, 4000
     buf = torch.zeros(wgs * 4, device="cuda:0")
@@ -88,6 +135,41 @@ def measure_valu(g, stream) -> float:
     ms, _ = time_launches(lambda: g.gemm_f32_probe_valu(wgs, iters, buf.data_ptr(), stream.cuda_stream),
                           5, 2, stream)
     return g.gemm_f32_probe_valu_flops(wgs, iters) / (ms * 1e-3) / 1e12
+
+
+def measure_fused(g, stream, settle_ms: float) -> dict:
+    """The fused probe at the skinny product's intensity (32 FLOP per stored
+    byte) with the FLOPs and the 1 GiB output of 16384 x 16384 x 64: MFMAs
+    and stores together, each alone, at one and two waves per SIMD.  Reports
+    each mode's time, rates and the engine clock the waves saw."""
+    import torch
+    dev = torch.device("cuda:0")
+    out = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    s = stream.cuda_stream
+    res = {}
+    for wgs, trips in ((256, 1024), (512, 512)):
+        clocks = torch.zeros(2 * wgs * 4, dtype=torch.int64, device=dev)
+        for mode, name in ((g.FUSED_BOTH, "both"), (g.FUSED_MFMA, "mfma_only"),
+                           (g.FUSED_STORE, "store_only")):
+            def call():
+                g.gemm_f32_probe_fused(mode, wgs, trips, out.data_ptr(), out.numel() * 4,
+                                       clocks.data_ptr(), s)
+            settle(call, settle_ms)
+            t = time_each(call, 10, 2, stream)
+            ms = t["median_ms"]
+            fl = g.gemm_f32_probe_fused_flops(mode, wgs, trips)
+            by = g.gemm_f32_probe_fused_bytes(mode, wgs, trips) if mode != g.FUSED_MFMA else 0
+            c = clocks.view(-1, 2).double()
+            mhz = float((c[:, 0] / c[:, 1]).mean().item() * 100.0)
+            res[f"{name}_w{wgs // 256}"] = {
+                "ms": round(ms, 5), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+                "gbps": round(by / (ms * 1e-3) / 1e9, 1), "clock_mhz": round(mhz, 1)}
+    del out
+    torch.cuda.empty_cache()
+    best = max((v for k, v in res.items() if k.startswith("both")), key=lambda v: v["tflops"])
+    res["best_both_tflops"] = best["tflops"]
+    res["best_both_gbps"] = best["gbps"]
+    return res
 
 
 def load_traffic(workload: str, config_label: str):
@@ -108,55 +190,124 @@ def load_traffic(workload: str, config_label: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(a, b, target_s: float) -> dict:
-    """The CPU oracle (test infrastructure) on a bounded row band of the same
-    workload: reported baseline only."""
-    import oracle
-    import numpy as np
-    K = a.shape[1]
-    N = b.shape[1]
-    probe_rows = 8
-    t0 = time.perf_counter()
-    oracle.gemm(np.ascontiguousarray(a[:probe_rows]), b)
-    t_probe = time.perf_counter() - t0
-    rows = int(min(a.shape[0], max(probe_rows, round(target_s / max(t_probe, 1e-6) * probe_rows))))
-    band = np.ascontiguousarray(a[:rows])
-    t0 = time.perf_counter()
-    oracle.gemm(band, b)
-    dt = time.perf_counter() - t0
-    flops = 2.0 * rows * N * K
-    cpu_model = platform.processor() or platform.machine()
+def cpu_model() -> str:
+    name = platform.processor() or platform.machine()
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
                 if line.startswith("model name"):
-                    cpu_model = line.split(":", 1)[1].strip()
-                    break
+                    return line.split(":", 1)[1].strip()
     except OSError:
         pass
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"rows 0..{rows - 1} of the {a.shape[0]}x{N}x{K} product "
-                      f"({rows}x{N} outputs, full K), {dt:.1f} s",
-            "seconds": round(dt, 2), "cpu_model": cpu_model}
+    return name
+
+
+def oracle_product(a, b) -> tuple:
+    """The CPU oracle (test infrastructure) on the whole product: (C, seconds)."""
+    import oracle
+    t0 = time.perf_counter()
+    c = oracle.gemm(a, b)
+    return c, time.perf_counter() - t0
+
+
+def compare_full(got, ref, K: int, exact: bool) -> dict:
+    """Every element of the GPU result against the oracle's, in fp64, a band
+    of rows at a time (bit-exact bar for integer inputs, else max |diff| <=
+    1e-4 sqrt(K) and relative Frobenius <= 1e-5)."""
+    import numpy as np
+    M, N = got.shape
+    rows = max(1, (1 << 22) // max(N, 1))
+    max_err, err2, ref2, mism, finite = 0.0, 0.0, 0.0, 0, True
+    for r0 in range(0, M, rows):
+        g64 = got[r0:r0 + rows].astype(np.float64)
+        r64 = ref[r0:r0 + rows].astype(np.float64)
+        finite = finite and bool(np.isfinite(g64).all())
+        d = np.abs(g64 - r64)
+        if d.size:
+            max_err = max(max_err, float(d.max()))
+        err2 += float(np.dot(d.ravel(), d.ravel()))
+        ref2 += float(np.dot(r64.ravel(), r64.ravel()))
+        mism += int(np.count_nonzero(got[r0:r0 + rows] != ref[r0:r0 + rows]))
+    fro = (err2 ** 0.5) / (ref2 ** 0.5) if ref2 > 0 else err2 ** 0.5
+    if exact:
+        ok = finite and mism == 0
+        bar = "bit-exact"
+    else:
+        ok = finite and max_err <= 1e-4 * max(K, 1) ** 0.5 and fro <= 1e-5
+        bar = "max|d| <= 1e-4 sqrt(K), rel Frobenius <= 1e-5"
+    return {"pass": ok, "bar": bar, "elements": int(M * N), "max_abs_err": max_err,
+            "rel_fro": fro, "mismatched_bits": mism}
+
+
+def workload_record(g, rf, name: str, stream, settle_ms: float, peaks: dict) -> dict:
+    """One workload through the automatic production entry: timing, roofline
+    fraction, the oracle's time on the same product, and the full comparison."""
+    import torch
+
+    from gemm_inputs import make_workload
+    w, a, b = make_workload(name)
+    dev = torch.device("cuda:0")
+    ta, tb = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+    tc = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
+    label = g.config_name("prod", -1, w.M, w.N, w.K)
+    s = stream.cuda_stream
+
+    def call():
+        g.gemm_f32_ex(w.M, w.N, w.K, ta.data_ptr(), w.K, tb.data_ptr(), w.N, tc.data_ptr(), w.N,
+                      "prod", -1, s)
+
+    settle(call, settle_ms)
+    t = time_each(call, RECORD_REPS.get(name, 20), 5, stream)
+    got = tc.cpu().numpy()
+    del ta, tb, tc
+    torch.cuda.empty_cache()
+    ms = t["median_ms"]
+    fl = rf.flops(w.M, w.N, w.K)
+    by = rf.compulsory_bytes(w.M, w.N, w.K)
+    tflops = fl / (ms * 1e-3) / 1e12
+    gbps = by / (ms * 1e-3) / 1e9
+    rec = {"workload": name, "M": w.M, "N": w.N, "K": w.K, "dist": w.dist, "seed": w.seed,
+           "kernel": label, **{k: round(v, 5) if isinstance(v, float) else v for k, v in t.items()},
+           "tflops": round(tflops, 3), "gbps": round(gbps, 1),
+           "intensity_flop_per_byte": round(rf.intensity(w.M, w.N, w.K), 2)}
+    ai = rf.intensity(w.M, w.N, w.K)
+    if name == "square_256":
+        rec["roof"] = "launch latency (a few microseconds): no roofline claim"
+        rec["frac_of_binding_roof"] = None
+    else:
+        pmeas = peaks.get("mfma_fp32_tflops", rf.PEAK_FP32_MFMA_TFLOPS)
+        bmeas = peaks.get("hbm_gbps", {}).get("best", rf.PEAK_HBM_GBPS)
+        roof = rf.binding_roof_tflops(w.M, w.N, w.K, pmeas, bmeas)
+        rec["roof"] = "mfma" if pmeas <= ai * bmeas / 1000 else "hbm"
+        rec["binding_roof_tflops"] = round(roof, 2)
+        rec["frac_of_binding_roof"] = round(tflops / roof, 4)
+        rec["frac_of_peak_fp32"] = round(tflops / rf.PEAK_FP32_MFMA_TFLOPS, 4)
+    log(f"{name} {label}: median {ms:.4f} ms, {tflops:.2f} TFLOP/s, {gbps:.0f} GB/s")
+    ref, osec = oracle_product(a, b)
+    import oracle
+    rec["oracle"] = {"seconds": round(osec, 3), "gflops": round(fl / osec / 1e9, 2),
+                     "cores": oracle.num_threads(), "cpu_model": cpu_model(),
+                     "gpu_over_oracle": round(osec / (ms * 1e-3), 1)}
+    rec["verdict"] = compare_full(got, ref, w.K, exact=(w.dist == "int4"))
+    log(f"{name}: oracle {osec:.2f} s on {oracle.num_threads()} threads; verdict {rec['verdict']}")
+    del got, ref
+    return rec
 
 
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    # Defaults long enough to reach steady clocks: a few milliseconds of work
-    # measure the clock ramp rather than the kernel.
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=500.0,
+                    help="wall time the benchmark call runs before warm-up and timing")
     ap.add_argument("--workload", default="square_4096")
     ap.add_argument("--variant", default="prod")
     ap.add_argument("--config", type=int, default=-1, help="launch-table entry (-1 = automatic)")
-    ap.add_argument("--skinny-steps", type=int, default=100)
-    ap.add_argument("--skinny-warmup", type=int, default=20)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--record-settle-ms", type=float, default=200.0)
     ap.add_argument("--no-probes", action="store_true")
-    ap.add_argument("--no-skinny", action="store_true")
+    ap.add_argument("--no-records", action="store_true",
+                    help="skip the per-workload records (and with them the oracle runs)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -168,7 +319,7 @@ def main() -> int:
     import torch
 
     import tiled_fp32_gemm_03_amd as g
-    from gemm_inputs import WORKLOADS, make_workload
+    from gemm_inputs import make_workload
     from tiled_fp32_gemm_03_amd import roofline as rf
 
     if not torch.cuda.is_available():
@@ -192,6 +343,8 @@ def main() -> int:
         g.gemm_f32_ex(w.M, w.N, w.K, ta.data_ptr(), w.K, tb.data_ptr(), w.N, tc.data_ptr(), w.N,
                       args.variant, args.config, s)
 
+    n_settle, t_settle = settle(step, args.settle_ms)
+    log(f"settled {label}: {n_settle} calls in {t_settle * 1e3:.0f} ms")
     log(f"timing {label}: {args.warmup} warmup + {args.steps} steps")
     ms, wall = time_launches(step, args.steps, args.warmup, stream)
     flops = rf.flops(w.M, w.N, w.K)
@@ -227,6 +380,7 @@ def main() -> int:
             "model_issued_load_bytes_per_launch": 4 * rf.issued_load_elements(
                 args.variant, w.M, w.N, w.K, tile),
         },
+        "settle": {"calls": n_settle, "ms": round(t_settle * 1e3, 1)},
         "wall_s_timed_region": round(wall, 4),
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    **g.gemm_f32_device_props(0)},
@@ -243,47 +397,42 @@ def main() -> int:
         log(f"fp32 MFMA probe: {pm:.1f} TFLOP/s")
         pv = measure_valu(g, stream)
         log(f"fp32 vector FMA probe: {pv:.1f} TFLOP/s")
+        fused = measure_fused(g, stream, args.record_settle_ms)
+        log(f"fused MFMA + store probe at 32 FLOP/B: {fused}")
         measured = {"hbm_gbps": hbm, "mfma_fp32_tflops": round(pm, 2),
-                    "valu_fp32_tflops": round(pv, 2)}
+                    "valu_fp32_tflops": round(pv, 2), "fused_k64": fused}
         result["measured_peaks"] = measured
         result["roofline"]["frac_of_measured_mfma"] = round(tflops / pm, 4)
 
-    if not args.no_skinny:
-        sw, sa, sb = make_workload("skinny_k64")
-        sta, stb = torch.from_numpy(sa).to(dev), torch.from_numpy(sb).to(dev)
-        stc = torch.empty((sw.M, sw.N), dtype=torch.float32, device=dev)
-        slabel = g.config_name("prod", -1, sw.M, sw.N, sw.K)
-
-        def sstep():
-            g.gemm_f32_ex(sw.M, sw.N, sw.K, sta.data_ptr(), sw.K, stb.data_ptr(), sw.N,
-                          stc.data_ptr(), sw.N, "prod", -1, s)
-
-        sms, _ = time_launches(sstep, args.skinny_steps, args.skinny_warmup, stream)
-        sbytes = rf.compulsory_bytes(sw.M, sw.N, sw.K)
-        gbps = sbytes / (sms * 1e-3) / 1e9
-        stf = rf.flops(sw.M, sw.N, sw.K) / (sms * 1e-3) / 1e12
-        log(f"skinny {slabel}: {sms:.4f} ms, {gbps:.0f} GB/s, {stf:.1f} TFLOP/s")
-        sk = {"workload": sw.name, "M": sw.M, "N": sw.N, "K": sw.K, "kernel": slabel,
-              "ms_per_launch": round(sms, 5), "gbps": round(gbps, 1),
-              "frac_of_peak_hbm": round(gbps / rf.PEAK_HBM_GBPS, 4),
-              "tflops": round(stf, 3), "frac_of_peak_fp32": round(stf / rf.PEAK_FP32_MFMA_TFLOPS, 4),
-              "intensity_flop_per_byte": round(rf.intensity(sw.M, sw.N, sw.K), 2)}
+    if not args.no_records:
+        records = {}
+        for name in WORKLOADS:
+            records[name] = workload_record(g, rf, name, stream, args.record_settle_ms, measured)
+        result["workloads"] = records
+        sk = dict(records["skinny_k64"])
+        sk.pop("verdict", None)
+        gbps = sk["gbps"]
+        sk["frac_of_peak_hbm"] = round(gbps / rf.PEAK_HBM_GBPS, 4)
         if measured:
             bmeas = measured["hbm_gbps"]["best"]
-            pmeas = measured["mfma_fp32_tflops"]
-            roof = rf.binding_roof_tflops(sw.M, sw.N, sw.K, pmeas, bmeas)
             sk["frac_of_measured_hbm"] = round(gbps / bmeas, 4)
-            sk["binding_roof_tflops"] = round(roof, 2)
-            sk["binding_roof"] = "mfma" if pmeas <= rf.intensity(sw.M, sw.N, sw.K) * bmeas / 1000 else "hbm"
-            sk["frac_of_binding_roof"] = round(stf / roof, 4)
+            sk["target_tflops_at_80pct_hbm"] = round(0.8 * bmeas * sk["intensity_flop_per_byte"] / 1000, 2)
+            fz = measured["fused_k64"]["best_both_tflops"]
+            sk["fused_probe_tflops"] = fz
+            sk["frac_of_fused_probe"] = round(sk["tflops"] / fz, 4)
+            sk["target_feasible_by_fused_probe"] = fz >= sk["target_tflops_at_80pct_hbm"]
+        sk["verdict_pass"] = records["skinny_k64"]["verdict"]["pass"]
         result["skinny_k64"] = sk
-        del sta, stb, stc
-        torch.cuda.empty_cache()
-
-    if not args.no_cpu_baseline:
-        log(f"CPU oracle baseline (~{args.cpu_seconds:.0f} s sample)")
-        result["cpu_baseline"] = cpu_baseline(a, b, args.cpu_seconds)
-        log(f"cpu baseline: {result['cpu_baseline']}")
+        c3 = records.get(w.name)
+        if c3 is not None:
+            o = c3["oracle"]
+            result["cpu_baseline"] = {
+                "value": round(flops / o["seconds"] / 1e12, 5), "unit": "TFLOP/s",
+                "cores": o["cores"], "kind": "oracle",
+                "sample": f"the whole {w.M}x{w.N}x{w.K} product ({w.M * w.N} outputs, full K), "
+                          f"{o['seconds']:.2f} s wall",
+                "seconds": o["seconds"], "cpu_model": o["cpu_model"]}
+        result["all_verdicts_pass"] = all(r["verdict"]["pass"] for r in records.values())
     else:
         result["cpu_baseline"] = None
 

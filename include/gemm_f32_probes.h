@@ -72,6 +72,44 @@ int gemm_f32_probe_lds(int workgroups, int iters, float *out, void *stream);
 long long gemm_f32_probe_lds_bytes(int workgroups, int iters);
 
 /*
+ * gemm_f32_probe_fused -- the hardware's rate at the intensity of the skinny
+ * K = 64 product, where the output is most of the traffic.  The pages bound
+ * a kernel by the lower of its compute roof and intensity x bandwidth
+ * (mayulu.co "CUDA 编程系列之三", sections 2-3); this probe measures what the
+ * part sustains when both kinds of work run together at one fixed ratio:
+ * `workgroups` workgroups of 256 threads (4 waves), each wave running `trips`
+ * rounds of 16 independent v_mfma_f32_16x16x4_f32 (32768 FLOP) followed by
+ * one 128-bit store per lane (1 KB), i.e. 32 FLOP per stored byte, which is
+ * K / 2 for K = 64.  With 256 workgroups and 1024 trips it does the FLOPs of
+ * a 16384 x 16384 x 64 product and writes its 1 GiB of output.
+ *   mode     GEMM_F32_FUSED_BOTH, _MFMA (no stores in the loop) or _STORE
+ *            (no MFMAs).
+ *   out      device buffer of at least gemm_f32_probe_fused_bytes(mode,
+ *            workgroups, trips) bytes, 16-byte aligned; out_bytes its size.
+ *            Round t of all waves writes one contiguous run of
+ *            workgroups * 4 KB.  After its loop each wave writes one more
+ *            KB, the sum of its chains, into round 0's run (all the
+ *            MFMA-only mode writes), so no MFMA result goes unused.
+ *   clocks   NULL, or 8-byte aligned device memory for 2 * workgroups * 4
+ *            values: per wave, shader-clock cycles (s_memtime) and constant
+ *            100 MHz real-time ticks (s_memrealtime) over its loop; cycles x
+ *            100 MHz / ticks is the engine clock under that load.
+ * workgroups >= 1, trips a positive multiple of 16 (round j of each group of
+ * 16 stores chain j, so every chain's result is used).  Returns
+ * GEMM_F32_BAD_ARG for an unknown mode,
+ * bad counts or a short buffer, GEMM_F32_NULL_PTR / GEMM_F32_MISALIGNED for
+ * bad pointers.  gemm_f32_probe_fused_flops and _bytes give the FLOPs and the
+ * bytes stored by such a call (-1 for invalid arguments).
+ */
+#define GEMM_F32_FUSED_BOTH 0
+#define GEMM_F32_FUSED_MFMA 1
+#define GEMM_F32_FUSED_STORE 2
+int gemm_f32_probe_fused(int mode, int workgroups, int trips, float *out, long long out_bytes,
+                         unsigned long long *clocks, void *stream);
+long long gemm_f32_probe_fused_flops(int mode, int workgroups, int trips);
+long long gemm_f32_probe_fused_bytes(int mode, int workgroups, int trips);
+
+/*
  * gemm_f32_device_props -- properties of HIP device `device` that the
  * roofline report quotes: compute units, peak engine clock (kHz), LDS bytes
  * per compute unit, wave size and L2 bytes.  Any output pointer may be NULL.

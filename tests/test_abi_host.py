@@ -33,6 +33,7 @@ def test_headers_declare_expected_entry_points():
             "gemm_f32_status_string", "gemm_f32_version", "gemm_f32_probe_stream",
             "gemm_f32_probe_mfma", "gemm_f32_probe_mfma_flops", "gemm_f32_probe_valu",
             "gemm_f32_probe_valu_flops", "gemm_f32_probe_lds", "gemm_f32_probe_lds_bytes",
+            "gemm_f32_probe_fused", "gemm_f32_probe_fused_flops", "gemm_f32_probe_fused_bytes",
             "gemm_f32_device_props", "gemm_mixed", "gemm_mixed_num_configs", "gemm_mixed_tile", "gemm_f32_splitk",
             "gemm_f32_splitk_plan"} <= names
 
@@ -216,6 +217,21 @@ def test_probe_validation():
     assert lib.gemm_f32_probe_lds(0, 1, 256, None) == 8
     assert lib.gemm_f32_probe_lds(1, 1, None, None) == 3
     assert g.gemm_f32_probe_lds_bytes(2, 3) == 2 * 256 * 3 * 8 * 16
+    # fused probe: 16 MFMAs of 2048 FLOP and one 1 KB store per wave and round
+    assert g.gemm_f32_probe_fused_flops(g.FUSED_BOTH, 256, 1024) == 2 * 16384 * 16384 * 64
+    assert g.gemm_f32_probe_fused_bytes(g.FUSED_BOTH, 256, 1024) == 16384 * 16384 * 4
+    assert g.gemm_f32_probe_fused_flops(g.FUSED_STORE, 2, 16) == 0
+    assert g.gemm_f32_probe_fused_bytes(g.FUSED_MFMA, 2, 32) == 2 * 4 * 1024
+    assert g.gemm_f32_probe_fused_flops(g.FUSED_MFMA, 2, 32) == 2 * 4 * 32 * 16 * 2048
+    for bad in ((3, 1, 16), (-1, 1, 16), (0, 0, 16), (0, 1, 0), (0, 1, 24)):
+        assert g.gemm_f32_probe_fused_flops(*bad) == -1
+        assert g.gemm_f32_probe_fused_bytes(*bad) == -1
+        assert lib.gemm_f32_probe_fused(*bad, 256, 1 << 30, None, None) == 8
+    need = g.gemm_f32_probe_fused_bytes(0, 1, 16)
+    assert lib.gemm_f32_probe_fused(0, 1, 16, None, need, None, None) == 3
+    assert lib.gemm_f32_probe_fused(0, 1, 16, 256 + 4, need, None, None) == 6
+    assert lib.gemm_f32_probe_fused(0, 1, 16, 256, need, 256 + 4, None) == 6
+    assert lib.gemm_f32_probe_fused(0, 1, 16, 256, need - 16, None, None) == 8
 
 
 def test_tile_queries():

@@ -482,10 +482,7 @@ def test_all_ones_full_ragged_shape(g, variant):
     (a property that holds at any size; every edge tile is exercised)."""
     w = WORKLOADS["ragged"]
     dev = _dev()
-    if variant == "naive":
-        M, N, K = 1025, 1023, 2049  # the naive rung is slow; same remainders
-    else:
-        M, N, K = w.M, w.N, w.K
+    M, N, K = w.M, w.N, w.K
     c = g.matmul(torch.ones((M, K), device=dev), torch.ones((K, N), device=dev), variant=variant)
     torch.cuda.synchronize()
     assert torch.all(c == float(K)).item()
@@ -556,6 +553,28 @@ def test_lds_probe_runs(g):
     g.gemm_f32_probe_lds(8, 10, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert torch.isfinite(out).all().item() and torch.all(out >= 0).item()
+
+
+def test_fused_probe_runs_and_reports_clock(g):
+    """Each mode writes what it promises (every 1 KB run of the fused and
+    store-only modes; one KB per wave for MFMA-only) and reports a plausible
+    engine clock from its shader-clock and real-time counters."""
+    dev = _dev()
+    wgs, trips = 8, 32
+    for mode in (g.FUSED_BOTH, g.FUSED_MFMA, g.FUSED_STORE):
+        nbytes = g.gemm_f32_probe_fused_bytes(mode, wgs, trips)
+        out = torch.full((nbytes // 4 + 64,), -5.0, device=dev)
+        clocks = torch.zeros(2 * wgs * 4, dtype=torch.int64, device=dev)
+        g.gemm_f32_probe_fused(mode, wgs, trips, out.data_ptr(), nbytes, clocks.data_ptr(),
+                               torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        body = out[: nbytes // 4]
+        assert torch.isfinite(body).all().item() and not torch.any(body == -5.0).item(), mode
+        assert torch.all(out[nbytes // 4:] == -5.0).item(), mode  # nothing past the buffer
+        c = clocks.view(-1, 2).double()
+        assert torch.all(c > 0).item(), mode
+        mhz = (c[:, 0] / c[:, 1] * 100.0)
+        assert torch.all((mhz > 300) & (mhz < 3500)).item(), (mode, mhz.tolist()[:4])
 
 
 def test_device_props(g):

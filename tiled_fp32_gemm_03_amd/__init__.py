@@ -13,6 +13,8 @@ Raw C-ABI mirrors (same names and argument order as ``include/gemm_f32.h``):
   gemm_f32_probe_mfma(workgroups, iters, out, stream), gemm_f32_probe_mfma_flops(...)
   gemm_f32_probe_valu(workgroups, iters, out, stream), gemm_f32_probe_valu_flops(...)
   gemm_f32_probe_lds(workgroups, iters, out, stream), gemm_f32_probe_lds_bytes(...)
+  gemm_f32_probe_fused(mode, workgroups, trips, out, out_bytes, clocks, stream),
+  gemm_f32_probe_fused_flops(mode, ...), gemm_f32_probe_fused_bytes(mode, ...)
   gemm_f32_device_props(device) -> dict
   gemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, config, splits, workspace,
                   workspace_bytes, stream), gemm_f32_splitk_plan(M, N, K, config, splits)
@@ -42,6 +44,8 @@ __all__ = [
     "gemm_f32_status_string", "gemm_f32_version", "gemm_f32_last_error", "gemm_f32_probe_stream",
     "gemm_f32_probe_mfma", "gemm_f32_probe_mfma_flops", "gemm_f32_probe_valu",
     "gemm_f32_probe_valu_flops", "gemm_f32_probe_lds", "gemm_f32_probe_lds_bytes",
+    "gemm_f32_probe_fused", "gemm_f32_probe_fused_flops", "gemm_f32_probe_fused_bytes",
+    "FUSED_BOTH", "FUSED_MFMA", "FUSED_STORE",
     "gemm_f32_device_props", "matmul",
     "gemm_f32_splitk", "gemm_f32_splitk_plan", "matmul_splitk",
     "gemm_mixed", "gemm_mixed_tile", "gemm_mixed_num_configs", "matmul_mixed", "MIXED_FORMATS",
@@ -92,6 +96,9 @@ _SIGS = {
     "gemm_mixed_tile": ([_i, _i, _i, _i, _ip, _ip, _ip, _ip, _ip], _i),
     "gemm_f32_probe_lds_bytes": ([_i, _i], _ll),
     "gemm_f32_device_props": ([_i, _ip, _ip, _ip, _ip, _ip], _i),
+    "gemm_f32_probe_fused": ([_i, _i, _i, _p, _ll, _p, _p], _i),
+    "gemm_f32_probe_fused_flops": ([_i, _i, _i], _ll),
+    "gemm_f32_probe_fused_bytes": ([_i, _i, _i], _ll),
 }
 for _name, (_args, _ret) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -102,6 +109,7 @@ for _name, (_args, _ret) in _SIGS.items():
 VARIANTS = {"naive": 0, "tiled": 1, "prod": 2, "tiled32": 3, "tiled4": 4, "tiled32_pad": 5,
             "valu": 6}
 PROBE_COPY, PROBE_FILL, PROBE_VADD = 0, 1, 2
+FUSED_BOTH, FUSED_MFMA, FUSED_STORE = 0, 1, 2
 # Input formats of include/gemm_mixed.h.
 MIXED_FORMATS = {"bf16": 0, "f16": 1}
 
@@ -202,6 +210,20 @@ def gemm_f32_probe_lds(workgroups, iters, out, stream=0) -> None:
 
 def gemm_f32_probe_lds_bytes(workgroups, iters) -> int:
     return int(_lib.gemm_f32_probe_lds_bytes(int(workgroups), int(iters)))
+
+
+def gemm_f32_probe_fused(mode, workgroups, trips, out, out_bytes, clocks=0, stream=0) -> None:
+    _check(_lib.gemm_f32_probe_fused(int(mode), int(workgroups), int(trips), out or None,
+                                     int(out_bytes), clocks or None, stream or None),
+           "gemm_f32_probe_fused")
+
+
+def gemm_f32_probe_fused_flops(mode, workgroups, trips) -> int:
+    return int(_lib.gemm_f32_probe_fused_flops(int(mode), int(workgroups), int(trips)))
+
+
+def gemm_f32_probe_fused_bytes(mode, workgroups, trips) -> int:
+    return int(_lib.gemm_f32_probe_fused_bytes(int(mode), int(workgroups), int(trips)))
 
 
 def gemm_f32_device_props(device: int = 0) -> dict:

@@ -64,7 +64,7 @@ struct MixedConfig {
 
 // The 16x16x32-MFMA kernel with direct loads (mixed16.hip): whether it
 // takes the product (16-byte aligned rows of A and B, N % 8 == 0, C at least
-// 256 x 256, K a positive multiple of 64, leading dimensions below 2^24),
+// 256 x 256, K a positive multiple of 64, 32-bit lane offsets: lane_offsets_fit),
 // and its launch.
 bool mixed16_fits(const MixedProblem &p);
 hipError_t launch_mixed16(int format, const MixedProblem &p, hipStream_t s);
@@ -77,8 +77,8 @@ hipError_t launch_zero_f32(float *C, int M, int N, long long ldc, hipStream_t s)
 
 // The 192x192, 192x256 and 128x128 direct-load kernels (w16_vgpr.hip): whether each
 // takes the product (16-byte aligned rows of A and B, N % 4 == 0, C at
-// least one tile each way, K a positive multiple of 32, leading dimensions
-// below 2^24), and its launch.
+// least one tile each way, K a positive multiple of 32, 32-bit lane offsets:
+// lane_offsets_fit), and its launch.
 bool big16_192_fits(const Problem &p);
 hipError_t launch_big16_192(const Problem &p, hipStream_t s);
 bool big16_192x256_fits(const Problem &p);

@@ -88,7 +88,8 @@ __device__ inline i16x8 m16_read_b(const char *st, int wn, int bn, int kg, int l
 
 // The launcher guarantees M >= 256, N >= 256 (tiles moved inside C at the
 // edges), K a positive multiple of 64, N % 8 == 0, 16-byte aligned rows of
-// A and B, and leading dimensions below 2^24 elements.
+// A and B, and 32-bit lane offsets (lane_offsets_fit over 256 rows of A and
+// 64 rows of B).
 template <int FMT>
 __global__ void __launch_bounds__(256) mixed16_kernel(MixedProblem p, int tiles_m, int tiles_n) {
   using W = M16;
@@ -253,7 +254,7 @@ bool mixed16_fits(const MixedProblem &p) {
   return (reinterpret_cast<uintptr_t>(p.A) & 15) == 0 &&
          (reinterpret_cast<uintptr_t>(p.B) & 15) == 0 && (p.lda & 7) == 0 && (p.ldb & 7) == 0 &&
          (p.N & 7) == 0 && p.M >= M16::BM && p.N >= M16::BN && p.K > 0 && p.K % M16::BK == 0 &&
-         p.lda < (1 << 24) && p.ldb < (1 << 24);
+         lane_offsets_fit(M16::BM, p.lda, 2) && lane_offsets_fit(M16::BK, p.ldb, 2);
 }
 
 hipError_t launch_mixed16(int format, const MixedProblem &p, hipStream_t s) {

@@ -128,6 +128,69 @@ __global__ void __launch_bounds__(kLdsThreads) lds_probe_kernel(int iters, float
   if ((tid & 63) == 0) out[blockIdx.x * (kLdsThreads / 64) + (tid >> 6)] = s;
 }
 
+// Matrix-core work and C-sized stores at the ratio of a K = 64 product:
+// each wave runs `trips` rounds of 16 independent v_mfma_f32_16x16x4_f32
+// (16 x 2048 FLOP) followed by one 128-bit store per lane (1 KB per wave),
+// i.e. 32 FLOP per stored byte, the intensity K / 2 of a product whose time
+// is its output.  The stores of round t from all waves fill one contiguous
+// run of waves KB, so the output is written once, front to back.  MODE 1
+// drops the stores (the matrix work alone), MODE 2 drops the MFMAs (the
+// stores alone).  Each wave also reports its shader-clock cycles
+// (s_memtime) and its constant 100 MHz real-time ticks (s_memrealtime) over
+// the loop: their ratio is the engine clock while the probe ran.
+constexpr int kFusedThreads = 256;
+constexpr int kFusedChains = 16;  // MFMAs per store
+
+template <int MODE>
+__global__ void __launch_bounds__(kFusedThreads)
+    fused_probe_kernel(int trips, f32x4 *__restrict__ out, unsigned long long *__restrict__ clocks) {
+  const int lane = threadIdx.x & 63;
+  const long long wave = (long long)blockIdx.x * (kFusedThreads / 64) + (threadIdx.x >> 6);
+  const long long waves = (long long)gridDim.x * (kFusedThreads / 64);
+  const float a = 1.0f + lane * 1e-3f;
+  const float b = 1.0f - lane * 1e-3f;
+  f32x4 acc[kFusedChains];
+#pragma unroll
+  for (int c = 0; c < kFusedChains; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  // Rounds in groups of kFusedChains: round j of a group first stores chain
+  // j (its last MFMA is 16 MFMAs back, so the store does not wait for it),
+  // then issues one MFMA per chain; every chain's result is used
+  // (trips % kFusedChains == 0).  The scheduling barriers keep one store
+  // per 16 MFMAs instead of letting the compiler gather the stores.
+  for (int t0r = 0; t0r < trips; t0r += kFusedChains) {
+#pragma unroll
+    for (int j = 0; j < kFusedChains; ++j) {
+      const long long t = t0r + j;
+      if constexpr (MODE == 0) {
+        out[(t * waves + wave) * 64 + lane] = acc[j];
+      } else if constexpr (MODE == 2) {
+        out[(t * waves + wave) * 64 + lane] = f32x4{1.f, 1.f, 1.f, (float)t};
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (MODE != 2) {
+#pragma unroll
+        for (int c = 0; c < kFusedChains; ++c)
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[c], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+  if constexpr (MODE != 2) {  // keep the last round's matrix work live
+    f32x4 s = acc[0];
+#pragma unroll
+    for (int c = 1; c < kFusedChains; ++c) s += acc[c];
+    out[wave * 64 + lane] = s;
+  }
+  if (clocks != nullptr && lane == 0) {
+    clocks[2 * wave] = t1 - t0;
+    clocks[2 * wave + 1] = r1 - r0;
+  }
+}
+
 bool misaligned16(const void *p) {
   return (reinterpret_cast<std::uintptr_t>(p) & 15u) != 0;
 }
@@ -221,6 +284,54 @@ extern "C" int gemm_f32_probe_lds(int workgroups, int iters, float *out, void *s
   if (reinterpret_cast<std::uintptr_t>(out) & 3u) return GEMM_F32_MISALIGNED;
   hipError_t e = launch_kernel(lds_probe_kernel, dim3(workgroups), dim3(kLdsThreads),
                                static_cast<hipStream_t>(stream), iters, out);
+  return e == hipSuccess ? GEMM_F32_OK : GEMM_F32_LAUNCH_FAILED;
+}
+
+extern "C" long long gemm_f32_probe_fused_flops(int mode, int workgroups, int trips) {
+  if (mode < GEMM_F32_FUSED_BOTH || mode > GEMM_F32_FUSED_STORE || workgroups < 1 || trips < 1 ||
+      trips % kFusedChains != 0)
+    return -1;
+  if (mode == GEMM_F32_FUSED_STORE) return 0;
+  return (long long)workgroups * (kFusedThreads / 64) * (long long)trips * kFusedChains *
+         (2LL * 16 * 16 * 4);
+}
+
+extern "C" long long gemm_f32_probe_fused_bytes(int mode, int workgroups, int trips) {
+  if (mode < GEMM_F32_FUSED_BOTH || mode > GEMM_F32_FUSED_STORE || workgroups < 1 || trips < 1 ||
+      trips % kFusedChains != 0)
+    return -1;
+  const long long per_round = (long long)workgroups * (kFusedThreads / 64) * 1024;
+  // MFMA-only mode stores one KB per wave at the end; the fused mode stores
+  // that last KB into round 0's run again (after its loop)
+  return mode == GEMM_F32_FUSED_MFMA ? per_round : per_round * trips;
+}
+
+extern "C" int gemm_f32_probe_fused(int mode, int workgroups, int trips, float *out,
+                                    long long out_bytes, unsigned long long *clocks,
+                                    void *stream) {
+  const long long need = gemm_f32_probe_fused_bytes(mode, workgroups, trips);
+  if (need < 0) return GEMM_F32_BAD_ARG;
+  if (out == nullptr) return GEMM_F32_NULL_PTR;
+  if (misaligned16(out) || (reinterpret_cast<std::uintptr_t>(clocks) & 7u))
+    return GEMM_F32_MISALIGNED;
+  if (out_bytes < need) return GEMM_F32_BAD_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  f32x4 *o = reinterpret_cast<f32x4 *>(out);
+  hipError_t e;
+  switch (mode) {
+    case GEMM_F32_FUSED_BOTH:
+      e = launch_kernel(fused_probe_kernel<0>, dim3(workgroups), dim3(kFusedThreads), s, trips, o,
+                        clocks);
+      break;
+    case GEMM_F32_FUSED_MFMA:
+      e = launch_kernel(fused_probe_kernel<1>, dim3(workgroups), dim3(kFusedThreads), s, trips, o,
+                        clocks);
+      break;
+    default:
+      e = launch_kernel(fused_probe_kernel<2>, dim3(workgroups), dim3(kFusedThreads), s, trips, o,
+                        clocks);
+      break;
+  }
   return e == hipSuccess ? GEMM_F32_OK : GEMM_F32_LAUNCH_FAILED;
 }
 

@@ -958,8 +958,8 @@ __device__ inline void ks_mfma(f32x4 (&acc)[4][4], const KsFrag &f, const unsign
 }
 
 // The launcher guarantees M, N >= 64 (every tile lies inside C after the
-// edge shift), N % 4 == 0, 16-byte aligned rows of A and B, and leading
-// dimensions below 2^24 (the per-lane byte offsets fit in 32 bits).
+// edge shift), N % 4 == 0, 16-byte aligned rows of A and B, and per-lane
+// byte offsets that fit in 32 bits (lane_offsets_fit over 64 rows of each).
 __global__ void __launch_bounds__(256) ksplit_kernel(Problem p, int tiles_m, int tiles_n) {
   static_assert((kKsStages * kKsStageFloats + kKsRedFloats) * 4 <= kLdsBytes, "LDS budget");
   __shared__ __attribute__((aligned(16))) float lds[kKsStages * kKsStageFloats + kKsRedFloats];
@@ -1196,8 +1196,9 @@ __device__ inline void w16_mfma(f32x4 (&acc)[W::TBM][W::TBN], const W16Frag<W> &
 }
 
 // The launcher guarantees M >= BM, N >= BN (every tile lies inside C after
-// the edge shift), N % 4 == 0, 16-byte aligned rows of A and B, and leading
-// dimensions below 2^24.
+// the edge shift), N % 4 == 0, 16-byte aligned rows of A and B, and per-lane
+// byte offsets that fit in 32 bits (lane_offsets_fit over BM rows of A and
+// BK rows of B).
 template <class W>
 __global__ void __launch_bounds__(256) w16_kernel(Problem p, int tiles_m, int tiles_n) {
   using T = W16Staging<W>;
@@ -1782,8 +1783,8 @@ __global__ void __launch_bounds__(S::NT)
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / S::WGN, wn = wave % S::WGN;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int panel = lid / chunks, chunk = lid % chunks;
-  if (panel >= panels) return;  // uniform per workgroup
+  const int panel = lid % panels, chunk = lid / panels;
+  if (chunk >= chunks) return;  // uniform per workgroup
   const int t0 = (int)((long long)chunk * tiles_n / chunks);
   const int t1 = (int)((long long)(chunk + 1) * tiles_n / chunks);
   const int n = t1 - t0;  // >= 1: the launcher keeps chunks <= tiles_n
@@ -2000,9 +2001,14 @@ __device__ __forceinline__ void arow16_tile(Acc16 &acc, Acc16 &prev, const Probl
 
 // Workgroup (panel, chunk) owns rows [256 panel, +256) and the column tiles
 // [t0, t1) of that panel, walked from a rotated start as in
-// panel_arow_kernel.  The launcher guarantees K == 64, M % 256 == 0,
-// N % 128 == 0, 16-byte aligned rows of A and B and leading dimensions
-// below 2^24.
+// panel_arow_kernel.  Logical ids run panel-fastest, so the run of ids that
+// xcd_remap gives one XCD shares one chunk of B (two chunks where a run
+// straddles a boundary): with 64 panels and 4 chunks on 8 XCDs, each XCD
+// streams a 1 MB chunk of B through its 4 MB L2 instead of all 4 MB.  The
+// rotation keeps the 32 workgroups of one chunk on 32 different column
+// tiles at any moment.  The launcher guarantees K == 64, M % 256 == 0,
+// N % 128 == 0, 16-byte aligned rows of A and B and byte offsets below 2^32
+// (rows of 256 A rows and 64 B rows).
 __global__ void __launch_bounds__(256) arow16_kernel(Problem p, int panels, int chunks,
                                                      int tiles_n) {
   using W = Arow16;
@@ -2013,8 +2019,8 @@ __global__ void __launch_bounds__(256) arow16_kernel(Problem p, int panels, int 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int panel = lid / chunks, chunk = lid % chunks;
-  if (panel >= panels) return;  // uniform per workgroup
+  const int panel = lid % panels, chunk = lid / panels;
+  if (chunk >= chunks) return;  // uniform per workgroup
   const int t0 = (int)((long long)chunk * tiles_n / chunks);
   const int t1 = (int)((long long)(chunk + 1) * tiles_n / chunks);
   const int n = t1 - t0;  // >= 1: the launcher keeps chunks <= tiles_n
@@ -2224,13 +2230,13 @@ hipError_t launch_kloop(const Problem &p, hipStream_t s) {
 
 // K split over the waves of a 64x64 tile (ksplit_kernel) when A and B rows
 // are 16-byte aligned, N % 4 == 0, C is at least one tile each way and the
-// leading dimensions are below 2^24; otherwise the register-staged 64x64x32
+// lane offsets fit in 32 bits; otherwise the register-staged 64x64x32
 // kernel.
 hipError_t launch_ksplit(const Problem &p, hipStream_t s) {
   const bool ok = (reinterpret_cast<uintptr_t>(p.A) & 15) == 0 &&
                   (reinterpret_cast<uintptr_t>(p.B) & 15) == 0 && (p.lda & 3) == 0 &&
                   (p.ldb & 3) == 0 && (p.N & 3) == 0 && p.M >= 64 && p.N >= 64 &&
-                  p.lda < (1 << 24) && p.ldb < (1 << 24);
+                  lane_offsets_fit(64, p.lda, 4) && lane_offsets_fit(64, p.ldb, 4);
   if (!ok) return launch_kloop<C3>(p, s);
   const long long tiles_m = ceil_div(p.M, 64), tiles_n = ceil_div(p.N, 64);
   const long long ntiles = tiles_m * tiles_n;
@@ -2243,14 +2249,14 @@ hipError_t launch_ksplit(const Problem &p, hipStream_t s) {
 
 // One wave per SIMD with 16x16 MFMAs (w16_kernel) when A and B rows are
 // 16-byte aligned, N % 4 == 0, C is at least one tile each way and the
-// leading dimensions are below 2^24; otherwise the register-staged kernel
+// lane offsets fit in 32 bits; otherwise the register-staged kernel
 // FALLBACK.
 template <class W, class FALLBACK>
 hipError_t launch_w16(const Problem &p, hipStream_t s) {
   const bool ok = (reinterpret_cast<uintptr_t>(p.A) & 15) == 0 &&
                   (reinterpret_cast<uintptr_t>(p.B) & 15) == 0 && (p.lda & 3) == 0 &&
                   (p.ldb & 3) == 0 && (p.N & 3) == 0 && p.M >= W::BM && p.N >= W::BN &&
-                  p.lda < (1 << 24) && p.ldb < (1 << 24);
+                  lane_offsets_fit(W::BM, p.lda, 4) && lane_offsets_fit(W::BK, p.ldb, 4);
   if (!ok) return launch_kloop<FALLBACK>(p, s);
   const long long tiles_m = ceil_div(p.M, W::BM), tiles_n = ceil_div(p.N, W::BN);
   const long long ntiles = tiles_m * tiles_n;
@@ -2263,8 +2269,8 @@ hipError_t launch_w16(const Problem &p, hipStream_t s) {
 
 // The 128x128-wave kernel with direct loads (big16_kernel) when A and B
 // rows are 16-byte aligned, N % 4 == 0, K is a positive multiple of the k
-// step, C is at least one tile each way and the leading dimensions are below
-// 2^24; otherwise FALLBACK (for the 256x256 tiles, the same tiles staged
+// step, C is at least one tile each way and the lane offsets fit in 32
+// bits; otherwise FALLBACK (for the 256x256 tiles, the same tiles staged
 // through registers).
 using Launcher = hipError_t (*)(const Problem &, hipStream_t);
 template <class W, Launcher FALLBACK>
@@ -2361,20 +2367,22 @@ hipError_t launch_big16(const Problem &p, hipStream_t s) {
   const bool direct = (reinterpret_cast<uintptr_t>(p.A) & 15) == 0 &&
                       (reinterpret_cast<uintptr_t>(p.B) & 15) == 0 && (p.lda & 3) == 0 &&
                       (p.ldb & 3) == 0 && (p.N & 3) == 0 && p.M >= W::BM && p.N >= W::BN &&
-                      p.K > 0 && p.K % W::BK == 0 && p.lda < (1 << 24) && p.ldb < (1 << 24);
+                      p.K > 0 && p.K % W::BK == 0 && lane_offsets_fit(W::BM, p.lda, 4) &&
+                      lane_offsets_fit(W::BK, p.ldb, 4);
   if (!direct) return FALLBACK(p, s);
   return launch_big16_grid<W, big16_kernel<W>>(p, s);
 }
 
 // The A-resident kernel on 16x16 MFMAs (arow16_kernel) when K == 64, C is
-// whole 256x128 tiles, A and B rows are 16-byte aligned and the leading
-// dimensions are below 2^24; otherwise the 32x32-MFMA A-resident kernel.
+// whole 256x128 tiles, A and B rows are 16-byte aligned and the lane
+// offsets fit in 32 bits; otherwise the 32x32-MFMA A-resident kernel.
 hipError_t launch_arow16(const Problem &p, hipStream_t s) {
   using W = Arow16;
   const bool ok = p.K == W::BK && p.M % W::BM == 0 && p.N % W::BN == 0 && p.M > 0 && p.N > 0 &&
                   (reinterpret_cast<uintptr_t>(p.A) & 15) == 0 &&
                   (reinterpret_cast<uintptr_t>(p.B) & 15) == 0 && (p.lda & 3) == 0 &&
-                  (p.ldb & 3) == 0 && p.lda < (1 << 24) && p.ldb < (1 << 24);
+                  (p.ldb & 3) == 0 && lane_offsets_fit(W::BM, p.lda, 4) &&
+                  lane_offsets_fit(W::BK, p.ldb, 4);
   if (!ok) return launch_arow<P9>(p, s);
   const long long panels = p.M / W::BM, tiles_n = p.N / W::BN;
   if (panels * tiles_n > 0x7fffffffLL) return hipErrorInvalidValue;

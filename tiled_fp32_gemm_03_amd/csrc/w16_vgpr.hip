@@ -27,13 +27,13 @@ using W192x256 = W16<96, 128, 32, 2>;
 
 // Direct loads need 16-byte aligned rows of A and B and N % 4 == 0; the
 // kernel needs C at least one tile each way, K a positive multiple of the
-// step and leading dimensions below 2^24 (32-bit lane offsets).
+// step and 32-bit lane offsets for its A tile and B step (lane_offsets_fit).
 template <class W>
 bool direct_fits(const Problem &p) {
   return (reinterpret_cast<uintptr_t>(p.A) & 15) == 0 &&
          (reinterpret_cast<uintptr_t>(p.B) & 15) == 0 && (p.lda & 3) == 0 && (p.ldb & 3) == 0 &&
          (p.N & 3) == 0 && p.M >= W::BM && p.N >= W::BN && p.K > 0 && p.K % W::BK == 0 &&
-         p.lda < (1 << 24) && p.ldb < (1 << 24);
+         lane_offsets_fit(W::BM, p.lda, 4) && lane_offsets_fit(W::BK, p.ldb, 4);
 }
 
 }  // namespace
