@@ -22,8 +22,9 @@
  *
  * Memory and ownership: A, B and C are device pointers owned by the caller
  * (for example the storage of torch tensors).  The library allocates no
- * device memory, keeps no per-call state, and is re-entrant.  C must not
- * overlap A or B.
+ * device memory, keeps no per-call state, and is re-entrant, with one
+ * exception: gemm_f32_splitk_noalloc keeps its split-K slabs in a fixed
+ * device array of the library (see there).  C must not overlap A or B.
  *
  * Streams: `stream` is a hipStream_t passed as void*; NULL means the null
  * stream.  Calls are asynchronous: they return once the kernel is enqueued.
@@ -52,6 +53,8 @@ extern "C" {
 #define GEMM_F32_BAD_ARG 8       /* other invalid argument (query helpers)  */
 #define GEMM_F32_BAD_WORKSPACE 9 /* split-K workspace NULL, too small or not
                                     4-byte aligned                          */
+#define GEMM_F32_SCRATCH_TOO_SMALL 10 /* the plan's slabs exceed the fixed
+                                         scratch of gemm_f32_splitk_noalloc */
 
 /* ---- variants: the kernel ladder ------------------------------------ */
 /* One thread per output element, operands read straight from global
@@ -161,6 +164,33 @@ int gemm_f32_splitk(int M, int N, int K, const float *A, int lda,
                     const float *B, int ldb, float *C, int ldc, int config,
                     int splits, void *workspace, long long workspace_bytes,
                     void *stream);
+
+/*
+ * gemm_f32_splitk_noalloc -- gemm_f32_splitk for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid allocation): the slabs live in a fixed device array
+ * inside the library, GEMM_F32_NOALLOC_SCRATCH_BYTES per GPU, held from the
+ * first call on that GPU until the process ends.  The call allocates nothing
+ * (no hipMalloc, no hipFree, no allocating library routine); the caller
+ * still owns A, B and C.
+ *   Arguments as gemm_f32_splitk without the workspace; the plan is
+ *   gemm_f32_splitk_plan's for (M, N, K, config, splits), so the result is
+ *   bit for bit gemm_f32_splitk's with the same plan.
+ *   stream  hipStream_t of the current device (NULL = its null stream);
+ *           a stream of another device gives GEMM_F32_BAD_ARG.
+ * Returns GEMM_F32_SCRATCH_TOO_SMALL, before anything is launched, when the
+ * plan's workspace_bytes exceed GEMM_F32_NOALLOC_SCRATCH_BYTES (ask for
+ * fewer splits, or use gemm_f32_splitk with a workspace); otherwise the
+ * codes of gemm_f32_splitk.  Every call on one GPU shares that GPU's array
+ * and leaves the last call's slabs in it: calls whose executions overlap on
+ * one GPU (different streams, or host threads without ordering) race and
+ * give undefined results.  The first call on a GPU looks up the array's
+ * device address (hipGetSymbolAddress) with that GPU current.
+ */
+#define GEMM_F32_NOALLOC_SCRATCH_BYTES (64LL << 20)
+int gemm_f32_splitk_noalloc(int M, int N, int K, const float *A, int lda,
+                            const float *B, int ldb, float *C, int ldc, int config,
+                            int splits, void *stream);
 
 /* Number of launch-table entries of a variant (0 for an unknown variant). */
 int gemm_f32_num_configs(int variant);

@@ -45,6 +45,26 @@ def test_every_declared_symbol_is_exported():
         assert name in g.exported_symbols(), name
 
 
+def test_noalloc_validation_before_any_gpu_call():
+    """The no-allocation split-K entry checks its arguments and its plan's
+    size against the fixed scratch before it touches the GPU."""
+    lib = g._lib
+    f = lib.gemm_f32_splitk_noalloc
+    assert f(-1, 4, 4, None, 4, None, 4, None, 4, -1, 0, None) == 1
+    assert f(4, 4, 4, None, 3, None, 4, None, 4, -1, 0, None) == 2
+    assert f(4, 4, 4, None, 4, None, 4, None, 4, -1, -1, None) == 8
+    assert f(4, 4, 4, None, 4, None, 4, None, 4, 99, 0, None) == 7
+    assert f(4, 4, 4, None, 4, None, 4, None, 4, -1, 0, None) == 3
+    assert f(0, 4, 4, None, 4, None, 4, None, 4, -1, 0, None) == 0
+    plan = g.gemm_f32_splitk_plan(2048, 2048, 4096, 0, 8)
+    assert plan["workspace_bytes"] > g.NOALLOC_SCRATCH_BYTES
+    assert f(2048, 2048, 4096, 256, 4096, 256, 2048, 256, 2048, 0, 8, None) == 10
+    assert "scratch" in g.gemm_f32_status_string(10)
+    hdr = open(os.path.join(INCLUDE, "gemm_f32.h")).read()
+    m = re.search(r"#define GEMM_F32_NOALLOC_SCRATCH_BYTES \((\d+)LL << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == g.NOALLOC_SCRATCH_BYTES
+
+
 def test_version():
     assert "gfx950" in g.gemm_f32_version()
 

@@ -18,6 +18,7 @@ Raw C-ABI mirrors (same names and argument order as ``include/gemm_f32.h``):
   gemm_f32_device_props(device) -> dict
   gemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, config, splits, workspace,
                   workspace_bytes, stream), gemm_f32_splitk_plan(M, N, K, config, splits)
+  gemm_f32_splitk_noalloc(M, N, K, A, lda, B, ldb, C, ldc, config, splits, stream)
   gemm_mixed(M, N, K, A, lda, B, ldb, C, ldc, format, config, stream)
   gemm_mixed_tile(config, M, N, K) -> dict, gemm_mixed_num_configs()
                                                         (include/gemm_mixed.h)
@@ -47,7 +48,8 @@ __all__ = [
     "gemm_f32_probe_fused", "gemm_f32_probe_fused_flops", "gemm_f32_probe_fused_bytes",
     "FUSED_BOTH", "FUSED_MFMA", "FUSED_STORE",
     "gemm_f32_device_props", "matmul",
-    "gemm_f32_splitk", "gemm_f32_splitk_plan", "matmul_splitk",
+    "gemm_f32_splitk", "gemm_f32_splitk_plan", "matmul_splitk", "gemm_f32_splitk_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
     "gemm_mixed", "gemm_mixed_tile", "gemm_mixed_num_configs", "matmul_mixed", "MIXED_FORMATS",
     "mixed_config_name",
     "library_path",
@@ -91,6 +93,7 @@ _SIGS = {
     "gemm_f32_probe_lds": ([_i, _i, _p, _p], _i),
     "gemm_f32_splitk": ([_i, _i, _i, _p, _i, _p, _i, _p, _i, _i, _i, _p, _ll, _p], _i),
     "gemm_f32_splitk_plan": ([_i, _i, _i, _i, _i, _ip, _ip, _ip, ctypes.POINTER(_ll)], _i),
+    "gemm_f32_splitk_noalloc": ([_i, _i, _i, _p, _i, _p, _i, _p, _i, _i, _i, _p], _i),
     "gemm_mixed": ([_i, _i, _i, _p, _i, _p, _i, _p, _i, _i, _i, _p], _i),
     "gemm_mixed_num_configs": ([], _i),
     "gemm_mixed_tile": ([_i, _i, _i, _i, _ip, _ip, _ip, _ip, _ip], _i),
@@ -110,6 +113,9 @@ VARIANTS = {"naive": 0, "tiled": 1, "prod": 2, "tiled32": 3, "tiled4": 4, "tiled
             "valu": 6}
 PROBE_COPY, PROBE_FILL, PROBE_VADD = 0, 1, 2
 FUSED_BOTH, FUSED_MFMA, FUSED_STORE = 0, 1, 2
+# GEMM_F32_NOALLOC_SCRATCH_BYTES of include/gemm_f32.h: the fixed split-K
+# scratch of gemm_f32_splitk_noalloc on each GPU.
+NOALLOC_SCRATCH_BYTES = 64 << 20
 # Input formats of include/gemm_mixed.h.
 MIXED_FORMATS = {"bf16": 0, "f16": 1}
 
@@ -251,6 +257,13 @@ def gemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, config, splits, workspace,
                               int(config), int(splits), workspace or None, int(workspace_bytes),
                               stream or None)
     _check(rc, "gemm_f32_splitk")
+
+
+def gemm_f32_splitk_noalloc(M, N, K, A, lda, B, ldb, C, ldc, config=-1, splits=0,
+                            stream=0) -> None:
+    rc = _lib.gemm_f32_splitk_noalloc(M, N, K, A or None, lda, B or None, ldb, C or None, ldc,
+                                      int(config), int(splits), stream or None)
+    _check(rc, "gemm_f32_splitk_noalloc")
 
 
 def _format(fmt) -> int:

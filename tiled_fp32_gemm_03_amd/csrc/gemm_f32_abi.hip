@@ -7,6 +7,7 @@
 
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 
 using namespace gemm_f32_impl;
 
@@ -170,6 +171,77 @@ extern "C" int gemm_f32_splitk(int M, int N, int K, const float *A, int lda, con
   return launch_status(launch_prod_split(plan, p, static_cast<float *>(workspace), s), "splitk");
 }
 
+// ---- split-K without allocation ---------------------------------------------
+//
+// The slabs of the split-K path live in `scratch`, a file-scope device array
+// of GEMM_F32_NOALLOC_SCRATCH_BYTES on every GPU the library runs on (each
+// device holds its own copy until the process ends).  In host code the
+// array's name is not a device address: the address is taken once per
+// device with hipGetSymbolAddress, with that device current, and only that
+// pointer is handed to kernels.  Every call on one device shares its array;
+// the split kernels overwrite each slab element they later sum, so nothing
+// has to be cleared between calls, but calls that overlap in time on one
+// device race on it.
+
+namespace {
+
+constexpr long long kScratchBytes = GEMM_F32_NOALLOC_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) float scratch[kScratchBytes / 4];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float *g_scratch[kMaxDevices];  // per device, set once under g_scratch_mu
+
+// This device's copy of `scratch`, looked up on the device's first call.
+int scratch_for_device(int dev, float **out) {
+  if (dev < 0 || dev >= kMaxDevices) return GEMM_F32_BAD_ARG;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return launch_status(e != hipSuccess ? e : hipErrorInvalidSymbol, "scratch address");
+    g_scratch[dev] = static_cast<float *>(ptr);
+  }
+  *out = g_scratch[dev];
+  return GEMM_F32_OK;
+}
+
+}  // namespace
+
+extern "C" int gemm_f32_splitk_noalloc(int M, int N, int K, const float *A, int lda,
+                                       const float *B, int ldb, float *C, int ldc, int config,
+                                       int splits, void *stream) {
+  int rc = check_shape(M, N, K);
+  if (rc != GEMM_F32_OK) return rc;
+  if (lda < max1(K) || ldb < max1(N) || ldc < max1(N)) return GEMM_F32_INVALID_LD;
+  if (splits < 0) return GEMM_F32_BAD_ARG;
+  SplitPlan plan;
+  if (!splitk_plan(M, N, K, config, splits, &plan)) return GEMM_F32_BAD_CONFIG;
+  if (plan.workspace_bytes > kScratchBytes) return GEMM_F32_SCRATCH_TOO_SMALL;
+  if (M == 0 || N == 0) return GEMM_F32_OK;
+  if (C == nullptr) return GEMM_F32_NULL_PTR;
+  if (K > 0 && (A == nullptr || B == nullptr)) return GEMM_F32_NULL_PTR;
+  if (misaligned(C) || (K > 0 && (misaligned(A) || misaligned(B))))
+    return GEMM_F32_MISALIGNED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // The stream's device must be the current one: the scratch address is
+  // looked up with that device current.
+  int dev = -1, sdev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return GEMM_F32_BAD_ARG;
+  if (s != nullptr) {
+    if (hipStreamGetDevice(s, &sdev) != hipSuccess || sdev != dev) return GEMM_F32_BAD_ARG;
+  }
+  const Problem p{M, N, K, A, lda, B, ldb, C, ldc};
+  if (K == 0) return launch_status(launch_zero(p, s), "zero fill");
+  float *ws = nullptr;
+  if (plan.workspace_bytes > 0) {
+    rc = scratch_for_device(dev, &ws);
+    if (rc != GEMM_F32_OK) return rc;
+  }
+  return launch_status(launch_prod_split(plan, p, ws, s), "splitk noalloc");
+}
+
 // ---- 16-bit inputs ---------------------------------------------------------
 
 namespace {
@@ -245,6 +317,8 @@ extern "C" const char *gemm_f32_status_string(int status) {
     case GEMM_F32_BAD_ARG: return "invalid argument";
     case GEMM_F32_BAD_WORKSPACE:
       return "split-K workspace missing, smaller than the plan needs, or not 4-byte aligned";
+    case GEMM_F32_SCRATCH_TOO_SMALL:
+      return "the split-K plan needs more than the library's fixed scratch array holds";
     default: return "unknown status";
   }
 }
