@@ -172,22 +172,26 @@ def measure_fused(g, stream, settle_ms: float) -> dict:
     return res
 
 
-def load_traffic(workload: str, config_label: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, or None when
-    absent or taken on a different version of the production kernel."""
+def load_traffic(workload: str, config_label: str) -> dict:
+    """Bytes per launch from committed rocprofv3 counter runs: calibrated
+    FETCH_SIZE + WRITE_SIZE (L2 to fabric), the DRAM-bound request counts
+    scaled the same way, and their split; empty when absent or taken on a
+    different version of the production kernel."""
     try:
         with open(TRAFFIC_FILE) as f:
             data = json.load(f)
     except (OSError, ValueError):
-        return None
+        return {}
     from tiled_fp32_gemm_03_amd.counters import prod_source_digest
 
     rec = data.get(workload)
     if not rec or rec.get("prod_source_sha256_16") != prod_source_digest():
-        return None
+        return {}
     if rec.get("config") != config_label:
-        return None
-    return rec.get("hbm_bytes_per_launch")
+        return {}
+    keys = ("hbm_bytes_per_launch", "l2_fabric_read_bytes", "l2_fabric_write_bytes",
+            "dram_bytes_per_launch", "dram_read_bytes", "dram_write_bytes")
+    return {k: rec[k] for k in keys if k in rec}
 
 
 def cpu_model() -> str:
@@ -373,7 +377,8 @@ def main() -> int:
             "peak": rf.PEAK_FP32_MFMA_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops / rf.PEAK_FP32_MFMA_TFLOPS, 4),
-            "traffic": traffic,
+            "traffic": traffic.get("hbm_bytes_per_launch"),
+            "traffic_detail": traffic or None,
             "kernel": label,
             "algorithmic_flops_per_launch": flops,
             "compulsory_bytes_per_launch": rf.compulsory_bytes(w.M, w.N, w.K),
@@ -399,6 +404,11 @@ def main() -> int:
         log(f"fp32 vector FMA probe: {pv:.1f} TFLOP/s")
         fused = measure_fused(g, stream, args.record_settle_ms)
         log(f"fused MFMA + store probe at 32 FLOP/B: {fused}")
+        # The fused probe's store-only mode is a streaming write too: the
+        # measured bandwidth is the best of every streaming rate of the run.
+        hbm["fused_store_only"] = max(v["gbps"] for k, v in fused.items()
+                                      if k.startswith("store_only"))
+        hbm["best"] = max(hbm["copy"], hbm["fill"], hbm["vector_add"], hbm["fused_store_only"])
         measured = {"hbm_gbps": hbm, "mfma_fp32_tflops": round(pm, 2),
                     "valu_fp32_tflops": round(pv, 2), "fused_k64": fused}
         result["measured_peaks"] = measured

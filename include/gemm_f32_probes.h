@@ -80,7 +80,9 @@ long long gemm_f32_probe_lds_bytes(int workgroups, int iters);
  * `workgroups` workgroups of 256 threads (4 waves), each wave running `trips`
  * rounds of 16 independent v_mfma_f32_16x16x4_f32 (32768 FLOP) followed by
  * one 128-bit store per lane (1 KB), i.e. 32 FLOP per stored byte, which is
- * K / 2 for K = 64.  With 256 workgroups and 1024 trips it does the FLOPs of
+ * K / 2 for K = 64.  The MFMA operands are random values rotated through
+ * registers, so the matrix cores draw the power a product's operands make
+ * them draw (the clock under this load depends on it).  With 256 workgroups and 1024 trips it does the FLOPs of
  * a 16384 x 16384 x 64 product and writes its 1 GiB of output.
  *   mode     GEMM_F32_FUSED_BOTH, _MFMA (no stores in the loop) or _STORE
  *            (no MFMAs).

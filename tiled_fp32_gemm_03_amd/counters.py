@@ -21,11 +21,20 @@ Two subcommands, both reading CSV files that rocprofv3 wrote
          a product may take several launches).  Counters are summed per
          record.  The streaming copy
          probe that the ladder runs first (``--copy-mib``) moves a known
-         number of bytes each way; FETCH_SIZE and WRITE_SIZE are scaled by
-         known / counted on that probe to give HBM bytes per launch.  With
-         ``--traffic-out`` the production kernels' calibrated bytes are
+         number of bytes each way; FETCH_SIZE and WRITE_SIZE (L2 to fabric
+         traffic, which includes Infinity-Cache hits) and the DRAM-bound
+         request counts TCC_EA0_RDREQ_DRAM and TCC_EA0_WRREQ_DRAM are each
+         scaled by known / counted on that probe to give bytes per launch.
+         With ``--traffic-out`` the production kernels' calibrated bytes are
          written for the benchmark, stamped with a digest of the kernel
          source so that a changed kernel reports no stale traffic.
+
+  clock  --counters <..._counter_collection.csv> --trace <..._kernel_trace.csv>
+         --command "<profiled command>"
+         The engine clock under each kernel's own load: GRBM_GUI_ACTIVE
+         (busy cycles, summed over the XCDs) divided by the number of XCDs
+         and by the dispatch's duration from the kernel trace of the same
+         run (joined on the dispatch id), per kernel and grid.
 """
 from __future__ import annotations
 
@@ -47,7 +56,7 @@ PROD_SOURCES = [os.path.join(HERE, "csrc", n)
 # (file-local kernels of probes.hip), matched on the raw kernel name.
 OUR_NAMESPACE = "gemm_f32_impl"
 OUR_PROBES = re.compile(r"\b(stream_kernel|stream_tail|mfma_probe_kernel|valu_probe_kernel|"
-                        r"lds_probe_kernel)\b")
+                        r"lds_probe_kernel|fused_probe_kernel)\b")
 
 
 def is_ours(raw_name: str) -> bool:
@@ -139,6 +148,70 @@ def cmd_trace(args) -> int:
 
 
 MARKER = "stream_tail<1>"
+DRAM_RD = "TCC_EA0_RDREQ_DRAM_sum"
+DRAM_WR = "TCC_EA0_WRREQ_DRAM_sum"
+
+
+def _compulsory(rec) -> int:
+    """4 (MK + KN + MN) bytes (2-byte inputs for the 16-bit rungs), from the
+    record's workload; 0 when it names none."""
+    try:
+        from gemm_inputs import WORKLOADS
+    except ImportError:
+        sys.path.insert(0, os.path.dirname(HERE))
+        from gemm_inputs import WORKLOADS
+    w = WORKLOADS.get(rec.get("workload", ""))
+    if w is None:
+        return 0
+    elem = 2 if rec.get("variant") in ("bf16", "f16") else 4
+    return elem * (w.M * w.K + w.K * w.N) + 4 * w.M * w.N
+
+
+def cmd_clock(args) -> int:
+    """Engine clock per kernel under its own load: GRBM_GUI_ACTIVE per XCD
+    over the dispatch's duration."""
+    active = defaultdict(float)
+    meta = {}
+    with open(args.counters, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != "GRBM_GUI_ACTIVE" or not is_ours(row["Kernel_Name"]):
+                continue
+            did = int(row["Dispatch_Id"])
+            active[did] += float(row["Counter_Value"])
+            meta[did] = short_name(row["Kernel_Name"])
+    dur = {}
+    for r in _trace_rows([args.trace]):
+        did = int(r["Dispatch_Id"])
+        if did in active:
+            dur[did] = ((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0,
+                        _workgroups(r))
+    groups: dict = OrderedDict()
+    for did in sorted(active):
+        if did not in dur:
+            continue
+        us, wgs = dur[did]
+        if us <= 0:
+            continue
+        mhz = active[did] / args.xcds / us
+        groups.setdefault((meta[did], wgs), []).append((us, mhz))
+    lines = [f"# {args.title}", "", "Command:", "", "```", *args.command, "```", "",
+             f"Clock = GRBM_GUI_ACTIVE / {args.xcds} XCDs / dispatch duration (same run, joined on "
+             "the dispatch id). Medians over the dispatches of each kernel and grid.", "",
+             "| kernel | workgroups | dispatches | median us | median MHz | min MHz | max MHz |",
+             "|---|---|---|---|---|---|---|"]
+    for (name, wgs), vals in groups.items():
+        if len(vals) < args.min_dispatches:
+            continue
+        us = statistics.median(v[0] for v in vals)
+        mhz = [v[1] for v in vals]
+        lines.append(f"| `{name}` | {wgs} | {len(vals)} | {us:.1f} | {statistics.median(mhz):.0f} "
+                     f"| {min(mhz):.0f} | {max(mhz):.0f} |")
+    text = "\n".join(lines) + "\n"
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    print(text)
+    return 0
 
 
 def _segments(dispatches):
@@ -202,6 +275,8 @@ def cmd_pmc(args) -> int:
                                  f"{joined[i]['rec'].get('kernel')} in another")
             joined[i]["counters"].update(d["counters"])
 
+    # known / counted on the copy probe: KiB per KiB for FETCH_SIZE and
+    # WRITE_SIZE, bytes per request for the DRAM request counts
     cal = {}
     for j in joined:
         if j["rec"].get("kernel") == "probe_copy":
@@ -209,6 +284,9 @@ def cmd_pmc(args) -> int:
             for cname in ("FETCH_SIZE", "WRITE_SIZE"):
                 if cname in j["counters"] and j["counters"][cname] > 0:
                     cal[cname] = kib / j["counters"][cname]
+            for cname in (DRAM_RD, DRAM_WR):
+                if cname in j["counters"] and j["counters"][cname] > 0:
+                    cal[cname] = j["rec"]["bytes_read"] / j["counters"][cname]
 
     counters = sorted({c for j in joined for c in j["counters"]})
     lines = [f"# {args.title}", "", "Commands:", "", "```", *args.command, "```", ""]
@@ -220,6 +298,11 @@ def cmd_pmc(args) -> int:
         hdr.append("HBM read MB (cal.)")
     if "WRITE_SIZE" in counters:
         hdr.append("HBM write MB (cal.)")
+    if DRAM_RD in counters:
+        hdr.append("DRAM read MB (cal.)")
+    if DRAM_WR in counters:
+        hdr.append("DRAM write MB (cal.)")
+    hdr.append("compulsory MB")
     hdr.append("model issued-load MB")
     lines += ["| " + " | ".join(hdr) + " |", "|" + "---|" * len(hdr)]
     traffic = {}
@@ -233,16 +316,32 @@ def cmd_pmc(args) -> int:
             row.append(f"{rd / 1e6:.1f}")
         if "WRITE_SIZE" in counters:
             row.append(f"{wr / 1e6:.1f}")
-        row.append(f"{r['model_issued_load_bytes'] / 1e6:.1f}" if "model_issued_load_bytes" in r else "-")
+        drd = c.get(DRAM_RD, 0.0) * cal.get(DRAM_RD, 64.0)
+        dwr = c.get(DRAM_WR, 0.0) * cal.get(DRAM_WR, 64.0)
+        if DRAM_RD in counters:
+            row.append(f"{drd / 1e6:.1f}" if DRAM_RD in c else "-")
+        if DRAM_WR in counters:
+            row.append(f"{dwr / 1e6:.1f}" if DRAM_WR in c else "-")
+        comp = _compulsory(r)
+        row.append(f"{comp / 1e6:.1f}" if comp else "-")
+        row.append(f"{r['model_issued_load_bytes'] / 1e6:.1f}" if r.get("model_issued_load_bytes") else "-")
         lines.append("| " + " | ".join(row) + " |")
         if (r.get("variant") == "prod" and "FETCH_SIZE" in c and "WRITE_SIZE" in c
                 and "FETCH_SIZE" in cal and "WRITE_SIZE" in cal):
-            traffic[r["workload"]] = {
+            rec = {
                 "config": r["kernel"], "prod_source_sha256_16": prod_source_digest(),
                 "fetch_kib_counted": c["FETCH_SIZE"], "write_kib_counted": c["WRITE_SIZE"],
                 "fetch_scale": cal["FETCH_SIZE"], "write_scale": cal["WRITE_SIZE"],
-                "hbm_read_bytes": round(rd), "hbm_write_bytes": round(wr),
-                "hbm_bytes_per_launch": round(rd + wr)}
+                "l2_fabric_read_bytes": round(rd), "l2_fabric_write_bytes": round(wr),
+                "hbm_bytes_per_launch": round(rd + wr),
+                "compulsory_bytes": comp}
+            if DRAM_RD in c and DRAM_WR in c and DRAM_RD in cal and DRAM_WR in cal:
+                rec.update({"dram_rdreq_counted": c[DRAM_RD], "dram_wrreq_counted": c[DRAM_WR],
+                            "dram_read_bytes_per_request": cal[DRAM_RD],
+                            "dram_write_bytes_per_request": cal[DRAM_WR],
+                            "dram_read_bytes": round(drd), "dram_write_bytes": round(dwr),
+                            "dram_bytes_per_launch": round(drd + dwr)})
+            traffic[r["workload"]] = rec
     text = "\n".join(lines) + "\n"
     if args.out:
         with open(args.out, "w") as f:
@@ -254,9 +353,14 @@ def cmd_pmc(args) -> int:
             with open(args.traffic_out) as f:
                 old = json.load(f)
         old.update(traffic)
-        old["_about"] = ("HBM bytes per launch of the production kernel: rocprofv3 FETCH_SIZE and "
-                         "WRITE_SIZE (KiB per dispatch) scaled by the streaming copy probe's "
-                         "known/counted ratio; commands in the matching profiles/*.md summary.")
+        old["_about"] = ("Bytes per product of the production kernel's automatic entry. "
+                         "hbm_bytes_per_launch = l2_fabric_read_bytes + l2_fabric_write_bytes: "
+                         "rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by "
+                         "the streaming copy probe's known/counted ratio; this is traffic from "
+                         "L2 to the fabric and includes Infinity-Cache hits. dram_* = "
+                         "TCC_EA0_RDREQ_DRAM and TCC_EA0_WRREQ_DRAM request counts scaled by the "
+                         "copy probe's known bytes per counted request. Commands in the matching "
+                         "profiles/*.md summary.")
         with open(args.traffic_out, "w") as f:
             json.dump(old, f, indent=1, sort_keys=True)
             f.write("\n")
@@ -279,8 +383,16 @@ def main(argv=None) -> int:
     p.add_argument("--title", default="rocprofv3 counters")
     p.add_argument("--out")
     p.add_argument("--traffic-out")
+    c = sub.add_parser("clock")
+    c.add_argument("--counters", required=True)
+    c.add_argument("--trace", required=True)
+    c.add_argument("--command", action="append", default=[])
+    c.add_argument("--title", default="Engine clock under load")
+    c.add_argument("--xcds", type=int, default=8)
+    c.add_argument("--min-dispatches", type=int, default=5)
+    c.add_argument("--out")
     args = ap.parse_args(argv)
-    return cmd_trace(args) if args.cmd == "trace" else cmd_pmc(args)
+    return {"trace": cmd_trace, "pmc": cmd_pmc, "clock": cmd_clock}[args.cmd](args)
 
 
 if __name__ == "__main__":

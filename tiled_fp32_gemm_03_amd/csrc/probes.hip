@@ -138,6 +138,12 @@ __global__ void __launch_bounds__(kLdsThreads) lds_probe_kernel(int iters, float
 // stores alone).  Each wave also reports its shader-clock cycles
 // (s_memtime) and its constant 100 MHz real-time ticks (s_memrealtime) over
 // the loop: their ratio is the engine clock while the probe ran.
+// The MFMA operands are 16 + 16 registers of random values in +-[1, 2),
+// drawn once per lane and rotated at compile-time indices, so consecutive
+// MFMAs see different operands as a product's do: with constant operands
+// the matrix cores draw less power, and with the stores running the part
+// then holds a higher clock than a real product gets (2.37 against 2.32 GHz,
+// 0.249 against 0.257 ms per 16384 x 16384 x 64 on one MI355X).
 constexpr int kFusedThreads = 256;
 constexpr int kFusedChains = 16;  // MFMAs per store
 
@@ -147,8 +153,19 @@ __global__ void __launch_bounds__(kFusedThreads)
   const int lane = threadIdx.x & 63;
   const long long wave = (long long)blockIdx.x * (kFusedThreads / 64) + (threadIdx.x >> 6);
   const long long waves = (long long)gridDim.x * (kFusedThreads / 64);
-  const float a = 1.0f + lane * 1e-3f;
-  const float b = 1.0f - lane * 1e-3f;
+  float av[kFusedChains], bv[kFusedChains];
+  unsigned xs = 0x9E3779B9u ^ (unsigned)(wave * 64 + lane) * 2654435761u;
+#pragma unroll
+  for (int q = 0; q < kFusedChains; ++q) {  // xorshift32; sign bit and 23 mantissa bits random
+    xs ^= xs << 13;
+    xs ^= xs >> 17;
+    xs ^= xs << 5;
+    av[q] = __uint_as_float(0x3F800000u | (xs >> 9) | (xs << 31));
+    xs ^= xs << 13;
+    xs ^= xs >> 17;
+    xs ^= xs << 5;
+    bv[q] = __uint_as_float(0x3F800000u | (xs >> 9) | (xs << 31));
+  }
   f32x4 acc[kFusedChains];
 #pragma unroll
   for (int c = 0; c < kFusedChains; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -172,7 +189,9 @@ __global__ void __launch_bounds__(kFusedThreads)
       if constexpr (MODE != 2) {
 #pragma unroll
         for (int c = 0; c < kFusedChains; ++c)
-          acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[c], 0, 0, 0);
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[(c + j) % kFusedChains],
+                                                        bv[(3 * c + 5 * j) % kFusedChains],
+                                                        acc[c], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }

@@ -10,9 +10,7 @@ The 16-bit rungs take each workload rounded to their format (the seeded
 generator's rounding) and report against the dense bf16/fp16 matrix peak.
 ``splitk`` runs the split-K form of the production kernel with its automatic
 plan; ``splitk:<s>`` asks for s chunks (workspace allocated once per record,
-outside the timed region).  ``lib_f32``, ``lib_bf16`` and ``lib_f16`` time
-``torch.mm`` on the same operands (fp32 result; the vendor BLAS behind it)
-as a reference point: not part of the library.  ``--alu-probes`` first measures the fp32
+outside the timed region).  ``--alu-probes`` first measures the fp32
 vector-FMA probe at 1, 2, 4, 8 and 16 waves per SIMD, the LDS read-bandwidth
 probe and the fp32 MFMA probe (the compute and on-chip roofs of the rungs).  ``--copy-mib N`` first runs the streaming copy
 probe once over N MiB (a kernel of known traffic: N MiB read, N MiB written)
@@ -29,7 +27,10 @@ compulsory-byte GB/s, the tiled load model; with ``--cold`` the same timings
 for calls that each follow a 1 GiB fill, i.e. inputs out of the caches);
 a markdown table goes to stderr at the end.  Inputs come from the seeded
 generator and are resident on the GPU before timing.  This tool does not
-check results; the test suite does.
+check results: it is part of the package, which never loads the CPU
+oracle.  The GPU test suite compares every element of every rung's result
+on these workloads with the oracle, and the benchmark reports that
+comparison for the production kernel's automatic entry on each workload.
 """
 from __future__ import annotations
 
@@ -45,7 +46,6 @@ if ROOT not in sys.path:
 
 
 MIXED = ("bf16", "f16")
-LIB = {"lib_f32": "f32", "lib_bf16": "bf16", "lib_f16": "f16"}  # torch.mm reference rows
 
 
 def _num_configs(g, name: str) -> int:
@@ -184,7 +184,7 @@ def main(argv=None) -> int:
     rows = []
     specs = _expand_variants(args.variants, g)
     for wname in [w for w in args.workloads.split(",") if w]:
-        fmts = sorted({v for v, _ in specs if v in MIXED} | {LIB[v] for v, _ in specs if LIB.get(v, "f32") != "f32"})
+        fmts = sorted({v for v, _ in specs if v in MIXED})
         w, a, b = make_workload(wname)
         ops = {"f32": (torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev))}
         for fmt in fmts:
@@ -200,11 +200,8 @@ def main(argv=None) -> int:
                 continue
             mixed = vname in MIXED
             split = vname == "splitk"
-            lib = LIB.get(vname)
             try:
-                if lib:
-                    tile = {"config": -1}
-                elif mixed:
+                if mixed:
                     tile = g.gemm_mixed_tile(cfg, w.M, w.N, w.K)
                 elif split:
                     plan = g.gemm_f32_splitk_plan(w.M, w.N, w.K, -1, max(cfg, 0))
@@ -213,9 +210,7 @@ def main(argv=None) -> int:
                     tile = g.gemm_f32_tile(vname, cfg, w.M, w.N, w.K)
             except g.GemmError:  # entry does not accept this shape (small-K entries)
                 continue
-            if lib:
-                label = f"torch.mm {lib}" + ("" if lib == "f32" else " -> f32")
-            elif mixed:
+            if mixed:
                 label = g.mixed_config_name(vname, cfg, w.M, w.N, w.K)
             elif split:
                 label = (g.config_name("prod", plan["config"], w.M, w.N, w.K).replace("prod", "splitk")
@@ -225,18 +220,9 @@ def main(argv=None) -> int:
                 label = g.config_name(vname, cfg, w.M, w.N, w.K)
             reps = args.reps if vname != "naive" else max(1, min(args.reps, 3))
             print(f"[ladder] {wname} {label} reps={reps}", file=sys.stderr, flush=True)
-            ta, tb = ops[vname if mixed else (lib or "f32")]
+            ta, tb = ops[vname if mixed else "f32"]
 
-            if lib:
-                tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[lib]
-                la, lb = ta.view(tdt), tb.view(tdt)
-
-                def call():
-                    if lib == "f32":
-                        torch.mm(la, lb, out=tc)
-                    else:
-                        torch.mm(la, lb, out_dtype=torch.float32, out=tc)
-            elif mixed:
+            if mixed:
                 def call():
                     g.gemm_mixed(w.M, w.N, w.K, ta.data_ptr(), w.K, tb.data_ptr(), w.N,
                                  tc.data_ptr(), w.N, vname, cfg, s)
@@ -255,7 +241,7 @@ def main(argv=None) -> int:
             ms, ms_med, ms_min = timed_stats(call, reps,
                                              args.warmup if vname != "naive" else min(args.warmup, 1))
             tflops = rf.flops(w.M, w.N, w.K) / (ms * 1e-3) / 1e12
-            half = mixed or (lib not in (None, "f32"))
+            half = mixed
             peak = rf.PEAK_BF16_MFMA_TFLOPS if half else rf.PEAK_FP32_MFMA_TFLOPS
             elem = 2 if half else 4
             rec = {"workload": wname, "kernel": label, "variant": vname, "config": tile["config"],
@@ -263,7 +249,7 @@ def main(argv=None) -> int:
                    "tflops": round(tflops, 3),
                    "frac_peak": round(tflops / peak, 4), "peak_tflops": peak,
                    "gbps_compulsory": round(rf.compulsory_bytes(w.M, w.N, w.K, elem) / (ms * 1e-3) / 1e9, 1),
-                   "model_issued_load_bytes": None if lib else elem * rf.issued_load_elements(
+                   "model_issued_load_bytes": elem * rf.issued_load_elements(
                        "prod" if (mixed or split) else vname, w.M, w.N, w.K, tile),
                    "flops": rf.flops(w.M, w.N, w.K)}
             if args.cold:
