@@ -202,6 +202,42 @@ def test_lds_dma_entry_matches_register_staged(g):
         _tol_check(outs[1][ii, jj], oracle.gemm_elems(a, b, ii, jj), K, f"lds-dma {M}x{N}x{K}")
 
 
+BIG16_DIRECT_ENTRY = 19  # 128x128-wave tiles with direct loads (tail form for K % 32 != 0)
+BIG16_STAGED_ENTRY = 20  # the same tiles, LDS layout and k order, staged through registers
+
+
+def test_direct_tail_form_matches_register_staged(g):
+    """The direct-load 128x128-wave kernel takes rows that are only 4-byte
+    aligned and K that is not a multiple of its 32-deep step (the partial
+    last step filled through registers, zero past K).  It sums every element
+    in the register-staged kernel's k order, so the two agree bit for bit on
+    float inputs: tails of 1..31, odd leading dimensions, operands one float
+    into their buffers, two tiles per workgroup, K between one and two
+    steps, and the ragged workload's own shape."""
+    dev = _dev()
+    cases = [  # (M, N, K, pad_a, pad_b, shift)
+        (4097, 4095, 2049, 0, 0, 0), (512, 512, 33, 0, 0, 0), (520, 300, 63, 1, 3, 1),
+        (256, 256, 47, 0, 0, 1), (1000, 1028, 1000, 0, 0, 0), (4352, 4096, 40, 0, 0, 0),
+        (777, 516, 95, 4, 8, 0), (300, 260, 2049, 1, 1, 1)]
+    for (M, N, K, pa, pb, sh) in cases:
+        print(f"case: direct tail vs staged {M}x{N}x{K} pad {pa},{pb} shift {sh}", flush=True)
+        a, b = make(M, N, K, "normal", seed=M + 7 * N + 13 * K)
+        abuf = torch.zeros((M * (K + pa) + sh,), device=dev)
+        bbuf = torch.zeros((K * (N + pb) + sh,), device=dev)
+        av = abuf[sh:].view(M, K + pa)
+        bv = bbuf[sh:].view(K, N + pb)
+        av[:, :K] = torch.from_numpy(a).to(dev)
+        bv[:, :N] = torch.from_numpy(b).to(dev)
+        outs = []
+        for cfg in (BIG16_STAGED_ENTRY, BIG16_DIRECT_ENTRY):
+            c = g.matmul(av[:, :K], bv[:, :N], variant="prod", config=cfg)
+            torch.cuda.synchronize()
+            outs.append(c.cpu().numpy())
+        assert np.array_equal(outs[0], outs[1]), (M, N, K, pa, pb, sh)
+        ii, jj = _sample_indices(M, N, 4000, seed=M + K)
+        _tol_check(outs[1][ii, jj], oracle.gemm_elems(a, b, ii, jj), K, f"direct tail {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("entry", OWN_ORDER_ENTRIES)
 def test_own_order_entries(g, entry):
     """Entries that sum each element in their own order: the 64x64 K-split

@@ -2266,11 +2266,11 @@ hipError_t launch_w16(const Problem &p, hipStream_t s) {
                        (int)tiles_n);
 }
 
-// The 128x128-wave kernel with direct loads (big16_kernel) when A and B
-// rows are 16-byte aligned, N % 4 == 0, K is a positive multiple of the k
-// step, C is at least one tile each way and the lane offsets fit in 32
-// bits; otherwise FALLBACK (for the 256x256 tiles, the same tiles staged
-// through registers).
+// The 128x128-wave kernel with direct loads (big16_kernel) when C is at
+// least one tile each way, K is at least one k step (a partial last step
+// takes the kernel's tail form) and the lane offsets fit in 32 bits;
+// otherwise FALLBACK (for the 256x256 tiles, the same tiles staged through
+// registers).  Rows need only the 4-byte alignment every call has.
 using Launcher = hipError_t (*)(const Problem &, hipStream_t);
 template <class W, Launcher FALLBACK>
 hipError_t launch_big16(const Problem &p, hipStream_t s);
@@ -2363,13 +2363,11 @@ hipError_t launch_big16r(const Problem &p, hipStream_t s) {
 
 template <class W, Launcher FALLBACK>
 hipError_t launch_big16(const Problem &p, hipStream_t s) {
-  const bool direct = (reinterpret_cast<uintptr_t>(p.A) & 15) == 0 &&
-                      (reinterpret_cast<uintptr_t>(p.B) & 15) == 0 && (p.lda & 3) == 0 &&
-                      (p.ldb & 3) == 0 && (p.N & 3) == 0 && p.M >= W::BM && p.N >= W::BN &&
-                      p.K > 0 && p.K % W::BK == 0 && lane_offsets_fit(W::BM, p.lda, 4) &&
-                      lane_offsets_fit(W::BK, p.ldb, 4);
+  const bool direct = p.M >= W::BM && p.N >= W::BN && p.K >= W::BK &&
+                      lane_offsets_fit(W::BM, p.lda, 4) && lane_offsets_fit(W::BK, p.ldb, 4);
   if (!direct) return FALLBACK(p, s);
-  return launch_big16_grid<W, big16_kernel<W>>(p, s);
+  if (p.K % W::BK != 0) return launch_big16_grid<W, big16_kernel<W, true>>(p, s);
+  return launch_big16_grid<W, big16_kernel<W, false>>(p, s);
 }
 
 // The A-resident kernel on 16x16 MFMAs (arow16_kernel) when K == 64, C is

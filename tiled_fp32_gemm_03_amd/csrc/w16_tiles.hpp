@@ -166,6 +166,61 @@ __device__ inline void w16_mfma_t(f32x4 (&acc)[W::TBM][W::TBN], const f32x4 (&a)
       acc[bm][bn] = __builtin_amdgcn_mfma_f32_16x16x4f32(b[bn], a[bm][t], acc[bm][bn], 0, 0, 0);
 }
 
+// Guarded fill of one stage for the partial k step of a tile (k0 < K <
+// k0 + BK), in the direct-load layout, by all 256 threads: A is read as
+// 4-float windows (an A chunk that straddles K is the window ending at K,
+// shifted into place; chunks past K are zero), B rows at or past K are
+// zero, and every load stays inside the matrices (rows need 4-byte
+// alignment, K >= 4).  The tile lies inside C.  Elements past K enter the
+// MFMAs as exact zeros, so the per-element k order is that of a full step.
+__device__ inline f32x4 w16_place_window(const f32x4 &w, int valid, int shift) {
+  f32x4 v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int j = e + shift;
+    const float x = j == 0 ? w[0] : j == 1 ? w[1] : j == 2 ? w[2] : w[3];
+    v[e] = e < valid ? x : 0.f;
+  }
+  return v;
+}
+
+template <class W>
+__device__ inline void w16_fill_partial(float *st, const Problem &p, int m0, int n0, int k0,
+                                        int tid) {
+  constexpr int A_ROWS = 256 / W::ACH, B_ROWS = 256 / W::BCH;  // rows per pass of 256 threads
+  constexpr int A_CHUNKS = W::BM / A_ROWS, B_CHUNKS = W::BK / B_ROWS;
+  static_assert(W::BM % A_ROWS == 0 && W::BK % B_ROWS == 0, "whole passes");
+  const int arow = tid / W::ACH, ac = tid % W::ACH;
+  const int bkr = tid / W::BCH, bc = tid % W::BCH;
+  const int kc = k0 + 4 * ac;
+  const int valid = kc + 4 <= p.K ? 4 : (kc < p.K ? p.K - kc : 0);
+  const int col = valid == 4 ? kc : p.K - 4;
+  const int shift = valid > 0 && valid < 4 ? kc - col : 0;
+  f32x4 ra[A_CHUNKS], rb[B_CHUNKS];
+  const float *as = p.A + (long long)(m0 + arow) * p.lda + col;
+#pragma unroll
+  for (int i = 0; i < A_CHUNKS; ++i)
+    ra[i] = *reinterpret_cast<const f32x4u *>(as + (long long)i * A_ROWS * p.lda);
+  int b_ok = 0;
+#pragma unroll
+  for (int i = 0; i < B_CHUNKS; ++i) {
+    const int k = k0 + bkr + i * B_ROWS;
+    const bool ok = k < p.K;
+    b_ok |= (int)ok << i;
+    rb[i] = *reinterpret_cast<const f32x4u *>(p.B + (long long)(ok ? k : p.K - 1) * p.ldb + n0 +
+                                              4 * bc);
+  }
+#pragma unroll
+  for (int i = 0; i < A_CHUNKS; ++i)
+    *reinterpret_cast<f32x4 *>(st + 4 * w16_a_pos<W::ACH>(arow + i * A_ROWS, ac)) =
+        w16_place_window(ra[i], valid, shift);
+  const f32x4 z{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < B_CHUNKS; ++i)
+    *reinterpret_cast<f32x4 *>(st + W::A_FLOATS + 4 * w16_b_pos<W::BCH>(bkr + i * B_ROWS, bc)) =
+        (b_ok >> i) & 1 ? rb[i] : z;
+}
+
 // Workgroups of a kernel resident on the whole device at once (cached per
 // kernel and device; computed on first use).
 constexpr int kMaxDevices = 64;
@@ -207,10 +262,21 @@ int resident_workgroups() {
 // into the idle stage.  LDS layouts and the per-element k order are those
 // of w16_kernel.
 //
+// With TAIL, K is not a multiple of the k step (K > BK): each tile's last
+// step is partial.  The step before it issues its direct loads as usual but
+// from the last whole step inside the matrices (A columns and B rows
+// [K - BK, K)), so the MFMA stream is the plain kernel's; after its MFMAs
+// each wave waits for its loads, a barrier, and then every thread rewrites
+// the whole idle stage through registers with the partial step zero-filled
+// (w16_fill_partial) -- once per tile, outside the MFMA stream -- and the
+// top-of-step barrier publishes it.  Direct loads need only 4-byte aligned
+// rows (checked on gfx950: a 16-byte direct load from a dword-aligned
+// address delivers the 16 bytes at that address, at the same speed).
+//
 // The body is shared by the plain kernel and the split-K kernel (which runs
 // it on one chunk of K per grid row); `bid` of `G` is the workgroup's place
 // in the persistent grid.
-template <class W>
+template <class W, bool TAIL = false>
 __device__ __forceinline__ void big16_body(Problem p, int tiles_m, int tiles_n, int bid, int G) {
   static_assert(W::STAGES == 2, "two stages");
   __shared__ __attribute__((aligned(16))) float lds[2 * W::STAGE];
@@ -221,7 +287,7 @@ __device__ __forceinline__ void big16_body(Problem p, int tiles_m, int tiles_n, 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int ntiles = tiles_m * tiles_n;
-  const int nk = p.K / W::BK;
+  const int nk = (p.K + W::BK - 1) / W::BK;
   const int lid = xcd_remap(bid, G);
   if (lid >= ntiles) return;  // uniform per workgroup
   const int my_tiles = (ntiles - lid + G - 1) / G;
@@ -254,6 +320,10 @@ __device__ __forceinline__ void big16_body(Problem p, int tiles_m, int tiles_n, 
     ab = p.A + (long long)m0 * p.lda;
     bb = p.B + n0;
   };
+  auto tile_m0n0 = [&](int t, int &m0, int &n0) __attribute__((always_inline)) {
+    bool interior;
+    tile_origin<W>(lid + t * G, tiles_m, tiles_n, m0, n0, interior, p);
+  };
   auto issue = [&](unsigned st, const float *ab, const float *bb, int q0, int q1)
       __attribute__((always_inline)) {
 #pragma unroll
@@ -282,8 +352,15 @@ __device__ __forceinline__ void big16_body(Problem p, int tiles_m, int tiles_n, 
 
     for (int kk = 0; kk < nk; ++kk) {
       const bool last = kk + 1 == nk;
+      const bool pre_tail = TAIL && kk + 2 == nk;  // the next step is the partial one
       const float *ia = last ? nt_a : is_a + W::BK;
       const float *ib = last ? nt_b : is_b + b_step;
+      if constexpr (TAIL) {  // stay inside the matrices; the fill below replaces this stage
+        if (pre_tail) {
+          ia = is_a - (long long)(nk - 2) * W::BK + (p.K - W::BK);
+          ib = is_b - (long long)(nk - 2) * b_step + (long long)(p.K - W::BK) * p.ldb;
+        }
+      }
       __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(0));  // this step's loads (own)
       ks_lds_barrier();                                // everyone's; stage stage^1 free
       const float *st = lds + stage * W::STAGE;
@@ -343,6 +420,15 @@ __device__ __forceinline__ void big16_body(Problem p, int tiles_m, int tiles_n, 
           }
         }
       }
+      if constexpr (TAIL) {
+        if (pre_tail) {  // every wave's loads into the idle stage landed; rewrite it
+          __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(0));
+          ks_lds_barrier();
+          int m0, n0;
+          tile_m0n0(t, m0, n0);
+          w16_fill_partial<W>(lds + (stage ^ 1) * W::STAGE, p, m0, n0, (nk - 1) * W::BK, tid);
+        }
+      }
       is_a = ia;
       is_b = ib;
       stage ^= 1;
@@ -376,9 +462,9 @@ __device__ __forceinline__ void big16_body(Problem p, int tiles_m, int tiles_n, 
   __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(0));  // the redundant last reload
 }
 
-template <class W>
+template <class W, bool TAIL = false>
 __global__ void __launch_bounds__(256) big16_kernel(Problem p, int tiles_m, int tiles_n) {
-  big16_body<W>(p, tiles_m, tiles_n, blockIdx.x, gridDim.x);
+  big16_body<W, TAIL>(p, tiles_m, tiles_n, blockIdx.x, gridDim.x);
 }
 
 // Split-K: grid row y computes the partial product over k in
