@@ -1,8 +1,9 @@
 """Build ``libgemm_f32.so`` for gfx950 in-tree with hipcc.
 
-Each ``csrc/*.hip`` translation unit is compiled to an object in parallel and
-the objects are linked into one shared library next to this file.  Packed
-fp32 VALU forms are disabled for all device code.
+Each ``csrc/*.hip`` translation unit is compiled to an object in parallel,
+the host-only planning unit ``csrc/host_plan.cpp`` with the host C++
+compiler, and the objects are linked into one shared library next to this
+file.  Packed fp32 VALU forms are disabled for all device code.
 """
 from __future__ import annotations
 
@@ -23,6 +24,10 @@ ARCH = "gfx950"
 SOURCES = ["gemm_f32_abi.hip", "naive_tiled.hip", "prod.hip", "w16_vgpr.hip", "valu.hip", "mixed.hip",
            "mixed16.hip", "probes.hip"]
 
+# Host-only C++ (no device code): argument checks, launch table, choice model.
+HOST_SOURCES = ["host_plan.cpp"]
+HOST_FLAGS = ["-std=c++17", "-O2", "-fPIC", "-Wall", "-Wextra", "-I", CSRC]
+
 # Per-source flags: the kernels of w16_vgpr.hip keep their accumulators in
 # VGPRs (the MFMAs' VGPR form); see that file.
 SOURCE_FLAGS = {"w16_vgpr.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
@@ -42,15 +47,25 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the gfx950 library)")
 
 
+def host_cxx() -> str:
+    for cand in (os.environ.get("CXX"), shutil.which("g++"), shutil.which("c++")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("no host C++ compiler (g++) found")
+
+
 def _compile(src: str, extra: list[str], verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src),
-           "-o", obj]
+    if src in HOST_SOURCES:
+        cmd = [host_cxx(), *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    else:
+        cmd = [hipcc(), *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-c",
+               os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+        raise RuntimeError(f"compiling {src} failed:\n{r.stdout}\n{r.stderr}")
     # The host pass does not know the packed-fp32 feature and says so; keep
     # every other diagnostic visible.
     noise = "is not a recognized feature for this target"
@@ -64,9 +79,10 @@ def _compile(src: str, extra: list[str], verbose: bool) -> str:
 def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     os.makedirs(BUILD, exist_ok=True)
     extra = list(extra or [])
-    jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4)))
+    srcs = SOURCES + HOST_SOURCES
+    jobs = min(len(srcs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4)))
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra, verbose), SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, extra, verbose), srcs))
     tmp = LIB + f".tmp{os.getpid()}"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:

@@ -51,7 +51,7 @@ from collections import OrderedDict, defaultdict
 HERE = os.path.dirname(os.path.abspath(__file__))
 # Sources that define the production kernel's code.
 PROD_SOURCES = [os.path.join(HERE, "csrc", n)
-                for n in ("prod.hip", "w16_tiles.hpp", "w16_vgpr.hip", "tile_order.hpp")]
+                for n in ("prod.hip", "w16_tiles.hpp", "w16_vgpr.hip", "addr_math.hpp", "host_plan.cpp", "host_plan.hpp")]
 # Kernels of this library: everything in its namespace, plus the probes
 # (file-local kernels of probes.hip), matched on the raw kernel name.
 OUR_NAMESPACE = "gemm_f32_impl"

@@ -11,6 +11,13 @@
 
 using namespace gemm_f32_impl;
 
+// host_plan.hpp repeats the status codes it returns; they must be the ABI's.
+static_assert(kOk == GEMM_F32_OK && kInvalidDim == GEMM_F32_INVALID_DIM &&
+                  kInvalidLd == GEMM_F32_INVALID_LD && kNullPtr == GEMM_F32_NULL_PTR &&
+                  kBadVariant == GEMM_F32_BAD_VARIANT && kMisaligned == GEMM_F32_MISALIGNED &&
+                  kBadConfig == GEMM_F32_BAD_CONFIG && kBadArg == GEMM_F32_BAD_ARG,
+              "status codes of host_plan.hpp and gemm_f32.h differ");
+
 namespace {
 
 constexpr int kTiledT[GEMM_F32_NUM_VARIANTS] = {0, 16, 0, 32, 4, 32, 0};
@@ -24,23 +31,11 @@ int launch_status(hipError_t err, const char *what) {
   return GEMM_F32_LAUNCH_FAILED;
 }
 
-bool misaligned(const void *p) {
-  return (reinterpret_cast<std::uintptr_t>(p) & 3u) != 0;
-}
-
-int max1(int v) { return v > 1 ? v : 1; }
-
 int num_configs(int variant) {
   if (variant < 0 || variant >= GEMM_F32_NUM_VARIANTS) return 0;
   if (variant == GEMM_F32_PROD) return prod_num_configs();
   if (variant == GEMM_F32_VALU) return valu_num_configs();
   return 1;
-}
-
-// Shape checks shared by the product and the tile query.
-int check_shape(int M, int N, int K) {
-  if (M < 0 || N < 0 || K < 0) return GEMM_F32_INVALID_DIM;
-  return GEMM_F32_OK;
 }
 
 int resolve_config(int variant, int config, int M, int N, int K, int *out) {
@@ -63,15 +58,22 @@ int validate(int M, int N, int K, const float *A, int lda, const float *B,
              int *chosen) {
   int rc = check_shape(M, N, K);
   if (rc != GEMM_F32_OK) return rc;
-  if (lda < max1(K) || ldb < max1(N) || ldc < max1(N))
-    return GEMM_F32_INVALID_LD;
+  rc = check_ld(N, K, lda, ldb, ldc);
+  if (rc != GEMM_F32_OK) return rc;
   rc = resolve_config(variant, config, M, N, K, chosen);
   if (rc != GEMM_F32_OK) return rc;
-  if (M == 0 || N == 0) return GEMM_F32_OK;
-  if (C == nullptr) return GEMM_F32_NULL_PTR;
-  if (K > 0 && (A == nullptr || B == nullptr)) return GEMM_F32_NULL_PTR;
-  if (misaligned(C) || (K > 0 && (misaligned(A) || misaligned(B))))
-    return GEMM_F32_MISALIGNED;
+  return check_pointers(M, N, K, A, B, C, 4);
+}
+
+// The checks of the split-K entries, in order, and their plan.
+int splitk_validate(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
+                    float *C, int ldc, int config, int splits, SplitPlan *plan) {
+  int rc = check_shape(M, N, K);
+  if (rc != GEMM_F32_OK) return rc;
+  rc = check_ld(N, K, lda, ldb, ldc);
+  if (rc != GEMM_F32_OK) return rc;
+  if (splits < 0) return GEMM_F32_BAD_ARG;
+  if (!splitk_plan(M, N, K, config, splits, plan)) return GEMM_F32_BAD_CONFIG;
   return GEMM_F32_OK;
 }
 
@@ -151,19 +153,14 @@ extern "C" int gemm_f32_splitk_plan(int M, int N, int K, int config, int splits,
 extern "C" int gemm_f32_splitk(int M, int N, int K, const float *A, int lda, const float *B,
                                int ldb, float *C, int ldc, int config, int splits,
                                void *workspace, long long workspace_bytes, void *stream) {
-  int rc = check_shape(M, N, K);
-  if (rc != GEMM_F32_OK) return rc;
-  if (lda < max1(K) || ldb < max1(N) || ldc < max1(N)) return GEMM_F32_INVALID_LD;
-  if (splits < 0) return GEMM_F32_BAD_ARG;
   SplitPlan plan;
-  if (!splitk_plan(M, N, K, config, splits, &plan)) return GEMM_F32_BAD_CONFIG;
+  int rc = splitk_validate(M, N, K, A, lda, B, ldb, C, ldc, config, splits, &plan);
+  if (rc != GEMM_F32_OK) return rc;
   if (M == 0 || N == 0) return GEMM_F32_OK;
-  if (C == nullptr) return GEMM_F32_NULL_PTR;
-  if (K > 0 && (A == nullptr || B == nullptr)) return GEMM_F32_NULL_PTR;
-  if (misaligned(C) || (K > 0 && (misaligned(A) || misaligned(B))))
-    return GEMM_F32_MISALIGNED;
+  rc = check_pointers(M, N, K, A, B, C, 4);
+  if (rc != GEMM_F32_OK) return rc;
   if (plan.workspace_bytes > 0 &&
-      (workspace == nullptr || workspace_bytes < plan.workspace_bytes || misaligned(workspace)))
+      (bad_buffer(workspace) || workspace_bytes < plan.workspace_bytes))
     return GEMM_F32_BAD_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Problem p{M, N, K, A, lda, B, ldb, C, ldc};
@@ -212,18 +209,13 @@ int scratch_for_device(int dev, float **out) {
 extern "C" int gemm_f32_splitk_noalloc(int M, int N, int K, const float *A, int lda,
                                        const float *B, int ldb, float *C, int ldc, int config,
                                        int splits, void *stream) {
-  int rc = check_shape(M, N, K);
-  if (rc != GEMM_F32_OK) return rc;
-  if (lda < max1(K) || ldb < max1(N) || ldc < max1(N)) return GEMM_F32_INVALID_LD;
-  if (splits < 0) return GEMM_F32_BAD_ARG;
   SplitPlan plan;
-  if (!splitk_plan(M, N, K, config, splits, &plan)) return GEMM_F32_BAD_CONFIG;
+  int rc = splitk_validate(M, N, K, A, lda, B, ldb, C, ldc, config, splits, &plan);
+  if (rc != GEMM_F32_OK) return rc;
   if (plan.workspace_bytes > kScratchBytes) return GEMM_F32_SCRATCH_TOO_SMALL;
   if (M == 0 || N == 0) return GEMM_F32_OK;
-  if (C == nullptr) return GEMM_F32_NULL_PTR;
-  if (K > 0 && (A == nullptr || B == nullptr)) return GEMM_F32_NULL_PTR;
-  if (misaligned(C) || (K > 0 && (misaligned(A) || misaligned(B))))
-    return GEMM_F32_MISALIGNED;
+  rc = check_pointers(M, N, K, A, B, C, 4);
+  if (rc != GEMM_F32_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // The stream's device must be the current one: the scratch address is
   // looked up with that device current.
@@ -252,10 +244,6 @@ int mixed_resolve(int config, int M, int N, int K, int *out) {
   return GEMM_F32_OK;
 }
 
-bool misaligned2(const void *p) {
-  return (reinterpret_cast<std::uintptr_t>(p) & 1u) != 0;
-}
-
 }  // namespace
 
 extern "C" int gemm_mixed(int M, int N, int K, const void *A, int lda, const void *B,
@@ -263,16 +251,15 @@ extern "C" int gemm_mixed(int M, int N, int K, const void *A, int lda, const voi
                           void *stream) {
   int rc = check_shape(M, N, K);
   if (rc != GEMM_F32_OK) return rc;
-  if (lda < max1(K) || ldb < max1(N) || ldc < max1(N)) return GEMM_F32_INVALID_LD;
+  rc = check_ld(N, K, lda, ldb, ldc);
+  if (rc != GEMM_F32_OK) return rc;
   if (format != GEMM_MIXED_BF16 && format != GEMM_MIXED_F16) return GEMM_F32_BAD_ARG;
   int chosen = 0;
   rc = mixed_resolve(config, M, N, K, &chosen);
   if (rc != GEMM_F32_OK) return rc;
   if (M == 0 || N == 0) return GEMM_F32_OK;
-  if (C == nullptr) return GEMM_F32_NULL_PTR;
-  if (K > 0 && (A == nullptr || B == nullptr)) return GEMM_F32_NULL_PTR;
-  if (misaligned(C) || (K > 0 && (misaligned2(A) || misaligned2(B))))
-    return GEMM_F32_MISALIGNED;
+  rc = check_pointers(M, N, K, A, B, C, 2);
+  if (rc != GEMM_F32_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (K == 0) return launch_status(launch_zero_f32(C, M, N, ldc, s), "zero fill");
   const MixedProblem p{M, N, K, static_cast<const uint16_t *>(A), lda,

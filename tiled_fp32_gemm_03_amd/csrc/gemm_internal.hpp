@@ -6,6 +6,8 @@
 
 #include <cstdint>
 
+#include "host_plan.hpp"
+
 namespace gemm_f32_impl {
 
 // One product C = A x B, row-major with leading dimensions (elements).
@@ -18,17 +20,6 @@ struct Problem {
   float *C;
   long long ldc;
 };
-
-// Launch-table entry of the production kernel.
-struct ProdConfig {
-  int BM, BN, BK;  // workgroup tile and k step
-  int WGM, WGN;    // waves along M and N (threads = 64 * WGM * WGN)
-  int occupancy;   // intended workgroups per CU (documentation, grid sizing)
-  const char *name;
-};
-
-// Largest grid.y the runtime accepts; kernels loop when a dimension exceeds it.
-constexpr int kMaxGridY = 65535;
 
 hipError_t launch_zero(const Problem &p, hipStream_t s);
 hipError_t launch_naive(const Problem &p, hipStream_t s);
@@ -93,23 +84,11 @@ bool big16_128_split_fits(const Problem &p, int kc);
 hipError_t launch_big16_128_split(const Problem &p, int splits, int kc, float *ws,
                                   hipStream_t s);
 
-int prod_num_configs();
-const ProdConfig &prod_config(int index);
-int prod_choose(int M, int N, int K, double *full_rate = nullptr);
-bool prod_supports(int index, int M, int N, int K);
+// One product on production launch-table entry `index` (host_plan.hpp holds
+// the table, the automatic choice and the split-K plan), and the split-K
+// form of a plan: each chunk's partial product into its own M x N slab of
+// `ws`, then the slabs summed in chunk order into C.
 hipError_t launch_prod(int index, const Problem &p, hipStream_t s);
-
-// Split-K form of the production kernel: K is cut into `splits` chunks of
-// kc (a multiple of the entry's BK); each chunk's partial product goes to its
-// own M x N slab of a caller-provided workspace, and a second kernel sums the
-// slabs in chunk order into C.
-struct SplitPlan {
-  int config;                 // launch-table entry
-  int splits;                 // chunks actually used (1 = plain product)
-  int kc;                     // k values per chunk
-  long long workspace_bytes;  // splits * M * N * 4, or 0 when splits == 1
-};
-bool splitk_plan(int M, int N, int K, int config, int splits, SplitPlan *out);
 hipError_t launch_prod_split(const SplitPlan &plan, const Problem &p, float *ws, hipStream_t s);
 
 }  // namespace gemm_f32_impl

@@ -25,7 +25,7 @@
 // (geek-doc.cn section 六; mayulu.co "CUDA 编程系列之三", section 7).
 #include "gemm_internal.hpp"
 #include "launch_util.hpp"
-#include "tile_order.hpp"
+#include "addr_math.hpp"
 
 #include <cstdint>
 #include <type_traits>

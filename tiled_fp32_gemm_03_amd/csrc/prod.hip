@@ -55,7 +55,7 @@
 // tiles sharing an XCD's L2 also share A rows and B columns.
 #include "gemm_internal.hpp"
 #include "launch_util.hpp"
-#include "tile_order.hpp"
+#include "addr_math.hpp"
 #include "w16_tiles.hpp"
 
 #include <atomic>
@@ -127,20 +127,7 @@ __device__ inline f32x4 load4(const float *src) {
 __device__ inline f32x4 load_chunk_guarded(const float *base, long long ld,
                                            int row, int rows, int col,
                                            int cols, int &meta) {
-  int valid = 0, shift = 0;
-  long long off = 0;
-  if (row < rows && col < cols) {
-    if (col + 4 <= cols) {
-      valid = 4;
-      off = (long long)row * ld + col;
-    } else {
-      valid = cols - col;
-      shift = col - (cols - 4);
-      off = (long long)row * ld + (cols - 4);
-    }
-  }
-  meta = (valid << 2) | shift;
-  return load4(base + off);
+  return load4(base + guarded_window(row, rows, col, cols, ld, meta));
 }
 
 // Four elements src[0..3] with those at index >= valid read as 0 (per
@@ -984,12 +971,8 @@ __global__ void __launch_bounds__(256) ksplit_kernel(Problem p, int tiles_m, int
   unsigned voff[8];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int r = 16 * wave + 4 * q + (lane >> 4);
-    const int c = (lane & 15) ^ (r & 15);
-    voff[q] = (unsigned)(((long long)r * p.lda + 4 * c) * 4);
-    const int k = 16 * wave + 4 * q + (lane >> 4);
-    const int cb = (lane & 15) ^ (4 * ((k >> 2) & 3));
-    voff[4 + q] = (unsigned)(((long long)k * p.ldb + 4 * cb) * 4);
+    voff[q] = (unsigned)(dma_a_elem<16>(4 * wave + q, lane, p.lda) * 4);
+    voff[4 + q] = (unsigned)(dma_b_elem<16>(64 * (4 * wave + q) + lane, p.ldb) * 4);
   }
   const unsigned wave_a = (unsigned)(16 * wave * 64 * 4);            // LDS bytes
   const unsigned wave_b = (unsigned)((64 * 64 + 16 * wave * 64) * 4);
@@ -1222,19 +1205,11 @@ __global__ void __launch_bounds__(256) w16_kernel(Problem p, int tiles_m, int ti
   // addresses (chunks permuted as in the LDS layouts).
   unsigned voff[W::DMA];
 #pragma unroll
-  for (int q = 0; q < W::A_DMA; ++q) {
-    const int blk = wave * W::A_DMA + q;
-    const int r = W::ARPI * blk + lane / W::ACH;
-    const int c = (lane % W::ACH) ^ w16_a_perm<W::ACH>(r);
-    voff[q] = (unsigned)(((long long)r * p.lda + 4 * c) * 4);
-  }
+  for (int q = 0; q < W::A_DMA; ++q)
+    voff[q] = (unsigned)(dma_a_elem<W::ACH>(wave * W::A_DMA + q, lane, p.lda) * 4);
 #pragma unroll
-  for (int q = 0; q < W::B_DMA; ++q) {
-    const int j = 64 * (wave * W::B_DMA + q) + lane;  // LDS chunk this lane fills
-    const int k = j / W::BCH;
-    const int c = (j % W::BCH) ^ (4 * ((k >> 2) & 3));
-    voff[W::A_DMA + q] = (unsigned)(((long long)k * p.ldb + 4 * c) * 4);
-  }
+  for (int q = 0; q < W::B_DMA; ++q)
+    voff[W::A_DMA + q] = (unsigned)(dma_b_elem<W::BCH>(64 * (wave * W::B_DMA + q) + lane, p.ldb) * 4);
   const unsigned wave_a = (unsigned)(wave * W::A_DMA * 1024);
   const unsigned wave_b = (unsigned)(W::A_FLOATS * 4 + wave * W::B_DMA * 1024);
 
@@ -1426,10 +1401,9 @@ __global__ void __launch_bounds__(256) big16r_kernel(Problem p, int tiles_m, int
   };
   // The guarded form of one step, loaded and written in one go.
   auto write_guarded = [&](float *st, int m0, int n0, int k0) __attribute__((always_inline)) {
-    const int kc = k0 + 4 * ac;
-    const int valid = kc + 4 <= p.K ? 4 : (kc < p.K ? p.K - kc : 0);
-    const int col = valid == 4 ? kc : p.K - 4;
-    const int a_meta = (valid << 2) | (valid > 0 && valid < 4 ? kc - col : 0);
+    int valid = 0, shift = 0;
+    const int col = tail_window(k0 + 4 * ac, p.K, valid, shift);
+    const int a_meta = (valid << 2) | shift;
     const float *as = p.A + (long long)(m0 + arow) * p.lda + col;
 #pragma unroll
     for (int i = 0; i < T::A_CHUNKS; ++i) ra[i] = load4(as + i * a_stride);
@@ -2033,19 +2007,15 @@ __global__ void __launch_bounds__(256) arow16_kernel(Problem p, int panels, int 
   // Direct-load offsets: the A panel (once) and a B tile (per tile).
   unsigned voff[W::B_DMA];
 #pragma unroll
-  for (int q = 0; q < W::B_DMA; ++q) {
-    const int k = W::BRPI * (wave * W::B_DMA + q) + lane / W::BCH;
-    const int c = (lane % W::BCH) ^ (4 * ((k >> 2) & 3));
-    voff[q] = (unsigned)(((long long)k * p.ldb + 4 * c) * 4);
-  }
+  for (int q = 0; q < W::B_DMA; ++q)
+    voff[q] = (unsigned)(dma_b_elem<W::BCH>(64 * (wave * W::B_DMA + q) + lane, p.ldb) * 4);
   {
     const float *asrc = p.A + (long long)m0 * p.lda;
 #pragma unroll
     for (int q = 0; q < W::A_DMA; ++q) {
       const int blk = wave * W::A_DMA + q;
-      const int r = W::ARPI * blk + lane / W::ACH;
-      const int c = (lane % W::ACH) ^ w16_a_perm<W::ACH>(r);
-      ks_load_to_lds16((unsigned)(((long long)r * p.lda + 4 * c) * 4), asrc, lds_u + blk * 1024);
+      ks_load_to_lds16((unsigned)(dma_a_elem<W::ACH>(blk, lane, p.lda) * 4), asrc,
+                       lds_u + blk * 1024);
     }
     const float *bsrc = p.B + col(0);
 #pragma unroll
@@ -2154,9 +2124,7 @@ hipError_t launch_strip(const Problem &p, hipStream_t s) {
   if (p.M <= 8) return launch_kernel(strip_kernel<8>, grid, block, s, p);
   return hipErrorInvalidValue;
 }
-constexpr int kStripMaxRows = 8;
-
-// ---- launch table ----------------------------------------------------
+// ---- launch table (its entries and the automatic choice: host_plan.cpp) --
 
 using C0 = Tile<128, 128, 32, 2, 2, false>;
 using C1 = Tile<128, 128, 16, 2, 2, false>;
@@ -2173,43 +2141,6 @@ using C11 = Tile<256, 256, 16, 4, 2, false>;
 using C12 = Tile<256, 256, 32, 4, 4, false>;
 
 
-enum Kind { kKloop, kPanel, kKsplit };
-
-struct Entry {
-  ProdConfig cfg;
-  Kind kind;
-};
-
-const Entry kEntries[] = {
-    {{128, 128, 32, 2, 2, 2, "128x128x32_w2x2"}, kKloop},
-    {{128, 128, 16, 2, 2, 3, "128x128x16_w2x2"}, kKloop},
-    {{256, 128, 16, 4, 2, 2, "256x128x16_w4x2"}, kKloop},
-    {{64, 64, 32, 2, 2, 4, "64x64x32_w2x2"}, kKloop},
-    {{128, 64, 32, 2, 2, 2, "128x64x32_w2x2"}, kKloop},
-    {{128, 128, 32, 2, 2, 2, "128x128x32_w2x2_nt"}, kKloop},
-    {{128, 128, 16, 2, 2, 3, "128x128x16_w2x2_nt"}, kKloop},
-    {{256, 128, 32, 4, 2, 1, "256x128x32_w4x2"}, kKloop},
-    {{128, 128, 64, 2, 2, 2, "panel128x128_k64"}, kPanel},
-    {{256, 128, 64, 4, 2, 1, "panel256x128_k64"}, kPanel},
-    {{256, 256, 16, 4, 4, 1, "256x256x16_w4x4"}, kKloop},
-    {{256, 256, 16, 4, 2, 1, "256x256x16_w4x2"}, kKloop},
-    {{256, 256, 32, 4, 4, 1, "256x256x32_w4x4"}, kKloop},
-    {{256, 128, 64, 4, 2, 1, "panel256x128_k64_pipe"}, kPanel},
-    {{256, 128, 64, 4, 2, 1, "panel256x128_k64_arow"}, kPanel},
-    {{256, 256, 32, 4, 4, 1, "256x256x32_w4x4_ldsdma"}, kKloop},
-    {{64, 64, 64, 2, 2, 1, "64x64x64_ksplit4_ldsdma"}, kKsplit},
-    {{128, 128, 64, 2, 2, 1, "128x128x64_w16_ldsdma"}, kKsplit},
-    {{256, 256, 32, 4, 4, 1, "256x256x32_w4x4_ldsdma_mfma16"}, kKsplit},
-    {{256, 256, 32, 2, 2, 1, "256x256x32_w2x2_ldsdma_mfma16"}, kKsplit},
-    {{256, 256, 32, 2, 2, 1, "256x256x32_w2x2_regs_mfma16"}, kKsplit},
-    {{256, 128, 64, 2, 2, 1, "panel256x128_k64_arow_mfma16"}, kPanel},
-    {{192, 192, 32, 2, 2, 1, "192x192x32_w2x2_ldsdma_mfma16"}, kKsplit},
-    {{128, 128, 32, 2, 2, 2, "128x128x32_w2x2_ldsdma_mfma16"}, kKsplit},
-    {{192, 256, 32, 2, 2, 1, "192x256x32_w2x2_ldsdma_mfma16"}, kKsplit},
-    {{256, 256, 32, 2, 2, 1, "rows256_rounds+rest"}, kKsplit},
-};
-constexpr int kNumConfigs = sizeof(kEntries) / sizeof(kEntries[0]);
-constexpr int kRemainderConfig = 3;  // thin edge strips
 
 template <class S, void (*KERNEL)(Problem, int, int)>
 hipError_t launch_grid(const Problem &p, hipStream_t s) {
@@ -2391,15 +2322,6 @@ hipError_t launch_arow16(const Problem &p, hipStream_t s) {
                        (int)panels, (int)chunks, (int)tiles_n);
 }
 
-// The best k-loop entry by the automatic choice's model, its modelled
-// TFLOP/s, and that rate again if its tiles fill every workgroup slot (else 0).
-struct KloopModel {
-  int entry;
-  double score, full_rate;
-};
-KloopModel model_kloop(int M, int N, int K);
-int region_rows(int M, int N, int K);
-
 hipError_t launch_one(int index, const Problem &p, hipStream_t s) {
   switch (index) {
     case 0: return launch_kloop<C0>(p, s);
@@ -2468,194 +2390,7 @@ hipError_t launch_split_one(int index, const Problem &p, int splits, int kc, flo
   }
 }
 
-// Rows (or columns) of a thin remainder strip worth a separate launch: an
-// overhanging tile row that is at most 1/8 full would cost a whole extra
-// round of tiles for almost no work.
-int thin_remainder(int extent, int tile) {
-  const int rem = extent % tile;
-  return (extent > tile && rem > 0 && rem * 8 <= tile) ? rem : 0;
-}
-
-// The model of the automatic choice (prod_choose, below).
-
-KloopModel model_kloop(int M, int N, int K) {
-  struct Cand {
-    int entry, bm, bn;
-    double rate;
-    int slots;  // resident workgroups on 256 CUs
-  };
-  const bool whole_steps = K % 32 == 0;
-  const Cand cands[] = {{19, 256, 256, whole_steps ? 148.0 : 135.0, 256},
-                        {24, 192, 256, whole_steps ? 140.0 : 0.0, 256},
-                        {22, 192, 192, whole_steps ? 138.0 : 0.0, 256},
-                        {23, 128, 128, whole_steps ? 141.0 : 0.0, 512},
-                        {17, 128, 128, 124.0, 256},
-                        {16, 64, 64, 108.0, 256}};
-  constexpr long long kCus = 256;  // CUs of an MI355X
-  KloopModel best{16, -1.0, 0.0};
-  for (const Cand &c : cands) {
-    const long long tm = ceil_div(M - thin_remainder(M, c.bm), c.bm);
-    const long long tn = ceil_div(N - thin_remainder(N, c.bn), c.bn);
-    const long long tiles = tm * tn;
-    if (tiles <= 0) continue;
-    const long long grid = tiles < c.slots ? tiles : c.slots;
-    const long long busy = ceil_div(grid, kCus) * ceil_div(tiles, grid);  // tile times per CU
-    // the last tile row and column are moved back inside C, so part of
-    // their work overlaps a neighbour's and is done twice
-    const double useful = (double)(M - thin_remainder(M, c.bm)) * (N - thin_remainder(N, c.bn)) /
-                          ((double)tm * c.bm * (double)tn * c.bn);
-    const double score = c.rate * useful * (double)tiles / (double)(busy * kCus);
-    if (score > best.score) best = {c.entry, score, tiles >= c.slots ? score : 0.0};
-  }
-  return best;
-}
-
-// Entry 25 cuts C by rows: rows [0, 256 r) run entry 19 on whole rounds of
-// 256x256 tiles (r * tiles-per-row <= 256 q for some q), the rest runs its
-// own best k-loop entry in a second launch.  Returns the r whose modelled
-// time beats the best single entry by more than a launch (4 us), else 0.
-int region_rows(int M, int N, int K) {
-  if (K % 32 != 0 || M < 512 || N < 256) return 0;
-  const long long tn = ceil_div(N - thin_remainder(N, 256), 256);
-  const long long tm = M / 256;
-  const double flops_per_row = 2.0 * N * (double)K;
-  const KloopModel whole = model_kloop(M, N, K);
-  double best_us = flops_per_row * M / (whole.score * 1e6);
-  int best_r = 0;
-  for (long long q = 1; q <= 8; ++q) {
-    const long long r = 256 * q / tn;
-    if (r < 1) continue;
-    if (r >= tm) break;
-    const int m1 = (int)(256 * r);
-    if (M - m1 < 128) break;
-    const double top = 148.0 * (double)(r * tn) / (double)(ceil_div(r * tn, 256) * 256);
-    const KloopModel rest = model_kloop(M - m1, N, K);
-    const double us = flops_per_row * m1 / (top * 1e6) +
-                      flops_per_row * (M - m1) / (rest.score * 1e6) + 4.0;
-    if (us < best_us) {
-      best_us = us;
-      best_r = (int)r;
-    }
-  }
-  return best_r;
-}
-
 }  // namespace
-
-int prod_num_configs() { return kNumConfigs; }
-
-const ProdConfig &prod_config(int index) { return kEntries[index].cfg; }
-
-bool prod_supports(int index, int M, int N, int K) {
-  (void)M;
-  (void)N;
-  return kEntries[index].kind != kPanel || K <= kEntries[index].cfg.BK;
-}
-
-// Shape-based choice from measurements on MI355X.  K <= 64 with many tiles:
-// the A-resident small-K panel kernel (only B moves per tile; C stores
-// interleaved with the next tile's MFMAs), on 16x16 MFMAs with one wave per
-// SIMD when K == 64 and the rows are aligned (entry 21's launcher falls
-// back to the 32x32 form otherwise).  Otherwise the k-loop entry with the
-// best modelled rate: its measured rate when every CU is busy, times the
-// fraction of the time the CUs are busy on the persistent grid -- G =
-// min(resident workgroups, tiles) workgroups, ceil(G / 256) of them per CU,
-// ceil(tiles / G) tiles each, against tiles / 256 if the work spread
-// evenly -- and times the useful fraction of the tiles' work (edge tiles
-// moved back inside C repeat part of a neighbour's), counting tiles after
-// the thin remainder strips are split off.  Candidates (K a multiple of 32
-// and aligned rows take the direct-load forms): 256x256x32 on 128x128 wave
-// tiles (148 TFLOP/s with direct loads, about 135 staged through
-// registers), 192x256x32 on 96x128 waves (140), 192x192x32 on 96x96 waves
-// (138), 128x128x32 on 64x64 waves, two workgroups per CU (141), 128x128x64
-// on 64x64 waves with a register path for K tails (124), and 64x64x64 with
-// K split over the waves (108 at 24 steps per tile; less for shorter K,
-// where it wins anyway by filling the CUs).  Entry 25 (region_rows) when
-// cutting C by rows into whole rounds of 256x256 tiles plus a remainder
-// models faster still.
-// Returns the plain product's automatic entry, and through `full_rate` (if
-// given) its modelled TFLOP/s when its tiles fill every workgroup slot (the
-// rates are full-occupancy rates), else 0.
-int prod_choose(int M, int N, int K, double *full_rate) {
-  if (full_rate) *full_rate = 0.0;
-  const long long t256x128 = ceil_div(M, 256) * ceil_div(N, 128);
-  if (K <= 64 && t256x128 >= 1024) return 21;
-  if (region_rows(M, N, K) > 0) return 25;
-  const KloopModel m = model_kloop(M, N, K);
-  if (full_rate) *full_rate = m.full_rate;
-  return m.entry;
-}
-
-// Entries the split-K path can run: the k-loop kernels without
-// non-temporal stores (the slabs are read back at once).
-static bool split_supports(int index) {
-  switch (index) {
-    case 0: case 1: case 2: case 3: case 4: case 7: case 12: case 23: return true;
-    default: return false;
-  }
-}
-
-// Split-K plan.  Automatic entry: 128 x 128 x 32 tiles (64 x 64 below a
-// 128 x 128 output), two workgroups per CU -- entry 23, whose split form
-// runs the direct-load 16x16-MFMA kernel where the product fits it and
-// entry 0's otherwise.  Automatic split count: the one with the least
-// estimated time, counted in k steps of one tile,
-//   rounds(s) * ceil(ksteps / s) + (partial-slab bytes written and read back) / B,
-// where rounds(s) = ceil(tiles * s / 256): a CU given two (tile, chunk) pairs
-// takes about twice as long as one given one, so the launch's time is its
-// busiest CU's; B is the HBM bytes moved in the time of one k step (a
-// 128x128x32 step is 1 MFLOP, about 2 us on one CU; HBM moves about 9 MB in
-// that time).  One split is the plain product: ceil(tiles / 256) * ksteps,
-// or, when the plain product's own entry fills every workgroup slot (so its
-// full-occupancy rate applies), that rate's time at 2 us per 1-MFLOP step.
-// Each split is at least four k steps deep; products with a tile for every
-// CU, or fewer than 32 k steps, are not split.  An
-// explicit count is honoured up to one k step per split.  The chunk kc is a
-// multiple of BK, and splits = ceil(K / kc).
-bool splitk_plan(int M, int N, int K, int config, int splits, SplitPlan *out) {
-  if (M < 0 || N < 0 || K < 0 || splits < 0) return false;
-  const bool auto_config = config == -1;
-  if (auto_config) config = (M < 128 && N < 128) ? 3 : 23;
-  if (config < 0 || config >= kNumConfigs || !split_supports(config)) return false;
-  const ProdConfig &c = kEntries[config].cfg;
-  const long long tiles = ceil_div(M, c.BM) * ceil_div(N, c.BN);
-  const long long ksteps = ceil_div(K, c.BK);
-  long long want = splits;
-  if (want == 0) {
-    const long long cus = 256;
-    want = 1;
-    if (tiles > 0 && tiles < cus && ksteps >= 32) {
-      // bytes HBM moves while one CU runs one k step of this entry's tile
-      const double step_bytes = 9.0e6 * ((double)c.BM * c.BN * c.BK / (128.0 * 128.0 * 32.0));
-      const double slab_bytes = 8.0 * M * N;  // one chunk's partial written and read back
-      long long most = ksteps / 4;
-      if (most > 4 * cus) most = 4 * cus;
-      double best = (double)ksteps;           // one split: one round, no slabs
-      double plain_rate;
-      prod_choose(M, N, K, &plain_rate);
-      if (plain_rate > 0.0) {                 // TFLOP/s -> k steps of 1 MFLOP at 2 us
-        const double plain_steps = 2.0 * M * N * (double)K / (plain_rate * 1e6) / 2.0;
-        if (plain_steps < best) best = plain_steps;
-      }
-      for (long long sp = 2; sp <= most; ++sp) {
-        const double est = (double)ceil_div(tiles * sp, cus) * ceil_div(ksteps, sp) +
-                           sp * slab_bytes / step_bytes;
-        if (est < best) { best = est; want = sp; }
-      }
-    }
-  }
-  if (want > ksteps) want = ksteps;
-  if (want > kMaxGridY) want = kMaxGridY;
-  if (want < 1) want = 1;
-  const long long kc = ceil_div(ksteps, want) * c.BK;
-  const long long used = K > 0 ? ceil_div(K, kc) : 1;
-  // Unsplit with an automatic entry: the plain product's own choice.
-  out->config = used == 1 && auto_config ? prod_choose(M, N, K) : config;
-  out->splits = (int)used;
-  out->kc = (int)kc;
-  out->workspace_bytes = used > 1 ? used * (long long)M * N * 4 : 0;
-  return true;
-}
 
 hipError_t launch_prod_split(const SplitPlan &plan, const Problem &p, float *ws, hipStream_t s) {
   if (plan.splits <= 1) return launch_prod(plan.config, p, s);
@@ -2668,10 +2403,10 @@ hipError_t launch_prod_split(const SplitPlan &plan, const Problem &p, float *ws,
 // order.
 hipError_t launch_prod(int index, const Problem &p, hipStream_t s) {
   if (!prod_supports(index, p.M, p.N, p.K)) return hipErrorInvalidValue;
-  const ProdConfig &c = kEntries[index].cfg;
+  const ProdConfig &c = prod_config(index);
   int rm = index == kRemainderConfig ? 0 : thin_remainder(p.M, c.BM);
   int rn = index == kRemainderConfig ? 0 : thin_remainder(p.N, c.BN);
-  if (kEntries[index].kind == kPanel) {  // whole tiles only; every remainder is a strip
+  if (prod_kind(index) == kPanel) {  // whole tiles only; every remainder is a strip
     rm = p.M % c.BM;
     rn = p.N % c.BN;
     if (p.M < c.BM || p.N < c.BN) return launch_one(kRemainderConfig, p, s);

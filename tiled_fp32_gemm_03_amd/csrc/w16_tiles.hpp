@@ -8,7 +8,7 @@
 
 #include "gemm_internal.hpp"
 #include "launch_util.hpp"
-#include "tile_order.hpp"
+#include "addr_math.hpp"
 
 #include <atomic>
 #include <cstdint>
@@ -24,20 +24,13 @@ constexpr int kLdsBytes = 160 * 1024;  // LDS of one gfx950 CU
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void global_void_t;
 
-// Tile t's origin.  A last tile row or column that would overhang C is
-// moved back to end at C's edge (when C is at least one tile wide): it then
-// overlaps its neighbour, and both compute the shared elements with the same
-// k order, so they store identical values -- while the tile needs no guarded
-// loads.  Only a product narrower than one tile keeps guarded edges.
+// Tile t's origin (edge_tile_origin: a tile that would overhang C is moved
+// back inside it), and whether the whole tile lies inside C -- only a
+// product narrower than one tile keeps guarded edges.
 template <class S>
 __device__ inline void tile_origin(int t, int tiles_m, int tiles_n, int &m0,
                                    int &n0, bool &interior, const Problem &p) {
-  int tm, tn;
-  tile_coords(t, tiles_m, tiles_n, tm, tn);
-  m0 = tm * S::BM;
-  n0 = tn * S::BN;
-  if (m0 + S::BM > p.M && p.M >= S::BM) m0 = p.M - S::BM;
-  if (n0 + S::BN > p.N && p.N >= S::BN) n0 = p.N - S::BN;
+  edge_tile_origin(t, tiles_m, tiles_n, S::BM, S::BN, p.M, p.N, m0, n0);
   interior = (m0 + S::BM <= p.M) && (n0 + S::BN <= p.N);
 }
 
@@ -115,20 +108,7 @@ struct W16 {
   static_assert(STAGES >= 2 && STAGES * STAGE * 4 <= kLdsBytes, "LDS budget");
 };
 
-// Row permutation of A chunks: 16 consecutive rows land on distinct banks
-// (rows of 128 B pair up in a 256-byte bank window; rows of 256 B fill it).
-template <int ACH>
-__device__ inline int w16_a_perm(int r) {
-  return ACH == 16 ? (r & 15) : ((r >> 1) & 7);
-}
-template <int ACH>
-__device__ inline int w16_a_pos(int r, int c) {
-  return r * ACH + (c ^ w16_a_perm<ACH>(r));
-}
-template <int BCH>
-__device__ inline int w16_b_pos(int k, int c) {
-  return k * BCH + (c ^ (4 * ((k >> 2) & 3)));
-}
+// LDS chunk layouts (w16_a_pos, w16_b_pos): addr_math.hpp.
 
 // Fragments, per lane (l16 = lane % 16, g = lane / 16): for 16-deep chunk
 // h, A[row l16 of block bm][k = 16 h + 4 g .. + 3] as one 16-byte read,
@@ -192,10 +172,8 @@ __device__ inline void w16_fill_partial(float *st, const Problem &p, int m0, int
   static_assert(W::BM % A_ROWS == 0 && W::BK % B_ROWS == 0, "whole passes");
   const int arow = tid / W::ACH, ac = tid % W::ACH;
   const int bkr = tid / W::BCH, bc = tid % W::BCH;
-  const int kc = k0 + 4 * ac;
-  const int valid = kc + 4 <= p.K ? 4 : (kc < p.K ? p.K - kc : 0);
-  const int col = valid == 4 ? kc : p.K - 4;
-  const int shift = valid > 0 && valid < 4 ? kc - col : 0;
+  int valid = 0, shift = 0;
+  const int col = tail_window(k0 + 4 * ac, p.K, valid, shift);
   f32x4 ra[A_CHUNKS], rb[B_CHUNKS];
   const float *as = p.A + (long long)(m0 + arow) * p.lda + col;
 #pragma unroll
@@ -296,19 +274,11 @@ __device__ __forceinline__ void big16_body(Problem p, int tiles_m, int tiles_n, 
   // addresses (chunks permuted as in the LDS layouts).
   unsigned voff[W::DMA];
 #pragma unroll
-  for (int q = 0; q < W::A_DMA; ++q) {
-    const int blk = wave * W::A_DMA + q;
-    const int r = W::ARPI * blk + lane / W::ACH;
-    const int c = (lane % W::ACH) ^ w16_a_perm<W::ACH>(r);
-    voff[q] = (unsigned)(((long long)r * p.lda + 4 * c) * 4);
-  }
+  for (int q = 0; q < W::A_DMA; ++q)
+    voff[q] = (unsigned)(dma_a_elem<W::ACH>(wave * W::A_DMA + q, lane, p.lda) * 4);
 #pragma unroll
-  for (int q = 0; q < W::B_DMA; ++q) {
-    const int j = 64 * (wave * W::B_DMA + q) + lane;  // LDS chunk this lane fills
-    const int k = j / W::BCH;
-    const int c = (j % W::BCH) ^ (4 * ((k >> 2) & 3));
-    voff[W::A_DMA + q] = (unsigned)(((long long)k * p.ldb + 4 * c) * 4);
-  }
+  for (int q = 0; q < W::B_DMA; ++q)
+    voff[W::A_DMA + q] = (unsigned)(dma_b_elem<W::BCH>(64 * (wave * W::B_DMA + q) + lane, p.ldb) * 4);
   const unsigned wave_a = (unsigned)(wave * W::A_DMA * 1024);
   const unsigned wave_b = (unsigned)(W::A_FLOATS * 4 + wave * W::B_DMA * 1024);
   const long long b_step = (long long)W::BK * p.ldb;
