@@ -51,7 +51,10 @@ constexpr int vmcnt_wait_imm(int n) {
 // as clobbered; the compiler warns that it reserves M0 for itself, and in
 // the kernels that use this load nothing else sets or reads M0 (the
 // generated code touches M0 only in these sequences), so no value of the
-// compiler's is lost.
+// compiler's is lost.  tests/test_m0_guard.py disassembles the built code
+// objects and fails if any other instruction in such a kernel writes M0 or
+// reads it implicitly.  The s_nop gives the one wait state the hardware
+// needs between writing M0 and an LDS DMA that reads it.
 __device__ inline void ks_load_to_lds16(unsigned voff, const float *sbase, unsigned lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
