@@ -431,6 +431,14 @@ def main() -> int:
             sk["fused_probe_tflops"] = fz
             sk["frac_of_fused_probe"] = round(sk["tflops"] / fz, 4)
             sk["target_feasible_by_fused_probe"] = fz >= sk["target_tflops_at_80pct_hbm"]
+            # The binding roof at this intensity is the lowest of the MFMA
+            # probe, intensity x measured bandwidth and the fused probe's
+            # rate (matrix work and output stores together, as measured).
+            if fz < sk["binding_roof_tflops"]:
+                for r in (sk, records["skinny_k64"]):
+                    r["binding_roof_tflops"] = fz
+                    r["roof"] = "fused mfma+store probe"
+                    r["frac_of_binding_roof"] = round(r["tflops"] / fz, 4)
         sk["verdict_pass"] = records["skinny_k64"]["verdict"]["pass"]
         result["skinny_k64"] = sk
         c3 = records.get(w.name)

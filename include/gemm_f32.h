@@ -68,12 +68,22 @@ extern "C" {
  * ①-⑧; mayulu.co section 6).  Elements outside the matrices are loaded as 0
  * (geek-doc.cn section 六; mayulu.co section 7). */
 #define GEMM_F32_TILED 1
-/* Production kernel: BM x BN workgroup tiles, 128-bit global loads into a
- * register stage, double-buffered padded LDS with one barrier per k step,
- * per-wave register-blocked 32x32 output blocks computed by fp32 MFMA
- * (v_mfma_f32_32x32x2_f32).  The "one thread, several outputs" and
- * "register / wave / instruction block" pyramid the pages point to
- * (geek-doc.cn sections 三 and 五) on CDNA4 matrix cores. */
+/* Production rung: fp32 matrix-core kernels (v_mfma_f32_16x16x4_f32, or
+ * 32x32x2 in the register-staged entries), chosen per shape from a launch
+ * table (gemm_f32_ex selects an entry, gemm_f32_tile reports the choice).
+ * The default for large products is a persistent grid, one 256-thread
+ * workgroup per CU, walking 256 x 256 output tiles in an XCD-aware order;
+ * each of the 4 waves keeps a 128 x 128 block in accumulation registers (64
+ * independent 16 x 16 MFMA chains); A and B go straight from global memory
+ * into the idle one of two LDS stages (16-byte direct loads, chunks
+ * permuted per row so fragment reads are free of bank conflicts), one
+ * barrier per 32-deep k step; a partial last k step is filled through
+ * registers with zeros past K; edge tiles are moved back inside C, and thin
+ * remainder strips run on their own kernel.  Few-tile products split each
+ * tile's k steps over the 4 waves and add the partial tiles in wave order;
+ * K = 64 products keep A in LDS and stream B.  The "one thread, several
+ * outputs" and "register / wave / instruction block" pyramid the pages
+ * point to (geek-doc.cn sections 三 and 五) on CDNA4 matrix cores. */
 #define GEMM_F32_PROD 2
 /* The textbook kernel with T = 32 (1024 threads per workgroup). */
 #define GEMM_F32_TILED32 3
