@@ -265,7 +265,7 @@ void replay_arow16(const Shape &s, int slots) {
 void replay_strip(const Shape &s) {
   const int wgs = (int)ceil_div(s.N, 16);
   for (int w = 0; w < wgs; ++w) {
-    const long long n0 = 16LL * w;
+    const long long n0 = 16LL * xcd_remap(w, wgs);
     const bool whole = n0 + 16 <= s.N;
     for (int tid = 0; tid < 512; tid += 1) {
       const int c4 = (tid & 3) * 4, ks = tid >> 2;
@@ -280,9 +280,10 @@ void replay_strip(const Shape &s) {
             if (n0 + c4 + j >= s.N) fail(s, "strip B element", k, n0 + c4 + j);
           }
         }
-        for (int r = 0; r < s.M && r < 8; ++r) {
+        for (int r = 0; r < 8; ++r) {  // rows past M read row M - 1
+          const int row = r < s.M ? r : s.M - 1;
           ++g_checks;
-          if (k >= s.K || (long long)r * s.lda + k >= (long long)(s.M - 1) * s.lda + s.K)
+          if (k >= s.K || row < 0 || (long long)row * s.lda + k >= (long long)(s.M - 1) * s.lda + s.K)
             fail(s, "strip A element", r, k);
         }
       }

@@ -218,7 +218,11 @@ def test_direct_tail_form_matches_register_staged(g):
     cases = [  # (M, N, K, pad_a, pad_b, shift)
         (4097, 4095, 2049, 0, 0, 0), (512, 512, 33, 0, 0, 0), (520, 300, 63, 1, 3, 1),
         (256, 256, 47, 0, 0, 1), (1000, 1028, 1000, 0, 0, 0), (4352, 4096, 40, 0, 0, 0),
-        (777, 516, 95, 4, 8, 0), (300, 260, 2049, 1, 1, 1)]
+        (777, 516, 95, 4, 8, 0), (300, 260, 2049, 1, 1, 1), (4352, 4096, 65, 0, 0, 0),
+        (4352, 4096, 34, 1, 1, 1)]
+    # Every tail length: r = 1 and 2 run one and two MFMA groups of the
+    # partial step, 3..16 four, 17..31 the whole step.
+    cases += [(256, 256, 64 + r, r % 3, (r * 5) % 7, r % 2) for r in range(1, 32)]
     for (M, N, K, pa, pb, sh) in cases:
         print(f"case: direct tail vs staged {M}x{N}x{K} pad {pa},{pb} shift {sh}", flush=True)
         a, b = make(M, N, K, "normal", seed=M + 7 * N + 13 * K)

@@ -257,9 +257,17 @@ int resident_workgroups() {
 // The body is shared by the plain kernel and the split-K kernel (which runs
 // it on one chunk of K per grid row); `bid` of `G` is the workgroup's place
 // in the persistent grid.
-template <class W, bool TAIL = false>
+template <class W, int VQ = 0>
 __device__ __forceinline__ void big16_body(Problem p, int tiles_m, int tiles_n, int bid, int G) {
   static_assert(W::STAGES == 2, "two stages");
+  // VQ = 0: K is a whole number of steps.  VQ = 1, 2 or 4: the partial
+  // last step of each tile runs only its first VQ MFMA groups (group 4 h + u
+  // takes k = 16 h + u + {0, 4, 8, 12} of the step; the launcher picks VQ so
+  // that every group holding a k below K runs), inside the step before it.
+  // VQ = BK / 4: the partial step runs the pinned loop.
+  constexpr bool TAIL = VQ > 0;
+  constexpr bool PEEL = TAIL && VQ < W::BK / 4;
+  static_assert(VQ == 0 || VQ == 1 || VQ == 2 || VQ == 4 || VQ == W::BK / 4, "k quads");
   __shared__ __attribute__((aligned(16))) float lds[2 * W::STAGE];
   const unsigned lds_u = (unsigned)(uintptr_t)(lds_void_t *)lds;
 
@@ -269,6 +277,7 @@ __device__ __forceinline__ void big16_body(Problem p, int tiles_m, int tiles_n, 
   const int wm = wave >> 1, wn = wave & 1;
   const int ntiles = tiles_m * tiles_n;
   const int nk = (p.K + W::BK - 1) / W::BK;
+  const int nk_full = PEEL ? nk - 1 : nk;  // steps of the pinned loop
   const int lid = xcd_remap(bid, G);
   if (lid >= ntiles) return;  // uniform per workgroup
   const int my_tiles = (ntiles - lid + G - 1) / G;
@@ -323,8 +332,8 @@ __device__ __forceinline__ void big16_body(Problem p, int tiles_m, int tiles_n, 
 #pragma unroll
       for (int j = 0; j < W::TBN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int kk = 0; kk < nk; ++kk) {
-      const bool last = kk + 1 == nk;
+    for (int kk = 0; kk < nk_full; ++kk) {
+      const bool last = !PEEL && kk + 1 == nk;     // a peeled partial step is the last
       const bool pre_tail = TAIL && kk + 2 == nk;  // the next step is the partial one
       const float *ia = last ? nt_a : is_a + W::BK;
       const float *ib = last ? nt_b : is_b + b_step;
@@ -400,6 +409,27 @@ __device__ __forceinline__ void big16_body(Problem p, int tiles_m, int tiles_n, 
           int m0, n0;
           tile_m0n0(t, m0, n0);
           w16_fill_partial<W>(lds + (stage ^ 1) * W::STAGE, p, m0, n0, (nk - 1) * W::BK, tid);
+          if constexpr (PEEL) {
+            // The partial step itself, here: the next tile's first loads
+            // go into the stage this step just read (every wave is past
+            // the barrier above, so done with it); then only the first VQ
+            // MFMA groups (the others hold no k below K and would add exact
+            // zeros), with fragments read as they go.
+            ks_lds_barrier();  // the fill is everyone's
+            const float *pst = lds + (stage ^ 1) * W::STAGE;
+            issue(lds_u + stage * W::STAGE * 4, nt_a, nt_b, 0, W::DMA);
+            f32x4 a[W::TBM];
+            float b[W::TBN];
+#pragma unroll
+            for (int grp = 0; grp < VQ; ++grp) {
+              if (grp % 4 == 0) w16_read_a<W>(a, pst, grp / 4, lane, wm);
+              w16_read_b<W>(b, pst, grp / 4, grp % 4, lane, wn);
+              w16_mfma_t<W>(acc, a, b, grp % 4);
+            }
+            ia = nt_a;    // the operands most recently issued
+            ib = nt_b;
+            stage ^= 1;   // with the flip below: the next tile reads `stage`
+          }
         }
       }
       is_a = ia;
@@ -418,7 +448,6 @@ __device__ __forceinline__ void big16_body(Problem p, int tiles_m, int tiles_n, 
           for (int j = 0; j < W::TBN; ++j) asm volatile("" : "+a"(acc[i][j]));
       }
     }
-
     int m0, n0;
     bool interior;
     tile_origin<W>(lid + t * G, tiles_m, tiles_n, m0, n0, interior, p);
@@ -435,9 +464,9 @@ __device__ __forceinline__ void big16_body(Problem p, int tiles_m, int tiles_n, 
   __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(0));  // the redundant last reload
 }
 
-template <class W, bool TAIL = false>
+template <class W, int VQ = 0>
 __global__ void __launch_bounds__(256) big16_kernel(Problem p, int tiles_m, int tiles_n) {
-  big16_body<W, TAIL>(p, tiles_m, tiles_n, blockIdx.x, gridDim.x);
+  big16_body<W, VQ>(p, tiles_m, tiles_n, blockIdx.x, gridDim.x);
 }
 
 // Split-K: grid row y computes the partial product over k in
