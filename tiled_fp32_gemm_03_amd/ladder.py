@@ -26,10 +26,13 @@ minimum of the per-call times read from events between the calls; TFLOP/s,
 compulsory-byte GB/s, the tiled load model; with ``--cold`` the same timings
 for calls that each follow a 1 GiB fill, i.e. inputs out of the caches);
 a markdown table goes to stderr at the end.  Inputs come from the seeded
-generator and are resident on the GPU before timing.  This tool does not
-check results: it is part of the package, which never loads the CPU
-oracle.  The GPU test suite compares every element of every rung's result
-on these workloads with the oracle, and the benchmark reports that
+generator and are resident on the GPU before timing.  After the timed calls
+each record checks a sample of its result (2048 random elements and the four
+corners) against dot products formed in float64 on the host with numpy:
+equal for integer-valued workloads, within 1e-4 sqrt(K) otherwise.  That
+reference is written here, not taken from the CPU oracle, which the package
+never loads; the GPU test suite compares every element of every rung's
+result on these workloads with the oracle, and the benchmark reports that
 comparison for the production kernel's automatic entry on each workload.
 """
 from __future__ import annotations
@@ -181,16 +184,44 @@ def main(argv=None) -> int:
                           "tflops": round(tf, 2)}), flush=True)
         del buf
 
+    def decode16(bits, fmt):
+        """float64 values of bf16 or fp16 codes (uint16 bit patterns)."""
+        bits = np.asarray(bits).view(np.uint16)
+        if fmt == "f16":
+            return bits.view(np.float16).astype(np.float64)
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+    def sampled_check(host, wl, fmt, n=2048):
+        """Sampled elements of tc against float64 dot products on the host."""
+        rng = np.random.default_rng(12345)
+        ii = np.concatenate([rng.integers(0, wl.M, n), [0, wl.M - 1, 0, wl.M - 1]])
+        jj = np.concatenate([rng.integers(0, wl.N, n), [0, 0, wl.N - 1, wl.N - 1]])
+        ha, hb = host[fmt]
+        if fmt == "f32":
+            ra, rb = ha[ii].astype(np.float64), hb[:, jj].astype(np.float64)
+        else:
+            ra, rb = decode16(ha[ii], fmt), decode16(hb[:, jj], fmt)
+        ref = np.einsum("ik,ki->i", ra, rb)
+        got = tc[torch.from_numpy(ii).to(dev), torch.from_numpy(jj).to(dev)].double().cpu().numpy()
+        err = float(np.max(np.abs(got - ref))) if len(ref) else 0.0
+        exact = wl.dist == "int4"
+        bar = 0.0 if exact else 1e-4 * float(np.sqrt(max(wl.K, 1)))
+        return {"samples": int(len(ref)), "max_abs_err": err,
+                "bar": "equal" if exact else f"max|d| <= 1e-4 sqrt(K) = {bar:.3g}",
+                "pass": bool(np.isfinite(got).all() and err <= bar)}
+
     rows = []
     specs = _expand_variants(args.variants, g)
     for wname in [w for w in args.workloads.split(",") if w]:
         fmts = sorted({v for v, _ in specs if v in MIXED})
         w, a, b = make_workload(wname)
         ops = {"f32": (torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev))}
+        host = {"f32": (a, b)}
         for fmt in fmts:
             _, a16, b16 = make_mixed_workload(wname, fmt)
             ops[fmt] = (torch.from_numpy(a16.view(np.int16)).to(dev),
                         torch.from_numpy(b16.view(np.int16)).to(dev))
+            host[fmt] = (a16, b16)
         del a, b
         tc = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
@@ -256,19 +287,26 @@ def main(argv=None) -> int:
                 cms, cmed, cmin = timed_stats(call, reps, 0, cold=True)
                 rec.update({"cold_ms": round(cms, 5), "cold_ms_median": round(cmed, 5),
                             "cold_ms_min": round(cmin, 5)})
+            torch.cuda.synchronize()
+            rec["check"] = sampled_check(host, w, vname if mixed else "f32")
             rows.append(rec)
             print(json.dumps(rec), flush=True)
-        del ops, tc
+        del ops, tc, host
         torch.cuda.empty_cache()
 
     print("\n| workload | kernel | ms | TFLOP/s | % of dtype peak | GB/s (compulsory) | median ms | min ms |"
-          + (" cold median ms |" if args.cold else ""), file=sys.stderr)
-    print("|---|---|---|---|---|---|---|---|" + ("---|" if args.cold else ""), file=sys.stderr)
+          + (" cold median ms |" if args.cold else "") + " sampled check |", file=sys.stderr)
+    print("|---|---|---|---|---|---|---|---|" + ("---|" if args.cold else "") + "---|", file=sys.stderr)
     for r in rows:
+        c = r["check"]
         print(f"| {r['workload']} | {r['kernel']} | {r['ms']:.4f} | {r['tflops']:.2f} | "
               f"{100 * r['frac_peak']:.1f} | {r['gbps_compulsory']:.0f} | {r['ms_median']:.4f} | "
-              f"{r['ms_min']:.4f} |" + (f" {r['cold_ms_median']:.4f} |" if args.cold else ""),
-              file=sys.stderr)
+              f"{r['ms_min']:.4f} |" + (f" {r['cold_ms_median']:.4f} |" if args.cold else "")
+              + f" {'pass' if c['pass'] else 'FAIL'} ({c['max_abs_err']:.2g}) |", file=sys.stderr)
+    failed = [r for r in rows if not r["check"]["pass"]]
+    if failed:
+        print(f"[ladder] {len(failed)} record(s) failed the sampled check", file=sys.stderr)
+        return 1
     return 0
 
 
