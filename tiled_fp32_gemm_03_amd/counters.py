@@ -129,13 +129,14 @@ def cmd_trace(args) -> int:
             cur.setdefault(key, []).append(dur)
         if len(segs) != len(recs):
             raise SystemExit(f"{len(recs)} ladder records but {len(segs)} marked segments")
-        lines += ["| workload | record | kernel | workgroups | threads/WG | calls | avg us | min us | max us |",
-                  "|---|---|---|---|---|---|---|---|---|"]
+        lines += ["| workload | record | kernel | workgroups | threads/WG | calls | avg us | median us "
+                  "| min us | max us |",
+                  "|---|---|---|---|---|---|---|---|---|---|"]
         for rec, seg in zip(recs, segs):
             for (name, wgs, wg), durs in seg.items():
                 lines.append(f"| {rec.get('workload', '-')} | {rec.get('kernel', '-')} | `{name}` | {wgs} "
-                             f"| {wg} | {len(durs)} | {statistics.mean(durs):.1f} | {min(durs):.1f} "
-                             f"| {max(durs):.1f} |")
+                             f"| {wg} | {len(durs)} | {statistics.mean(durs):.1f} "
+                             f"| {statistics.median(durs):.1f} | {min(durs):.1f} | {max(durs):.1f} |")
     else:
         groups: dict = OrderedDict()
         for r in rows:
@@ -144,11 +145,11 @@ def cmd_trace(args) -> int:
             key = (short_name(r["Kernel_Name"]), _workgroups(r), _threads(r))
             dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
             groups.setdefault(key, []).append(dur)
-        lines += ["| kernel | workgroups | threads/WG | calls | avg us | min us | max us |",
-                  "|---|---|---|---|---|---|---|"]
+        lines += ["| kernel | workgroups | threads/WG | calls | avg us | median us | min us | max us |",
+                  "|---|---|---|---|---|---|---|---|"]
         for (name, wgs, wg), durs in groups.items():
             lines.append(f"| `{name}` | {wgs} | {wg} | {len(durs)} | {statistics.mean(durs):.1f} "
-                         f"| {min(durs):.1f} | {max(durs):.1f} |")
+                         f"| {statistics.median(durs):.1f} | {min(durs):.1f} | {max(durs):.1f} |")
     text = "\n".join(lines) + "\n"
     if args.out:
         with open(args.out, "w") as f:
