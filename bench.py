@@ -390,6 +390,14 @@ def main() -> int:
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    **g.gemm_f32_device_props(0)},
     }
+    if traffic and tile["BM"] == 256 and tile["BN"] == 256:
+        # The floor eight L2s set: each XCD fetches every panel its tiles
+        # touch once (one persistent workgroup per CU).
+        cus = props.multi_processor_count
+        floor = rf.xcd_panel_bytes(w.M, w.N, w.K, 256, 256,
+                                   min(cus, rf._cdiv(w.M, 256) * rf._cdiv(w.N, 256)))
+        result["roofline"]["traffic_floor_xcd_panels"] = {
+            **floor, "measured_over_floor": round(traffic["hbm_bytes_per_launch"] / floor["bytes"], 4)}
     del tc
     torch.cuda.empty_cache()
 

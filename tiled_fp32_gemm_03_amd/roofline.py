@@ -52,3 +52,48 @@ def issued_load_elements(variant: str, M: int, N: int, K: int, tile: dict) -> in
 
 def binding_roof_tflops(M: int, N: int, K: int, peak_tflops: float, bw_gbps: float) -> float:
     return min(peak_tflops, intensity(M, N, K) * bw_gbps / 1000.0)
+
+
+# ---- the floor that eight separate L2s set on a persistent tiled product ----
+# The dispatcher deals consecutive workgroups to the 8 XCDs round robin; the
+# persistent kernels renumber them so each XCD's workgroups walk a block of
+# tiles (8 tile rows at a time, column by column), and each XCD's L2 then
+# has to fetch every A row panel and B column panel its tiles touch at least
+# once.  This mirrors that mapping (xcd_remap and tile_coords of the kernels)
+# to count those panels: a measured L2-to-fabric read volume at this floor
+# means no panel is fetched twice into one L2.
+
+def _xcd_remap(b: int, grid: int, xcds: int) -> int:
+    per, rem, x = grid // xcds, grid % xcds, b % xcds
+    return x * per + min(x, rem) + b // xcds
+
+
+def _tile_coords(lid: int, tiles_m: int, tiles_n: int, group_rows: int) -> tuple[int, int]:
+    per_group = group_rows * tiles_n
+    g = lid // per_group
+    first = g * group_rows
+    rows = min(tiles_m - first, group_rows)
+    r = lid - g * per_group
+    return first + r % rows, r // rows
+
+
+def xcd_panel_bytes(M: int, N: int, K: int, BM: int, BN: int, grid: int, in_bytes: int = 4,
+                    xcds: int = 8, group_rows: int = 8) -> dict:
+    """Bytes each XCD's L2 must fetch (every A row panel and B column panel
+    its workgroups' tiles touch, once) plus C written once, for a persistent
+    grid of ``grid`` workgroups over BM x BN tiles with full-K panels."""
+    tiles_m, tiles_n = _cdiv(M, BM), _cdiv(N, BN)
+    ntiles = tiles_m * tiles_n
+    rows = [set() for _ in range(xcds)]
+    cols = [set() for _ in range(xcds)]
+    for b in range(grid):
+        t = _xcd_remap(b, grid, xcds)
+        while t < ntiles:
+            tm, tn = _tile_coords(t, tiles_m, tiles_n, group_rows)
+            rows[b % xcds].add(tm)
+            cols[b % xcds].add(tn)
+            t += grid
+    a = sum(len(r) for r in rows) * min(BM, M) * K * in_bytes
+    b = sum(len(c) for c in cols) * min(BN, N) * K * in_bytes
+    return {"read_bytes": a + b, "write_bytes": 4 * M * N, "bytes": a + b + 4 * M * N,
+            "a_panel_fetches": sum(len(r) for r in rows), "b_panel_fetches": sum(len(c) for c in cols)}
