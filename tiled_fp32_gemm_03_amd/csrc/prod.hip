@@ -140,17 +140,12 @@ __device__ inline f32x4 load_partial(const float *src, int valid) {
   return v;
 }
 
-__device__ inline float pick(const f32x4 &w, int j) {
-  return j == 0 ? w[0] : j == 1 ? w[1] : j == 2 ? w[2] : w[3];
-}
-
-// Place a loaded window according to its meta code (see Stage).
+// Place a loaded window according to its meta code (see Stage): element e
+// is w[e + shift] for e < valid, else 0 -- the w16 fill's branch-free select
+// network (an index select per element compiles to branches on the per-lane
+// shift).
 __device__ inline f32x4 place(const f32x4 &w, int meta) {
-  const int valid = meta >> 2, shift = meta & 3;
-  f32x4 v;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) v[e] = e < valid ? pick(w, e + shift) : 0.f;
-  return v;
+  return w16_place_window(w, meta >> 2, meta & 3);
 }
 
 template <class S, bool GUARD, bool DO_A = true, bool DO_B = true>
