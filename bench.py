@@ -394,8 +394,8 @@ def main() -> int:
         # The floor eight L2s set: each XCD fetches every panel its tiles
         # touch once (one persistent workgroup per CU).
         cus = props.multi_processor_count
-        floor = rf.xcd_panel_bytes(w.M, w.N, w.K, 256, 256,
-                                   min(cus, rf._cdiv(w.M, 256) * rf._cdiv(w.N, 256)))
+        tiles = -(-w.M // 256) * -(-w.N // 256)
+        floor = rf.xcd_panel_bytes(w.M, w.N, w.K, 256, 256, min(cus, tiles))
         result["roofline"]["traffic_floor_xcd_panels"] = {
             **floor, "measured_over_floor": round(traffic["hbm_bytes_per_launch"] / floor["bytes"], 4)}
     del tc
