@@ -1874,6 +1874,24 @@ __device__ inline void arow16_read_b(float (&b)[Arow16::TBN], const Arow16Lane &
     b[bn] = o.b[bn][KROW * Arow16::BN + BUF * Arow16::B_FLOATS];
 }
 
+// One MFMA of the stream, accumulating in place (FIRST: from 0, so the tile
+// needs no zeroed accumulators).  Issued as inline assembly with the
+// accumulator tied to the destination: with the builtin, the register
+// allocator renamed destinations away from their sources and copied the
+// accumulators back, about 600 accumulator moves per two tiles in the MFMA
+// stream (measured: 294 -> 288 us on 16384 x 16384 x 64).  The compiler does
+// not see these as MFMAs, so it inserts no wait states after them: sources
+// come from LDS reads (waited for by lgkmcnt, which the compiler does track),
+// each chain's next MFMA is 32 MFMAs later, and the tile ends with 24 wait
+// states before anything may read a result.
+template <bool FIRST>
+__device__ __forceinline__ void arow16_mfma(f32x4 &acc, float b, float a) {
+  if constexpr (FIRST)
+    asm volatile("v_mfma_f32_16x16x4_f32 %0, %1, %2, 0" : "=a"(acc) : "v"(b), "v"(a));
+  else
+    asm volatile("v_mfma_f32_16x16x4_f32 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
+}
+
 template <bool STORE, int BUF>
 __device__ __forceinline__ void arow16_tile(Acc16 &acc, Acc16 &prev, const Problem &p,
                                             int m0, int pn0, int nn0, const float *lds,
@@ -1882,10 +1900,6 @@ __device__ __forceinline__ void arow16_tile(Acc16 &acc, Acc16 &prev, const Probl
                                             int lane) {
   constexpr int buf = BUF;
   using W = Arow16;
-#pragma unroll
-  for (int i = 0; i < W::TBM; ++i)
-#pragma unroll
-    for (int j = 0; j < W::TBN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float *bsrc = p.B + nn0;
   const unsigned bdst = lds_u + (W::A_FLOATS + (buf ^ 1) * W::B_FLOATS) * 4 + wave * W::B_DMA * 1024;
   f32x4 a0[W::TBM], a1[W::TBM];
@@ -1905,8 +1919,7 @@ __device__ __forceinline__ void arow16_tile(Acc16 &acc, Acc16 &prev, const Probl
     for (int bm = 0; bm < W::TBM; ++bm) {
 #pragma unroll
       for (int bn = 0; bn < W::TBN; ++bn)
-        acc[bm][bn] =
-            __builtin_amdgcn_mfma_f32_16x16x4f32(bcur[bn], acur[bm][u], acc[bm][bn], 0, 0, 0);
+        arow16_mfma<grp == 0>(acc[bm][bn], bcur[bn], acur[bm][u]);
       // rows of 4 MFMAs: the next B's direct loads after rows 0, 2, ..,
       // then one C store after every third row
       const int row = grp * W::TBM + bm;
@@ -1955,6 +1968,11 @@ __device__ __forceinline__ void arow16_tile(Acc16 &acc, Acc16 &prev, const Probl
   mfma_rows(I3{}, I1{}, a1, a0, b1, b0);
   mfma_rows(I3{}, I2{}, a1, a0, b0, b1);
   mfma_rows(I3{}, I3{}, a1, a0, b1, b0);
+  // 24 wait states after the last MFMA before anything may read its result
+  // (arow16_mfma).
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+  __builtin_amdgcn_sched_barrier(0);
   // The next B is in (own loads; the stores issued after them may drain),
   // then every wave's, and every wave is done with this buffer.
   __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(STORE ? W::STORES : 0));
