@@ -6,8 +6,8 @@
 // launch_prod's split of each product into a main part and thin strips,
 // takes the entry the automatic choice runs, and replays every tile of the
 // kernels those workloads use -- the direct-load 128x128-wave kernel (whole
-// and partial last k steps), the K-split 64x64 kernel (direct loads and its
-// guarded register tail), the A-resident small-K kernel and the thin-M
+// and partial last k steps), the K-split 64x64 kernel (per-wave direct loads and
+// its per-wave register tail), the A-resident small-K kernel and the thin-M
 // strip kernel -- with the same constexpr index functions the kernels call
 // (addr_math.hpp): every 16-byte load must lie inside its matrix's rows and
 // columns (not merely inside the allocation), every store inside C's M x N
@@ -71,6 +71,12 @@ void check_a(const Shape &s, long long e, const char *what) {
   if (e < 0) return fail(s, what, e, -1);
   const long long row = e / s.lda, col = e % s.lda;
   if (row >= s.M || col + 4 > s.K) fail(s, what, row, col);
+}
+
+// A one-element load of A[row][col].
+void check_a1(const Shape &s, long long row, long long col, const char *what) {
+  ++g_checks;
+  if (row < 0 || col < 0 || row >= s.M || col >= s.K) fail(s, what, row, col);
 }
 
 void check_b(const Shape &s, long long e, const char *what) {
@@ -173,27 +179,31 @@ void replay_ksplit(const Shape &s) {
     int m0 = 0, n0 = 0;
     origin(t, tiles_m, tiles_n, 64, 64, s, m0, n0);
     for (int k0 : k0s)
-      for (int blk = 0; blk < 16; ++blk)
-        for (int lane = 0; lane < 64; ++lane) {
-          const long long ea = dma_a_elem<16>(blk, lane, s.lda);
-          const long long eb = dma_b_elem<16>(64 * blk + lane, s.ldb);
-          check_voff(s, ea, "ksplit A lane offset");
-          check_voff(s, eb, "ksplit B lane offset");
-          check_a(s, (long long)m0 * s.lda + k0 + ea, "ksplit A direct load");
-          check_b(s, (long long)k0 * s.ldb + n0 + eb, "ksplit B direct load");
-        }
-    if (tail) {  // register path: guarded windows of a 64x64x64 staging map
+      for (int wave = 0; wave < 4; ++wave)
+        for (int q = 0; q < 4; ++q)
+          for (int lane = 0; lane < 64; ++lane) {
+            const long long ea = ks_dma_a_elem(q, lane, wave, s.lda);
+            const long long eb = dma_b_elem<16>(64 * (4 * wave + q) + lane, s.ldb);
+            check_voff(s, ea, "ksplit A lane offset");
+            check_voff(s, eb, "ksplit B lane offset");
+            check_a(s, (long long)m0 * s.lda + k0 + ea, "ksplit A direct load");
+            check_b(s, (long long)k0 * s.ldb + n0 + eb, "ksplit B direct load");
+          }
+    if (tail) {  // ks_fill_partial: each wave its own quarter, zero past K
       const int k0 = (nk - 1) * 64;
-      for (int tid = 0; tid < 256; ++tid)
-        for (int i = 0; i < 4; ++i) {
-          int meta = 0;
-          const long long ea = guarded_window(m0 + tid / 16 + 16 * i, s.M, k0 + 4 * (tid % 16),
-                                              s.K, s.lda, meta);
-          check_a(s, ea, "ksplit tail A");
-          const long long eb = guarded_window(k0 + tid / 16 + 16 * i, s.K, n0 + 4 * (tid % 16),
-                                              s.N, s.ldb, meta);
-          check_b(s, eb, "ksplit tail B");
-        }
+      for (int wave = 0; wave < 4; ++wave)
+        for (int lane = 0; lane < 64; ++lane)
+          for (int q = 0; q < 4; ++q) {
+            const int r = 16 * q + lane / 4, kc = k0 + 16 * wave + 4 * (lane & 3);
+            const int valid = chunk_valid(kc, s.K);
+            if (valid == 4)
+              check_a(s, (long long)(m0 + r) * s.lda + kc, "ksplit tail A");
+            else
+              for (int e = 0; e < valid; ++e)
+                check_a1(s, m0 + r, kc + e, "ksplit tail A element");
+            const int k = k0 + 16 * wave + 4 * q + lane / 16;
+            if (k < s.K) check_b(s, (long long)k * s.ldb + n0 + 4 * (lane & 15), "ksplit tail B");
+          }
     }
     // final reduction: wave w stores rows 16 w .. 16 w + 15, 4 chunks per lane
     for (int wave = 0; wave < 4; ++wave)

@@ -250,15 +250,16 @@ def test_own_order_entries(g, entry):
     MFMA entries.  They are held to the fp32 bar (exact on integers), not to
     bit agreement with the other entries.  Shapes: one tile per CU, K tails
     (register path), K below one step, tiles moved inside C, several tiles
-    per workgroup, a single tile, padded leading dimensions, unaligned rows
-    and products narrower than a tile (the register-staged fallbacks)."""
+    per workgroup (also with one k step each, and unevenly dealt), an odd
+    number of k steps, a single tile, padded leading dimensions, unaligned
+    rows and products narrower than a tile (the register-staged fallbacks)."""
     dev = _dev()
     cases = [  # (M, N, K, pad_a, pad_b, pad_c)
         (1024, 1024, 1024, 0, 0, 0), (1000, 1028, 1000, 0, 0, 0), (100, 68, 4, 0, 0, 0),
         (130, 1000, 2048, 0, 0, 0), (2048, 2048, 512, 0, 0, 0), (64, 64, 64, 0, 0, 0),
         (777, 516, 700, 4, 8, 5), (300, 300, 257, 1, 0, 0), (512, 260, 96, 0, 3, 0),
         (2304, 1280, 320, 0, 0, 0), (260, 132, 100, 0, 0, 0), (4352, 4100, 32, 0, 0, 0),
-        (600, 520, 96, 4, 8, 5),
+        (600, 520, 96, 4, 8, 5), (2048, 1024, 64, 0, 0, 0), (1088, 1024, 128, 0, 4, 0),
         # register-staged 128x128-wave path: K below one step, a tail of 1
         # after one full step, the 4-element minimum, rows not 16-byte
         # aligned, and workgroups that walk two tiles with a K tail

@@ -96,6 +96,27 @@ constexpr long long dma_b_elem(int j, long long ldb) {
   return (long long)k * ldb + 4 * c;
 }
 
+// K-split 64x64 kernel: wave w reads only k in [16 w, 16 w + 16) of each
+// 64-deep step, so it loads that quarter of the tile's 64 A rows itself,
+// into an LDS region no other wave reads (its B k rows, 16 w .. 16 w + 15
+// of dma_b_elem<16>'s layout, are likewise its own).  The A quarter holds
+// 64 rows of 4 chunks, chunk c of row r at position 4 r + (c ^ ks_a_swz(r)):
+// a fragment read takes one chunk of 16 consecutive rows, and the swizzle
+// puts any 8 (or 16) consecutive rows' chunks on distinct 16-byte bank
+// groups of a 128-byte (or 256-byte) bank window.
+constexpr int ks_a_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+constexpr int ks_a_pos(int r, int c) { return 4 * r + (c ^ ks_a_swz(r)); }
+// Direct load q (0..3) of wave w: lane l fills position 64 q + l, which is
+// row 16 q + l / 4.  Element offset from the k step's base (the tile's
+// first row, the step's first k column).
+constexpr long long ks_dma_a_elem(int q, int lane, int wave, long long lda) {
+  const int r = 16 * q + lane / 4;
+  const int c = (lane & 3) ^ ks_a_swz(r);
+  return (long long)r * lda + 16 * wave + 4 * c;
+}
+// How many of the 4 elements of a chunk starting at column kc lie inside K.
+constexpr int chunk_valid(int kc, int K) { return kc + 4 <= K ? 4 : (kc < K ? K - kc : 0); }
+
 // ---- guarded and partial windows -------------------------------------------
 
 // Branch-free guarded chunk load of the register-staged kernels: the chunk

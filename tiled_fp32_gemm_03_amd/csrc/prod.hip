@@ -60,6 +60,7 @@
 
 #include <atomic>
 #include <cstdint>
+#include <type_traits>
 
 namespace gemm_f32_impl {
 namespace {
@@ -840,6 +841,26 @@ __global__ void __launch_bounds__(S::NT) lds_dma16_kernel(Problem p, int tiles_m
   }
 }
 
+// One v_mfma_f32_16x16x4_f32 accumulating in place (FIRST: from 0, so a
+// tile needs no zeroed accumulators), for the A-resident and the
+// whole-step K-split kernels.  Issued as inline assembly with the
+// accumulator tied to the destination: with the builtin, the register
+// allocator renamed destinations away from their sources and copied the
+// accumulators back inside the MFMA stream (about 600 accumulator moves per
+// two tiles of the A-resident kernel: measured 294 -> 288 us on 16384 x
+// 16384 x 64).  The compiler does not see these as MFMAs, so it inserts no
+// wait states after them: the callers take their sources straight from LDS
+// reads (waited for by lgkmcnt, which the compiler does track), keep each
+// chain's next MFMA 16 or more MFMAs later, and issue 24 wait states after
+// the stream before anything reads a result.
+template <bool FIRST>
+__device__ __forceinline__ void mfma_inplace(f32x4 &acc, float b, float a) {
+  if constexpr (FIRST)
+    asm volatile("v_mfma_f32_16x16x4_f32 %0, %1, %2, 0" : "=a"(acc) : "v"(b), "v"(a));
+  else
+    asm volatile("v_mfma_f32_16x16x4_f32 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
+}
+
 // ---- 64x64 tiles with K split over the waves, 3-stage direct-load pipe --
 // For products with about one 64x64 tile per CU (1024^3 has 256), where a
 // k step of a 64x64 tile is too short to hide the latency of its loads.
@@ -849,42 +870,61 @@ __global__ void __launch_bounds__(S::NT) lds_dma16_kernel(Problem p, int tiles_m
 // so one wave per SIMD keeps the matrix pipe busy.  The four partial tiles
 // are added in wave order through LDS at the end of the tile, so the result
 // is deterministic (but summed in a different order from the other entries).
-// Operands arrive by global_load_lds_dwordx4 into three LDS stages: the
-// loads for step i + 3 are issued during step i, into the stage whose
-// fragments every wave already holds in registers (fragments are read one
-// step ahead), so each load has two steps to land.
+//
+// A wave loads exactly the operands it reads -- its k quarter of the tile's
+// 64 A rows and its 16 k rows of B -- into LDS regions of its own, so the k
+// loop has no workgroup barrier: each wave waits only for its own loads and
+// runs at its own pace until the tile's partial sums meet.  Operands arrive
+// by global_load_lds_dwordx4 into three LDS stages: the loads for step i + 3
+// are issued during step i, into the stage whose fragments the wave already
+// holds in registers (fragments are read one step ahead), so each load has
+// two steps to land.  A partial last k step goes through registers, zero
+// past K, into the same regions.
 //
 // MFMA operand roles: B is the first operand, A the second, so lane l of
 // block (bm, bn) holds C[m = 16 bm + l % 16][n = 16 bn + 4 (l / 16) + r],
 // r = 0..3.  Within a wave's 16 k of a step, MFMA t takes k = 4 g + t for
 // lane group g = l / 16, so a lane's A operand for t = 0..3 is one 128-bit
-// LDS read.  LDS layouts (16-byte chunks, rows of 64 floats):
-//   A: chunk c of row r at position c ^ (r & 15);
-//   B: chunk c of k row k at position c ^ (4 ((k >> 2) & 3)).
-// Both make the fragment reads of a wave conflict-free.
-using KsTile = Tile<64, 64, 64, 2, 2, false>;  // staging map for the register path
+// LDS read.  LDS layouts of a stage (16-byte chunks):
+//   A: wave w's quarter at float 1024 w, chunk c of row r at ks_a_pos(r, c);
+//   B: from float 4096, chunk c of k row k at 16 k + (c ^ (4 ((k >> 2) & 3))).
+// Both make the fragment reads of a wave conflict-free.  The partial tiles
+// use rows of 16 chunks, chunk c of row r at 16 r + (c ^ (r & 15)).
+using KsTile = Tile<64, 64, 64, 2, 2, false>;  // tile origins
 constexpr int kKsStages = 3;
 constexpr int kKsStageFloats = 64 * 64 * 2;   // A and B, unpadded
+constexpr int kKsQuarterFloats = 64 * 16;     // a wave's A quarter
 constexpr int kKsRedFloats = 4 * 64 * 64;     // the four partial tiles
 constexpr int kKsDmaPerWave = 8;              // 4 A + 4 B instructions of 1 KB
 
-__device__ inline int ks_a_pos(int r, int c) { return r * 16 + (c ^ (r & 15)); }
+__device__ inline int ks_red_pos(int r, int c) { return r * 16 + (c ^ (r & 15)); }
 __device__ inline int ks_b_pos(int k, int c) { return k * 16 + (c ^ (4 * ((k >> 2) & 3))); }
 
-template <bool PLACED>
-__device__ inline void ks_store_stage(const Stage<KsTile> &sg, float *st, int tid) {
-  const int arow = tid / 16, c = tid % 16;
+// A partial k step through registers: wave `wave` loads its quarter of the
+// step starting at column k0 -- A rows m0 .. m0 + 63, columns k0 + 16 w ..
+// + 15, and B rows k0 + 16 w .. + 15, columns n0 .. n0 + 63 -- with zeros
+// for k >= K, and writes it to its own regions of stage `st`.  Rows of A and
+// B are 16-byte aligned and chunks start at multiples of 4, so a chunk lies
+// wholly inside K (one 128-bit load), partly (per-element loads) or outside.
+__device__ inline void ks_fill_partial(const Problem &p, int m0, int n0, int k0, float *st,
+                                       int lane, int wave) {
+  f32x4 a[4], b[4];
 #pragma unroll
-  for (int i = 0; i < KsTile::A_CHUNKS; ++i) {
-    const int r = arow + i * KsTile::A_ROWS_PER_PASS;
-    *reinterpret_cast<f32x4 *>(st + 4 * ks_a_pos(r, c)) =
-        PLACED ? place(sg.a[i], sg.ameta[i]) : sg.a[i];
+  for (int q = 0; q < 4; ++q) {
+    const int r = 16 * q + lane / 4, kc = k0 + 16 * wave + 4 * (lane & 3);
+    const int valid = chunk_valid(kc, p.K);
+    const float *src = p.A + (long long)(m0 + r) * p.lda + kc;
+    a[q] = valid == 4 ? load4(src) : load_partial(src, valid);
+    const int k = k0 + 16 * wave + 4 * q + lane / 16;
+    b[q] = k < p.K ? load4(p.B + (long long)k * p.ldb + n0 + 4 * (lane & 15))
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  float *sa = st + wave * kKsQuarterFloats;
 #pragma unroll
-  for (int i = 0; i < KsTile::B_CHUNKS; ++i) {
-    const int k = arow + i * KsTile::B_ROWS_PER_PASS;
-    *reinterpret_cast<f32x4 *>(st + 64 * 64 + 4 * ks_b_pos(k, c)) =
-        PLACED ? place(sg.b[i], sg.bmeta[i]) : sg.b[i];
+  for (int q = 0; q < 4; ++q) {
+    *reinterpret_cast<f32x4 *>(sa + 4 * ks_a_pos(16 * q + lane / 4, lane & 3)) = a[q];
+    *reinterpret_cast<f32x4 *>(st + 64 * 64 +
+                               4 * ks_b_pos(16 * wave + 4 * q + lane / 16, lane & 15)) = b[q];
   }
 }
 
@@ -895,10 +935,10 @@ struct KsFrag {
 
 __device__ inline void ks_read_frag(KsFrag &f, const float *st, int lane, int wave) {
   const int l16 = lane & 15, g = lane >> 4;
-  const int ca = 4 * wave + g;  // A chunk holding k = 16 w + 4 g .. + 3
+  const float *sa = st + wave * kKsQuarterFloats;
 #pragma unroll
   for (int bm = 0; bm < 4; ++bm)
-    f.a[bm] = *reinterpret_cast<const f32x4 *>(st + 4 * ks_a_pos(16 * bm + l16, ca));
+    f.a[bm] = *reinterpret_cast<const f32x4 *>(sa + 4 * ks_a_pos(16 * bm + l16, g));
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int k = 16 * wave + 4 * g + t;
@@ -913,7 +953,10 @@ __device__ inline void ks_read_frag(KsFrag &f, const float *st, int lane, int wa
 // The step's 64 MFMAs in 8 groups of 8; with DMA, direct load q of the next
 // stage is issued after group q, so its issue overlaps the matrix work of a
 // lone wave.
-template <bool DMA>
+// ACC: how the MFMAs accumulate -- kKsBuiltin (the compiler's MFMA),
+// kKsInPlace or kKsFromZero (mfma_inplace, the latter starting the tile).
+enum KsAcc { kKsBuiltin, kKsInPlace, kKsFromZero };
+template <bool DMA, KsAcc ACC = kKsBuiltin>
 __device__ inline void ks_mfma(f32x4 (&acc)[4][4], const KsFrag &f, const unsigned (&voff)[8],
                                const float *abase, const float *bbase, unsigned lds_a,
                                unsigned lds_b) {
@@ -924,9 +967,15 @@ __device__ inline void ks_mfma(f32x4 (&acc)[4][4], const KsFrag &f, const unsign
 #pragma unroll
       for (int bm = 2 * half; bm < 2 * half + 2; ++bm)
 #pragma unroll
-        for (int bn = 0; bn < 4; ++bn)
-          acc[bm][bn] = __builtin_amdgcn_mfma_f32_16x16x4f32(f.b[bn][t], f.a[bm][t],
-                                                             acc[bm][bn], 0, 0, 0);
+        for (int bn = 0; bn < 4; ++bn) {
+          if constexpr (ACC == kKsBuiltin)
+            acc[bm][bn] = __builtin_amdgcn_mfma_f32_16x16x4f32(f.b[bn][t], f.a[bm][t],
+                                                               acc[bm][bn], 0, 0, 0);
+          else if (ACC == kKsFromZero && t == 0)
+            mfma_inplace<true>(acc[bm][bn], f.b[bn][t], f.a[bm][t]);
+          else
+            mfma_inplace<false>(acc[bm][bn], f.b[bn][t], f.a[bm][t]);
+        }
       if constexpr (DMA) {
         __builtin_amdgcn_sched_barrier(0);  // keep each load after its group
         const int q = 2 * t + half;
@@ -937,6 +986,47 @@ __device__ inline void ks_mfma(f32x4 (&acc)[4][4], const KsFrag &f, const unsign
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+}
+
+// Waits for this wave's vector-memory operations down to `n` outstanding
+// (n is 0, 8 or 16: one step's direct loads per 8).  A wave reads only LDS
+// its own loads wrote, so this wait -- no barrier -- makes a stage readable;
+// the empty assembly keeps the compiler from moving LDS reads above it.
+__device__ inline void ks_wait_own(int n) {
+  if (n >= 16)
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(16));
+  else if (n >= 8)
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(8));
+  else
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(0));
+  asm volatile("" ::: "memory");
+}
+
+// The end of a tile: each wave writes its partial 64x64 tile to LDS, and
+// after a barrier wave w adds rows 16 w .. 16 w + 15 of the four in wave
+// order (lane (row, q) takes chunks 4 j + q, j = 0..3, of its row) and
+// stores them to C.
+__device__ inline void ks_finish_tile(const f32x4 (&acc)[4][4], float *red, const Problem &p,
+                                      int m0, int n0, int lane, int wave) {
+  const int l16 = lane & 15, g = lane >> 4;
+  float *mine = red + wave * 64 * 64;
+#pragma unroll
+  for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < 4; ++bn)
+      *reinterpret_cast<f32x4 *>(mine + 4 * ks_red_pos(16 * bm + l16, 4 * bn + g)) = acc[bm][bn];
+  ks_lds_barrier();
+  const int row = 16 * wave + (lane >> 2), q = lane & 3;
+  const int gm = m0 + row;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = 4 * j + q;
+    f32x4 v = *reinterpret_cast<const f32x4 *>(red + 4 * ks_red_pos(row, c));
+#pragma unroll
+    for (int w = 1; w < 4; ++w)
+      v += *reinterpret_cast<const f32x4 *>(red + w * 64 * 64 + 4 * ks_red_pos(row, c));
+    *reinterpret_cast<f32x4u *>(p.C + (long long)gm * p.ldc + n0 + 4 * c) = v;
+  }
 }
 
 // The launcher guarantees M, N >= 64 (every tile lies inside C after the
@@ -961,15 +1051,15 @@ __global__ void __launch_bounds__(256) ksplit_kernel(Problem p, int tiles_m, int
   const bool k_tail = (p.K & 63) != 0;  // the last step of every tile is partial
 
   // Per-lane byte offsets of this wave's direct loads from the step's base
-  // addresses: q < 4 are A rows 16 w + 4 q + l / 16, the others B k rows
-  // 16 w + 4 (q - 4) + l / 16; the chunk is permuted as in the LDS layout.
+  // addresses: q < 4 fill its A quarter (rows 16 q + l / 4), the others its
+  // B k rows 16 w + 4 (q - 4) + l / 16; chunks permuted as in the layouts.
   unsigned voff[8];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    voff[q] = (unsigned)(dma_a_elem<16>(4 * wave + q, lane, p.lda) * 4);
+    voff[q] = (unsigned)(ks_dma_a_elem(q, lane, wave, p.lda) * 4);
     voff[4 + q] = (unsigned)(dma_b_elem<16>(64 * (4 * wave + q) + lane, p.ldb) * 4);
   }
-  const unsigned wave_a = (unsigned)(16 * wave * 64 * 4);            // LDS bytes
+  const unsigned wave_a = (unsigned)(wave * kKsQuarterFloats * 4);  // LDS bytes
   const unsigned wave_b = (unsigned)((64 * 64 + 16 * wave * 64) * 4);
 
   // The issue side walks steps it + 3 ahead of the consumer: its tile, k
@@ -989,17 +1079,12 @@ __global__ void __launch_bounds__(256) ksplit_kernel(Problem p, int tiles_m, int
   auto issue_direct = [&]() __attribute__((always_inline)) {
     return !k_tail || is_k != nk - 1;
   };
-  // Register path for one step (the K tail): loads, placement, LDS writes.
+  // Register path for one step (the K tail).  Nothing of it stays
+  // outstanding: without this wait the compiler, merging paths, would wait
+  // on all vector memory before later LDS reads, which includes the direct
+  // loads in flight.
   auto issue_regs = [&](float *st) __attribute__((always_inline)) {
-    Stage<KsTile> sg;
-    const bool g = load_step<KsTile>(sg, p, is_m0, is_n0, is_k * 64, true, tid);
-    if (g)
-      ks_store_stage<true>(sg, st, tid);
-    else
-      ks_store_stage<false>(sg, st, tid);
-    // Nothing of this path stays outstanding: without this wait the
-    // compiler, merging paths, would wait on all vector memory before later
-    // LDS reads, which includes the direct loads in flight.
+    ks_fill_partial(p, is_m0, is_n0, is_k * 64, st, lane, wave);
     __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(0));
   };
   auto abase_of = [&]() __attribute__((always_inline)) {
@@ -1011,7 +1096,10 @@ __global__ void __launch_bounds__(256) ksplit_kernel(Problem p, int tiles_m, int
 
   f32x4 acc[4][4];
   issue_origin();
-  // Prologue: steps 0..2 in flight, step 0 visible, its fragments read.
+  // Prologue: steps 0..2 in flight; wait for step 0 only.  `after` counts
+  // the direct loads issued after step 0's (a register step completes
+  // everything before it).
+  int after = 0;
   for (int s = 0; s < kKsStages && s < steps; ++s) {
     const unsigned st = lds_u + s * kKsStageFloats * 4;
     if (issue_direct()) {
@@ -1021,34 +1109,31 @@ __global__ void __launch_bounds__(256) ksplit_kernel(Problem p, int tiles_m, int
         ks_load_to_lds16(voff[q], ab, st + wave_a + q * 4 * 64 * 4);
         ks_load_to_lds16(voff[4 + q], bb, st + wave_b + q * 4 * 64 * 4);
       }
+      if (s > 0) after += kKsDmaPerWave;
     } else {
       issue_regs(lds + s * kKsStageFloats);
+      after = 0;
     }
     issue_advance();
   }
-  __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(0));
-  ks_lds_barrier();
+  ks_wait_own(after);
   KsFrag f0, f1;
   ks_read_frag(f0, lds, lane, wave);
 
   // One step: `fc` holds this step's fragments, `fn` receives the next's.
   auto step = [&](int it, KsFrag &fc, KsFrag &fn) __attribute__((always_inline)) {
     const int cur = it % kKsStages;
-    // Stage of step it + 1 has landed (own loads), and every wave holds the
-    // fragments of step it (own reads), so after the barrier stage `cur`
-    // may be refilled and stage it + 1 may be read.  Step it + 2 is the
-    // issue side's previous step.
+    // This wave's reads of stage `cur` (the fragments of step it) are
+    // complete, so the stage may be refilled; once step it + 1's loads have
+    // landed its stage may be read.  Step it + 2 is the issue side's
+    // previous step.
+    __builtin_amdgcn_s_waitcnt(kLgkmWait0);
     if (it + 1 < steps) {
       const bool next2_direct =
           it + 2 < steps && (!k_tail || (is_k + nk - 1) % nk != nk - 1);
-      if (next2_direct)
-        __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(kKsDmaPerWave));
-      else
-        __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(0));
-    }
-    ks_lds_barrier();
-    if (it + 1 < steps)
+      ks_wait_own(next2_direct ? kKsDmaPerWave : 0);
       ks_read_frag(fn, lds + ((it + 1) % kKsStages) * kKsStageFloats, lane, wave);
+    }
     // Step it + 3 goes into stage `cur`: direct loads spread over this
     // step's MFMAs, or (for a K tail) the register path before them.
     if (it + kKsStages < steps) {
@@ -1064,36 +1149,15 @@ __global__ void __launch_bounds__(256) ksplit_kernel(Problem p, int tiles_m, int
       ks_mfma<false>(acc, fc, voff, nullptr, nullptr, 0, 0);
     }
   };
-  // Tile done: add the four partial tiles in wave order and store.
+  // Tile done: add the four partial tiles in wave order and store.  The
+  // next tile's partial tiles overwrite the buffer: every wave must have
+  // read it first (the k loop has no barrier of its own).
   auto finish_tile = [&](int t) __attribute__((always_inline)) {
     int m0, n0;
     bool interior;
     tile_origin<KsTile>(lid + t * G, tiles_m, tiles_n, m0, n0, interior, p);
-    const int l16 = lane & 15, g = lane >> 4;
-    float *mine = red + wave * 64 * 64;
-#pragma unroll
-    for (int bm = 0; bm < 4; ++bm)
-#pragma unroll
-      for (int bn = 0; bn < 4; ++bn)
-        *reinterpret_cast<f32x4 *>(mine + 4 * ks_a_pos(16 * bm + l16, 4 * bn + g)) =
-            acc[bm][bn];
-    ks_lds_barrier();
-    // Wave w finishes rows 16 w .. 16 w + 15: lane (row, q) holds chunks
-    // 4 j + q, j = 0..3, of its row.
-    const int row = 16 * wave + (lane >> 2), q = lane & 3;
-    const int gm = m0 + row;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = 4 * j + q;
-      f32x4 v = *reinterpret_cast<const f32x4 *>(red + 4 * ks_a_pos(row, c));
-#pragma unroll
-      for (int w = 1; w < 4; ++w)
-        v += *reinterpret_cast<const f32x4 *>(red + w * 64 * 64 + 4 * ks_a_pos(row, c));
-      const int gn = n0 + 4 * c;
-      *reinterpret_cast<f32x4u *>(p.C + (long long)gm * p.ldc + gn) = v;
-    }
-    // The partial-tile buffer is rewritten only at the next tile's end,
-    // after the barriers of that tile's steps.
+    ks_finish_tile(acc, red, p, m0, n0, lane, wave);
+    if (t + 1 < my_tiles) ks_lds_barrier();
   };
 
   // Tile loop outside, k steps inside (unrolled by two so that the fragment
@@ -1114,6 +1178,131 @@ __global__ void __launch_bounds__(256) ksplit_kernel(Problem p, int tiles_m, int
       f0 = f1;  // the next step's fragments are read into f1
     }
     finish_tile(t);
+  }
+}
+
+// ksplit_kernel for K a multiple of 64, without its per-step conditions.
+// The issue side never runs past the last step: having reached it, it
+// issues that step's loads again (in bounds; nothing reads them), so every
+// step waits for the same count, reads the next step's fragments and issues
+// one step of loads, and the loop's only branches are its own and the issue
+// side's move to the next tile.  Same launch conditions as ksplit_kernel.
+__global__ void __launch_bounds__(256) ksplit_whole_kernel(Problem p, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(16))) float lds[kKsStages * kKsStageFloats + kKsRedFloats];
+  float *const red = lds + kKsStages * kKsStageFloats;
+  const unsigned lds_u = (unsigned)(uintptr_t)(lds_void_t *)lds;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ntiles = tiles_m * tiles_n;
+  const int nk = p.K / 64;
+  const int G = gridDim.x;
+  const int lid = xcd_remap(blockIdx.x, G);
+  if (lid >= ntiles) return;  // uniform per workgroup
+  const int my_tiles = (ntiles - lid + G - 1) / G;
+
+  unsigned voff[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    voff[q] = (unsigned)(ks_dma_a_elem(q, lane, wave, p.lda) * 4);
+    voff[4 + q] = (unsigned)(dma_b_elem<16>(64 * (4 * wave + q) + lane, p.ldb) * 4);
+  }
+  const unsigned wave_a = (unsigned)(wave * kKsQuarterFloats * 4);  // LDS bytes
+  const unsigned wave_b = (unsigned)((64 * 64 + 16 * wave * 64) * 4);
+
+  // Issue side: tile is_t, k step is_k, and that step's base addresses.
+  int is_t = 0, is_k = 0;
+  const float *a_is = p.A, *b_is = p.B;
+  const long long b_step = 64LL * p.ldb;
+  auto issue_origin = [&]() __attribute__((always_inline)) {
+    int m0, n0;
+    bool interior;
+    tile_origin<KsTile>(lid + is_t * G, tiles_m, tiles_n, m0, n0, interior, p);
+    a_is = p.A + (long long)m0 * p.lda;
+    b_is = p.B + n0;
+  };
+  auto issue_advance = [&]() __attribute__((always_inline)) {
+    if (++is_k < nk) {
+      a_is += 64;
+      b_is += b_step;
+    } else if (is_t + 1 < my_tiles) {
+      is_k = 0;
+      ++is_t;
+      issue_origin();
+    } else {
+      is_k = nk - 1;  // past the last step: repeat its loads
+    }
+  };
+  // Stages of steps it, it + 1 and it + 2 (float offsets into lds).
+  int o_c = 0, o_1 = kKsStageFloats, o_2 = 2 * kKsStageFloats;
+  auto issue_into = [&](int o) __attribute__((always_inline)) {
+    const unsigned st = lds_u + o * 4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ks_load_to_lds16(voff[q], a_is, st + wave_a + q * 4 * 64 * 4);
+      ks_load_to_lds16(voff[4 + q], b_is, st + wave_b + q * 4 * 64 * 4);
+    }
+    issue_advance();
+  };
+
+  f32x4 acc[4][4];
+  issue_origin();
+  issue_into(o_c);
+  issue_into(o_1);
+  issue_into(o_2);
+  ks_wait_own(2 * kKsDmaPerWave);
+  KsFrag f0, f1;
+  ks_read_frag(f0, lds + o_c, lane, wave);
+
+  // One step: wait for step it + 1 (step it + 2's loads stay in flight),
+  // read its fragments, and run step it's MFMAs with step it + 3's loads
+  // going into step it's stage, whose fragments this wave already holds.
+  auto step = [&](auto acc_mode, KsFrag &fc, KsFrag &fn) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(kLgkmWait0);
+    ks_wait_own(kKsDmaPerWave);
+    ks_read_frag(fn, lds + o_1, lane, wave);
+    const unsigned st = lds_u + o_c * 4;
+    ks_mfma<true, decltype(acc_mode)::value>(acc, fc, voff, a_is, b_is, st + wave_a,
+                                              st + wave_b);
+    issue_advance();
+    const int o = o_c;
+    o_c = o_1;
+    o_1 = o_2;
+    o_2 = o;
+  };
+  using First = std::integral_constant<KsAcc, kKsFromZero>;
+  using Next = std::integral_constant<KsAcc, kKsInPlace>;
+
+  for (int t = 0; t < my_tiles; ++t) {
+    // The tile's first step starts its accumulators from 0.
+    if (nk == 1) {
+      step(First{}, f0, f1);
+      f0 = f1;  // the next step's fragments are read into f1
+    } else {
+      step(First{}, f0, f1);
+      step(Next{}, f1, f0);
+      for (int kk = 2; kk + 1 < nk; kk += 2) {
+        step(Next{}, f0, f1);
+        step(Next{}, f1, f0);
+      }
+      if (nk & 1) {
+        step(Next{}, f0, f1);
+        f0 = f1;
+      }
+    }
+    // 24 wait states after the last MFMA before its results are read
+    // (mfma_inplace); the repeated loads of the last tile land before the
+    // workgroup ends.
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+    __builtin_amdgcn_sched_barrier(0);
+    if (t + 1 == my_tiles) ks_wait_own(0);
+    int m0, n0;
+    bool interior;
+    tile_origin<KsTile>(lid + t * G, tiles_m, tiles_n, m0, n0, interior, p);
+    ks_finish_tile(acc, red, p, m0, n0, lane, wave);
+    if (t + 1 < my_tiles) ks_lds_barrier();
   }
 }
 
@@ -1874,24 +2063,6 @@ __device__ inline void arow16_read_b(float (&b)[Arow16::TBN], const Arow16Lane &
     b[bn] = o.b[bn][KROW * Arow16::BN + BUF * Arow16::B_FLOATS];
 }
 
-// One MFMA of the stream, accumulating in place (FIRST: from 0, so the tile
-// needs no zeroed accumulators).  Issued as inline assembly with the
-// accumulator tied to the destination: with the builtin, the register
-// allocator renamed destinations away from their sources and copied the
-// accumulators back, about 600 accumulator moves per two tiles in the MFMA
-// stream (measured: 294 -> 288 us on 16384 x 16384 x 64).  The compiler does
-// not see these as MFMAs, so it inserts no wait states after them: sources
-// come from LDS reads (waited for by lgkmcnt, which the compiler does track),
-// each chain's next MFMA is 32 MFMAs later, and the tile ends with 24 wait
-// states before anything may read a result.
-template <bool FIRST>
-__device__ __forceinline__ void arow16_mfma(f32x4 &acc, float b, float a) {
-  if constexpr (FIRST)
-    asm volatile("v_mfma_f32_16x16x4_f32 %0, %1, %2, 0" : "=a"(acc) : "v"(b), "v"(a));
-  else
-    asm volatile("v_mfma_f32_16x16x4_f32 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
-}
-
 template <bool STORE, int BUF>
 __device__ __forceinline__ void arow16_tile(Acc16 &acc, Acc16 &prev, const Problem &p,
                                             int m0, int pn0, int nn0, const float *lds,
@@ -1919,7 +2090,7 @@ __device__ __forceinline__ void arow16_tile(Acc16 &acc, Acc16 &prev, const Probl
     for (int bm = 0; bm < W::TBM; ++bm) {
 #pragma unroll
       for (int bn = 0; bn < W::TBN; ++bn)
-        arow16_mfma<grp == 0>(acc[bm][bn], bcur[bn], acur[bm][u]);
+        mfma_inplace<grp == 0>(acc[bm][bn], bcur[bn], acur[bm][u]);
       // rows of 4 MFMAs: the next B's direct loads after rows 0, 2, ..,
       // then one C store after every third row
       const int row = grp * W::TBM + bm;
@@ -1969,7 +2140,7 @@ __device__ __forceinline__ void arow16_tile(Acc16 &acc, Acc16 &prev, const Probl
   mfma_rows(I3{}, I2{}, a1, a0, b0, b1);
   mfma_rows(I3{}, I3{}, a1, a0, b1, b0);
   // 24 wait states after the last MFMA before anything may read its result
-  // (arow16_mfma).
+  // (mfma_inplace).
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
   __builtin_amdgcn_sched_barrier(0);
@@ -2210,6 +2381,12 @@ hipError_t launch_ksplit(const Problem &p, hipStream_t s) {
   const long long tiles_m = ceil_div(p.M, 64), tiles_n = ceil_div(p.N, 64);
   const long long ntiles = tiles_m * tiles_n;
   if (ntiles > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (p.K % 64 == 0) {
+    long long grid = resident_workgroups<ksplit_whole_kernel, 256>();
+    if (grid > ntiles) grid = ntiles;
+    return launch_kernel(ksplit_whole_kernel, dim3((unsigned)grid), dim3(256), s, p,
+                         (int)tiles_m, (int)tiles_n);
+  }
   long long grid = resident_workgroups<ksplit_kernel, 256>();
   if (grid > ntiles) grid = ntiles;
   return launch_kernel(ksplit_kernel, dim3((unsigned)grid), dim3(256), s, p, (int)tiles_m,
