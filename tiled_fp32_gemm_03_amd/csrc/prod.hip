@@ -841,26 +841,6 @@ __global__ void __launch_bounds__(S::NT) lds_dma16_kernel(Problem p, int tiles_m
   }
 }
 
-// One v_mfma_f32_16x16x4_f32 accumulating in place (FIRST: from 0, so a
-// tile needs no zeroed accumulators), for the A-resident and the
-// whole-step K-split kernels.  Issued as inline assembly with the
-// accumulator tied to the destination: with the builtin, the register
-// allocator renamed destinations away from their sources and copied the
-// accumulators back inside the MFMA stream (about 600 accumulator moves per
-// two tiles of the A-resident kernel: measured 294 -> 288 us on 16384 x
-// 16384 x 64).  The compiler does not see these as MFMAs, so it inserts no
-// wait states after them: the callers take their sources straight from LDS
-// reads (waited for by lgkmcnt, which the compiler does track), keep each
-// chain's next MFMA 16 or more MFMAs later, and issue 24 wait states after
-// the stream before anything reads a result.
-template <bool FIRST>
-__device__ __forceinline__ void mfma_inplace(f32x4 &acc, float b, float a) {
-  if constexpr (FIRST)
-    asm volatile("v_mfma_f32_16x16x4_f32 %0, %1, %2, 0" : "=a"(acc) : "v"(b), "v"(a));
-  else
-    asm volatile("v_mfma_f32_16x16x4_f32 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
-}
-
 // ---- 64x64 tiles with K split over the waves, 3-stage direct-load pipe --
 // For products with about one 64x64 tile per CU (1024^3 has 256), where a
 // k step of a 64x64 tile is too short to hide the latency of its loads.

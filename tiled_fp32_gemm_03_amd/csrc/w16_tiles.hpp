@@ -139,14 +139,38 @@ __device__ inline void w16_read_b(float (&b)[W::TBN], const float *st, int h, in
 
 // MFMA t of a chunk over all blocks of the wave tile, from separately held
 // A (chunk) and B (MFMA t) fragments.
-template <class W>
+// One v_mfma_f32_16x16x4_f32 accumulating in place (FIRST: from 0, so a
+// tile needs no zeroed accumulators), for the A-resident and the
+// whole-step K-split kernels and the 128x128-wave
+// tiles.  Issued as inline assembly with the
+// accumulator tied to the destination: with the builtin, the register
+// allocator renamed destinations away from their sources and copied the
+// accumulators back inside the MFMA stream (about 600 accumulator moves per
+// two tiles of the A-resident kernel: measured 294 -> 288 us on 16384 x
+// 16384 x 64).  The compiler does not see these as MFMAs, so it inserts no
+// wait states after them: the callers take their sources straight from LDS
+// reads (waited for by lgkmcnt, which the compiler does track), keep each
+// chain's next MFMA 16 or more MFMAs later, and issue 24 wait states after
+// the stream before anything reads a result.
+template <bool FIRST>
+__device__ __forceinline__ void mfma_inplace(f32x4 &acc, float b, float a) {
+  if constexpr (FIRST)
+    asm volatile("v_mfma_f32_16x16x4_f32 %0, %1, %2, 0" : "=a"(acc) : "v"(b), "v"(a));
+  else
+    asm volatile("v_mfma_f32_16x16x4_f32 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
+}
+
+template <class W, bool IN_PLACE = false>
 __device__ inline void w16_mfma_t(f32x4 (&acc)[W::TBM][W::TBN], const f32x4 (&a)[W::TBM],
                                   const float (&b)[W::TBN], int t) {
 #pragma unroll
   for (int bm = 0; bm < W::TBM; ++bm)
 #pragma unroll
     for (int bn = 0; bn < W::TBN; ++bn)
-      acc[bm][bn] = __builtin_amdgcn_mfma_f32_16x16x4f32(b[bn], a[bm][t], acc[bm][bn], 0, 0, 0);
+      if constexpr (IN_PLACE)
+        mfma_inplace<false>(acc[bm][bn], b[bn], a[bm][t]);
+      else
+        acc[bm][bn] = __builtin_amdgcn_mfma_f32_16x16x4f32(b[bn], a[bm][t], acc[bm][bn], 0, 0, 0);
 }
 
 // Guarded fill of one stage for the partial k step of a tile (k0 < K <
@@ -269,6 +293,12 @@ __device__ __forceinline__ void big16_body(Problem p, int tiles_m, int tiles_n, 
   // VQ = BK / 4: the partial step runs the pinned loop.
   constexpr bool TAIL = VQ > 0;
   constexpr bool PEEL = TAIL && VQ < W::BK / 4;
+  // The tail forms' MFMAs accumulate in place (mfma_inplace): with the
+  // builtin, the register allocator copied one accumulator block out and
+  // back every step of their loop (24 moves; measured 2 us of the 4096 x
+  // 4096 x 2049 product).  The plain form keeps the builtin, which is
+  // faster there (930 against 935 us on 4096^3).
+  constexpr bool kInPlace = TAIL && W::TBM * W::TBN * 4 == 256;
   static_assert(VQ == 0 || VQ == 1 || VQ == 2 || VQ == 4 || VQ == W::BK / 4, "k quads");
   __shared__ __attribute__((aligned(16))) float lds[2 * W::STAGE];
   const unsigned lds_u = (unsigned)(uintptr_t)(lds_void_t *)lds;
@@ -296,6 +326,10 @@ __device__ __forceinline__ void big16_body(Problem p, int tiles_m, int tiles_n, 
   const unsigned wave_a = (unsigned)(wave * W::A_DMA * 1024);
   const unsigned wave_b = (unsigned)(W::A_FLOATS * 4 + wave * W::B_DMA * 1024);
   const long long b_step = (long long)W::BK * p.ldb;
+  // From the step before a partial one to the last whole step inside the
+  // matrices, which starts at column (A) or row (B) K - BK.
+  const long long a_inc_tail = p.K - (long long)(nk - 1) * W::BK;
+  const long long b_inc_tail = a_inc_tail * p.ldb;
 
   auto tile_base = [&](int t, const float *&ab, const float *&bb) __attribute__((always_inline)) {
     int m0, n0;
@@ -337,14 +371,12 @@ __device__ __forceinline__ void big16_body(Problem p, int tiles_m, int tiles_n, 
     for (int kk = 0; kk < nk_full; ++kk) {
       const bool last = !PEEL && kk + 1 == nk;     // a peeled partial step is the last
       const bool pre_tail = TAIL && kk + 2 == nk;  // the next step is the partial one
-      const float *ia = last ? nt_a : is_a + W::BK;
-      const float *ib = last ? nt_b : is_b + b_step;
-      if constexpr (TAIL) {  // stay inside the matrices; the fill below replaces this stage
-        if (pre_tail) {
-          ia = is_a - (long long)(nk - 2) * W::BK + (p.K - W::BK);
-          ib = is_b - (long long)(nk - 2) * b_step + (long long)(p.K - W::BK) * p.ldb;
-        }
-      }
+      // Step kk + 1's operands; before a partial step, the last whole step
+      // inside the matrices (A columns and B rows [K - BK, K)), which the
+      // fill below replaces.  Only a select per step: the increments are
+      // fixed per product.
+      const float *ia = last ? nt_a : is_a + (pre_tail ? a_inc_tail : (long long)W::BK);
+      const float *ib = last ? nt_b : is_b + (pre_tail ? b_inc_tail : b_step);
       __builtin_amdgcn_s_waitcnt(vmcnt_wait_imm(0));  // this step's loads (own)
       ks_lds_barrier();                                // everyone's; stage stage^1 free
       const float *st = lds + stage * W::STAGE;
@@ -383,8 +415,11 @@ __device__ __forceinline__ void big16_body(Problem p, int tiles_m, int tiles_n, 
           for (int bm = 0; bm < W::TBM; ++bm) {
 #pragma unroll
             for (int bn = 0; bn < W::TBN; ++bn)
-              acc[bm][bn] =
-                  __builtin_amdgcn_mfma_f32_16x16x4f32(bc[bn], ac[bm][u], acc[bm][bn], 0, 0, 0);
+              if constexpr (kInPlace)
+                mfma_inplace<false>(acc[bm][bn], bc[bn], ac[bm][u]);
+              else
+                acc[bm][bn] =
+                    __builtin_amdgcn_mfma_f32_16x16x4f32(bc[bn], ac[bm][u], acc[bm][bn], 0, 0, 0);
             constexpr int kRowsPerLoad = 2;
             const int row = grp * W::TBM + bm;
             if (row % kRowsPerLoad == 0 && row / kRowsPerLoad < W::DMA) {
@@ -414,19 +449,22 @@ __device__ __forceinline__ void big16_body(Problem p, int tiles_m, int tiles_n, 
           if constexpr (PEEL) {
             // The partial step itself, here: the next tile's first loads
             // go into the stage this step just read (every wave is past
-            // the barrier above, so done with it); then only the first VQ
-            // MFMA groups (the others hold no k below K and would add exact
-            // zeros), with fragments read as they go.
+            // the barrier above, so done with it) -- none after the last
+            // tile, where nothing reads them and the final wait would sit
+            // on their latency (7 us of the 4096 x 4096 x 2049 product);
+            // then only the first VQ MFMA groups (the others hold no k
+            // below K and would add exact zeros), with fragments read as
+            // they go.
             ks_lds_barrier();  // the fill is everyone's
             const float *pst = lds + (stage ^ 1) * W::STAGE;
-            issue(lds_u + stage * W::STAGE * 4, nt_a, nt_b, 0, W::DMA);
+            if (t + 1 < my_tiles) issue(lds_u + stage * W::STAGE * 4, nt_a, nt_b, 0, W::DMA);
             f32x4 a[W::TBM];
             float b[W::TBN];
 #pragma unroll
             for (int grp = 0; grp < VQ; ++grp) {
               if (grp % 4 == 0) w16_read_a<W>(a, pst, grp / 4, lane, wm);
               w16_read_b<W>(b, pst, grp / 4, grp % 4, lane, wn);
-              w16_mfma_t<W>(acc, a, b, grp % 4);
+              w16_mfma_t<W, kInPlace>(acc, a, b, grp % 4);
             }
             ia = nt_a;    // the operands most recently issued
             ib = nt_b;
@@ -449,6 +487,13 @@ __device__ __forceinline__ void big16_body(Problem p, int tiles_m, int tiles_n, 
 #pragma unroll
           for (int j = 0; j < W::TBN; ++j) asm volatile("" : "+a"(acc[i][j]));
       }
+    }
+    if constexpr (kInPlace) {
+      // 24 wait states after the last MFMA before its results are read
+      // (mfma_inplace).
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+      __builtin_amdgcn_sched_barrier(0);
     }
     int m0, n0;
     bool interior;
