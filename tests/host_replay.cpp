@@ -375,6 +375,46 @@ void boundary_b(int rows, const char *family) {
       check_voff(s, dma_b_elem<BCH>(64 * blk + lane, ld), family);
 }
 
+// The K-split kernel's per-wave A quarters: at the guard's boundary every
+// lane offset fits, the layout is a bijection of a wave's 256 chunk
+// positions, a direct load's lane lands where the layout puts its chunk,
+// and a fragment read (one chunk of 16 consecutive rows) touches distinct
+// 16-byte bank groups within every 8 and every 16 lanes.
+void check_ksplit_quarters() {
+  const Shape s{64, 64, 64, 0, 0, 0, "K-split A quarters"};
+  const long long ld = (1LL << 32) / (64 * 4LL);
+  if (!lane_offsets_fit(64, ld, 4) || lane_offsets_fit(64, ld + 1, 4))
+    fail(s, "guard boundary (K-split A)", ld, 64);
+  for (int wave = 0; wave < 4; ++wave)
+    for (int q = 0; q < 4; ++q)
+      for (int lane = 0; lane < 64; ++lane) {
+        const long long e = ks_dma_a_elem(q, lane, wave, ld);
+        check_voff(s, e, "K-split A lane offset at the boundary");
+        const int r = (int)(e / ld), c = (int)((e % ld) - 16 * wave) / 4;
+        ++g_checks;
+        if (r != 16 * q + lane / 4 || c < 0 || c > 3 || ks_a_pos(r, c) != 64 * q + lane)
+          fail(s, "K-split A load position", 64 * q + lane, ks_a_pos(r, c));
+      }
+  std::vector<char> seen(256, 0);
+  for (int r = 0; r < 64; ++r)
+    for (int c = 0; c < 4; ++c) {
+      const int pos = ks_a_pos(r, c);
+      ++g_checks;
+      if (pos < 0 || pos >= 256 || seen[pos]++) fail(s, "K-split A layout not a bijection", r, c);
+    }
+  for (int r0 = 0; r0 < 64; r0 += 16)
+    for (int c = 0; c < 4; ++c)
+      for (int span : {8, 16})
+        for (int l0 = 0; l0 < 16; l0 += span) {
+          std::vector<char> bank(span, 0);
+          for (int l = l0; l < l0 + span; ++l) {
+            const int b = ks_a_pos(r0 + l, c) % span;
+            ++g_checks;
+            if (bank[b]++) fail(s, "K-split A fragment read bank conflict", r0 + l, c);
+          }
+        }
+}
+
 // ---- windows, exhaustively on small sizes ---------------------------------------
 void check_windows() {
   const Shape s{0, 0, 0, 0, 0, 0, "windows"};
@@ -505,6 +545,7 @@ int main(int argc, char **argv) {
   boundary_b<32>(32, "128-column B steps, BK 32");
   boundary_b<32>(64, "128-column B steps, BK 64");
   boundary_b<16>(64, "64-column B steps, BK 64");
+  check_ksplit_quarters();
   check_windows();
   check_orders();
   std::printf("replay: %d shapes, %lld checks, %d failures\n", (int)shapes.size(), g_checks,
