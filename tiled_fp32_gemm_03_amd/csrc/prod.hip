@@ -2348,10 +2348,11 @@ hipError_t launch_kloop(const Problem &p, hipStream_t s) {
   return launch_grid<S, prod_kernel<S>>(p, s);
 }
 
-// K split over the waves of a 64x64 tile (ksplit_kernel) when A and B rows
-// are 16-byte aligned, N % 4 == 0, C is at least one tile each way and the
-// lane offsets fit in 32 bits; otherwise the register-staged 64x64x32
-// kernel.
+// K split over the waves of a 64x64 tile when A and B rows are 16-byte
+// aligned, N % 4 == 0, C is at least one tile each way and the lane offsets
+// fit in 32 bits -- the whole-step form (ksplit_whole_kernel) when K is a
+// multiple of 64, else ksplit_kernel; otherwise the register-staged
+// 64x64x32 kernel.
 hipError_t launch_ksplit(const Problem &p, hipStream_t s) {
   const bool ok = (reinterpret_cast<uintptr_t>(p.A) & 15) == 0 &&
                   (reinterpret_cast<uintptr_t>(p.B) & 15) == 0 && (p.lda & 3) == 0 &&
