@@ -140,9 +140,9 @@ __device__ inline void w16_read_b(float (&b)[W::TBN], const float *st, int h, in
 // MFMA t of a chunk over all blocks of the wave tile, from separately held
 // A (chunk) and B (MFMA t) fragments.
 // One v_mfma_f32_16x16x4_f32 accumulating in place (FIRST: from 0, so a
-// tile needs no zeroed accumulators), for the A-resident and the
-// whole-step K-split kernels and the 128x128-wave
-// tiles.  Issued as inline assembly with the
+// tile needs no zeroed accumulators), for the A-resident kernel, the
+// whole-step K-split kernel and the tail forms of the 128x128-wave kernel.
+// Issued as inline assembly with the
 // accumulator tied to the destination: with the builtin, the register
 // allocator renamed destinations away from their sources and copied the
 // accumulators back inside the MFMA stream (about 600 accumulator moves per
@@ -297,7 +297,10 @@ __device__ __forceinline__ void big16_body(Problem p, int tiles_m, int tiles_n, 
   // builtin, the register allocator copied one accumulator block out and
   // back every step of their loop (24 moves; measured 2 us of the 4096 x
   // 4096 x 2049 product).  The plain form keeps the builtin, which is
-  // faster there (930 against 935 us on 4096^3).
+  // faster there (930 against 935 us on 4096^3).  The accumulators are
+  // zeroed ahead of the k loop, whose first MFMA follows a wait, a barrier
+  // and the fragment reads (37 instructions or more in the built code), so
+  // the zeroing needs no wait states of its own.
   constexpr bool kInPlace = TAIL && W::TBM * W::TBN * 4 == 256;
   static_assert(VQ == 0 || VQ == 1 || VQ == 2 || VQ == 4 || VQ == W::BK / 4, "k quads");
   __shared__ __attribute__((aligned(16))) float lds[2 * W::STAGE];
