@@ -79,8 +79,10 @@ extern "C" {
  * permuted per row so fragment reads are free of bank conflicts), one
  * barrier per 32-deep k step; a partial last k step is filled through
  * registers with zeros past K; edge tiles are moved back inside C, and thin
- * remainder strips run on their own kernel.  Few-tile products split each
- * tile's k steps over the 4 waves and add the partial tiles in wave order;
+ * remainder strips run on their own kernel, which also computes whole
+ * products of at most 8 rows (a stream of B, read once).  Few-tile
+ * products split each tile's k steps over the 4 waves and add the partial
+ * tiles in wave order;
  * K = 64 products keep A in LDS and stream B.  The "one thread, several
  * outputs" and "register / wave / instruction block" pyramid the pages
  * point to (geek-doc.cn sections 三 and 五) on CDNA4 matrix cores. */
@@ -123,7 +125,9 @@ int gemm_f32(int M, int N, int K, const float *A, int lda, const float *B,
  *   config  -1 picks the entry gemm_f32 would use for this shape; otherwise
  *           an index below gemm_f32_num_configs(variant).  Production
  *           entries whose kernel holds all of K in one LDS stage ("panel"
- *           entries, reported with BK = their K limit) accept K <= BK only.
+ *           entries, reported with BK = their K limit) accept K <= BK only;
+ *           the thin-M strip entry (reported with BN = 16, BK = 1 and BM =
+ *           the rows a workgroup holds for this M) accepts M <= 8 only.
  *           Whatever the entry, a thin remainder strip of rows or columns
  *           (an overhanging tile at most 1/8 full) is computed by a second
  *           launch with small tiles on the same stream.

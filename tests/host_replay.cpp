@@ -274,31 +274,43 @@ void replay_arow16(const Shape &s, int slots) {
 // 512 threads: 4 column quads x 128 k slices, 16 columns per workgroup.
 void replay_strip(const Shape &s) {
   const int wgs = (int)ceil_div(s.N, 16);
+  const int R = strip_rows(s.M), NB = strip_batch_quads(R), KB = 512;
+  auto row_of = [&](int r) { return r < s.M ? r : s.M - 1; };  // rows past M read row M - 1
   for (int w = 0; w < wgs; ++w) {
     const long long n0 = 16LL * xcd_remap(w, wgs);
     const bool whole = n0 + 16 <= s.N;
-    for (int tid = 0; tid < 512; tid += 1) {
-      const int c4 = (tid & 3) * 4, ks = tid >> 2;
+    for (int tid = 0; tid < 512; ++tid) {
+      const int c4 = (tid & 3) * 4, k0 = 4 * (tid >> 2);
       const int valid = (int)(s.N - n0) - c4;
-      for (int k = ks; k < s.K; k += 128) {
-        if (k != ks && k + 128 < s.K) continue;  // first and last k of the slice
+      auto b_row = [&](int k, const char *what) {
         if (whole) {
-          check_b(s, (long long)k * s.ldb + n0 + c4, "strip B load");
+          check_b(s, (long long)k * s.ldb + n0 + c4, what);
         } else {
           for (int j = 0; j < 4 && j < valid; ++j) {
             ++g_checks;
-            if (n0 + c4 + j >= s.N) fail(s, "strip B element", k, n0 + c4 + j);
+            if (k < 0 || k >= s.K || n0 + c4 + j >= s.N) fail(s, what, k, n0 + c4 + j);
           }
         }
-        for (int r = 0; r < 8; ++r) {  // rows past M read row M - 1
-          const int row = r < s.M ? r : s.M - 1;
-          ++g_checks;
-          if (k >= s.K || row < 0 || (long long)row * s.lda + k >= (long long)(s.M - 1) * s.lda + s.K)
-            fail(s, "strip A element", r, k);
+      };
+      int k = k0;
+      for (; k + (NB - 1) * KB + 3 < s.K; k += NB * KB) {  // whole batches
+        if (k != k0 && k + (2 * NB - 1) * KB + 3 < s.K) continue;  // first and last batch
+        for (int u = 0; u < NB; ++u) {
+          for (int t = 0; t < 4; ++t) b_row(k + u * KB + t, "strip B row");
+          for (int r = 0; r < R; ++r)
+            check_a(s, (long long)row_of(r) * s.lda + k + u * KB, "strip A chunk");
         }
       }
+      if (k < s.K) {  // the guarded batch: k past K clamped to K - 1
+        for (int u = 0; u < NB; ++u)
+          for (int t = 0; t < 4; ++t) {
+            const int kk = k + u * KB + t, kc = kk < s.K ? kk : s.K - 1;
+            b_row(kc, "strip guarded B row");
+            for (int r = 0; r < R; ++r) check_a1(s, row_of(r), kc, "strip guarded A");
+          }
+      }
     }
-    for (int tid = 0; tid < 16 * 8; ++tid) {
+    for (int tid = 0; tid < 16 * R; ++tid) {
       const int r = tid / 16, c = tid % 16;
       if (r < s.M && n0 + c < s.N) check_c(s, r, n0 + c, 1, "strip C store");
     }
@@ -323,6 +335,7 @@ void replay_entry(int entry, const Shape &s) {
     replay_entry(19, top);
     return replay_entry(model_kloop(rest.M, rest.N, rest.K).entry, rest);
   }
+  if (prod_kind(entry) == kStrip) return replay_strip(s);
   const ProdConfig &c = prod_config(entry);
   int rm = entry == kRemainderConfig ? 0 : thin_remainder(s.M, c.BM);
   int rn = entry == kRemainderConfig ? 0 : thin_remainder(s.N, c.BN);
@@ -517,6 +530,11 @@ int main(int argc, char **argv) {
       {16384, 16384, 64, 64, 16384, 16384, "skinny_k64"},
       {4097, 4095, 2049, 2053, 4099, 4100, "ragged, padded ld"},
       {8192, 8192, 33, 33, 8192, 8192, "K below two steps"},
+      {1, 4095, 2049, 2049, 4095, 4095, "one-row strip product"},
+      {8, 8191, 4097, 4099, 8193, 8191, "8-row strip product, padded ld"},
+      {4, 16384, 1027, 1027, 16384, 16384, "4-row strip product"},
+      {2, 17, 2051, 2053, 19, 17, "2-row strip, partial column group"},
+      {5, 300, 3, 3, 300, 300, "5-row strip, K below one quad"},
   };
   // edge sweep: sizes around multiples of 16 .. 256, and K tails
   const int sizes[] = {1, 2, 3, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257,

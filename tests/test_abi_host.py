@@ -266,10 +266,23 @@ def test_tile_queries():
         assert g.gemm_f32_tile("valu", i, 9, 9, 9)["config"] == i
     n = g.gemm_f32_num_configs("prod")
     assert n >= 3
+    strip = g.gemm_f32_tile("prod", -1, 1, 4095, 2049)["config"]
     for i in range(n):
+        if i == strip:
+            continue
         q = g.gemm_f32_tile("prod", i, 64, 64, 64)
         assert q["config"] == i and q["threads"] % 64 == 0
         assert q["BM"] % 32 == 0 and q["BN"] % 32 == 0 and q["BK"] % 8 == 0
+    # products of at most 8 rows run the thin-M strip kernel whole; its entry
+    # reports the rows a workgroup holds and refuses a ninth row
+    for M, bm in ((1, 1), (2, 2), (3, 4), (4, 4), (5, 8), (8, 8)):
+        q = g.gemm_f32_tile("prod", -1, M, 77, 5)
+        assert (q["config"], q["BM"], q["BN"], q["threads"]) == (strip, bm, 16, 512)
+    assert g.gemm_f32_tile("prod", -1, 9, 4095, 2049)["config"] != strip
+    with pytest.raises(g.GemmError) as e:
+        g.gemm_f32_tile("prod", strip, 9, 64, 64)
+    assert e.value.status == 7
+    assert _call(9, 64, 64, A=64, B=64, C=64, variant=2, config=strip) == 7
     with pytest.raises(g.GemmError):
         g.gemm_f32_tile("prod", n, 64, 64, 64)
     # automatic choice for the skinny K = 64 shape is a small-K entry; such

@@ -143,7 +143,8 @@ def test_kloop_entries_agree_bitwise_on_ragged_floats(g):
     back inside C (overlapping a neighbour) -- so on float inputs they must
     agree bit for bit.  The shapes leave no thin remainder for any tile size
     (a thin strip goes to the strip kernel, which sums K in another order)."""
-    kloop = [c for c in _prod_configs(g) if _supported(g, c, 1, 1, 65) and c not in OWN_ORDER_ENTRIES]
+    kloop = [c for c in _prod_configs(g)
+             if _supported(g, c, 1, 1, 65) and c not in OWN_ORDER_ENTRIES + (STRIP_ENTRY,)]
     for (M, N, K) in [(1000, 1003, 515), (3000, 300, 129), (700, 4000, 64)]:
         for cfg in kloop:
             t = g.gemm_f32_tile("prod", cfg, M, N, K)
@@ -164,6 +165,9 @@ W16_ENTRIES = (17, 18, 19, 20, 22, 23, 24)
 # or the whole product on the model's entry: the order of whichever runs
 ROW_REGION_ENTRY = 25
 OWN_ORDER_ENTRIES = (KSPLIT_ENTRY,) + W16_ENTRIES + (ROW_REGION_ENTRY,)
+# the thin-M strip kernel on whole products of at most 8 rows (k-slices
+# summed at the end, its own order; test_strip_entry_whole_product)
+STRIP_ENTRY = 26
 LDS_DMA_ENTRY = 15  # 256x256x32 with direct-to-LDS loads
 REG_STAGED_ENTRY = 12  # the same tiles through registers
 
@@ -361,6 +365,39 @@ def test_strip_kernel_long_k(g):
             assert np.array_equal(_run(g, a, b, "prod", cfg), oracle.gemm(a, b)), (cfg, M, N, K)
             a, b = make(M, N, K, "normal", seed=cfg + r + N * K)
             _tol_check(_run(g, a, b, "prod", cfg), oracle.gemm(a, b), K, f"strip long-k cfg {cfg}")
+
+
+def test_strip_entry_whole_product(g):
+    """Products of 1-8 rows: the automatic choice runs the thin-M strip kernel
+    on the whole product.  Column counts below, at and past a group of 16
+    (partial last group), K from 1 to several batches of its k-slices, and
+    padded leading dimensions (odd ldb and ldc: rows only 4-byte aligned)
+    with the padding left untouched."""
+    dev = _dev()
+    strip = g.gemm_f32_tile("prod", -1, 1, 4095, 2049)["config"]
+    assert strip == STRIP_ENTRY
+    for M in range(1, 9):
+        for (N, K) in [(1, 1), (15, 3), (16, 129), (17, 2049), (300, 40), (4095, 513)]:
+            assert g.gemm_f32_tile("prod", -1, M, N, K)["config"] == strip
+            print(f"case: strip entry {M}x{N}x{K}", flush=True)
+            a, b = make(M, N, K, "small_int", seed=M * 1009 + N + K)
+            assert np.array_equal(_run(g, a, b, "prod"), oracle.gemm(a, b)), (M, N, K)
+            a, b = make(M, N, K, "normal", seed=M * 1013 + N * K)
+            _tol_check(_run(g, a, b, "prod"), oracle.gemm(a, b), K, f"strip entry {M}x{N}x{K}")
+    for (M, N, K, lda, ldb, ldc) in [(3, 300, 129, 133, 301, 303), (8, 4095, 2049, 2050, 4097, 4099),
+                                     (1, 17, 5, 5, 21, 17)]:
+        print(f"case: strip entry padded {M}x{N}x{K} lds {lda},{ldb},{ldc}", flush=True)
+        a, b = make(M, N, K, "small_int", seed=lda + ldb)
+        abuf = torch.full((M, lda), 7.0, device=dev)
+        bbuf = torch.full((K, ldb), 7.0, device=dev)
+        cbuf = torch.full((M, ldc), -1.0, device=dev)
+        abuf[:, :K] = torch.from_numpy(a).to(dev)
+        bbuf[:, :N] = torch.from_numpy(b).to(dev)
+        g.matmul(abuf[:, :K], bbuf[:, :N], out=cbuf[:, :N], variant="prod")
+        torch.cuda.synchronize()
+        c = cbuf.cpu().numpy()
+        assert np.array_equal(c[:, :N], oracle.gemm(a, b)), (M, N, K)
+        assert np.all(c[:, N:] == -1.0)
 
 
 def test_guarded_windows_short_rows(g):

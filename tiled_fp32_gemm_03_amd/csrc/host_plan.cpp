@@ -54,8 +54,9 @@ struct Entry {
 
 // Index = launch-table entry of GEMM_F32_PROD.  The kernels behind each
 // entry are in prod.hip and w16_vgpr.hip; the automatic choice uses 16, 19,
-// 21, 22, 23, 24 and 25 (and 3 for thin strips), the others stay reachable
-// by index for tests and measurements.
+// 21, 22, 23, 24, 25 and 26 (and 3 for thin strips), the others stay
+// reachable by index for tests and measurements.  Entry 26 reports the most
+// rows its workgroup holds (BM 8); gemm_f32_tile reports strip_rows(M).
 const Entry kEntries[] = {
     {{128, 128, 32, 2, 2, 2, "128x128x32_w2x2"}, kKloop},
     {{128, 128, 16, 2, 2, 3, "128x128x16_w2x2"}, kKloop},
@@ -83,6 +84,7 @@ const Entry kEntries[] = {
     {{128, 128, 32, 2, 2, 2, "128x128x32_w2x2_ldsdma_mfma16"}, kKsplit},
     {{192, 256, 32, 2, 2, 1, "192x256x32_w2x2_ldsdma_mfma16"}, kKsplit},
     {{256, 256, 32, 2, 2, 1, "rows256_rounds+rest"}, kKsplit},
+    {{8, 16, 1, 4, 2, 1, "strip_rows8_cols16"}, kStrip},
 };
 constexpr int kNumConfigs = sizeof(kEntries) / sizeof(kEntries[0]);
 
@@ -132,9 +134,9 @@ const ProdConfig &prod_config(int index) { return kEntries[index].cfg; }
 ProdKind prod_kind(int index) { return kEntries[index].kind; }
 
 bool prod_supports(int index, int M, int N, int K) {
-  (void)M;
   (void)N;
   if (index < 0 || index >= kNumConfigs) return false;
+  if (kEntries[index].kind == kStrip) return M <= kStripMaxRows;
   return kEntries[index].kind != kPanel || K <= kEntries[index].cfg.BK;
 }
 
@@ -204,14 +206,19 @@ int region_rows(int M, int N, int K) {
   return best_r;
 }
 
-// Shape-based choice.  K <= 64 with many tiles: the A-resident small-K
-// kernel (only B moves per tile; C stores of one tile drained during the
-// next tile's MFMAs), on 16x16 MFMAs with one wave per SIMD when K == 64
-// and the rows are aligned (entry 21's launcher falls back to the 32x32
-// form otherwise).  Otherwise entry 25 when its row cut models faster, else
-// the k-loop entry with the best modelled rate (model_kloop).
+// Shape-based choice.  At most kStripMaxRows rows: the thin-M strip kernel
+// (entry 26), which streams B once, where a tile kernel would fill its 64-
+// to 256-row tiles with one to eight useful rows (1 x 4095 x 2049: 91 us on
+// the 64 x 64 K-split entry, 13 us as a strip).  K <= 64 with many tiles:
+// the A-resident small-K kernel (only B moves per tile; C stores of one
+// tile drained during the next tile's MFMAs), on 16x16 MFMAs with one wave
+// per SIMD when K == 64 and the rows are aligned (entry 21's launcher falls
+// back to the 32x32 form otherwise).  Otherwise entry 25 when its row cut
+// models faster, else the k-loop entry with the best modelled rate
+// (model_kloop).
 int prod_choose(int M, int N, int K, double *full_rate) {
   if (full_rate) *full_rate = 0.0;
+  if (M <= kStripMaxRows) return kStripConfig;
   const long long t256x128 = ceil_div(M, 256) * ceil_div(N, 128);
   if (K <= 64 && t256x128 >= 1024) return 21;
   if (region_rows(M, N, K) > 0) return 25;

@@ -65,8 +65,9 @@ struct ProdConfig {
 
 // kKloop: any K, k loop over steps of BK.  kPanel: all of K in one LDS
 // stage, K <= BK, whole tiles only (remainders become strips).  kKsplit: the
-// 16x16-MFMA families, any K.
-enum ProdKind { kKloop, kPanel, kKsplit };
+// 16x16-MFMA families, any K.  kStrip: the thin-M strip kernel on the whole
+// product, M <= kStripMaxRows.
+enum ProdKind { kKloop, kPanel, kKsplit, kStrip };
 
 int prod_num_configs();
 const ProdConfig &prod_config(int index);
@@ -77,6 +78,16 @@ bool prod_supports(int index, int M, int N, int K);
 // strip may have to go to the thin-M strip kernel.
 constexpr int kRemainderConfig = 3;
 constexpr int kStripMaxRows = 8;
+// The launch-table entry that runs the thin-M strip kernel on a whole
+// product of at most kStripMaxRows rows, and the rows one of its workgroups
+// holds for an M-row product (the kernel is instantiated for 1, 2, 4 and 8).
+constexpr int kStripConfig = 26;
+constexpr int strip_rows(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
+// Quads of k whose loads a strip lane issues before using any (its batch),
+// per row count: measured kernel durations on N = 1024-32768, K = 2049-8192
+// (1 x 4095 x 2049: 10.7, 11.4, 13.0 us for 1, 2, 4 quads; 8 x 8191 x 4096:
+// 36.0 us for 1, 38.8 for 2; 4 x 16384 x 4096: 49.6 for 1, 44.9 for 2).
+constexpr int strip_batch_quads(int rows) { return rows == 2 || rows == 4 ? 2 : 1; }
 
 // Rows (or columns) of a thin remainder strip worth a separate launch: an
 // overhanging tile row that is at most 1/8 full.

@@ -2210,110 +2210,140 @@ __global__ void __launch_bounds__(256) arow16_kernel(Problem p, int panels, int 
   }
 }
 
-// Thin-M kernel for a bottom remainder strip of at most R rows (a strip too
-// thin for MFMA tiles: a 256-row tile holding one valid row would cost a
-// whole round of tiles).  The strip's time is the stream of B, so the kernel
-// is built to keep many 128-bit loads in flight: each workgroup owns 16
-// columns, and its 512 threads are 4 column quads x 128 k-slices (slice q
-// takes k = q, q + 128, ...), each lane loading 4 columns of a B row at once.
-// Workgroups are dealt to the XCDs so that each XCD streams one contiguous
-// band of B's columns, and the 128-byte lines that neighbouring 64-byte
-// column groups share are fetched into one L2 (measured: the one-row strip
-// of a 4097 x 4095 x 2049 product in 11 us instead of 16).
-// A lane issues the loads of a whole batch of its k values (16, or 8 for
-// more than 2 rows) before it uses any of them: a loop whose every
-// iteration may exit would wait for each load in turn, one memory round
-// trip per k.  Each thread accumulates its R x 4 outputs in fp32 over its
-// slice in ascending k; the 128 slice sums are added in slice order through
-// LDS, so the result is deterministic.  Rows of B need only 4-byte
-// alignment.
+// Thin-M kernel for a strip of at most 8 rows: a bottom remainder strip, or
+// a whole product of that few rows (a 64- to 256-row MFMA tile holding one
+// to eight valid rows would cost a whole tile's work per column block).  Its
+// time is the stream of B, read once: each workgroup owns 16 columns, and
+// its 512 threads are 4 column quads x 128 k-slices; slice s takes the
+// quads of consecutive k starting at 4 s, 4 s + 512, ..., so a lane loads
+// 4 B rows of its 4 columns and one 16-byte chunk per A row per quad.  A
+// lane issues the loads of NB quads before it uses any of them (a loop
+// whose every iteration may exit would wait for each load in turn, one
+// memory round trip per quad); the last quads of a lane, any of them past
+// K, go in one guarded batch.  Workgroups are dealt to the XCDs so that
+// each XCD streams one contiguous band of B's columns, and the 128-byte
+// lines that neighbouring 64-byte column groups share are fetched into one
+// L2.  Each thread accumulates its R x 4 outputs in fp32 over its slice in
+// ascending k; the 16 slices of a wave are added by a fixed butterfly of
+// lane exchanges and the 8 waves' sums in wave order through LDS, so the
+// result is deterministic.  Rows of A and B need only 4-byte alignment.
 constexpr int kStripThreads = 512;
 constexpr int kStripCols = 16;
 constexpr int kStripSlices = kStripThreads / (kStripCols / 4);
+constexpr int kStripWaves = kStripThreads / 64;
 
-template <int R>
+template <int R, int NB>
 __global__ void __launch_bounds__(kStripThreads) strip_kernel(Problem p) {
-  constexpr int KS = kStripSlices;
-  __shared__ float red[KS][R][kStripCols];
+  constexpr int KB = 4 * kStripSlices;  // k per quad round of the workgroup
+  __shared__ float red[kStripWaves][R][kStripCols];
   const int tid = threadIdx.x;
   const int c4 = (tid & 3) * 4;  // first of this lane's 4 columns
-  const int ks = tid >> 2;       // k slice
+  const int k0 = 4 * (tid >> 2);  // first k of this lane's first quad
   const long long n0 = (long long)xcd_remap(blockIdx.x, gridDim.x) * kStripCols;
   float acc[R][4];
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[r][j] = 0.f;
+  // Rows past M read row M - 1 (never stored), so no load is conditional.
+  const float *arow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) arow[r] = p.A + (long long)(r < p.M ? r : p.M - 1) * p.lda;
+  const bool whole = n0 + kStripCols <= p.N;
+  const int valid = (int)(p.N - n0) - c4;  // columns of this lane inside C (whole: >= 4)
   const float *bp = p.B + n0 + c4;
-  if (n0 + kStripCols <= p.N) {  // whole workgroup inside: 128-bit loads
-    constexpr int NB = R <= 2 ? 16 : 8;  // k values per batch
-    int k = ks;
-    for (; k + (NB - 1) * KS < p.K; k += NB * KS) {
-      f32x4 b[NB];
-      float a[R][NB];
+  auto load_b = [&](int k) __attribute__((always_inline)) {
+    f32x4 v;
+    if (whole) {
+      v = *reinterpret_cast<const f32x4u *>(bp + (long long)k * p.ldb);
+    } else {
 #pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        b[i] = *reinterpret_cast<const f32x4u *>(bp + (long long)(k + i * KS) * p.ldb);
-        // Rows past M read row M - 1 (never stored), so no load is conditional.
+      for (int j = 0; j < 4; ++j) v[j] = j < valid ? bp[(long long)k * p.ldb + j] : 0.f;
+    }
+    return v;
+  };
+  int k = k0;
+  // Whole batches: NB quads, every k inside K.
+  for (; k + (NB - 1) * KB + 3 < p.K; k += NB * KB) {
+    f32x4 b[NB][4], a[NB][R];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) b[u][t] = load_b(k + u * KB + t);
+#pragma unroll
+      for (int r = 0; r < R; ++r) a[u][r] = *reinterpret_cast<const f32x4u *>(arow[r] + k + u * KB);
+    }
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int r = 0; r < R; ++r)
-          a[r][i] = p.A[(long long)(r < p.M ? r : p.M - 1) * p.lda + k + i * KS];
-      }
 #pragma unroll
-      for (int i = 0; i < NB; ++i)
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[r][j] += a[r][i] * b[i][j];
-    }
-    for (; k < p.K; k += KS) {
-      const f32x4 b = *reinterpret_cast<const f32x4u *>(bp + (long long)k * p.ldb);
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const float a = p.A[(long long)(r < p.M ? r : p.M - 1) * p.lda + k];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[r][j] += a * b[j];
-      }
-    }
-  } else {  // last workgroup of a ragged strip: per-element guards
-    const int valid = (int)(p.N - n0) - c4;  // columns of this lane inside C
-    for (int k = ks; k < p.K; k += KS) {
-      float b[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = j < valid ? bp[(long long)k * p.ldb + j] : 0.f;
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-        if (r < p.M) {
-          const float a = p.A[(long long)r * p.lda + k];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[r][j] += a * b[j];
-        }
-    }
+          for (int j = 0; j < 4; ++j) acc[r][j] += a[u][r][t] * b[u][t][j];
   }
+  // The rest of this slice (fewer than NB quads, the last possibly partial):
+  // one batch, k past K loading row K - 1 and adding nothing.
+  if (k < p.K) {
+    f32x4 b[NB][4], a[NB][R];
 #pragma unroll
-  for (int r = 0; r < R; ++r)
+    for (int u = 0; u < NB; ++u)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) red[ks][r][c4 + j] = acc[r][j];
+      for (int t = 0; t < 4; ++t) {
+        const int kk = k + u * KB + t;
+        const int kc = kk < p.K ? kk : p.K - 1;
+        b[u][t] = load_b(kc);
+#pragma unroll
+        for (int r = 0; r < R; ++r) a[u][r][t] = arow[r][kc];
+      }
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (k + u * KB + t < p.K) {
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[r][j] += a[u][r][t] * b[u][t][j];
+        }
+  }
+  // Slices of one wave: lanes 4 s + q (s = 0..15) hold column quad q.
+#pragma unroll
+  for (int m = 4; m < 64; m <<= 1)
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[r][j] += __shfl_xor(acc[r][j], m);
+  const int wave = tid >> 6;
+  if ((tid & 63) < 4) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) red[wave][r][c4 + j] = acc[r][j];
+  }
   __syncthreads();
   if (tid < kStripCols * R) {
     const int r = tid / kStripCols, c = tid % kStripCols;
     if (r < p.M && n0 + c < p.N) {
-      float sum = 0.f;
-#pragma unroll 16
-      for (int q = 0; q < KS; ++q) sum += red[q][r][c];
+      float sum = red[0][r][c];
+#pragma unroll
+      for (int w = 1; w < kStripWaves; ++w) sum += red[w][r][c];
       p.C[(long long)r * p.ldc + n0 + c] = sum;
     }
   }
 }
 
 hipError_t launch_strip(const Problem &p, hipStream_t s) {
+  if (p.M < 1 || p.M > kStripMaxRows) return hipErrorInvalidValue;
   const dim3 grid((unsigned)ceil_div(p.N, kStripCols)), block(kStripThreads);
-  if (p.M <= 1) return launch_kernel(strip_kernel<1>, grid, block, s, p);
-  if (p.M <= 2) return launch_kernel(strip_kernel<2>, grid, block, s, p);
-  if (p.M <= 4) return launch_kernel(strip_kernel<4>, grid, block, s, p);
-  if (p.M <= 8) return launch_kernel(strip_kernel<8>, grid, block, s, p);
-  return hipErrorInvalidValue;
+  switch (strip_rows(p.M)) {
+    case 1: return launch_kernel(strip_kernel<1, strip_batch_quads(1)>, grid, block, s, p);
+    case 2: return launch_kernel(strip_kernel<2, strip_batch_quads(2)>, grid, block, s, p);
+    case 4: return launch_kernel(strip_kernel<4, strip_batch_quads(4)>, grid, block, s, p);
+    default: return launch_kernel(strip_kernel<8, strip_batch_quads(8)>, grid, block, s, p);
+  }
 }
+
 // ---- launch table (its entries and the automatic choice: host_plan.cpp) --
 
 using C0 = Tile<128, 128, 32, 2, 2, false>;
@@ -2573,7 +2603,7 @@ hipError_t launch_one(int index, const Problem &p, hipStream_t s) {
                                : launch_big16r<W16<128, 128, 32, 2>>(p, s);
     case 23:  // 128x128 direct-load tiles (built apart); else entry 17's launcher
       return big16_128_fits(p) ? launch_big16_128(p, s) : launch_w16<W16<64, 64, 64, 2>, C0>(p, s);
-
+    case kStripConfig: return launch_strip(p, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -2607,9 +2637,10 @@ hipError_t launch_prod_split(const SplitPlan &plan, const Problem &p, float *ws,
 // One product with launch-table entry `index`.  Thin remainder strips along
 // M or N (and, for the small-K panel entries, any remainder) go to separate
 // launches with small tiles; all launches share the stream, so they run in
-// order.
+// order.  The strip entry is the thin-M kernel on the whole product.
 hipError_t launch_prod(int index, const Problem &p, hipStream_t s) {
   if (!prod_supports(index, p.M, p.N, p.K)) return hipErrorInvalidValue;
+  if (prod_kind(index) == kStrip) return launch_strip(p, s);
   const ProdConfig &c = prod_config(index);
   int rm = index == kRemainderConfig ? 0 : thin_remainder(p.M, c.BM);
   int rn = index == kRemainderConfig ? 0 : thin_remainder(p.N, c.BN);
