@@ -80,7 +80,8 @@ extern "C" {
  * barrier per 32-deep k step; a partial last k step is filled through
  * registers with zeros past K; edge tiles are moved back inside C, and thin
  * remainder strips run on their own kernel, which also computes whole
- * products of at most 8 rows (a stream of B, read once).  Few-tile
+ * products of at most 8 rows (a stream of B, read once); products of at
+ * most 8 columns run on a thin-N kernel (a stream of A).  Few-tile
  * products split each tile's k steps over the 4 waves and add the partial
  * tiles in wave order;
  * K = 64 products keep A in LDS and stream B.  The "one thread, several
@@ -127,7 +128,9 @@ int gemm_f32(int M, int N, int K, const float *A, int lda, const float *B,
  *           entries whose kernel holds all of K in one LDS stage ("panel"
  *           entries, reported with BK = their K limit) accept K <= BK only;
  *           the thin-M strip entry (reported with BN = 16, BK = 1 and BM =
- *           the rows a workgroup holds for this M) accepts M <= 8 only.
+ *           the rows a workgroup holds for this M) accepts M <= 8 only, the
+ *           thin-N entry (BM = 16, BK = 1, BN = the columns it holds for
+ *           this N) N <= 8 only.
  *           Whatever the entry, a thin remainder strip of rows or columns
  *           (an overhanging tile at most 1/8 full) is computed by a second
  *           launch with small tiles on the same stream.

@@ -317,6 +317,48 @@ void replay_strip(const Shape &s) {
   }
 }
 
+// Thin-N kernel (colstrip_kernel): per workgroup of 16 rows and lane, the
+// B values it stages per chunk of 1024 k, its A quads (whole or per element
+// past K), and the C stores.  First and last chunks of each lane.
+void check_b1(const Shape &s, long long k, long long n, const char *what) {
+  ++g_checks;
+  if (k < 0 || n < 0 || k >= s.K || n >= s.N) fail(s, what, k, n);
+}
+
+void replay_colstrip(const Shape &s) {
+  const int NC = strip_cols(s.N), KC = 1024, STEP = 128;
+  const long long wgs = ceil_div(s.M, 16);
+  for (long long w = 0; w < wgs; ++w) {
+    const long long m0 = 16 * w;
+    for (int tid = 0; tid < 512; ++tid) {
+      const int lane = tid & 63, wave = tid >> 6, split = wave >> 1;
+      const int r = 8 * (wave & 1) + (lane >> 3), q = lane & 7;
+      const long long m = m0 + r < s.M ? m0 + r : s.M - 1;  // rows past M read row M - 1
+      for (int kc0 = 0; kc0 < s.K; kc0 += KC) {
+        if (kc0 != 0 && kc0 + 2 * KC < s.K) continue;
+        const int kn = s.K - kc0 < KC ? s.K - kc0 : KC;
+        for (int v = 0; v < KC * NC / 512; ++v) {
+          const int i = tid + 512 * v, k = i / NC, n = i % NC;
+          if (k < kn && n < s.N) check_b1(s, kc0 + k, n, "colstrip B staging");
+        }
+        for (int j = 0; j < KC / STEP; ++j) {
+          const int k = kc0 + STEP * j + 32 * split + 4 * q;
+          if (kn == KC || k + 4 <= s.K) {
+            check_a(s, m * s.lda + k, "colstrip A quad");
+          } else {
+            for (int t = 0; t < 4; ++t)
+              if (k + t < s.K) check_a1(s, m, k + t, "colstrip A tail");
+          }
+        }
+      }
+    }
+    for (int tid = 0; tid < 16 * NC; ++tid) {
+      const int rr = tid / NC, n = tid % NC;
+      if (m0 + rr < s.M && n < s.N) check_c(s, m0 + rr, n, 1, "colstrip C store");
+    }
+  }
+}
+
 // ---- one product as launch_prod runs it --------------------------------------
 // The entry's main part, its thin strips (bottom strips of up to 8 rows on
 // the thin-M kernel are replayed; other strips run entry 3's register path),
@@ -336,6 +378,7 @@ void replay_entry(int entry, const Shape &s) {
     return replay_entry(model_kloop(rest.M, rest.N, rest.K).entry, rest);
   }
   if (prod_kind(entry) == kStrip) return replay_strip(s);
+  if (prod_kind(entry) == kStripN) return replay_colstrip(s);
   const ProdConfig &c = prod_config(entry);
   int rm = entry == kRemainderConfig ? 0 : thin_remainder(s.M, c.BM);
   int rn = entry == kRemainderConfig ? 0 : thin_remainder(s.N, c.BN);
@@ -535,6 +578,11 @@ int main(int argc, char **argv) {
       {4, 16384, 1027, 1027, 16384, 16384, "4-row strip product"},
       {2, 17, 2051, 2053, 19, 17, "2-row strip, partial column group"},
       {5, 300, 3, 3, 300, 300, "5-row strip, K below one quad"},
+      {4097, 1, 4096, 4096, 1, 1, "one-column product"},
+      {4096, 8, 4097, 4099, 9, 11, "8-column product, padded ld"},
+      {300, 3, 1023, 1023, 3, 3, "3-column product, K below one chunk"},
+      {17, 5, 2049, 2051, 5, 7, "5-column product, partial row group"},
+      {9, 2, 1, 1, 2, 2, "2-column product, K = 1"},
   };
   // edge sweep: sizes around multiples of 16 .. 256, and K tails
   const int sizes[] = {1, 2, 3, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257,

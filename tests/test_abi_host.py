@@ -267,8 +267,10 @@ def test_tile_queries():
     n = g.gemm_f32_num_configs("prod")
     assert n >= 3
     strip = g.gemm_f32_tile("prod", -1, 1, 4095, 2049)["config"]
+    colstrip = g.gemm_f32_tile("prod", -1, 4095, 1, 2049)["config"]
+    assert colstrip != strip
     for i in range(n):
-        if i == strip:
+        if i in (strip, colstrip):
             continue
         q = g.gemm_f32_tile("prod", i, 64, 64, 64)
         assert q["config"] == i and q["threads"] % 64 == 0
@@ -283,6 +285,16 @@ def test_tile_queries():
         g.gemm_f32_tile("prod", strip, 9, 64, 64)
     assert e.value.status == 7
     assert _call(9, 64, 64, A=64, B=64, C=64, variant=2, config=strip) == 7
+    # products of at most 8 columns (and more than 8 rows) run the thin-N
+    # kernel whole; its entry reports the columns it holds and refuses a ninth
+    for N, bn in ((1, 1), (2, 2), (3, 4), (4, 4), (5, 8), (8, 8)):
+        q = g.gemm_f32_tile("prod", -1, 77, N, 5)
+        assert (q["config"], q["BM"], q["BN"], q["threads"]) == (colstrip, 16, bn, 512)
+    assert g.gemm_f32_tile("prod", -1, 8, 8, 8)["config"] == strip
+    assert g.gemm_f32_tile("prod", -1, 4095, 9, 2049)["config"] not in (strip, colstrip)
+    with pytest.raises(g.GemmError) as e:
+        g.gemm_f32_tile("prod", colstrip, 64, 9, 64)
+    assert e.value.status == 7
     with pytest.raises(g.GemmError):
         g.gemm_f32_tile("prod", n, 64, 64, 64)
     # automatic choice for the skinny K = 64 shape is a small-K entry; such

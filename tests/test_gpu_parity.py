@@ -144,7 +144,7 @@ def test_kloop_entries_agree_bitwise_on_ragged_floats(g):
     agree bit for bit.  The shapes leave no thin remainder for any tile size
     (a thin strip goes to the strip kernel, which sums K in another order)."""
     kloop = [c for c in _prod_configs(g)
-             if _supported(g, c, 1, 1, 65) and c not in OWN_ORDER_ENTRIES + (STRIP_ENTRY,)]
+             if _supported(g, c, 1, 1, 65) and c not in OWN_ORDER_ENTRIES + STRIP_ENTRIES]
     for (M, N, K) in [(1000, 1003, 515), (3000, 300, 129), (700, 4000, 64)]:
         for cfg in kloop:
             t = g.gemm_f32_tile("prod", cfg, M, N, K)
@@ -165,9 +165,12 @@ W16_ENTRIES = (17, 18, 19, 20, 22, 23, 24)
 # or the whole product on the model's entry: the order of whichever runs
 ROW_REGION_ENTRY = 25
 OWN_ORDER_ENTRIES = (KSPLIT_ENTRY,) + W16_ENTRIES + (ROW_REGION_ENTRY,)
-# the thin-M strip kernel on whole products of at most 8 rows (k-slices
-# summed at the end, its own order; test_strip_entry_whole_product)
+# the thin-M and thin-N kernels on whole products of at most 8 rows or
+# columns (k-slices summed at the end, their own order;
+# test_strip_entry_whole_product, test_colstrip_entry_whole_product)
 STRIP_ENTRY = 26
+COLSTRIP_ENTRY = 27
+STRIP_ENTRIES = (STRIP_ENTRY, COLSTRIP_ENTRY)
 LDS_DMA_ENTRY = 15  # 256x256x32 with direct-to-LDS loads
 REG_STAGED_ENTRY = 12  # the same tiles through registers
 
@@ -388,6 +391,39 @@ def test_strip_entry_whole_product(g):
                                      (1, 17, 5, 5, 21, 17)]:
         print(f"case: strip entry padded {M}x{N}x{K} lds {lda},{ldb},{ldc}", flush=True)
         a, b = make(M, N, K, "small_int", seed=lda + ldb)
+        abuf = torch.full((M, lda), 7.0, device=dev)
+        bbuf = torch.full((K, ldb), 7.0, device=dev)
+        cbuf = torch.full((M, ldc), -1.0, device=dev)
+        abuf[:, :K] = torch.from_numpy(a).to(dev)
+        bbuf[:, :N] = torch.from_numpy(b).to(dev)
+        g.matmul(abuf[:, :K], bbuf[:, :N], out=cbuf[:, :N], variant="prod")
+        torch.cuda.synchronize()
+        c = cbuf.cpu().numpy()
+        assert np.array_equal(c[:, :N], oracle.gemm(a, b)), (M, N, K)
+        assert np.all(c[:, N:] == -1.0)
+
+
+def test_colstrip_entry_whole_product(g):
+    """Products of more than 8 rows and 1-8 columns: the automatic choice
+    runs the thin-N kernel on the whole product.  Row counts below, at and
+    past a workgroup's 16 (partial last group), K from 1 to past one 1024-k
+    chunk of B (the guarded last chunk: partial quads and quads wholly past
+    K), and padded leading dimensions (rows only 4-byte aligned) with the
+    padding left untouched."""
+    dev = _dev()
+    assert g.gemm_f32_tile("prod", -1, 4095, 1, 2049)["config"] == COLSTRIP_ENTRY
+    for N in range(1, 9):
+        for (M, K) in [(9, 1), (16, 3), (17, 129), (300, 1024), (1000, 1025), (4097, 2051)]:
+            assert g.gemm_f32_tile("prod", -1, M, N, K)["config"] == COLSTRIP_ENTRY
+            print(f"case: colstrip entry {M}x{N}x{K}", flush=True)
+            a, b = make(M, N, K, "small_int", seed=N * 1019 + M + K)
+            assert np.array_equal(_run(g, a, b, "prod"), oracle.gemm(a, b)), (M, N, K)
+            a, b = make(M, N, K, "normal", seed=N * 1021 + M * K)
+            _tol_check(_run(g, a, b, "prod"), oracle.gemm(a, b), K, f"colstrip entry {M}x{N}x{K}")
+    for (M, N, K, lda, ldb, ldc) in [(300, 3, 129, 133, 5, 7), (4097, 8, 2049, 2050, 9, 11),
+                                     (17, 1, 5, 9, 1, 2)]:
+        print(f"case: colstrip entry padded {M}x{N}x{K} lds {lda},{ldb},{ldc}", flush=True)
+        a, b = make(M, N, K, "small_int", seed=lda + ldb + ldc)
         abuf = torch.full((M, lda), 7.0, device=dev)
         bbuf = torch.full((K, ldb), 7.0, device=dev)
         cbuf = torch.full((M, ldc), -1.0, device=dev)

@@ -119,7 +119,8 @@ extern "C" int gemm_f32_tile(int variant, int config, int M, int N, int K,
   } else if (variant == GEMM_F32_PROD) {
     const ProdConfig &c = prod_config(chosen);
     bm = prod_kind(chosen) == kStrip ? strip_rows(M) : c.BM;
-    bn = c.BN, bk = c.BK, nt = 64 * c.WGM * c.WGN;
+    bn = prod_kind(chosen) == kStripN ? strip_cols(N) : c.BN;
+    bk = c.BK, nt = 64 * c.WGM * c.WGN;
   } else if (variant == GEMM_F32_VALU) {
     bm = bn = kValuTile, bk = kValuBK, nt = kValuThreads;
   } else {

@@ -54,9 +54,10 @@ struct Entry {
 
 // Index = launch-table entry of GEMM_F32_PROD.  The kernels behind each
 // entry are in prod.hip and w16_vgpr.hip; the automatic choice uses 16, 19,
-// 21, 22, 23, 24, 25 and 26 (and 3 for thin strips), the others stay
-// reachable by index for tests and measurements.  Entry 26 reports the most
-// rows its workgroup holds (BM 8); gemm_f32_tile reports strip_rows(M).
+// 21, 22, 23, 24, 25, 26 and 27 (and 3 for thin strips), the others stay
+// reachable by index for tests and measurements.  Entries 26 and 27 list
+// the most rows (columns) a workgroup holds; gemm_f32_tile reports
+// strip_rows(M) (strip_cols(N)).
 const Entry kEntries[] = {
     {{128, 128, 32, 2, 2, 2, "128x128x32_w2x2"}, kKloop},
     {{128, 128, 16, 2, 2, 3, "128x128x16_w2x2"}, kKloop},
@@ -85,6 +86,7 @@ const Entry kEntries[] = {
     {{192, 256, 32, 2, 2, 1, "192x256x32_w2x2_ldsdma_mfma16"}, kKsplit},
     {{256, 256, 32, 2, 2, 1, "rows256_rounds+rest"}, kKsplit},
     {{8, 16, 1, 4, 2, 1, "strip_rows8_cols16"}, kStrip},
+    {{16, 8, 1, 4, 2, 1, "strip_cols8_rows16"}, kStripN},
 };
 constexpr int kNumConfigs = sizeof(kEntries) / sizeof(kEntries[0]);
 
@@ -134,9 +136,9 @@ const ProdConfig &prod_config(int index) { return kEntries[index].cfg; }
 ProdKind prod_kind(int index) { return kEntries[index].kind; }
 
 bool prod_supports(int index, int M, int N, int K) {
-  (void)N;
   if (index < 0 || index >= kNumConfigs) return false;
   if (kEntries[index].kind == kStrip) return M <= kStripMaxRows;
+  if (kEntries[index].kind == kStripN) return N <= kStripMaxCols;
   return kEntries[index].kind != kPanel || K <= kEntries[index].cfg.BK;
 }
 
@@ -209,7 +211,8 @@ int region_rows(int M, int N, int K) {
 // Shape-based choice.  At most kStripMaxRows rows: the thin-M strip kernel
 // (entry 26), which streams B once, where a tile kernel would fill its 64-
 // to 256-row tiles with one to eight useful rows (1 x 4095 x 2049: 91 us on
-// the 64 x 64 K-split entry, 13 us as a strip).  K <= 64 with many tiles:
+// the 64 x 64 K-split entry, 13 us as a strip).  At most kStripMaxCols
+// columns: the thin-N kernel (entry 27), which streams A once.  K <= 64 with many tiles:
 // the A-resident small-K kernel (only B moves per tile; C stores of one
 // tile drained during the next tile's MFMAs), on 16x16 MFMAs with one wave
 // per SIMD when K == 64 and the rows are aligned (entry 21's launcher falls
@@ -219,6 +222,7 @@ int region_rows(int M, int N, int K) {
 int prod_choose(int M, int N, int K, double *full_rate) {
   if (full_rate) *full_rate = 0.0;
   if (M <= kStripMaxRows) return kStripConfig;
+  if (N <= kStripMaxCols) return kColStripConfig;
   const long long t256x128 = ceil_div(M, 256) * ceil_div(N, 128);
   if (K <= 64 && t256x128 >= 1024) return 21;
   if (region_rows(M, N, K) > 0) return 25;

@@ -66,8 +66,9 @@ struct ProdConfig {
 // kKloop: any K, k loop over steps of BK.  kPanel: all of K in one LDS
 // stage, K <= BK, whole tiles only (remainders become strips).  kKsplit: the
 // 16x16-MFMA families, any K.  kStrip: the thin-M strip kernel on the whole
-// product, M <= kStripMaxRows.
-enum ProdKind { kKloop, kPanel, kKsplit, kStrip };
+// product, M <= kStripMaxRows.  kStripN: the thin-N kernel on the whole
+// product, N <= kStripMaxCols.
+enum ProdKind { kKloop, kPanel, kKsplit, kStrip, kStripN };
 
 int prod_num_configs();
 const ProdConfig &prod_config(int index);
@@ -88,6 +89,11 @@ constexpr int strip_rows(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 
 // (1 x 4095 x 2049: 10.7, 11.4, 13.0 us for 1, 2, 4 quads; 8 x 8191 x 4096:
 // 36.0 us for 1, 38.8 for 2; 4 x 16384 x 4096: 49.6 for 1, 44.9 for 2).
 constexpr int strip_batch_quads(int rows) { return rows == 2 || rows == 4 ? 2 : 1; }
+// The launch-table entry that runs the thin-N kernel on a whole product of
+// at most kStripMaxCols columns, and the columns it is instantiated for.
+constexpr int kStripMaxCols = 8;
+constexpr int kColStripConfig = 27;
+constexpr int strip_cols(int N) { return N <= 1 ? 1 : N <= 2 ? 2 : N <= 4 ? 4 : 8; }
 
 // Rows (or columns) of a thin remainder strip worth a separate launch: an
 // overhanging tile row that is at most 1/8 full.

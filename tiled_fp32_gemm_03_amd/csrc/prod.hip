@@ -2344,6 +2344,131 @@ hipError_t launch_strip(const Problem &p, hipStream_t s) {
   }
 }
 
+// Thin-N kernel for a whole product of at most 8 columns: a stream of A,
+// read once (a 64- to 256-column MFMA tile holding one to eight valid
+// columns would cost a whole tile's work per row block).  A workgroup of
+// 512 threads owns 16 rows of C: 8 lanes per row read 128 consecutive bytes
+// of it per load (one 16-byte quad of k each), the two row halves take one
+// wave each, and 4 wave pairs split k (pair s takes k = 128 j + 32 s + 4 q
+// for lane q of a row), so at each step a workgroup reads 512 bytes of each
+// of its rows.  B goes through LDS a chunk of KC k at a time, quad of k by
+// quad of k: the 4 x NC values of a quad as NC runs of 4 k (column n's run
+// at 4 n), a quad's block padded to 4 NC + 4 floats for NC >= 2 so that the
+// 8 quads a wave reads at once fall on distinct banks; a lane reads one
+// 16-byte run per column per quad.  A lane issues its chunk's B staging
+// loads, then all its A loads, and waits for the B values alone before
+// writing them to LDS.  Elements past K or N are zeros on both sides, and
+// quads wholly past K are skipped.  Each lane sums its k in ascending order;
+// the 8 lanes of a row are added by a fixed butterfly of lane exchanges and
+// the 4 k-splits in split order through LDS, so the result is
+// deterministic.  Rows of A and B need only 4-byte alignment.
+constexpr int kColThreads = 512;
+constexpr int kColRows = 16;
+constexpr int kColSplits = 4;
+constexpr int kColStep = 4 * 8 * kColSplits;  // k per step of a row: 8 lanes x 4 k x 4 splits
+constexpr int kColChunk = 1024;               // k per B chunk in LDS
+
+template <int NC>
+constexpr int col_quad_floats() {
+  return NC == 1 ? 4 : 4 * NC + 4;
+}
+
+template <int NC>
+__global__ void __launch_bounds__(kColThreads) colstrip_kernel(Problem p) {
+  constexpr int QF = col_quad_floats<NC>();
+  constexpr int KC = kColChunk, NJ = KC / kColStep;
+  constexpr int BV = KC * NC / kColThreads;  // B values a thread stages per chunk
+  static_assert(KC % kColStep == 0 && (KC * NC) % kColThreads == 0, "chunk shape");
+  __shared__ __attribute__((aligned(16))) float bq[KC / 4 * QF];
+  __shared__ float red[kColSplits][kColRows][NC];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int split = wave >> 1;
+  const int r = 8 * (wave & 1) + (lane >> 3);  // row within the workgroup
+  const int q = lane & 7;
+  const long long m0 = (long long)blockIdx.x * kColRows;
+  // Rows past M read row M - 1 (never stored), so no A load is conditional.
+  const float *arow = p.A + (m0 + r < p.M ? m0 + r : p.M - 1) * p.lda;
+  float acc[NC];
+#pragma unroll
+  for (int n = 0; n < NC; ++n) acc[n] = 0.f;
+  for (int kc0 = 0; kc0 < p.K; kc0 += KC) {
+    const int kn = p.K - kc0 < KC ? p.K - kc0 : KC;  // k of this chunk inside K
+    float bv[BV];
+#pragma unroll
+    for (int v = 0; v < BV; ++v) {
+      const int i = tid + kColThreads * v, k = i / NC, n = i % NC;
+      bv[v] = k < kn && n < p.N ? p.B[(long long)(kc0 + k) * p.ldb + n] : 0.f;
+    }
+    f32x4 a[NJ];
+    if (kn == KC) {  // every quad of the chunk inside K
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        a[j] = *reinterpret_cast<const f32x4u *>(arow + kc0 + kColStep * j + 32 * split + 4 * q);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int k = kc0 + kColStep * j + 32 * split + 4 * q;
+        if (k + 4 <= p.K) {
+          a[j] = *reinterpret_cast<const f32x4u *>(arow + k);
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) a[j][t] = k + t < p.K ? arow[k + t] : 0.f;
+        }
+      }
+    }
+    __syncthreads();  // every lane is done with the previous chunk's B
+#pragma unroll
+    for (int v = 0; v < BV; ++v) {
+      const int i = tid + kColThreads * v, k = i / NC, n = i % NC;
+      bq[(k >> 2) * QF + 4 * n + (k & 3)] = bv[v];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int kl = kColStep * j + 32 * split + 4 * q;
+      if (kl < kn) {
+#pragma unroll
+        for (int n = 0; n < NC; ++n) {
+          const f32x4 b = *reinterpret_cast<const f32x4 *>(bq + (kl >> 2) * QF + 4 * n);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[n] += a[j][t] * b[t];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < 8; m <<= 1)
+#pragma unroll
+    for (int n = 0; n < NC; ++n) acc[n] += __shfl_xor(acc[n], m);
+  if (q == 0) {
+#pragma unroll
+    for (int n = 0; n < NC; ++n) red[split][r][n] = acc[n];
+  }
+  __syncthreads();
+  if (tid < kColRows * NC) {
+    const int rr = tid / NC, n = tid % NC;
+    if (m0 + rr < p.M && n < p.N) {
+      float sum = red[0][rr][n];
+#pragma unroll
+      for (int sp = 1; sp < kColSplits; ++sp) sum += red[sp][rr][n];
+      p.C[(m0 + rr) * p.ldc + n] = sum;
+    }
+  }
+}
+
+hipError_t launch_colstrip(const Problem &p, hipStream_t s) {
+  if (p.N < 1 || p.N > kStripMaxCols || p.M < 1) return hipErrorInvalidValue;
+  const long long wgs = ceil_div(p.M, kColRows);
+  if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)wgs), block(kColThreads);
+  switch (strip_cols(p.N)) {
+    case 1: return launch_kernel(colstrip_kernel<1>, grid, block, s, p);
+    case 2: return launch_kernel(colstrip_kernel<2>, grid, block, s, p);
+    case 4: return launch_kernel(colstrip_kernel<4>, grid, block, s, p);
+    default: return launch_kernel(colstrip_kernel<8>, grid, block, s, p);
+  }
+}
+
 // ---- launch table (its entries and the automatic choice: host_plan.cpp) --
 
 using C0 = Tile<128, 128, 32, 2, 2, false>;
@@ -2604,6 +2729,7 @@ hipError_t launch_one(int index, const Problem &p, hipStream_t s) {
     case 23:  // 128x128 direct-load tiles (built apart); else entry 17's launcher
       return big16_128_fits(p) ? launch_big16_128(p, s) : launch_w16<W16<64, 64, 64, 2>, C0>(p, s);
     case kStripConfig: return launch_strip(p, s);
+    case kColStripConfig: return launch_colstrip(p, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -2637,10 +2763,12 @@ hipError_t launch_prod_split(const SplitPlan &plan, const Problem &p, float *ws,
 // One product with launch-table entry `index`.  Thin remainder strips along
 // M or N (and, for the small-K panel entries, any remainder) go to separate
 // launches with small tiles; all launches share the stream, so they run in
-// order.  The strip entry is the thin-M kernel on the whole product.
+// order.  The strip entries are the thin-M and thin-N kernels on the whole
+// product.
 hipError_t launch_prod(int index, const Problem &p, hipStream_t s) {
   if (!prod_supports(index, p.M, p.N, p.K)) return hipErrorInvalidValue;
   if (prod_kind(index) == kStrip) return launch_strip(p, s);
+  if (prod_kind(index) == kStripN) return launch_colstrip(p, s);
   const ProdConfig &c = prod_config(index);
   int rm = index == kRemainderConfig ? 0 : thin_remainder(p.M, c.BM);
   int rn = index == kRemainderConfig ? 0 : thin_remainder(p.N, c.BN);
