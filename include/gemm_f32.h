@@ -80,13 +80,13 @@ extern "C" {
  * barrier per 32-deep k step; a partial last k step is filled through
  * registers with zeros past K; edge tiles are moved back inside C, and thin
  * remainder strips run on their own kernel, which also computes whole
- * products of at most 8 rows (a stream of B, read once); products of at
- * most 8 columns run on a thin-N kernel (a stream of A).  Few-tile
- * products split each tile's k steps over the 4 waves and add the partial
- * tiles in wave order;
- * K = 64 products keep A in LDS and stream B.  The "one thread, several
- * outputs" and "register / wave / instruction block" pyramid the pages
- * point to (geek-doc.cn sections 三 and 五) on CDNA4 matrix cores. */
+ * products of at most 32 rows (a stream of B, read once per 16 rows);
+ * products of at most 16 columns run on a thin-N kernel (a stream of A).
+ * Few-tile products split each tile's k steps over the 4 waves and add the
+ * partial tiles in wave order; K = 64 products keep A in LDS and stream B.
+ * The "one thread, several outputs" and "register / wave / instruction
+ * block" pyramid the pages point to (geek-doc.cn sections 三 and 五) on
+ * CDNA4 matrix cores. */
 #define GEMM_F32_PROD 2
 /* The textbook kernel with T = 32 (1024 threads per workgroup). */
 #define GEMM_F32_TILED32 3
@@ -128,12 +128,13 @@ int gemm_f32(int M, int N, int K, const float *A, int lda, const float *B,
  *           entries whose kernel holds all of K in one LDS stage ("panel"
  *           entries, reported with BK = their K limit) accept K <= BK only;
  *           the thin-M strip entry (reported with BN = 16, BK = 1 and BM =
- *           the rows a workgroup holds for this M) accepts M <= 8 only, the
+ *           the rows a workgroup holds for this M) accepts M <= 32 only, the
  *           thin-N entry (BM = 16, BK = 1, BN = the columns it holds for
- *           this N) N <= 8 only.
+ *           this N) N <= 16 only.
  *           Whatever the entry, a thin remainder strip of rows or columns
- *           (an overhanging tile at most 1/8 full) is computed by a second
- *           launch with small tiles on the same stream.
+ *           (an overhanging tile at most 1/8 full) is computed by further
+ *           launches on the same stream: rows on the thin-M strip kernel,
+ *           columns with small tiles.
  * Same semantics and errors as gemm_f32, plus GEMM_F32_BAD_CONFIG.
  */
 int gemm_f32_ex(int M, int N, int K, const float *A, int lda, const float *B,

@@ -272,7 +272,19 @@ void replay_arow16(const Shape &s, int slots) {
 
 // ---- thin-M strip kernel ------------------------------------------------------
 // 512 threads: 4 column quads x 128 k slices, 16 columns per workgroup.
-void replay_strip(const Shape &s) {
+void replay_strip_pass(const Shape &s);
+
+void replay_strip(const Shape &s) {  // passes of kStripPassRows rows
+  for (int r0 = 0; r0 < s.M; r0 += kStripPassRows) {
+    Shape pass = s;
+    pass.M = s.M - r0 < kStripPassRows ? s.M - r0 : kStripPassRows;
+    // Offsets of the pass are relative to its first row, whose rows of A and C
+    // exist: the pass's checks run against its own M rows.
+    replay_strip_pass(pass);
+  }
+}
+
+void replay_strip_pass(const Shape &s) {
   const int wgs = (int)ceil_div(s.N, 16);
   const int R = strip_rows(s.M), NB = strip_batch_quads(R), KB = 512;
   auto row_of = [&](int r) { return r < s.M ? r : s.M - 1; };  // rows past M read row M - 1
@@ -326,7 +338,7 @@ void check_b1(const Shape &s, long long k, long long n, const char *what) {
 }
 
 void replay_colstrip(const Shape &s) {
-  const int NC = strip_cols(s.N), KC = 1024, STEP = 128;
+  const int NC = strip_cols(s.N), KC = col_chunk(NC), STEP = 128;
   const long long wgs = ceil_div(s.M, 16);
   for (long long w = 0; w < wgs; ++w) {
     const long long m0 = 16 * w;

@@ -275,25 +275,27 @@ def test_tile_queries():
         q = g.gemm_f32_tile("prod", i, 64, 64, 64)
         assert q["config"] == i and q["threads"] % 64 == 0
         assert q["BM"] % 32 == 0 and q["BN"] % 32 == 0 and q["BK"] % 8 == 0
-    # products of at most 8 rows run the thin-M strip kernel whole; its entry
-    # reports the rows a workgroup holds and refuses a ninth row
-    for M, bm in ((1, 1), (2, 2), (3, 4), (4, 4), (5, 8), (8, 8)):
+    # products of at most 32 rows run the thin-M strip kernel whole, 16 rows
+    # per launch; its entry reports the rows a workgroup holds and refuses a
+    # 33rd row
+    for M, bm in ((1, 1), (2, 2), (3, 4), (4, 4), (5, 8), (8, 8), (9, 16), (16, 16), (17, 16),
+                  (32, 16)):
         q = g.gemm_f32_tile("prod", -1, M, 77, 5)
         assert (q["config"], q["BM"], q["BN"], q["threads"]) == (strip, bm, 16, 512)
-    assert g.gemm_f32_tile("prod", -1, 9, 4095, 2049)["config"] != strip
+    assert g.gemm_f32_tile("prod", -1, 33, 4095, 2049)["config"] != strip
     with pytest.raises(g.GemmError) as e:
-        g.gemm_f32_tile("prod", strip, 9, 64, 64)
+        g.gemm_f32_tile("prod", strip, 33, 64, 64)
     assert e.value.status == 7
-    assert _call(9, 64, 64, A=64, B=64, C=64, variant=2, config=strip) == 7
-    # products of at most 8 columns (and more than 8 rows) run the thin-N
-    # kernel whole; its entry reports the columns it holds and refuses a ninth
-    for N, bn in ((1, 1), (2, 2), (3, 4), (4, 4), (5, 8), (8, 8)):
+    assert _call(33, 64, 64, A=64, B=64, C=64, variant=2, config=strip) == 7
+    # products of at most 16 columns (and more than 32 rows) run the thin-N
+    # kernel whole; its entry reports the columns it holds and refuses a 17th
+    for N, bn in ((1, 1), (2, 2), (3, 4), (4, 4), (5, 8), (8, 8), (9, 16), (16, 16)):
         q = g.gemm_f32_tile("prod", -1, 77, N, 5)
         assert (q["config"], q["BM"], q["BN"], q["threads"]) == (colstrip, 16, bn, 512)
-    assert g.gemm_f32_tile("prod", -1, 8, 8, 8)["config"] == strip
-    assert g.gemm_f32_tile("prod", -1, 4095, 9, 2049)["config"] not in (strip, colstrip)
+    assert g.gemm_f32_tile("prod", -1, 32, 16, 16)["config"] == strip
+    assert g.gemm_f32_tile("prod", -1, 4095, 17, 2049)["config"] not in (strip, colstrip)
     with pytest.raises(g.GemmError) as e:
-        g.gemm_f32_tile("prod", colstrip, 64, 9, 64)
+        g.gemm_f32_tile("prod", colstrip, 64, 17, 64)
     assert e.value.status == 7
     with pytest.raises(g.GemmError):
         g.gemm_f32_tile("prod", n, 64, 64, 64)

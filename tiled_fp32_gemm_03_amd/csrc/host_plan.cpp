@@ -85,8 +85,8 @@ const Entry kEntries[] = {
     {{128, 128, 32, 2, 2, 2, "128x128x32_w2x2_ldsdma_mfma16"}, kKsplit},
     {{192, 256, 32, 2, 2, 1, "192x256x32_w2x2_ldsdma_mfma16"}, kKsplit},
     {{256, 256, 32, 2, 2, 1, "rows256_rounds+rest"}, kKsplit},
-    {{8, 16, 1, 4, 2, 1, "strip_rows8_cols16"}, kStrip},
-    {{16, 8, 1, 4, 2, 1, "strip_cols8_rows16"}, kStripN},
+    {{16, 16, 1, 4, 2, 1, "strip_rows16_cols16"}, kStrip},
+    {{16, 16, 1, 4, 2, 1, "strip_cols16_rows16"}, kStripN},
 };
 constexpr int kNumConfigs = sizeof(kEntries) / sizeof(kEntries[0]);
 
@@ -209,11 +209,12 @@ int region_rows(int M, int N, int K) {
 }
 
 // Shape-based choice.  At most kStripMaxRows rows: the thin-M strip kernel
-// (entry 26), which streams B once, where a tile kernel would fill its 64-
-// to 256-row tiles with one to eight useful rows (1 x 4095 x 2049: 91 us on
-// the 64 x 64 K-split entry, 13 us as a strip).  At most kStripMaxCols
-// columns: the thin-N kernel (entry 27), which streams A once.  K <= 64 with many tiles:
-// the A-resident small-K kernel (only B moves per tile; C stores of one
+// (entry 26), which streams B once per 16 rows, where a tile kernel would
+// fill its 64- to 256-row tiles with 1 to 32 useful rows (1 x 4095 x 2049:
+// 91 us on the 64 x 64 K-split entry, 13 us as a strip; 32 x 4095 x 2049:
+// 101 against 42 us).  At most kStripMaxCols columns: the thin-N kernel
+// (entry 27), which streams A once.  K <= 64 with many tiles: the
+// A-resident small-K kernel (only B moves per tile; C stores of one
 // tile drained during the next tile's MFMAs), on 16x16 MFMAs with one wave
 // per SIMD when K == 64 and the rows are aligned (entry 21's launcher falls
 // back to the 32x32 form otherwise).  Otherwise entry 25 when its row cut

@@ -78,22 +78,27 @@ bool prod_supports(int index, int M, int N, int K);
 // The entry that computes thin remainder strips, and the most rows a bottom
 // strip may have to go to the thin-M strip kernel.
 constexpr int kRemainderConfig = 3;
-constexpr int kStripMaxRows = 8;
+constexpr int kStripMaxRows = 32;
 // The launch-table entry that runs the thin-M strip kernel on a whole
-// product of at most kStripMaxRows rows, and the rows one of its workgroups
-// holds for an M-row product (the kernel is instantiated for 1, 2, 4 and 8).
+// product of at most kStripMaxRows rows, the rows one launch of it covers
+// (more rows take one launch per kStripPassRows, each reading all of B), and
+// the rows one of its workgroups holds for an M-row product (the kernel is
+// instantiated for 1, 2, 4, 8 and 16).
 constexpr int kStripConfig = 26;
-constexpr int strip_rows(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
+constexpr int kStripPassRows = 16;
+constexpr int strip_rows(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
 // Quads of k whose loads a strip lane issues before using any (its batch),
 // per row count: measured kernel durations on N = 1024-32768, K = 2049-8192
 // (1 x 4095 x 2049: 10.7, 11.4, 13.0 us for 1, 2, 4 quads; 8 x 8191 x 4096:
 // 36.0 us for 1, 38.8 for 2; 4 x 16384 x 4096: 49.6 for 1, 44.9 for 2).
 constexpr int strip_batch_quads(int rows) { return rows == 2 || rows == 4 ? 2 : 1; }
 // The launch-table entry that runs the thin-N kernel on a whole product of
-// at most kStripMaxCols columns, and the columns it is instantiated for.
-constexpr int kStripMaxCols = 8;
+// at most kStripMaxCols columns, the columns it is instantiated for, and
+// the k of B it stages in LDS at a time for that many columns.
+constexpr int kStripMaxCols = 16;
 constexpr int kColStripConfig = 27;
-constexpr int strip_cols(int N) { return N <= 1 ? 1 : N <= 2 ? 2 : N <= 4 ? 4 : 8; }
+constexpr int strip_cols(int N) { return N <= 1 ? 1 : N <= 2 ? 2 : N <= 4 ? 4 : N <= 8 ? 8 : 16; }
+constexpr int col_chunk(int cols) { return cols <= 8 ? 1024 : 512; }
 
 // Rows (or columns) of a thin remainder strip worth a separate launch: an
 // overhanging tile row that is at most 1/8 full.

@@ -2210,9 +2210,9 @@ __global__ void __launch_bounds__(256) arow16_kernel(Problem p, int panels, int 
   }
 }
 
-// Thin-M kernel for a strip of at most 8 rows: a bottom remainder strip, or
+// Thin-M kernel for a strip of at most 16 rows: a bottom remainder strip, or
 // a whole product of that few rows (a 64- to 256-row MFMA tile holding one
-// to eight valid rows would cost a whole tile's work per column block).  Its
+// to sixteen valid rows would cost a whole tile's work per column block).  Its
 // time is the stream of B, read once: each workgroup owns 16 columns, and
 // its 512 threads are 4 column quads x 128 k-slices; slice s takes the
 // quads of consecutive k starting at 4 s, 4 s + 512, ..., so a lane loads
@@ -2333,25 +2333,40 @@ __global__ void __launch_bounds__(kStripThreads) strip_kernel(Problem p) {
   }
 }
 
-hipError_t launch_strip(const Problem &p, hipStream_t s) {
-  if (p.M < 1 || p.M > kStripMaxRows) return hipErrorInvalidValue;
+hipError_t launch_strip_pass(const Problem &p, hipStream_t s) {
   const dim3 grid((unsigned)ceil_div(p.N, kStripCols)), block(kStripThreads);
   switch (strip_rows(p.M)) {
     case 1: return launch_kernel(strip_kernel<1, strip_batch_quads(1)>, grid, block, s, p);
     case 2: return launch_kernel(strip_kernel<2, strip_batch_quads(2)>, grid, block, s, p);
     case 4: return launch_kernel(strip_kernel<4, strip_batch_quads(4)>, grid, block, s, p);
-    default: return launch_kernel(strip_kernel<8, strip_batch_quads(8)>, grid, block, s, p);
+    case 8: return launch_kernel(strip_kernel<8, strip_batch_quads(8)>, grid, block, s, p);
+    default: return launch_kernel(strip_kernel<16, strip_batch_quads(16)>, grid, block, s, p);
   }
 }
 
-// Thin-N kernel for a whole product of at most 8 columns: a stream of A,
+// Up to kStripPassRows rows per launch, in order on the stream.
+hipError_t launch_strip(const Problem &p, hipStream_t s) {
+  if (p.M < 1 || p.M > kStripMaxRows) return hipErrorInvalidValue;
+  for (int r0 = 0; r0 < p.M; r0 += kStripPassRows) {
+    Problem pass = p;
+    pass.M = p.M - r0 < kStripPassRows ? p.M - r0 : kStripPassRows;
+    pass.A = p.A + (long long)r0 * p.lda;
+    pass.C = p.C + (long long)r0 * p.ldc;
+    const hipError_t e = launch_strip_pass(pass, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// Thin-N kernel for a whole product of at most 16 columns: a stream of A,
 // read once (a 64- to 256-column MFMA tile holding one to eight valid
 // columns would cost a whole tile's work per row block).  A workgroup of
 // 512 threads owns 16 rows of C: 8 lanes per row read 128 consecutive bytes
 // of it per load (one 16-byte quad of k each), the two row halves take one
 // wave each, and 4 wave pairs split k (pair s takes k = 128 j + 32 s + 4 q
 // for lane q of a row), so at each step a workgroup reads 512 bytes of each
-// of its rows.  B goes through LDS a chunk of KC k at a time, quad of k by
+// of its rows.  B goes through LDS a chunk of KC k at a time (1024, or 512
+// for 16 columns), quad of k by
 // quad of k: the 4 x NC values of a quad as NC runs of 4 k (column n's run
 // at 4 n), a quad's block padded to 4 NC + 4 floats for NC >= 2 so that the
 // 8 quads a wave reads at once fall on distinct banks; a lane reads one
@@ -2366,7 +2381,6 @@ constexpr int kColThreads = 512;
 constexpr int kColRows = 16;
 constexpr int kColSplits = 4;
 constexpr int kColStep = 4 * 8 * kColSplits;  // k per step of a row: 8 lanes x 4 k x 4 splits
-constexpr int kColChunk = 1024;               // k per B chunk in LDS
 
 template <int NC>
 constexpr int col_quad_floats() {
@@ -2376,7 +2390,7 @@ constexpr int col_quad_floats() {
 template <int NC>
 __global__ void __launch_bounds__(kColThreads) colstrip_kernel(Problem p) {
   constexpr int QF = col_quad_floats<NC>();
-  constexpr int KC = kColChunk, NJ = KC / kColStep;
+  constexpr int KC = col_chunk(NC), NJ = KC / kColStep;
   constexpr int BV = KC * NC / kColThreads;  // B values a thread stages per chunk
   static_assert(KC % kColStep == 0 && (KC * NC) % kColThreads == 0, "chunk shape");
   __shared__ __attribute__((aligned(16))) float bq[KC / 4 * QF];
@@ -2465,7 +2479,8 @@ hipError_t launch_colstrip(const Problem &p, hipStream_t s) {
     case 1: return launch_kernel(colstrip_kernel<1>, grid, block, s, p);
     case 2: return launch_kernel(colstrip_kernel<2>, grid, block, s, p);
     case 4: return launch_kernel(colstrip_kernel<4>, grid, block, s, p);
-    default: return launch_kernel(colstrip_kernel<8>, grid, block, s, p);
+    case 8: return launch_kernel(colstrip_kernel<8>, grid, block, s, p);
+    default: return launch_kernel(colstrip_kernel<16>, grid, block, s, p);
   }
 }
 
