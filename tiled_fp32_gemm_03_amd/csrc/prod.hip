@@ -1985,7 +1985,6 @@ struct Arow16 {
   static constexpr int A_FLOATS = BM * BK, B_FLOATS = BK * BN;
   static constexpr int A_DMA = A_FLOATS / 1024;  // per wave: (A_FLOATS * 4 / 1024) / 4
   static constexpr int B_DMA = B_FLOATS / 1024;
-  static constexpr int ARPI = 64 / ACH, BRPI = 64 / BCH;
   static constexpr int STORES = TBM * TBN;  // 16-byte stores per lane and tile
   static_assert((A_FLOATS + 2 * B_FLOATS) * 4 <= kLdsBytes, "A and two B buffers fit");
   static_assert(STORES + B_DMA < 64, "vmcnt holds at most 63");
@@ -2366,17 +2365,25 @@ hipError_t launch_strip(const Problem &p, hipStream_t s) {
 // wave each, and 4 wave pairs split k (pair s takes k = 128 j + 32 s + 4 q
 // for lane q of a row), so at each step a workgroup reads 512 bytes of each
 // of its rows.  B goes through LDS a chunk of KC k at a time (1024, or 512
-// for 16 columns), quad of k by
-// quad of k: the 4 x NC values of a quad as NC runs of 4 k (column n's run
-// at 4 n), a quad's block padded to 4 NC + 4 floats for NC >= 2 so that the
-// 8 quads a wave reads at once fall on distinct banks; a lane reads one
-// 16-byte run per column per quad.  A lane issues its chunk's B staging
-// loads, then all its A loads, and waits for the B values alone before
-// writing them to LDS.  Elements past K or N are zeros on both sides, and
-// quads wholly past K are skipped.  Each lane sums its k in ascending order;
-// the 8 lanes of a row are added by a fixed butterfly of lane exchanges and
-// the 4 k-splits in split order through LDS, so the result is
-// deterministic.  Rows of A and B need only 4-byte alignment.
+// for 16 columns), quad of k by quad of k: the 4 x NC values of a quad as
+// NC runs of 4 k (column n's run at 4 n), a quad's block padded to 4 NC + 4
+// floats for NC >= 2 so that the 8 quads a wave reads at once fall on
+// distinct banks; a lane reads one 16-byte run per column per quad.  A lane
+// loads a chunk's B values and A quads together, B first, and waits for the
+// B values alone before writing them to LDS.  With PREFETCH it issues the
+// next chunk's loads before it computes on the current one, holding them
+// in registers until the next barrier: against loading each chunk when it
+// starts, 4096 x 16 x 4096 35.4 -> 28.9 us, 16384 x 16 x 4096 120.7 ->
+// 107.0, 4096 x 1 x 4096 17.5 -> 16.2 (the same prefetch made the thin-M
+// strip slower, 10.5 -> 12.7 us on 1 x 4095 x 2049).  The extra registers
+// can halve the workgroups resident per CU (2 columns: 90 -> 142 VGPRs;
+// 100000 x 2 x 512 40.5 -> 69.1 us), so the launcher takes the prefetching
+// form only where that costs no residency the grid would use.  Elements
+// past K or N are zeros on both
+// sides, and quads wholly past K are skipped.  Each lane sums its k in
+// ascending order; the 8 lanes of a row are added by a fixed butterfly of
+// lane exchanges and the 4 k-splits in split order through LDS, so the
+// result is deterministic.  Rows of A and B need only 4-byte alignment.
 constexpr int kColThreads = 512;
 constexpr int kColRows = 16;
 constexpr int kColSplits = 4;
@@ -2387,7 +2394,7 @@ constexpr int col_quad_floats() {
   return NC == 1 ? 4 : 4 * NC + 4;
 }
 
-template <int NC>
+template <int NC, bool PREFETCH>
 __global__ void __launch_bounds__(kColThreads) colstrip_kernel(Problem p) {
   constexpr int QF = col_quad_floats<NC>();
   constexpr int KC = col_chunk(NC), NJ = KC / kColStep;
@@ -2405,16 +2412,14 @@ __global__ void __launch_bounds__(kColThreads) colstrip_kernel(Problem p) {
   float acc[NC];
 #pragma unroll
   for (int n = 0; n < NC; ++n) acc[n] = 0.f;
-  for (int kc0 = 0; kc0 < p.K; kc0 += KC) {
-    const int kn = p.K - kc0 < KC ? p.K - kc0 : KC;  // k of this chunk inside K
-    float bv[BV];
+  auto load_chunk = [&](float(&bv)[BV], f32x4(&a)[NJ], int kc0) __attribute__((always_inline)) {
+    const int kn = p.K - kc0 < KC ? p.K - kc0 : KC;
 #pragma unroll
     for (int v = 0; v < BV; ++v) {
       const int i = tid + kColThreads * v, k = i / NC, n = i % NC;
       bv[v] = k < kn && n < p.N ? p.B[(long long)(kc0 + k) * p.ldb + n] : 0.f;
     }
-    f32x4 a[NJ];
-    if (kn == KC) {  // every quad of the chunk inside K
+    if (kn == KC) {
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
         a[j] = *reinterpret_cast<const f32x4u *>(arow + kc0 + kColStep * j + 32 * split + 4 * q);
@@ -2430,6 +2435,13 @@ __global__ void __launch_bounds__(kColThreads) colstrip_kernel(Problem p) {
         }
       }
     }
+  };
+  float bv[BV];
+  f32x4 a[NJ];
+  if constexpr (PREFETCH) load_chunk(bv, a, 0);
+  for (int kc0 = 0; kc0 < p.K; kc0 += KC) {
+    const int kn = p.K - kc0 < KC ? p.K - kc0 : KC;
+    if constexpr (!PREFETCH) load_chunk(bv, a, kc0);
     __syncthreads();  // every lane is done with the previous chunk's B
 #pragma unroll
     for (int v = 0; v < BV; ++v) {
@@ -2437,6 +2449,9 @@ __global__ void __launch_bounds__(kColThreads) colstrip_kernel(Problem p) {
       bq[(k >> 2) * QF + 4 * n + (k & 3)] = bv[v];
     }
     __syncthreads();
+    const bool more = PREFETCH && kc0 + KC < p.K;
+    f32x4 an[NJ];
+    if (more) load_chunk(bv, an, kc0 + KC);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int kl = kColStep * j + 32 * split + 4 * q;
@@ -2448,6 +2463,10 @@ __global__ void __launch_bounds__(kColThreads) colstrip_kernel(Problem p) {
           for (int t = 0; t < 4; ++t) acc[n] += a[j][t] * b[t];
         }
       }
+    }
+    if (more) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) a[j] = an[j];
     }
   }
 #pragma unroll
@@ -2470,17 +2489,28 @@ __global__ void __launch_bounds__(kColThreads) colstrip_kernel(Problem p) {
   }
 }
 
+// The prefetching form unless it holds fewer workgroups resident than the
+// plain one while the grid needs more than it holds.
+template <int NC>
+hipError_t launch_colstrip_nc(const Problem &p, long long wgs, hipStream_t s) {
+  const dim3 grid((unsigned)wgs), block(kColThreads);
+  const long long with = resident_workgroups<colstrip_kernel<NC, true>, kColThreads>();
+  const long long without = resident_workgroups<colstrip_kernel<NC, false>, kColThreads>();
+  if (wgs <= with || with >= without)
+    return launch_kernel(colstrip_kernel<NC, true>, grid, block, s, p);
+  return launch_kernel(colstrip_kernel<NC, false>, grid, block, s, p);
+}
+
 hipError_t launch_colstrip(const Problem &p, hipStream_t s) {
   if (p.N < 1 || p.N > kStripMaxCols || p.M < 1) return hipErrorInvalidValue;
   const long long wgs = ceil_div(p.M, kColRows);
   if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)wgs), block(kColThreads);
   switch (strip_cols(p.N)) {
-    case 1: return launch_kernel(colstrip_kernel<1>, grid, block, s, p);
-    case 2: return launch_kernel(colstrip_kernel<2>, grid, block, s, p);
-    case 4: return launch_kernel(colstrip_kernel<4>, grid, block, s, p);
-    case 8: return launch_kernel(colstrip_kernel<8>, grid, block, s, p);
-    default: return launch_kernel(colstrip_kernel<16>, grid, block, s, p);
+    case 1: return launch_colstrip_nc<1>(p, wgs, s);
+    case 2: return launch_colstrip_nc<2>(p, wgs, s);
+    case 4: return launch_colstrip_nc<4>(p, wgs, s);
+    case 8: return launch_colstrip_nc<8>(p, wgs, s);
+    default: return launch_colstrip_nc<16>(p, wgs, s);
   }
 }
 
