@@ -60,8 +60,11 @@ _LDS = {"A_edge": (LD_A_EDGE, 0, 0), "A": (LD_A, 0, 0), "B_edge": (0, LD_B_EDGE,
 
 
 @pytest.mark.parametrize("which", list(_LDS))
-@pytest.mark.parametrize("shape", [(256, 256, 64), (300, 260, 65)])
+@pytest.mark.parametrize("shape", [(256, 256, 64), (300, 260, 65), (5, 300, 65), (300, 5, 65)])
 def test_f32_leading_dimension_beyond_32bit_offsets(g, which, shape):
+    """Every entry that takes the shape; the thin ones (5 rows: the thin-M
+    strip; 5 columns: the thin-N kernel) address with 64-bit offsets
+    throughout."""
     M, N, K = shape
     dev = torch.device("cuda:0")
     a, b = make(M, N, K, "normal", seed=M + N + K)
