@@ -80,7 +80,7 @@ extern "C" {
  * barrier per 32-deep k step; a partial last k step is filled through
  * registers with zeros past K; edge tiles are moved back inside C, and thin
  * remainder strips run on their own kernel, which also computes whole
- * products of at most 32 rows (a stream of B, read once per 16 rows);
+ * products of at most 32 rows (a stream of B, read once);
  * products of at most 16 columns run on a thin-N kernel (a stream of A).
  * Few-tile products split each tile's k steps over the 4 waves and add the
  * partial tiles in wave order; K = 64 products keep A in LDS and stream B.

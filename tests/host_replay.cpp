@@ -272,19 +272,7 @@ void replay_arow16(const Shape &s, int slots) {
 
 // ---- thin-M strip kernel ------------------------------------------------------
 // 512 threads: 4 column quads x 128 k slices, 16 columns per workgroup.
-void replay_strip_pass(const Shape &s);
-
-void replay_strip(const Shape &s) {  // passes of kStripPassRows rows
-  for (int r0 = 0; r0 < s.M; r0 += kStripPassRows) {
-    Shape pass = s;
-    pass.M = s.M - r0 < kStripPassRows ? s.M - r0 : kStripPassRows;
-    // Offsets of the pass are relative to its first row, whose rows of A and C
-    // exist: the pass's checks run against its own M rows.
-    replay_strip_pass(pass);
-  }
-}
-
-void replay_strip_pass(const Shape &s) {
+void replay_strip(const Shape &s) {
   const int wgs = (int)ceil_div(s.N, 16);
   const int R = strip_rows(s.M), NB = strip_batch_quads(R), KB = 512;
   auto row_of = [&](int r) { return r < s.M ? r : s.M - 1; };  // rows past M read row M - 1

@@ -275,11 +275,10 @@ def test_tile_queries():
         q = g.gemm_f32_tile("prod", i, 64, 64, 64)
         assert q["config"] == i and q["threads"] % 64 == 0
         assert q["BM"] % 32 == 0 and q["BN"] % 32 == 0 and q["BK"] % 8 == 0
-    # products of at most 32 rows run the thin-M strip kernel whole, 16 rows
-    # per launch; its entry reports the rows a workgroup holds and refuses a
-    # 33rd row
-    for M, bm in ((1, 1), (2, 2), (3, 4), (4, 4), (5, 8), (8, 8), (9, 16), (16, 16), (17, 16),
-                  (32, 16)):
+    # products of at most 32 rows run the thin-M strip kernel whole; its
+    # entry reports the rows a workgroup holds and refuses a 33rd row
+    for M, bm in ((1, 1), (2, 2), (3, 4), (4, 4), (5, 8), (8, 8), (9, 16), (16, 16), (17, 32),
+                  (32, 32)):
         q = g.gemm_f32_tile("prod", -1, M, 77, 5)
         assert (q["config"], q["BM"], q["BN"], q["threads"]) == (strip, bm, 16, 512)
     assert g.gemm_f32_tile("prod", -1, 33, 4095, 2049)["config"] != strip

@@ -339,7 +339,7 @@ def test_small_k_padded_leading_dimensions(g):
 
 def test_thin_remainder_strips(g):
     """Main block plus thin remainder strips: a bottom strip of up to BM/8
-    rows (at most 32) goes to the thin-M strip kernel, 16 rows per launch; a
+    rows (at most 32) goes to the thin-M strip kernel in one launch; a
     right strip of up to BN/8 columns to small tiles."""
     for cfg in (0, 2, 7):
         t = g.gemm_f32_tile("prod", cfg, 1, 1, 1)
@@ -372,14 +372,14 @@ def test_strip_kernel_long_k(g):
 
 def test_strip_entry_whole_product(g):
     """Products of 1-32 rows: the automatic choice runs the thin-M strip kernel
-    on the whole product (16 rows per launch).  Column counts below, at and past a group of 16
+    on the whole product.  Column counts below, at and past a group of 16
     (partial last group), K from 1 to several batches of its k-slices, and
     padded leading dimensions (odd ldb and ldc: rows only 4-byte aligned)
     with the padding left untouched."""
     dev = _dev()
     strip = g.gemm_f32_tile("prod", -1, 1, 4095, 2049)["config"]
     assert strip == STRIP_ENTRY
-    for M in list(range(1, 10)) + [12, 16, 17, 24, 32]:
+    for M in list(range(1, 10)) + [12, 16, 17, 24, 31, 32]:
         for (N, K) in [(1, 1), (15, 3), (16, 129), (17, 2049), (300, 40), (4095, 513)]:
             assert g.gemm_f32_tile("prod", -1, M, N, K)["config"] == strip
             print(f"case: strip entry {M}x{N}x{K}", flush=True)
@@ -389,7 +389,7 @@ def test_strip_entry_whole_product(g):
             _tol_check(_run(g, a, b, "prod"), oracle.gemm(a, b), K, f"strip entry {M}x{N}x{K}")
     for (M, N, K, lda, ldb, ldc) in [(3, 300, 129, 133, 301, 303), (8, 4095, 2049, 2050, 4097, 4099),
                                      (1, 17, 5, 5, 21, 17), (13, 1000, 1025, 1027, 1001, 1003),
-                                     (29, 333, 77, 79, 335, 337)]:
+                                     (29, 333, 77, 79, 335, 337), (32, 129, 2049, 2051, 131, 133)]:
         assert g.gemm_f32_tile("prod", -1, M, N, K)["config"] == STRIP_ENTRY
         print(f"case: strip entry padded {M}x{N}x{K} lds {lda},{ldb},{ldc}", flush=True)
         a, b = make(M, N, K, "small_int", seed=lda + ldb)
@@ -423,7 +423,7 @@ def test_colstrip_entry_whole_product(g):
             a, b = make(M, N, K, "normal", seed=N * 1021 + M * K)
             _tol_check(_run(g, a, b, "prod"), oracle.gemm(a, b), K, f"colstrip entry {M}x{N}x{K}")
     for (M, N, K, lda, ldb, ldc) in [(300, 3, 129, 133, 5, 7), (4097, 8, 2049, 2050, 9, 11),
-                                     (40, 1, 5, 9, 1, 2), (1000, 13, 513, 515, 17, 14)]:
+                                     (70, 1, 5, 9, 1, 2), (1000, 13, 513, 515, 17, 14)]:
         assert g.gemm_f32_tile("prod", -1, M, N, K)["config"] == COLSTRIP_ENTRY
         print(f"case: colstrip entry padded {M}x{N}x{K} lds {lda},{ldb},{ldc}", flush=True)
         a, b = make(M, N, K, "small_int", seed=lda + ldb + ldc)

@@ -209,10 +209,10 @@ int region_rows(int M, int N, int K) {
 }
 
 // Shape-based choice.  At most kStripMaxRows rows: the thin-M strip kernel
-// (entry 26), which streams B once per 16 rows, where a tile kernel would
-// fill its 64- to 256-row tiles with 1 to 32 useful rows (1 x 4095 x 2049:
-// 91 us on the 64 x 64 K-split entry, 13 us as a strip; 32 x 4095 x 2049:
-// 101 against 42 us).  At most kStripMaxCols columns: the thin-N kernel
+// (entry 26), which streams B once, where a tile kernel would fill its 64-
+// to 256-row tiles with 1 to 32 useful rows (1 x 4095 x 2049: 91 us on the
+// 64 x 64 K-split entry, 13 us as a strip; 32 x 4095 x 2049: 101 against
+// 34 us).  At most kStripMaxCols columns: the thin-N kernel
 // (entry 27), which streams A once.  K <= 64 with many tiles: the
 // A-resident small-K kernel (only B moves per tile; C stores of one
 // tile drained during the next tile's MFMAs), on 16x16 MFMAs with one wave

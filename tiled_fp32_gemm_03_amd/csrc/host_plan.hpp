@@ -80,13 +80,14 @@ bool prod_supports(int index, int M, int N, int K);
 constexpr int kRemainderConfig = 3;
 constexpr int kStripMaxRows = 32;
 // The launch-table entry that runs the thin-M strip kernel on a whole
-// product of at most kStripMaxRows rows, the rows one launch of it covers
-// (more rows take one launch per kStripPassRows, each reading all of B), and
+// product of at most kStripMaxRows rows (one launch; it reads B once), and
 // the rows one of its workgroups holds for an M-row product (the kernel is
-// instantiated for 1, 2, 4, 8 and 16).
+// instantiated for 1, 2, 4, 8, 16 and 32).  Two launches of 32 rows lose to
+// the tile entries where those fill the chip (64 x 16384 x 4096: 303 us).
 constexpr int kStripConfig = 26;
-constexpr int kStripPassRows = 16;
-constexpr int strip_rows(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
+constexpr int strip_rows(int M) {
+  return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : M <= 16 ? 16 : 32;
+}
 // Quads of k whose loads a strip lane issues before using any (its batch),
 // per row count: measured kernel durations on N = 1024-32768, K = 2049-8192
 // (1 x 4095 x 2049: 10.7, 11.4, 13.0 us for 1, 2, 4 quads; 8 x 8191 x 4096:

@@ -2209,9 +2209,9 @@ __global__ void __launch_bounds__(256) arow16_kernel(Problem p, int panels, int 
   }
 }
 
-// Thin-M kernel for a strip of at most 16 rows: a bottom remainder strip, or
-// a whole product of that few rows (a 64- to 256-row MFMA tile holding one
-// to sixteen valid rows would cost a whole tile's work per column block).  Its
+// Thin-M kernel for a strip of at most 32 rows: a bottom remainder strip, or
+// a whole product of that few rows (a 64- to 256-row MFMA tile holding 1 to
+// 32 valid rows would cost a whole tile's work per column block).  Its
 // time is the stream of B, read once: each workgroup owns 16 columns, and
 // its 512 threads are 4 column quads x 128 k-slices; slice s takes the
 // quads of consecutive k starting at 4 s, 4 s + 512, ..., so a lane loads
@@ -2234,6 +2234,7 @@ constexpr int kStripWaves = kStripThreads / 64;
 template <int R, int NB>
 __global__ void __launch_bounds__(kStripThreads) strip_kernel(Problem p) {
   constexpr int KB = 4 * kStripSlices;  // k per quad round of the workgroup
+  constexpr int RS = R <= 16 ? R : 8;   // rows whose A chunks a lane holds at once
   __shared__ float red[kStripWaves][R][kStripCols];
   const int tid = threadIdx.x;
   const int c4 = (tid & 3) * 4;  // first of this lane's 4 columns
@@ -2245,9 +2246,11 @@ __global__ void __launch_bounds__(kStripThreads) strip_kernel(Problem p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[r][j] = 0.f;
   // Rows past M read row M - 1 (never stored), so no load is conditional.
-  const float *arow[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) arow[r] = p.A + (long long)(r < p.M ? r : p.M - 1) * p.lda;
+  // Row starts are formed where they are used (32 held pointers would take
+  // 64 registers).
+  auto arow = [&](int r) __attribute__((always_inline)) {
+    return p.A + (long long)(r < p.M ? r : p.M - 1) * p.lda;
+  };
   const bool whole = n0 + kStripCols <= p.N;
   const int valid = (int)(p.N - n0) - c4;  // columns of this lane inside C (whole: >= 4)
   const float *bp = p.B + n0 + c4;
@@ -2262,57 +2265,82 @@ __global__ void __launch_bounds__(kStripThreads) strip_kernel(Problem p) {
     return v;
   };
   int k = k0;
-  // Whole batches: NB quads, every k inside K.
+  // Whole batches: NB quads, every k inside K.  Rows go in sets of RS (all
+  // R up to 16 rows; four sets of 8 for 32), each set's A chunks loaded
+  // after the previous set's FMAs, so that the 32-row form fits its
+  // registers beside its 128 accumulators.
   for (; k + (NB - 1) * KB + 3 < p.K; k += NB * KB) {
-    f32x4 b[NB][4], a[NB][R];
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) b[u][t] = load_b(k + u * KB + t);
-#pragma unroll
-      for (int r = 0; r < R; ++r) a[u][r] = *reinterpret_cast<const f32x4u *>(arow[r] + k + u * KB);
-    }
+    f32x4 b[NB][4];
 #pragma unroll
     for (int u = 0; u < NB; ++u)
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < 4; ++t) b[u][t] = load_b(k + u * KB + t);
 #pragma unroll
-        for (int r = 0; r < R; ++r)
+    for (int r0 = 0; r0 < R; r0 += RS) {
+      f32x4 a[NB][RS];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[r][j] += a[u][r][t] * b[u][t][j];
+      for (int u = 0; u < NB; ++u)
+#pragma unroll
+        for (int r = 0; r < RS; ++r)
+          a[u][r] = *reinterpret_cast<const f32x4u *>(arow(r0 + r) + k + u * KB);
+#pragma unroll
+      for (int u = 0; u < NB; ++u)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int r = 0; r < RS; ++r)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[r0 + r][j] += a[u][r][t] * b[u][t][j];
+      // keep the next set's loads after these FMAs
+      if constexpr (RS < R) __builtin_amdgcn_sched_barrier(0);
+    }
   }
   // The rest of this slice (fewer than NB quads, the last possibly partial):
   // one batch, k past K loading row K - 1 and adding nothing.
   if (k < p.K) {
-    f32x4 b[NB][4], a[NB][R];
+    f32x4 b[NB][4];
 #pragma unroll
     for (int u = 0; u < NB; ++u)
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int kk = k + u * KB + t;
-        const int kc = kk < p.K ? kk : p.K - 1;
-        b[u][t] = load_b(kc);
-#pragma unroll
-        for (int r = 0; r < R; ++r) a[u][r][t] = arow[r][kc];
+        b[u][t] = load_b(kk < p.K ? kk : p.K - 1);
       }
 #pragma unroll
-    for (int u = 0; u < NB; ++u)
+    for (int r0 = 0; r0 < R; r0 += RS) {
+      f32x4 a[NB][RS];
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        if (k + u * KB + t < p.K) {
+      for (int u = 0; u < NB; ++u)
 #pragma unroll
-          for (int r = 0; r < R; ++r)
+        for (int t = 0; t < 4; ++t) {
+          const int kk = k + u * KB + t;
+          const int kc = kk < p.K ? kk : p.K - 1;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[r][j] += a[u][r][t] * b[u][t][j];
+          for (int r = 0; r < RS; ++r) a[u][r][t] = arow(r0 + r)[kc];
         }
+#pragma unroll
+      for (int u = 0; u < NB; ++u)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          if (k + u * KB + t < p.K) {
+#pragma unroll
+            for (int r = 0; r < RS; ++r)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) acc[r0 + r][j] += a[u][r][t] * b[u][t][j];
+          }
+      if constexpr (RS < R) __builtin_amdgcn_sched_barrier(0);
+    }
   }
-  // Slices of one wave: lanes 4 s + q (s = 0..15) hold column quad q.
+  // Slices of one wave: lanes 4 s + q (s = 0..15) hold column quad q.  Row
+  // by row, so that few exchanged values are in flight at once.
 #pragma unroll
-  for (int m = 4; m < 64; m <<= 1)
+  for (int r = 0; r < R; ++r) {
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int m = 4; m < 64; m <<= 1)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[r][j] += __shfl_xor(acc[r][j], m);
+    if constexpr (RS < R) __builtin_amdgcn_sched_barrier(0);
+  }
   const int wave = tid >> 6;
   if ((tid & 63) < 4) {
 #pragma unroll
@@ -2332,30 +2360,19 @@ __global__ void __launch_bounds__(kStripThreads) strip_kernel(Problem p) {
   }
 }
 
-hipError_t launch_strip_pass(const Problem &p, hipStream_t s) {
+hipError_t launch_strip(const Problem &p, hipStream_t s) {
+  if (p.M < 1 || p.M > kStripMaxRows) return hipErrorInvalidValue;
   const dim3 grid((unsigned)ceil_div(p.N, kStripCols)), block(kStripThreads);
   switch (strip_rows(p.M)) {
     case 1: return launch_kernel(strip_kernel<1, strip_batch_quads(1)>, grid, block, s, p);
     case 2: return launch_kernel(strip_kernel<2, strip_batch_quads(2)>, grid, block, s, p);
     case 4: return launch_kernel(strip_kernel<4, strip_batch_quads(4)>, grid, block, s, p);
     case 8: return launch_kernel(strip_kernel<8, strip_batch_quads(8)>, grid, block, s, p);
-    default: return launch_kernel(strip_kernel<16, strip_batch_quads(16)>, grid, block, s, p);
+    case 16: return launch_kernel(strip_kernel<16, strip_batch_quads(16)>, grid, block, s, p);
+    default: return launch_kernel(strip_kernel<32, strip_batch_quads(32)>, grid, block, s, p);
   }
 }
 
-// Up to kStripPassRows rows per launch, in order on the stream.
-hipError_t launch_strip(const Problem &p, hipStream_t s) {
-  if (p.M < 1 || p.M > kStripMaxRows) return hipErrorInvalidValue;
-  for (int r0 = 0; r0 < p.M; r0 += kStripPassRows) {
-    Problem pass = p;
-    pass.M = p.M - r0 < kStripPassRows ? p.M - r0 : kStripPassRows;
-    pass.A = p.A + (long long)r0 * p.lda;
-    pass.C = p.C + (long long)r0 * p.ldc;
-    const hipError_t e = launch_strip_pass(pass, s);
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
-}
 
 // Thin-N kernel for a whole product of at most 16 columns: a stream of A,
 // read once (a 64- to 256-column MFMA tile holding one to eight valid
