@@ -56,7 +56,11 @@ extern "C" {
  * blocks per wave; entry 3 loads both operands straight into LDS in their
  * row-major layouts (16-byte aligned rows of A and B, N % 8 == 0 and K a
  * multiple of 64; otherwise it runs entry 0), reads B's operands with the
- * transposing LDS read and computes on v_mfma_f32_16x16x32_bf16 / _f16.
+ * transposing LDS read and computes on v_mfma_f32_16x16x32_bf16 / _f16;
+ * entry 4 is the same pipeline on v_mfma_f32_32x32x16_bf16 / _f16 (same
+ * conditions, same fallback) and gives entry 0's bits.  The automatic
+ * choice takes entry 4 for K == 64 and entry 3 for other multiples of 64
+ * when 256 x 256 tiles fill the GPU.
  */
 int gemm_mixed(int M, int N, int K, const void *A, int lda, const void *B,
                int ldb, float *C, int ldc, int format, int config,

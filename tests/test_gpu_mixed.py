@@ -170,20 +170,21 @@ def test_all_ones_full_ragged_shape(g, fmt):
         assert torch.all(c == float(w.K)).item()
 
 
-DIRECT_ENTRY = 3  # 16x16x32 MFMAs with direct loads: its own summation order
+DIRECT_ENTRIES = (3, 4)  # direct loads on 16x16x32 (its own summation order) and 32x32x16 MFMAs
 
 
+@pytest.mark.parametrize("entry", DIRECT_ENTRIES)
 @pytest.mark.parametrize("fmt", FORMATS)
-def test_direct_entry_many_tiles(g, fmt):
-    """The direct-load entry where workgroups walk two tiles and the last
+def test_direct_entry_many_tiles(g, fmt, entry):
+    """A direct-load entry where workgroups walk two tiles and the last
     tile row and column are moved back inside C: exact on small integers
     (sampled elements plus whole edge rows and columns), within the fp32
     bar on normal inputs (sampled)."""
     M, N, K = 4400, 4352, 128
     for dist in ("small_int", "normal"):
-        print(f"case: mixed {fmt} direct entry {M}x{N}x{K} {dist}", flush=True)
+        print(f"case: mixed {fmt} direct entry {entry} {M}x{N}x{K} {dist}", flush=True)
         a, b = make_mixed(M, N, K, dist, seed=M + K, fmt=fmt)
-        c = g.matmul_mixed(_to_dev(a, fmt), _to_dev(b, fmt), config=DIRECT_ENTRY)
+        c = g.matmul_mixed(_to_dev(a, fmt), _to_dev(b, fmt), config=entry)
         torch.cuda.synchronize()
         ii, jj = sample_indices(M, N, 20000, seed=K)
         got = c[torch.from_numpy(ii).to(_dev()), torch.from_numpy(jj).to(_dev())].cpu().numpy()
@@ -198,6 +199,23 @@ def test_direct_entry_many_tiles(g, fmt):
             assert np.array_equal(got_e, oracle.gemm_mixed_elems(a, b, fmt, edge_i, edge_j))
         else:
             tol_check(got, ref, K, f"{fmt} direct entry")
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("shape", [(512, 768, 64), (1024, 512, 1024), (300, 513, 192)])
+def test_direct_32x32_entry_matches_register_staged_bitwise(g, fmt, shape):
+    """Entry 4 runs the direct-load pipeline on the 32x32x16 MFMAs of entry
+    0, adding each element's k in the same 16-deep groups in ascending
+    order, so on float inputs its result equals entry 0's bit for bit
+    (these shapes fit its kernel: K a multiple of 64, at least 256 rows and
+    columns, one or more tiles per workgroup), and it meets the fp32 bar
+    against the oracle."""
+    M, N, K = shape
+    print(f"case: mixed {fmt} entry 4 against entry 0 {shape}", flush=True)
+    a, b = make_mixed(M, N, K, "normal", seed=M + 3 * N + K, fmt=fmt)
+    c4 = _run(g, a, b, fmt, 4)
+    assert np.array_equal(c4, _run(g, a, b, fmt, 0))
+    tol_check(c4, oracle.gemm_mixed(a, b, fmt), K, f"{fmt} entry 4 {shape}")
 
 
 @pytest.mark.parametrize("fmt", FORMATS)

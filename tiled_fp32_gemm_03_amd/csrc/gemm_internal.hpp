@@ -58,7 +58,7 @@ struct MixedConfig {
 // 256 x 256, K a positive multiple of 64, 32-bit lane offsets: lane_offsets_fit),
 // and its launch.
 bool mixed16_fits(const MixedProblem &p);
-hipError_t launch_mixed16(int format, const MixedProblem &p, hipStream_t s);
+hipError_t launch_mixed16(int format, const MixedProblem &p, hipStream_t s, bool mfma32);
 
 int mixed_num_configs();
 const MixedConfig &mixed_config(int index);

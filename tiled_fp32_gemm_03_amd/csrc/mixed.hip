@@ -278,6 +278,7 @@ const MixedConfig kMixedConfigs[] = {
     {Mixed256w16::BM, Mixed256w16::BN, kMixedBK, Mixed256w16::WGM, Mixed256w16::WGN, 1,
      "256x256x64 w4x4"},
     {256, 256, kMixedBK, 2, 2, 1, "256x256x64 w2x2 ldsdma mfma16x16x32"},
+    {256, 256, kMixedBK, 2, 2, 1, "256x256x64 w2x2 ldsdma mfma32x32x16"},
 };
 constexpr int kMixedNumConfigs = sizeof(kMixedConfigs) / sizeof(kMixedConfigs[0]);
 
@@ -312,8 +313,15 @@ const MixedConfig &mixed_config(int index) { return kMixedConfigs[index]; }
 // product whose K is a multiple of its 64-deep step and whose 256 x 256
 // tiles fill the GPU, and any other 256 x 256 choice with such a K; its
 // launcher falls back to entry 0 for rows that are not 16-byte aligned.
+// With K = 64 (one step per tile, the time mostly the C stores) entry 4,
+// the same kernel on 32x32x16 MFMAs, is faster (16384 x 16384 x 64: 200
+// against 223 us); with more steps per tile the operand traffic through
+// LDS bounds both and entry 3 is ahead (4096^3: 102 against 109 us;
+// 4400 x 4352 x 128: 27.9 against 29.9).
 int mixed_choose(int M, int N, int K) {
-  if (K % kMixedBK == 0 && ceil_div(M, 256) * ceil_div(N, 256) >= 256) return 3;
+  const long long tiles256 = (long long)ceil_div(M, 256) * ceil_div(N, 256);
+  if (K == kMixedBK && tiles256 >= 256) return 4;
+  if (K % kMixedBK == 0 && tiles256 >= 256) return 3;
   if (K < 4 * kMixedBK) return 1;
   int best = 0;
   double best_cost = 0;
@@ -337,7 +345,10 @@ hipError_t launch_mixed(int format, int index, const MixedProblem &p, hipStream_
     case 2:
       return bf ? launch_one<Mixed256w16, kMixedBf16>(p, s) : launch_one<Mixed256w16, kMixedF16>(p, s);
     case 3:  // direct loads on 16x16x32 MFMAs where they fit, else entry 0
-      if (mixed16_fits(p)) return launch_mixed16(format, p, s);
+      if (mixed16_fits(p)) return launch_mixed16(format, p, s, false);
+      return bf ? launch_one<Mixed256, kMixedBf16>(p, s) : launch_one<Mixed256, kMixedF16>(p, s);
+    case 4:  // the same on 32x32x16 MFMAs
+      if (mixed16_fits(p)) return launch_mixed16(format, p, s, true);
       return bf ? launch_one<Mixed256, kMixedBf16>(p, s) : launch_one<Mixed256, kMixedF16>(p, s);
     default: return hipErrorInvalidValue;
   }
