@@ -128,6 +128,22 @@ def measure_mfma(g, stream) -> float:
     return g.gemm_f32_probe_mfma_flops(wgs, iters) / (ms * 1e-3) / 1e12
 
 
+def measure_mfma16(g, stream) -> dict:
+    """bf16 MFMA probe at one wave per SIMD (one 256-thread workgroup per
+    CU), the 16-bit rung's occupancy: TFLOP/s of independent 16x16x32 and
+    32x32x16 chains; 20 timed launches after 5 warm-up ones, about 1 ms each."""
+    import torch
+    wgs = 256
+    buf = torch.zeros(wgs * 4, device="cuda:0")
+    out = {}
+    for shape, iters in ((16, 2500), (32, 7000)):
+        ms, _ = time_launches(lambda: g.gemm_f32_probe_mfma16(shape, wgs, iters, buf.data_ptr(),
+                                                              stream.cuda_stream), 20, 5, stream)
+        name = "16x16x32" if shape == 16 else "32x32x16"
+        out[name] = round(g.gemm_f32_probe_mfma16_flops(shape, wgs, iters) / (ms * 1e-3) / 1e12, 1)
+    return out
+
+
 def measure_valu(g, stream) -> float:
     import torch
     wgs, iters = 256 * 8, 500
@@ -417,6 +433,8 @@ def main() -> int:
         log(f"fp32 MFMA probe: {pm:.1f} TFLOP/s")
         pv = measure_valu(g, stream)
         log(f"fp32 vector FMA probe: {pv:.1f} TFLOP/s")
+        pb = measure_mfma16(g, stream)
+        log(f"bf16 MFMA probe, one wave per SIMD: {pb} TFLOP/s")
         fused = measure_fused(g, stream, args.record_settle_ms)
         log(f"fused MFMA + store probe at 32 FLOP/B: {fused}")
         # The fused probe's store-only mode is a streaming write too: the
@@ -425,7 +443,8 @@ def main() -> int:
                                       if k.startswith("store_only"))
         hbm["best"] = max(hbm["copy"], hbm["fill"], hbm["vector_add"], hbm["fused_store_only"])
         measured = {"hbm_gbps": hbm, "mfma_fp32_tflops": round(pm, 2),
-                    "valu_fp32_tflops": round(pv, 2), "fused_k64": fused}
+                    "valu_fp32_tflops": round(pv, 2), "mfma_bf16_one_wave_per_simd_tflops": pb,
+                    "fused_k64": fused}
         result["measured_peaks"] = measured
         result["roofline"]["frac_of_measured_mfma"] = round(tflops / pm, 4)
 

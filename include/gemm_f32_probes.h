@@ -47,6 +47,23 @@ int gemm_f32_probe_mfma(int workgroups, int iters, float *out, void *stream);
 long long gemm_f32_probe_mfma_flops(int workgroups, int iters);
 
 /*
+ * gemm_f32_probe_mfma16 -- bf16 matrix-core throughput probe, the measured
+ * compute roof of the 16-bit rung (geek-doc.cn, "矩阵乘法 tiling", §五
+ * names 16-bit matrix-core GEMM as the next step; mayulu.co, "CUDA 编程系列之三",
+ * §2-§3: a kernel is bounded by the compute roof it can reach).  No memory
+ * traffic in its loop: `workgroups` workgroups of 256 threads (one wave per
+ * SIMD when workgroups <= the CU count), each wave running `iters` rounds
+ * of 32 independent v_mfma_f32_16x16x32_bf16 chains (shape 16) or 8
+ * independent v_mfma_f32_32x32x16_bf16 chains (shape 32).  One float per
+ * wave is written to out (out must hold workgroups * 4 floats, 4-byte
+ * aligned).  shape is 16 or 32, workgroups >= 1, iters >= 1, else
+ * GEMM_F32_BAD_ARG.  gemm_f32_probe_mfma16_flops returns the FLOPs such a
+ * call performs (-1 for invalid arguments).
+ */
+int gemm_f32_probe_mfma16(int shape, int workgroups, int iters, float *out, void *stream);
+long long gemm_f32_probe_mfma16_flops(int shape, int workgroups, int iters);
+
+/*
  * gemm_f32_probe_valu -- fp32 vector-ALU throughput probe, the compute roof
  * of kernels that multiply-add on the vector ALU rather than on matrix cores:
  * `workgroups` workgroups of 256 threads, each lane running `iters` loop

@@ -31,7 +31,8 @@ def test_headers_declare_expected_entry_points():
     names = set(_declared_functions())
     assert {"gemm_f32", "gemm_f32_ex", "gemm_f32_tile", "gemm_f32_num_configs",
             "gemm_f32_status_string", "gemm_f32_version", "gemm_f32_probe_stream",
-            "gemm_f32_probe_mfma", "gemm_f32_probe_mfma_flops", "gemm_f32_probe_valu",
+            "gemm_f32_probe_mfma", "gemm_f32_probe_mfma_flops", "gemm_f32_probe_mfma16",
+            "gemm_f32_probe_mfma16_flops", "gemm_f32_probe_valu",
             "gemm_f32_probe_valu_flops", "gemm_f32_probe_lds", "gemm_f32_probe_lds_bytes",
             "gemm_f32_probe_fused", "gemm_f32_probe_fused_flops", "gemm_f32_probe_fused_bytes",
             "gemm_f32_device_props", "gemm_mixed", "gemm_mixed_num_configs", "gemm_mixed_tile", "gemm_f32_splitk",
@@ -228,6 +229,13 @@ def test_probe_validation():
     assert lib.gemm_f32_probe_mfma(1, 1, None, None) == 3
     assert g.gemm_f32_probe_mfma_flops(2, 3) == 2 * 4 * 3 * 8 * (2 * 32 * 32 * 2)
     assert g.gemm_f32_probe_mfma_flops(0, 3) == -1
+    assert lib.gemm_f32_probe_mfma16(16, 0, 1, 256, None) == 8
+    assert lib.gemm_f32_probe_mfma16(24, 1, 1, 256, None) == 8
+    assert lib.gemm_f32_probe_mfma16(32, 1, 1, None, None) == 3
+    assert lib.gemm_f32_probe_mfma16(32, 1, 1, 258, None) == 6
+    assert g.gemm_f32_probe_mfma16_flops(16, 2, 3) == 2 * 4 * 3 * 32 * (2 * 16 * 16 * 32)
+    assert g.gemm_f32_probe_mfma16_flops(32, 2, 3) == 2 * 4 * 3 * 8 * (2 * 32 * 32 * 16)
+    assert g.gemm_f32_probe_mfma16_flops(8, 2, 3) == -1
     assert lib.gemm_f32_probe_valu(0, 1, 256, None) == 8
     assert lib.gemm_f32_probe_valu(1, 0, 256, None) == 8
     assert lib.gemm_f32_probe_valu(1, 1, None, None) == 3

@@ -656,6 +656,15 @@ def test_mfma_probe_runs(g):
     assert torch.isfinite(out).all().item() and torch.all(out != 0).item()
 
 
+@pytest.mark.parametrize("shape", [16, 32])
+def test_mfma16_probe_runs(g, shape):
+    dev = _dev()
+    out = torch.zeros(8 * 4, device=dev)
+    g.gemm_f32_probe_mfma16(shape, 8, 10, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item() and torch.all(out > 0).item()
+
+
 def test_valu_probe_runs(g):
     dev = _dev()
     out = torch.zeros(8 * 4, device=dev)

@@ -11,6 +11,7 @@ Raw C-ABI mirrors (same names and argument order as ``include/gemm_f32.h``):
   gemm_f32_num_configs(variant), gemm_f32_status_string(rc), gemm_f32_version()
   gemm_f32_probe_stream(kind, n, x, y, z, stream)      (include/gemm_f32_probes.h)
   gemm_f32_probe_mfma(workgroups, iters, out, stream), gemm_f32_probe_mfma_flops(...)
+  gemm_f32_probe_mfma16(shape, workgroups, iters, out, stream), gemm_f32_probe_mfma16_flops(...)
   gemm_f32_probe_valu(workgroups, iters, out, stream), gemm_f32_probe_valu_flops(...)
   gemm_f32_probe_lds(workgroups, iters, out, stream), gemm_f32_probe_lds_bytes(...)
   gemm_f32_probe_fused(mode, workgroups, trips, out, out_bytes, clocks, stream),
@@ -43,7 +44,8 @@ __all__ = [
     "GemmError", "VARIANTS", "config_name", "PROBE_COPY", "PROBE_FILL", "PROBE_VADD",
     "gemm_f32", "gemm_f32_ex", "gemm_f32_tile", "gemm_f32_num_configs",
     "gemm_f32_status_string", "gemm_f32_version", "gemm_f32_last_error", "gemm_f32_probe_stream",
-    "gemm_f32_probe_mfma", "gemm_f32_probe_mfma_flops", "gemm_f32_probe_valu",
+    "gemm_f32_probe_mfma", "gemm_f32_probe_mfma_flops", "gemm_f32_probe_mfma16",
+    "gemm_f32_probe_mfma16_flops", "gemm_f32_probe_valu",
     "gemm_f32_probe_valu_flops", "gemm_f32_probe_lds", "gemm_f32_probe_lds_bytes",
     "gemm_f32_probe_fused", "gemm_f32_probe_fused_flops", "gemm_f32_probe_fused_bytes",
     "FUSED_BOTH", "FUSED_MFMA", "FUSED_STORE",
@@ -88,6 +90,8 @@ _SIGS = {
     "gemm_f32_probe_stream": ([_i, _ll, _p, _p, _p, _p], _i),
     "gemm_f32_probe_mfma": ([_i, _i, _p, _p], _i),
     "gemm_f32_probe_mfma_flops": ([_i, _i], _ll),
+    "gemm_f32_probe_mfma16": ([_i, _i, _i, _p, _p], _i),
+    "gemm_f32_probe_mfma16_flops": ([_i, _i, _i], _ll),
     "gemm_f32_probe_valu": ([_i, _i, _p, _p], _i),
     "gemm_f32_probe_valu_flops": ([_i, _i], _ll),
     "gemm_f32_probe_lds": ([_i, _i, _p, _p], _i),
@@ -198,6 +202,15 @@ def gemm_f32_probe_mfma(workgroups, iters, out, stream=0) -> None:
 
 def gemm_f32_probe_mfma_flops(workgroups, iters) -> int:
     return int(_lib.gemm_f32_probe_mfma_flops(int(workgroups), int(iters)))
+
+
+def gemm_f32_probe_mfma16(shape, workgroups, iters, out, stream=0) -> None:
+    _check(_lib.gemm_f32_probe_mfma16(int(shape), int(workgroups), int(iters), out or None,
+                                      stream or None), "gemm_f32_probe_mfma16")
+
+
+def gemm_f32_probe_mfma16_flops(shape, workgroups, iters) -> int:
+    return int(_lib.gemm_f32_probe_mfma16_flops(int(shape), int(workgroups), int(iters)))
 
 
 def gemm_f32_probe_valu(workgroups, iters, out, stream=0) -> None:

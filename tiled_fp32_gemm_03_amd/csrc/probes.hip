@@ -75,6 +75,56 @@ __global__ void __launch_bounds__(kMfmaThreads)
   if (lane == 0) out[blockIdx.x * (kMfmaThreads / 64) + (threadIdx.x >> 6)] = s;
 }
 
+// bf16 matrix-core throughput at one wave per SIMD (256 threads per
+// workgroup), the occupancy of the 16-bit rung's direct-load kernels: each
+// wave runs `iters` rounds of CH16 independent v_mfma_f32_16x16x32_bf16
+// chains (SHAPE 16) or CH32 independent v_mfma_f32_32x32x16_bf16 chains
+// (SHAPE 32) on register operands.  The operands are small positive
+// values, so the accumulators grow by a bounded amount per round and stay
+// finite for any iteration count.
+constexpr int kMfma16Threads = 256;
+constexpr int kMfma16Chains16 = 32, kMfma16Chains32 = 8;
+typedef __bf16 bf16x8p __attribute__((ext_vector_type(8)));
+typedef float f32x4p __attribute__((ext_vector_type(4)));
+
+template <int SHAPE>
+__global__ void __launch_bounds__(kMfma16Threads) mfma16_probe_kernel(int iters, float *out) {
+  const int lane = threadIdx.x & 63;
+  bf16x8p a, b;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    a[j] = (__bf16)(1e-3f * (1 + ((lane + j) & 7)));
+    b[j] = (__bf16)(1e-3f * (1 + ((lane + 3 * j) & 7)));
+  }
+  float s = 0.f;
+  if constexpr (SHAPE == 16) {
+    f32x4p acc[kMfma16Chains16];
+#pragma unroll
+    for (int c = 0; c < kMfma16Chains16; ++c) acc[c] = f32x4p{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int c = 0; c < kMfma16Chains16; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < kMfma16Chains16; ++c) s += acc[c][0] + acc[c][3];
+  } else {
+    f32x16 acc[kMfma16Chains32];
+#pragma unroll
+    for (int c = 0; c < kMfma16Chains32; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[c][r] = 0.f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int c = 0; c < kMfma16Chains32; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < kMfma16Chains32; ++c) s += acc[c][0] + acc[c][15];
+  }
+  if (lane == 0) out[blockIdx.x * (kMfma16Threads / 64) + (threadIdx.x >> 6)] = s;
+}
+
 constexpr int kValuChains = 16;
 constexpr int kValuRounds = 8;  // rounds per loop trip, so the branch is rare
 constexpr int kValuThreads = 256;
@@ -272,6 +322,28 @@ extern "C" int gemm_f32_probe_mfma(int workgroups, int iters, float *out,
   hipError_t e = launch_kernel(mfma_probe_kernel, dim3(workgroups),
                                dim3(kMfmaThreads), static_cast<hipStream_t>(stream),
                                iters, out);
+  return e == hipSuccess ? GEMM_F32_OK : GEMM_F32_LAUNCH_FAILED;
+}
+
+extern "C" long long gemm_f32_probe_mfma16_flops(int shape, int workgroups, int iters) {
+  if ((shape != 16 && shape != 32) || workgroups < 1 || iters < 1) return -1;
+  const long long per_wave_round =
+      shape == 16 ? kMfma16Chains16 * (2LL * 16 * 16 * 32) : kMfma16Chains32 * (2LL * 32 * 32 * 16);
+  return (long long)workgroups * (kMfma16Threads / 64) * (long long)iters * per_wave_round;
+}
+
+extern "C" int gemm_f32_probe_mfma16(int shape, int workgroups, int iters, float *out,
+                                     void *stream) {
+  if ((shape != 16 && shape != 32) || workgroups < 1 || iters < 1) return GEMM_F32_BAD_ARG;
+  if (out == nullptr) return GEMM_F32_NULL_PTR;
+  if (reinterpret_cast<std::uintptr_t>(out) & 3u) return GEMM_F32_MISALIGNED;
+  hipError_t e = shape == 16
+                     ? launch_kernel(mfma16_probe_kernel<16>, dim3(workgroups),
+                                     dim3(kMfma16Threads), static_cast<hipStream_t>(stream),
+                                     iters, out)
+                     : launch_kernel(mfma16_probe_kernel<32>, dim3(workgroups),
+                                     dim3(kMfma16Threads), static_cast<hipStream_t>(stream),
+                                     iters, out);
   return e == hipSuccess ? GEMM_F32_OK : GEMM_F32_LAUNCH_FAILED;
 }
 
