@@ -13,8 +13,9 @@
 // columns (not merely inside the allocation), every store inside C's M x N
 // window, and every direct-load lane offset below 2^32.  It also checks the
 // 32-bit offset guard at its boundary for each direct-load tile family, the
-// guarded and partial windows exhaustively on small sizes, and invariants
-// of the automatic choice and the split-K plan.
+// guarded and partial windows exhaustively on small sizes, the 16-bit
+// kernels' LDS layouts, and invariants of the automatic choice and the
+// split-K plan.
 //
 // Loads at k steps between the first and the last whole step are not all
 // replayed: for a fixed lane and instruction the column (A) or row (B) grows
@@ -471,6 +472,108 @@ void check_ksplit_quarters() {
         }
 }
 
+// ---- the 16-bit direct-load kernels' LDS layouts (entries 3 and 4 of gemm_mixed) --
+// Each layout is a bijection of its stage's 16-byte chunks; the lane of a
+// direct load that fills position j loads the chunk the layout puts at j;
+// at the guard's boundary (2-byte codes) every lane offset fits.  Fragment
+// reads: a 16-byte A read of 16 consecutive rows lands on 16 distinct
+// 16-byte bank groups of a 256-byte window; a transposing 8-byte B read
+// puts each 16-lane group's four 32-byte pieces on distinct positions of a
+// 128-byte window and each 32-lane half's eight on distinct positions of a
+// 256-byte window.
+void check_voff16(const Shape &s, long long elem, const char *what) {
+  ++g_checks;
+  if (elem < 0 || elem * 2 + 16 > (1LL << 32)) fail(s, what, elem, 0);
+}
+
+template <bool M32>
+void check_mixed16_b(const Shape &s) {
+  const char *name = M32 ? "32x32x16 B" : "16x16x32 B";
+  std::vector<char> seen(64 * 16, 0);
+  for (int k = 0; k < 64; ++k)
+    for (int sl = 0; sl < 16; ++sl) {
+      const int pos = M32 ? m32_b_slot(k, sl) : m16_b_slot(k, sl);
+      ++g_checks;
+      if (pos < 0 || pos >= 16 || seen[16 * k + pos]++) fail(s, name, k, sl);
+    }
+  const long long ld = 1000;
+  for (int j = 0; j < 64 * 32; ++j) {
+    const long long e = m16_dma_b_elem<M32>(j, ld);
+    const int k = (int)(e / ld), col = (int)(e % ld), sl = col / 16;
+    const int pos = M32 ? m32_b_slot(k, sl) : m16_b_slot(k, sl);
+    ++g_checks;
+    if (k != j / 32 || col % 8 != 0 || sl >= 16 || 32 * k + 2 * pos + (col % 16) / 8 != j)
+      fail(s, "16-bit B load position", j, e);
+  }
+  // Transposing reads: lane (16-lane group q, l16) reads 8 bytes at byte
+  // 32 * slot_pos + 8 (l16 % 4) of k row kbase + l16 / 4 (+ 8 for the second
+  // half of the 16x16x32 kernel's groups); rows are 512 bytes apart.
+  for (int kb = 0; kb < 64; kb += 4)
+    for (int sl0 = 0; sl0 < 16; ++sl0) {
+      if (M32 && (sl0 & 1)) continue;
+      if (!M32 && (kb & 8)) continue;
+      if (!M32 && kb + 8 + 3 >= 64) continue;
+      std::vector<long long> addr;
+      for (int lane = 0; lane < 32; ++lane) {
+        const int q = lane / 16, l16 = lane % 16;
+        const int k = kb + l16 / 4 + (M32 ? 0 : 8 * q);
+        const int sl = M32 ? sl0 + q : sl0;
+        const int pos = M32 ? m32_b_slot(k, sl) : m16_b_slot(k, sl);
+        addr.push_back(512LL * k + 32 * pos + 8 * (l16 % 4));
+      }
+      for (int span : {16, 32}) {
+        const int window = 8 * span;  // bytes served per cycle in that model
+        for (int l0 = 0; l0 < 32; l0 += span) {
+          std::vector<char> bank(window / 8, 0);
+          for (int l = l0; l < l0 + span; ++l) {
+            ++g_checks;
+            if (bank[(addr[l] % window) / 8]++) fail(s, "16-bit B transposing read bank conflict", kb, sl0);
+          }
+        }
+      }
+    }
+}
+
+void check_mixed16_layouts() {
+  const Shape s{256, 256, 64, 0, 0, 0, "16-bit direct-load layouts"};
+  std::vector<char> seen(256 * 8, 0);
+  for (int r = 0; r < 256; ++r)
+    for (int c = 0; c < 8; ++c) {
+      const int pos = m16_a_pos(r, c);
+      ++g_checks;
+      if (pos < 0 || pos >= 2048 || seen[pos]++) fail(s, "16-bit A layout not a bijection", r, c);
+    }
+  const long long ld = 1000;
+  for (int j = 0; j < 2048; ++j) {
+    const long long e = m16_dma_a_elem(j, ld);
+    const int r = (int)(e / ld), col = (int)(e % ld);
+    ++g_checks;
+    if (col % 8 != 0 || col / 8 >= 8 || m16_a_pos(r, col / 8) != j)
+      fail(s, "16-bit A load position", j, e);
+  }
+  for (int r0 = 0; r0 < 256; r0 += 16)
+    for (int c = 0; c < 8; ++c) {
+      std::vector<char> bank(16, 0);
+      for (int l = 0; l < 16; ++l) {
+        ++g_checks;
+        if (bank[m16_a_pos(r0 + l, c) % 16]++) fail(s, "16-bit A fragment read bank conflict", r0 + l, c);
+      }
+    }
+  check_mixed16_b<false>(s);
+  check_mixed16_b<true>(s);
+  // the guard: 256 rows of A and 64 k rows of B, 2-byte codes
+  const long long lda = (1LL << 32) / (256 * 2LL), ldb = (1LL << 32) / (64 * 2LL);
+  if (!lane_offsets_fit(256, lda, 2) || lane_offsets_fit(256, lda + 1, 2))
+    fail(s, "guard boundary (16-bit A)", lda, 256);
+  if (!lane_offsets_fit(64, ldb, 2) || lane_offsets_fit(64, ldb + 1, 2))
+    fail(s, "guard boundary (16-bit B)", ldb, 64);
+  for (int j = 0; j < 2048; ++j) check_voff16(s, m16_dma_a_elem(j, lda), "16-bit A lane offset");
+  for (int j = 0; j < 2048; ++j) {
+    check_voff16(s, m16_dma_b_elem<false>(j, ldb), "16-bit B lane offset (16x16x32)");
+    check_voff16(s, m16_dma_b_elem<true>(j, ldb), "16-bit B lane offset (32x32x16)");
+  }
+}
+
 // ---- windows, exhaustively on small sizes ---------------------------------------
 void check_windows() {
   const Shape s{0, 0, 0, 0, 0, 0, "windows"};
@@ -612,6 +715,7 @@ int main(int argc, char **argv) {
   boundary_b<32>(64, "128-column B steps, BK 64");
   boundary_b<16>(64, "64-column B steps, BK 64");
   check_ksplit_quarters();
+  check_mixed16_layouts();
   check_windows();
   check_orders();
   std::printf("replay: %d shapes, %lld checks, %d failures\n", (int)shapes.size(), g_checks,

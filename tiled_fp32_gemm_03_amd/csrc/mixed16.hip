@@ -52,8 +52,7 @@ struct M16 {
   static_assert(DMA <= 2 * KG * TBM, "two direct loads per row of MFMAs cover a step's");
 };
 
-__device__ inline int m16_a_pos(int r, int c) { return r * M16::ACH + (c ^ ((r >> 1) & 7)); }
-__device__ inline int m16_b_slot(int k, int s) { return s ^ ((k & 3) | (((k >> 3) & 1) << 2)); }
+static_assert(M16::ACH == 8 && M16::BSL == 16, "layouts of addr_math.hpp (m16_a_pos, m16_b_slot)");
 
 template <int FMT>
 __device__ inline f32x4 mfma32(i16x8 b, i16x8 a, f32x4 acc) {
@@ -110,20 +109,12 @@ __global__ void __launch_bounds__(256) mixed16_kernel(MixedProblem p, int tiles_
   // addresses: instruction q fills 1 KB of the stage in layout order.
   unsigned voff[W::DMA];
 #pragma unroll
-  for (int q = 0; q < W::A_DMA; ++q) {
-    const int j = 64 * (wave * W::A_DMA + q) + lane;  // A chunk position
-    const int r = j / W::ACH;
-    const int c = (j % W::ACH) ^ ((r >> 1) & 7);
-    voff[q] = (unsigned)(((long long)r * p.lda + 8 * c) * 2);
-  }
+  for (int q = 0; q < W::A_DMA; ++q)
+    voff[q] = (unsigned)(m16_dma_a_elem(64 * (wave * W::A_DMA + q) + lane, p.lda) * 2);
 #pragma unroll
-  for (int q = 0; q < W::B_DMA; ++q) {
-    const int j = 64 * (wave * W::B_DMA + q) + lane;  // B chunk position
-    const int k = j / (2 * W::BSL);
-    const int pos = j % (2 * W::BSL);
-    const int c = 2 * m16_b_slot(k, pos >> 1) + (pos & 1);  // the permutation is an involution
-    voff[W::A_DMA + q] = (unsigned)(((long long)k * p.ldb + 8 * c) * 2);
-  }
+  for (int q = 0; q < W::B_DMA; ++q)
+    voff[W::A_DMA + q] =
+        (unsigned)(m16_dma_b_elem<false>(64 * (wave * W::B_DMA + q) + lane, p.ldb) * 2);
   const unsigned wave_a = (unsigned)(wave * W::A_DMA * 1024);
   const unsigned wave_b = (unsigned)(W::A_BYTES + wave * W::B_DMA * 1024);
   const long long b_step = (long long)W::BK * p.ldb;
@@ -261,9 +252,9 @@ __global__ void __launch_bounds__(256) mixed16_kernel(MixedProblem p, int tiles_
 // two transposing reads: 16-lane group q = lane / 16 reads the 16 columns
 // 32 bn + 16 (q % 2) .. + 15 at k rows 16 kg + 8 (q / 2) + 4 half .. + 3.
 // B rows of 256 n (16 slots of 32 bytes), slot s of k row k at
-// s ^ (2 (k % 4)): a 32-lane half reads two adjacent slots in four
-// consecutive k rows, and the permutation puts those eight 32-byte pieces
-// on distinct banks (rows are 512 bytes, two whole bank rounds, apart).
+// m32_b_slot(k, s) (addr_math.hpp): a 32-lane half reads two adjacent
+// slots in four consecutive k rows, and the permutation puts those eight
+// 32-byte pieces, and each 16-lane group's four, on distinct banks.
 // Each element is summed in 16-deep groups in ascending k, as by the
 // 32 x 32 x 16 entries that stage through registers, so the bits are
 // theirs.
@@ -286,7 +277,6 @@ struct M32 {
   static_assert(DMA == 2 * 2 * TBM, "two direct loads per row of the first two groups");
 };
 
-__device__ inline int m32_b_slot(int k, int s) { return s ^ (2 * (k & 3)); }
 
 template <int FMT>
 __device__ inline f32x16 mfma32x32(i16x8 b, i16x8 a, f32x16 acc) {
@@ -334,20 +324,12 @@ __global__ void __launch_bounds__(256) mixed32_kernel(MixedProblem p, int tiles_
 
   unsigned voff[W::DMA];
 #pragma unroll
-  for (int q = 0; q < W::A_DMA; ++q) {
-    const int j = 64 * (wave * W::A_DMA + q) + lane;  // A chunk position
-    const int r = j / W::ACH;
-    const int c = (j % W::ACH) ^ ((r >> 1) & 7);
-    voff[q] = (unsigned)(((long long)r * p.lda + 8 * c) * 2);
-  }
+  for (int q = 0; q < W::A_DMA; ++q)
+    voff[q] = (unsigned)(m16_dma_a_elem(64 * (wave * W::A_DMA + q) + lane, p.lda) * 2);
 #pragma unroll
-  for (int q = 0; q < W::B_DMA; ++q) {
-    const int j = 64 * (wave * W::B_DMA + q) + lane;  // B chunk position
-    const int k = j / (2 * W::BSL);
-    const int pos = j % (2 * W::BSL);
-    const int c = 2 * m32_b_slot(k, pos >> 1) + (pos & 1);  // the permutation is an involution
-    voff[W::A_DMA + q] = (unsigned)(((long long)k * p.ldb + 8 * c) * 2);
-  }
+  for (int q = 0; q < W::B_DMA; ++q)
+    voff[W::A_DMA + q] =
+        (unsigned)(m16_dma_b_elem<true>(64 * (wave * W::B_DMA + q) + lane, p.ldb) * 2);
   const unsigned wave_a = (unsigned)(wave * W::A_DMA * 1024);
   const unsigned wave_b = (unsigned)(W::A_BYTES + wave * W::B_DMA * 1024);
   const long long b_step = (long long)W::BK * p.ldb;
