@@ -26,6 +26,7 @@
 #include <vector>
 
 #include "addr_math.hpp"
+#include "addr_math16.hpp"
 #include "host_plan.hpp"
 
 using namespace gemm_f32_impl;

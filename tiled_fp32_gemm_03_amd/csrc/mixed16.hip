@@ -25,6 +25,7 @@
 // entries.
 #include "gemm_internal.hpp"
 #include "w16_tiles.hpp"
+#include "addr_math16.hpp"
 
 namespace gemm_f32_impl {
 namespace {
@@ -52,7 +53,7 @@ struct M16 {
   static_assert(DMA <= 2 * KG * TBM, "two direct loads per row of MFMAs cover a step's");
 };
 
-static_assert(M16::ACH == 8 && M16::BSL == 16, "layouts of addr_math.hpp (m16_a_pos, m16_b_slot)");
+static_assert(M16::ACH == 8 && M16::BSL == 16, "layouts of addr_math16.hpp (m16_a_pos, m16_b_slot)");
 
 template <int FMT>
 __device__ inline f32x4 mfma32(i16x8 b, i16x8 a, f32x4 acc) {
@@ -252,7 +253,7 @@ __global__ void __launch_bounds__(256) mixed16_kernel(MixedProblem p, int tiles_
 // two transposing reads: 16-lane group q = lane / 16 reads the 16 columns
 // 32 bn + 16 (q % 2) .. + 15 at k rows 16 kg + 8 (q / 2) + 4 half .. + 3.
 // B rows of 256 n (16 slots of 32 bytes), slot s of k row k at
-// m32_b_slot(k, s) (addr_math.hpp): a 32-lane half reads two adjacent
+// m32_b_slot(k, s) (addr_math16.hpp): a 32-lane half reads two adjacent
 // slots in four consecutive k rows, and the permutation puts those eight
 // 32-byte pieces, and each 16-lane group's four, on distinct banks.
 // Each element is summed in 16-deep groups in ascending k, as by the
