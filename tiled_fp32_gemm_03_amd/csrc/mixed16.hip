@@ -241,11 +241,14 @@ __global__ void __launch_bounds__(256) mixed16_kernel(MixedProblem p, int tiles_
 }
 
 // The same tile, waves, steps and direct loads on 32x32x16 MFMAs.  One
-// wave per SIMD issuing independent v_mfma_f32_16x16x32_bf16 reaches about
-// 1.45 PFLOP/s on the whole chip with no memory traffic at all, and
-// v_mfma_f32_32x32x16_bf16 about 2.03 (each instruction is twice the work,
-// so a lone wave keeps the matrix pipe full); the 16x16 form above runs at
-// about 0.9 of its instruction's ceiling.  A wave's 128 x 128 is 4 x 4
+// wave per SIMD issuing independent v_mfma_f32_16x16x32_bf16 reaches 1.3 to
+// 1.5 PFLOP/s on the whole chip with no memory traffic at all, and
+// v_mfma_f32_32x32x16_bf16 2.0 to 2.4 (each instruction is twice the work,
+// so a lone wave keeps the matrix pipe full; gemm_f32_probe_mfma16).  The
+// 16x16 form above runs at about 0.86 of its instruction's ceiling; this
+// one needs 8% fewer cycles for a 4096^3 product, but under its load the
+// engine clock settles about 14% lower (2.0 against 2.3 GHz), so it is
+// faster only where the C stores dominate (K = 64).  A wave's 128 x 128 is 4 x 4
 // blocks of 32 x 32 (16 accumulators each, 256 in all); a 64-deep step is
 // 4 groups of 16 k, 16 MFMAs per group.  Fragments per lane (l32 = lane %
 // 32, h = lane / 32): A row l32 of block bm, k = 16 kg + 8 h .. + 7, one
