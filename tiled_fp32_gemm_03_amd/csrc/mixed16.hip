@@ -462,12 +462,12 @@ bool mixed16_fits(const MixedProblem &p) {
          lane_offsets_fit(M16::BM, p.lda, 2) && lane_offsets_fit(M16::BK, p.ldb, 2);
 }
 
-hipError_t launch_mixed16(int format, const MixedProblem &p, hipStream_t s, bool prefetch) {
+hipError_t launch_mixed16(int format, const MixedProblem &p, hipStream_t s, bool mfma32) {
   if (!mixed16_fits(p)) return hipErrorInvalidValue;
   const long long tiles_m = ceil_div(p.M, M16::BM), tiles_n = ceil_div(p.N, M16::BN);
   const long long ntiles = tiles_m * tiles_n;
   if (ntiles > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (prefetch) {
+  if (mfma32) {
     auto kern = format == kMixedBf16 ? mixed32_kernel<kMixedBf16> : mixed32_kernel<kMixedF16>;
     long long grid = format == kMixedBf16 ? resident_workgroups<mixed32_kernel<kMixedBf16>, 256>()
                                           : resident_workgroups<mixed32_kernel<kMixedF16>, 256>();
