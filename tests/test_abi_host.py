@@ -268,10 +268,11 @@ def test_tile_queries():
         q = g.gemm_f32_tile(name, -1, 100, 100, 100)
         assert (q["BM"], q["BN"], q["BK"], q["threads"]) == (t, t, t, t * t)
     q = g.gemm_f32_tile("valu", -1, 100, 100, 100)
-    assert (q["BM"], q["BN"], q["BK"], q["threads"]) == (128, 128, 8, 256)
-    assert g.gemm_f32_num_configs("valu") >= 2
+    assert (q["BM"], q["BN"], q["BK"], q["threads"], q["config"]) == (128, 128, 16, 256, 5)
+    assert g.gemm_f32_num_configs("valu") == 6
     for i in range(g.gemm_f32_num_configs("valu")):
-        assert g.gemm_f32_tile("valu", i, 9, 9, 9)["config"] == i
+        q = g.gemm_f32_tile("valu", i, 9, 9, 9)
+        assert q["config"] == i and q["BK"] == (8 if i < 4 else 16)
     n = g.gemm_f32_num_configs("prod")
     assert n >= 3
     strip = g.gemm_f32_tile("prod", -1, 1, 4095, 2049)["config"]
@@ -329,7 +330,8 @@ def test_package_load_model_matches_oracle_model():
             t = g.gemm_f32_tile(v, -1, M, N, K)
             assert roofline.issued_load_elements(v, M, N, K, t) == model.tiled_loads(M, N, K, t["BM"])
         t = g.gemm_f32_tile("valu", -1, M, N, K)
-        assert roofline.issued_load_elements("valu", M, N, K, t) == model.blocked_loads(M, N, K, 128, 128, 8)
+        assert roofline.issued_load_elements("valu", M, N, K, t) == model.blocked_loads(
+            M, N, K, 128, 128, t["BK"])
         for i in range(g.gemm_f32_num_configs("prod")):
             try:
                 t = g.gemm_f32_tile("prod", i, M, N, K)

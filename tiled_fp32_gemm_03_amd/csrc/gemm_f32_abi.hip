@@ -122,7 +122,7 @@ extern "C" int gemm_f32_tile(int variant, int config, int M, int N, int K,
     bn = prod_kind(chosen) == kStripN ? strip_cols(N) : c.BN;
     bk = c.BK, nt = 64 * c.WGM * c.WGN;
   } else if (variant == GEMM_F32_VALU) {
-    bm = bn = kValuTile, bk = kValuBK, nt = kValuThreads;
+    bm = bn = kValuTile, bk = valu_config_bk(chosen), nt = kValuThreads;
   } else {
     const int t = kTiledT[variant];
     bm = bn = bk = t, nt = t * t;

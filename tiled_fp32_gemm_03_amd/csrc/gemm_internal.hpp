@@ -27,8 +27,9 @@ hipError_t launch_tiled(int T, bool padded, const Problem &p, hipStream_t s);
 
 // Register-blocked VALU kernel: 128 x 128 tiles, 256 threads, k step 8; its
 // launch-table entries differ only in register budget.
-constexpr int kValuTile = 128, kValuBK = 8, kValuThreads = 256;
+constexpr int kValuTile = 128, kValuThreads = 256;
 int valu_num_configs();
+int valu_config_bk(int index);  // the k step of launch-table entry `index`
 int valu_choose(int M, int N, int K);
 hipError_t launch_valu(int index, const Problem &p, hipStream_t s);
 

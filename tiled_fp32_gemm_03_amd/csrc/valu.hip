@@ -28,55 +28,81 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
 
 constexpr int kVT = kValuTile;      // tile edge
-constexpr int kVBK = kValuBK;       // k step
 constexpr int kVPad = 4;            // floats after each LDS row
 constexpr int kVS = kVT + kVPad;
 constexpr int kVThreads = kValuThreads;
-static_assert(kVT == 128 && kVBK == 8 && kVThreads == 256,
-              "thread-to-element maps below assume 128 x 128 x 8 and 256 threads");
+static_assert(kVT == 128 && kVThreads == 256,
+              "thread-to-element maps below assume 128 x 128 tiles and 256 threads");
 
+// One k step of BK (8 or 16) staged through registers: BK / 8 chunks of 4
+// floats of A and of B per thread.  Chunk j of thread tid is A chunk
+// tid + 256 j of the tile's 128 rows x BK / 4 chunks and B chunk tid + 256 j
+// of its BK rows x 32 chunks.
+template <int BK>
 struct ValuStage {
-  f32x4 a;  // A[m][k0 + 4c .. +3] for this thread's (m, c)
-  f32x4 b;  // B[k][n .. n+3] for this thread's (k, n)
+  static constexpr int CH = BK / 8;
+  f32x4 a[CH];  // A[m][k0 + 4c .. +3] for this thread's (m, c)
+  f32x4 b[CH];  // B[k][n .. n+3] for this thread's (k, n)
 };
 
-template <bool GUARD>
-__device__ inline void valu_load(ValuStage &st, const Problem &p, int m0, int n0,
+template <int BK>
+__device__ inline void valu_a_chunk(int j, int tid, int &am, int &ac) {
+  const int c = tid + kVThreads * j;
+  am = c / (BK / 4);
+  ac = (c % (BK / 4)) * 4;
+}
+__device__ inline void valu_b_chunk(int j, int tid, int &bk, int &bn) {
+  const int c = tid + kVThreads * j;
+  bk = c >> 5;
+  bn = (c & 31) * 4;
+}
+
+template <int BK, bool GUARD>
+__device__ inline void valu_load(ValuStage<BK> &st, const Problem &p, int m0, int n0,
                                  int k0, int tid) {
-  const int am = tid >> 1, ac = (tid & 1) * 4;      // 128 rows x 2 chunks
-  const int bk = tid >> 5, bn = (tid & 31) * 4;     // 8 rows x 32 chunks
-  const int gm = m0 + am, gka = k0 + ac;
-  const int gkb = k0 + bk, gn = n0 + bn;
-  const float *pa = p.A + (long long)gm * p.lda + gka;
-  const float *pb = p.B + (long long)gkb * p.ldb + gn;
-  if (!GUARD) {
-    st.a = *reinterpret_cast<const f32x4u *>(pa);
-    st.b = *reinterpret_cast<const f32x4u *>(pb);
-  } else {
-    f32x4 a{0.f, 0.f, 0.f, 0.f}, b{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (gm < p.M && gka + e < p.K) a[e] = pa[e];
-      if (gkb < p.K && gn + e < p.N) b[e] = pb[e];
+  for (int j = 0; j < ValuStage<BK>::CH; ++j) {
+    int am, ac, bk, bn;
+    valu_a_chunk<BK>(j, tid, am, ac);
+    valu_b_chunk(j, tid, bk, bn);
+    const int gm = m0 + am, gka = k0 + ac;
+    const int gkb = k0 + bk, gn = n0 + bn;
+    const float *pa = p.A + (long long)gm * p.lda + gka;
+    const float *pb = p.B + (long long)gkb * p.ldb + gn;
+    if (!GUARD) {
+      st.a[j] = *reinterpret_cast<const f32x4u *>(pa);
+      st.b[j] = *reinterpret_cast<const f32x4u *>(pb);
+    } else {
+      f32x4 a{0.f, 0.f, 0.f, 0.f}, b{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (gm < p.M && gka + e < p.K) a[e] = pa[e];
+        if (gkb < p.K && gn + e < p.N) b[e] = pb[e];
+      }
+      st.a[j] = a;
+      st.b[j] = b;
     }
-    st.a = a;
-    st.b = b;
   }
 }
 
-__device__ inline void valu_store_lds(const ValuStage &st, float *as, float *bs,
-                                      int tid) {
-  const int am = tid >> 1, ac = (tid & 1) * 4;
-  const int bk = tid >> 5, bn = (tid & 31) * 4;
+template <int BK>
+__device__ inline void valu_store_lds(const ValuStage<BK> &st, float *as, float *bs, int tid) {
 #pragma unroll
-  for (int e = 0; e < 4; ++e) as[(ac + e) * kVS + am] = st.a[e];  // transposed
-  *reinterpret_cast<f32x4 *>(bs + bk * kVS + bn) = st.b;
+  for (int j = 0; j < ValuStage<BK>::CH; ++j) {
+    int am, ac, bk, bn;
+    valu_a_chunk<BK>(j, tid, am, ac);
+    valu_b_chunk(j, tid, bk, bn);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) as[(ac + e) * kVS + am] = st.a[j][e];  // transposed
+    *reinterpret_cast<f32x4 *>(bs + bk * kVS + bn) = st.b[j];
+  }
 }
 
 // KUNROLL: how many of the BK k values the compiler may unroll, i.e. how far
 // LDS reads run ahead of the FMAs; fewer live fragments means fewer VGPRs.
-// WAVES: waves per SIMD the register allocation must allow.
-template <int KUNROLL, int WAVES>
+// WAVES: waves per SIMD the register allocation must allow.  BK: the k
+// step, i.e. how many k share one barrier and one round of staging.
+template <int KUNROLL, int WAVES, int kVBK>
 __global__ void __launch_bounds__(kVThreads) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES)))
     valu_kernel(Problem p, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(16))) float as[2][kVBK * kVS];
@@ -101,9 +127,9 @@ __global__ void __launch_bounds__(kVThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
 
-    ValuStage st;
-    if (interior && kVBK <= p.K) valu_load<false>(st, p, m0, n0, 0, tid);
-    else valu_load<true>(st, p, m0, n0, 0, tid);
+    ValuStage<kVBK> st;
+    if (interior && kVBK <= p.K) valu_load<kVBK, false>(st, p, m0, n0, 0, tid);
+    else valu_load<kVBK, true>(st, p, m0, n0, 0, tid);
     valu_store_lds(st, as[0], bs[0], tid);
     __syncthreads();
 
@@ -112,8 +138,8 @@ __global__ void __launch_bounds__(kVThreads) __attribute__((amdgpu_waves_per_eu(
       const bool more = kt + 1 < nk;
       if (more) {
         const int k1 = (kt + 1) * kVBK;
-        if (interior && k1 + kVBK <= p.K) valu_load<false>(st, p, m0, n0, k1, tid);
-        else valu_load<true>(st, p, m0, n0, k1, tid);
+        if (interior && k1 + kVBK <= p.K) valu_load<kVBK, false>(st, p, m0, n0, k1, tid);
+        else valu_load<kVBK, true>(st, p, m0, n0, k1, tid);
       }
       const float *a_s = as[cur];
       const float *b_s = bs[cur];
@@ -160,13 +186,15 @@ __global__ void __launch_bounds__(kVThreads) __attribute__((amdgpu_waves_per_eu(
 // single wave issues a vector instruction only every few cycles, so the
 // vector ALU needs several resident waves per SIMD to stay busy.
 struct ValuEntry {
-  int kunroll, waves;
+  int kunroll, waves, bk;
 };
 constexpr ValuEntry kValuEntries[] = {
-    {8, 2},  // 0: fully unrolled k step, ~232 VGPRs, 2 waves per SIMD
-    {1, 4},  // 1: rolled k loop, 118 VGPRs, 4 waves per SIMD
-    {2, 3},  // 2: k loop unrolled by 2, 3 waves per SIMD
-    {4, 4},  // 3: k loop unrolled by 4 under a 4-wave budget
+    {8, 2, 8},   // 0: fully unrolled k step, ~232 VGPRs, 2 waves per SIMD
+    {1, 4, 8},   // 1: rolled k loop, 118 VGPRs, 4 waves per SIMD
+    {2, 3, 8},   // 2: k loop unrolled by 2, 3 waves per SIMD
+    {4, 4, 8},   // 3: k loop unrolled by 4 under a 4-wave budget
+    {4, 4, 16},  // 4: entry 3 with 16-deep steps (half the barriers)
+    {2, 4, 16},  // 5: 16-deep steps, k loop unrolled by 2
 };
 constexpr int kValuNumEntries = sizeof(kValuEntries) / sizeof(kValuEntries[0]);
 
@@ -174,14 +202,19 @@ template <int E>
 hipError_t launch_valu_entry(dim3 grid, const Problem &p, int tiles_m, int tiles_n,
                              hipStream_t s) {
   constexpr ValuEntry e = kValuEntries[E];
-  return launch_kernel(valu_kernel<e.kunroll, e.waves>, grid, dim3(kVThreads), s, p,
+  return launch_kernel(valu_kernel<e.kunroll, e.waves, e.bk>, grid, dim3(kVThreads), s, p,
                        tiles_m, tiles_n);
 }
 
 }  // namespace
 
 int valu_num_configs() { return kValuNumEntries; }
-int valu_choose(int M, int N, int K) { return 3; }
+
+int valu_config_bk(int index) { return kValuEntries[index].bk; }
+// Entry 5: best or within run-to-run spread of the best on the measured
+// workloads (4096^3 87.7 TFLOP/s against 86.1 for entry 3 and 88.6 for
+// entry 0; 4097 x 4095 x 2049 71.8; 16384 x 16384 x 64 76.4).
+int valu_choose(int M, int N, int K) { return 5; }
 
 hipError_t launch_valu(int index, const Problem &p, hipStream_t s) {
   const long long tiles_m = ceil_div(p.M, kVT), tiles_n = ceil_div(p.N, kVT);
@@ -195,6 +228,8 @@ hipError_t launch_valu(int index, const Problem &p, hipStream_t s) {
     case 1: return launch_valu_entry<1>(g, p, (int)tiles_m, (int)tiles_n, s);
     case 2: return launch_valu_entry<2>(g, p, (int)tiles_m, (int)tiles_n, s);
     case 3: return launch_valu_entry<3>(g, p, (int)tiles_m, (int)tiles_n, s);
+    case 4: return launch_valu_entry<4>(g, p, (int)tiles_m, (int)tiles_n, s);
+    case 5: return launch_valu_entry<5>(g, p, (int)tiles_m, (int)tiles_n, s);
     default: return hipErrorInvalidValue;
   }
 }
