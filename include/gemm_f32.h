@@ -101,8 +101,9 @@ extern "C" {
 /* Register-blocked kernel on the vector ALU (no matrix cores): 128 x 128
  * workgroup tiles, 256 threads, each thread owns 8 x 8 outputs (four 4 x 4
  * blocks) in registers and does 64 fp32 FMAs per k from 16 LDS values; A is
- * stored k-major in LDS, two LDS stages, one barrier per 8-deep k step,
- * out-of-range elements loaded as 0.  The "one thread, several outputs"
+ * stored k-major in LDS, two LDS stages, one barrier per 8- or 16-deep k
+ * step (launch-table entries 0-3 and 4-5; entry 5 by default), out-of-range
+ * elements loaded as 0.  The "one thread, several outputs"
  * step the pages point to (geek-doc.cn sections 三 and 五) without MFMA. */
 #define GEMM_F32_VALU 6
 #define GEMM_F32_NUM_VARIANTS 7
